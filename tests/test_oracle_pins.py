@@ -1,0 +1,301 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+* brute force: every output element from the definition in scalar pure-Python
+  loops over a padded [B, Lmax] index space, on tiny inputs;
+* a library special case: torch's fp64 CPU scaled_dot_product_attention and
+  its autograd gradients, per sequence;
+* closed forms and invariants of softmax and SiLU attention;
+* central finite differences of the gradients.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from jagged_attention_ads_amd.workloads import offsets_from_lengths
+
+CASES = [
+    # (q_lengths, kv_lengths, H, d)
+    ([3, 1, 5, 2], [3, 1, 5, 2], 2, 4),       # self, ragged
+    ([2, 4, 1], [5, 3, 7], 2, 3),             # cross, Lq < Lk and Lq > Lk
+    ([9, 6], [9, 6], 1, 8),                   # longer self
+    ([4, 0, 3, 2], [6, 2, 0, 2], 3, 2),       # empty query / empty key sequences
+    ([1], [1], 1, 1),
+]
+
+
+def _draw(qlen, klen, H, d, seed, std=1.0):
+    rng = np.random.default_rng(seed)
+    qo, ko = offsets_from_lengths(qlen), offsets_from_lengths(klen)
+    q = std * rng.standard_normal((qo[-1], H, d))
+    k = std * rng.standard_normal((ko[-1], H, d))
+    v = rng.standard_normal((ko[-1], H, d))
+    do = rng.standard_normal((qo[-1], H, d))
+    return q, k, v, do, qo, ko
+
+
+def brute_force_fwd(q, k, v, qo, ko, scale, activation, causal):
+    """Independent scalar implementation: padded index space, explicit mask."""
+    B = len(qo) - 1
+    H, d = q.shape[1], q.shape[2]
+    lmax_q = max([qo[b + 1] - qo[b] for b in range(B)] + [0])
+    lmax_k = max([ko[b + 1] - ko[b] for b in range(B)] + [0])
+    out = np.zeros(q.shape)
+    lse = np.full((H, q.shape[0]), -math.inf)
+    for b in range(B):
+        lq, lk = qo[b + 1] - qo[b], ko[b + 1] - ko[b]
+        for h in range(H):
+            for i in range(lmax_q):
+                if i >= lq:
+                    continue
+                scores, weights_idx = [], []
+                for j in range(lmax_k):
+                    keep = j < lk and (not causal or j - i <= lk - lq)
+                    if keep:
+                        s = 0.0
+                        for c in range(d):
+                            s += q[qo[b] + i, h, c] * k[ko[b] + j, h, c]
+                        scores.append(scale * s)
+                        weights_idx.append(j)
+                if activation == "softmax":
+                    if not scores:
+                        continue
+                    mx = max(scores)
+                    ex = [math.exp(s - mx) for s in scores]
+                    tot = sum(ex)
+                    w = [e / tot for e in ex]
+                    lse[h, qo[b] + i] = mx + math.log(tot)
+                else:
+                    w = [s / (1.0 + math.exp(-s)) / lk for s in scores]
+                for wj, j in zip(w, weights_idx):
+                    for c in range(d):
+                        out[qo[b] + i, h, c] += wj * v[ko[b] + j, h, c]
+    return out, lse
+
+
+@pytest.mark.parametrize("activation", ["softmax", "silu"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_forward_matches_brute_force(case, causal, activation):
+    qlen, klen, H, d = CASES[case]
+    q, k, v, _, qo, ko = _draw(qlen, klen, H, d, seed=case)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = oracle.attention_fwd(q, k, v, qo, ko, scale, activation, causal)
+    ref_out, ref_lse = brute_force_fwd(q, k, v, qo, ko, scale, activation, causal)
+    np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
+    if activation == "softmax":
+        assert np.array_equal(np.isneginf(lse), np.isneginf(ref_lse))
+        fin = np.isfinite(ref_lse)
+        np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=0, atol=1e-12)
+    else:
+        assert lse is None
+
+
+def _sdpa_per_sequence(q, k, v, do, qo, ko, scale, causal):
+    """torch fp64 CPU SDPA per (sequence), with autograd gradients."""
+    out = np.zeros(q.shape)
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(len(qo) - 1):
+        qs, qe, ks, ke = qo[b], qo[b + 1], ko[b], ko[b + 1]
+        if qe == qs or ke == ks:
+            continue
+        Q = torch.tensor(q[qs:qe].transpose(1, 0, 2), requires_grad=True)
+        K = torch.tensor(k[ks:ke].transpose(1, 0, 2), requires_grad=True)
+        V = torch.tensor(v[ks:ke].transpose(1, 0, 2), requires_grad=True)
+        O = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=causal, scale=scale)
+        O.backward(torch.tensor(do[qs:qe].transpose(1, 0, 2)))
+        out[qs:qe] = O.detach().numpy().transpose(1, 0, 2)
+        dq[qs:qe] = Q.grad.numpy().transpose(1, 0, 2)
+        dk[ks:ke] = K.grad.numpy().transpose(1, 0, 2)
+        dv[ks:ke] = V.grad.numpy().transpose(1, 0, 2)
+    return out, dq, dk, dv
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_matches_torch_sdpa_fp64(causal):
+    rng = np.random.default_rng(7)
+    qlen = rng.integers(1, 40, size=6)
+    klen = qlen.copy() if causal else rng.integers(1, 40, size=6)   # torch's is_causal is top-left
+    q, k, v, do, qo, ko = _draw(qlen, klen, 3, 16, seed=11)
+    scale = 0.25
+    out, _ = oracle.attention_fwd(q, k, v, qo, ko, scale, "softmax", causal)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, qo, ko, scale, "softmax", causal)
+    r_out, r_dq, r_dk, r_dv = _sdpa_per_sequence(q, k, v, do, qo, ko, scale, causal)
+    for a, r in [(out, r_out), (dq, r_dq), (dk, r_dk), (dv, r_dv)]:
+        np.testing.assert_allclose(a, r, rtol=0, atol=1e-12)
+
+
+def test_golden_closed_forms():
+    """Hand-derived cases stored under tests/golden (derivations inside)."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "closed_form_cases.json")
+    with open(path) as f:
+        cases = json.load(f)["cases"]
+    assert len(cases) >= 4
+    for c in cases:
+        q = np.array(c["q"], float)[:, None, :]
+        k = np.array(c["k"], float)[:, None, :]
+        v = np.array(c["v"], float)[:, None, :]
+        out, lse = oracle.attention_fwd(q, k, v, c["q_offsets"], c["kv_offsets"], c["scale"],
+                                        c["activation"], c["causal"])
+        exp_out = np.array([[eval(x, {"ln": math.log}) for x in row] for row in c["out"]])
+        np.testing.assert_allclose(out[:, 0, :], exp_out, rtol=0, atol=1e-14, err_msg=c["name"])
+        if "lse" in c:
+            exp_lse = np.array([-math.inf if x == "-inf" else eval(x, {"ln": math.log}) for x in c["lse"]])
+            assert np.array_equal(np.isneginf(lse[0]), np.isneginf(exp_lse)), c["name"]
+            fin = np.isfinite(exp_lse)
+            np.testing.assert_allclose(lse[0][fin], exp_lse[fin], rtol=0, atol=1e-14, err_msg=c["name"])
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_rows_sum_to_one(causal):
+    qlen, klen = [5, 3, 7, 2], [6, 3, 2, 9]
+    q, k, _, _, qo, ko = _draw(qlen, klen, 2, 4, seed=3)
+    v = np.ones_like(k)
+    out, lse = oracle.attention_fwd(q, k, v, qo, ko, 0.5, "softmax", causal)
+    live = np.isfinite(lse.T)                  # [T_q, H]
+    np.testing.assert_allclose(out[live], 1.0, rtol=0, atol=1e-13)
+    assert np.all(out[~live] == 0.0)
+    if causal:   # rows i < Lq - Lk of a cross pair see no key
+        assert not live.all()
+
+
+def test_softmax_single_key():
+    qlen = [4, 1, 6]
+    q, k, v, _, qo, ko = _draw(qlen, [1, 1, 1], 2, 5, seed=4)
+    s = 0.3
+    for causal in (False, True):
+        out, lse = oracle.attention_fwd(q, k, v, qo, ko, s, "softmax", causal)
+        for b in range(3):
+            rows = slice(qo[b], qo[b + 1])
+            lq = qo[b + 1] - qo[b]
+            live = np.arange(lq) >= (lq - 1 if causal else 0)
+            np.testing.assert_allclose(out[rows][live], np.broadcast_to(v[b], out[rows][live].shape), atol=1e-14)
+            exp_lse = s * np.einsum("thd,hd->ht", q[rows], k[b])
+            np.testing.assert_allclose(lse[:, rows][:, live], exp_lse[:, live], atol=1e-13)
+            assert np.all(np.isneginf(lse[:, rows][:, ~live]))
+
+
+def test_causal_first_row_is_first_value():
+    q, k, v, _, qo, ko = _draw([5, 8], [5, 8], 2, 3, seed=5)
+    out, _ = oracle.attention_fwd(q, k, v, qo, ko, 1.0, "softmax", True)
+    for b in range(2):
+        np.testing.assert_allclose(out[qo[b]], v[ko[b]], atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_keys_give_prefix_mean(causal):
+    qlen = [6, 4]
+    q, _, v, _, qo, ko = _draw(qlen, qlen, 2, 3, seed=6)
+    k = np.zeros((ko[-1], 2, 3))
+    out, lse = oracle.attention_fwd(q, k, v, qo, ko, 1.0, "softmax", causal)
+    for b in range(2):
+        lq = qlen[b]
+        for i in range(lq):
+            n = i + 1 if causal else lq
+            np.testing.assert_allclose(out[qo[b] + i], v[ko[b]:ko[b] + n].mean(axis=0), atol=1e-14)
+            np.testing.assert_allclose(lse[:, qo[b] + i], math.log(n), atol=1e-14)
+
+
+def test_key_shift_invariance():
+    qlen, klen = [4, 7], [9, 3]
+    q, k, v, _, qo, ko = _draw(qlen, klen, 2, 4, seed=8)
+    s = 0.7
+    u = np.array([[0.3, -1.0, 2.0, 0.5], [1.5, 0.0, -0.25, 1.0]])   # per head
+    out0, lse0 = oracle.attention_fwd(q, k, v, qo, ko, s, "softmax", False)
+    out1, lse1 = oracle.attention_fwd(q, k + u[None], v, qo, ko, s, "softmax", False)
+    np.testing.assert_allclose(out1, out0, atol=1e-12)
+    np.testing.assert_allclose(lse1, lse0 + s * np.einsum("thd,hd->ht", q, u), atol=1e-12)
+
+
+@pytest.mark.parametrize("activation", ["softmax", "silu"])
+def test_sequence_permutation(activation):
+    qlen, klen = np.array([3, 8, 1, 5]), np.array([7, 2, 4, 5])
+    q, k, v, do, qo, ko = _draw(qlen, klen, 2, 4, seed=9)
+    perm = [2, 0, 3, 1]
+    qo2, ko2 = offsets_from_lengths(qlen[perm]), offsets_from_lengths(klen[perm])
+    cat = lambda x, o: np.concatenate([x[o[p]:o[p + 1]] for p in perm])  # noqa: E731
+    args = (0.5, activation, True)
+    out, lse = oracle.attention_fwd(q, k, v, qo, ko, *args)
+    out2, lse2 = oracle.attention_fwd(cat(q, qo), cat(k, ko), cat(v, ko), qo2, ko2, *args)
+    np.testing.assert_array_equal(out2, cat(out, qo))
+    g = oracle.attention_bwd(q, k, v, do, qo, ko, *args)
+    g2 = oracle.attention_bwd(cat(q, qo), cat(k, ko), cat(v, ko), cat(do, qo), qo2, ko2, *args)
+    np.testing.assert_array_equal(g2[0], cat(g[0], qo))
+    np.testing.assert_array_equal(g2[1], cat(g[1], ko))
+    np.testing.assert_array_equal(g2[2], cat(g[2], ko))
+
+
+@pytest.mark.parametrize("activation", ["softmax", "silu"])
+def test_linear_in_v(activation):
+    q, k, v, _, qo, ko = _draw([5, 3], [4, 6], 2, 3, seed=10)
+    v2 = np.random.default_rng(1).standard_normal(v.shape)
+    f = lambda vv: oracle.attention_fwd(q, k, vv, qo, ko, 0.5, activation, False)[0]  # noqa: E731
+    np.testing.assert_allclose(f(2.0 * v - 3.0 * v2), 2.0 * f(v) - 3.0 * f(v2), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_gradient_sums(causal):
+    qlen, klen = [5, 7, 3], [5, 7, 3]
+    q, k, v, do, qo, ko = _draw(qlen, klen, 2, 4, seed=12)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, qo, ko, 0.6, "softmax", causal)
+    for b in range(3):
+        np.testing.assert_allclose(dk[ko[b]:ko[b + 1]].sum(axis=0), 0.0, atol=1e-12)
+        np.testing.assert_allclose(dv[ko[b]:ko[b + 1]].sum(axis=0), do[qo[b]:qo[b + 1]].sum(axis=0), atol=1e-12)
+
+
+def test_silu_closed_forms():
+    q, k, v, _, qo, ko = _draw([4, 2], [4, 2], 2, 3, seed=13)
+    for zero in ("q", "k"):
+        qq = np.zeros_like(q) if zero == "q" else q
+        kk = np.zeros_like(k) if zero == "k" else k
+        out, _ = oracle.attention_fwd(qq, kk, v, qo, ko, 1.0, "silu", True)
+        assert np.all(out == 0.0)
+    q, k, v, _, qo, ko = _draw([3, 5], [1, 1], 2, 3, seed=14)
+    s = 0.4
+    out, _ = oracle.attention_fwd(q, k, v, qo, ko, s, "silu", False)
+    for b in range(2):
+        x = s * np.einsum("thd,hd->th", q[qo[b]:qo[b + 1]], k[b])
+        silu = x / (1 + np.exp(-x))
+        np.testing.assert_allclose(out[qo[b]:qo[b + 1]], silu[:, :, None] * v[b][None], atol=1e-14)
+
+
+def test_empty_sequences():
+    q, k, v, do, qo, ko = _draw([3, 0, 2], [0, 4, 5], 2, 3, seed=15)
+    out, lse = oracle.attention_fwd(q, k, v, qo, ko, 1.0, "softmax", False)
+    assert np.all(out[0:3] == 0) and np.all(np.isneginf(lse[:, 0:3]))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, qo, ko, 1.0, "softmax", False)
+    assert np.all(dq[0:3] == 0)
+    assert np.all(dk[0:4] == 0) and np.all(dv[0:4] == 0)      # keys nobody reads
+
+
+# ---------------------------------------------------------------- finite differences
+
+@pytest.mark.parametrize("activation", ["softmax", "silu"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradients_by_central_differences(activation, causal):
+    qlen, klen = [3, 4], [5, 2]
+    q, k, v, do, qo, ko = _draw(qlen, klen, 2, 3, seed=16)
+    s = 0.8
+    loss = lambda qq, kk, vv: float((oracle.attention_fwd(qq, kk, vv, qo, ko, s, activation, causal)[0] * do).sum())  # noqa: E731
+    grads = oracle.attention_bwd(q, k, v, do, qo, ko, s, activation, causal)
+    h = 1e-6
+    for which, g in zip(range(3), grads):
+        base = [q, k, v]
+        num = np.zeros_like(g)
+        it = np.nditer(base[which], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        err = np.linalg.norm(num - g) / max(np.linalg.norm(g), 1e-30)
+        assert err <= 1e-6, (which, err)
