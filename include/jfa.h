@@ -1,0 +1,142 @@
+/*
+ * jfa.h -- C ABI of libjfa.so: jagged (variable-length) multi-head attention,
+ * forward and backward, on one AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Jagged Flash Attention as described on the web page
+ * piletech.kr/articles/112134 (Meta's GEM ads-model training efficiency
+ * write-up), section 상세 정리 (Detailed notes):
+ *   - jagged-input item: every sequence of a batch has its own length;
+ *     attention runs per sequence with no padding, for self attention and for
+ *     cross attention with different query and key lengths;
+ *   - Jagged Flash Attention item: exact attention computed directly on the
+ *     packed variable-length tensors, masking by subtraction instead of a
+ *     -inf fill, and a backward pass whose parallel split has no atomics;
+ *   - GDPA item: a non-softmax activation in place of softmax.  This library
+ *     implements it as silu(scale * q.k) / L_kv, L_kv being the sequence's key
+ *     count (also under causal masking).
+ * For one sequence b and head h, with S = scale * Q K^T over its Lq queries
+ * and Lk keys, and query i seeing key j iff j < Lk and (not causal or
+ * j <= i + Lk - Lq):
+ *   softmax: out_i = sum_j P_ij V_j, P = softmax over the visible keys,
+ *            lse_i = ln sum_j exp(S_ij) over visible j;
+ *            a row with no visible key gives out_i = 0 and lse_i = -inf;
+ *   silu:    out_i = sum_j silu(S_ij) / Lk * V_j over visible j.
+ * The backward returns the gradients of sum(out * dout) w.r.t. q, k and v.
+ *
+ * Layout (all row-major, contiguous, device memory owned by the caller):
+ *   q, out, dout, dq : [total_q, heads, head_dim]
+ *   k, v, dk, dv     : [total_kv, heads, head_dim]
+ *   lse              : float [heads, total_q] (natural log)
+ *   q_offsets        : int32 [batch + 1], q_offsets[0] = 0,
+ *                      q_offsets[batch] = total_q, non-decreasing
+ *   kv_offsets       : int32 [batch + 1], likewise with total_kv
+ * Sequence b owns rows q_offsets[b] .. q_offsets[b+1]-1 of q (and of out,
+ * dout, dq) and rows kv_offsets[b] .. kv_offsets[b+1]-1 of k (and v, dk, dv).
+ * Element type: dtype JFA_DTYPE_BF16 (bfloat16) or JFA_DTYPE_FP32 (float) for
+ * q, k, v, out, dout, dq, dk, dv alike.  Arithmetic: bf16 operands with fp32
+ * accumulation (fp32 operands for JFA_DTYPE_FP32); results are rounded to
+ * the element type to nearest even.
+ *
+ * Ownership and side effects.  The library never allocates or frees device
+ * memory: scratch space is the caller's `workspace` (size from
+ * jfa_workspace_size).  Inputs, offsets included, are only read.  Every
+ * (row, head) of out, lse, dq, dk and dv that belongs to a sequence is
+ * written exactly once; nothing else is written, so outputs need no
+ * clearing.  Calls are asynchronous: they enqueue kernels on `stream` and
+ * return; no call synchronises with the host.  The library holds no mutable
+ * global state, so calls from several threads are safe; calls that share a
+ * workspace must be ordered on one stream.
+ *
+ * Errors.  Every function returns a jfa_status.  Arguments are validated on
+ * the host before anything is enqueued:
+ *   JFA_ERR_INVALID_ARGUMENT  a required pointer is NULL; batch < 0;
+ *       heads < 1; a total or max length < 0; a non-finite scale; a bad
+ *       activation, dtype or causal flag; a value pointer not 16-byte
+ *       aligned; total_* * heads * head_dim >= 2^31 elements;
+ *   JFA_ERR_UNSUPPORTED  head_dim not in {32, 64, 128}; heads > 256; a
+ *       maximum length whose tile count exceeds the scheduler's 1023 cost
+ *       classes (max_kv_len > 65472, or max_q_len > 65472 in the backward);
+ *   JFA_ERR_WORKSPACE_TOO_SMALL  workspace_bytes < jfa_workspace_size(...);
+ *   JFA_ERR_HIP  a HIP launch failed; jfa_last_error() has HIP's message.
+ * batch == 0 (or no rows at all) is a successful no-op.  The offsets live in
+ * device memory and are NOT validated: offsets that break the rules above,
+ * or lengths above max_q_len / max_kv_len, are undefined behaviour.
+ */
+#ifndef JFA_H_
+#define JFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum jfa_status {
+  JFA_OK = 0,
+  JFA_ERR_INVALID_ARGUMENT = 1,
+  JFA_ERR_UNSUPPORTED = 2,
+  JFA_ERR_WORKSPACE_TOO_SMALL = 3,
+  JFA_ERR_HIP = 4
+};
+
+enum jfa_activation { JFA_ACT_SOFTMAX = 0, JFA_ACT_SILU = 1 };
+enum jfa_dtype { JFA_DTYPE_BF16 = 0, JFA_DTYPE_FP32 = 1 };
+enum jfa_pass { JFA_PASS_QUERY_TILES = 0, JFA_PASS_KEY_TILES = 1 };
+
+/* Bytes of device workspace jfa_forward (for_backward = 0) or jfa_backward
+ * (for_backward = 1) needs for these sizes.  Never fails; returns 0 for
+ * arguments the calls would reject. */
+size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                          int32_t total_kv, int32_t for_backward);
+
+/* Forward pass (Jagged Flash Attention item; GDPA item for JFA_ACT_SILU).
+ * scale: score scale, typically 1/sqrt(head_dim).  lse may be NULL only for
+ * JFA_ACT_SILU (no log-sum-exp exists there); it is not written for SILU.
+ * Enqueues: the work-list builder, then the attention kernel. */
+int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim,
+                int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale,
+                int32_t activation, int32_t causal, int32_t dtype, void* out, float* lse, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Backward pass (Jagged Flash Attention item: no atomics -- dK/dV are
+ * formed by key-tile-major work items and dQ by query-tile-major ones, each
+ * output row summed in registers and stored once).  out and lse are the
+ * forward's outputs; both may be NULL only for JFA_ACT_SILU.  Results are
+ * bitwise reproducible from run to run. */
+int jfa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
+                 int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
+                 int32_t max_kv_len, float scale, int32_t activation, int32_t causal, int32_t dtype, void* dq,
+                 void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Inspection of the tile scheduler (software tile scheduling for jagged
+ * tensors, GDPA item; persistent-kernel scheduling, JFA item).
+ * jfa_worklist_bytes: size of the buffer jfa_build_worklist writes.
+ * jfa_tile_shape: for a pass, the rows per work-item tile (*tile_rows) and
+ * the rows per inner block whose count is an item's cost (*block_rows).
+ * jfa_build_worklist: enqueues the builder the attention calls use and
+ * writes into `out` (device, >= jfa_worklist_bytes): int32 item count at byte
+ * 0, then from byte 16 int32 pairs (sequence, tile << 8 | head), one per
+ * item, ordered by cost descending then (sequence, head, tile) ascending,
+ * then int32 tile_start[batch + 1].  JFA_PASS_QUERY_TILES is the list of the
+ * forward and dQ kernels, JFA_PASS_KEY_TILES that of the dK/dV kernel. */
+size_t jfa_worklist_bytes(int32_t pass, int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv);
+int jfa_tile_shape(int32_t pass, int32_t* tile_rows, int32_t* block_rows);
+int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
+                       int32_t heads, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
+                       int32_t causal, void* out, size_t out_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* jfa_status_string(int status);
+/* Message of the last JFA_ERR_HIP or argument error on the calling thread. */
+const char* jfa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JFA_H_ */

@@ -1,0 +1,264 @@
+// C ABI of libjfa.so: argument validation, workspace carving and the launch
+// sequence of the forward and backward passes.  See include/jfa.h for the
+// contract.
+#include "jfa.h"
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "jfa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(JFA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct WsLayout {
+  jfa::WorklistLayout wq{}, wkv{};
+  size_t off_wq = 0, off_wkv = 0, off_delta = 0, bytes = 0;
+};
+
+WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv, bool backward) {
+  WsLayout L;
+  L.wq = jfa::worklist_layout(jfa::kPassQ, batch, heads, total_q);
+  L.off_wq = 0;
+  size_t off = L.wq.bytes;
+  if (backward) {
+    L.wkv = jfa::worklist_layout(jfa::kPassKV, batch, heads, total_kv);
+    L.off_wkv = off;
+    off += L.wkv.bytes;
+    L.off_delta = off;
+    off += align256(static_cast<size_t>(heads) * static_cast<size_t>(total_q) * sizeof(float));
+  }
+  L.bytes = off;
+  return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t buckets_for(int32_t max_len, int32_t block) { return (max_len + block - 1) / block + 1; }
+
+// Checks shared by every entry point that takes sizes.
+int check_sizes(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
+                int32_t max_q_len, int32_t max_kv_len) {
+  if (batch < 0) return fail(JFA_ERR_INVALID_ARGUMENT, "batch < 0");
+  if (heads < 1) return fail(JFA_ERR_INVALID_ARGUMENT, "heads < 1");
+  if (total_q < 0 || total_kv < 0) return fail(JFA_ERR_INVALID_ARGUMENT, "negative total length");
+  if (max_q_len < 0 || max_kv_len < 0) return fail(JFA_ERR_INVALID_ARGUMENT, "negative max length");
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(JFA_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+  if (heads > jfa::kMaxHeads) return fail(JFA_ERR_UNSUPPORTED, "heads > 256");
+  const int64_t lim = int64_t(1) << 31;
+  if (int64_t(total_q) * heads * head_dim >= lim || int64_t(total_kv) * heads * head_dim >= lim)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "tensor has 2^31 or more elements");
+  return JFA_OK;
+}
+
+int check_common(const void* q, const void* k, const void* v, const int32_t* qo, const int32_t* ko,
+                 int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
+                 int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation, int32_t causal,
+                 int32_t dtype) {
+  // value pointers may be NULL only when their tensor has no rows
+  if (!qo || !ko) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL offsets pointer");
+  if ((total_q > 0 && !q) || (total_kv > 0 && (!k || !v))) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL input pointer");
+  if (!std::isfinite(scale)) return fail(JFA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (activation != JFA_ACT_SOFTMAX && activation != JFA_ACT_SILU)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "bad activation");
+  if (causal != 0 && causal != 1) return fail(JFA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_FP32) return fail(JFA_ERR_INVALID_ARGUMENT, "bad dtype");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "value pointer not 16-byte aligned");
+  return check_sizes(batch, heads, head_dim, total_q, total_kv, max_q_len, max_kv_len);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* jfa_status_string(int status) {
+  switch (status) {
+    case JFA_OK: return "JFA_OK";
+    case JFA_ERR_INVALID_ARGUMENT: return "JFA_ERR_INVALID_ARGUMENT";
+    case JFA_ERR_UNSUPPORTED: return "JFA_ERR_UNSUPPORTED";
+    case JFA_ERR_WORKSPACE_TOO_SMALL: return "JFA_ERR_WORKSPACE_TOO_SMALL";
+    case JFA_ERR_HIP: return "JFA_ERR_HIP";
+  }
+  return "unknown jfa status";
+}
+
+const char* jfa_last_error(void) { return g_last_error.c_str(); }
+
+size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
+                          int32_t for_backward) {
+  if (check_sizes(batch, heads, head_dim, total_q, total_kv, 0, 0) != JFA_OK) return 0;
+  return ws_layout(batch, heads, total_q, total_kv, for_backward != 0).bytes;
+}
+
+size_t jfa_worklist_bytes(int32_t pass, int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv) {
+  if (pass != JFA_PASS_QUERY_TILES && pass != JFA_PASS_KEY_TILES) return 0;
+  if (check_sizes(batch, heads, 32, total_q, total_kv, 0, 0) != JFA_OK) return 0;
+  return jfa::worklist_layout(pass, batch, heads, pass == JFA_PASS_QUERY_TILES ? total_q : total_kv).bytes;
+}
+
+int jfa_tile_shape(int32_t pass, int32_t* tile_rows, int32_t* block_rows) {
+  if (!tile_rows || !block_rows) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL output pointer");
+  if (pass == JFA_PASS_QUERY_TILES) {
+    *tile_rows = jfa::kFwdBM;
+    *block_rows = jfa::kFwdBN;
+  } else if (pass == JFA_PASS_KEY_TILES) {
+    *tile_rows = jfa::kBwdBN;
+    *block_rows = jfa::kBwdBM;
+  } else {
+    return fail(JFA_ERR_INVALID_ARGUMENT, "bad pass");
+  }
+  return JFA_OK;
+}
+
+int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
+                       int32_t heads, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
+                       int32_t causal, void* out, size_t out_bytes, hipStream_t stream) {
+  if (pass != JFA_PASS_QUERY_TILES && pass != JFA_PASS_KEY_TILES)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "bad pass");
+  if (!q_offsets || !kv_offsets) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL offsets pointer");
+  if (causal != 0 && causal != 1) return fail(JFA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  int st = check_sizes(batch, heads, 32, total_q, total_kv, max_q_len, max_kv_len);
+  if (st != JFA_OK) return st;
+  const int32_t nb = pass == JFA_PASS_QUERY_TILES ? buckets_for(max_kv_len, jfa::kFwdBN)
+                                                  : buckets_for(max_q_len, jfa::kBwdBM);
+  if (nb > jfa::kMaxBuckets) return fail(JFA_ERR_UNSUPPORTED, "maximum length exceeds the scheduler's range");
+  const jfa::WorklistLayout lay =
+      jfa::worklist_layout(pass, batch, heads, pass == JFA_PASS_QUERY_TILES ? total_q : total_kv);
+  if (batch == 0) return JFA_OK;
+  if (!out) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL output pointer");
+  if (out_bytes < lay.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "worklist buffer too small");
+  hipError_t e = jfa::launch_sched(pass, q_offsets, kv_offsets, batch, heads, causal, nb, out, lay, stream);
+  if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+  return JFA_OK;
+}
+
+int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
+                int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
+                int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation, int32_t causal,
+                int32_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  int st = check_common(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
+                        max_kv_len, scale, activation, causal, dtype);
+  if (st != JFA_OK) return st;
+  if (total_q > 0 && !out) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL out");
+  if (!aligned16(out)) return fail(JFA_ERR_INVALID_ARGUMENT, "out not 16-byte aligned");
+  if (activation == JFA_ACT_SOFTMAX && total_q > 0 && !lse)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "NULL lse for softmax");
+  const int32_t nb = buckets_for(max_kv_len, jfa::kFwdBN);
+  if (nb > jfa::kMaxBuckets) return fail(JFA_ERR_UNSUPPORTED, "max_kv_len exceeds the scheduler's range");
+  if (batch == 0 || total_q == 0) return JFA_OK;   // nothing to write
+  const WsLayout L = ws_layout(batch, heads, total_q, total_kv, false);
+  if (!workspace || workspace_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nb, ws + L.off_wq,
+                                   L.wq, stream);
+  if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+  jfa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.qo = q_offsets;
+  a.ko = kv_offsets;
+  a.items = reinterpret_cast<const int2*>(ws + L.off_wq + L.wq.items_off);
+  a.n_items = reinterpret_cast<const int32_t*>(ws + L.off_wq);
+  a.out = out;
+  a.lse = lse;
+  a.heads = heads;
+  a.total_q = total_q;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  e = jfa::launch_fwd(a, head_dim, dtype, activation, L.wq.capacity, stream);
+  if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
+  return JFA_OK;
+}
+
+int jfa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch, int32_t heads,
+                 int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
+                 float scale, int32_t activation, int32_t causal, int32_t dtype, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
+                        max_kv_len, scale, activation, causal, dtype);
+  if (st != JFA_OK) return st;
+  if ((total_q > 0 && (!dout || !dq)) || (total_kv > 0 && (!dk || !dv)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "NULL gradient pointer");
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "gradient pointer not 16-byte aligned");
+  if (activation == JFA_ACT_SOFTMAX) {
+    if (total_q > 0 && (!out || !lse)) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL out or lse for softmax");
+    if (!aligned16(out)) return fail(JFA_ERR_INVALID_ARGUMENT, "out not 16-byte aligned");
+  }
+  const int32_t nbq = buckets_for(max_kv_len, jfa::kFwdBN);
+  const int32_t nbk = buckets_for(max_q_len, jfa::kBwdBM);
+  if (nbq > jfa::kMaxBuckets || nbk > jfa::kMaxBuckets)
+    return fail(JFA_ERR_UNSUPPORTED, "maximum length exceeds the scheduler's range");
+  if (batch == 0 || (total_q == 0 && total_kv == 0)) return JFA_OK;   // nothing to write
+  const WsLayout L = ws_layout(batch, heads, total_q, total_kv, true);
+  if (!workspace || workspace_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e;
+  jfa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.qo = q_offsets;
+  a.ko = kv_offsets;
+  a.items_q = reinterpret_cast<const int2*>(ws + L.off_wq + L.wq.items_off);
+  a.n_items_q = reinterpret_cast<const int32_t*>(ws + L.off_wq);
+  a.items_kv = reinterpret_cast<const int2*>(ws + L.off_wkv + L.wkv.items_off);
+  a.n_items_kv = reinterpret_cast<const int32_t*>(ws + L.off_wkv);
+  a.delta = reinterpret_cast<float*>(ws + L.off_delta);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.heads = heads;
+  a.total_q = total_q;
+  a.total_kv = total_kv;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  if (total_q > 0) {
+    e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq, stream);
+    if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+    if (activation == JFA_ACT_SOFTMAX) {
+      e = jfa::launch_bwd_pre(a, head_dim, dtype, stream);
+      if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+    }
+  }
+  if (total_kv > 0) {
+    e = jfa::launch_sched(jfa::kPassKV, q_offsets, kv_offsets, batch, heads, causal, nbk, ws + L.off_wkv, L.wkv,
+                          stream);
+    if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+    e = jfa::launch_bwd_dkdv(a, head_dim, dtype, activation, L.wkv.capacity, stream);
+    if (e != hipSuccess) return hip_fail(e, "dK/dV kernel launch");
+  }
+  if (total_q > 0) {
+    e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, L.wq.capacity, stream);
+    if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
+  }
+  return JFA_OK;
+}
+
+}  // extern "C"

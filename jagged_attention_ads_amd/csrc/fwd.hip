@@ -1,0 +1,211 @@
+// Jagged attention forward (softmax and GDPA/SiLU) for gfx950.
+//
+// Method: piletech.kr/articles/112134, section 상세 정리 (Detailed notes) --
+// Jagged Flash Attention item (attention computed directly on the packed
+// variable-length tensors, masking by subtraction instead of a -inf fill)
+// and GDPA item (a non-softmax activation; here silu(s*q.k)/L_kv).
+//
+// One workgroup (4 waves) per work item = (sequence, head, 128-query tile),
+// taken from the longest-first list the scheduler built.  Each wave owns 32
+// query rows and keeps them in registers as the B operand of S^T = K Q^T, so
+// that every lane ends up owning one query row (its column of S^T): the
+// online-softmax statistics are per-lane scalars, reduced with a single
+// permlane32 swap.  K and V tiles of 64 keys are staged in LDS
+// (double-buffered through registers); V^T fragments come straight from the
+// row-major V tile through ds_read_b64_tr_b16.  Ragged tails and the causal
+// diagonal are masked arithmetically, only on the tiles that need it.
+#include "jfa_common.hpp"
+#include "jfa_internal.h"
+
+namespace jfa {
+
+template <typename T, int D>
+struct FwdCfg {
+  static constexpr int BM = kFwdBM, BN = kFwdBN, NT = 256;
+  static constexpr int ES = sizeof(T);
+  static constexpr int KS = D * ES + 16;   // K tile row stride in bytes
+  static constexpr int VS = D * ES + 32;   // V tile row stride in bytes
+  static constexpr int KT = BN * KS, VT = BN * VS;
+  static constexpr int STAGE = KT + VT;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int ND = D / 32;        // 32-wide d blocks of O^T
+  static constexpr int NK = D / 16;        // k-steps of S^T
+};
+
+template <typename T, int D, int ACT>
+__global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd_kernel(FwdArgs a) {
+  using C = FwdCfg<T, D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+  if ((int)blockIdx.x >= *a.n_items) return;
+  int b, h, t;
+  unpack_item(a.items[blockIdx.x], b, h, t);
+  const int qs = a.qo[b], lq = a.qo[b + 1] - qs;
+  const int ks = a.ko[b], lk = a.ko[b + 1] - ks;
+  const int off = lk - lq;   // causal: query i sees keys j <= i + off
+
+  const int tid = threadIdx.x, l = lane_id(), w = tid >> 6, g = l >> 5, c32 = l & 31;
+  const int row0 = t * C::BM + 32 * w;   // first query row of this wave
+  const int my_row = row0 + c32;         // the query row this lane owns
+  const bool wave_live = row0 < lq;
+  const int n_kv = q_tile_kv_blocks(lq, lk, t, C::BM, C::BN, a.causal);
+  const size_t rs = (size_t)a.heads * D;  // elements between consecutive tokens
+
+  const T* kb = static_cast<const T*>(a.k) + (size_t)ks * rs + (size_t)h * D;
+  const T* vb = static_cast<const T*>(a.v) + (size_t)ks * rs + (size_t)h * D;
+
+  frag_t<T> qf[C::NK];
+  {
+    const int r = min(my_row, lq - 1);
+    const T* qp = static_cast<const T*>(a.q) + (size_t)(qs + r) * rs + (size_t)h * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) qf[kk] = global_frag<T>(qp + 16 * kk);
+  }
+
+  f32x16 o[C::ND];
+#pragma unroll
+  for (int i = 0; i < C::ND; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
+
+  TileStage<T, D, C::BN, C::KS, true> kst;   // K rows stored swap23-permuted
+  TileStage<T, D, C::BN, C::VS, false> vst;
+  auto gload = [&](int kvt) {
+    kst.load(kb, rs, kvt * C::BN, lk, tid);
+    vst.load(vb, rs, kvt * C::BN, lk, tid);
+  };
+  auto lstore = [&](int buf) {
+    char* kt = smem + buf * C::STAGE;
+    kst.store(kt, tid);
+    vst.store(kt + C::KT, tid);
+  };
+
+  if (n_kv > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_kv; ++it) {
+    if (it + 1 < n_kv) gload(it + 1);
+    const int kv0 = it * C::BN;
+    const char* kt = smem + (it & 1) * C::STAGE;
+    const char* vt = kt + C::KT;
+    const bool active = wave_live && (!a.causal || kv0 <= row0 + 31 + off);
+    if (active) {
+      // S^T (64 keys x 32 queries) = K Q^T, as two 32-key tiles
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < C::NK; ++kk) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const frag_t<T> kf = lds_row_frag<T>(kt + (32 * mt + c32) * C::KS + (16 * kk + 8 * g) * C::ES);
+          mma(s[mt], kf, qf[kk]);
+        }
+      }
+      const bool need_mask = (kv0 + C::BN > lk) || (a.causal && kv0 + C::BN - 1 > row0 + off);
+      // register r of tile mt holds key kv0 + 32*mt + 16*(r/8) + 8*g + r%8
+      if constexpr (ACT == 0) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = s[mt][r] * a.scale_log2;
+            if (need_mask) {
+              const int j = kv0 + 32 * mt + 16 * (r >> 3) + 8 * g + (r & 7);
+              const bool masked = (j >= lk) || (a.causal && j > my_row + off);
+              x -= masked ? kMaskShift : 0.f;
+            }
+            s[mt][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+        mx = xor32_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::ND; ++i) o[i] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(s[mt][r] - m_new);
+            l_run += p;
+            s[mt][r] = p;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float raw = s[mt][r];
+            const float sig = fast_rcp(1.0f + fast_exp2(-raw * a.scale_log2));
+            float y = raw * a.scale * sig * inv_lk;
+            if (need_mask) {
+              const int j = kv0 + 32 * mt + 16 * (r >> 3) + 8 * g + (r & 7);
+              const bool masked = (j >= lk) || (a.causal && j > my_row + off);
+              y = masked ? 0.f : y;
+            }
+            s[mt][r] = y;
+          }
+        }
+      }
+      // O^T (D x 32 queries) += V^T P^T; k-step (mt, ss) covers keys kv0 + 32*mt + 16*ss + 0..15
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+          const frag_t<T> pf = pack_frag<T>(s[mt], ss);
+#pragma unroll
+          for (int dt = 0; dt < C::ND; ++dt) {
+            const frag_t<T> vf = lds_col_frag<T, C::VS, false>(vt, 32 * mt + 16 * ss, 32 * dt);
+            mma(o[dt], vf, pf);
+          }
+        }
+      }
+    }
+    if (it + 1 < n_kv) lstore((it + 1) & 1);
+    __syncthreads();
+  }
+
+  if (!wave_live) return;
+  const float l_tot = ACT == 0 ? xor32_sum(l_run) : 1.f;
+  if (my_row >= lq) return;
+  const bool row_live = lk > 0 && (!a.causal || my_row + off >= 0);
+  float f = 0.f;
+  if (row_live) f = ACT == 0 ? 1.0f / l_tot : 1.0f;
+  T* op = static_cast<T*>(a.out) + (size_t)(qs + my_row) * rs + (size_t)h * D;
+  store_row<T, C::ND>(op, o, f);
+  if (ACT == 0 && g == 0) {
+    a.lse[(size_t)h * a.total_q + qs + my_row] = row_live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename T, int D, int ACT>
+static hipError_t launch_one(const FwdArgs& a, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_kernel<T, D, ACT>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int ACT>
+static hipError_t launch_d(const FwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
+  switch (head_dim) {
+    case 32: return launch_one<T, 32, ACT>(a, grid, stream);
+    case 64: return launch_one<T, 64, ACT>(a, grid, stream);
+    case 128: return launch_one<T, 128, ACT>(a, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (dtype == 0) return act == 0 ? launch_d<__bf16, 0>(a, head_dim, grid, stream)
+                                  : launch_d<__bf16, 1>(a, head_dim, grid, stream);
+  return act == 0 ? launch_d<float, 0>(a, head_dim, grid, stream) : launch_d<float, 1>(a, head_dim, grid, stream);
+}
+
+}  // namespace jfa

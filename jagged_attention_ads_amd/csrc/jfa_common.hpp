@@ -1,0 +1,278 @@
+// Shared device helpers of the jagged attention kernels (gfx950 / CDNA4).
+//
+// Register layouts used throughout (v_mfma_f32_32x32x16_bf16, checked on the
+// hardware; the fp32 path runs eight v_mfma_f32_32x32x2_f32 over the same
+// fragment layout):
+//   A operand (32 x 16):  lane l holds row l%32, k-slots 8*(l/32) + 0..7
+//   B operand (16 x 32):  lane l holds column l%32, k-slots 8*(l/32) + 0..7
+//   C/D (32 x 32, f32x16): lane l, register r holds
+//                          row 8*(r/4) + 4*(l/32) + r%4, column l%32
+// A "fragment" is the 8 k-slot values one lane contributes to an A or B
+// operand.  Any permutation of k applied to both operands leaves a product
+// unchanged; the kernels use that freedom so that an accumulator tile can be
+// fed straight back as the B operand of the next product (see swap23 below).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Masked scores are pushed down by this finite amount instead of being
+// replaced by -inf: exp2 of (score - kMaskShift - rowmax) is exactly 0 in
+// fp32 for any finite score, and no inf/NaN ever enters the running max.
+constexpr float kMaskShift = 1.0e30f;
+
+constexpr int kWave = 64;
+
+#define JFA_LDS __attribute__((address_space(3)))
+
+template <typename T> struct Frag;
+template <> struct Frag<__bf16> { using type = bf16x8; };
+template <> struct Frag<float> { using type = f32x8; };
+template <typename T> using frag_t = typename Frag<T>::type;
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Rows of a 32-row tile are stored (and produced) in an order whose bits 2
+// and 3 are swapped.  With that order, accumulator register 8*s + e of lane
+// group g = l/32 in a 32 x 32 C tile sits at logical row 16*s + 8*g + e, i.e.
+// the 8 consecutive k-slots of a B-operand fragment.
+__device__ __forceinline__ int swap23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ void mma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ bf16x8 to_frag_bf16(const float* x) {
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (__bf16)x[e];
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ frag_t<T> pack_frag(const f32x16& acc, int s) {
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = acc[8 * s + e];
+  if constexpr (sizeof(T) == 2) {
+    return to_frag_bf16(x);
+  } else {
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = x[e];
+    return f;
+  }
+}
+
+// ---------------------------------------------------------------- LDS access
+
+// 8 consecutive elements of one LDS row.
+template <typename T>
+__device__ __forceinline__ frag_t<T> lds_row_frag(const char* p) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  } else {
+    // rows are only 16-byte aligned: two 16-byte reads
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = __uint_as_float(a[e]);
+      f[4 + e] = __uint_as_float(b[e]);
+    }
+    return f;
+  }
+}
+
+// Transposed fragment of a row-major LDS tile: lane l gets the elements at
+// logical rows row0 + 8*(l/32) + 0..7 of column col0 + l%32.  `rowmap`
+// maps a logical row to its stored row; it must keep aligned groups of four
+// rows together (swap23 and the identity do).
+template <typename T, int STRIDE, bool SWAPPED>
+__device__ __forceinline__ frag_t<T> lds_col_frag(const char* tile, int row0, int col0) {
+  const int l = lane_id();
+  if constexpr (sizeof(T) == 2) {
+    // ds_read_b64_tr_b16 (layout checked on the hardware): within each
+    // 16-lane block, source lane s addresses the 4 elements at row r0 + s/4,
+    // columns c0 + 4*(s%4) .. +3; output lane o receives column c0 + o at
+    // rows r0 .. r0+3.  Two reads give the 8 rows of a fragment.
+    const int blk = l >> 4, s = l & 15;
+    const int g = blk >> 1, half = blk & 1;
+    const int col = col0 + 16 * half + 4 * (s & 3);
+    bf16x8 f;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      int row = row0 + 8 * g + 4 * rd + (s >> 2);
+      if (SWAPPED) row = swap23(row);
+      const char* p = tile + row * STRIDE + col * 2;
+      i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JFA_LDS i16x4*)(p));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[4 * rd + e] = __builtin_bit_cast(__bf16, t[e]);
+    }
+    return f;
+  } else {
+    const int g = l >> 5, c = col0 + (l & 31);
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int row = row0 + 8 * g + e;
+      if (SWAPPED) row = swap23(row);
+      f[e] = *reinterpret_cast<const float*>(tile + row * STRIDE + c * 4);
+    }
+    return f;
+  }
+}
+
+// ---------------------------------------------------------------- cross-lane
+
+__device__ __forceinline__ float xor32_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xor32_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ---------------------------------------------------------------- tile staging
+
+// A ROWS x D tile of one head, read from global memory into registers (16
+// bytes per access, rows clamped into the sequence so nothing outside it is
+// ever read) and written to a row-major LDS tile of STRIDE bytes per row.
+// With SWAP, row r is stored at row swap23(r).
+template <typename T, int D, int ROWS, int STRIDE, bool SWAP, int NT = 256>
+struct TileStage {
+  static constexpr int CH = D * (int)sizeof(T) / 16;
+  static constexpr int N = ROWS * CH / NT;
+  static_assert(ROWS * CH % NT == 0, "tile must split evenly over the threads");
+  u32x4 r[N];
+
+  // rows row0 .. row0+ROWS-1 of a sequence of `nrows` rows (nrows >= 1)
+  __device__ __forceinline__ void load(const T* base, size_t row_stride, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + i * NT, row = c / CH, col = c % CH;
+      const int j = min(row0 + row, nrows - 1);
+      r[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base + (size_t)j * row_stride) + col * 16);
+    }
+  }
+  __device__ __forceinline__ void store(char* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + i * NT, row = c / CH, col = c % CH;
+      const int rr = SWAP ? swap23(row) : row;
+      *reinterpret_cast<u32x4*>(tile + rr * STRIDE + col * 16) = r[i];
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ frag_t<T> global_frag(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  } else {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 4);
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = __uint_as_float(a[e]);
+      f[4 + e] = __uint_as_float(b[e]);
+    }
+    return f;
+  }
+}
+
+// Store 4 consecutive output elements (rounded to nearest even for bf16).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float x0, float x1, float x2, float x3) {
+  if constexpr (sizeof(T) == 2) {
+    u32x2 u;
+    u[0] = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x0) |
+           ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x1) << 16);
+    u[1] = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x2) |
+           ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x3) << 16);
+    *reinterpret_cast<u32x2*>(p) = u;
+  } else {
+    f32x4 f = {x0, x1, x2, x3};
+    *reinterpret_cast<f32x4*>(p) = f;
+  }
+}
+
+// Write a D x 32 accumulator block set (ND blocks of 32 x 32, lane = column)
+// as the lane's row of a [rows, heads, D] tensor, times f.
+template <typename T, int ND>
+__device__ __forceinline__ void store_row(T* row, const f32x16* acc, float f) {
+  const int g = lane_id() >> 5;
+  // register r of block dt holds element d = 32*dt + 8*(r/4) + 4*g + r%4
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      store4<T>(row + 32 * dt + 8 * q4 + 4 * g, acc[dt][4 * q4] * f, acc[dt][4 * q4 + 1] * f,
+                acc[dt][4 * q4 + 2] * f, acc[dt][4 * q4 + 3] * f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- work items
+
+// Item packing: x = sequence index, y = (tile << 8) | head.
+__device__ __forceinline__ void unpack_item(int2 it, int& b, int& h, int& t) {
+  b = it.x;
+  h = it.y & 255;
+  t = it.y >> 8;
+}
+
+// Number of `bn`-key blocks a `bm`-query tile visits (forward and dQ).
+__device__ __forceinline__ int q_tile_kv_blocks(int lq, int lk, int t, int bm, int bn, int causal) {
+  int last_row = min((t + 1) * bm, lq) - 1;
+  int kv_end = lk;
+  if (causal) kv_end = min(lk, max(0, last_row + lk - lq + 1));
+  return ceil_div(kv_end, bn);
+}
+
+// Number of `bm`-query blocks a `bn`-key tile visits (dK/dV), and the first.
+__device__ __forceinline__ int kv_tile_first_q_block(int lq, int lk, int t, int bm, int bn, int causal) {
+  if (!causal) return 0;
+  int first_row = max(0, t * bn - (lk - lq));
+  return first_row / bm;
+}
+__device__ __forceinline__ int kv_tile_q_blocks(int lq, int lk, int t, int bm, int bn, int causal) {
+  int nqb = ceil_div(lq, bm);
+  if (!causal) return nqb;
+  int first_row = max(0, t * bn - (lk - lq));
+  return first_row < lq ? nqb - first_row / bm : 0;
+}
+
+}  // namespace jfa

@@ -1,0 +1,83 @@
+// Internal interfaces between the C-ABI layer (api.cpp) and the kernel
+// translation units.  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace jfa {
+
+// Tile geometry, shared by the launchers and the host-side sizing code.
+constexpr int kFwdBM = 128;     // query rows per forward / dQ work item
+constexpr int kFwdBN = 64;      // key rows per forward / dQ inner step
+constexpr int kBwdBN = 128;     // key rows per dK/dV work item
+constexpr int kBwdBM = 64;      // query rows per dK/dV inner step
+constexpr int kMaxBuckets = 1024;   // distinct tile costs the scheduler can sort
+constexpr int kMaxHeads = 256;      // head index is packed into 8 bits
+
+enum Pass { kPassQ = 0, kPassKV = 1 };
+
+// Device layout of a work list (all offsets in bytes from its base):
+//   0              int32 item count
+//   16             int2  items[capacity]   (x = sequence, y = tile << 8 | head)
+//   16 + 8*cap     int32 tile_start[batch + 1]
+struct WorklistLayout {
+  int64_t capacity;
+  size_t items_off, tile_start_off, bytes;
+};
+WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t total_rows);
+
+hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
+                        int32_t causal, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
+                        hipStream_t stream);
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* qo;
+  const int32_t* ko;
+  const int2* items;
+  const int32_t* n_items;
+  void* out;
+  float* lse;
+  int32_t heads;
+  int32_t total_q;
+  int32_t causal;
+  float scale;        // softmax / silu score scale
+  float scale_log2;   // scale * log2(e)
+};
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  const int32_t* qo;
+  const int32_t* ko;
+  const int2* items_q;     // query-tile list (dQ pass)
+  const int32_t* n_items_q;
+  const int2* items_kv;    // key-tile list (dK/dV pass)
+  const int32_t* n_items_kv;
+  float* delta;            // [heads, total_q] workspace
+  void* dq;
+  void* dk;
+  void* dv;
+  int32_t heads;
+  int32_t total_q;
+  int32_t total_kv;
+  int32_t causal;
+  float scale;
+  float scale_log2;
+};
+
+hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
+
+}  // namespace jfa

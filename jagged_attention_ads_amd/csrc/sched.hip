@@ -1,0 +1,227 @@
+// Device-side work-list builder: the software tile scheduler for jagged
+// tensors (piletech.kr/articles/112134, section 상세 정리 / Detailed notes,
+// items on Jagged Flash Attention -- persistent-kernel scheduling -- and on
+// GDPA -- software tile scheduling for jagged tensors).
+//
+// From the offsets alone it enumerates every work item (sequence b, head h,
+// tile t), prices it by the number of inner blocks the attention kernel will
+// visit for it, and writes the items longest first (cost descending), ties
+// in (b, h, t) order -- a stable counting sort by cost.  One workgroup of
+// 1024 threads does it all on the device, so the caller's stream never waits
+// for the host.
+#include "jfa_common.hpp"
+#include "jfa_internal.h"
+
+namespace jfa {
+
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedWaves = kSchedThreads / kWave;
+
+// Exclusive block scan of one value per thread.  `tmp` holds kSchedWaves ints.
+__device__ int block_excl_scan(int v, int* tmp, int& total) {
+  const int l = lane_id(), w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int y = __shfl_up(x, off, kWave);
+    if (l >= off) x += y;
+  }
+  if (l == kWave - 1) tmp[w] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kSchedWaves; ++i) {
+    int s = tmp[i];
+    before += (i < w) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return before + x - v;
+}
+
+// Last sequence b in [0, B) with tile_start[b] <= u.
+__device__ int find_seq(const int* ts, int B, int u) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (ts[mid] <= u) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <int PASS>
+struct TileRule {
+  // Tiles split the query side (PASS == kPassQ) or the key side.
+  static constexpr int kTile = PASS == kPassQ ? kFwdBM : kBwdBN;
+  __device__ static int rows(int lq, int lk) { return PASS == kPassQ ? lq : lk; }
+  __device__ static int cost(int lq, int lk, int t, int causal) {
+    if (PASS == kPassQ) return q_tile_kv_blocks(lq, lk, t, kFwdBM, kFwdBN, causal);
+    return kv_tile_q_blocks(lq, lk, t, kBwdBM, kBwdBN, causal);
+  }
+  // Costs are monotone in t within a sequence: non-decreasing for query
+  // tiles (later rows see more keys), non-increasing for key tiles (later
+  // keys are seen by fewer rows).  before_or_eq(x, c): a tile of cost x may
+  // come before (or is in) the run of cost c; after_or_eq: after or in it.
+  __device__ static bool before_or_eq(int x, int c) { return PASS == kPassQ ? x <= c : x >= c; }
+  __device__ static bool after_or_eq(int x, int c) { return PASS == kPassQ ? x >= c : x <= c; }
+};
+
+template <int PASS>
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restrict__ qo, const int* __restrict__ ko,
+                                                              int B, int H, int causal, int nbuckets,
+                                                              int64_t capacity, int* __restrict__ count,
+                                                              int2* __restrict__ items, int* __restrict__ tile_start) {
+  using R = TileRule<PASS>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int* hist = reinterpret_cast<int*>(smem);
+  int* start = hist + nbuckets;
+  int* carry = start + nbuckets;
+  int* tmp = carry + nbuckets;                       // kSchedWaves ints (+pad)
+  unsigned short* chunk_tot = reinterpret_cast<unsigned short*>(tmp + 32);
+  unsigned short* wave_cnt = chunk_tot + nbuckets;   // [kSchedWaves][nbuckets]
+
+  const int tid = threadIdx.x, l = lane_id(), w = tid / kWave;
+
+  // 1. tiles per sequence -> exclusive prefix tile_start[b]
+  int run = 0;
+  for (int base = 0; base < B; base += kSchedThreads) {
+    const int b = base + tid;
+    int n = 0;
+    if (b < B) n = ceil_div(R::rows(qo[b + 1] - qo[b], ko[b + 1] - ko[b]), R::kTile);
+    int tot;
+    const int ex = block_excl_scan(n, tmp, tot);
+    if (b < B) tile_start[b] = run + ex;
+    run += tot;
+  }
+  const int total_tiles = run;
+  if (tid == 0) tile_start[B] = total_tiles;
+  for (int c = tid; c < nbuckets; c += kSchedThreads) {
+    hist[c] = 0;
+    carry[c] = 0;
+  }
+  __syncthreads();
+
+  // 2. histogram of tile costs
+  for (int u = tid; u < total_tiles; u += kSchedThreads) {
+    const int b = find_seq(tile_start, B, u);
+    const int t = u - tile_start[b];
+    const int c = min(R::cost(qo[b + 1] - qo[b], ko[b + 1] - ko[b], t, causal), nbuckets - 1);
+    atomicAdd(&hist[c], 1);
+  }
+  __syncthreads();
+
+  // 3. first output slot of each cost bucket, largest cost first
+  run = 0;
+  for (int base = 0; base < nbuckets; base += kSchedThreads) {
+    const int o = base + tid;
+    const int c = nbuckets - 1 - o;
+    const int n = (o < nbuckets) ? hist[c] : 0;
+    int tot;
+    const int ex = block_excl_scan(n, tmp, tot);
+    if (o < nbuckets) start[c] = H * (run + ex);
+    run += tot;
+  }
+  __syncthreads();
+
+  // 4. stable rank of each tile among the tiles of equal cost, then its H items
+  for (int base = 0; base < total_tiles; base += kSchedThreads) {
+    for (int i = tid; i < kSchedWaves * nbuckets; i += kSchedThreads) wave_cnt[i] = 0;
+    __syncthreads();
+    const int u = base + tid;
+    const bool valid = u < total_tiles;
+    int b = 0, t = 0, c = -1, lq = 0, lk = 0;
+    if (valid) {
+      b = find_seq(tile_start, B, u);
+      t = u - tile_start[b];
+      lq = qo[b + 1] - qo[b];
+      lk = ko[b + 1] - ko[b];
+      c = min(R::cost(lq, lk, t, causal), nbuckets - 1);
+    }
+    // rank inside the wave: one ballot per distinct cost present
+    unsigned long long pending = __ballot(valid);
+    int local = 0;
+    while (pending) {
+      const int leader = __ffsll((unsigned long long)pending) - 1;
+      const int lc = __shfl(c, leader, kWave);
+      const unsigned long long m = __ballot(c == lc);
+      if (c == lc) local = __popcll(m & ((1ull << l) - 1ull));
+      if (l == leader) wave_cnt[w * nbuckets + lc] = (unsigned short)__popcll(m);
+      pending &= ~m;
+    }
+    __syncthreads();
+    // rank offset of each wave inside this chunk, per cost
+    for (int cc = tid; cc < nbuckets; cc += kSchedThreads) {
+      int r = 0;
+      for (int ww = 0; ww < kSchedWaves; ++ww) {
+        const int x = wave_cnt[ww * nbuckets + cc];
+        wave_cnt[ww * nbuckets + cc] = (unsigned short)r;
+        r += x;
+      }
+      chunk_tot[cc] = (unsigned short)r;
+    }
+    __syncthreads();
+    if (valid) {
+      const int rank = carry[c] + wave_cnt[w * nbuckets + c] + local;
+      // the run of tiles of sequence b with this same cost: [first, last]
+      const int ntiles = tile_start[b + 1] - tile_start[b];
+      int lo = 0, hi = t;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (R::after_or_eq(min(R::cost(lq, lk, mid, causal), nbuckets - 1), c)) hi = mid; else lo = mid + 1;
+      }
+      const int first = lo;
+      lo = t;
+      hi = ntiles - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (R::before_or_eq(min(R::cost(lq, lk, mid, causal), nbuckets - 1), c)) lo = mid; else hi = mid - 1;
+      }
+      const int len = lo - first + 1;
+      const int k = t - first;
+      // items of bucket c are ordered (b, h, t): all earlier sequences' tiles
+      // of this cost (rank - k of them) times H, then h runs of length len
+      const int p0 = start[c] + H * (rank - k) + k;
+      for (int hh = 0; hh < H; ++hh) {
+        const int64_t p = (int64_t)p0 + (int64_t)hh * len;
+        if (p >= 0 && p < capacity) items[p] = make_int2(b, (t << 8) | hh);   // true for valid offsets
+      }
+    }
+    __syncthreads();
+    for (int cc = tid; cc < nbuckets; cc += kSchedThreads) carry[cc] += chunk_tot[cc];
+    __syncthreads();
+  }
+  if (tid == 0) *count = H * total_tiles;
+}
+
+WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t total_rows) {
+  const int64_t tile = pass == kPassQ ? kFwdBM : kBwdBN;
+  // sum over sequences of ceil(L_b / tile) <= (total + batch * (tile - 1)) / tile
+  const int64_t tiles = (static_cast<int64_t>(total_rows) + static_cast<int64_t>(batch) * (tile - 1)) / tile;
+  WorklistLayout lay;
+  lay.capacity = tiles * heads;
+  lay.items_off = 16;
+  lay.tile_start_off = lay.items_off + static_cast<size_t>(lay.capacity) * 8;
+  lay.bytes = lay.tile_start_off + (static_cast<size_t>(batch) + 1) * 4;
+  lay.bytes = (lay.bytes + 255) & ~static_cast<size_t>(255);
+  return lay;
+}
+
+hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
+                        int32_t causal, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
+                        hipStream_t stream) {
+  char* base = static_cast<char*>(wl_base);
+  int* count = reinterpret_cast<int*>(base);
+  int2* items = reinterpret_cast<int2*>(base + lay.items_off);
+  int* tile_start = reinterpret_cast<int*>(base + lay.tile_start_off);
+  const size_t lds = static_cast<size_t>(nbuckets) * (3 * 4 + 2 + 2 * kSchedWaves) + 32 * 4;
+  if (pass == kPassQ)
+    hipLaunchKernelGGL(sched_kernel<kPassQ>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
+                       causal, nbuckets, lay.capacity, count, items, tile_start);
+  else
+    hipLaunchKernelGGL(sched_kernel<kPassKV>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
+                       causal, nbuckets, lay.capacity, count, items, tile_start);
+  return hipGetLastError();
+}
+
+}  // namespace jfa

@@ -1,0 +1,211 @@
+"""Thin Python binding of libjfa.so (argument marshalling only).
+
+The functions named like the C entry points (jfa_forward, jfa_backward, ...)
+take torch tensors, check their dtype/device/contiguity, pass raw device
+pointers and the current HIP stream, and raise JfaError on a non-zero
+status.  Every step of the computation runs in the library's HIP kernels;
+torch only provides device memory and the stream.  ``forward`` and
+``backward`` additionally allocate the outputs and the workspace.
+
+There is no fallback: without the built library (see
+``jagged_attention_ads_amd.build``) every call raises.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjfa.so")
+
+JFA_OK = 0
+STATUS_NAMES = {0: "JFA_OK", 1: "JFA_ERR_INVALID_ARGUMENT", 2: "JFA_ERR_UNSUPPORTED",
+                3: "JFA_ERR_WORKSPACE_TOO_SMALL", 4: "JFA_ERR_HIP"}
+ACTIVATIONS = {"softmax": 0, "silu": 1}
+DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+PASS_QUERY_TILES = 0
+PASS_KEY_TILES = 1
+
+EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_worklist_bytes", "jfa_tile_shape",
+            "jfa_build_worklist", "jfa_status_string", "jfa_last_error")
+
+
+class JfaError(RuntimeError):
+    def __init__(self, status, message=""):
+        self.status = status
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, str(status)), message))
+
+
+_lib = None
+
+_i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+
+def lib():
+    """The loaded libjfa.so (loaded on first use; raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libjfa.so is not built at %s; run `python -m jagged_attention_ads_amd.build`"
+                              % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        L.jfa_workspace_size.restype = _sz
+        L.jfa_workspace_size.argtypes = [_i32] * 6
+        L.jfa_forward.restype = ctypes.c_int
+        L.jfa_forward.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_i32] * 7 + [_f32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+        L.jfa_backward.restype = ctypes.c_int
+        L.jfa_backward.argtypes = [_vp] * 8 + [_i32] * 7 + [_f32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.jfa_worklist_bytes.restype = _sz
+        L.jfa_worklist_bytes.argtypes = [_i32] * 5
+        L.jfa_tile_shape.restype = ctypes.c_int
+        L.jfa_tile_shape.argtypes = [_i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
+        L.jfa_build_worklist.restype = ctypes.c_int
+        L.jfa_build_worklist.argtypes = [_i32, _vp, _vp] + [_i32] * 7 + [_vp, _sz, _vp]
+        L.jfa_status_string.restype = ctypes.c_char_p
+        L.jfa_status_string.argtypes = [ctypes.c_int]
+        L.jfa_last_error.restype = ctypes.c_char_p
+        L.jfa_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != JFA_OK:
+        raise JfaError(status, lib().jfa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype not in DTYPES:
+        raise TypeError("values must be bfloat16 or float32, got %s" % t.dtype)
+    return DTYPES[t.dtype]
+
+
+def _values(name, t, dtype):
+    if not t.is_cuda or not t.is_contiguous() or t.dim() != 3 or t.dtype != dtype:
+        raise ValueError("%s must be a contiguous 3-D %s CUDA tensor [rows, heads, head_dim]" % (name, dtype))
+
+
+def _offsets(name, t):
+    if not t.is_cuda or t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous 1-D int32 CUDA tensor" % name)
+
+
+# ---------------------------------------------------------------- C names
+
+def jfa_status_string(status):
+    return lib().jfa_status_string(status).decode()
+
+
+def jfa_workspace_size(batch, heads, head_dim, total_q, total_kv, for_backward):
+    return lib().jfa_workspace_size(batch, heads, head_dim, total_q, total_kv, int(for_backward))
+
+
+def jfa_worklist_bytes(pass_, batch, heads, total_q, total_kv):
+    return lib().jfa_worklist_bytes(pass_, batch, heads, total_q, total_kv)
+
+
+def jfa_tile_shape(pass_):
+    a, b = _i32(), _i32()
+    _check(lib().jfa_tile_shape(pass_, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def jfa_forward(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation, causal, out, lse,
+                workspace):
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _values(name, t, q.dtype)
+    _offsets("q_offsets", q_offsets)
+    _offsets("kv_offsets", kv_offsets)
+    T_q, H, D = q.shape
+    _check(lib().jfa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), q_offsets.numel() - 1,
+                             H, D, T_q, k.shape[0], int(max_q_len), int(max_kv_len), float(scale),
+                             ACTIVATIONS[activation], int(bool(causal)), dt, _ptr(out), _ptr(lse), _ptr(workspace),
+                             workspace.numel() if workspace is not None else 0, _stream()))
+
+
+def jfa_backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation, causal,
+                 dq, dk, dv, workspace):
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _values(name, t, q.dtype)
+    if out is not None:
+        _values("out", out, q.dtype)
+    _offsets("q_offsets", q_offsets)
+    _offsets("kv_offsets", kv_offsets)
+    T_q, H, D = q.shape
+    _check(lib().jfa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(q_offsets),
+                              _ptr(kv_offsets), q_offsets.numel() - 1, H, D, T_q, k.shape[0], int(max_q_len),
+                              int(max_kv_len), float(scale), ACTIVATIONS[activation], int(bool(causal)), dt,
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                              workspace.numel() if workspace is not None else 0, _stream()))
+
+
+def jfa_build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, max_q_len, max_kv_len, causal,
+                       out):
+    _offsets("q_offsets", q_offsets)
+    _offsets("kv_offsets", kv_offsets)
+    _check(lib().jfa_build_worklist(pass_, _ptr(q_offsets), _ptr(kv_offsets), q_offsets.numel() - 1, heads,
+                                    total_q, total_kv, int(max_q_len), int(max_kv_len), int(bool(causal)),
+                                    _ptr(out), out.numel(), _stream()))
+
+
+# ---------------------------------------------------------------- allocating wrappers
+
+def workspace(batch, heads, head_dim, total_q, total_kv, for_backward, device):
+    n = jfa_workspace_size(batch, heads, head_dim, total_q, total_kv, for_backward)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def forward(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale=None, activation="softmax",
+            causal=False, ws=None):
+    """Returns (out, lse); lse is None for silu."""
+    T_q, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, T_q), dtype=torch.float32, device=q.device) if activation == "softmax" else None
+    if ws is None:
+        ws = workspace(q_offsets.numel() - 1, H, D, T_q, k.shape[0], False, q.device)
+    jfa_forward(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation, causal, out, lse, ws)
+    return out, lse
+
+
+def backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_len, scale=None,
+             activation="softmax", causal=False, ws=None):
+    """Returns (dq, dk, dv)."""
+    T_q, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if ws is None:
+        ws = workspace(q_offsets.numel() - 1, H, D, T_q, k.shape[0], True, q.device)
+    jfa_backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation,
+                 causal, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
+def build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, max_q_len, max_kv_len, causal):
+    """Runs the device work-list builder; returns (items int32 [n, 2], tile_start int32 [B+1]) on the host."""
+    B = q_offsets.numel() - 1
+    nbytes = jfa_worklist_bytes(pass_, B, heads, total_q, total_kv)
+    buf = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q_offsets.device)
+    jfa_build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, max_q_len, max_kv_len, causal, buf)
+    host = buf.cpu()
+    words = host.view(torch.int32)
+    count = int(words[0])
+    tile = jfa_tile_shape(pass_)[0]
+    rows = total_q if pass_ == PASS_QUERY_TILES else total_kv
+    cap = ((rows + B * (tile - 1)) // tile) * heads
+    items = words[4:4 + 2 * cap].view(cap, 2)[:count].clone()
+    tile_start = words[4 + 2 * cap:4 + 2 * cap + B + 1].clone()
+    return items, tile_start

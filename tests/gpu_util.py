@@ -1,0 +1,136 @@
+"""Helpers of the GPU tests: move a drawn batch to the device, run the HIP
+path through the C ABI binding, and compare with the CPU oracle."""
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from jagged_attention_ads_amd import jfa
+from jagged_attention_ads_amd.workloads import bf16_bits_to_f64, offsets_from_lengths
+
+FWD_ATOL = 1e-2      # forward max abs error vs the fp64 oracle
+LSE_ATOL = 1e-3      # lse abs error (fp32 kernel value vs fp64)
+GRAD_RTOL = 2e-2     # per-tensor relative L2 error of dq, dk, dv
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def values_to_device(arr, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev())
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev())
+
+
+def to_f64(t):
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.double().cpu().numpy()
+
+
+class Dev:
+    """A batch on the device."""
+
+    def __init__(self, batch):
+        self.b = batch
+        wl = batch.workload
+        self.dtype = wl.dtype
+        self.q = values_to_device(batch.q, wl.dtype)
+        self.k = values_to_device(batch.k, wl.dtype)
+        self.v = values_to_device(batch.v, wl.dtype)
+        self.do = values_to_device(batch.dout, wl.dtype) if batch.dout is not None else None
+        self.qo = torch.from_numpy(batch.q_offsets.astype(np.int32)).to(dev())
+        self.ko = torch.from_numpy(batch.kv_offsets.astype(np.int32)).to(dev())
+        self.mq = int(batch.q_lengths.max()) if len(batch.q_lengths) else 0
+        self.mk = int(batch.kv_lengths.max()) if len(batch.kv_lengths) else 0
+        self.scale = 1.0 / math.sqrt(wl.head_dim)
+        self.act = wl.activation
+        self.causal = wl.causal
+
+    def forward(self):
+        return jfa.forward(self.q, self.k, self.v, self.qo, self.ko, self.mq, self.mk, self.scale, self.act,
+                           self.causal)
+
+    def backward(self, out, lse):
+        return jfa.backward(self.q, self.k, self.v, out, self.do, lse, self.qo, self.ko, self.mq, self.mk,
+                            self.scale, self.act, self.causal)
+
+
+def oracle_fwd(batch, seqs=None):
+    """Oracle forward, for all sequences or only those in `seqs` (returns
+    arrays restricted to those sequences' rows, plus the row index maps)."""
+    wl = batch.workload
+    s = 1.0 / math.sqrt(wl.head_dim)
+    q, k, v = batch.f64("q"), batch.f64("k"), batch.f64("v")
+    qo, ko = batch.q_offsets, batch.kv_offsets
+    if seqs is None:
+        return oracle.attention_fwd(q, k, v, qo, ko, s, wl.activation, wl.causal)
+    qi, ki, qs, ks = _subset(batch, seqs)
+    return oracle.attention_fwd(q[qi], k[ki], v[ki], qs, ks, s, wl.activation, wl.causal)
+
+
+def oracle_bwd(batch, seqs=None):
+    wl = batch.workload
+    s = 1.0 / math.sqrt(wl.head_dim)
+    q, k, v, do = batch.f64("q"), batch.f64("k"), batch.f64("v"), batch.f64("dout")
+    qo, ko = batch.q_offsets, batch.kv_offsets
+    if seqs is None:
+        return oracle.attention_bwd(q, k, v, do, qo, ko, s, wl.activation, wl.causal)
+    qi, ki, qs, ks = _subset(batch, seqs)
+    return oracle.attention_bwd(q[qi], k[ki], v[ki], do[qi], qs, ks, s, wl.activation, wl.causal)
+
+
+def _subset(batch, seqs):
+    qo, ko = batch.q_offsets, batch.kv_offsets
+    qi = np.concatenate([np.arange(qo[b], qo[b + 1]) for b in seqs]).astype(np.int64)
+    ki = np.concatenate([np.arange(ko[b], ko[b + 1]) for b in seqs]).astype(np.int64)
+    qs = offsets_from_lengths([qo[b + 1] - qo[b] for b in seqs])
+    ks = offsets_from_lengths([ko[b + 1] - ko[b] for b in seqs])
+    return qi, ki, qs, ks
+
+
+def rows_of(batch, seqs, side="q"):
+    o = batch.q_offsets if side == "q" else batch.kv_offsets
+    return np.concatenate([np.arange(o[b], o[b + 1]) for b in seqs]).astype(np.int64)
+
+
+def check_forward(out, lse, ref_out, ref_lse, activation, q_rows=None):
+    o = to_f64(out)
+    if q_rows is not None:
+        o = o[q_rows]
+    err = float(np.abs(o - ref_out).max()) if o.size else 0.0
+    assert err <= FWD_ATOL, "forward max abs error %.4g > %g" % (err, FWD_ATOL)
+    if activation == "softmax":
+        l = lse.cpu().numpy().astype(np.float64)
+        if q_rows is not None:
+            l = l[:, q_rows]
+        ninf = np.isneginf(ref_lse)
+        assert np.array_equal(np.isneginf(l), ninf), "lse -inf pattern differs"
+        if (~ninf).any():
+            lerr = float(np.abs(l[~ninf] - ref_lse[~ninf]).max())
+            assert lerr <= LSE_ATOL, "lse abs error %.4g" % lerr
+    return err
+
+
+def rel_l2(a, r):
+    nr = np.linalg.norm(r)
+    na = np.linalg.norm(a - r)
+    if nr == 0:
+        return na
+    return na / nr
+
+
+def check_backward(grads, refs, q_rows=None, k_rows=None):
+    errs = []
+    for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+        a = to_f64(g)
+        rows = q_rows if name == "dq" else k_rows
+        if rows is not None:
+            a = a[rows]
+        e = rel_l2(a, r)
+        assert e <= GRAD_RTOL, "%s relative L2 error %.4g > %g" % (name, e, GRAD_RTOL)
+        errs.append(e)
+    return errs

@@ -1,0 +1,115 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/jfa.h declares, and host-side validation returns the documented
+status before anything is enqueued (the pointers below are never
+dereferenced: every call is rejected, or is a no-op, on the host)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from jagged_attention_ads_amd import jfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jfa.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+P = 4096          # a 16-byte aligned fake device address, never dereferenced
+MIS = 4098        # misaligned
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jfa_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert len(names) == 8, names
+    L = jfa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(jfa.EXPORTED)
+
+
+def test_status_strings():
+    for code, name in jfa.STATUS_NAMES.items():
+        assert jfa.jfa_status_string(code) == name
+    assert "unknown" in jfa.jfa_status_string(99)
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, qo=P, ko=P, batch=2, heads=2, d=64, tq=10, tk=10, mq=5, mk=5, scale=0.125,
+             act=0, causal=0, dtype=0, out=P, lse=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return jfa.lib().jfa_forward(a["q"], a["k"], a["v"], a["qo"], a["ko"], a["batch"], a["heads"], a["d"], a["tq"],
+                                 a["tk"], a["mq"], a["mk"], a["scale"], a["act"], a["causal"], a["dtype"],
+                                 a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, out=P, do=P, lse=P, qo=P, ko=P, batch=2, heads=2, d=64, tq=10, tk=10, mq=5, mk=5,
+             scale=0.125, act=0, causal=0, dtype=0, dq=P, dk=P, dv=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return jfa.lib().jfa_backward(a["q"], a["k"], a["v"], a["out"], a["do"], a["lse"], a["qo"], a["ko"],
+                                  a["batch"], a["heads"], a["d"], a["tq"], a["tk"], a["mq"], a["mk"], a["scale"],
+                                  a["act"], a["causal"], a["dtype"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"],
+                                  None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(qo=None), INVALID), (dict(out=None), INVALID),
+    (dict(lse=None), INVALID), (dict(batch=-1), INVALID), (dict(heads=0), INVALID),
+    (dict(tq=-3), INVALID), (dict(mk=-1), INVALID), (dict(scale=math.nan), INVALID),
+    (dict(scale=math.inf), INVALID), (dict(act=2), INVALID), (dict(causal=2), INVALID), (dict(dtype=5), INVALID),
+    (dict(k=MIS), INVALID), (dict(out=MIS), INVALID), (dict(tq=1 << 24, heads=2, d=128), INVALID),
+    (dict(d=48), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(heads=257), UNSUPPORTED),
+    (dict(mk=64 * 1023 + 1), UNSUPPORTED), (dict(ws=None), WS_SMALL), (dict(wsb=16), WS_SMALL),
+])
+def test_forward_rejects(kw, status):
+    assert _fwd(**kw) == status
+    assert jfa.lib().jfa_last_error()
+
+
+def test_forward_noop_and_silu_without_lse():
+    assert _fwd(batch=0, ws=None, wsb=0) == OK
+    assert _fwd(tq=0, q=None, out=None, lse=None, ws=None, wsb=0) == OK
+    # silu needs no lse; the call is still rejected here only for the workspace
+    assert _fwd(act=1, lse=None, ws=None) == WS_SMALL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(do=None), INVALID), (dict(dk=None), INVALID), (dict(lse=None), INVALID), (dict(out=None), INVALID),
+    (dict(dv=MIS), INVALID), (dict(mq=64 * 1023 + 1), UNSUPPORTED), (dict(d=16), UNSUPPORTED),
+    (dict(wsb=100), WS_SMALL),
+])
+def test_backward_rejects(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_backward_noop_and_silu_optional():
+    assert _bwd(batch=0, ws=None, wsb=0) == OK
+    assert _bwd(act=1, out=None, lse=None, wsb=100) == WS_SMALL   # out/lse not required for silu
+
+
+def test_workspace_sizes():
+    fwd = jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 0)
+    bwd = jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 1)
+    assert 0 < fwd < bwd
+    assert bwd - fwd >= 4 * 97000 * 4            # holds delta [heads, total_q] fp32
+    assert jfa.jfa_workspace_size(2, 2, 48, 10, 10, 0) == 0
+
+
+def test_tile_shapes_and_worklist_size():
+    assert jfa.jfa_tile_shape(jfa.PASS_QUERY_TILES) == (128, 64)
+    assert jfa.jfa_tile_shape(jfa.PASS_KEY_TILES) == (128, 64)
+    with pytest.raises(jfa.JfaError):
+        jfa.jfa_tile_shape(7)
+    # capacity bound: sum ceil(L/128) <= (T + B*127)/128 items per head
+    n = jfa.jfa_worklist_bytes(jfa.PASS_QUERY_TILES, 3, 2, 300, 10)
+    cap = ((300 + 3 * 127) // 128) * 2
+    assert n >= 16 + 8 * cap + 4 * 4
+    assert jfa.jfa_worklist_bytes(9, 3, 2, 300, 10) == 0

@@ -1,0 +1,196 @@
+"""Bit-exact bookkeeping of the HIP path.
+
+* the device-built work lists equal the oracle's CPU enumeration bit for bit;
+* offsets are left unchanged;
+* every (row, head) slot of out / lse / dq / dk / dv is written, and nothing
+  beyond the tensors (guard rows) is;
+* outputs are bitwise reproducible, bitwise invariant (up to the permutation)
+  under reordering of the sequences, and a sequence's outputs do not depend on
+  its neighbours (no leakage, even from neighbours holding +-1e4).
+"""
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from jagged_attention_ads_amd import jfa
+from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch, offsets_from_lengths
+from tests.gpu_util import Dev, dev, values_to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _worklist_case(name, batch, causal):
+    b = make_batch(name, 7, batch=batch, with_dout=False)
+    return b.q_offsets, b.kv_offsets, b.workload.heads, causal
+
+
+WL_CASES = [
+    ("selfattn_causal", 64, True),
+    ("selfattn_causal", 64, False),
+    ("cross_asym", 512, False),
+    ("cross_asym", 300, True),
+    ("pareto_train", 1024, True),
+    ("gdpa_silu", 256, True),
+]
+
+
+@pytest.mark.parametrize("name,batch,causal", WL_CASES)
+@pytest.mark.parametrize("pass_", [jfa.PASS_QUERY_TILES, jfa.PASS_KEY_TILES])
+def test_worklist_bit_exact(name, batch, causal, pass_):
+    qo, ko, H, causal = _worklist_case(name, batch, causal)
+    tile, block = jfa.jfa_tile_shape(pass_)
+    if pass_ == jfa.PASS_QUERY_TILES:
+        costs = oracle.fwd_tile_costs(qo, ko, tile, block, causal)
+    else:
+        costs = oracle.kv_tile_costs(qo, ko, block, tile, causal)
+    ref = oracle.worklist(costs, H)
+    ref_arr = np.array([[b, (t << 8) | h] for b, h, t, _ in ref], dtype=np.int32).reshape(-1, 2)
+    qo_d = torch.from_numpy(qo.astype(np.int32)).to(dev())
+    ko_d = torch.from_numpy(ko.astype(np.int32)).to(dev())
+    lq, lk = np.diff(qo), np.diff(ko)
+    items, tile_start = jfa.build_worklist(pass_, qo_d, ko_d, H, int(qo[-1]), int(ko[-1]), int(lq.max()),
+                                           int(lk.max()), causal)
+    assert np.array_equal(items.numpy(), ref_arr)
+    lens = lq if pass_ == jfa.PASS_QUERY_TILES else lk
+    assert np.array_equal(tile_start.numpy(), offsets_from_lengths(-(-lens // tile)).astype(np.int32))
+    # offsets untouched
+    assert np.array_equal(qo_d.cpu().numpy(), qo.astype(np.int32))
+    assert np.array_equal(ko_d.cpu().numpy(), ko.astype(np.int32))
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["selfattn_causal", "gdpa_silu", "tiny_fp32"])
+def test_every_slot_written_once_and_guards_intact(name):
+    wl = dataclasses.replace(WORKLOADS[name], backward=True)
+    b = make_batch(wl, 3, q_lengths=[5, 0, 140, 64, 1], kv_lengths=[5, 7, 140, 0, 1] if not wl.causal
+                   else [5, 0, 140, 64, 1], with_dout=True)
+    d = Dev(b)
+    G = 3   # guard rows after each tensor
+    T_q, H, D = d.q.shape
+    T_k = d.k.shape[0]
+    canary = float("nan")
+
+    def buf(rows):
+        return torch.full((rows + G, H, D), canary, dtype=d.q.dtype, device=dev())
+
+    out_b, dq_b, dk_b, dv_b = buf(T_q), buf(T_q), buf(T_k), buf(T_k)
+    lse_b = torch.full((H * T_q + 7,), canary, dtype=torch.float32, device=dev())
+    out, dq, dk, dv = out_b[:T_q], dq_b[:T_q], dk_b[:T_k], dv_b[:T_k]
+    lse = lse_b[:H * T_q].view(H, T_q) if wl.activation == "softmax" else None
+    ws = jfa.workspace(len(b.q_lengths), H, D, T_q, T_k, True, dev())
+    jfa.jfa_forward(d.q, d.k, d.v, d.qo, d.ko, d.mq, d.mk, d.scale, d.act, d.causal, out, lse, ws)
+    jfa.jfa_backward(d.q, d.k, d.v, out, d.do, lse, d.qo, d.ko, d.mq, d.mk, d.scale, d.act, d.causal, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    for t in (out, dq, dk, dv):
+        assert not torch.isnan(t).any(), "a slot was left unwritten"
+    for t, n in ((out_b, T_q), (dq_b, T_q), (dk_b, T_k), (dv_b, T_k)):
+        assert torch.isnan(t[n:]).all(), "a guard row was written"
+    if lse is not None:
+        assert not torch.isnan(lse).any()
+        assert torch.isnan(lse_b[H * T_q:]).all()
+    else:
+        assert torch.isnan(lse_b).all()
+
+
+@pytest.mark.parametrize("name", ["selfattn_causal", "gdpa_silu", "pareto_train"])
+def test_bitwise_reproducible(name):
+    b = make_batch(name, 5, batch=48 if name != "pareto_train" else 256)
+    d = Dev(b)
+    runs = []
+    for _ in range(2):
+        out, lse = d.forward()
+        g = d.backward(out, lse)
+        torch.cuda.synchronize()
+        runs.append([_bits(x) for x in (out,) + tuple(g)] + ([lse.cpu().numpy()] if lse is not None else []))
+    for a, z in zip(*runs):
+        assert np.array_equal(a, z)
+
+
+@pytest.mark.parametrize("name", ["selfattn_causal", "cross_asym", "gdpa_silu"])
+def test_permutation_bitwise(name):
+    wl = dataclasses.replace(WORKLOADS[name], backward=True)
+    b = make_batch(wl, 9, batch=20, with_dout=True)
+    perm = np.random.default_rng(1).permutation(20)
+    qo, ko = b.q_offsets, b.kv_offsets
+
+    def cat(x, o):
+        return np.concatenate([x[o[p]:o[p + 1]] for p in perm])
+    b2 = dataclasses.replace(b, q_lengths=b.q_lengths[perm], kv_lengths=b.kv_lengths[perm],
+                             q_offsets=offsets_from_lengths(b.q_lengths[perm]),
+                             kv_offsets=offsets_from_lengths(b.kv_lengths[perm]),
+                             q=cat(b.q, qo), k=cat(b.k, ko), v=cat(b.v, ko), dout=cat(b.dout, qo))
+    res = []
+    for bb in (b, b2):
+        d = Dev(bb)
+        out, lse = d.forward()
+        g = d.backward(out, lse)
+        torch.cuda.synchronize()
+        res.append((out, lse, g))
+    (o1, l1, g1), (o2, l2, g2) = res
+    assert np.array_equal(cat(_bits(o1), qo), _bits(o2))
+    if l1 is not None:
+        assert np.array_equal(np.concatenate([l1.cpu().numpy()[:, qo[p]:qo[p + 1]] for p in perm], axis=1),
+                              l2.cpu().numpy())
+    assert np.array_equal(cat(_bits(g1[0]), qo), _bits(g2[0]))
+    assert np.array_equal(cat(_bits(g1[1]), ko), _bits(g2[1]))
+    assert np.array_equal(cat(_bits(g1[2]), ko), _bits(g2[2]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_no_leakage_from_extreme_neighbours(causal):
+    """A 77-token sequence between neighbours holding +-1e4 (and a last
+    sequence that ends exactly at the end of the allocation) gives bitwise the
+    same outputs as the sequence alone."""
+    wl = dataclasses.replace(WORKLOADS["selfattn_causal"], causal=causal, head_dim=64)
+    lens = [130, 77, 200]
+    b = make_batch(wl, 11, q_lengths=lens, kv_lengths=lens, with_dout=True)
+    big = np.float32(1e4)
+    rng = np.random.default_rng(2)
+    for name in ("q", "k", "v", "dout"):
+        arr = getattr(b, name)
+        for s in (0, 2):
+            o = b.q_offsets
+            sl = slice(o[s], o[s + 1])
+            signs = np.where(rng.random(arr[sl].shape) < 0.5, -big, big).astype(np.float32)
+            arr[sl] = (signs.view(np.uint32) >> 16).astype(np.uint16)
+    alone = make_batch(wl, 11, q_lengths=[77], kv_lengths=[77], with_dout=True)
+    o = b.q_offsets
+    for name in ("q", "k", "v", "dout"):
+        setattr(alone, name, getattr(b, name)[o[1]:o[2]].copy())
+    res = []
+    for bb in (b, alone):
+        d = Dev(bb)
+        out, lse = d.forward()
+        g = d.backward(out, lse)
+        torch.cuda.synchronize()
+        res.append((out, lse, g))
+    (o1, l1, g1), (o2, l2, g2) = res
+    r = slice(o[1], o[2])
+    assert np.array_equal(_bits(o1[r]), _bits(o2))
+    assert np.array_equal(l1[:, r].cpu().numpy(), l2.cpu().numpy())
+    for x, y in zip(g1, g2):
+        assert np.array_equal(_bits(x[r]), _bits(y))
+    assert torch.isfinite(o2).all()
+
+
+def test_noop_and_zero_rows():
+    H, D = 2, 64
+    q = torch.zeros((0, H, D), dtype=torch.bfloat16, device=dev())
+    qo = torch.zeros(1, dtype=torch.int32, device=dev())
+    out, lse = jfa.forward(q, q, q, qo, qo, 0, 0)
+    assert out.shape == (0, H, D)
+    # keys nobody reads: dk = dv = 0
+    qo = torch.tensor([0, 0], dtype=torch.int32, device=dev())
+    ko = torch.tensor([0, 5], dtype=torch.int32, device=dev())
+    k = torch.randn((5, H, D), device=dev()).to(torch.bfloat16)
+    dq, dk, dv = jfa.backward(q, k, k, q, q, torch.empty((H, 0), device=dev()), qo, ko, 0, 5)
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
