@@ -113,6 +113,27 @@ int jfa_backward(const void* q, const void* k, const void* v, const void* out, c
                  int32_t max_kv_len, float scale, int32_t activation, int32_t causal, int32_t dtype, void* dq,
                  void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The same two calls, additionally recording caller-created HIP events on
+ * `stream` between their kernel launches, for per-kernel timing (every
+ * kernel still runs; with events == NULL they are jfa_forward and
+ * jfa_backward).  Forward: 3 events -- [0] before the work-list builder,
+ * [1] before the attention kernel, [2] after it.  Backward: 6 events --
+ * [0] start, [1] after the query-tile work list, [2] after the delta
+ * preprocess (softmax only), [3] after the key-tile work list, [4] after the
+ * dK/dV kernel, [5] after the dQ kernel.  Events are not recorded when the
+ * call is a no-op or is rejected. */
+int jfa_forward_profiled(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                         const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                         int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation,
+                         int32_t causal, int32_t dtype, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+int jfa_backward_profiled(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                          const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
+                          int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
+                          int32_t max_kv_len, float scale, int32_t activation, int32_t causal, int32_t dtype,
+                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream, hipEvent_t* events);
+
 /* Inspection of the tile scheduler (software tile scheduling for jagged
  * tensors, GDPA item; persistent-kernel scheduling, JFA item).
  * jfa_worklist_bytes: size of the buffer jfa_build_worklist writes.

@@ -45,6 +45,12 @@ WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_
   return L;
 }
 
+// Records events[i] on the stream when the caller asked for stage events.
+hipError_t record(hipEvent_t* events, int i, hipStream_t stream) {
+  if (!events) return hipSuccess;
+  return hipEventRecord(events[i], stream);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int32_t buckets_for(int32_t max_len, int32_t block) { return (max_len + block - 1) / block + 1; }
@@ -147,11 +153,11 @@ int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv
   return JFA_OK;
 }
 
-int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
-                int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
-                int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation, int32_t causal,
-                int32_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+int jfa_forward_profiled(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                         const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                         int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation,
+                         int32_t causal, int32_t dtype, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
   int st = check_common(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
                         max_kv_len, scale, activation, causal, dtype);
   if (st != JFA_OK) return st;
@@ -166,9 +172,11 @@ int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_of
   if (!workspace || workspace_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
 
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nb, ws + L.off_wq,
-                                   L.wq, stream);
+  hipError_t e;
+  if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
+  e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nb, ws + L.off_wq, L.wq, stream);
   if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+  if ((e = record(events, 1, stream)) != hipSuccess) return hip_fail(e, "event record");
   jfa::FwdArgs a{};
   a.q = q;
   a.k = k;
@@ -186,14 +194,26 @@ int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_of
   a.scale_log2 = scale * 1.4426950408889634f;
   e = jfa::launch_fwd(a, head_dim, dtype, activation, L.wq.capacity, stream);
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
+  if ((e = record(events, 2, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;
 }
 
-int jfa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                 const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch, int32_t heads,
-                 int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
-                 float scale, int32_t activation, int32_t causal, int32_t dtype, void* dq, void* dk, void* dv,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
+                int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
+                int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation, int32_t causal,
+                int32_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  return jfa_forward_profiled(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
+                              max_kv_len, scale, activation, causal, dtype, out, lse, workspace, workspace_bytes,
+                              stream, nullptr);
+}
+
+int jfa_backward_profiled(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                          const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
+                          int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
+                          int32_t max_kv_len, float scale, int32_t activation, int32_t causal, int32_t dtype,
+                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream, hipEvent_t* events) {
   int st = check_common(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
                         max_kv_len, scale, activation, causal, dtype);
   if (st != JFA_OK) return st;
@@ -239,26 +259,44 @@ int jfa_backward(const void* q, const void* k, const void* v, const void* out, c
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
 
+  if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (total_q > 0) {
     e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq, stream);
     if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
-    if (activation == JFA_ACT_SOFTMAX) {
-      e = jfa::launch_bwd_pre(a, head_dim, dtype, stream);
-      if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-    }
   }
+  if ((e = record(events, 1, stream)) != hipSuccess) return hip_fail(e, "event record");
+  if (total_q > 0 && activation == JFA_ACT_SOFTMAX) {
+    e = jfa::launch_bwd_pre(a, head_dim, dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+  }
+  if ((e = record(events, 2, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (total_kv > 0) {
     e = jfa::launch_sched(jfa::kPassKV, q_offsets, kv_offsets, batch, heads, causal, nbk, ws + L.off_wkv, L.wkv,
                           stream);
     if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+  }
+  if ((e = record(events, 3, stream)) != hipSuccess) return hip_fail(e, "event record");
+  if (total_kv > 0) {
     e = jfa::launch_bwd_dkdv(a, head_dim, dtype, activation, L.wkv.capacity, stream);
     if (e != hipSuccess) return hip_fail(e, "dK/dV kernel launch");
   }
+  if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (total_q > 0) {
     e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, L.wq.capacity, stream);
     if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
   }
+  if ((e = record(events, 5, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;
+}
+
+int jfa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch, int32_t heads,
+                 int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
+                 float scale, int32_t activation, int32_t causal, int32_t dtype, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return jfa_backward_profiled(q, k, v, out, dout, lse, q_offsets, kv_offsets, batch, heads, head_dim, total_q,
+                               total_kv, max_q_len, max_kv_len, scale, activation, causal, dtype, dq, dk, dv,
+                               workspace, workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"

@@ -65,7 +65,9 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   f32x16 o[C::ND];
 #pragma unroll
   for (int i = 0; i < C::ND; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // running max, running sum of the exact weights (for lse) and of the
+  // weights as rounded into the P operand (for normalising O)
+  float m_run = -INFINITY, l_run = 0.f, l_used = 0.f;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
 
   TileStage<T, D, C::BN, C::KS, true> kst;   // K rows stored swap23-permuted
@@ -126,6 +128,7 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
+        l_used *= alpha;
 #pragma unroll
         for (int i = 0; i < C::ND; ++i) o[i] *= alpha;
 #pragma unroll
@@ -155,15 +158,29 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
         }
       }
       // O^T (D x 32 queries) += V^T P^T; k-step (mt, ss) covers keys kv0 + 32*mt + 16*ss + 0..15
+      frag_t<T> pf[2][2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) pf[mt][ss] = pack_frag<T>(s[mt], ss);
+      }
+      if constexpr (ACT == 0) {
+        // normalise by the sum of the weights the product really uses, so
+        // that O stays a convex combination of V rows after P is rounded
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int ss = 0; ss < 2; ++ss) l_used += frag_sum(pf[mt][ss]);
+        }
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) {
-          const frag_t<T> pf = pack_frag<T>(s[mt], ss);
 #pragma unroll
           for (int dt = 0; dt < C::ND; ++dt) {
             const frag_t<T> vf = lds_col_frag<T, C::VS, false>(vt, 32 * mt + 16 * ss, 32 * dt);
-            mma(o[dt], vf, pf);
+            mma(o[dt], vf, pf[mt][ss]);
           }
         }
       }
@@ -174,10 +191,11 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
 
   if (!wave_live) return;
   const float l_tot = ACT == 0 ? xor32_sum(l_run) : 1.f;
+  const float l_out = ACT == 0 ? xor32_sum(l_used) : 1.f;
   if (my_row >= lq) return;
   const bool row_live = lk > 0 && (!a.causal || my_row + off >= 0);
   float f = 0.f;
-  if (row_live) f = ACT == 0 ? 1.0f / l_tot : 1.0f;
+  if (row_live) f = ACT == 0 ? 1.0f / l_out : 1.0f;
   T* op = static_cast<T*>(a.out) + (size_t)(qs + my_row) * rs + (size_t)h * D;
   store_row<T, C::ND>(op, o, f);
   if (ACT == 0 && g == 0) {

@@ -89,6 +89,21 @@ __device__ __forceinline__ frag_t<T> pack_frag(const f32x16& acc, int s) {
   }
 }
 
+// Sum of the 8 values of a fragment as it will enter the MFMA.
+__device__ __forceinline__ float frag_sum(const bf16x8& f) {
+  const u32x4 w = __builtin_bit_cast(u32x4, f);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc += __uint_as_float(w[i] << 16) + __uint_as_float(w[i] & 0xffff0000u);
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(const f32x8& f) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc += f[i];
+  return acc;
+}
+
 // ---------------------------------------------------------------- LDS access
 
 // 8 consecutive elements of one LDS row.
@@ -125,17 +140,18 @@ __device__ __forceinline__ frag_t<T> lds_col_frag(const char* tile, int row0, in
     const int blk = l >> 4, s = l & 15;
     const int g = blk >> 1, half = blk & 1;
     const int col = col0 + 16 * half + 4 * (s & 3);
-    bf16x8 f;
+    u32x2 w[2];
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
       int row = row0 + 8 * g + 4 * rd + (s >> 2);
       if (SWAPPED) row = swap23(row);
       const char* p = tile + row * STRIDE + col * 2;
-      i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JFA_LDS i16x4*)(p));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f[4 * rd + e] = __builtin_bit_cast(__bf16, t[e]);
+      // whole 32-bit words only: per-element bf16 extraction of this
+      // builtin's result is not compiled correctly by this toolchain
+      w[rd] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((JFA_LDS i16x4*)(p)));
     }
-    return f;
+    const u32x4 words = {w[0][0], w[0][1], w[1][0], w[1][1]};
+    return __builtin_bit_cast(bf16x8, words);
   } else {
     const int g = l >> 5, c = col0 + (l & 31);
     f32x8 f;
