@@ -229,12 +229,6 @@ def main():
         if st != 0:
             raise jfa.JfaError(st, L.jfa_last_error().decode())
 
-    L.jfa_forward_profiled.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 7 + [
-        ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
-        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
-    L.jfa_backward_profiled.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int32] * 7 + [
-        ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4 + [
-        ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
 
     torch.cuda.synchronize()
     ev = HipEvents()

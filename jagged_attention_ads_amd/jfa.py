@@ -27,8 +27,8 @@ DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 PASS_QUERY_TILES = 0
 PASS_KEY_TILES = 1
 
-EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_worklist_bytes", "jfa_tile_shape",
-            "jfa_build_worklist", "jfa_status_string", "jfa_last_error")
+EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_profiled", "jfa_backward_profiled",
+            "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_status_string", "jfa_last_error")
 
 
 class JfaError(RuntimeError):
@@ -56,6 +56,10 @@ def lib():
         L.jfa_forward.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_i32] * 7 + [_f32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
         L.jfa_backward.restype = ctypes.c_int
         L.jfa_backward.argtypes = [_vp] * 8 + [_i32] * 7 + [_f32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.jfa_forward_profiled.restype = ctypes.c_int
+        L.jfa_forward_profiled.argtypes = L.jfa_forward.argtypes + [_vp]
+        L.jfa_backward_profiled.restype = ctypes.c_int
+        L.jfa_backward_profiled.argtypes = L.jfa_backward.argtypes + [_vp]
         L.jfa_worklist_bytes.restype = _sz
         L.jfa_worklist_bytes.argtypes = [_i32] * 5
         L.jfa_tile_shape.restype = ctypes.c_int
