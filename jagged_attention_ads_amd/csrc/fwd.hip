@@ -108,34 +108,44 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
       const bool need_mask = (kv0 + C::BN > lk) || (a.causal && kv0 + C::BN - 1 > row0 + off);
       // register r of tile mt holds key kv0 + 32*mt + 16*(r/8) + 8*g + r%8
       if constexpr (ACT == 0) {
-        float mx = -INFINITY;
+        if (need_mask) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+          for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = s[mt][r] * a.scale_log2;
-            if (need_mask) {
+            for (int r = 0; r < 16; ++r) {
               const int j = kv0 + 32 * mt + 16 * (r >> 3) + 8 * g + (r & 7);
               const bool masked = (j >= lk) || (a.causal && j > my_row + off);
-              x -= masked ? kMaskShift : 0.f;
+              s[mt][r] -= masked ? kMaskShift : 0.f;
             }
-            s[mt][r] = x;
-            mx = fmaxf(mx, x);
           }
         }
-        mx = xor32_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        l_used *= alpha;
+        // row max of the raw scores (the scale is positive), three at a time
+        float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-        for (int i = 0; i < C::ND; ++i) o[i] *= alpha;
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+        mx = xor32_max(mx) * a.scale_log2;
+        // Rescale O and the sums only when the max grows by more than
+        // kLazyRescale (log2 units); otherwise keep the stale max, so the
+        // weights stay below 2^kLazyRescale.  Wave-uniform branch.
+        const bool grow = mx > m_run + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          // a row whose keys are all masked so far takes a max near -1.3e29;
+          // flooring it keeps its weights at exactly 0 (a live row's max is
+          // a real score, far above the floor)
+          const float m_use = grow ? fmaxf(mx, kMaxFloor) : m_run;
+          const float alpha = fast_exp2(m_run - m_use);
+          m_run = m_use;
+          l_run *= alpha;
+          l_used *= alpha;
+#pragma unroll
+          for (int i = 0; i < C::ND; ++i) o[i] *= alpha;
+        }
+        const float neg_m = -m_run;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(s[mt][r] - m_new);
+            const float p = fast_exp2(fmaf(s[mt][r], a.scale_log2, neg_m));
             l_run += p;
             s[mt][r] = p;
           }
@@ -170,7 +180,7 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-          for (int ss = 0; ss < 2; ++ss) l_used += frag_sum(pf[mt][ss]);
+          for (int ss = 0; ss < 2; ++ss) frag_sum_into(l_used, pf[mt][ss]);
         }
       }
 #pragma unroll

@@ -32,6 +32,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 // replaced by -inf: exp2 of (score - kMaskShift - rowmax) is exactly 0 in
 // fp32 for any finite score, and no inf/NaN ever enters the running max.
 constexpr float kMaskShift = 1.0e30f;
+// The online softmax keeps a stale row max until the true max exceeds it by
+// more than this (log2 units): weights then stay below 2^8, and O is rescaled
+// only when a row's max really moves.
+constexpr float kLazyRescale = 8.0f;
+// Lower bound of the running max (log2 units): masked scores sit near
+// -1.3e29 after scaling, so a fully masked row's weights exp2(x - max) stay 0.
+constexpr float kMaxFloor = -1.0e20f;
 
 constexpr int kWave = 64;
 
@@ -89,19 +96,27 @@ __device__ __forceinline__ frag_t<T> pack_frag(const f32x16& acc, int s) {
   }
 }
 
-// Sum of the 8 values of a fragment as it will enter the MFMA.
-__device__ __forceinline__ float frag_sum(const bf16x8& f) {
+// acc += sum of the 8 values of a fragment as it will enter the MFMA: one
+// v_dot2c_f32_bf16 against (1.0, 1.0) per packed word, chained through the
+// accumulator.  Issued as one inline-assembly block on plain 32-bit words
+// (through the builtin's bf16-pair vector type this toolchain fed the first
+// word to all four instructions).  The block ends with the 3 wait states a
+// DOT result needs before another VALU instruction may read it; the
+// compiler cannot insert them for inline assembly.
+__device__ __forceinline__ void frag_sum_into(float& acc, const bf16x8& f) {
   const u32x4 w = __builtin_bit_cast(u32x4, f);
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc += __uint_as_float(w[i] << 16) + __uint_as_float(w[i] & 0xffff0000u);
-  return acc;
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+  asm("v_dot2c_f32_bf16 %0, %1, %2\n\t"
+      "v_dot2c_f32_bf16 %0, %1, %3\n\t"
+      "v_dot2c_f32_bf16 %0, %1, %4\n\t"
+      "v_dot2c_f32_bf16 %0, %1, %5\n\t"
+      "s_nop 2"
+      : "+v"(acc)
+      : "s"(0x3f803f80u), "v"(w0), "v"(w1), "v"(w2), "v"(w3));
 }
-__device__ __forceinline__ float frag_sum(const f32x8& f) {
-  float acc = 0.f;
+__device__ __forceinline__ void frag_sum_into(float& acc, const f32x8& f) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc += f[i];
-  return acc;
 }
 
 // ---------------------------------------------------------------- LDS access
