@@ -36,6 +36,8 @@ def flags():
         "-O3",
         "-std=c++17",
         "-fPIC",
+        # no NaN inputs are supported; lets max() skip NaN canonicalisation
+        "-fno-honor-nans",
         # packed fp32 VALU ops stay off (only scalar fp32 VALU is emitted)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I" + INCLUDE,

@@ -3,8 +3,8 @@
 // contract.
 #include "jfa.h"
 
-#include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <string>
 
 #include "jfa_internal.h"
@@ -51,6 +51,14 @@ hipError_t record(hipEvent_t* events, int i, hipStream_t stream) {
   return hipEventRecord(events[i], stream);
 }
 
+// Finite test on the bit pattern (the library is built with NaN-free
+// floating-point assumptions, which may fold std::isfinite).
+bool finite_float(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, sizeof(u));
+  return (u & 0x7f800000u) != 0x7f800000u;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int32_t buckets_for(int32_t max_len, int32_t block) { return (max_len + block - 1) / block + 1; }
@@ -78,7 +86,7 @@ int check_common(const void* q, const void* k, const void* v, const int32_t* qo,
   // value pointers may be NULL only when their tensor has no rows
   if (!qo || !ko) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL offsets pointer");
   if ((total_q > 0 && !q) || (total_kv > 0 && (!k || !v))) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL input pointer");
-  if (!std::isfinite(scale)) return fail(JFA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!finite_float(scale)) return fail(JFA_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (activation != JFA_ACT_SOFTMAX && activation != JFA_ACT_SILU)
     return fail(JFA_ERR_INVALID_ARGUMENT, "bad activation");
   if (causal != 0 && causal != 1) return fail(JFA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");

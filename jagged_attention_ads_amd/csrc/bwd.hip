@@ -8,7 +8,7 @@
 // stored once:
 //   dK/dV pass -- one work item per (sequence, head, 128-key tile); each wave
 //     owns 32 keys (its K and V rows live in registers) and walks the
-//     64-query blocks that see them, staged in LDS.  P and dS are recomputed
+//     64-query blocks that see them, staged in swizzled LDS tiles.  P and dS are recomputed
 //     from lse (softmax) or from the scores (SiLU).
 //   dQ pass -- one work item per (sequence, head, 128-query tile); each wave
 //     owns 32 queries and walks the 64-key blocks that they see.
@@ -88,8 +88,7 @@ template <typename T, int D>
 struct DkdvCfg {
   static constexpr int BN = kBwdBN, BM = kBwdBM, NT = 256;
   static constexpr int ES = sizeof(T);
-  static constexpr int RS = D * ES + 16;          // Q / dO tile row stride
-  static constexpr int QT = BM * RS;
+  static constexpr int QT = Swz<T, D>::tile_bytes(BM);   // Q / dO tile
   static constexpr int STAGE = 2 * QT + 2 * BM * 4;   // Q, dO, lse2, delta
   static constexpr int LDS = 2 * STAGE;
   static constexpr int ND = D / 32, NK = D / 16;
@@ -140,12 +139,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   const float* lse_h = ACT == 0 ? a.lse + (size_t)h * a.total_q + qs : nullptr;
   const float* del_h = ACT == 0 ? a.delta + (size_t)h * a.total_q + qs : nullptr;
 
-  TileStage<T, D, C::BM, C::RS, true> qst, dst;   // query rows stored swap23-permuted
+  TileStage<T, D, C::BM, true> qst, dst;   // query rows stored swap23-permuted
   float st_lse = 0.f, st_del = 0.f;
   auto gload = [&](int qblk) {
     const int r0 = qblk * C::BM;
-    qst.load(qb, rs, r0, lq, tid);
-    dst.load(db, rs, r0, lq, tid);
+    qst.load(qb, (int)rs, r0, lq, tid);
+    dst.load(db, (int)rs, r0, lq, tid);
     if (ACT == 0 && tid < C::BM) {
       const int r = min(r0 + tid, lq - 1);
       st_lse = lse_log2(lse_h[r]);
@@ -186,9 +185,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < C::NK; ++kk) {
-          const frag_t<T> qfr = lds_row_frag<T>(qt + (32 * sb + c32) * C::RS + (16 * kk + 8 * g) * C::ES);
+          const frag_t<T> qfr = lds_row_frag<T, D>(qt, 32 * sb + c32, 16 * kk + 8 * g);
           mma(s, qfr, kf[kk]);
-          const frag_t<T> dfr = lds_row_frag<T>(dt_ + (32 * sb + c32) * C::RS + (16 * kk + 8 * g) * C::ES);
+          const frag_t<T> dfr = lds_row_frag<T, D>(dt_, 32 * sb + c32, 16 * kk + 8 * g);
           mma(dp, dfr, vf[kk]);
         }
         const bool need_mask = (qa + 32 > lq) || (kw0 + 32 > lk) || (a.causal && kw0 + 31 > qa + off);
@@ -212,9 +211,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
           const frag_t<T> sf = pack_frag<T>(dp, ss);
 #pragma unroll
           for (int d2 = 0; d2 < C::ND; ++d2) {
-            const frag_t<T> dof = lds_col_frag<T, C::RS, true>(dt_, 32 * sb + 16 * ss, 32 * d2);
+            const frag_t<T> dof = lds_col_frag<T, D, true>(dt_, 32 * sb + 16 * ss, 32 * d2);
             mma(dv[d2], dof, pf);
-            const frag_t<T> qtf = lds_col_frag<T, C::RS, true>(qt, 32 * sb + 16 * ss, 32 * d2);
+            const frag_t<T> qtf = lds_col_frag<T, D, true>(qt, 32 * sb + 16 * ss, 32 * d2);
             mma(dk[d2], qtf, sf);
           }
         }
@@ -237,8 +236,7 @@ template <typename T, int D>
 struct DqCfg {
   static constexpr int BM = kFwdBM, BN = kFwdBN, NT = 256;
   static constexpr int ES = sizeof(T);
-  static constexpr int RS = D * ES + 16;   // K / V tile row stride
-  static constexpr int KT = BN * RS;
+  static constexpr int KT = Swz<T, D>::tile_bytes(BN);   // K / V tile
   static constexpr int STAGE = 2 * KT;
   static constexpr int LDS = 2 * STAGE;
   static constexpr int ND = D / 32, NK = D / 16;
@@ -286,10 +284,10 @@ __global__ __launch_bounds__(256, (D >= 128 || sizeof(T) == 4) ? 1 : 2) void dq_
 
   const T* kb = static_cast<const T*>(a.k) + (size_t)ks * rs + (size_t)h * D;
   const T* vb = static_cast<const T*>(a.v) + (size_t)ks * rs + (size_t)h * D;
-  TileStage<T, D, C::BN, C::RS, true> kst, vst;   // key rows stored swap23-permuted
+  TileStage<T, D, C::BN, true> kst, vst;   // key rows stored swap23-permuted
   auto gload = [&](int kvt) {
-    kst.load(kb, rs, kvt * C::BN, lk, tid);
-    vst.load(vb, rs, kvt * C::BN, lk, tid);
+    kst.load(kb, (int)rs, kvt * C::BN, lk, tid);
+    vst.load(vb, (int)rs, kvt * C::BN, lk, tid);
   };
   auto lstore = [&](int buf) {
     char* st = smem + buf * C::STAGE;
@@ -316,9 +314,9 @@ __global__ __launch_bounds__(256, (D >= 128 || sizeof(T) == 4) ? 1 : 2) void dq_
       for (int kk = 0; kk < C::NK; ++kk) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const frag_t<T> kfr = lds_row_frag<T>(kt + (32 * mt + c32) * C::RS + (16 * kk + 8 * g) * C::ES);
+          const frag_t<T> kfr = lds_row_frag<T, D>(kt, 32 * mt + c32, 16 * kk + 8 * g);
           mma(s[mt], kfr, qf[kk]);
-          const frag_t<T> vfr = lds_row_frag<T>(vt + (32 * mt + c32) * C::RS + (16 * kk + 8 * g) * C::ES);
+          const frag_t<T> vfr = lds_row_frag<T, D>(vt, 32 * mt + c32, 16 * kk + 8 * g);
           mma(dp[mt], vfr, df[kk]);
         }
       }
@@ -343,7 +341,7 @@ __global__ __launch_bounds__(256, (D >= 128 || sizeof(T) == 4) ? 1 : 2) void dq_
           const frag_t<T> sf = pack_frag<T>(dp[mt], ss);
 #pragma unroll
           for (int d2 = 0; d2 < C::ND; ++d2) {
-            const frag_t<T> ktf = lds_col_frag<T, C::RS, true>(kt, 32 * mt + 16 * ss, 32 * d2);
+            const frag_t<T> ktf = lds_col_frag<T, D, true>(kt, 32 * mt + 16 * ss, 32 * d2);
             mma(dq[d2], ktf, sf);
           }
         }

@@ -10,10 +10,15 @@
 // query rows and keeps them in registers as the B operand of S^T = K Q^T, so
 // that every lane ends up owning one query row (its column of S^T): the
 // online-softmax statistics are per-lane scalars, reduced with a single
-// permlane32 swap.  K and V tiles of 64 keys are staged in LDS
-// (double-buffered through registers); V^T fragments come straight from the
-// row-major V tile through ds_read_b64_tr_b16.  Ragged tails and the causal
-// diagonal are masked arithmetically, only on the tiles that need it.
+// permlane32 swap.  K and V tiles of 64 keys are copied from HBM straight
+// into swizzled LDS tiles (buffer loads that write LDS, two slots each), and
+// the loop is software-pipelined: the scores of the next key tile are
+// computed on the matrix cores while the softmax of the current one runs on
+// the vector ALUs.  V^T fragments come straight from the row-major V tile
+// through ds_read_b64_tr_b16.  Ragged tails and the causal diagonal are
+// masked arithmetically, only on the tiles that need it.
+#include <type_traits>
+
 #include "jfa_common.hpp"
 #include "jfa_internal.h"
 
@@ -22,20 +27,18 @@ namespace jfa {
 template <typename T, int D>
 struct FwdCfg {
   static constexpr int BM = kFwdBM, BN = kFwdBN, NT = 256;
-  static constexpr int ES = sizeof(T);
-  static constexpr int KS = D * ES + 16;   // K tile row stride in bytes
-  static constexpr int VS = D * ES + 32;   // V tile row stride in bytes
-  static constexpr int KT = BN * KS, VT = BN * VS;
-  static constexpr int STAGE = KT + VT;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int ND = D / 32;        // 32-wide d blocks of O^T
-  static constexpr int NK = D / 16;        // k-steps of S^T
+  static constexpr int KT = Swz<T, D>::tile_bytes(BN);   // one K or V tile
+  static constexpr int LDS = 4 * KT;                     // K slots 0, 1; V slots 0, 1
+  static constexpr int ND = D / 32;                      // 32-wide d blocks of O^T
+  static constexpr int NK = D / 16;                      // k-steps of S^T
 };
 
 template <typename T, int D, int ACT>
 __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<T, D>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  char* const kslot0 = smem;
+  char* const vslot0 = smem + 2 * C::KT;
 
   if ((int)blockIdx.x >= *a.n_items) return;
   int b, h, t;
@@ -49,10 +52,23 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   const int my_row = row0 + c32;         // the query row this lane owns
   const bool wave_live = row0 < lq;
   const int n_kv = q_tile_kv_blocks(lq, lk, t, C::BM, C::BN, a.causal);
-  const size_t rs = (size_t)a.heads * D;  // elements between consecutive tokens
+  const int rs = a.heads * D;            // elements between consecutive tokens
 
   const T* kb = static_cast<const T*>(a.k) + (size_t)ks * rs + (size_t)h * D;
   const T* vb = static_cast<const T*>(a.v) + (size_t)ks * rs + (size_t)h * D;
+
+  // K rows are stored swap23-permuted, V rows in order (see the header note)
+  TileDma<T, D, C::BN, true> kdma;
+  TileDma<T, D, C::BN, false> vdma;
+  kdma.init(rs, tid);
+  vdma.init(rs, tid);
+
+  // Prologue: K(0), V(0), K(1) into LDS while the Q fragments arrive.
+  if (n_kv > 0) {
+    kdma.issue(kslot0, kb, rs, 0, lk, tid);
+    vdma.issue(vslot0, vb, rs, 0, lk, tid);
+  }
+  if (n_kv > 1) kdma.issue(kslot0 + C::KT, kb, rs, C::BN, lk, tid);
 
   frag_t<T> qf[C::NK];
   {
@@ -70,133 +86,164 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   float m_run = -INFINITY, l_run = 0.f, l_used = 0.f;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
 
-  TileStage<T, D, C::BN, C::KS, true> kst;   // K rows stored swap23-permuted
-  TileStage<T, D, C::BN, C::VS, false> vst;
-  auto gload = [&](int kvt) {
-    kst.load(kb, rs, kvt * C::BN, lk, tid);
-    vst.load(vb, rs, kvt * C::BN, lk, tid);
-  };
-  auto lstore = [&](int buf) {
-    char* kt = smem + buf * C::STAGE;
-    kst.store(kt, tid);
-    vst.store(kt + C::KT, tid);
+  // a wave takes part in key tile j iff some of its rows see a key of it
+  auto wave_active = [&](int j) { return wave_live && (!a.causal || j * C::BN <= row0 + 31 + off); };
+
+  // S^T (64 keys x 32 queries) = K Q^T for key tile j, as two 32-key tiles
+  auto scores = [&](f32x16* s, int j) {
+    const char* kt = kslot0 + (j & 1) * C::KT;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) mma(s[mt], lds_row_frag<T, D>(kt, 32 * mt + c32, 16 * kk + 8 * g), qf[kk]);
+    }
   };
 
-  if (n_kv > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+  // Keys of key tile j at or beyond `limit - kv0` are masked for this lane's
+  // row (ragged tail and causal diagonal).  Register r of 32-key tile mt
+  // holds key kv0 + 32*mt + 16*(r/8) + 8*g + r%8.
+  const int row_limit = a.causal ? min(lk, my_row + off + 1) : lk;
+  auto needs_mask = [&](int j) {
+    const int kv0 = j * C::BN;
+    return (kv0 + C::BN > lk) || (a.causal && kv0 + C::BN - 1 > row0 + off);
+  };
 
-  for (int it = 0; it < n_kv; ++it) {
-    if (it + 1 < n_kv) gload(it + 1);
-    const int kv0 = it * C::BN;
-    const char* kt = smem + (it & 1) * C::STAGE;
-    const char* vt = kt + C::KT;
-    const bool active = wave_live && (!a.causal || kv0 <= row0 + 31 + off);
-    if (active) {
-      // S^T (64 keys x 32 queries) = K Q^T, as two 32-key tiles
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kk = 0; kk < C::NK; ++kk) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const frag_t<T> kf = lds_row_frag<T>(kt + (32 * mt + c32) * C::KS + (16 * kk + 8 * g) * C::ES);
-          mma(s[mt], kf, qf[kk]);
-        }
-      }
-      const bool need_mask = (kv0 + C::BN > lk) || (a.causal && kv0 + C::BN - 1 > row0 + off);
-      // register r of tile mt holds key kv0 + 32*mt + 16*(r/8) + 8*g + r%8
-      if constexpr (ACT == 0) {
-        if (need_mask) {
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int j = kv0 + 32 * mt + 16 * (r >> 3) + 8 * g + (r & 7);
-              const bool masked = (j >= lk) || (a.causal && j > my_row + off);
-              s[mt][r] -= masked ? kMaskShift : 0.f;
-            }
-          }
-        }
-        // row max of the raw scores (the scale is positive), three at a time
-        float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-        mx = xor32_max(mx) * a.scale_log2;
-        // Rescale O and the sums only when the max grows by more than
-        // kLazyRescale (log2 units); otherwise keep the stale max, so the
-        // weights stay below 2^kLazyRescale.  Wave-uniform branch.
-        const bool grow = mx > m_run + kLazyRescale;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          // a row whose keys are all masked so far takes a max near -1.3e29;
-          // flooring it keeps its weights at exactly 0 (a live row's max is
-          // a real score, far above the floor)
-          const float m_use = grow ? fmaxf(mx, kMaxFloor) : m_run;
-          const float alpha = fast_exp2(m_run - m_use);
-          m_run = m_use;
-          l_run *= alpha;
-          l_used *= alpha;
-#pragma unroll
-          for (int i = 0; i < C::ND; ++i) o[i] *= alpha;
-        }
-        const float neg_m = -m_run;
+  // Softmax weights of tile j in s (in place), with the S^T MFMAs of tile
+  // j+1 (into s_nxt, when NEXT) interleaved with them, then
+  // O^T += V^T P^T for tile j.  MASK: tile j needs masking.  Both flags are
+  // compile-time so that the interleaved region has no branch.
+  auto tile_step = [&](auto MASK, auto NEXT, f32x16* s, f32x16* s_nxt, int j) {
+    constexpr bool kMask = decltype(MASK)::value;
+    constexpr bool kNext = decltype(NEXT)::value;
+    const int lim = row_limit - j * C::BN - 8 * g;   // masked iff key offset >= lim
+    if constexpr (ACT == 0) {
+      if constexpr (kMask) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(s[mt][r], a.scale_log2, neg_m));
-            l_run += p;
-            s[mt][r] = p;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float raw = s[mt][r];
-            const float sig = fast_rcp(1.0f + fast_exp2(-raw * a.scale_log2));
-            float y = raw * a.scale * sig * inv_lk;
-            if (need_mask) {
-              const int j = kv0 + 32 * mt + 16 * (r >> 3) + 8 * g + (r & 7);
-              const bool masked = (j >= lk) || (a.causal && j > my_row + off);
-              y = masked ? 0.f : y;
-            }
-            s[mt][r] = y;
+            const int ko = 32 * mt + 16 * (r >> 3) + (r & 7);
+            s[mt][r] -= (ko >= lim) ? kMaskShift : 0.f;
           }
         }
       }
-      // O^T (D x 32 queries) += V^T P^T; k-step (mt, ss) covers keys kv0 + 32*mt + 16*ss + 0..15
-      frag_t<T> pf[2][2];
+      // row max of the raw scores (the scale is positive)
+      float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      mx = xor32_max(mx) * a.scale_log2;
+      // Rescale O and the sums only when the max grows by more than
+      // kLazyRescale (log2 units); otherwise keep the stale max, so the
+      // weights stay below 2^kLazyRescale.  Wave-uniform branch.
+      const bool grow = mx > m_run + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        // a row whose keys are all masked so far takes a max near -1.3e29;
+        // flooring it keeps its weights at exactly 0 (a live row's max is
+        // a real score, far above the floor)
+        const float m_use = grow ? fmaxf(mx, kMaxFloor) : m_run;
+        const float alpha = fast_exp2(m_run - m_use);
+        m_run = m_use;
+        l_run *= alpha;
+        l_used *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::ND; ++i) o[i] *= alpha;
+      }
+    }
+    // --- straight-line region: next scores (MFMA) + weights (VALU) ---
+    if constexpr (kNext) scores(s_nxt, j + 1);
+    if constexpr (ACT == 0) {
+      const float neg_m = -m_run;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int ss = 0; ss < 2; ++ss) pf[mt][ss] = pack_frag<T>(s[mt], ss);
-      }
-      if constexpr (ACT == 0) {
-        // normalise by the sum of the weights the product really uses, so
-        // that O stays a convex combination of V rows after P is rounded
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-          for (int ss = 0; ss < 2; ++ss) frag_sum_into(l_used, pf[mt][ss]);
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[mt][r], a.scale_log2, neg_m));
+          l_run += p;
+          s[mt][r] = p;
         }
       }
+    } else {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-#pragma unroll
-          for (int dt = 0; dt < C::ND; ++dt) {
-            const frag_t<T> vf = lds_col_frag<T, C::VS, false>(vt, 32 * mt + 16 * ss, 32 * dt);
-            mma(o[dt], vf, pf[mt][ss]);
+        for (int r = 0; r < 16; ++r) {
+          const float raw = s[mt][r];
+          const float sig = fast_rcp(1.0f + fast_exp2(-raw * a.scale_log2));
+          float y = raw * a.scale * sig * inv_lk;
+          if constexpr (kMask) {
+            const int ko = 32 * mt + 16 * (r >> 3) + (r & 7);
+            y = (ko >= lim) ? 0.f : y;
           }
+          s[mt][r] = y;
         }
       }
     }
-    if (it + 1 < n_kv) lstore((it + 1) & 1);
+    frag_t<T> pf[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) pf[mt][ss] = pack_frag<T>(s[mt], ss);
+    }
+    // --- P V for tile j ---
+    if constexpr (ACT == 0) {
+      // normalise by the sum of the weights the product really uses, so
+      // that O stays a convex combination of V rows after P is rounded
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) frag_sum_into(l_used, pf[mt][ss]);
+      }
+    }
+    const char* vt = vslot0 + (j & 1) * C::KT;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+        for (int dt = 0; dt < C::ND; ++dt) {
+          const frag_t<T> vf = lds_col_frag<T, D, false>(vt, 32 * mt + 16 * ss, 32 * dt);
+          mma(o[dt], vf, pf[mt][ss]);
+        }
+      }
+    }
+  };
+
+  // One pipelined step for key tile j: start the copies of K(j+2) and
+  // V(j+1), compute the scores of tile j+1 (MFMA) while the weights of tile
+  // j are formed (VALU), accumulate P V for tile j, then wait and barrier.
+  // Slot reuse: K(j+2) overwrites K(j), whose scores were formed in the
+  // previous step; V(j+1) overwrites V(j-1), consumed in the previous step.
+  auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
+    if (j + 2 < n_kv) kdma.issue(kslot0 + (j & 1) * C::KT, kb, rs, (j + 2) * C::BN, lk, tid);
+    if (j + 1 < n_kv) vdma.issue(vslot0 + ((j + 1) & 1) * C::KT, vb, rs, (j + 1) * C::BN, lk, tid);
+    const bool nxt = j + 1 < n_kv && wave_active(j + 1);
+    if (wave_active(j)) {
+      const bool msk = needs_mask(j);
+      if (nxt) {
+        if (msk) tile_step(std::true_type{}, std::true_type{}, s_cur, s_nxt, j);
+        else tile_step(std::false_type{}, std::true_type{}, s_cur, s_nxt, j);
+      } else {
+        if (msk) tile_step(std::true_type{}, std::false_type{}, s_cur, s_nxt, j);
+        else tile_step(std::false_type{}, std::false_type{}, s_cur, s_nxt, j);
+      }
+    } else if (nxt) {
+      scores(s_nxt, j + 1);
+    }
+    dma_wait();
     __syncthreads();
+  };
+
+  dma_wait();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (n_kv > 0 && wave_active(0)) scores(sa, 0);
+  // the first step copies K(2) over K(0): every wave must be done reading it
+  __syncthreads();
+  for (int j = 0; j < n_kv; j += 2) {
+    step(j, sa, sb);
+    if (j + 1 < n_kv) step(j + 1, sb, sa);
   }
 
   if (!wave_live) return;
@@ -212,6 +259,15 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
     a.lse[(size_t)h * a.total_q + qs + my_row] = row_live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
+
+// Explicit instantiation of every variant (the host pass otherwise left some
+// kernel stubs undefined).
+#define JFA_FWD_INST(T, D, ACT) template __global__ void fwd_kernel<T, D, ACT>(FwdArgs);
+JFA_FWD_INST(__bf16, 32, 0) JFA_FWD_INST(__bf16, 64, 0) JFA_FWD_INST(__bf16, 128, 0)
+JFA_FWD_INST(__bf16, 32, 1) JFA_FWD_INST(__bf16, 64, 1) JFA_FWD_INST(__bf16, 128, 1)
+JFA_FWD_INST(float, 32, 0) JFA_FWD_INST(float, 64, 0) JFA_FWD_INST(float, 128, 0)
+JFA_FWD_INST(float, 32, 1) JFA_FWD_INST(float, 64, 1) JFA_FWD_INST(float, 128, 1)
+#undef JFA_FWD_INST
 
 template <typename T, int D, int ACT>
 static hipError_t launch_one(const FwdArgs& a, int64_t grid, hipStream_t stream) {

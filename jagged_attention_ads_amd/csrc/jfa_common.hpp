@@ -121,15 +121,61 @@ __device__ __forceinline__ void frag_sum_into(float& acc, const f32x8& f) {
 
 // ---------------------------------------------------------------- LDS access
 
-// 8 consecutive elements of one LDS row.
-template <typename T>
-__device__ __forceinline__ frag_t<T> lds_row_frag(const char* p) {
+// Dense LDS tiles of D-element rows, addressed in 16-byte chunks whose index
+// is XOR-swizzled with a function of the row.  With 64 banks of 4 bytes a
+// 256-byte line is served per cycle; the swizzle makes both read patterns
+// of the kernels hit 16 distinct 16-byte bank groups:
+//   - 16 consecutive rows, one chunk each (A/B operand rows, ds_read_b128);
+//   - 4 consecutive aligned rows, 4 consecutive aligned chunks each
+//     (transposed operand reads, ds_read_b64_tr_b16 over a half-wave).
+template <typename T, int D>
+struct Swz {
+  static constexpr int CH = D * (int)sizeof(T) / 16;   // chunks per row
+  static constexpr int ROW_BYTES = CH * 16;
+  // byte offset of chunk c of row r
+  __device__ static __forceinline__ int off(int r, int c) {
+    if constexpr (CH >= 16) {
+      const int g = ((r & 3) << 2) ^ ((r >> 2) & 3);
+      return r * ROW_BYTES + ((c & ~15) | ((c & 15) ^ g)) * 16;
+    } else if constexpr (CH == 8) {            // two rows per 256-byte line
+      const int line = r >> 1;
+      const int g = ((line & 1) << 2) ^ ((line >> 1) & 3);
+      return line * 256 + (((r & 1) << 3) | (c ^ g)) * 16;
+    } else {                                   // CH == 4: four rows per line
+      static_assert(CH == 4, "unsupported row size");
+      const int line = r >> 2;
+      return line * 256 + (((r & 3) << 2) | (c ^ (line & 3))) * 16;
+    }
+  }
+  static constexpr int tile_bytes(int rows) { return rows * ROW_BYTES; }
+  // inverse: physical 16-byte chunk index p -> (row r, chunk c)
+  __device__ static __forceinline__ void inv(int p, int& r, int& c) {
+    if constexpr (CH >= 16) {
+      r = p / CH;
+      const int g = ((r & 3) << 2) ^ ((r >> 2) & 3);
+      const int q = p % CH;
+      c = (q & ~15) | ((q & 15) ^ g);
+    } else if constexpr (CH == 8) {
+      const int line = p >> 4;
+      r = 2 * line + ((p >> 3) & 1);
+      c = (p & 7) ^ (((line & 1) << 2) ^ ((line >> 1) & 3));
+    } else {
+      const int line = p >> 4;
+      r = 4 * line + ((p >> 2) & 3);
+      c = (p & 3) ^ (line & 3);
+    }
+  }
+};
+
+// 8 consecutive elements (col .. col+7, col a multiple of 8) of one row.
+template <typename T, int D>
+__device__ __forceinline__ frag_t<T> lds_row_frag(const char* tile, int row, int col) {
+  using S = Swz<T, D>;
   if constexpr (sizeof(T) == 2) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + S::off(row, col >> 3)));
   } else {
-    // rows are only 16-byte aligned: two 16-byte reads
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
+    const u32x4 a = *reinterpret_cast<const u32x4*>(tile + S::off(row, col >> 2));
+    const u32x4 b = *reinterpret_cast<const u32x4*>(tile + S::off(row, (col >> 2) + 1));
     f32x8 f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -140,12 +186,13 @@ __device__ __forceinline__ frag_t<T> lds_row_frag(const char* p) {
   }
 }
 
-// Transposed fragment of a row-major LDS tile: lane l gets the elements at
-// logical rows row0 + 8*(l/32) + 0..7 of column col0 + l%32.  `rowmap`
-// maps a logical row to its stored row; it must keep aligned groups of four
-// rows together (swap23 and the identity do).
-template <typename T, int STRIDE, bool SWAPPED>
+// Transposed fragment: lane l gets the elements at logical rows
+// row0 + 8*(l/32) + 0..7 of column col0 + l%32 (row0 a multiple of 8, col0
+// a multiple of 32).  With SWAPPED, logical row r is stored at row swap23(r)
+// (swap23 keeps aligned groups of four rows together).
+template <typename T, int D, bool SWAPPED>
 __device__ __forceinline__ frag_t<T> lds_col_frag(const char* tile, int row0, int col0) {
+  using S = Swz<T, D>;
   const int l = lane_id();
   if constexpr (sizeof(T) == 2) {
     // ds_read_b64_tr_b16 (layout checked on the hardware): within each
@@ -154,13 +201,14 @@ __device__ __forceinline__ frag_t<T> lds_col_frag(const char* tile, int row0, in
     // rows r0 .. r0+3.  Two reads give the 8 rows of a fragment.
     const int blk = l >> 4, s = l & 15;
     const int g = blk >> 1, half = blk & 1;
-    const int col = col0 + 16 * half + 4 * (s & 3);
+    const int col = col0 + 16 * half + 4 * (s & 3);      // element column
+    const int chunk = col >> 3, within = (col & 7) * 2;  // 16-byte chunk, byte in it
     u32x2 w[2];
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
       int row = row0 + 8 * g + 4 * rd + (s >> 2);
       if (SWAPPED) row = swap23(row);
-      const char* p = tile + row * STRIDE + col * 2;
+      const char* p = tile + S::off(row, chunk) + within;
       // whole 32-bit words only: per-element bf16 extraction of this
       // builtin's result is not compiled correctly by this toolchain
       w[rd] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((JFA_LDS i16x4*)(p)));
@@ -174,7 +222,7 @@ __device__ __forceinline__ frag_t<T> lds_col_frag(const char* tile, int row0, in
     for (int e = 0; e < 8; ++e) {
       int row = row0 + 8 * g + e;
       if (SWAPPED) row = swap23(row);
-      f[e] = *reinterpret_cast<const float*>(tile + row * STRIDE + c * 4);
+      f[e] = *reinterpret_cast<const float*>(tile + S::off(row, c >> 2) + (c & 3) * 4);
     }
     return f;
   }
@@ -197,35 +245,88 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 
 // ---------------------------------------------------------------- tile staging
 
-// A ROWS x D tile of one head, read from global memory into registers (16
-// bytes per access, rows clamped into the sequence so nothing outside it is
-// ever read) and written to a row-major LDS tile of STRIDE bytes per row.
-// With SWAP, row r is stored at row swap23(r).
-template <typename T, int D, int ROWS, int STRIDE, bool SWAP, int NT = 256>
+// Buffer-resource word 3 for raw (untyped, unswizzled) dword buffer access.
+constexpr int kBufferWord3 = 0x00020000;
+
+// A ROWS x D tile of one head read from global memory into registers with
+// raw buffer loads (16 bytes per access) and written to a swizzled LDS tile.
+// The buffer of each load covers only the rows that belong to the sequence,
+// so rows past its end read as zeros: nothing outside the sequence is read,
+// and no per-row clamp or 64-bit address arithmetic is needed.  With SWAP,
+// row r is stored at row swap23(r).
+template <typename T, int D, int ROWS, bool SWAP, int NT = 256>
 struct TileStage {
-  static constexpr int CH = D * (int)sizeof(T) / 16;
+  using S = Swz<T, D>;
+  static constexpr int CH = S::CH;
   static constexpr int N = ROWS * CH / NT;
   static_assert(ROWS * CH % NT == 0, "tile must split evenly over the threads");
   u32x4 r[N];
 
-  // rows row0 .. row0+ROWS-1 of a sequence of `nrows` rows (nrows >= 1)
-  __device__ __forceinline__ void load(const T* base, size_t row_stride, int row0, int nrows, int tid) {
+  // rows row0 .. row0+ROWS-1 of a sequence whose row j starts at
+  // base + j*row_stride elements and which has nrows rows (row0 < nrows)
+  __device__ __forceinline__ void load(const T* base, int row_stride, int row0, int nrows, int tid) {
+    const int valid = min(ROWS, nrows - row0);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(base + (size_t)row0 * row_stride), 0, valid * row_stride * (int)sizeof(T), kBufferWord3);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int c = tid + i * NT, row = c / CH, col = c % CH;
-      const int j = min(row0 + row, nrows - 1);
-      r[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base + (size_t)j * row_stride) + col * 16);
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rsrc, row * row_stride * (int)sizeof(T) + col * 16, 0, 0));
     }
   }
   __device__ __forceinline__ void store(char* tile, int tid) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int c = tid + i * NT, row = c / CH, col = c % CH;
-      const int rr = SWAP ? swap23(row) : row;
-      *reinterpret_cast<u32x4*>(tile + rr * STRIDE + col * 16) = r[i];
+      *reinterpret_cast<u32x4*>(tile + S::off(SWAP ? swap23(row) : row, col)) = r[i];
     }
   }
 };
+
+// A ROWS x D tile of one head copied straight from global memory into a
+// swizzled LDS tile with buffer loads that write LDS (no register staging).
+// Each such load writes its 64 lanes' 16-byte chunks to 1 KB of consecutive
+// LDS, so every lane loads the global chunk that the swizzle maps to its LDS
+// slot.  Rows past the sequence's end read as zeros (the buffer covers only
+// the sequence's rows).  With SWAP, LDS row r holds tile row swap23(r).
+// Completion is tracked by the wave's vector-memory counter: wait for it
+// (dma_wait) and then barrier before any wave reads the tile.
+template <typename T, int D, int ROWS, bool SWAP, int NT = 256>
+struct TileDma {
+  using S = Swz<T, D>;
+  static constexpr int CH = S::CH;
+  static constexpr int N = ROWS * CH / NT;   // loads per thread per tile
+  static_assert(ROWS * CH % NT == 0, "tile must split evenly over the threads");
+  int voff[N];                               // per-thread byte offsets into the tile's rows
+
+  __device__ __forceinline__ void init(int row_stride, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int r, c;
+      S::inv(i * NT + tid, r, c);
+      const int row = SWAP ? swap23(r) : r;
+      voff[i] = row * row_stride * (int)sizeof(T) + c * 16;
+    }
+  }
+  // rows row0 .. row0+ROWS-1 of a sequence whose row j starts at
+  // base + j*row_stride elements and which has nrows rows (row0 < nrows)
+  __device__ __forceinline__ void issue(char* tile, const T* base, int row_stride, int row0, int nrows,
+                                        int tid) const {
+    const int valid = min(ROWS, nrows - row0);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(base + (size_t)row0 * row_stride), 0, valid * row_stride * (int)sizeof(T), kBufferWord3);
+    const int wave_base = (tid & ~(kWave - 1)) * 16;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (JFA_LDS void*)(tile + i * NT * 16 + wave_base), 16, voff[i], 0,
+                                               0, 0);
+    }
+  }
+};
+
+// Wait until this wave's outstanding global->LDS copies have landed.
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <typename T>
 __device__ __forceinline__ frag_t<T> global_frag(const T* p) {
