@@ -26,7 +26,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
   jfa::WorklistLayout wq{}, wkv{};
-  size_t off_wq = 0, off_wkv = 0, off_delta = 0, bytes = 0;
+  size_t off_wq = 0, off_wkv = 0, off_stats = 0, bytes = 0;
 };
 
 WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv, bool backward) {
@@ -38,8 +38,8 @@ WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_
     L.wkv = jfa::worklist_layout(jfa::kPassKV, batch, heads, total_kv);
     L.off_wkv = off;
     off += L.wkv.bytes;
-    L.off_delta = off;
-    off += align256(static_cast<size_t>(heads) * static_cast<size_t>(total_q) * sizeof(float));
+    L.off_stats = off;
+    off += align256(static_cast<size_t>(heads) * static_cast<size_t>(total_q) * 2 * sizeof(float));
   }
   L.bytes = off;
   return L;
@@ -256,7 +256,7 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   a.n_items_q = reinterpret_cast<const int32_t*>(ws + L.off_wq);
   a.items_kv = reinterpret_cast<const int2*>(ws + L.off_wkv + L.wkv.items_off);
   a.n_items_kv = reinterpret_cast<const int32_t*>(ws + L.off_wkv);
-  a.delta = reinterpret_cast<float*>(ws + L.off_delta);
+  a.stats = reinterpret_cast<float2*>(ws + L.off_stats);
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

@@ -7,19 +7,28 @@
 // two passes so that every output row is owned by exactly one workgroup and
 // stored once:
 //   dK/dV pass -- one work item per (sequence, head, 128-key tile); each wave
-//     owns 32 keys (its K and V rows live in registers) and walks the
-//     64-query blocks that see them, staged in swizzled LDS tiles.  P and dS are recomputed
-//     from lse (softmax) or from the scores (SiLU).
+//     owns 32 keys (its K and V rows live in registers) and walks the query
+//     rows that see them in 32-row sub-blocks.  P and dS are recomputed from
+//     lse (softmax) or from the scores (SiLU).
 //   dQ pass -- one work item per (sequence, head, 128-query tile); each wave
-//     owns 32 queries and walks the 64-key blocks that they see.
+//     owns 32 queries and walks the keys they see in 32-key sub-blocks.
 // A preprocess kernel first forms delta_i = sum_c dO_ic O_ic (softmax only),
-// the row sum of P o dP that the softmax Jacobian needs.
+// the row sum of P o dP that the softmax Jacobian needs, and stores it next to
+// lse_i * log2(e).
+//
+// Both passes stream the operand they walk (Q and dO, or K and V) from HBM
+// straight into a ring of four swizzled LDS stages, two stages ahead of use
+// (buffer loads that write LDS), and are software-pipelined: the S and dP
+// products of the next sub-block run on the matrix cores while P and dS of
+// the current one are formed on the vector ALUs.
 //
 // Per (query i, key j) pair, with x = scale * q_i.k_j:
 //   softmax: P = exp(x - lse_i);        dS = P (dP - delta_i)
 //   silu:    P = silu(x) / Lk;          dS = dP silu'(x) / Lk,
 //            silu'(x) = sig(x) (1 + x (1 - sig(x)))
 //   dV_j += P dO_i,  dP = dO_i . V_j,  dK_j += scale dS q_i,  dQ_i += scale dS k_j
+#include <type_traits>
+
 #include "jfa_common.hpp"
 #include "jfa_internal.h"
 
@@ -27,9 +36,14 @@ namespace jfa {
 
 // ---------------------------------------------------------------- delta
 
+// lse in log2 units, with rows that see no key (lse = -inf) mapped to 0:
+// those rows are fully masked, and a finite value keeps every product finite.
+__device__ __forceinline__ float lse_log2(float lse) { return lse > -INFINITY ? lse * kLog2e : 0.f; }
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out, const T* __restrict__ dout,
-                                                      float* __restrict__ delta, int heads, int total_q) {
+                                                      const float* __restrict__ lse, float2* __restrict__ stats,
+                                                      int heads, int total_q) {
   constexpr int LPR = D * (int)sizeof(T) / 16;   // lanes per (row, head)
   constexpr int RPB = 256 / LPR;                 // (row, head) pairs per block
   const int sub = threadIdx.x % LPR;
@@ -55,23 +69,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
   for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, kWave);
   if (pair < npairs && sub == 0) {
     const int64_t row = pair / heads, head = pair % heads;
-    delta[head * total_q + row] = acc;
+    const size_t i = (size_t)head * total_q + row;
+    stats[i] = make_float2(lse_log2(lse[i]), acc);
   }
 }
 
 // ---------------------------------------------------------------- shared math
 
-// lse in log2 units, with rows that see no key (lse = -inf) mapped to 0:
-// those rows are fully masked, and a finite value keeps exp2 at exactly 0.
-__device__ __forceinline__ float lse_log2(float lse) { return lse > -INFINITY ? lse * kLog2e : 0.f; }
-
-// P and dS of one score, softmax (ACT 0) or silu (ACT 1).
+// P and dS of one score, softmax (ACT 0) or silu (ACT 1); masked pairs give 0.
 template <int ACT>
 __device__ __forceinline__ void p_ds(float raw, float dp, float lse2, float delta, float scale, float scale_log2,
                                      float inv_lk, bool masked, float& p, float& ds) {
   if constexpr (ACT == 0) {
-    const float x = raw * scale_log2 - lse2 - (masked ? kMaskShift : 0.f);
-    p = fast_exp2(x);
+    const float e = fast_exp2(fmaf(raw, scale_log2, -lse2));
+    p = masked ? 0.f : e;
     ds = p * (dp - delta);
   } else {
     const float x = raw * scale;
@@ -82,21 +93,54 @@ __device__ __forceinline__ void p_ds(float raw, float dp, float lse2, float delt
   }
 }
 
+// Calls f(std::integral_constant<bool, A>, std::integral_constant<bool, B>):
+// two runtime flags turned into compile-time ones, so that the code region
+// they select is straight-line.
+template <typename F>
+__device__ __forceinline__ void with_flags(bool a, bool b, F&& f) {
+  if (a) {
+    if (b) f(std::true_type{}, std::true_type{});
+    else f(std::true_type{}, std::false_type{});
+  } else {
+    if (b) f(std::false_type{}, std::true_type{});
+    else f(std::false_type{}, std::false_type{});
+  }
+}
+
+// Ring of LDS stages fed two stages ahead.  Stage s lives in slot s % 4.
+// When stage s is opened (wait + barrier), every wave has finished with
+// stage s-2 (the pipeline reads at most stages s-1 and s from then on), so
+// its slot is refilled with stage s+2 right after the barrier.
+constexpr int kStages = 4;
+
+// Waits until stage s has landed while `ahead` (0..2) later stages, of
+// N copies each per thread, may still be in flight.
+template <int N>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if (ahead >= 2) dma_wait_all_but<2 * N>();
+  else if (ahead == 1) dma_wait_all_but<N>();
+  else dma_wait_all_but<0>();
+}
+
 // ---------------------------------------------------------------- dK / dV
 
 template <typename T, int D>
 struct DkdvCfg {
-  static constexpr int BN = kBwdBN, BM = kBwdBM, NT = 256;
+  static constexpr int BN = kBwdBN, NT = 256;
   static constexpr int ES = sizeof(T);
-  static constexpr int QT = Swz<T, D>::tile_bytes(BM);   // Q / dO tile
-  static constexpr int STAGE = 2 * QT + 2 * BM * 4;   // Q, dO, lse2, delta
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int SR = (D * ES <= 256) ? 64 : 32;   // query rows per stage
+  static constexpr int SPS = SR / 32;                    // 32-row sub-blocks per stage
+  static constexpr int QT = Swz<T, D>::tile_bytes(SR);   // Q or dO tile
+  static constexpr int STAGE = 2 * QT + 1024;            // Q, dO, row statistics
+  static constexpr int LDS = kStages * STAGE;
   static constexpr int ND = D / 32, NK = D / 16;
 };
 
 template <typename T, int D, int ACT>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<T, D>;
+  using Dma = TileDma<T, D, C::SR, true>;   // query rows stored swap23-permuted
+  constexpr int NPS = 2 * Dma::N + (ACT == 0 ? 1 : 0);   // copies per thread per stage
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
   if ((int)blockIdx.x >= *a.n_items_kv) return;
@@ -110,9 +154,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   const int kw0 = t * C::BN + 32 * w;    // first key of this wave
   const int my_key = kw0 + c32;          // the key this lane owns (its column of S)
   const bool wave_live = kw0 < lk;
-  const int nqb = kv_tile_q_blocks(lq, lk, t, C::BM, C::BN, a.causal);
-  const int qb_first = kv_tile_first_q_block(lq, lk, t, C::BM, C::BN, a.causal);
-  const size_t rs = (size_t)a.heads * D;
+  const int nst = kv_tile_q_blocks(lq, lk, t, C::SR, C::BN, a.causal);
+  const int q_first = kv_tile_first_q_block(lq, lk, t, C::SR, C::BN, a.causal) * C::SR;
+  const int nsub = nst * C::SPS;
+  const int rs = a.heads * D;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
 
   // this lane's key and value rows as B-operand fragments (d-slots 16*kk + 8*g + e)
@@ -127,6 +172,23 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       vf[kk] = global_frag<T>(vp + 16 * kk);
     }
   }
+
+  const T* qb = static_cast<const T*>(a.q) + (size_t)qs * rs + (size_t)h * D;
+  const T* db = static_cast<const T*>(a.dout) + (size_t)qs * rs + (size_t)h * D;
+  const float2* stats_h = ACT == 0 ? a.stats + (size_t)h * a.total_q + qs : nullptr;
+  Dma dma;   // Q and dO tiles share the geometry, hence the offsets
+  dma.init(rs, tid);
+  auto slot = [&](int s) { return smem + (s & (kStages - 1)) * C::STAGE; };
+  auto issue_stage = [&](int s) {
+    char* st = slot(s);
+    const int r0 = q_first + s * C::SR;
+    dma.issue(st, qb, rs, r0, lq, tid);
+    dma.issue(st + C::QT, db, rs, r0, lq, tid);
+    if constexpr (ACT == 0) stats_dma(st + 2 * C::QT, stats_h, r0, min(C::SR, lq - r0));
+  };
+  const int pro = min(kStages - 2, nst - 1);   // last stage the prologue issues
+  for (int s = 0; s <= pro; ++s) issue_stage(s);
+
   f32x16 dk[C::ND], dv[C::ND];
 #pragma unroll
   for (int i = 0; i < C::ND; ++i) {
@@ -134,93 +196,110 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
 
-  const T* qb = static_cast<const T*>(a.q) + (size_t)qs * rs + (size_t)h * D;
-  const T* db = static_cast<const T*>(a.dout) + (size_t)qs * rs + (size_t)h * D;
-  const float* lse_h = ACT == 0 ? a.lse + (size_t)h * a.total_q + qs : nullptr;
-  const float* del_h = ACT == 0 ? a.delta + (size_t)h * a.total_q + qs : nullptr;
-
-  TileStage<T, D, C::BM, true> qst, dst;   // query rows stored swap23-permuted
-  float st_lse = 0.f, st_del = 0.f;
-  auto gload = [&](int qblk) {
-    const int r0 = qblk * C::BM;
-    qst.load(qb, (int)rs, r0, lq, tid);
-    dst.load(db, (int)rs, r0, lq, tid);
-    if (ACT == 0 && tid < C::BM) {
-      const int r = min(r0 + tid, lq - 1);
-      st_lse = lse_log2(lse_h[r]);
-      st_del = del_h[r];
-    }
+  // a wave takes part in sub-block n iff it has rows and some see its keys
+  auto visible = [&](int n) {
+    const int qa = q_first + 32 * n;
+    return wave_live && qa < lq && !(a.causal && qa + 31 + off < kw0);
   };
-  auto lstore = [&](int buf) {
-    char* st = smem + buf * C::STAGE;
-    qst.store(st, tid);
-    dst.store(st + C::QT, tid);
-    if (ACT == 0 && tid < C::BM) {
-      reinterpret_cast<float*>(st + 2 * C::QT)[tid] = st_lse;
-      reinterpret_cast<float*>(st + 2 * C::QT + C::BM * 4)[tid] = st_del;
-    }
+  auto needs_mask = [&](int n) {
+    const int qa = q_first + 32 * n;
+    return (qa + 32 > lq) || (kw0 + 32 > lk) || (a.causal && kw0 + 31 > qa + off);
   };
 
-  if (nqb > 0) {
-    gload(qb_first);
-    lstore(0);
-  }
-  __syncthreads();
+  // S and dP (32 queries x 32 keys) of sub-block n; register r holds query
+  // q_first + 32*n + 16*(r/8) + 8*g + r%8
+  auto products = [&](f32x16& s, f32x16& dp, int n) {
+    const char* qt = slot(n / C::SPS);
+    const char* dt = qt + C::QT;
+    const int rl = 32 * (n % C::SPS);
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) {
+      mma(s, lds_row_frag<T, D>(qt, rl + c32, 16 * kk + 8 * g), kf[kk]);
+      mma(dp, lds_row_frag<T, D>(dt, rl + c32, 16 * kk + 8 * g), vf[kk]);
+    }
+  };
 
-  for (int it = 0; it < nqb; ++it) {
-    const int qblk = qb_first + it;
-    if (it + 1 < nqb) gload(qblk + 1);
-    const char* st = smem + (it & 1) * C::STAGE;
-    const char* qt = st;
-    const char* dt_ = st + C::QT;
-    const float* lse2 = reinterpret_cast<const float*>(st + 2 * C::QT);
-    const float* dlt = lse2 + C::BM;
-    if (wave_live) {
+  // P and dS of sub-block n from s, dp (in place), with the products of
+  // sub-block n+1 (when NEXT) interleaved, then dV^T += dO^T P and
+  // dK^T += Q^T dS.  MASK and NEXT are compile-time: the region is
+  // straight-line.
+  auto sub_step = [&](auto MASK, auto NEXT, f32x16& s, f32x16& dp, f32x16& s_nxt, f32x16& dp_nxt, int n) {
+    constexpr bool kMask = decltype(MASK)::value;
+    constexpr bool kNext = decltype(NEXT)::value;
+    const char* qt = slot(n / C::SPS);
+    const char* dt = qt + C::QT;
+    const int rl = 32 * (n % C::SPS);
+    const int qa = q_first + 32 * n;
+    // lse2 and delta of this lane's 16 rows rl + 16*(r/8) + 8*g + r%8
+    float l2[16], de[16];
+    if constexpr (ACT == 0) {
+      const char* sp = qt + 2 * C::QT + (rl + 8 * g) * (int)sizeof(float2);
 #pragma unroll
-      for (int sb = 0; sb < C::BM / 32; ++sb) {
-        const int qa = qblk * C::BM + 32 * sb;   // first query row of the sub-block
-        if (qa >= lq) break;
-        if (a.causal && qa + 31 + off < kw0) continue;   // no row here sees this wave's keys
-        // S and dP (32 queries x 32 keys); register r holds query qa + 16*(r/8) + 8*g + r%8
-        f32x16 s = f32x16{}, dp = f32x16{};
+      for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-        for (int kk = 0; kk < C::NK; ++kk) {
-          const frag_t<T> qfr = lds_row_frag<T, D>(qt, 32 * sb + c32, 16 * kk + 8 * g);
-          mma(s, qfr, kf[kk]);
-          const frag_t<T> dfr = lds_row_frag<T, D>(dt_, 32 * sb + c32, 16 * kk + 8 * g);
-          mma(dp, dfr, vf[kk]);
-        }
-        const bool need_mask = (qa + 32 > lq) || (kw0 + 32 > lk) || (a.causal && kw0 + 31 > qa + off);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = 16 * (r >> 3) + 8 * g + (r & 7);   // row within the sub-block
-          const int i = qa + qi;
-          bool masked = false;
-          if (need_mask) masked = (i >= lq) || (my_key >= lk) || (a.causal && my_key > i + off);
-          float p, ds;
-          const float l2 = ACT == 0 ? lse2[32 * sb + qi] : 0.f;
-          const float de = ACT == 0 ? dlt[32 * sb + qi] : 0.f;
-          p_ds<ACT>(s[r], dp[r], l2, de, a.scale, a.scale_log2, inv_lk, masked, p, ds);
-          s[r] = p;
-          dp[r] = ds;
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS; k-step ss covers rows 16*ss .. +15 of the sub-block
-#pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          const frag_t<T> pf = pack_frag<T>(s, ss);
-          const frag_t<T> sf = pack_frag<T>(dp, ss);
-#pragma unroll
-          for (int d2 = 0; d2 < C::ND; ++d2) {
-            const frag_t<T> dof = lds_col_frag<T, D, true>(dt_, 32 * sb + 16 * ss, 32 * d2);
-            mma(dv[d2], dof, pf);
-            const frag_t<T> qtf = lds_col_frag<T, D, true>(qt, 32 * sb + 16 * ss, 32 * d2);
-            mma(dk[d2], qtf, sf);
-          }
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sp + (16 * h2 + 2 * q2) * (int)sizeof(float2));
+          l2[8 * h2 + 2 * q2] = v[0];
+          de[8 * h2 + 2 * q2] = v[1];
+          l2[8 * h2 + 2 * q2 + 1] = v[2];
+          de[8 * h2 + 2 * q2 + 1] = v[3];
         }
       }
     }
-    if (it + 1 < nqb) lstore((it + 1) & 1);
-    __syncthreads();
+    if constexpr (kNext) products(s_nxt, dp_nxt, n + 1);
+    // row qi = 16*(r/8) + r%8 + 8*g of the sub-block is visible to this
+    // lane's key iff lo <= qi < lo + span (one unsigned compare)
+    const int lo = (a.causal ? my_key - off : 0) - qa - 8 * g;
+    const int span = max((my_key < lk) ? (lq - qa - 8 * g) - lo : 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 16 * (r >> 3) + (r & 7);
+      bool masked = false;
+      if constexpr (kMask) masked = (unsigned)(c - lo) >= (unsigned)span;
+      float p, ds;
+      p_ds<ACT>(s[r], dp[r], ACT == 0 ? l2[r] : 0.f, ACT == 0 ? de[r] : 0.f, a.scale, a.scale_log2, inv_lk,
+                masked, p, ds);
+      s[r] = p;
+      dp[r] = ds;
+    }
+    // k-step ss covers rows 16*ss .. +15 of the sub-block
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const frag_t<T> pf = pack_frag<T>(s, ss);
+      const frag_t<T> sf = pack_frag<T>(dp, ss);
+#pragma unroll
+      for (int d2 = 0; d2 < C::ND; ++d2) {
+        mma(dv[d2], lds_col_frag<T, D, true>(dt, rl + 16 * ss, 32 * d2), pf);
+        mma(dk[d2], lds_col_frag<T, D, true>(qt, rl + 16 * ss, 32 * d2), sf);
+      }
+    }
+  };
+
+  auto iter = [&](int n, f32x16& s, f32x16& dp, f32x16& s_nxt, f32x16& dp_nxt) {
+    const bool has_next = n + 1 < nsub;
+    if (has_next && (n + 1) % C::SPS == 0) {   // sub-block n+1 opens stage st
+      const int st = (n + 1) / C::SPS;
+      wait_stage<NPS>(min(kStages - 3, nst - 1 - st));
+      __syncthreads();
+      if (st + kStages - 2 < nst) issue_stage(st + kStages - 2);
+    }
+    const bool nxt = has_next && visible(n + 1);
+    if (visible(n)) {
+      with_flags(needs_mask(n), nxt, [&](auto MASK, auto NEXT) { sub_step(MASK, NEXT, s, dp, s_nxt, dp_nxt, n); });
+    } else if (nxt) {
+      products(s_nxt, dp_nxt, n + 1);
+    }
+  };
+
+  if (nst > 0) wait_stage<NPS>(pro);
+  __syncthreads();
+  f32x16 sa, da, sb, db_;
+  if (nsub > 0 && visible(0)) products(sa, da, 0);
+  for (int n = 0; n < nsub; n += 2) {
+    iter(n, sa, da, sb, db_);
+    if (n + 1 < nsub) iter(n + 1, sb, db_, sa, da);
   }
 
   if (!wave_live || my_key >= lk) return;
@@ -234,17 +313,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
 
 template <typename T, int D>
 struct DqCfg {
-  static constexpr int BM = kFwdBM, BN = kFwdBN, NT = 256;
+  static constexpr int BM = kFwdBM, NT = 256;
   static constexpr int ES = sizeof(T);
-  static constexpr int KT = Swz<T, D>::tile_bytes(BN);   // K / V tile
+  static constexpr int SR = (D * ES >= 128) ? 32 : 64;   // key rows per stage (>= 256 chunks)
+  static constexpr int SPS = SR / 32;                    // 32-key sub-blocks per stage
+  static constexpr int KT = Swz<T, D>::tile_bytes(SR);   // K or V tile
   static constexpr int STAGE = 2 * KT;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = kStages * STAGE;
   static constexpr int ND = D / 32, NK = D / 16;
 };
 
 template <typename T, int D, int ACT>
-__global__ __launch_bounds__(256, (D >= 128 || sizeof(T) == 4) ? 1 : 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void dq_kernel(BwdArgs a) {
   using C = DqCfg<T, D>;
+  using Dma = TileDma<T, D, C::SR, true>;   // key rows stored swap23-permuted
+  constexpr int NPS = 2 * Dma::N;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
   if ((int)blockIdx.x >= *a.n_items_q) return;
@@ -258,8 +341,9 @@ __global__ __launch_bounds__(256, (D >= 128 || sizeof(T) == 4) ? 1 : 2) void dq_
   const int row0 = t * C::BM + 32 * w;
   const int my_row = row0 + c32;
   const bool wave_live = row0 < lq;
-  const int n_kv = q_tile_kv_blocks(lq, lk, t, C::BM, C::BN, a.causal);
-  const size_t rs = (size_t)a.heads * D;
+  const int nst = q_tile_kv_blocks(lq, lk, t, C::BM, C::SR, a.causal);
+  const int nsub = nst * C::SPS;
+  const int rs = a.heads * D;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
 
   frag_t<T> qf[C::NK], df[C::NK];
@@ -274,87 +358,114 @@ __global__ __launch_bounds__(256, (D >= 128 || sizeof(T) == 4) ? 1 : 2) void dq_
       df[kk] = global_frag<T>(dp + 16 * kk);
     }
     if (ACT == 0) {
-      lse2 = lse_log2(a.lse[(size_t)h * a.total_q + qs + r]);
-      dlt = a.delta[(size_t)h * a.total_q + qs + r];
+      const float2 st = a.stats[(size_t)h * a.total_q + qs + r];
+      lse2 = st.x;
+      dlt = st.y;
     }
   }
+
+  const T* kb = static_cast<const T*>(a.k) + (size_t)ks * rs + (size_t)h * D;
+  const T* vb = static_cast<const T*>(a.v) + (size_t)ks * rs + (size_t)h * D;
+  Dma dma;   // K and V tiles share the geometry
+  dma.init(rs, tid);
+  auto slot = [&](int s) { return smem + (s & (kStages - 1)) * C::STAGE; };
+  auto issue_stage = [&](int s) {
+    char* st = slot(s);
+    dma.issue(st, kb, rs, s * C::SR, lk, tid);
+    dma.issue(st + C::KT, vb, rs, s * C::SR, lk, tid);
+  };
+  const int pro = min(kStages - 2, nst - 1);
+  for (int s = 0; s <= pro; ++s) issue_stage(s);
+
   f32x16 dq[C::ND];
 #pragma unroll
   for (int i = 0; i < C::ND; ++i) dq[i] = f32x16{};
 
-  const T* kb = static_cast<const T*>(a.k) + (size_t)ks * rs + (size_t)h * D;
-  const T* vb = static_cast<const T*>(a.v) + (size_t)ks * rs + (size_t)h * D;
-  TileStage<T, D, C::BN, true> kst, vst;   // key rows stored swap23-permuted
-  auto gload = [&](int kvt) {
-    kst.load(kb, (int)rs, kvt * C::BN, lk, tid);
-    vst.load(vb, (int)rs, kvt * C::BN, lk, tid);
+  auto visible = [&](int n) { return wave_live && (!a.causal || 32 * n <= row0 + 31 + off); };
+  auto needs_mask = [&](int n) {
+    return (32 * n + 32 > lk) || (a.causal && 32 * n + 31 > row0 + off) || (row0 + 32 > lq);
   };
-  auto lstore = [&](int buf) {
-    char* st = smem + buf * C::STAGE;
-    kst.store(st, tid);
-    vst.store(st + C::KT, tid);
-  };
+  // keys at offset >= this (relative to the sub-block's first key + 8*g) are masked
+  const int key_end = my_row < lq ? min(lk, a.causal ? my_row + off + 1 : lk) - 8 * g : -(1 << 30);
 
-  if (n_kv > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n_kv; ++it) {
-    if (it + 1 < n_kv) gload(it + 1);
-    const int kv0 = it * C::BN;
-    const char* kt = smem + (it & 1) * C::STAGE;
+  // S^T and dP^T (32 keys x 32 queries) of sub-block n; register r holds key
+  // 32*n + 16*(r/8) + 8*g + r%8
+  auto products = [&](f32x16& s, f32x16& dp, int n) {
+    const char* kt = slot(n / C::SPS);
     const char* vt = kt + C::KT;
-    const bool active = wave_live && (!a.causal || kv0 <= row0 + 31 + off);
-    if (active) {
-      // S^T and dP^T (64 keys x 32 queries) as two 32-key tiles
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    const int rl = 32 * (n % C::SPS);
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < C::NK; ++kk) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const frag_t<T> kfr = lds_row_frag<T, D>(kt, 32 * mt + c32, 16 * kk + 8 * g);
-          mma(s[mt], kfr, qf[kk]);
-          const frag_t<T> vfr = lds_row_frag<T, D>(vt, 32 * mt + c32, 16 * kk + 8 * g);
-          mma(dp[mt], vfr, df[kk]);
-        }
-      }
-      const bool need_mask = (kv0 + C::BN > lk) || (a.causal && kv0 + C::BN - 1 > row0 + off) || (row0 + 32 > lq);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kv0 + 32 * mt + 16 * (r >> 3) + 8 * g + (r & 7);
-          bool masked = false;
-          if (need_mask) masked = (j >= lk) || (my_row >= lq) || (a.causal && j > my_row + off);
-          float p, ds;
-          p_ds<ACT>(s[mt][r], dp[mt][r], lse2, dlt, a.scale, a.scale_log2, inv_lk, masked, p, ds);
-          dp[mt][r] = ds;
-        }
-      }
-      // dQ^T (D x 32 queries) += K^T dS^T
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          const frag_t<T> sf = pack_frag<T>(dp[mt], ss);
-#pragma unroll
-          for (int d2 = 0; d2 < C::ND; ++d2) {
-            const frag_t<T> ktf = lds_col_frag<T, D, true>(kt, 32 * mt + 16 * ss, 32 * d2);
-            mma(dq[d2], ktf, sf);
-          }
-        }
-      }
+    for (int kk = 0; kk < C::NK; ++kk) {
+      mma(s, lds_row_frag<T, D>(kt, rl + c32, 16 * kk + 8 * g), qf[kk]);
+      mma(dp, lds_row_frag<T, D>(vt, rl + c32, 16 * kk + 8 * g), df[kk]);
     }
-    if (it + 1 < n_kv) lstore((it + 1) & 1);
-    __syncthreads();
+  };
+
+  auto sub_step = [&](auto MASK, auto NEXT, f32x16& s, f32x16& dp, f32x16& s_nxt, f32x16& dp_nxt, int n) {
+    constexpr bool kMask = decltype(MASK)::value;
+    constexpr bool kNext = decltype(NEXT)::value;
+    const char* kt = slot(n / C::SPS);
+    const int rl = 32 * (n % C::SPS);
+    if constexpr (kNext) products(s_nxt, dp_nxt, n + 1);
+    const int lim = key_end - 32 * n;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 16 * (r >> 3) + (r & 7);
+      bool masked = false;
+      if constexpr (kMask) masked = c >= lim;
+      float p, ds;
+      p_ds<ACT>(s[r], dp[r], lse2, dlt, a.scale, a.scale_log2, inv_lk, masked, p, ds);
+      dp[r] = ds;
+    }
+    // dQ^T (D x 32 queries) += K^T dS^T; k-step ss covers keys 16*ss .. +15
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const frag_t<T> sf = pack_frag<T>(dp, ss);
+#pragma unroll
+      for (int d2 = 0; d2 < C::ND; ++d2) mma(dq[d2], lds_col_frag<T, D, true>(kt, rl + 16 * ss, 32 * d2), sf);
+    }
+  };
+
+  auto iter = [&](int n, f32x16& s, f32x16& dp, f32x16& s_nxt, f32x16& dp_nxt) {
+    const bool has_next = n + 1 < nsub;
+    if (has_next && (n + 1) % C::SPS == 0) {
+      const int st = (n + 1) / C::SPS;
+      wait_stage<NPS>(min(kStages - 3, nst - 1 - st));
+      __syncthreads();
+      if (st + kStages - 2 < nst) issue_stage(st + kStages - 2);
+    }
+    const bool nxt = has_next && visible(n + 1);
+    if (visible(n)) {
+      with_flags(needs_mask(n), nxt, [&](auto MASK, auto NEXT) { sub_step(MASK, NEXT, s, dp, s_nxt, dp_nxt, n); });
+    } else if (nxt) {
+      products(s_nxt, dp_nxt, n + 1);
+    }
+  };
+
+  if (nst > 0) wait_stage<NPS>(pro);
+  __syncthreads();
+  f32x16 sa, da, sb, db_;
+  if (nsub > 0 && visible(0)) products(sa, da, 0);
+  for (int n = 0; n < nsub; n += 2) {
+    iter(n, sa, da, sb, db_);
+    if (n + 1 < nsub) iter(n + 1, sb, db_, sa, da);
   }
 
   if (!wave_live || my_row >= lq) return;
   T* dqp = static_cast<T*>(a.dq) + (size_t)(qs + my_row) * rs + (size_t)h * D;
   store_row<T, C::ND>(dqp, dq, a.scale);
 }
+
+#define JFA_BWD_INST(T, D, ACT)                                      \
+  template __global__ void dkdv_kernel<T, D, ACT>(BwdArgs);          \
+  template __global__ void dq_kernel<T, D, ACT>(BwdArgs);
+JFA_BWD_INST(__bf16, 32, 0) JFA_BWD_INST(__bf16, 64, 0) JFA_BWD_INST(__bf16, 128, 0)
+JFA_BWD_INST(__bf16, 32, 1) JFA_BWD_INST(__bf16, 64, 1) JFA_BWD_INST(__bf16, 128, 1)
+JFA_BWD_INST(float, 32, 0) JFA_BWD_INST(float, 64, 0) JFA_BWD_INST(float, 128, 0)
+JFA_BWD_INST(float, 32, 1) JFA_BWD_INST(float, 64, 1) JFA_BWD_INST(float, 128, 1)
+#undef JFA_BWD_INST
 
 // ---------------------------------------------------------------- launchers
 
@@ -369,9 +480,9 @@ static hipError_t pre_d(const BwdArgs& a, int head_dim, hipStream_t stream) {
   const T* o = static_cast<const T*>(a.out);
   const T* d = static_cast<const T*>(a.dout);
   switch (head_dim) {
-    case 32: hipLaunchKernelGGL((bwd_pre_kernel<T, 32>), dim3(grid(32)), dim3(256), 0, stream, o, d, a.delta, a.heads, a.total_q); break;
-    case 64: hipLaunchKernelGGL((bwd_pre_kernel<T, 64>), dim3(grid(64)), dim3(256), 0, stream, o, d, a.delta, a.heads, a.total_q); break;
-    case 128: hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), dim3(grid(128)), dim3(256), 0, stream, o, d, a.delta, a.heads, a.total_q); break;
+    case 32: hipLaunchKernelGGL((bwd_pre_kernel<T, 32>), dim3(grid(32)), dim3(256), 0, stream, o, d, a.lse, a.stats, a.heads, a.total_q); break;
+    case 64: hipLaunchKernelGGL((bwd_pre_kernel<T, 64>), dim3(grid(64)), dim3(256), 0, stream, o, d, a.lse, a.stats, a.heads, a.total_q); break;
+    case 128: hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), dim3(grid(128)), dim3(256), 0, stream, o, d, a.lse, a.stats, a.heads, a.total_q); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -328,6 +328,25 @@ struct TileDma {
 // Wait until this wave's outstanding global->LDS copies have landed.
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N of this wave's vector-memory operations are still in
+// flight (they complete in issue order): the copies issued before the last N
+// have landed.
+template <int N>
+__device__ __forceinline__ void dma_wait_all_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Per-row (lse * log2(e), delta) pairs of rows row0 .. row0+valid-1 (valid
+// <= 64) copied into `dst` (1 KB of LDS; pairs past `valid` read as zeros).
+// Every wave that calls it writes the same bytes, so that all waves issue the
+// same number of copies per stage.
+__device__ __forceinline__ void stats_dma(char* dst, const float2* base, int row0, int valid) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float2*>(base + row0), 0, valid * (int)sizeof(float2), kBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (JFA_LDS void*)dst, 16, lane_id() * 16, 0, 0, 0);
+}
+
 template <typename T>
 __device__ __forceinline__ frag_t<T> global_frag(const T* p) {
   if constexpr (sizeof(T) == 2) {
@@ -346,15 +365,16 @@ __device__ __forceinline__ frag_t<T> global_frag(const T* p) {
 }
 
 // Store 4 consecutive output elements (rounded to nearest even for bf16).
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float x0, float x1, float x2, float x3) {
   if constexpr (sizeof(T) == 2) {
-    u32x2 u;
-    u[0] = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x0) |
-           ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x1) << 16);
-    u[1] = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x2) |
-           ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)x3) << 16);
-    *reinterpret_cast<u32x2*>(p) = u;
+    bf16x4 f;
+    f[0] = (__bf16)x0;
+    f[1] = (__bf16)x1;
+    f[2] = (__bf16)x2;
+    f[3] = (__bf16)x3;
+    *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, f);
   } else {
     f32x4 f = {x0, x1, x2, x3};
     *reinterpret_cast<f32x4*>(p) = f;

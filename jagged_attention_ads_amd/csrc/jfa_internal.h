@@ -64,7 +64,7 @@ struct BwdArgs {
   const int32_t* n_items_q;
   const int2* items_kv;    // key-tile list (dK/dV pass)
   const int32_t* n_items_kv;
-  float* delta;            // [heads, total_q] workspace
+  float2* stats;           // [heads, total_q] workspace: (lse * log2(e), delta) per row
   void* dq;
   void* dk;
   void* dv;
