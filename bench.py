@@ -5,7 +5,8 @@
 
 A step is one pass of the whole hot path over one batch: the forward call
 (work-list build + attention kernel) and the backward call (work-list
-builds, delta preprocess, dK/dV kernel, dQ kernel).  Inputs are generated on
+builds, dQ kernel -- which also forms the softmax row statistics -- and
+dK/dV kernel).  Inputs are generated on
 the host, copied to HBM before timing, and stay resident.  Prints one JSON
 line: useful TFLOPS counted on the visible (query, key) pairs of the real,
 unpadded tokens -- 4*d FLOPs per pair forward, 10*d backward -- the split
@@ -111,11 +112,10 @@ def kernel_accounting(wl, T_q, T_k, pairs_total):
                     bytes=q_bytes + 2 * k_bytes + q_bytes + (row_f32 if soft else 0)),
         "bwd_dkdv": dict(flops=8 * d * H * pairs_total,
                          bytes=2 * q_bytes + 2 * k_bytes + (2 * row_f32 if soft else 0) + 2 * k_bytes),
-        "bwd_dq": dict(flops=6 * d * H * pairs_total,
-                       bytes=2 * q_bytes + 2 * k_bytes + (2 * row_f32 if soft else 0) + q_bytes),
+        # softmax: also reads O and lse and writes the (lse, delta) row pairs
+        "bwd_dq": dict(flops=6 * d * H * pairs_total + (2 * T_q * H * d if soft else 0),
+                       bytes=2 * q_bytes + 2 * k_bytes + q_bytes + ((q_bytes + 3 * row_f32) if soft else 0)),
     }
-    if soft:
-        acc["bwd_pre"] = dict(flops=2 * T_q * H * d, bytes=2 * q_bytes + row_f32)
     return acc
 
 
@@ -241,7 +241,7 @@ def main():
 
     K = args.steps
     ef = [ev.create(3) for _ in range(K)]
-    eb = [ev.create(6) for _ in range(K)] if run_bwd else []
+    eb = [ev.create(5) for _ in range(K)] if run_bwd else []
     edge = ev.create(2)
     torch.cuda.synchronize()
     ev.lib.hipEventRecord(edge[0], stream)
@@ -260,9 +260,9 @@ def main():
     fwd_ms = avg(ef, 0, 2)
     bwd_ms = 0.0
     if run_bwd:
-        kern_ms.update({"bwd_sched_q": avg(eb, 0, 1), "bwd_pre": avg(eb, 1, 2), "bwd_sched_kv": avg(eb, 2, 3),
-                        "bwd_dkdv": avg(eb, 3, 4), "bwd_dq": avg(eb, 4, 5)})
-        bwd_ms = avg(eb, 0, 5)
+        kern_ms.update({"bwd_sched_q": avg(eb, 0, 1), "bwd_dq": avg(eb, 1, 2), "bwd_sched_kv": avg(eb, 2, 3),
+                        "bwd_dkdv": avg(eb, 3, 4)})
+        bwd_ms = avg(eb, 0, 4)
 
     pairs = int(visible_pairs(batch.q_lengths, batch.kv_lengths, wl.causal).sum())
     useful_fwd = 4.0 * D * H * pairs

@@ -273,9 +273,10 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
     if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
   }
   if ((e = record(events, 1, stream)) != hipSuccess) return hip_fail(e, "event record");
-  if (total_q > 0 && activation == JFA_ACT_SOFTMAX) {
-    e = jfa::launch_bwd_pre(a, head_dim, dtype, stream);
-    if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+  // dQ first: it also writes the per-row (lse, delta) pairs the dK/dV pass reads
+  if (total_q > 0) {
+    e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, L.wq.capacity, stream);
+    if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
   }
   if ((e = record(events, 2, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (total_kv > 0) {
@@ -289,11 +290,6 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
     if (e != hipSuccess) return hip_fail(e, "dK/dV kernel launch");
   }
   if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");
-  if (total_q > 0) {
-    e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, L.wq.capacity, stream);
-    if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
-  }
-  if ((e = record(events, 5, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;
 }
 

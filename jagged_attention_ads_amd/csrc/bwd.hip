@@ -12,9 +12,10 @@
 //     lse (softmax) or from the scores (SiLU).
 //   dQ pass -- one work item per (sequence, head, 128-query tile); each wave
 //     owns 32 queries and walks the keys they see in 32-key sub-blocks.
-// A preprocess kernel first forms delta_i = sum_c dO_ic O_ic (softmax only),
-// the row sum of P o dP that the softmax Jacobian needs, and stores it next to
-// lse_i * log2(e).
+// The dQ pass runs first: while loading its rows it also forms
+// delta_i = sum_c dO_ic O_ic (softmax only), the row sum of P o dP that the
+// softmax Jacobian needs, and stores it next to lse_i * log2(e) for the
+// dK/dV pass.
 //
 // Both passes stream the operand they walk (Q and dO, or K and V) from HBM
 // straight into a ring of four swizzled LDS stages, two stages ahead of use
@@ -34,47 +35,29 @@
 
 namespace jfa {
 
-// ---------------------------------------------------------------- delta
+// ---------------------------------------------------------------- shared math
 
 // lse in log2 units, with rows that see no key (lse = -inf) mapped to 0:
 // those rows are fully masked, and a finite value keeps every product finite.
 __device__ __forceinline__ float lse_log2(float lse) { return lse > -INFINITY ? lse * kLog2e : 0.f; }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out, const T* __restrict__ dout,
-                                                      const float* __restrict__ lse, float2* __restrict__ stats,
-                                                      int heads, int total_q) {
-  constexpr int LPR = D * (int)sizeof(T) / 16;   // lanes per (row, head)
-  constexpr int RPB = 256 / LPR;                 // (row, head) pairs per block
-  const int sub = threadIdx.x % LPR;
-  const int64_t pair = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // = row * heads + head
-  const int64_t npairs = (int64_t)total_q * heads;
+// Sum of the products of the 8 elements of two fragments.
+__device__ __forceinline__ float frag_dot(const bf16x8& x, const bf16x8& y) {
+  const u32x4 a = __builtin_bit_cast(u32x4, x), b = __builtin_bit_cast(u32x4, y);
   float acc = 0.f;
-  if (pair < npairs) {
-    const char* po = reinterpret_cast<const char*>(out + pair * D) + sub * 16;
-    const char* pd = reinterpret_cast<const char*>(dout + pair * D) + sub * 16;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(po);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(pd);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (sizeof(T) == 2) {
-        acc += __uint_as_float(a[e] << 16) * __uint_as_float(b[e] << 16);
-        acc += __uint_as_float(a[e] & 0xffff0000u) * __uint_as_float(b[e] & 0xffff0000u);
-      } else {
-        acc += __uint_as_float(a[e]) * __uint_as_float(b[e]);
-      }
-    }
+  for (int e = 0; e < 4; ++e) {
+    acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
+    acc = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), acc);
   }
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, kWave);
-  if (pair < npairs && sub == 0) {
-    const int64_t row = pair / heads, head = pair % heads;
-    const size_t i = (size_t)head * total_q + row;
-    stats[i] = make_float2(lse_log2(lse[i]), acc);
-  }
+  return acc;
 }
-
-// ---------------------------------------------------------------- shared math
+__device__ __forceinline__ float frag_dot(const f32x8& x, const f32x8& y) {
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf(x[e], y[e], acc);
+  return acc;
+}
 
 // P and dS of one score, softmax (ACT 0) or silu (ACT 1); masked pairs give 0.
 template <int ACT>
@@ -160,19 +143,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   const int rs = a.heads * D;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
 
-  // this lane's key and value rows as B-operand fragments (d-slots 16*kk + 8*g + e)
-  frag_t<T> kf[C::NK], vf[C::NK];
-  {
-    const int j = min(my_key, lk - 1);
-    const T* kp = static_cast<const T*>(a.k) + (size_t)(ks + j) * rs + (size_t)h * D + 8 * g;
-    const T* vp = static_cast<const T*>(a.v) + (size_t)(ks + j) * rs + (size_t)h * D + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) {
-      kf[kk] = global_frag<T>(kp + 16 * kk);
-      vf[kk] = global_frag<T>(vp + 16 * kk);
-    }
-  }
-
   const T* qb = static_cast<const T*>(a.q) + (size_t)qs * rs + (size_t)h * D;
   const T* db = static_cast<const T*>(a.dout) + (size_t)qs * rs + (size_t)h * D;
   const float2* stats_h = ACT == 0 ? a.stats + (size_t)h * a.total_q + qs : nullptr;
@@ -186,8 +156,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     dma.issue(st + C::QT, db, rs, r0, lq, tid);
     if constexpr (ACT == 0) stats_dma(st + 2 * C::QT, stats_h, r0, min(C::SR, lq - r0));
   };
-  const int pro = min(kStages - 2, nst - 1);   // last stage the prologue issues
-  for (int s = 0; s <= pro; ++s) issue_stage(s);
+  // Prologue: stages 0 and 1, then this lane's key and value rows as
+  // B-operand fragments (d-slots 16*kk + 8*g + e); all of it lands before
+  // the loop, and stage 2 is issued after the barrier.
+  for (int s = 0; s < min(2, nst); ++s) issue_stage(s);
+  frag_t<T> kf[C::NK], vf[C::NK];
+  {
+    const int j = min(my_key, lk - 1);
+    const T* kp = static_cast<const T*>(a.k) + (size_t)(ks + j) * rs + (size_t)h * D + 8 * g;
+    const T* vp = static_cast<const T*>(a.v) + (size_t)(ks + j) * rs + (size_t)h * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) {
+      kf[kk] = global_frag<T>(kp + 16 * kk);
+      vf[kk] = global_frag<T>(vp + 16 * kk);
+    }
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) {
+      settle(kf[kk]);
+      settle(vf[kk]);
+    }
+  }
 
   f32x16 dk[C::ND], dv[C::ND];
 #pragma unroll
@@ -293,8 +281,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     }
   };
 
-  if (nst > 0) wait_stage<NPS>(pro);
+  dma_wait();
   __syncthreads();
+  if (2 < nst) issue_stage(2);
   f32x16 sa, da, sb, db_;
   if (nsub > 0 && visible(0)) products(sa, da, 0);
   for (int n = 0; n < nsub; n += 2) {
@@ -346,6 +335,19 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void dq_
   const int rs = a.heads * D;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
 
+  const T* kb = static_cast<const T*>(a.k) + (size_t)ks * rs + (size_t)h * D;
+  const T* vb = static_cast<const T*>(a.v) + (size_t)ks * rs + (size_t)h * D;
+  Dma dma;   // K and V tiles share the geometry
+  dma.init(rs, tid);
+  auto slot = [&](int s) { return smem + (s & (kStages - 1)) * C::STAGE; };
+  auto issue_stage = [&](int s) {
+    char* st = slot(s);
+    dma.issue(st, kb, rs, s * C::SR, lk, tid);
+    dma.issue(st + C::KT, vb, rs, s * C::SR, lk, tid);
+  };
+  // Prologue: stages 0 and 1, then this lane's query and output-gradient
+  // rows and statistics; all of it lands before the loop.
+  for (int s = 0; s < min(2, nst); ++s) issue_stage(s);
   frag_t<T> qf[C::NK], df[C::NK];
   float lse2 = 0.f, dlt = 0.f;
   {
@@ -358,24 +360,29 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void dq_
       df[kk] = global_frag<T>(dp + 16 * kk);
     }
     if (ACT == 0) {
-      const float2 st = a.stats[(size_t)h * a.total_q + qs + r];
-      lse2 = st.x;
-      dlt = st.y;
+      // delta of this lane's row: each lane group holds half the row's
+      // d-slots, summed across the two groups; stored with lse2 for the
+      // dK/dV pass
+      const T* op = static_cast<const T*>(a.out) + (size_t)(qs + r) * rs + (size_t)h * D + 8 * g;
+      frag_t<T> of[C::NK];
+#pragma unroll
+      for (int kk = 0; kk < C::NK; ++kk) of[kk] = global_frag<T>(op + 16 * kk);
+      const size_t si = (size_t)h * a.total_q + qs + r;
+      lse2 = lse_log2(a.lse[si]);
+      float part = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < C::NK; ++kk) part += frag_dot(of[kk], df[kk]);
+      dlt = xor32_sum(part);
+      if (g == 0 && my_row < lq) a.stats[si] = make_float2(lse2, dlt);
     }
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) {
+      settle(qf[kk]);
+      settle(df[kk]);
+    }
+    settle(lse2);
+    settle(dlt);
   }
-
-  const T* kb = static_cast<const T*>(a.k) + (size_t)ks * rs + (size_t)h * D;
-  const T* vb = static_cast<const T*>(a.v) + (size_t)ks * rs + (size_t)h * D;
-  Dma dma;   // K and V tiles share the geometry
-  dma.init(rs, tid);
-  auto slot = [&](int s) { return smem + (s & (kStages - 1)) * C::STAGE; };
-  auto issue_stage = [&](int s) {
-    char* st = slot(s);
-    dma.issue(st, kb, rs, s * C::SR, lk, tid);
-    dma.issue(st + C::KT, vb, rs, s * C::SR, lk, tid);
-  };
-  const int pro = min(kStages - 2, nst - 1);
-  for (int s = 0; s <= pro; ++s) issue_stage(s);
 
   f32x16 dq[C::ND];
 #pragma unroll
@@ -444,8 +451,9 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void dq_
     }
   };
 
-  if (nst > 0) wait_stage<NPS>(pro);
+  dma_wait();
   __syncthreads();
+  if (2 < nst) issue_stage(2);
   f32x16 sa, da, sb, db_;
   if (nsub > 0 && visible(0)) products(sa, da, 0);
   for (int n = 0; n < nsub; n += 2) {
@@ -468,30 +476,6 @@ JFA_BWD_INST(float, 32, 1) JFA_BWD_INST(float, 64, 1) JFA_BWD_INST(float, 128, 1
 #undef JFA_BWD_INST
 
 // ---------------------------------------------------------------- launchers
-
-template <typename T>
-static hipError_t pre_d(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  const int64_t pairs = (int64_t)a.total_q * a.heads;
-  // (row, head) pairs per 256-thread block: 256 / (16-byte chunks per row)
-  auto grid = [&](int D) {
-    const int64_t per_block = 256 / (D * (int64_t)sizeof(T) / 16);
-    return (unsigned)((pairs + per_block - 1) / per_block);
-  };
-  const T* o = static_cast<const T*>(a.out);
-  const T* d = static_cast<const T*>(a.dout);
-  switch (head_dim) {
-    case 32: hipLaunchKernelGGL((bwd_pre_kernel<T, 32>), dim3(grid(32)), dim3(256), 0, stream, o, d, a.lse, a.stats, a.heads, a.total_q); break;
-    case 64: hipLaunchKernelGGL((bwd_pre_kernel<T, 64>), dim3(grid(64)), dim3(256), 0, stream, o, d, a.lse, a.stats, a.heads, a.total_q); break;
-    case 128: hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), dim3(grid(128)), dim3(256), 0, stream, o, d, a.lse, a.stats, a.heads, a.total_q); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream) {
-  if ((int64_t)a.total_q * a.heads == 0) return hipSuccess;
-  return dtype == 0 ? pre_d<__bf16>(a, head_dim, stream) : pre_d<float>(a, head_dim, stream);
-}
 
 #define JFA_BWD_LAUNCHER(NAME, KERNEL)                                                                   \
   template <typename T, int ACT>                                                                         \

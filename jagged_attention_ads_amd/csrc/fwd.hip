@@ -76,6 +76,8 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
     const T* qp = static_cast<const T*>(a.q) + (size_t)(qs + r) * rs + (size_t)h * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < C::NK; ++kk) qf[kk] = global_frag<T>(qp + 16 * kk);
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) settle(qf[kk]);
   }
 
   f32x16 o[C::ND];

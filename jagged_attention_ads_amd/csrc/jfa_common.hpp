@@ -284,6 +284,18 @@ struct TileStage {
   }
 };
 
+// One buffer load that writes LDS: every lane reads 16 bytes at byte offset
+// `voff` of the buffer and the wave's 64 chunks land at lds .. lds + 1023
+// (lane order).  Issued as inline assembly on purpose: for the builtin form
+// the compiler cannot tell which LDS bytes the copy writes, and makes every
+// later LDS read wait for all copies in flight, which would serialise the
+// copies of stages that are meant to stay in flight behind the compute.
+// Completion is the caller's business (vector-memory counter, then barrier).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, int voff, const char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(JFA_LDS const char*)lds;
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+}
+
 // A ROWS x D tile of one head copied straight from global memory into a
 // swizzled LDS tile with buffer loads that write LDS (no register staging).
 // Each such load writes its 64 lanes' 16-byte chunks to 1 KB of consecutive
@@ -318,10 +330,7 @@ struct TileDma {
         const_cast<T*>(base + (size_t)row0 * row_stride), 0, valid * row_stride * (int)sizeof(T), kBufferWord3);
     const int wave_base = (tid & ~(kWave - 1)) * 16;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (JFA_LDS void*)(tile + i * NT * 16 + wave_base), 16, voff[i], 0,
-                                               0, 0);
-    }
+    for (int i = 0; i < N; ++i) buffer_load_lds16(rsrc, voff[i], tile + i * NT * 16 + wave_base);
   }
 };
 
@@ -337,6 +346,15 @@ __device__ __forceinline__ void dma_wait_all_but() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Makes the compiler wait here for the register load that produced x.  Its
+// own wait bookkeeping cannot see the inline-assembly LDS copies; settling
+// every register load before a loop keeps it from inserting waits inside
+// the loop, where they would also drain the copies meant to stay in flight.
+template <typename X>
+__device__ __forceinline__ void settle(const X& x) {
+  asm volatile("" ::"v"(x));
+}
+
 // Per-row (lse * log2(e), delta) pairs of rows row0 .. row0+valid-1 (valid
 // <= 64) copied into `dst` (1 KB of LDS; pairs past `valid` read as zeros).
 // Every wave that calls it writes the same bytes, so that all waves issue the
@@ -344,7 +362,7 @@ __device__ __forceinline__ void dma_wait_all_but() {
 __device__ __forceinline__ void stats_dma(char* dst, const float2* base, int row0, int valid) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float2*>(base + row0), 0, valid * (int)sizeof(float2), kBufferWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (JFA_LDS void*)dst, 16, lane_id() * 16, 0, 0, 0);
+  buffer_load_lds16(rsrc, lane_id() * 16, dst);
 }
 
 template <typename T>

@@ -64,7 +64,8 @@ struct BwdArgs {
   const int32_t* n_items_q;
   const int2* items_kv;    // key-tile list (dK/dV pass)
   const int32_t* n_items_kv;
-  float2* stats;           // [heads, total_q] workspace: (lse * log2(e), delta) per row
+  float2* stats;           // [heads, total_q] workspace: (lse * log2(e), delta) per row,
+                           // written by the dQ pass, read by the dK/dV pass
   void* dq;
   void* dk;
   void* dv;
@@ -76,7 +77,6 @@ struct BwdArgs {
   float scale_log2;
 };
 
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
 

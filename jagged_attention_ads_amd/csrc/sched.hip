@@ -50,6 +50,14 @@ __device__ int find_seq(const int* ts, int B, int u) {
   return lo;
 }
 
+// LDS bytes of the builder's cost-bucket arrays, and of the optional copy of
+// the per-sequence tile starts and lengths.
+__host__ __device__ constexpr size_t sched_lds_fixed(int nbuckets) {
+  return (((size_t)nbuckets * (3 * 4 + 2 + 2 * kSchedWaves) + 32 * 4) + 15) & ~(size_t)15;
+}
+__host__ __device__ constexpr size_t sched_lds_seqs(int batch) { return ((size_t)3 * batch + 1) * 4; }
+constexpr size_t kSchedMaxLds = 64 * 1024;
+
 template <int PASS>
 struct TileRule {
   // Tiles split the query side (PASS == kPassQ) or the key side.
@@ -70,8 +78,9 @@ struct TileRule {
 template <int PASS>
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restrict__ qo, const int* __restrict__ ko,
                                                               int B, int H, int causal, int nbuckets,
-                                                              int64_t capacity, int* __restrict__ count,
-                                                              int2* __restrict__ items, int* __restrict__ tile_start) {
+                                                              int64_t capacity, int stage_seqs,
+                                                              int* __restrict__ count, int2* __restrict__ items,
+                                                              int* __restrict__ tile_start) {
   using R = TileRule<PASS>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int* hist = reinterpret_cast<int*>(smem);
@@ -80,6 +89,22 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
   int* tmp = carry + nbuckets;                       // kSchedWaves ints (+pad)
   unsigned short* chunk_tot = reinterpret_cast<unsigned short*>(tmp + 32);
   unsigned short* wave_cnt = chunk_tot + nbuckets;   // [kSchedWaves][nbuckets]
+  // Per-sequence tile starts and lengths, read by every tile's binary
+  // search: staged in LDS when the launch provided room (stage_seqs), else
+  // read from global memory.
+  int* seq_lds = reinterpret_cast<int*>(smem + sched_lds_fixed(nbuckets));
+  int* ts = stage_seqs ? seq_lds : tile_start;
+  int* len_q = stage_seqs ? seq_lds + (B + 1) : nullptr;
+  int* len_k = stage_seqs ? seq_lds + (2 * B + 1) : nullptr;
+  auto lengths = [&](int b, int& lq, int& lk) {
+    if (stage_seqs) {
+      lq = len_q[b];
+      lk = len_k[b];
+    } else {
+      lq = qo[b + 1] - qo[b];
+      lk = ko[b + 1] - ko[b];
+    }
+  };
 
   const int tid = threadIdx.x, l = lane_id(), w = tid / kWave;
 
@@ -88,14 +113,27 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
   for (int base = 0; base < B; base += kSchedThreads) {
     const int b = base + tid;
     int n = 0;
-    if (b < B) n = ceil_div(R::rows(qo[b + 1] - qo[b], ko[b + 1] - ko[b]), R::kTile);
+    if (b < B) {
+      const int lq = qo[b + 1] - qo[b], lk = ko[b + 1] - ko[b];
+      n = ceil_div(R::rows(lq, lk), R::kTile);
+      if (stage_seqs) {
+        len_q[b] = lq;
+        len_k[b] = lk;
+      }
+    }
     int tot;
     const int ex = block_excl_scan(n, tmp, tot);
-    if (b < B) tile_start[b] = run + ex;
+    if (b < B) {
+      tile_start[b] = run + ex;
+      if (stage_seqs) ts[b] = run + ex;
+    }
     run += tot;
   }
   const int total_tiles = run;
-  if (tid == 0) tile_start[B] = total_tiles;
+  if (tid == 0) {
+    tile_start[B] = total_tiles;
+    if (stage_seqs) ts[B] = total_tiles;
+  }
   for (int c = tid; c < nbuckets; c += kSchedThreads) {
     hist[c] = 0;
     carry[c] = 0;
@@ -104,9 +142,11 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
 
   // 2. histogram of tile costs
   for (int u = tid; u < total_tiles; u += kSchedThreads) {
-    const int b = find_seq(tile_start, B, u);
-    const int t = u - tile_start[b];
-    const int c = min(R::cost(qo[b + 1] - qo[b], ko[b + 1] - ko[b], t, causal), nbuckets - 1);
+    const int b = find_seq(ts, B, u);
+    const int t = u - ts[b];
+    int lq, lk;
+    lengths(b, lq, lk);
+    const int c = min(R::cost(lq, lk, t, causal), nbuckets - 1);
     atomicAdd(&hist[c], 1);
   }
   __syncthreads();
@@ -132,10 +172,9 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
     const bool valid = u < total_tiles;
     int b = 0, t = 0, c = -1, lq = 0, lk = 0;
     if (valid) {
-      b = find_seq(tile_start, B, u);
-      t = u - tile_start[b];
-      lq = qo[b + 1] - qo[b];
-      lk = ko[b + 1] - ko[b];
+      b = find_seq(ts, B, u);
+      t = u - ts[b];
+      lengths(b, lq, lk);
       c = min(R::cost(lq, lk, t, causal), nbuckets - 1);
     }
     // rank inside the wave: one ballot per distinct cost present
@@ -164,7 +203,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
     if (valid) {
       const int rank = carry[c] + wave_cnt[w * nbuckets + c] + local;
       // the run of tiles of sequence b with this same cost: [first, last]
-      const int ntiles = tile_start[b + 1] - tile_start[b];
+      const int ntiles = ts[b + 1] - ts[b];
       int lo = 0, hi = t;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -214,13 +253,15 @@ hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t 
   int* count = reinterpret_cast<int*>(base);
   int2* items = reinterpret_cast<int2*>(base + lay.items_off);
   int* tile_start = reinterpret_cast<int*>(base + lay.tile_start_off);
-  const size_t lds = static_cast<size_t>(nbuckets) * (3 * 4 + 2 + 2 * kSchedWaves) + 32 * 4;
+  size_t lds = sched_lds_fixed(nbuckets);
+  const int stage = lds + sched_lds_seqs(batch) <= kSchedMaxLds ? 1 : 0;
+  if (stage) lds += sched_lds_seqs(batch);
   if (pass == kPassQ)
     hipLaunchKernelGGL(sched_kernel<kPassQ>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
-                       causal, nbuckets, lay.capacity, count, items, tile_start);
+                       causal, nbuckets, lay.capacity, stage, count, items, tile_start);
   else
     hipLaunchKernelGGL(sched_kernel<kPassKV>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
-                       causal, nbuckets, lay.capacity, count, items, tile_start);
+                       causal, nbuckets, lay.capacity, stage, count, items, tile_start);
   return hipGetLastError();
 }
 
