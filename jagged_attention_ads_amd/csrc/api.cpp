@@ -256,7 +256,8 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   a.n_items_q = reinterpret_cast<const int32_t*>(ws + L.off_wq);
   a.items_kv = reinterpret_cast<const int2*>(ws + L.off_wkv + L.wkv.items_off);
   a.n_items_kv = reinterpret_cast<const int32_t*>(ws + L.off_wkv);
-  a.stats = reinterpret_cast<float2*>(ws + L.off_stats);
+  a.lse2 = reinterpret_cast<float*>(ws + L.off_stats);
+  a.delta = a.lse2 + static_cast<size_t>(heads) * static_cast<size_t>(total_q);
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

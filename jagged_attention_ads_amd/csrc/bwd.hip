@@ -6,22 +6,20 @@
 // The gradient sums over queries (dK, dV) and over keys (dQ) are split into
 // two passes so that every output row is owned by exactly one workgroup and
 // stored once:
-//   dK/dV pass -- one work item per (sequence, head, 128-key tile); each wave
-//     owns 32 keys (its K and V rows live in registers) and walks the query
-//     rows that see them in 32-row sub-blocks.  P and dS are recomputed from
-//     lse (softmax) or from the scores (SiLU).
+//   dK/dV pass -- one work item per (sequence, head, 128-key tile); each
+//     pair of waves owns 32 keys and walks the query rows that see them in
+//     32-row sub-blocks.  P and dS are recomputed from lse (softmax) or from
+//     the scores (SiLU).
 //   dQ pass -- one work item per (sequence, head, 128-query tile); each wave
 //     owns 32 queries and walks the keys they see in 32-key sub-blocks.
 // The dQ pass runs first: while loading its rows it also forms
 // delta_i = sum_c dO_ic O_ic (softmax only), the row sum of P o dP that the
-// softmax Jacobian needs, and stores it next to lse_i * log2(e) for the
-// dK/dV pass.
+// softmax Jacobian needs, and stores it and lse_i * log2(e) for the dK/dV
+// pass.
 //
 // Both passes stream the operand they walk (Q and dO, or K and V) from HBM
-// straight into a ring of four swizzled LDS stages, two stages ahead of use
-// (buffer loads that write LDS), and are software-pipelined: the S and dP
-// products of the next sub-block run on the matrix cores while P and dS of
-// the current one are formed on the vector ALUs.
+// straight into a ring of swizzled LDS stages, two or more stages ahead of
+// use (buffer loads that write LDS).
 //
 // Per (query i, key j) pair, with x = scale * q_i.k_j:
 //   softmax: P = exp(x - lse_i);        dS = P (dP - delta_i)
@@ -107,24 +105,38 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 
 // ---------------------------------------------------------------- dK / dV
 
+// Eight waves per item: four pairs, each pair owning 32 keys.  Wave A of a
+// pair forms S = Q K^T and P (masks applied) and accumulates dV^T += dO^T P;
+// wave B forms dP = dO V^T, takes P from wave A through LDS, forms dS and
+// accumulates dK^T += Q^T dS.  The matrix work splits evenly, nothing is
+// computed twice, and a wave's registers (one of K or V, one accumulator
+// set) fit two waves per SIMD, so one wave's vector work and LDS waits
+// overlap the other's products.  Per 32-row sub-block n, one barrier: A
+// hands over P(n) (or, for SiLU, the derivative factor) before it, B reads
+// it after.
 template <typename T, int D>
 struct DkdvCfg {
-  static constexpr int BN = kBwdBN, NT = 256;
+  static constexpr int BN = kBwdBN, NT = 512;
   static constexpr int ES = sizeof(T);
-  static constexpr int SR = (D * ES <= 256) ? 64 : 32;   // query rows per stage
-  static constexpr int SPS = SR / 32;                    // 32-row sub-blocks per stage
+  static constexpr int SR = 32;                          // query rows per stage = one sub-block
   static constexpr int QT = Swz<T, D>::tile_bytes(SR);   // Q or dO tile
-  static constexpr int STAGE = 2 * QT + 1024;            // Q, dO, row statistics
-  static constexpr int LDS = kStages * STAGE;
+  static constexpr int STATS = NT / 64 * 256;            // per wave: its 64 rows of lse2 or delta
+  static constexpr int STAGE = 2 * QT + STATS;
+  static constexpr int XCH = 4 * 2 * 4096;               // per pair: two 32 x 32 fp32 hand-over slots
+  static constexpr int SINK = NT / 64 * 1024;            // surplus tile loads, 1 KB per wave
+  static constexpr int NS = (4 * STAGE + XCH + SINK <= 160 * 1024) ? 4 : 3;   // stages in the ring
+  static constexpr int LDS = NS * STAGE + XCH + SINK;
   static constexpr int ND = D / 32, NK = D / 16;
 };
 
 template <typename T, int D, int ACT>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<T, D>;
-  using Dma = TileDma<T, D, C::SR, true>;   // query rows stored swap23-permuted
+  using Dma = TileDma<T, D, C::SR, true, C::NT>;   // query rows stored swap23-permuted
   constexpr int NPS = 2 * Dma::N + (ACT == 0 ? 1 : 0);   // copies per thread per stage
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  char* const xch = smem + C::NS * C::STAGE;
+  char* const sink = xch + C::XCH;
 
   if ((int)blockIdx.x >= *a.n_items_kv) return;
   int b, h, t;
@@ -134,57 +146,107 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   const int off = lk - lq;
 
   const int tid = threadIdx.x, l = lane_id(), w = tid >> 6, g = l >> 5, c32 = l & 31;
-  const int kw0 = t * C::BN + 32 * w;    // first key of this wave
-  const int my_key = kw0 + c32;          // the key this lane owns (its column of S)
+  const int pair = w & 3;
+  const bool role_a = w < 4;               // A: S, P, dV;  B: dP, dS, dK
+  const int kw0 = t * C::BN + 32 * pair;   // first key of this pair
+  const int my_key = kw0 + c32;            // the key this lane owns (its column of S)
   const bool wave_live = kw0 < lk;
   const int nst = kv_tile_q_blocks(lq, lk, t, C::SR, C::BN, a.causal);
   const int q_first = kv_tile_first_q_block(lq, lk, t, C::SR, C::BN, a.causal) * C::SR;
-  const int nsub = nst * C::SPS;
   const int rs = a.heads * D;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
 
   const T* qb = static_cast<const T*>(a.q) + (size_t)qs * rs + (size_t)h * D;
   const T* db = static_cast<const T*>(a.dout) + (size_t)qs * rs + (size_t)h * D;
-  const float2* stats_h = ACT == 0 ? a.stats + (size_t)h * a.total_q + qs : nullptr;
+  // A needs lse2 of the rows, B needs delta
+  const float* row_h = ACT == 0 ? (role_a ? a.lse2 : a.delta) + (size_t)h * a.total_q + qs : nullptr;
   Dma dma;   // Q and dO tiles share the geometry, hence the offsets
   dma.init(rs, tid);
-  auto slot = [&](int s) { return smem + (s & (kStages - 1)) * C::STAGE; };
+  auto slot = [&](int s) { return smem + (s % C::NS) * C::STAGE; };
   auto issue_stage = [&](int s) {
     char* st = slot(s);
     const int r0 = q_first + s * C::SR;
-    dma.issue(st, qb, rs, r0, lq, tid);
-    dma.issue(st + C::QT, db, rs, r0, lq, tid);
-    if constexpr (ACT == 0) stats_dma(st + 2 * C::QT, stats_h, r0, min(C::SR, lq - r0));
+    dma.issue(st, qb, rs, r0, lq, tid, sink);
+    dma.issue(st + C::QT, db, rs, r0, lq, tid, sink);
+    if constexpr (ACT == 0) rows_dma(st + 2 * C::QT + w * 256, row_h, r0, lq);
   };
-  // Prologue: stages 0 and 1, then this lane's key and value rows as
+
+  // Prologue: stages 0 and 1, then this lane's key (A) or value (B) row as
   // B-operand fragments (d-slots 16*kk + 8*g + e); all of it lands before
-  // the loop, and stage 2 is issued after the barrier.
+  // the loop, and the rest of the ring is issued after the barrier.
   for (int s = 0; s < min(2, nst); ++s) issue_stage(s);
-  frag_t<T> kf[C::NK], vf[C::NK];
+  frag_t<T> xf[C::NK];
   {
     const int j = min(my_key, lk - 1);
-    const T* kp = static_cast<const T*>(a.k) + (size_t)(ks + j) * rs + (size_t)h * D + 8 * g;
-    const T* vp = static_cast<const T*>(a.v) + (size_t)(ks + j) * rs + (size_t)h * D + 8 * g;
+    const T* xp = static_cast<const T*>(role_a ? a.k : a.v) + (size_t)(ks + j) * rs + (size_t)h * D + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) {
-      kf[kk] = global_frag<T>(kp + 16 * kk);
-      vf[kk] = global_frag<T>(vp + 16 * kk);
-    }
+    for (int kk = 0; kk < C::NK; ++kk) xf[kk] = global_frag<T>(xp + 16 * kk);
 #pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) {
-      settle(kf[kk]);
-      settle(vf[kk]);
-    }
+    for (int kk = 0; kk < C::NK; ++kk) settle(xf[kk]);
   }
+  dma_wait();
+  __syncthreads();
+  for (int s = 2; s <= C::NS - 2; ++s)
+    if (s < nst) issue_stage(s);
 
-  f32x16 dk[C::ND], dv[C::ND];
+  f32x16 acc[C::ND];   // dV^T (A) or dK^T (B): lane = key, registers = d
 #pragma unroll
-  for (int i = 0; i < C::ND; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
-  }
+  for (int i = 0; i < C::ND; ++i) acc[i] = f32x16{};
 
-  // a wave takes part in sub-block n iff it has rows and some see its keys
+  // S (A) or dP (B) of sub-block n: 32 queries x 32 keys; register r holds
+  // query q_first + 32*n + 16*(r/8) + 8*g + r%8 of this lane's key
+  auto products = [&](f32x16& x, const char* tile) {
+    x = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) mma(x, lds_row_frag<T, D>(tile, c32, 16 * kk + 8 * g), xf[kk]);
+  };
+  // hand-over slot of sub-block n: [r/4][lane][4] floats
+  auto xslot = [&](int n) { return xch + (pair * 2 + (n & 1)) * 4096; };
+
+  // Wave A, phase 1: P (kept in x for dV) and the value B needs (written to
+  // the hand-over slot): P itself (softmax) or silu'(x)/Lk (SiLU).
+  auto a_weights = [&](auto MASK, f32x16& x, int n, const char* st) {
+    constexpr bool kMask = decltype(MASK)::value;
+    const int qa = q_first + 32 * n;
+    const int lo = (a.causal ? my_key - off : 0) - qa - 8 * g;
+    const int span = max((my_key < lk) ? (lq - qa - 8 * g) - lo : 0, 0);
+    float l2[16];
+    if constexpr (ACT == 0) {
+      const char* sp = st + 2 * C::QT + w * 256 + 8 * g * (int)sizeof(float);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(sp + (16 * (q4 >> 1) + 4 * (q4 & 1)) * (int)sizeof(float));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l2[4 * q4 + e] = v[e];
+      }
+    }
+    f32x16 e_out;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 16 * (r >> 3) + (r & 7);
+      bool masked = false;
+      if constexpr (kMask) masked = (unsigned)(c - lo) >= (unsigned)span;
+      if constexpr (ACT == 0) {
+        const float p = fast_exp2(fmaf(x[r], a.scale_log2, -l2[r]));
+        x[r] = masked ? 0.f : p;
+        e_out[r] = x[r];
+      } else {
+        const float xs = x[r] * a.scale;
+        const float sig = fast_rcp(1.0f + fast_exp2(-x[r] * a.scale_log2));
+        const float keep = masked ? 0.f : inv_lk;
+        x[r] = xs * sig * keep;
+        e_out[r] = sig * (1.0f + xs * (1.0f - sig)) * keep;
+      }
+    }
+    char* xo = xslot(n) + l * 16;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 v = {e_out[4 * q4], e_out[4 * q4 + 1], e_out[4 * q4 + 2], e_out[4 * q4 + 3]};
+      *reinterpret_cast<f32x4*>(xo + q4 * 1024) = v;
+    }
+  };
+
+  // sub-blocks in which this pair's keys are seen by some row
   auto visible = [&](int n) {
     const int qa = q_first + 32 * n;
     return wave_live && qa < lq && !(a.causal && qa + 31 + off < kw0);
@@ -194,108 +256,68 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     return (qa + 32 > lq) || (kw0 + 32 > lk) || (a.causal && kw0 + 31 > qa + off);
   };
 
-  // S and dP (32 queries x 32 keys) of sub-block n; register r holds query
-  // q_first + 32*n + 16*(r/8) + 8*g + r%8
-  auto products = [&](f32x16& s, f32x16& dp, int n) {
-    const char* qt = slot(n / C::SPS);
-    const char* dt = qt + C::QT;
-    const int rl = 32 * (n % C::SPS);
-    s = f32x16{};
-    dp = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) {
-      mma(s, lds_row_frag<T, D>(qt, rl + c32, 16 * kk + 8 * g), kf[kk]);
-      mma(dp, lds_row_frag<T, D>(dt, rl + c32, 16 * kk + 8 * g), vf[kk]);
+  for (int n = 0; n < nst; ++n) {
+    const char* st = slot(n);
+    const char* qt = st;
+    const char* dt = st + C::QT;
+    const bool vis = visible(n);
+    f32x16 x;
+    if (vis) {
+      products(x, role_a ? qt : dt);
+      if (role_a) {
+        if (needs_mask(n)) a_weights(std::true_type{}, x, n, st);
+        else a_weights(std::false_type{}, x, n, st);
+      }
     }
-  };
-
-  // P and dS of sub-block n from s, dp (in place), with the products of
-  // sub-block n+1 (when NEXT) interleaved, then dV^T += dO^T P and
-  // dK^T += Q^T dS.  MASK and NEXT are compile-time: the region is
-  // straight-line.
-  auto sub_step = [&](auto MASK, auto NEXT, f32x16& s, f32x16& dp, f32x16& s_nxt, f32x16& dp_nxt, int n) {
-    constexpr bool kMask = decltype(MASK)::value;
-    constexpr bool kNext = decltype(NEXT)::value;
-    const char* qt = slot(n / C::SPS);
-    const char* dt = qt + C::QT;
-    const int rl = 32 * (n % C::SPS);
-    const int qa = q_first + 32 * n;
-    // lse2 and delta of this lane's 16 rows rl + 16*(r/8) + 8*g + r%8
-    float l2[16], de[16];
-    if constexpr (ACT == 0) {
-      const char* sp = qt + 2 * C::QT + (rl + 8 * g) * (int)sizeof(float2);
+    // stage n+1 must have landed before the barrier; later ones may be in flight
+    if (n + 1 < nst) wait_stage<NPS>(min(C::NS - 3, nst - 2 - n));
+    __syncthreads();
+    // every wave is done with stage n-1: refill its slot
+    if (n + C::NS - 1 < nst) issue_stage(n + C::NS - 1);
+    if (vis) {
+      if (role_a) {
+        // dV^T += dO^T P; k-step ss covers rows 16*ss .. +15 of the sub-block
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
+        for (int ss = 0; ss < 2; ++ss) {
+          const frag_t<T> pf = pack_frag<T>(x, ss);
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(sp + (16 * h2 + 2 * q2) * (int)sizeof(float2));
-          l2[8 * h2 + 2 * q2] = v[0];
-          de[8 * h2 + 2 * q2] = v[1];
-          l2[8 * h2 + 2 * q2 + 1] = v[2];
-          de[8 * h2 + 2 * q2 + 1] = v[3];
+          for (int d2 = 0; d2 < C::ND; ++d2) mma(acc[d2], lds_col_frag<T, D, true>(dt, 16 * ss, 32 * d2), pf);
+        }
+      } else {
+        const char* xi = xslot(n) + l * 16;
+        float dl[16];
+        if constexpr (ACT == 0) {
+          const char* sp = st + 2 * C::QT + w * 256 + 8 * g * (int)sizeof(float);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sp + (16 * (q4 >> 1) + 4 * (q4 & 1)) * (int)sizeof(float));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dl[4 * q4 + e] = v[e];
+          }
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 e4 = *reinterpret_cast<const f32x4*>(xi + q4 * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            x[r] = ACT == 0 ? e4[e] * (x[r] - dl[r]) : x[r] * e4[e];   // dS
+          }
+        }
+        // dK^T += Q^T dS
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+          const frag_t<T> sf = pack_frag<T>(x, ss);
+#pragma unroll
+          for (int d2 = 0; d2 < C::ND; ++d2) mma(acc[d2], lds_col_frag<T, D, true>(qt, 16 * ss, 32 * d2), sf);
         }
       }
     }
-    if constexpr (kNext) products(s_nxt, dp_nxt, n + 1);
-    // row qi = 16*(r/8) + r%8 + 8*g of the sub-block is visible to this
-    // lane's key iff lo <= qi < lo + span (one unsigned compare)
-    const int lo = (a.causal ? my_key - off : 0) - qa - 8 * g;
-    const int span = max((my_key < lk) ? (lq - qa - 8 * g) - lo : 0, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int c = 16 * (r >> 3) + (r & 7);
-      bool masked = false;
-      if constexpr (kMask) masked = (unsigned)(c - lo) >= (unsigned)span;
-      float p, ds;
-      p_ds<ACT>(s[r], dp[r], ACT == 0 ? l2[r] : 0.f, ACT == 0 ? de[r] : 0.f, a.scale, a.scale_log2, inv_lk,
-                masked, p, ds);
-      s[r] = p;
-      dp[r] = ds;
-    }
-    // k-step ss covers rows 16*ss .. +15 of the sub-block
-#pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      const frag_t<T> pf = pack_frag<T>(s, ss);
-      const frag_t<T> sf = pack_frag<T>(dp, ss);
-#pragma unroll
-      for (int d2 = 0; d2 < C::ND; ++d2) {
-        mma(dv[d2], lds_col_frag<T, D, true>(dt, rl + 16 * ss, 32 * d2), pf);
-        mma(dk[d2], lds_col_frag<T, D, true>(qt, rl + 16 * ss, 32 * d2), sf);
-      }
-    }
-  };
-
-  auto iter = [&](int n, f32x16& s, f32x16& dp, f32x16& s_nxt, f32x16& dp_nxt) {
-    const bool has_next = n + 1 < nsub;
-    if (has_next && (n + 1) % C::SPS == 0) {   // sub-block n+1 opens stage st
-      const int st = (n + 1) / C::SPS;
-      wait_stage<NPS>(min(kStages - 3, nst - 1 - st));
-      __syncthreads();
-      if (st + kStages - 2 < nst) issue_stage(st + kStages - 2);
-    }
-    const bool nxt = has_next && visible(n + 1);
-    if (visible(n)) {
-      with_flags(needs_mask(n), nxt, [&](auto MASK, auto NEXT) { sub_step(MASK, NEXT, s, dp, s_nxt, dp_nxt, n); });
-    } else if (nxt) {
-      products(s_nxt, dp_nxt, n + 1);
-    }
-  };
-
-  dma_wait();
-  __syncthreads();
-  if (2 < nst) issue_stage(2);
-  f32x16 sa, da, sb, db_;
-  if (nsub > 0 && visible(0)) products(sa, da, 0);
-  for (int n = 0; n < nsub; n += 2) {
-    iter(n, sa, da, sb, db_);
-    if (n + 1 < nsub) iter(n + 1, sb, db_, sa, da);
   }
 
   if (!wave_live || my_key >= lk) return;
-  T* dkp = static_cast<T*>(a.dk) + (size_t)(ks + my_key) * rs + (size_t)h * D;
-  T* dvp = static_cast<T*>(a.dv) + (size_t)(ks + my_key) * rs + (size_t)h * D;
-  store_row<T, C::ND>(dkp, dk, a.scale);
-  store_row<T, C::ND>(dvp, dv, 1.0f);
+  T* op = static_cast<T*>(role_a ? a.dv : a.dk) + (size_t)(ks + my_key) * rs + (size_t)h * D;
+  store_row<T, C::ND>(op, acc, role_a ? 1.0f : a.scale);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -373,7 +395,10 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void dq_
 #pragma unroll
       for (int kk = 0; kk < C::NK; ++kk) part += frag_dot(of[kk], df[kk]);
       dlt = xor32_sum(part);
-      if (g == 0 && my_row < lq) a.stats[si] = make_float2(lse2, dlt);
+      if (my_row < lq) {
+        if (g == 0) a.lse2[si] = lse2;
+        else a.delta[si] = dlt;
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < C::NK; ++kk) {
@@ -477,13 +502,13 @@ JFA_BWD_INST(float, 32, 1) JFA_BWD_INST(float, 64, 1) JFA_BWD_INST(float, 128, 1
 
 // ---------------------------------------------------------------- launchers
 
-#define JFA_BWD_LAUNCHER(NAME, KERNEL)                                                                   \
+#define JFA_BWD_LAUNCHER(NAME, KERNEL, THREADS)                                                          \
   template <typename T, int ACT>                                                                         \
   static hipError_t NAME##_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {         \
     switch (head_dim) {                                                                                  \
-      case 32: hipLaunchKernelGGL((KERNEL<T, 32, ACT>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;  \
-      case 64: hipLaunchKernelGGL((KERNEL<T, 64, ACT>), dim3((unsigned)grid), dim3(256), 0, stream, a); break;  \
-      case 128: hipLaunchKernelGGL((KERNEL<T, 128, ACT>), dim3((unsigned)grid), dim3(256), 0, stream, a); break; \
+      case 32: hipLaunchKernelGGL((KERNEL<T, 32, ACT>), dim3((unsigned)grid), dim3(THREADS), 0, stream, a); break;  \
+      case 64: hipLaunchKernelGGL((KERNEL<T, 64, ACT>), dim3((unsigned)grid), dim3(THREADS), 0, stream, a); break;  \
+      case 128: hipLaunchKernelGGL((KERNEL<T, 128, ACT>), dim3((unsigned)grid), dim3(THREADS), 0, stream, a); break; \
       default: return hipErrorInvalidValue;                                                              \
     }                                                                                                    \
     return hipGetLastError();                                                                            \
@@ -497,7 +522,7 @@ JFA_BWD_INST(float, 32, 1) JFA_BWD_INST(float, 64, 1) JFA_BWD_INST(float, 128, 1
                     : NAME##_d<float, 1>(a, head_dim, grid, stream);                                     \
   }
 
-JFA_BWD_LAUNCHER(dkdv, dkdv_kernel)
-JFA_BWD_LAUNCHER(dq, dq_kernel)
+JFA_BWD_LAUNCHER(dkdv, dkdv_kernel, 512)
+JFA_BWD_LAUNCHER(dq, dq_kernel, 256)
 
 }  // namespace jfa

@@ -291,9 +291,28 @@ struct TileStage {
 // later LDS read wait for all copies in flight, which would serialise the
 // copies of stages that are meant to stay in flight behind the compute.
 // Completion is the caller's business (vector-memory counter, then barrier).
+// The assembly starts with 5 wait states: the buffer descriptor's scalar
+// registers may have just been written by a vector instruction
+// (readfirstlane), which a vector-memory read of them must not follow
+// sooner, and M0 may have just been written by a scalar instruction, which
+// an LDS copy must not follow in the next cycle.  The compiler inserts these
+// waits for its own instructions but cannot see into inline assembly.
 __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, int voff, const char* lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(JFA_LDS const char*)lds;
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+  const uint32_t m0 = (uint32_t)(uintptr_t)(JFA_LDS const char*)lds;   // the compiler moves it to M0
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+}
+
+// Raw buffer resource over `bytes` bytes at `base`, for values that are
+// uniform across each wave but that the compiler cannot prove uniform (they
+// depend on the wave index): passing them through readfirstlane lets it keep
+// the descriptor in scalar registers, which the buffer instructions need.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(bytes);
+  void* p = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, n, kBufferWord3);
 }
 
 // A ROWS x D tile of one head copied straight from global memory into a
@@ -302,35 +321,51 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, i
 // LDS, so every lane loads the global chunk that the swizzle maps to its LDS
 // slot.  Rows past the sequence's end read as zeros (the buffer covers only
 // the sequence's rows).  With SWAP, LDS row r holds tile row swap23(r).
-// Completion is tracked by the wave's vector-memory counter: wait for it
-// (dma_wait) and then barrier before any wave reads the tile.
+// When the tile has fewer chunks than N * NT, the surplus waves still issue
+// their loads (so that every wave issues the same number), reading past the
+// buffer (zeros) into `sink`, 1 KB of LDS per wave of the workgroup (each
+// wave writes only its own KB).  Completion is tracked by the
+// wave's vector-memory counter: wait for it and then barrier before any wave
+// reads the tile.
 template <typename T, int D, int ROWS, bool SWAP, int NT = 256>
 struct TileDma {
   using S = Swz<T, D>;
   static constexpr int CH = S::CH;
-  static constexpr int N = ROWS * CH / NT;   // loads per thread per tile
-  static_assert(ROWS * CH % NT == 0, "tile must split evenly over the threads");
-  int voff[N];                               // per-thread byte offsets into the tile's rows
+  static constexpr int CHUNKS = ROWS * CH;
+  static constexpr int N = (CHUNKS + NT - 1) / NT;   // loads per thread per tile
+  static_assert(CHUNKS % kWave == 0, "a wave's loads must be all in the tile or all surplus");
+  static constexpr int kPastEnd = 0x7ffffff0;        // offset beyond any buffer: reads zeros
+  int voff[N];                                       // per-thread byte offsets into the tile's rows
 
   __device__ __forceinline__ void init(int row_stride, int tid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      int r, c;
-      S::inv(i * NT + tid, r, c);
-      const int row = SWAP ? swap23(r) : r;
-      voff[i] = row * row_stride * (int)sizeof(T) + c * 16;
+      const int p = i * NT + tid;
+      if (p < CHUNKS) {
+        int r, c;
+        S::inv(p, r, c);
+        const int row = SWAP ? swap23(r) : r;
+        voff[i] = row * row_stride * (int)sizeof(T) + c * 16;
+      } else {
+        voff[i] = kPastEnd;
+      }
     }
   }
   // rows row0 .. row0+ROWS-1 of a sequence whose row j starts at
   // base + j*row_stride elements and which has nrows rows (row0 < nrows)
-  __device__ __forceinline__ void issue(char* tile, const T* base, int row_stride, int row0, int nrows,
-                                        int tid) const {
+  __device__ __forceinline__ void issue(char* tile, const T* base, int row_stride, int row0, int nrows, int tid,
+                                        char* sink = nullptr) const {
     const int valid = min(ROWS, nrows - row0);
+    // base, row0 and nrows are uniform across the workgroup, so the
+    // compiler keeps the descriptor in scalar registers
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T*>(base + (size_t)row0 * row_stride), 0, valid * row_stride * (int)sizeof(T), kBufferWord3);
-    const int wave_base = (tid & ~(kWave - 1)) * 16;
+    const int wave0 = tid & ~(kWave - 1);
 #pragma unroll
-    for (int i = 0; i < N; ++i) buffer_load_lds16(rsrc, voff[i], tile + i * NT * 16 + wave_base);
+    for (int i = 0; i < N; ++i) {
+      const bool real = (N * NT == CHUNKS) || (i * NT + wave0 < CHUNKS);
+      buffer_load_lds16(rsrc, voff[i], real ? tile + (i * NT + wave0) * 16 : sink + wave0 * 16);
+    }
   }
 };
 
@@ -355,14 +390,19 @@ __device__ __forceinline__ void settle(const X& x) {
   asm volatile("" ::"v"(x));
 }
 
-// Per-row (lse * log2(e), delta) pairs of rows row0 .. row0+valid-1 (valid
-// <= 64) copied into `dst` (1 KB of LDS; pairs past `valid` read as zeros).
-// Every wave that calls it writes the same bytes, so that all waves issue the
-// same number of copies per stage.
-__device__ __forceinline__ void stats_dma(char* dst, const float2* base, int row0, int valid) {
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float2*>(base + row0), 0, valid * (int)sizeof(float2), kBufferWord3);
-  buffer_load_lds16(rsrc, lane_id() * 16, dst);
+// One buffer load that writes LDS with 4 bytes per lane: lane l's dword
+// lands at lds + 4*l (256 bytes per wave).  Same contract and the same
+// leading wait states as buffer_load_lds16.
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t rsrc, int voff, const char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(JFA_LDS const char*)lds;   // the compiler moves it to M0
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+}
+
+// Per-row values base[row0 .. row0+63] of a sequence with nrows rows copied
+// into this wave's own 256 bytes of LDS at `dst` (rows past the sequence
+// read as zeros).  Each wave copies into a region no other wave writes.
+__device__ __forceinline__ void rows_dma(char* dst, const float* base, int row0, int nrows) {
+  buffer_load_lds4(uniform_rsrc(base + row0, min(64, nrows - row0) * (int)sizeof(float)), lane_id() * 4, dst);
 }
 
 template <typename T>

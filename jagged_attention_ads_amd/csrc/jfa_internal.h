@@ -64,8 +64,9 @@ struct BwdArgs {
   const int32_t* n_items_q;
   const int2* items_kv;    // key-tile list (dK/dV pass)
   const int32_t* n_items_kv;
-  float2* stats;           // [heads, total_q] workspace: (lse * log2(e), delta) per row,
-                           // written by the dQ pass, read by the dK/dV pass
+  float* lse2;             // [heads, total_q] workspace: lse * log2(e) per row, and
+  float* delta;            // [heads, total_q] delta per row; both written by the dQ pass
+                           // (softmax), read by the dK/dV pass
   void* dq;
   void* dk;
   void* dv;
