@@ -6,7 +6,7 @@
 // The gradient sums over queries (dK, dV) and over keys (dQ) are split into
 // two passes so that every output row is owned by exactly one workgroup and
 // stored once:
-//   dK/dV pass -- one work item per (sequence, head, 128-key tile); each
+//   dK/dV pass -- one work item per (sequence, head, 64-key tile); each
 //     pair of waves owns 32 keys and walks the query rows that see them in
 //     32-row sub-blocks.  P and dS are recomputed from lse (softmax) or from
 //     the scores (SiLU).
@@ -105,32 +105,34 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 
 // ---------------------------------------------------------------- dK / dV
 
-// Eight waves per item: four pairs, each pair owning 32 keys.  Wave A of a
+// Four waves per 64-key item: two pairs, each pair owning 32 keys.  Wave A of a
 // pair forms S = Q K^T and P (masks applied) and accumulates dV^T += dO^T P;
 // wave B forms dP = dO V^T, takes P from wave A through LDS, forms dS and
 // accumulates dK^T += Q^T dS.  The matrix work splits evenly, nothing is
 // computed twice, and a wave's registers (one of K or V, one accumulator
-// set) fit two waves per SIMD, so one wave's vector work and LDS waits
-// overlap the other's products.  Per 32-row sub-block n, one barrier: A
+// set) and the item's LDS fit two workgroups per CU: one's vector work, LDS
+// waits and prologue overlap the other's products.  Per 32-row sub-block n, one barrier: A
 // hands over P(n) (or, for SiLU, the derivative factor) before it, B reads
 // it after.
 template <typename T, int D>
 struct DkdvCfg {
-  static constexpr int BN = kBwdBN, NT = 512;
+  static constexpr int BN = kBwdBN;
+  static constexpr int NPAIRS = BN / 32;                 // 32-key slices per item
+  static constexpr int NT = NPAIRS * 2 * kWave;          // an A and a B wave per slice
   static constexpr int ES = sizeof(T);
   static constexpr int SR = 32;                          // query rows per stage = one sub-block
   static constexpr int QT = Swz<T, D>::tile_bytes(SR);   // Q or dO tile
   static constexpr int STATS = NT / 64 * 256;            // per wave: its 64 rows of lse2 or delta
   static constexpr int STAGE = 2 * QT + STATS;
-  static constexpr int XCH = 4 * 2 * 4096;               // per pair: two 32 x 32 fp32 hand-over slots
+  static constexpr int XCH = NPAIRS * 2 * 4096;          // per pair: two 32 x 32 fp32 hand-over slots
   static constexpr int SINK = NT / 64 * 1024;            // surplus tile loads, 1 KB per wave
-  static constexpr int NS = (4 * STAGE + XCH + SINK <= 160 * 1024) ? 4 : 3;   // stages in the ring
+  static constexpr int NS = 3;                           // stages in the ring
   static constexpr int LDS = NS * STAGE + XCH + SINK;
   static constexpr int ND = D / 32, NK = D / 16;
 };
 
 template <typename T, int D, int ACT>
-__global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<T, D>;
   using Dma = TileDma<T, D, C::SR, true, C::NT>;   // query rows stored swap23-permuted
   constexpr int NPS = 2 * Dma::N + (ACT == 0 ? 1 : 0);   // copies per thread per stage
@@ -146,8 +148,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(BwdArgs a) {
   const int off = lk - lq;
 
   const int tid = threadIdx.x, l = lane_id(), w = tid >> 6, g = l >> 5, c32 = l & 31;
-  const int pair = w & 3;
-  const bool role_a = w < 4;               // A: S, P, dV;  B: dP, dS, dK
+  const int pair = w % C::NPAIRS;
+  const bool role_a = w < C::NPAIRS;       // A: S, P, dV;  B: dP, dS, dK
   const int kw0 = t * C::BN + 32 * pair;   // first key of this pair
   const int my_key = kw0 + c32;            // the key this lane owns (its column of S)
   const bool wave_live = kw0 < lk;
@@ -522,7 +524,7 @@ JFA_BWD_INST(float, 32, 1) JFA_BWD_INST(float, 64, 1) JFA_BWD_INST(float, 128, 1
                     : NAME##_d<float, 1>(a, head_dim, grid, stream);                                     \
   }
 
-JFA_BWD_LAUNCHER(dkdv, dkdv_kernel, 512)
+JFA_BWD_LAUNCHER(dkdv, dkdv_kernel, 256)
 JFA_BWD_LAUNCHER(dq, dq_kernel, 256)
 
 }  // namespace jfa

@@ -11,7 +11,7 @@ namespace jfa {
 // Tile geometry, shared by the launchers and the host-side sizing code.
 constexpr int kFwdBM = 128;     // query rows per forward / dQ work item
 constexpr int kFwdBN = 64;      // key rows per forward / dQ inner step
-constexpr int kBwdBN = 128;     // key rows per dK/dV work item
+constexpr int kBwdBN = 64;      // key rows per dK/dV work item
 constexpr int kBwdBM = 64;      // query rows per dK/dV inner step
 constexpr int kMaxBuckets = 1024;   // distinct tile costs the scheduler can sort
 constexpr int kMaxHeads = 256;      // head index is packed into 8 bits
