@@ -241,7 +241,7 @@ def main():
 
     K = args.steps
     ef = [ev.create(3) for _ in range(K)]
-    eb = [ev.create(5) for _ in range(K)] if run_bwd else []
+    eb = [ev.create(4) for _ in range(K)] if run_bwd else []
     edge = ev.create(2)
     torch.cuda.synchronize()
     ev.lib.hipEventRecord(edge[0], stream)
@@ -260,9 +260,8 @@ def main():
     fwd_ms = avg(ef, 0, 2)
     bwd_ms = 0.0
     if run_bwd:
-        kern_ms.update({"bwd_sched_q": avg(eb, 0, 1), "bwd_dq": avg(eb, 1, 2), "bwd_sched_kv": avg(eb, 2, 3),
-                        "bwd_dkdv": avg(eb, 3, 4)})
-        bwd_ms = avg(eb, 0, 4)
+        kern_ms.update({"bwd_sched": avg(eb, 0, 1), "bwd_dq": avg(eb, 1, 2), "bwd_dkdv": avg(eb, 2, 3)})
+        bwd_ms = avg(eb, 0, 3)
 
     pairs = int(visible_pairs(batch.q_lengths, batch.kv_lengths, wl.causal).sum())
     useful_fwd = 4.0 * D * H * pairs

@@ -106,7 +106,9 @@ int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_of
  * formed by key-tile-major work items and dQ by query-tile-major ones, each
  * output row summed in registers and stored once).  out and lse are the
  * forward's outputs; both may be NULL only for JFA_ACT_SILU.  Results are
- * bitwise reproducible from run to run. */
+ * bitwise reproducible from run to run.  Enqueues: the work-list builder
+ * (both lists), the dQ kernel (which also writes the per-row softmax
+ * statistics into the workspace), then the dK/dV kernel. */
 int jfa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
                  int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
@@ -117,10 +119,10 @@ int jfa_backward(const void* q, const void* k, const void* v, const void* out, c
  * `stream` between their kernel launches, for per-kernel timing (every
  * kernel still runs; with events == NULL they are jfa_forward and
  * jfa_backward).  Forward: 3 events -- [0] before the work-list builder,
- * [1] before the attention kernel, [2] after it.  Backward: 5 events --
- * [0] start, [1] after the query-tile work list, [2] after the dQ kernel
- * (which also forms the per-row softmax statistics), [3] after the key-tile
- * work list, [4] after the dK/dV kernel.  Events are not recorded when the
+ * [1] before the attention kernel, [2] after it.  Backward: 4 events --
+ * [0] start, [1] after the work-list builder (both lists, one launch),
+ * [2] after the dQ kernel (which also forms the per-row softmax
+ * statistics), [3] after the dK/dV kernel.  Events are not recorded when the
  * call is a no-op or is rejected. */
 int jfa_forward_profiled(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                          const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,

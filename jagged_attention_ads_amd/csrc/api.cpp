@@ -269,28 +269,28 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   a.scale_log2 = scale * 1.4426950408889634f;
 
   if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
-  if (total_q > 0) {
+  if (total_q > 0 && total_kv > 0) {
+    e = jfa::launch_sched_pair(q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq, nbk,
+                               ws + L.off_wkv, L.wkv, stream);
+  } else if (total_q > 0) {
     e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq, stream);
-    if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+  } else {
+    e = jfa::launch_sched(jfa::kPassKV, q_offsets, kv_offsets, batch, heads, causal, nbk, ws + L.off_wkv, L.wkv,
+                          stream);
   }
+  if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
   if ((e = record(events, 1, stream)) != hipSuccess) return hip_fail(e, "event record");
-  // dQ first: it also writes the per-row (lse, delta) pairs the dK/dV pass reads
+  // dQ first: it also writes the per-row lse and delta the dK/dV pass reads
   if (total_q > 0) {
     e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, L.wq.capacity, stream);
     if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
   }
   if ((e = record(events, 2, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (total_kv > 0) {
-    e = jfa::launch_sched(jfa::kPassKV, q_offsets, kv_offsets, batch, heads, causal, nbk, ws + L.off_wkv, L.wkv,
-                          stream);
-    if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
-  }
-  if ((e = record(events, 3, stream)) != hipSuccess) return hip_fail(e, "event record");
-  if (total_kv > 0) {
     e = jfa::launch_bwd_dkdv(a, head_dim, dtype, activation, L.wkv.capacity, stream);
     if (e != hipSuccess) return hip_fail(e, "dK/dV kernel launch");
   }
-  if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = record(events, 3, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;
 }
 

@@ -31,6 +31,10 @@ WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t t
 hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                         int32_t causal, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
                         hipStream_t stream);
+// Both passes' lists in one launch (two workgroups).
+hipError_t launch_sched_pair(const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads, int32_t causal,
+                             int32_t nb_q, void* wl_q, const WorklistLayout& lay_q, int32_t nb_kv, void* wl_kv,
+                             const WorklistLayout& lay_kv, hipStream_t stream);
 
 struct FwdArgs {
   const void* q;

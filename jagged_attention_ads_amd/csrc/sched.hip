@@ -75,14 +75,25 @@ struct TileRule {
   __device__ static bool after_or_eq(int x, int c) { return PASS == kPassQ ? x >= c : x <= c; }
 };
 
+// One pass's work list: where it goes and how it is built.
+struct SchedJob {
+  int nbuckets;
+  int64_t capacity;
+  int stage_seqs;
+  int* count;
+  int2* items;
+  int* tile_start;
+};
+
 template <int PASS>
-__global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restrict__ qo, const int* __restrict__ ko,
-                                                              int B, int H, int causal, int nbuckets,
-                                                              int64_t capacity, int stage_seqs,
-                                                              int* __restrict__ count, int2* __restrict__ items,
-                                                              int* __restrict__ tile_start) {
+__device__ void sched_body(const int* __restrict__ qo, const int* __restrict__ ko, int B, int H, int causal,
+                           const SchedJob& job, char* smem) {
   using R = TileRule<PASS>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nbuckets = job.nbuckets, stage_seqs = job.stage_seqs;
+  const int64_t capacity = job.capacity;
+  int* const count = job.count;
+  int2* const items = job.items;
+  int* const tile_start = job.tile_start;
   int* hist = reinterpret_cast<int*>(smem);
   int* start = hist + nbuckets;
   int* carry = start + nbuckets;
@@ -233,6 +244,23 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
   if (tid == 0) *count = H * total_tiles;
 }
 
+template <int PASS>
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restrict__ qo, const int* __restrict__ ko,
+                                                              int B, int H, int causal, SchedJob job) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  sched_body<PASS>(qo, ko, B, H, causal, job, smem);
+}
+
+// Both passes' lists in one launch: workgroup 0 builds the query-tile list,
+// workgroup 1 the key-tile list.
+__global__ __launch_bounds__(kSchedThreads) void sched_pair_kernel(const int* __restrict__ qo,
+                                                                   const int* __restrict__ ko, int B, int H,
+                                                                   int causal, SchedJob jq, SchedJob jkv) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  if (blockIdx.x == 0) sched_body<kPassQ>(qo, ko, B, H, causal, jq, smem);
+  else sched_body<kPassKV>(qo, ko, B, H, causal, jkv, smem);
+}
+
 WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t total_rows) {
   const int64_t tile = pass == kPassQ ? kFwdBM : kBwdBN;
   // sum over sequences of ceil(L_b / tile) <= (total + batch * (tile - 1)) / tile
@@ -246,22 +274,43 @@ WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t t
   return lay;
 }
 
+// The job of one pass and the dynamic LDS it needs.
+static SchedJob make_job(int32_t batch, int32_t nbuckets, void* wl_base, const WorklistLayout& lay, size_t& lds) {
+  char* base = static_cast<char*>(wl_base);
+  SchedJob j;
+  j.nbuckets = nbuckets;
+  j.capacity = lay.capacity;
+  lds = sched_lds_fixed(nbuckets);
+  j.stage_seqs = lds + sched_lds_seqs(batch) <= kSchedMaxLds ? 1 : 0;
+  if (j.stage_seqs) lds += sched_lds_seqs(batch);
+  j.count = reinterpret_cast<int*>(base);
+  j.items = reinterpret_cast<int2*>(base + lay.items_off);
+  j.tile_start = reinterpret_cast<int*>(base + lay.tile_start_off);
+  return j;
+}
+
 hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                         int32_t causal, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
                         hipStream_t stream) {
-  char* base = static_cast<char*>(wl_base);
-  int* count = reinterpret_cast<int*>(base);
-  int2* items = reinterpret_cast<int2*>(base + lay.items_off);
-  int* tile_start = reinterpret_cast<int*>(base + lay.tile_start_off);
-  size_t lds = sched_lds_fixed(nbuckets);
-  const int stage = lds + sched_lds_seqs(batch) <= kSchedMaxLds ? 1 : 0;
-  if (stage) lds += sched_lds_seqs(batch);
+  size_t lds;
+  const SchedJob j = make_job(batch, nbuckets, wl_base, lay, lds);
   if (pass == kPassQ)
     hipLaunchKernelGGL(sched_kernel<kPassQ>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
-                       causal, nbuckets, lay.capacity, stage, count, items, tile_start);
+                       causal, j);
   else
     hipLaunchKernelGGL(sched_kernel<kPassKV>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
-                       causal, nbuckets, lay.capacity, stage, count, items, tile_start);
+                       causal, j);
+  return hipGetLastError();
+}
+
+hipError_t launch_sched_pair(const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads, int32_t causal,
+                             int32_t nb_q, void* wl_q, const WorklistLayout& lay_q, int32_t nb_kv, void* wl_kv,
+                             const WorklistLayout& lay_kv, hipStream_t stream) {
+  size_t lds_q, lds_kv;
+  const SchedJob jq = make_job(batch, nb_q, wl_q, lay_q, lds_q);
+  const SchedJob jkv = make_job(batch, nb_kv, wl_kv, lay_kv, lds_kv);
+  hipLaunchKernelGGL(sched_pair_kernel, dim3(2), dim3(kSchedThreads), lds_q > lds_kv ? lds_q : lds_kv, stream, qo,
+                     ko, batch, heads, causal, jq, jkv);
   return hipGetLastError();
 }
 
