@@ -29,9 +29,11 @@ struct WsLayout {
   size_t off_wq = 0, off_wkv = 0, off_stats = 0, bytes = 0;
 };
 
+// Forward: the query-tile list.  Backward: the dQ-tile list (in the same
+// slot), the key-tile list and the per-row statistics.
 WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv, bool backward) {
   WsLayout L;
-  L.wq = jfa::worklist_layout(jfa::kPassQ, batch, heads, total_q);
+  L.wq = jfa::worklist_layout(backward ? jfa::kPassDQ : jfa::kPassQ, batch, heads, total_q);
   L.off_wq = 0;
   size_t off = L.wq.bytes;
   if (backward) {
@@ -119,10 +121,14 @@ size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_
   return ws_layout(batch, heads, total_q, total_kv, for_backward != 0).bytes;
 }
 
+bool valid_pass(int32_t pass) {
+  return pass == JFA_PASS_QUERY_TILES || pass == JFA_PASS_KEY_TILES || pass == JFA_PASS_DQ_TILES;
+}
+
 size_t jfa_worklist_bytes(int32_t pass, int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv) {
-  if (pass != JFA_PASS_QUERY_TILES && pass != JFA_PASS_KEY_TILES) return 0;
+  if (!valid_pass(pass)) return 0;
   if (check_sizes(batch, heads, 32, total_q, total_kv, 0, 0) != JFA_OK) return 0;
-  return jfa::worklist_layout(pass, batch, heads, pass == JFA_PASS_QUERY_TILES ? total_q : total_kv).bytes;
+  return jfa::worklist_layout(pass, batch, heads, pass == JFA_PASS_KEY_TILES ? total_kv : total_q).bytes;
 }
 
 int jfa_tile_shape(int32_t pass, int32_t* tile_rows, int32_t* block_rows) {
@@ -133,6 +139,9 @@ int jfa_tile_shape(int32_t pass, int32_t* tile_rows, int32_t* block_rows) {
   } else if (pass == JFA_PASS_KEY_TILES) {
     *tile_rows = jfa::kBwdBN;
     *block_rows = jfa::kBwdBM;
+  } else if (pass == JFA_PASS_DQ_TILES) {
+    *tile_rows = jfa::kDqBM;
+    *block_rows = jfa::kDqBN;
   } else {
     return fail(JFA_ERR_INVALID_ARGUMENT, "bad pass");
   }
@@ -142,17 +151,17 @@ int jfa_tile_shape(int32_t pass, int32_t* tile_rows, int32_t* block_rows) {
 int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
                        int32_t heads, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
                        int32_t causal, void* out, size_t out_bytes, hipStream_t stream) {
-  if (pass != JFA_PASS_QUERY_TILES && pass != JFA_PASS_KEY_TILES)
-    return fail(JFA_ERR_INVALID_ARGUMENT, "bad pass");
+  if (!valid_pass(pass)) return fail(JFA_ERR_INVALID_ARGUMENT, "bad pass");
   if (!q_offsets || !kv_offsets) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL offsets pointer");
   if (causal != 0 && causal != 1) return fail(JFA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   int st = check_sizes(batch, heads, 32, total_q, total_kv, max_q_len, max_kv_len);
   if (st != JFA_OK) return st;
   const int32_t nb = pass == JFA_PASS_QUERY_TILES ? buckets_for(max_kv_len, jfa::kFwdBN)
-                                                  : buckets_for(max_q_len, jfa::kBwdBM);
+                     : pass == JFA_PASS_DQ_TILES    ? buckets_for(max_kv_len, jfa::kDqBN)
+                                                    : buckets_for(max_q_len, jfa::kBwdBM);
   if (nb > jfa::kMaxBuckets) return fail(JFA_ERR_UNSUPPORTED, "maximum length exceeds the scheduler's range");
   const jfa::WorklistLayout lay =
-      jfa::worklist_layout(pass, batch, heads, pass == JFA_PASS_QUERY_TILES ? total_q : total_kv);
+      jfa::worklist_layout(pass, batch, heads, pass == JFA_PASS_KEY_TILES ? total_kv : total_q);
   if (batch == 0) return JFA_OK;
   if (!out) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL output pointer");
   if (out_bytes < lay.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "worklist buffer too small");
@@ -233,7 +242,7 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
     if (total_q > 0 && (!out || !lse)) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL out or lse for softmax");
     if (!aligned16(out)) return fail(JFA_ERR_INVALID_ARGUMENT, "out not 16-byte aligned");
   }
-  const int32_t nbq = buckets_for(max_kv_len, jfa::kFwdBN);
+  const int32_t nbq = buckets_for(max_kv_len, jfa::kDqBN);
   const int32_t nbk = buckets_for(max_q_len, jfa::kBwdBM);
   if (nbq > jfa::kMaxBuckets || nbk > jfa::kMaxBuckets)
     return fail(JFA_ERR_UNSUPPORTED, "maximum length exceeds the scheduler's range");
@@ -273,7 +282,8 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
     e = jfa::launch_sched_pair(q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq, nbk,
                                ws + L.off_wkv, L.wkv, stream);
   } else if (total_q > 0) {
-    e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq, stream);
+    e = jfa::launch_sched(jfa::kPassDQ, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq,
+                          stream);
   } else {
     e = jfa::launch_sched(jfa::kPassKV, q_offsets, kv_offsets, batch, heads, causal, nbk, ws + L.off_wkv, L.wkv,
                           stream);

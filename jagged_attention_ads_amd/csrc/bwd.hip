@@ -324,24 +324,38 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dQ
 
+// Four waves per 64-query item: two pairs, each owning 32 queries.  Wave A
+// of a pair forms S^T = K Q^T for 32-key sub-block n and from it P (softmax)
+// or silu'(x)/Lk (SiLU), which it hands over through LDS; wave B runs one
+// sub-block behind: it forms dS^T of sub-block n-1 from its own
+// dP^T = V dO^T and the handed-over values, accumulates dQ^T += K^T dS^T,
+// then forms dP^T of sub-block n.  A's exponentials overlap B's products on
+// the same SIMD; one barrier per sub-block.  Every lane owns one query, so
+// lse and delta are per-lane scalars (written here for the dK/dV pass).
 template <typename T, int D>
 struct DqCfg {
-  static constexpr int BM = kFwdBM, NT = 256;
-  static constexpr int ES = sizeof(T);
-  static constexpr int SR = (D * ES >= 128) ? 32 : 64;   // key rows per stage (>= 256 chunks)
-  static constexpr int SPS = SR / 32;                    // 32-key sub-blocks per stage
+  static constexpr int BM = kDqBM;
+  static constexpr int NPAIRS = BM / 32;
+  static constexpr int NT = NPAIRS * 2 * kWave;
+  static constexpr int SR = 32;                          // key rows per stage = one sub-block
   static constexpr int KT = Swz<T, D>::tile_bytes(SR);   // K or V tile
   static constexpr int STAGE = 2 * KT;
-  static constexpr int LDS = kStages * STAGE;
+  static constexpr int XCH = NPAIRS * 2 * 4096;          // per pair: two 32 x 32 fp32 hand-over slots
+  using Dma = TileDma<T, D, SR, true, NT>;               // key rows stored swap23-permuted
+  static constexpr int SINK = Dma::N * NT > Dma::CHUNKS ? NT / kWave * 1024 : 0;
+  static constexpr int NS = (4 * STAGE + XCH + SINK <= 80 * 1024) ? 4 : 3;   // two workgroups per CU
+  static constexpr int LDS = NS * STAGE + XCH + SINK;
   static constexpr int ND = D / 32, NK = D / 16;
 };
 
 template <typename T, int D, int ACT>
-__global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   using C = DqCfg<T, D>;
-  using Dma = TileDma<T, D, C::SR, true>;   // key rows stored swap23-permuted
-  constexpr int NPS = 2 * Dma::N;
+  using Dma = typename C::Dma;
+  constexpr int NPS = 2 * Dma::N;   // copies per thread per stage
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  char* const xch = smem + C::NS * C::STAGE;
+  char* const sink = xch + C::XCH;
 
   if ((int)blockIdx.x >= *a.n_items_q) return;
   int b, h, t;
@@ -351,11 +365,12 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void dq_
   const int off = lk - lq;
 
   const int tid = threadIdx.x, l = lane_id(), w = tid >> 6, g = l >> 5, c32 = l & 31;
-  const int row0 = t * C::BM + 32 * w;
-  const int my_row = row0 + c32;
+  const int pair = w % C::NPAIRS;
+  const bool role_a = w < C::NPAIRS;         // A: S, P;  B: dP, dS, dQ
+  const int row0 = t * C::BM + 32 * pair;    // first query of this pair
+  const int my_row = row0 + c32;             // the query this lane owns
   const bool wave_live = row0 < lq;
   const int nst = q_tile_kv_blocks(lq, lk, t, C::BM, C::SR, a.causal);
-  const int nsub = nst * C::SPS;
   const int rs = a.heads * D;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
 
@@ -363,58 +378,61 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void dq_
   const T* vb = static_cast<const T*>(a.v) + (size_t)ks * rs + (size_t)h * D;
   Dma dma;   // K and V tiles share the geometry
   dma.init(rs, tid);
-  auto slot = [&](int s) { return smem + (s & (kStages - 1)) * C::STAGE; };
+  auto slot = [&](int s) { return smem + (s % C::NS) * C::STAGE; };
   auto issue_stage = [&](int s) {
     char* st = slot(s);
-    dma.issue(st, kb, rs, s * C::SR, lk, tid);
-    dma.issue(st + C::KT, vb, rs, s * C::SR, lk, tid);
+    dma.issue(st, kb, rs, s * C::SR, lk, tid, sink);
+    dma.issue(st + C::KT, vb, rs, s * C::SR, lk, tid, sink);
   };
-  // Prologue: stages 0 and 1, then this lane's query and output-gradient
-  // rows and statistics; all of it lands before the loop.
+
+  // Prologue: stages 0 and 1, then this lane's query (A) or output-gradient
+  // (B) row and its statistic; all of it lands before the loop.
   for (int s = 0; s < min(2, nst); ++s) issue_stage(s);
-  frag_t<T> qf[C::NK], df[C::NK];
-  float lse2 = 0.f, dlt = 0.f;
+  frag_t<T> xf[C::NK];
+  float stat = 0.f;   // A: lse2;  B: delta
   {
     const int r = min(my_row, lq - 1);
-    const T* qp = static_cast<const T*>(a.q) + (size_t)(qs + r) * rs + (size_t)h * D + 8 * g;
-    const T* dp = static_cast<const T*>(a.dout) + (size_t)(qs + r) * rs + (size_t)h * D + 8 * g;
+    const size_t ro = (size_t)(qs + r) * rs + (size_t)h * D + 8 * g;
+    const T* xp = static_cast<const T*>(role_a ? a.q : a.dout) + ro;
 #pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) {
-      qf[kk] = global_frag<T>(qp + 16 * kk);
-      df[kk] = global_frag<T>(dp + 16 * kk);
-    }
+    for (int kk = 0; kk < C::NK; ++kk) xf[kk] = global_frag<T>(xp + 16 * kk);
     if (ACT == 0) {
-      // delta of this lane's row: each lane group holds half the row's
-      // d-slots, summed across the two groups; stored with lse2 for the
-      // dK/dV pass
-      const T* op = static_cast<const T*>(a.out) + (size_t)(qs + r) * rs + (size_t)h * D + 8 * g;
-      frag_t<T> of[C::NK];
-#pragma unroll
-      for (int kk = 0; kk < C::NK; ++kk) of[kk] = global_frag<T>(op + 16 * kk);
       const size_t si = (size_t)h * a.total_q + qs + r;
-      lse2 = lse_log2(a.lse[si]);
-      float part = 0.f;
+      if (role_a) {
+        stat = lse_log2(a.lse[si]);
+      } else {
+        // delta of this lane's row: each lane group holds half the row's
+        // d-slots, summed across the two groups
+        const T* op = static_cast<const T*>(a.out) + ro;
+        float part = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < C::NK; ++kk) part += frag_dot(of[kk], df[kk]);
-      dlt = xor32_sum(part);
-      if (my_row < lq) {
-        if (g == 0) a.lse2[si] = lse2;
-        else a.delta[si] = dlt;
+        for (int kk = 0; kk < C::NK; ++kk) part += frag_dot(global_frag<T>(op + 16 * kk), xf[kk]);
+        stat = xor32_sum(part);
       }
+      if (g == 0 && my_row < lq) (role_a ? a.lse2 : a.delta)[si] = stat;
     }
 #pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) {
-      settle(qf[kk]);
-      settle(df[kk]);
-    }
-    settle(lse2);
-    settle(dlt);
+    for (int kk = 0; kk < C::NK; ++kk) settle(xf[kk]);
+    settle(stat);
   }
+  dma_wait();
+  __syncthreads();
+  for (int s = 2; s <= C::NS - 2; ++s)
+    if (s < nst) issue_stage(s);
 
-  f32x16 dq[C::ND];
+  f32x16 dq[C::ND];   // B: dQ^T (d x queries), lane = query
 #pragma unroll
   for (int i = 0; i < C::ND; ++i) dq[i] = f32x16{};
 
+  // S^T (A) or dP^T (B) of sub-block n: 32 keys x 32 queries; register r
+  // holds key 32*n + 16*(r/8) + 8*g + r%8 of this lane's query
+  auto products = [&](f32x16& x, const char* tile) {
+    x = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) mma(x, lds_row_frag<T, D>(tile, c32, 16 * kk + 8 * g), xf[kk]);
+  };
+  // hand-over slot of sub-block n: [r/4][lane][4] floats
+  auto xslot = [&](int n) { return xch + (pair * 2 + (n & 1)) * 4096; };
   auto visible = [&](int n) { return wave_live && (!a.causal || 32 * n <= row0 + 31 + off); };
   auto needs_mask = [&](int n) {
     return (32 * n + 32 > lk) || (a.causal && 32 * n + 31 > row0 + off) || (row0 + 32 > lq);
@@ -422,73 +440,77 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void dq_
   // keys at offset >= this (relative to the sub-block's first key + 8*g) are masked
   const int key_end = my_row < lq ? min(lk, a.causal ? my_row + off + 1 : lk) - 8 * g : -(1 << 30);
 
-  // S^T and dP^T (32 keys x 32 queries) of sub-block n; register r holds key
-  // 32*n + 16*(r/8) + 8*g + r%8
-  auto products = [&](f32x16& s, f32x16& dp, int n) {
-    const char* kt = slot(n / C::SPS);
-    const char* vt = kt + C::KT;
-    const int rl = 32 * (n % C::SPS);
-    s = f32x16{};
-    dp = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) {
-      mma(s, lds_row_frag<T, D>(kt, rl + c32, 16 * kk + 8 * g), qf[kk]);
-      mma(dp, lds_row_frag<T, D>(vt, rl + c32, 16 * kk + 8 * g), df[kk]);
-    }
-  };
-
-  auto sub_step = [&](auto MASK, auto NEXT, f32x16& s, f32x16& dp, f32x16& s_nxt, f32x16& dp_nxt, int n) {
+  // Wave A: the value B needs for sub-block n, written to its hand-over slot
+  auto a_weights = [&](auto MASK, f32x16& x, int n) {
     constexpr bool kMask = decltype(MASK)::value;
-    constexpr bool kNext = decltype(NEXT)::value;
-    const char* kt = slot(n / C::SPS);
-    const int rl = 32 * (n % C::SPS);
-    if constexpr (kNext) products(s_nxt, dp_nxt, n + 1);
     const int lim = key_end - 32 * n;
+    f32x16 e_out;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int c = 16 * (r >> 3) + (r & 7);
       bool masked = false;
       if constexpr (kMask) masked = c >= lim;
-      float p, ds;
-      p_ds<ACT>(s[r], dp[r], lse2, dlt, a.scale, a.scale_log2, inv_lk, masked, p, ds);
-      dp[r] = ds;
+      if constexpr (ACT == 0) {
+        const float p = fast_exp2(fmaf(x[r], a.scale_log2, -stat));
+        e_out[r] = masked ? 0.f : p;
+      } else {
+        const float xs = x[r] * a.scale;
+        const float sig = fast_rcp(1.0f + fast_exp2(-x[r] * a.scale_log2));
+        const float keep = masked ? 0.f : inv_lk;
+        e_out[r] = sig * (1.0f + xs * (1.0f - sig)) * keep;
+      }
     }
-    // dQ^T (D x 32 queries) += K^T dS^T; k-step ss covers keys 16*ss .. +15
+    char* xo = xslot(n) + l * 16;
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      const frag_t<T> sf = pack_frag<T>(dp, ss);
-#pragma unroll
-      for (int d2 = 0; d2 < C::ND; ++d2) mma(dq[d2], lds_col_frag<T, D, true>(kt, rl + 16 * ss, 32 * d2), sf);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 v = {e_out[4 * q4], e_out[4 * q4 + 1], e_out[4 * q4 + 2], e_out[4 * q4 + 3]};
+      *reinterpret_cast<f32x4*>(xo + q4 * 1024) = v;
     }
   };
 
-  auto iter = [&](int n, f32x16& s, f32x16& dp, f32x16& s_nxt, f32x16& dp_nxt) {
-    const bool has_next = n + 1 < nsub;
-    if (has_next && (n + 1) % C::SPS == 0) {
-      const int st = (n + 1) / C::SPS;
-      wait_stage<NPS>(min(kStages - 3, nst - 1 - st));
-      __syncthreads();
-      if (st + kStages - 2 < nst) issue_stage(st + kStages - 2);
+  f32x16 dp_prev;             // B: dP^T of the previous sub-block
+  bool prev_visible = false;
+  for (int n = 0; n <= nst; ++n) {
+    const bool cur = n < nst && visible(n);
+    if (role_a) {
+      if (cur) {
+        f32x16 x;
+        products(x, slot(n));   // K rows of stage n
+        if (needs_mask(n)) a_weights(std::true_type{}, x, n);
+        else a_weights(std::false_type{}, x, n);
+      }
+    } else {
+      if (prev_visible) {
+        // dS^T of sub-block n-1, then dQ^T += K^T dS^T; k-step ss covers keys 16*ss .. +15
+        const char* xi = xslot(n - 1) + l * 16;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 e4 = *reinterpret_cast<const f32x4*>(xi + q4 * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            dp_prev[r] = ACT == 0 ? e4[e] * (dp_prev[r] - stat) : dp_prev[r] * e4[e];
+          }
+        }
+        const char* kt = slot(n - 1);
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+          const frag_t<T> sf = pack_frag<T>(dp_prev, ss);
+#pragma unroll
+          for (int d2 = 0; d2 < C::ND; ++d2) mma(dq[d2], lds_col_frag<T, D, true>(kt, 16 * ss, 32 * d2), sf);
+        }
+      }
+      if (cur) products(dp_prev, slot(n) + C::KT);   // V rows of stage n
     }
-    const bool nxt = has_next && visible(n + 1);
-    if (visible(n)) {
-      with_flags(needs_mask(n), nxt, [&](auto MASK, auto NEXT) { sub_step(MASK, NEXT, s, dp, s_nxt, dp_nxt, n); });
-    } else if (nxt) {
-      products(s_nxt, dp_nxt, n + 1);
-    }
-  };
-
-  dma_wait();
-  __syncthreads();
-  if (2 < nst) issue_stage(2);
-  f32x16 sa, da, sb, db_;
-  if (nsub > 0 && visible(0)) products(sa, da, 0);
-  for (int n = 0; n < nsub; n += 2) {
-    iter(n, sa, da, sb, db_);
-    if (n + 1 < nsub) iter(n + 1, sb, db_, sa, da);
+    prev_visible = cur;
+    // stage n+1 must have landed before the barrier; later ones may be in flight
+    if (n + 1 < nst) wait_stage<NPS>(min(C::NS - 3, nst - 2 - n));
+    __syncthreads();
+    // every wave is done with stage n-1: refill its slot
+    if (n + C::NS - 1 < nst) issue_stage(n + C::NS - 1);
   }
 
-  if (!wave_live || my_row >= lq) return;
+  if (role_a || !wave_live || my_row >= lq) return;
   T* dqp = static_cast<T*>(a.dq) + (size_t)(qs + my_row) * rs + (size_t)h * D;
   store_row<T, C::ND>(dqp, dq, a.scale);
 }

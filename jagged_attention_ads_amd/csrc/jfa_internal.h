@@ -12,11 +12,13 @@ namespace jfa {
 constexpr int kFwdBM = 128;     // query rows per forward / dQ work item
 constexpr int kFwdBN = 64;      // key rows per forward / dQ inner step
 constexpr int kBwdBN = 64;      // key rows per dK/dV work item
-constexpr int kBwdBM = 64;      // query rows per dK/dV inner step
+constexpr int kBwdBM = 64;      // query rows per dK/dV cost block
+constexpr int kDqBM = 64;       // query rows per dQ work item
+constexpr int kDqBN = 64;       // key rows per dQ cost block
 constexpr int kMaxBuckets = 1024;   // distinct tile costs the scheduler can sort
 constexpr int kMaxHeads = 256;      // head index is packed into 8 bits
 
-enum Pass { kPassQ = 0, kPassKV = 1 };
+enum Pass { kPassQ = 0, kPassKV = 1, kPassDQ = 2 };
 
 // Device layout of a work list (all offsets in bytes from its base):
 //   0              int32 item count
@@ -31,9 +33,9 @@ WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t t
 hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                         int32_t causal, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
                         hipStream_t stream);
-// Both passes' lists in one launch (two workgroups).
+// The backward's two lists in one launch (two workgroups): dQ tiles and key tiles.
 hipError_t launch_sched_pair(const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads, int32_t causal,
-                             int32_t nb_q, void* wl_q, const WorklistLayout& lay_q, int32_t nb_kv, void* wl_kv,
+                             int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv, void* wl_kv,
                              const WorklistLayout& lay_kv, hipStream_t stream);
 
 struct FwdArgs {
@@ -64,7 +66,7 @@ struct BwdArgs {
   const float* lse;
   const int32_t* qo;
   const int32_t* ko;
-  const int2* items_q;     // query-tile list (dQ pass)
+  const int2* items_q;     // dQ-tile list (dQ pass)
   const int32_t* n_items_q;
   const int2* items_kv;    // key-tile list (dK/dV pass)
   const int32_t* n_items_kv;

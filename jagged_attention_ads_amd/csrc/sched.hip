@@ -60,19 +60,22 @@ constexpr size_t kSchedMaxLds = 64 * 1024;
 
 template <int PASS>
 struct TileRule {
-  // Tiles split the query side (PASS == kPassQ) or the key side.
-  static constexpr int kTile = PASS == kPassQ ? kFwdBM : kBwdBN;
-  __device__ static int rows(int lq, int lk) { return PASS == kPassQ ? lq : lk; }
+  // Tiles split the query side (forward: kPassQ, dQ: kPassDQ) or the key
+  // side (dK/dV: kPassKV).
+  static constexpr bool kQuery = PASS != kPassKV;
+  static constexpr int kTile = PASS == kPassQ ? kFwdBM : PASS == kPassDQ ? kDqBM : kBwdBN;
+  __device__ static int rows(int lq, int lk) { return kQuery ? lq : lk; }
   __device__ static int cost(int lq, int lk, int t, int causal) {
     if (PASS == kPassQ) return q_tile_kv_blocks(lq, lk, t, kFwdBM, kFwdBN, causal);
+    if (PASS == kPassDQ) return q_tile_kv_blocks(lq, lk, t, kDqBM, kDqBN, causal);
     return kv_tile_q_blocks(lq, lk, t, kBwdBM, kBwdBN, causal);
   }
   // Costs are monotone in t within a sequence: non-decreasing for query
   // tiles (later rows see more keys), non-increasing for key tiles (later
   // keys are seen by fewer rows).  before_or_eq(x, c): a tile of cost x may
   // come before (or is in) the run of cost c; after_or_eq: after or in it.
-  __device__ static bool before_or_eq(int x, int c) { return PASS == kPassQ ? x <= c : x >= c; }
-  __device__ static bool after_or_eq(int x, int c) { return PASS == kPassQ ? x >= c : x <= c; }
+  __device__ static bool before_or_eq(int x, int c) { return kQuery ? x <= c : x >= c; }
+  __device__ static bool after_or_eq(int x, int c) { return kQuery ? x >= c : x <= c; }
 };
 
 // One pass's work list: where it goes and how it is built.
@@ -251,18 +254,18 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
   sched_body<PASS>(qo, ko, B, H, causal, job, smem);
 }
 
-// Both passes' lists in one launch: workgroup 0 builds the query-tile list,
-// workgroup 1 the key-tile list.
+// The backward's two lists in one launch: workgroup 0 builds the dQ-tile
+// list, workgroup 1 the key-tile list.
 __global__ __launch_bounds__(kSchedThreads) void sched_pair_kernel(const int* __restrict__ qo,
                                                                    const int* __restrict__ ko, int B, int H,
-                                                                   int causal, SchedJob jq, SchedJob jkv) {
+                                                                   int causal, SchedJob jdq, SchedJob jkv) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  if (blockIdx.x == 0) sched_body<kPassQ>(qo, ko, B, H, causal, jq, smem);
+  if (blockIdx.x == 0) sched_body<kPassDQ>(qo, ko, B, H, causal, jdq, smem);
   else sched_body<kPassKV>(qo, ko, B, H, causal, jkv, smem);
 }
 
 WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t total_rows) {
-  const int64_t tile = pass == kPassQ ? kFwdBM : kBwdBN;
+  const int64_t tile = pass == kPassQ ? kFwdBM : pass == kPassDQ ? kDqBM : kBwdBN;
   // sum over sequences of ceil(L_b / tile) <= (total + batch * (tile - 1)) / tile
   const int64_t tiles = (static_cast<int64_t>(total_rows) + static_cast<int64_t>(batch) * (tile - 1)) / tile;
   WorklistLayout lay;
@@ -297,6 +300,9 @@ hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t 
   if (pass == kPassQ)
     hipLaunchKernelGGL(sched_kernel<kPassQ>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
                        causal, j);
+  else if (pass == kPassDQ)
+    hipLaunchKernelGGL(sched_kernel<kPassDQ>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
+                       causal, j);
   else
     hipLaunchKernelGGL(sched_kernel<kPassKV>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
                        causal, j);
@@ -304,10 +310,10 @@ hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t 
 }
 
 hipError_t launch_sched_pair(const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads, int32_t causal,
-                             int32_t nb_q, void* wl_q, const WorklistLayout& lay_q, int32_t nb_kv, void* wl_kv,
+                             int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv, void* wl_kv,
                              const WorklistLayout& lay_kv, hipStream_t stream) {
   size_t lds_q, lds_kv;
-  const SchedJob jq = make_job(batch, nb_q, wl_q, lay_q, lds_q);
+  const SchedJob jq = make_job(batch, nb_dq, wl_dq, lay_dq, lds_q);
   const SchedJob jkv = make_job(batch, nb_kv, wl_kv, lay_kv, lds_kv);
   hipLaunchKernelGGL(sched_pair_kernel, dim3(2), dim3(kSchedThreads), lds_q > lds_kv ? lds_q : lds_kv, stream, qo,
                      ko, batch, heads, causal, jq, jkv);

@@ -26,6 +26,7 @@ ACTIVATIONS = {"softmax": 0, "silu": 1}
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 PASS_QUERY_TILES = 0
 PASS_KEY_TILES = 1
+PASS_DQ_TILES = 2
 
 EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_profiled", "jfa_backward_profiled",
             "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_status_string", "jfa_last_error")
@@ -208,7 +209,7 @@ def build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, max_q
     words = host.view(torch.int32)
     count = int(words[0])
     tile = jfa_tile_shape(pass_)[0]
-    rows = total_q if pass_ == PASS_QUERY_TILES else total_kv
+    rows = total_kv if pass_ == PASS_KEY_TILES else total_q
     cap = ((rows + B * (tile - 1)) // tile) * heads
     items = words[4:4 + 2 * cap].view(cap, 2)[:count].clone()
     tile_start = words[4 + 2 * cap:4 + 2 * cap + B + 1].clone()

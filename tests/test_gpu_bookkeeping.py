@@ -40,11 +40,11 @@ WL_CASES = [
 
 
 @pytest.mark.parametrize("name,batch,causal", WL_CASES)
-@pytest.mark.parametrize("pass_", [jfa.PASS_QUERY_TILES, jfa.PASS_KEY_TILES])
+@pytest.mark.parametrize("pass_", [jfa.PASS_QUERY_TILES, jfa.PASS_KEY_TILES, jfa.PASS_DQ_TILES])
 def test_worklist_bit_exact(name, batch, causal, pass_):
     qo, ko, H, causal = _worklist_case(name, batch, causal)
     tile, block = jfa.jfa_tile_shape(pass_)
-    if pass_ == jfa.PASS_QUERY_TILES:
+    if pass_ != jfa.PASS_KEY_TILES:
         costs = oracle.fwd_tile_costs(qo, ko, tile, block, causal)
     else:
         costs = oracle.kv_tile_costs(qo, ko, block, tile, causal)
@@ -56,7 +56,7 @@ def test_worklist_bit_exact(name, batch, causal, pass_):
     items, tile_start = jfa.build_worklist(pass_, qo_d, ko_d, H, int(qo[-1]), int(ko[-1]), int(lq.max()),
                                            int(lk.max()), causal)
     assert np.array_equal(items.numpy(), ref_arr)
-    lens = lq if pass_ == jfa.PASS_QUERY_TILES else lk
+    lens = lk if pass_ == jfa.PASS_KEY_TILES else lq
     assert np.array_equal(tile_start.numpy(), offsets_from_lengths(-(-lens // tile)).astype(np.int32))
     # offsets untouched
     assert np.array_equal(qo_d.cpu().numpy(), qo.astype(np.int32))
