@@ -57,6 +57,20 @@ __device__ __forceinline__ float frag_dot(const f32x8& x, const f32x8& y) {
   return acc;
 }
 
+// The 8 values of a fragment as floats (element e of the fragment -> v[e]).
+__device__ __forceinline__ void frag_unpack(const bf16x8& f, float* v) {
+  const u32x4 u = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(u[e] << 16);
+    v[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void frag_unpack(const f32x8& f, float* v) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = f[e];
+}
+
 // P and dS of one score, softmax (ACT 0) or silu (ACT 1); masked pairs give 0.
 template <int ACT>
 __device__ __forceinline__ void p_ds(float raw, float dp, float lse2, float delta, float scale, float scale_log2,
@@ -105,28 +119,33 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 
 // ---------------------------------------------------------------- dK / dV
 
-// Four waves per 64-key item: two pairs, each pair owning 32 keys.  Wave A of a
-// pair forms S = Q K^T and P (masks applied) and accumulates dV^T += dO^T P;
+// Four waves per 64-key item: two pairs, each pair owning 32 keys.  Wave A of
+// a pair forms S = Q K^T and P (masks applied) and accumulates dV^T += dO^T P;
 // wave B forms dP = dO V^T, takes P from wave A through LDS, forms dS and
 // accumulates dK^T += Q^T dS.  The matrix work splits evenly, nothing is
 // computed twice, and a wave's registers (one of K or V, one accumulator
 // set) and the item's LDS fit two workgroups per CU: one's vector work, LDS
-// waits and prologue overlap the other's products.  Per 32-row sub-block n, one barrier: A
-// hands over P(n) (or, for SiLU, the derivative factor) before it, B reads
-// it after.
+// waits and prologue overlap the other's products.
+//
+// Per 32-row sub-block n there is one barrier.  Before it, A turns S(n) into
+// P(n) and hands P over (the packed P fragments its own dV product uses, or
+// for SiLU the derivative factor packed the same way) while B forms dP(n);
+// after it, A accumulates dV(n) and already forms S(n+1), and B forms dS(n)
+// and accumulates dK(n).
 template <typename T, int D>
 struct DkdvCfg {
   static constexpr int BN = kBwdBN;
   static constexpr int NPAIRS = BN / 32;                 // 32-key slices per item
   static constexpr int NT = NPAIRS * 2 * kWave;          // an A and a B wave per slice
-  static constexpr int ES = sizeof(T);
   static constexpr int SR = 32;                          // query rows per stage = one sub-block
   static constexpr int QT = Swz<T, D>::tile_bytes(SR);   // Q or dO tile
-  static constexpr int STATS = NT / 64 * 256;            // per wave: its 64 rows of lse2 or delta
+  static constexpr int STATS = NT / kWave * 256;         // per wave: its 64 rows of lse2 or delta
   static constexpr int STAGE = 2 * QT + STATS;
-  static constexpr int XCH = NPAIRS * 2 * 4096;          // per pair: two 32 x 32 fp32 hand-over slots
-  static constexpr int SINK = NT / 64 * 1024;            // surplus tile loads, 1 KB per wave
-  static constexpr int NS = 3;                           // stages in the ring
+  static constexpr int XSLOT = kWave * 2 * (int)sizeof(frag_t<T>);   // one hand-over: 2 fragments per lane
+  static constexpr int XCH = NPAIRS * 2 * XSLOT;         // per pair, two slots
+  using Dma = TileDma<T, D, SR, true, NT>;               // query rows stored swap23-permuted
+  static constexpr int SINK = Dma::N * NT > Dma::CHUNKS ? NT / kWave * 1024 : 0;
+  static constexpr int NS = (4 * STAGE + XCH + SINK <= 80 * 1024) ? 4 : 3;   // stages in the ring
   static constexpr int LDS = NS * STAGE + XCH + SINK;
   static constexpr int ND = D / 32, NK = D / 16;
 };
@@ -134,7 +153,7 @@ struct DkdvCfg {
 template <typename T, int D, int ACT>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<T, D>;
-  using Dma = TileDma<T, D, C::SR, true, C::NT>;   // query rows stored swap23-permuted
+  using Dma = typename C::Dma;
   constexpr int NPS = 2 * Dma::N + (ACT == 0 ? 1 : 0);   // copies per thread per stage
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   char* const xch = smem + C::NS * C::STAGE;
@@ -202,27 +221,29 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < C::NK; ++kk) mma(x, lds_row_frag<T, D>(tile, c32, 16 * kk + 8 * g), xf[kk]);
   };
-  // hand-over slot of sub-block n: [r/4][lane][4] floats
-  auto xslot = [&](int n) { return xch + (pair * 2 + (n & 1)) * 4096; };
+  // hand-over slot of sub-block n: [fragment ss][lane]
+  auto xslot = [&](int n) { return xch + (pair * 2 + (n & 1)) * C::XSLOT; };
+  auto row_stats = [&](const char* st, float* v) {   // this wave's 16 rows of lse2 or delta
+    const char* sp = st + 2 * C::QT + w * 256 + 8 * g * (int)sizeof(float);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(sp + (16 * (q4 >> 1) + 4 * (q4 & 1)) * (int)sizeof(float));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q4 + e] = x4[e];
+    }
+  };
 
-  // Wave A, phase 1: P (kept in x for dV) and the value B needs (written to
-  // the hand-over slot): P itself (softmax) or silu'(x)/Lk (SiLU).
+  // Wave A, before the barrier of sub-block n: P(n) from S(n) in x (in place)
+  // and its packed fragments pf; writes what B needs to the hand-over slot.
+  frag_t<T> pf[2];
   auto a_weights = [&](auto MASK, f32x16& x, int n, const char* st) {
     constexpr bool kMask = decltype(MASK)::value;
     const int qa = q_first + 32 * n;
     const int lo = (a.causal ? my_key - off : 0) - qa - 8 * g;
     const int span = max((my_key < lk) ? (lq - qa - 8 * g) - lo : 0, 0);
     float l2[16];
-    if constexpr (ACT == 0) {
-      const char* sp = st + 2 * C::QT + w * 256 + 8 * g * (int)sizeof(float);
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(sp + (16 * (q4 >> 1) + 4 * (q4 & 1)) * (int)sizeof(float));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) l2[4 * q4 + e] = v[e];
-      }
-    }
-    f32x16 e_out;
+    if constexpr (ACT == 0) row_stats(st, l2);
+    f32x16 gfac;   // SiLU: silu'(x)/Lk
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int c = 16 * (r >> 3) + (r & 7);
@@ -231,20 +252,20 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
       if constexpr (ACT == 0) {
         const float p = fast_exp2(fmaf(x[r], a.scale_log2, -l2[r]));
         x[r] = masked ? 0.f : p;
-        e_out[r] = x[r];
       } else {
         const float xs = x[r] * a.scale;
         const float sig = fast_rcp(1.0f + fast_exp2(-x[r] * a.scale_log2));
         const float keep = masked ? 0.f : inv_lk;
         x[r] = xs * sig * keep;
-        e_out[r] = sig * (1.0f + xs * (1.0f - sig)) * keep;
+        gfac[r] = sig * (1.0f + xs * (1.0f - sig)) * keep;
       }
     }
-    char* xo = xslot(n) + l * 16;
+    char* xo = xslot(n) + l * (int)sizeof(frag_t<T>);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 v = {e_out[4 * q4], e_out[4 * q4 + 1], e_out[4 * q4 + 2], e_out[4 * q4 + 3]};
-      *reinterpret_cast<f32x4*>(xo + q4 * 1024) = v;
+    for (int ss = 0; ss < 2; ++ss) {
+      pf[ss] = pack_frag<T>(x, ss);
+      *reinterpret_cast<frag_t<T>*>(xo + ss * kWave * (int)sizeof(frag_t<T>)) =
+          ACT == 0 ? pf[ss] : pack_frag<T>(gfac, ss);
     }
   };
 
@@ -258,17 +279,19 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     return (qa + 32 > lq) || (kw0 + 32 > lk) || (a.causal && kw0 + 31 > qa + off);
   };
 
+  f32x16 x;   // A: S(n), then P(n);  B: dP(n), then dS(n)
+  if (role_a && nst > 0 && visible(0)) products(x, slot(0));
   for (int n = 0; n < nst; ++n) {
     const char* st = slot(n);
     const char* qt = st;
     const char* dt = st + C::QT;
     const bool vis = visible(n);
-    f32x16 x;
     if (vis) {
-      products(x, role_a ? qt : dt);
       if (role_a) {
         if (needs_mask(n)) a_weights(std::true_type{}, x, n, st);
         else a_weights(std::false_type{}, x, n, st);
+      } else {
+        products(x, dt);
       }
     }
     // stage n+1 must have landed before the barrier; later ones may be in flight
@@ -276,43 +299,37 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     __syncthreads();
     // every wave is done with stage n-1: refill its slot
     if (n + C::NS - 1 < nst) issue_stage(n + C::NS - 1);
-    if (vis) {
-      if (role_a) {
-        // dV^T += dO^T P; k-step ss covers rows 16*ss .. +15 of the sub-block
+    if (role_a) {
+      // dV^T += dO^T P(n); k-step ss covers rows 16*ss .. +15 of the sub-block
+      if (vis) {
 #pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          const frag_t<T> pf = pack_frag<T>(x, ss);
+        for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-          for (int d2 = 0; d2 < C::ND; ++d2) mma(acc[d2], lds_col_frag<T, D, true>(dt, 16 * ss, 32 * d2), pf);
+          for (int d2 = 0; d2 < C::ND; ++d2) mma(acc[d2], lds_col_frag<T, D, true>(dt, 16 * ss, 32 * d2), pf[ss]);
+      }
+      // S(n+1), whose stage has landed (waited for before the barrier)
+      if (n + 1 < nst && visible(n + 1)) products(x, slot(n + 1));
+    } else if (vis) {
+      float dl[16];
+      if constexpr (ACT == 0) row_stats(st, dl);
+      const char* xi = xslot(n) + l * (int)sizeof(frag_t<T>);
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        const frag_t<T> ef = *reinterpret_cast<const frag_t<T>*>(xi + ss * kWave * (int)sizeof(frag_t<T>));
+        float e8[8];
+        frag_unpack(ef, e8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * ss + e;
+          x[r] = ACT == 0 ? e8[e] * (x[r] - dl[r]) : x[r] * e8[e];   // dS
         }
-      } else {
-        const char* xi = xslot(n) + l * 16;
-        float dl[16];
-        if constexpr (ACT == 0) {
-          const char* sp = st + 2 * C::QT + w * 256 + 8 * g * (int)sizeof(float);
+      }
+      // dK^T += Q^T dS
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(sp + (16 * (q4 >> 1) + 4 * (q4 & 1)) * (int)sizeof(float));
+      for (int ss = 0; ss < 2; ++ss) {
+        const frag_t<T> sf = pack_frag<T>(x, ss);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dl[4 * q4 + e] = v[e];
-          }
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 e4 = *reinterpret_cast<const f32x4*>(xi + q4 * 1024);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * q4 + e;
-            x[r] = ACT == 0 ? e4[e] * (x[r] - dl[r]) : x[r] * e4[e];   // dS
-          }
-        }
-        // dK^T += Q^T dS
-#pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          const frag_t<T> sf = pack_frag<T>(x, ss);
-#pragma unroll
-          for (int d2 = 0; d2 < C::ND; ++d2) mma(acc[d2], lds_col_frag<T, D, true>(qt, 16 * ss, 32 * d2), sf);
-        }
+        for (int d2 = 0; d2 < C::ND; ++d2) mma(acc[d2], lds_col_frag<T, D, true>(qt, 16 * ss, 32 * d2), sf);
       }
     }
   }
