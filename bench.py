@@ -166,6 +166,23 @@ def cpu_baseline(batch, budget_s):
     }
 
 
+COPY_BYTES = 256 << 20
+
+
+def calibrate_copy():
+    """One elementwise kernel per dispatch that reads and writes COPY_BYTES:
+    what a perfect kernel's FETCH_SIZE / WRITE_SIZE read for that traffic."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "dispatches": 3}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,7 +192,13 @@ def main():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain elementwise copy of known size (256 MiB read + 256 MiB written per "
+                         "dispatch, 3 dispatches), to scale the HBM byte counters")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sequences are independent; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
