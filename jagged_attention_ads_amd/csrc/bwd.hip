@@ -153,6 +153,7 @@ struct DkdvCfg {
 template <typename T, int D, int ACT>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<T, D>;
+  static_assert(C::NT / kWave * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
   using Dma = typename C::Dma;
   constexpr int NPS = 2 * Dma::N + (ACT == 0 ? 1 : 0);   // copies per thread per stage
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -334,9 +335,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     }
   }
 
-  if (!wave_live || my_key >= lk) return;
-  T* op = static_cast<T*>(role_a ? a.dv : a.dk) + (size_t)(ks + my_key) * rs + (size_t)h * D;
-  store_row<T, C::ND>(op, acc, role_a ? 1.0f : a.scale);
+  // the ring is free once every wave is past the loop: stage the rows there
+  __syncthreads();
+  if (!wave_live) return;
+  T* op = static_cast<T*>(role_a ? a.dv : a.dk) + (size_t)(ks + kw0) * rs + (size_t)h * D;
+  store_rows_lds<T, D>(op, rs, min(32, lk - kw0), acc, role_a ? 1.0f : a.scale,
+                       smem + w * store_scratch_bytes<T, D>());
 }
 
 // ---------------------------------------------------------------- dQ
@@ -368,6 +372,7 @@ struct DqCfg {
 template <typename T, int D, int ACT>
 __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   using C = DqCfg<T, D>;
+  static_assert(C::NT / kWave * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
   using Dma = typename C::Dma;
   constexpr int NPS = 2 * Dma::N;   // copies per thread per stage
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -527,9 +532,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     if (n + C::NS - 1 < nst) issue_stage(n + C::NS - 1);
   }
 
-  if (role_a || !wave_live || my_row >= lq) return;
-  T* dqp = static_cast<T*>(a.dq) + (size_t)(qs + my_row) * rs + (size_t)h * D;
-  store_row<T, C::ND>(dqp, dq, a.scale);
+  // the loop's last barrier follows every wave's last LDS read: stage the rows there
+  if (role_a || !wave_live) return;
+  T* dqp = static_cast<T*>(a.dq) + (size_t)(qs + row0) * rs + (size_t)h * D;
+  store_rows_lds<T, D>(dqp, rs, min(32, lq - row0), dq, a.scale, smem + w * store_scratch_bytes<T, D>());
 }
 
 #define JFA_BWD_INST(T, D, ACT)                                      \

@@ -36,6 +36,7 @@ struct FwdCfg {
 template <typename T, int D, int ACT>
 __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<T, D>;
+  static_assert(4 * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   char* const kslot0 = smem;
   char* const vslot0 = smem + 2 * C::KT;
@@ -251,13 +252,13 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   if (!wave_live) return;
   const float l_tot = ACT == 0 ? xor32_sum(l_run) : 1.f;
   const float l_out = ACT == 0 ? xor32_sum(l_used) : 1.f;
-  if (my_row >= lq) return;
-  const bool row_live = lk > 0 && (!a.causal || my_row + off >= 0);
+  const bool row_live = my_row < lq && lk > 0 && (!a.causal || my_row + off >= 0);
   float f = 0.f;
   if (row_live) f = ACT == 0 ? 1.0f / l_out : 1.0f;
-  T* op = static_cast<T*>(a.out) + (size_t)(qs + my_row) * rs + (size_t)h * D;
-  store_row<T, C::ND>(op, o, f);
-  if (ACT == 0 && g == 0) {
+  // every step ends with a barrier after its last LDS read: stage the rows there
+  T* op = static_cast<T*>(a.out) + (size_t)(qs + row0) * rs + (size_t)h * D;
+  store_rows_lds<T, D>(op, rs, min(32, lq - row0), o, f, smem + w * store_scratch_bytes<T, D>());
+  if (ACT == 0 && g == 0 && my_row < lq) {
     a.lse[(size_t)h * a.total_q + qs + my_row] = row_live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }

@@ -455,6 +455,54 @@ __device__ __forceinline__ void store_row(T* row, const f32x16* acc, float f) {
   }
 }
 
+// Bytes of the per-wave LDS staging that store_rows_lds needs.
+template <typename T, int D>
+constexpr int store_scratch_bytes() {
+  return 32 * (D * (int)sizeof(T) + 16);
+}
+
+// The same rows as store_row -- 32 rows starting at `base`, row i at
+// base + i*row_stride elements, of which the first `nvalid` exist; lane
+// l%32 owns row l%32 and register r of block dt holds element
+// 32*dt + 8*(r/4) + 4*g + r%4, times the lane's `f` -- written with stores
+// that cover whole rows: the wave assembles the rows in its own `scratch`
+// (store_scratch_bytes of LDS, written by no other wave), then each 16-byte
+// store lands next to its neighbours' in HBM.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows_lds(T* base, int row_stride, int nvalid, const f32x16* acc, float f,
+                                               char* scratch) {
+  constexpr int ND = D / 32;
+  constexpr int RB = D * (int)sizeof(T);   // bytes of one row
+  constexpr int RS = RB + 16;              // padded LDS row stride
+  const int l = lane_id(), g = l >> 5, c32 = l & 31;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      char* p = scratch + c32 * RS + (32 * dt + 8 * q4 + 4 * g) * (int)sizeof(T);
+      const float x0 = acc[dt][4 * q4] * f, x1 = acc[dt][4 * q4 + 1] * f;
+      const float x2 = acc[dt][4 * q4 + 2] * f, x3 = acc[dt][4 * q4 + 3] * f;
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 v;
+        v[0] = (__bf16)x0;
+        v[1] = (__bf16)x1;
+        v[2] = (__bf16)x2;
+        v[3] = (__bf16)x3;
+        *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
+      } else {
+        *reinterpret_cast<f32x4*>(p) = f32x4{x0, x1, x2, x3};
+      }
+    }
+  }
+  constexpr int CPR = RB / 16;             // 16-byte chunks per row
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / kWave; ++i) {
+    const int k = i * kWave + l, row = k / CPR, ch = k % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(scratch + row * RS + ch * 16);
+    if (row < nvalid) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base + (size_t)row * row_stride) + ch * 16) = v;
+  }
+}
+
 // ---------------------------------------------------------------- work items
 
 // Item packing: x = sequence index, y = (tile << 8) | head.
