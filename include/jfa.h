@@ -145,7 +145,9 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
  * writes into `out` (device, >= jfa_worklist_bytes): int32 item count at byte
  * 0, then from byte 16 int32 pairs (sequence, tile << 8 | head), one per
  * item, ordered by cost descending then (sequence, head, tile) ascending,
- * then int32 tile_start[batch + 1].  JFA_PASS_QUERY_TILES is the list of the
+ * then int32 tile_start[batch + 1], then (32-byte aligned) the per-item
+ * records the attention kernels read, whose layout is internal.
+ * JFA_PASS_QUERY_TILES is the list of the
  * forward kernel, JFA_PASS_DQ_TILES that of the dQ kernel (smaller query
  * tiles) and JFA_PASS_KEY_TILES that of the dK/dV kernel. */
 size_t jfa_worklist_bytes(int32_t pass, int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv);

@@ -200,8 +200,7 @@ int jfa_forward_profiled(const void* q, const void* k, const void* v, const int3
   a.v = v;
   a.qo = q_offsets;
   a.ko = kv_offsets;
-  a.items = reinterpret_cast<const int2*>(ws + L.off_wq + L.wq.items_off);
-  a.n_items = reinterpret_cast<const int32_t*>(ws + L.off_wq);
+  a.meta = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + L.wq.meta_off);
   a.out = out;
   a.lse = lse;
   a.heads = heads;
@@ -261,10 +260,8 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   a.lse = lse;
   a.qo = q_offsets;
   a.ko = kv_offsets;
-  a.items_q = reinterpret_cast<const int2*>(ws + L.off_wq + L.wq.items_off);
-  a.n_items_q = reinterpret_cast<const int32_t*>(ws + L.off_wq);
-  a.items_kv = reinterpret_cast<const int2*>(ws + L.off_wkv + L.wkv.items_off);
-  a.n_items_kv = reinterpret_cast<const int32_t*>(ws + L.off_wkv);
+  a.meta_q = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + L.wq.meta_off);
+  a.meta_kv = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wkv + L.wkv.meta_off);
   a.lse2 = reinterpret_cast<float*>(ws + L.off_stats);
   a.delta = a.lse2 + static_cast<size_t>(heads) * static_cast<size_t>(total_q);
   a.dq = dq;

@@ -160,11 +160,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   char* const xch = smem + C::NS * C::STAGE;
   char* const sink = xch + C::XCH;
 
-  if ((int)blockIdx.x >= *a.n_items_kv) return;
-  int b, h, t;
-  unpack_item(a.items_kv[blockIdx.x], b, h, t);
-  const int qs = a.qo[b], lq = a.qo[b + 1] - qs;
-  const int ks = a.ko[b], lk = a.ko[b + 1] - ks;
+  const ItemMeta m = a.meta_kv[blockIdx.x];   // one load: offsets, lengths, head, tile
+  if (m.lq < 0) return;                       // past the item count
+  const int qs = m.qs, lq = m.lq, ks = m.ks, lk = m.lk, h = m.head, t = m.tile;
   const int off = lk - lq;
 
   const int tid = threadIdx.x, l = lane_id(), w = tid >> 6, g = l >> 5, c32 = l & 31;
@@ -220,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   auto products = [&](f32x16& x, const char* tile) {
     x = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) mma(x, lds_row_frag<T, D>(tile, c32, 16 * kk + 8 * g), xf[kk]);
+    for (int kk = 0; kk < C::NK; ++kk) mma(x, lds_row_frag<T, D>(tile, 0, c32, 16 * kk + 8 * g), xf[kk]);
   };
   // hand-over slot of sub-block n: [fragment ss][lane]
   auto xslot = [&](int n) { return xch + (pair * 2 + (n & 1)) * C::XSLOT; };
@@ -379,11 +377,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   char* const xch = smem + C::NS * C::STAGE;
   char* const sink = xch + C::XCH;
 
-  if ((int)blockIdx.x >= *a.n_items_q) return;
-  int b, h, t;
-  unpack_item(a.items_q[blockIdx.x], b, h, t);
-  const int qs = a.qo[b], lq = a.qo[b + 1] - qs;
-  const int ks = a.ko[b], lk = a.ko[b + 1] - ks;
+  const ItemMeta m = a.meta_q[blockIdx.x];   // one load: offsets, lengths, head, tile
+  if (m.lq < 0) return;                       // past the item count
+  const int qs = m.qs, lq = m.lq, ks = m.ks, lk = m.lk, h = m.head, t = m.tile;
   const int off = lk - lq;
 
   const int tid = threadIdx.x, l = lane_id(), w = tid >> 6, g = l >> 5, c32 = l & 31;
@@ -451,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   auto products = [&](f32x16& x, const char* tile) {
     x = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) mma(x, lds_row_frag<T, D>(tile, c32, 16 * kk + 8 * g), xf[kk]);
+    for (int kk = 0; kk < C::NK; ++kk) mma(x, lds_row_frag<T, D>(tile, 0, c32, 16 * kk + 8 * g), xf[kk]);
   };
   // hand-over slot of sub-block n: [r/4][lane][4] floats
   auto xslot = [&](int n) { return xch + (pair * 2 + (n & 1)) * 4096; };

@@ -41,11 +41,9 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   char* const kslot0 = smem;
   char* const vslot0 = smem + 2 * C::KT;
 
-  if ((int)blockIdx.x >= *a.n_items) return;
-  int b, h, t;
-  unpack_item(a.items[blockIdx.x], b, h, t);
-  const int qs = a.qo[b], lq = a.qo[b + 1] - qs;
-  const int ks = a.ko[b], lk = a.ko[b + 1] - ks;
+  const ItemMeta m = a.meta[blockIdx.x];   // one load: offsets, lengths, head, tile
+  if (m.lq < 0) return;                       // past the item count
+  const int qs = m.qs, lq = m.lq, ks = m.ks, lk = m.lk, h = m.head, t = m.tile;
   const int off = lk - lq;   // causal: query i sees keys j <= i + off
 
   const int tid = threadIdx.x, l = lane_id(), w = tid >> 6, g = l >> 5, c32 = l & 31;
@@ -87,20 +85,24 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   // running max, running sum of the exact weights (for lse) and of the
   // weights as rounded into the P operand (for normalising O)
   float m_run = -INFINITY, l_run = 0.f, l_used = 0.f;
-  const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
+  // silu weights: y = s * scale / L_kv * sigmoid(s * scale) for raw score s
+  const float silu_out = lk > 0 ? a.scale / (float)lk : 0.f;
+  const float silu_neg_l2 = -a.scale_log2;
 
   // a wave takes part in key tile j iff some of its rows see a key of it
   auto wave_active = [&](int j) { return wave_live && (!a.causal || j * C::BN <= row0 + 31 + off); };
 
-  // S^T (64 keys x 32 queries) = K Q^T for key tile j, as two 32-key tiles
-  auto scores = [&](f32x16* s, int j) {
-    const char* kt = kslot0 + (j & 1) * C::KT;
+  // S^T (64 keys x 32 queries) = K Q^T for the key tile in K slot PAR
+  // (the slot of key tile j is j & 1; a compile-time slot keeps the slot
+  // offset in the reads' immediate field), as two 32-key tiles
+  auto scores = [&](auto PAR, f32x16* s) {
+    const char* kt = kslot0 + decltype(PAR)::value * C::KT;
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::NK; ++kk) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) mma(s[mt], lds_row_frag<T, D>(kt, 32 * mt + c32, 16 * kk + 8 * g), qf[kk]);
+      for (int mt = 0; mt < 2; ++mt) mma(s[mt], lds_row_frag<T, D>(kt, 32 * mt, c32, 16 * kk + 8 * g), qf[kk]);
     }
   };
 
@@ -117,9 +119,10 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   // j+1 (into s_nxt, when NEXT) interleaved with them, then
   // O^T += V^T P^T for tile j.  MASK: tile j needs masking.  Both flags are
   // compile-time so that the interleaved region has no branch.
-  auto tile_step = [&](auto MASK, auto NEXT, f32x16* s, f32x16* s_nxt, int j) {
+  auto tile_step = [&](auto MASK, auto NEXT, auto PAR, f32x16* s, f32x16* s_nxt, int j) {
     constexpr bool kMask = decltype(MASK)::value;
     constexpr bool kNext = decltype(NEXT)::value;
+    constexpr int kPar = decltype(PAR)::value;   // == j & 1
     const int lim = row_limit - j * C::BN - 8 * g;   // masked iff key offset >= lim
     if constexpr (ACT == 0) {
       if constexpr (kMask) {
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
       }
     }
     // --- straight-line region: next scores (MFMA) + weights (VALU) ---
-    if constexpr (kNext) scores(s_nxt, j + 1);
+    if constexpr (kNext) scores(std::integral_constant<int, 1 - kPar>{}, s_nxt);
     if constexpr (ACT == 0) {
       const float neg_m = -m_run;
 #pragma unroll
@@ -173,8 +176,8 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float raw = s[mt][r];
-          const float sig = fast_rcp(1.0f + fast_exp2(-raw * a.scale_log2));
-          float y = raw * a.scale * sig * inv_lk;
+          const float sig = fast_rcp(1.0f + fast_exp2(raw * silu_neg_l2));
+          float y = raw * silu_out * sig;
           if constexpr (kMask) {
             const int ko = 32 * mt + 16 * (r >> 3) + (r & 7);
             y = (ko >= lim) ? 0.f : y;
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
         for (int ss = 0; ss < 2; ++ss) frag_sum_into(l_used, pf[mt][ss]);
       }
     }
-    const char* vt = vslot0 + (j & 1) * C::KT;
+    const char* vt = vslot0 + kPar * C::KT;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -218,21 +221,22 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   // j are formed (VALU), accumulate P V for tile j, then wait and barrier.
   // Slot reuse: K(j+2) overwrites K(j), whose scores were formed in the
   // previous step; V(j+1) overwrites V(j-1), consumed in the previous step.
-  auto step = [&](int j, f32x16* s_cur, f32x16* s_nxt) {
-    if (j + 2 < n_kv) kdma.issue(kslot0 + (j & 1) * C::KT, kb, rs, (j + 2) * C::BN, lk, tid);
-    if (j + 1 < n_kv) vdma.issue(vslot0 + ((j + 1) & 1) * C::KT, vb, rs, (j + 1) * C::BN, lk, tid);
+  auto step = [&](auto PAR, int j, f32x16* s_cur, f32x16* s_nxt) {
+    constexpr int kPar = decltype(PAR)::value;   // == j & 1
+    if (j + 2 < n_kv) kdma.issue(kslot0 + kPar * C::KT, kb, rs, (j + 2) * C::BN, lk, tid);
+    if (j + 1 < n_kv) vdma.issue(vslot0 + (1 - kPar) * C::KT, vb, rs, (j + 1) * C::BN, lk, tid);
     const bool nxt = j + 1 < n_kv && wave_active(j + 1);
     if (wave_active(j)) {
       const bool msk = needs_mask(j);
       if (nxt) {
-        if (msk) tile_step(std::true_type{}, std::true_type{}, s_cur, s_nxt, j);
-        else tile_step(std::false_type{}, std::true_type{}, s_cur, s_nxt, j);
+        if (msk) tile_step(std::true_type{}, std::true_type{}, PAR, s_cur, s_nxt, j);
+        else tile_step(std::false_type{}, std::true_type{}, PAR, s_cur, s_nxt, j);
       } else {
-        if (msk) tile_step(std::true_type{}, std::false_type{}, s_cur, s_nxt, j);
-        else tile_step(std::false_type{}, std::false_type{}, s_cur, s_nxt, j);
+        if (msk) tile_step(std::true_type{}, std::false_type{}, PAR, s_cur, s_nxt, j);
+        else tile_step(std::false_type{}, std::false_type{}, PAR, s_cur, s_nxt, j);
       }
     } else if (nxt) {
-      scores(s_nxt, j + 1);
+      scores(std::integral_constant<int, 1 - kPar>{}, s_nxt);
     }
     dma_wait();
     __syncthreads();
@@ -241,12 +245,12 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   dma_wait();
   __syncthreads();
   f32x16 sa[2], sb[2];
-  if (n_kv > 0 && wave_active(0)) scores(sa, 0);
+  if (n_kv > 0 && wave_active(0)) scores(std::integral_constant<int, 0>{}, sa);
   // the first step copies K(2) over K(0): every wave must be done reading it
   __syncthreads();
   for (int j = 0; j < n_kv; j += 2) {
-    step(j, sa, sb);
-    if (j + 1 < n_kv) step(j + 1, sb, sa);
+    step(std::integral_constant<int, 0>{}, j, sa, sb);
+    if (j + 1 < n_kv) step(std::integral_constant<int, 1>{}, j + 1, sb, sa);
   }
 
   if (!wave_live) return;

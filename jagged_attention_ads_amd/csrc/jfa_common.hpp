@@ -167,10 +167,13 @@ struct Swz {
   }
 };
 
-// 8 consecutive elements (col .. col+7, col a multiple of 8) of one row.
+// 8 consecutive elements (col .. col+7, col a multiple of 8) of row
+// row0 + row, row0 a multiple of 16 (an immediate offset: the swizzle of a
+// row depends on its low four bits only).
 template <typename T, int D>
-__device__ __forceinline__ frag_t<T> lds_row_frag(const char* tile, int row, int col) {
+__device__ __forceinline__ frag_t<T> lds_row_frag(const char* tile, int row0, int row, int col) {
   using S = Swz<T, D>;
+  tile += row0 * S::ROW_BYTES;
   if constexpr (sizeof(T) == 2) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + S::off(row, col >> 3)));
   } else {
@@ -187,13 +190,19 @@ __device__ __forceinline__ frag_t<T> lds_row_frag(const char* tile, int row, int
 }
 
 // Transposed fragment: lane l gets the elements at logical rows
-// row0 + 8*(l/32) + 0..7 of column col0 + l%32 (row0 a multiple of 8, col0
+// row0 + 8*(l/32) + 0..7 of column col0 + l%32 (row0 a multiple of 16, col0
 // a multiple of 32).  With SWAPPED, logical row r is stored at row swap23(r)
 // (swap23 keeps aligned groups of four rows together).
+// The swizzle of a row depends on its low four bits only and swap23 moves
+// bits 2 and 3, so rows row0 + x sit at row0 * ROW_BYTES plus the offsets
+// of rows x: the lane-dependent part is the same for every row0, and row0
+// becomes an immediate offset of the read.
 template <typename T, int D, bool SWAPPED>
 __device__ __forceinline__ frag_t<T> lds_col_frag(const char* tile, int row0, int col0) {
   using S = Swz<T, D>;
   const int l = lane_id();
+  tile += row0 * S::ROW_BYTES;
+  row0 = 0;
   if constexpr (sizeof(T) == 2) {
     // ds_read_b64_tr_b16 (layout checked on the hardware): within each
     // 16-lane block, source lane s addresses the 4 elements at row r0 + s/4,
@@ -504,13 +513,6 @@ __device__ __forceinline__ void store_rows_lds(T* base, int row_stride, int nval
 }
 
 // ---------------------------------------------------------------- work items
-
-// Item packing: x = sequence index, y = (tile << 8) | head.
-__device__ __forceinline__ void unpack_item(int2 it, int& b, int& h, int& t) {
-  b = it.x;
-  h = it.y & 255;
-  t = it.y >> 8;
-}
 
 // Number of `bn`-key blocks a `bm`-query tile visits (forward and dQ).
 __device__ __forceinline__ int q_tile_kv_blocks(int lq, int lk, int t, int bm, int bn, int causal) {

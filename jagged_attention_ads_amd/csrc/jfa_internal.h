@@ -20,13 +20,21 @@ constexpr int kMaxHeads = 256;      // head index is packed into 8 bits
 
 enum Pass { kPassQ = 0, kPassKV = 1, kPassDQ = 2 };
 
+// Per-item record the attention kernels read with one load: the sequence's
+// first query and key rows and lengths, and the item's head and tile.
+// Records past the item count have lq = -1.
+struct ItemMeta {
+  int32_t qs, lq, ks, lk, head, tile, unused0, unused1;
+};
+
 // Device layout of a work list (all offsets in bytes from its base):
-//   0              int32 item count
-//   16             int2  items[capacity]   (x = sequence, y = tile << 8 | head)
-//   16 + 8*cap     int32 tile_start[batch + 1]
+//   0                      int32   item count
+//   16                     int2    items[capacity]   (x = sequence, y = tile << 8 | head)
+//   16 + 8*cap             int32   tile_start[batch + 1]
+//   meta_off (32-aligned)  ItemMeta meta[capacity]
 struct WorklistLayout {
   int64_t capacity;
-  size_t items_off, tile_start_off, bytes;
+  size_t items_off, tile_start_off, meta_off, bytes;
 };
 WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t total_rows);
 
@@ -44,8 +52,7 @@ struct FwdArgs {
   const void* v;
   const int32_t* qo;
   const int32_t* ko;
-  const int2* items;
-  const int32_t* n_items;
+  const ItemMeta* meta;     // query-tile records
   void* out;
   float* lse;
   int32_t heads;
@@ -66,10 +73,8 @@ struct BwdArgs {
   const float* lse;
   const int32_t* qo;
   const int32_t* ko;
-  const int2* items_q;     // dQ-tile list (dQ pass)
-  const int32_t* n_items_q;
-  const int2* items_kv;    // key-tile list (dK/dV pass)
-  const int32_t* n_items_kv;
+  const ItemMeta* meta_q;   // dQ-tile records (dQ pass)
+  const ItemMeta* meta_kv;  // key-tile records (dK/dV pass)
   float* lse2;             // [heads, total_q] workspace: lse * log2(e) per row, and
   float* delta;            // [heads, total_q] delta per row; both written by the dQ pass
                            // (softmax), read by the dK/dV pass

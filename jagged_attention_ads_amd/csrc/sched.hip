@@ -55,7 +55,7 @@ __device__ int find_seq(const int* ts, int B, int u) {
 __host__ __device__ constexpr size_t sched_lds_fixed(int nbuckets) {
   return (((size_t)nbuckets * (3 * 4 + 2 + 2 * kSchedWaves) + 32 * 4) + 15) & ~(size_t)15;
 }
-__host__ __device__ constexpr size_t sched_lds_seqs(int batch) { return ((size_t)3 * batch + 1) * 4; }
+__host__ __device__ constexpr size_t sched_lds_seqs(int batch) { return ((size_t)3 * batch + 3) * 4; }
 constexpr size_t kSchedMaxLds = 64 * 1024;
 
 template <int PASS>
@@ -86,6 +86,7 @@ struct SchedJob {
   int* count;
   int2* items;
   int* tile_start;
+  ItemMeta* meta;
 };
 
 template <int PASS>
@@ -97,6 +98,7 @@ __device__ void sched_body(const int* __restrict__ qo, const int* __restrict__ k
   int* const count = job.count;
   int2* const items = job.items;
   int* const tile_start = job.tile_start;
+  ItemMeta* const meta = job.meta;
   int* hist = reinterpret_cast<int*>(smem);
   int* start = hist + nbuckets;
   int* carry = start + nbuckets;
@@ -108,16 +110,11 @@ __device__ void sched_body(const int* __restrict__ qo, const int* __restrict__ k
   // read from global memory.
   int* seq_lds = reinterpret_cast<int*>(smem + sched_lds_fixed(nbuckets));
   int* ts = stage_seqs ? seq_lds : tile_start;
-  int* len_q = stage_seqs ? seq_lds + (B + 1) : nullptr;
-  int* len_k = stage_seqs ? seq_lds + (2 * B + 1) : nullptr;
+  const int* q_off = stage_seqs ? seq_lds + (B + 1) : qo;
+  const int* k_off = stage_seqs ? seq_lds + (2 * B + 2) : ko;
   auto lengths = [&](int b, int& lq, int& lk) {
-    if (stage_seqs) {
-      lq = len_q[b];
-      lk = len_k[b];
-    } else {
-      lq = qo[b + 1] - qo[b];
-      lk = ko[b + 1] - ko[b];
-    }
+    lq = q_off[b + 1] - q_off[b];
+    lk = k_off[b + 1] - k_off[b];
   };
 
   const int tid = threadIdx.x, l = lane_id(), w = tid / kWave;
@@ -128,11 +125,15 @@ __device__ void sched_body(const int* __restrict__ qo, const int* __restrict__ k
     const int b = base + tid;
     int n = 0;
     if (b < B) {
-      const int lq = qo[b + 1] - qo[b], lk = ko[b + 1] - ko[b];
-      n = ceil_div(R::rows(lq, lk), R::kTile);
+      const int q0 = qo[b], q1 = qo[b + 1], k0 = ko[b], k1 = ko[b + 1];
+      n = ceil_div(R::rows(q1 - q0, k1 - k0), R::kTile);
       if (stage_seqs) {
-        len_q[b] = lq;
-        len_k[b] = lk;
+        seq_lds[B + 1 + b] = q0;
+        seq_lds[2 * B + 2 + b] = k0;
+        if (b == B - 1) {
+          seq_lds[2 * B + 1] = q1;
+          seq_lds[3 * B + 2] = k1;
+        }
       }
     }
     int tot;
@@ -235,9 +236,13 @@ __device__ void sched_body(const int* __restrict__ qo, const int* __restrict__ k
       // items of bucket c are ordered (b, h, t): all earlier sequences' tiles
       // of this cost (rank - k of them) times H, then h runs of length len
       const int p0 = start[c] + H * (rank - k) + k;
+      const int qs0 = q_off[b], ks0 = k_off[b];
       for (int hh = 0; hh < H; ++hh) {
         const int64_t p = (int64_t)p0 + (int64_t)hh * len;
-        if (p >= 0 && p < capacity) items[p] = make_int2(b, (t << 8) | hh);   // true for valid offsets
+        if (p >= 0 && p < capacity) {   // true for valid offsets
+          items[p] = make_int2(b, (t << 8) | hh);
+          meta[p] = ItemMeta{qs0, lq, ks0, lk, hh, t, 0, 0};
+        }
       }
     }
     __syncthreads();
@@ -245,6 +250,8 @@ __device__ void sched_body(const int* __restrict__ qo, const int* __restrict__ k
     __syncthreads();
   }
   if (tid == 0) *count = H * total_tiles;
+  // records past the count tell the kernels' surplus workgroups to exit
+  for (int64_t p = (int64_t)H * total_tiles + tid; p < capacity; p += kSchedThreads) meta[p].lq = -1;
 }
 
 template <int PASS>
@@ -272,7 +279,8 @@ WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t t
   lay.capacity = tiles * heads;
   lay.items_off = 16;
   lay.tile_start_off = lay.items_off + static_cast<size_t>(lay.capacity) * 8;
-  lay.bytes = lay.tile_start_off + (static_cast<size_t>(batch) + 1) * 4;
+  lay.meta_off = (lay.tile_start_off + (static_cast<size_t>(batch) + 1) * 4 + 31) & ~static_cast<size_t>(31);
+  lay.bytes = lay.meta_off + static_cast<size_t>(lay.capacity) * sizeof(ItemMeta);
   lay.bytes = (lay.bytes + 255) & ~static_cast<size_t>(255);
   return lay;
 }
@@ -289,6 +297,7 @@ static SchedJob make_job(int32_t batch, int32_t nbuckets, void* wl_base, const W
   j.count = reinterpret_cast<int*>(base);
   j.items = reinterpret_cast<int2*>(base + lay.items_off);
   j.tile_start = reinterpret_cast<int*>(base + lay.tile_start_off);
+  j.meta = reinterpret_cast<ItemMeta*>(base + lay.meta_off);
   return j;
 }
 
