@@ -89,6 +89,10 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   const float silu_out = lk > 0 ? a.scale / (float)lk : 0.f;
   const float silu_neg_l2 = -a.scale_log2;
 
+  // lane address bases of the K row and V column fragment reads (bf16)
+  [[maybe_unused]] const int k_addr = sizeof(T) == 2 ? RowFragAddr<T, D>::base() : 0;
+  [[maybe_unused]] const int v_addr = sizeof(T) == 2 ? ColFragAddr<T, D, false>::base() : 0;
+
   // a wave takes part in key tile j iff some of its rows see a key of it
   auto wave_active = [&](int j) { return wave_live && (!a.causal || j * C::BN <= row0 + 31 + off); };
 
@@ -99,10 +103,19 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
     const char* kt = kslot0 + decltype(PAR)::value * C::KT;
     s[0] = f32x16{};
     s[1] = f32x16{};
+    if constexpr (sizeof(T) == 2) {
+      const int kx = refresh(k_addr);
 #pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) {
+      for (int kk = 0; kk < C::NK; ++kk) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) mma(s[mt], lds_row_frag<T, D>(kt, 32 * mt, c32, 16 * kk + 8 * g), qf[kk]);
+        for (int mt = 0; mt < 2; ++mt) mma(s[mt], lds_row_frag_x<T, D>(kt, 32 * mt, kk, kx), qf[kk]);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < C::NK; ++kk) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) mma(s[mt], lds_row_frag<T, D>(kt, 32 * mt, c32, 16 * kk + 8 * g), qf[kk]);
+      }
     }
   };
 
@@ -203,13 +216,16 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
       }
     }
     const char* vt = vslot0 + kPar * C::KT;
+    [[maybe_unused]] const int vx = refresh(v_addr);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
 #pragma unroll
         for (int dt = 0; dt < C::ND; ++dt) {
-          const frag_t<T> vf = lds_col_frag<T, D, false>(vt, 32 * mt + 16 * ss, 32 * dt);
+          frag_t<T> vf;
+          if constexpr (sizeof(T) == 2) vf = lds_col_frag_x<T, D, false>(vt, 32 * mt + 16 * ss, dt, vx);
+          else vf = lds_col_frag<T, D, false>(vt, 32 * mt + 16 * ss, 32 * dt);
           mma(o[dt], vf, pf[mt][ss]);
         }
       }

@@ -55,7 +55,7 @@ __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 // and 3 are swapped.  With that order, accumulator register 8*s + e of lane
 // group g = l/32 in a 32 x 32 C tile sits at logical row 16*s + 8*g + e, i.e.
 // the 8 consecutive k-slots of a B-operand fragment.
-__device__ __forceinline__ int swap23(int m) {
+__host__ __device__ constexpr int swap23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
@@ -133,7 +133,7 @@ struct Swz {
   static constexpr int CH = D * (int)sizeof(T) / 16;   // chunks per row
   static constexpr int ROW_BYTES = CH * 16;
   // byte offset of chunk c of row r
-  __device__ static __forceinline__ int off(int r, int c) {
+  __host__ __device__ static constexpr int off(int r, int c) {
     if constexpr (CH >= 16) {
       const int g = ((r & 3) << 2) ^ ((r >> 2) & 3);
       return r * ROW_BYTES + ((c & ~15) | ((c & 15) ^ g)) * 16;
@@ -235,6 +235,84 @@ __device__ __forceinline__ frag_t<T> lds_col_frag(const char* tile, int row0, in
     }
     return f;
   }
+}
+
+// One address register per operand.  In every swizzle above, moving a
+// read by whole 16-column steps (row fragments), by whole 32-column blocks
+// or to the second four rows (transposed fragments) flips address bits that
+// the first read of each lane leaves fixed: every read is that first
+// address XOR a compile-time constant.  valid() checks this for every lane.
+// A kernel that refreshes the base inside its loop (see refresh) recomputes
+// the reads' addresses with one XOR each instead of holding one register per
+// read across the loop.
+template <typename T, int D>
+struct RowFragAddr {
+  using S = Swz<T, D>;
+  // lane l's read of columns 16*kk + 8*(l/32) .. +7 of row l%32
+  __host__ __device__ static constexpr int lane_off(int l, int kk) {
+    return S::off(l & 31, (16 * kk + 8 * (l >> 5)) * (int)sizeof(T) / 16);
+  }
+  __host__ __device__ static constexpr int xor_k(int kk) { return lane_off(0, kk) ^ lane_off(0, 0); }
+  static constexpr bool valid() {
+    for (int l = 0; l < kWave; ++l)
+      for (int kk = 0; kk < D / 16; ++kk)
+        if (lane_off(l, kk) != (lane_off(l, 0) ^ xor_k(kk))) return false;
+    return true;
+  }
+  __device__ static __forceinline__ int base() { return lane_off(lane_id(), 0); }
+};
+
+template <typename T, int D, bool SWAPPED>
+struct ColFragAddr {
+  using S = Swz<T, D>;
+  // lane l's rd-th ds_read_b64_tr_b16 of column block cb (layout as in
+  // lds_col_frag), rows 0..15 of the tile
+  __host__ __device__ static constexpr int lane_off(int l, int cb, int rd) {
+    const int blk = l >> 4, s = l & 15, g = blk >> 1, half = blk & 1;
+    const int col = 32 * cb + 16 * half + 4 * (s & 3);
+    const int row = 8 * g + 4 * rd + (s >> 2);
+    return S::off(SWAPPED ? swap23(row) : row, col >> 3) + (col & 7) * 2;
+  }
+  __host__ __device__ static constexpr int xor_k(int cb, int rd) { return lane_off(0, cb, rd) ^ lane_off(0, 0, 0); }
+  static constexpr bool valid() {
+    for (int l = 0; l < kWave; ++l)
+      for (int cb = 0; cb < D / 32; ++cb)
+        for (int rd = 0; rd < 2; ++rd)
+          if (lane_off(l, cb, rd) != (lane_off(l, 0, 0) ^ xor_k(cb, rd))) return false;
+    return true;
+  }
+  __device__ static __forceinline__ int base() { return lane_off(lane_id(), 0, 0); }
+};
+
+// An opaque copy of an address base: the compiler cannot hoist what is
+// computed from it out of the loop it is refreshed in.
+__device__ __forceinline__ int refresh(int base) {
+  asm volatile("" : "+v"(base));
+  return base;
+}
+
+// lds_row_frag of row row0 + l%32, columns 16*kk + 8*(l/32) .. +7, from a
+// RowFragAddr base (bf16 only).
+template <typename T, int D>
+__device__ __forceinline__ frag_t<T> lds_row_frag_x(const char* tile, int row0, int kk, int base) {
+  static_assert(sizeof(T) == 2 && RowFragAddr<T, D>::valid(), "XOR addressing needs bf16 rows");
+  const char* p = tile + row0 * Swz<T, D>::ROW_BYTES + (base ^ RowFragAddr<T, D>::xor_k(kk));
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// lds_col_frag(tile, row0, 32 * cb) from a ColFragAddr base (bf16 only).
+template <typename T, int D, bool SWAPPED>
+__device__ __forceinline__ frag_t<T> lds_col_frag_x(const char* tile, int row0, int cb, int base) {
+  using A = ColFragAddr<T, D, SWAPPED>;
+  static_assert(sizeof(T) == 2 && A::valid(), "XOR addressing needs bf16 rows");
+  tile += row0 * Swz<T, D>::ROW_BYTES;
+  u32x2 w[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd)
+    w[rd] = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((JFA_LDS i16x4*)(tile + (base ^ A::xor_k(cb, rd)))));
+  const u32x4 words = {w[0][0], w[0][1], w[1][0], w[1][1]};
+  return __builtin_bit_cast(bf16x8, words);
 }
 
 // ---------------------------------------------------------------- cross-lane

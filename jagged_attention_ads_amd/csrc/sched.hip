@@ -236,13 +236,9 @@ __device__ void sched_body(const int* __restrict__ qo, const int* __restrict__ k
       // items of bucket c are ordered (b, h, t): all earlier sequences' tiles
       // of this cost (rank - k of them) times H, then h runs of length len
       const int p0 = start[c] + H * (rank - k) + k;
-      const int qs0 = q_off[b], ks0 = k_off[b];
       for (int hh = 0; hh < H; ++hh) {
         const int64_t p = (int64_t)p0 + (int64_t)hh * len;
-        if (p >= 0 && p < capacity) {   // true for valid offsets
-          items[p] = make_int2(b, (t << 8) | hh);
-          meta[p] = ItemMeta{qs0, lq, ks0, lk, hh, t, 0, 0};
-        }
+        if (p >= 0 && p < capacity) items[p] = make_int2(b, (t << 8) | hh);   // true for valid offsets
       }
     }
     __syncthreads();
@@ -250,8 +246,48 @@ __device__ void sched_body(const int* __restrict__ qo, const int* __restrict__ k
     __syncthreads();
   }
   if (tid == 0) *count = H * total_tiles;
-  // records past the count tell the kernels' surplus workgroups to exit
-  for (int64_t p = (int64_t)H * total_tiles + tid; p < capacity; p += kSchedThreads) meta[p].lq = -1;
+
+  // 5. the kernels' records, in list order.  Written from the (now final)
+  // item list rather than where step 4 places each item: step 4 scatters,
+  // and scattered 32-byte records cost far more than contiguous ones.
+  // Records past the count (lq = -1) tell surplus workgroups to exit.  The
+  // barrier at the end of step 4 makes the item stores visible here.
+  // The offsets are read from LDS when staged (a separate copy of the loop,
+  // so that its waits cover LDS reads only).  Buffer accesses bounded to the
+  // list keep the loop free of branches: loads past the item count read
+  // zeros, stores past the capacity are dropped.
+  const int64_t n_items = (int64_t)H * total_tiles;
+  auto records = [&](const int* qof, const int* kof) {
+    constexpr int kUnroll = 4, kPer = kUnroll * kSchedThreads;
+    for (int64_t base = 0; base < capacity; base += kPer) {
+      const int n_in = (int)max((int64_t)0, min(n_items - base, (int64_t)kPer));
+      const int n_cap = (int)min(capacity - base, (int64_t)kPer);
+      const __amdgpu_buffer_rsrc_t irs =
+          __builtin_amdgcn_make_buffer_rsrc(items + base, 0, n_in * (int)sizeof(int2), kBufferWord3);
+      const __amdgpu_buffer_rsrc_t mrs =
+          __builtin_amdgcn_make_buffer_rsrc(meta + base, 0, n_cap * (int)sizeof(ItemMeta), kBufferWord3);
+      int2 it[kUnroll];
+#pragma unroll
+      for (int r = 0; r < kUnroll; ++r) {
+        const int i = r * kSchedThreads + tid;
+        it[r] = __builtin_bit_cast(int2, __builtin_amdgcn_raw_buffer_load_b64(irs, i * (int)sizeof(int2), 0, 0));
+      }
+#pragma unroll
+      for (int r = 0; r < kUnroll; ++r) {
+        const int i = r * kSchedThreads + tid;
+        const int b = it[r].x;   // 0 past the count: a valid sequence to read
+        const int q0 = qof[b], q1 = qof[b + 1], k0 = kof[b], k1 = kof[b + 1];
+        const int lq = i < n_in ? q1 - q0 : -1;
+        const u32x4 lo = {(uint32_t)q0, (uint32_t)lq, (uint32_t)k0, (uint32_t)(k1 - k0)};
+        const u32x4 hi = {(uint32_t)(it[r].y & 255), (uint32_t)(it[r].y >> 8), 0u, 0u};
+        const int off = i * (int)sizeof(ItemMeta);
+        __builtin_amdgcn_raw_buffer_store_b128(lo, mrs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(hi, mrs, off + 16, 0, 0);
+      }
+    }
+  };
+  if (stage_seqs) records(q_off, k_off);
+  else records(qo, ko);
 }
 
 template <int PASS>
