@@ -199,8 +199,13 @@ def backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_l
     return dq, dk, dv
 
 
-def build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, max_q_len, max_kv_len, causal):
-    """Runs the device work-list builder; returns (items int32 [n, 2], tile_start int32 [B+1]) on the host."""
+def build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, max_q_len, max_kv_len, causal,
+                   with_records=False):
+    """Runs the device work-list builder; returns (items int32 [n, 2], tile_start int32 [B+1]) on the host.
+
+    with_records: also return the per-item records the attention kernels read,
+    int32 [capacity, 8] = (q start, q length, kv start, kv length, head, tile, 0, 0),
+    q length -1 past the item count (an internal layout, for tests)."""
     B = q_offsets.numel() - 1
     nbytes = jfa_worklist_bytes(pass_, B, heads, total_q, total_kv)
     buf = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q_offsets.device)
@@ -213,4 +218,8 @@ def build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, max_q
     cap = ((rows + B * (tile - 1)) // tile) * heads
     items = words[4:4 + 2 * cap].view(cap, 2)[:count].clone()
     tile_start = words[4 + 2 * cap:4 + 2 * cap + B + 1].clone()
-    return items, tile_start
+    if not with_records:
+        return items, tile_start
+    meta_off = (16 + 8 * cap + 4 * (B + 1) + 31) // 32 * 32
+    records = words[meta_off // 4:meta_off // 4 + 8 * cap].view(cap, 8).clone()
+    return items, tile_start, records

@@ -10,6 +10,7 @@
 """
 
 import dataclasses
+import functools
 import math
 
 import numpy as np
@@ -39,9 +40,9 @@ WL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,batch,causal", WL_CASES)
-@pytest.mark.parametrize("pass_", [jfa.PASS_QUERY_TILES, jfa.PASS_KEY_TILES, jfa.PASS_DQ_TILES])
-def test_worklist_bit_exact(name, batch, causal, pass_):
+@functools.lru_cache(maxsize=None)
+def _worklist_ref(name, batch, causal, pass_):
+    """The oracle's list for a case, as int32 [n, 2] (computed once for both bodies)."""
     qo, ko, H, causal = _worklist_case(name, batch, causal)
     tile, block = jfa.jfa_tile_shape(pass_)
     if pass_ != jfa.PASS_KEY_TILES:
@@ -49,13 +50,37 @@ def test_worklist_bit_exact(name, batch, causal, pass_):
     else:
         costs = oracle.kv_tile_costs(qo, ko, block, tile, causal)
     ref = oracle.worklist(costs, H)
-    ref_arr = np.array([[b, (t << 8) | h] for b, h, t, _ in ref], dtype=np.int32).reshape(-1, 2)
+    return np.array([[b, (t << 8) | h] for b, h, t, _ in ref], dtype=np.int32).reshape(-1, 2)
+
+
+@pytest.fixture(params=["1", "0"])
+def sched_stage(request, monkeypatch):
+    """Both bodies of the builder (1: all in LDS where it fits, 0: global memory)."""
+    monkeypatch.setenv("JFA_SCHED_STAGE", request.param)
+    return request.param
+
+
+@pytest.mark.parametrize("name,batch,causal", WL_CASES)
+@pytest.mark.parametrize("pass_", [jfa.PASS_QUERY_TILES, jfa.PASS_KEY_TILES, jfa.PASS_DQ_TILES])
+def test_worklist_bit_exact(name, batch, causal, pass_, sched_stage):
+    qo, ko, H, causal = _worklist_case(name, batch, causal)
+    tile = jfa.jfa_tile_shape(pass_)[0]
+    ref_arr = _worklist_ref(name, batch, causal, pass_)
     qo_d = torch.from_numpy(qo.astype(np.int32)).to(dev())
     ko_d = torch.from_numpy(ko.astype(np.int32)).to(dev())
     lq, lk = np.diff(qo), np.diff(ko)
-    items, tile_start = jfa.build_worklist(pass_, qo_d, ko_d, H, int(qo[-1]), int(ko[-1]), int(lq.max()),
-                                           int(lk.max()), causal)
+    items, tile_start, records = jfa.build_worklist(pass_, qo_d, ko_d, H, int(qo[-1]), int(ko[-1]), int(lq.max()),
+                                                    int(lk.max()), causal, with_records=True)
     assert np.array_equal(items.numpy(), ref_arr)
+    # the kernels' per-item records: offsets, lengths, head and tile of each
+    # item in list order, then lq = -1 up to the capacity
+    n = len(ref_arr)
+    bb = ref_arr[:, 0].astype(np.int64)
+    want = np.stack([qo[bb], lq[bb], ko[bb], lk[bb], ref_arr[:, 1] & 255, ref_arr[:, 1] >> 8,
+                     np.zeros(n, np.int64), np.zeros(n, np.int64)], axis=1).astype(np.int32)
+    rec = records.numpy()
+    assert np.array_equal(rec[:n], want)
+    assert np.all(rec[n:, 1] == -1)
     lens = lk if pass_ == jfa.PASS_KEY_TILES else lq
     assert np.array_equal(tile_start.numpy(), offsets_from_lengths(-(-lens // tile)).astype(np.int32))
     # offsets untouched
