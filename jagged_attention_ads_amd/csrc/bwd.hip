@@ -129,9 +129,10 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 //
 // Per 32-row sub-block n there is one barrier.  Before it, A turns S(n) into
 // P(n) and hands P over (the packed P fragments its own dV product uses, or
-// for SiLU the derivative factor packed the same way) while B forms dP(n);
-// after it, A accumulates dV(n) and already forms S(n+1), and B forms dS(n)
-// and accumulates dK(n).
+// for SiLU the derivative factor packed the same way) while B accumulates
+// dK(n-1) and forms dP(n); after it, A accumulates dV(n) and already forms
+// S(n+1), and B forms dS(n).  B's dK runs one sub-block behind so that both
+// sides of the barrier carry MFMA work for both waves.
 template <typename T, int D>
 struct DkdvCfg {
   static constexpr int BN = kBwdBN;
@@ -143,8 +144,11 @@ struct DkdvCfg {
   static constexpr int STAGE = 2 * QT + STATS;
   static constexpr int XSLOT = kWave * 2 * (int)sizeof(frag_t<T>);   // one hand-over: 2 fragments per lane
   static constexpr int XCH = NPAIRS * 2 * XSLOT;         // per pair, two slots
-  using Dma = TileDma<T, D, SR, true, NT>;               // query rows stored swap23-permuted
-  static constexpr int SINK = Dma::N * NT > Dma::CHUNKS ? NT / kWave * 1024 : 0;
+  // The B waves issue every copy of the ring (query rows stored
+  // swap23-permuted): A's path is the longer one, and a burst of copies
+  // right after the barrier stalls the waves that issue it.
+  using Dma = TileDma<T, D, SR, true, NT / 2>;
+  static constexpr int SINK = Dma::N * (NT / 2) > Dma::CHUNKS ? NT / 2 / kWave * 1024 : 0;
   static constexpr int NS = (4 * STAGE + XCH + SINK <= 80 * 1024) ? 4 : 3;   // stages in the ring
   static constexpr int LDS = NS * STAGE + XCH + SINK;
   static constexpr int ND = D / 32, NK = D / 16;
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<T, D>;
   static_assert(C::NT / kWave * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
   using Dma = typename C::Dma;
-  constexpr int NPS = 2 * Dma::N + (ACT == 0 ? 1 : 0);   // copies per thread per stage
+  constexpr int NPS = 2 * Dma::N + (ACT == 0 ? 2 : 0);   // copies per B thread per stage
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   char* const xch = smem + C::NS * C::STAGE;
   char* const sink = xch + C::XCH;
@@ -178,23 +182,30 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
 
   const T* qb = static_cast<const T*>(a.q) + (size_t)qs * rs + (size_t)h * D;
   const T* db = static_cast<const T*>(a.dout) + (size_t)qs * rs + (size_t)h * D;
-  // A needs lse2 of the rows, B needs delta
-  const float* row_h = ACT == 0 ? (role_a ? a.lse2 : a.delta) + (size_t)h * a.total_q + qs : nullptr;
+  // A needs lse2 of the rows, B needs delta: B copies both, each into its
+  // wave's private area of the stage
+  const float* lse2_h = ACT == 0 ? a.lse2 + (size_t)h * a.total_q + qs : nullptr;
+  const float* delta_h = ACT == 0 ? a.delta + (size_t)h * a.total_q + qs : nullptr;
+  const int tid_b = tid - C::NT / 2;   // B waves: 0 .. NT/2-1
   Dma dma;   // Q and dO tiles share the geometry, hence the offsets
-  dma.init(rs, tid);
+  if (!role_a) dma.init(rs, tid_b);
   auto slot = [&](int s) { return smem + (s % C::NS) * C::STAGE; };
-  auto issue_stage = [&](int s) {
+  auto issue_stage = [&](int s) {   // B waves only
     char* st = slot(s);
     const int r0 = q_first + s * C::SR;
-    dma.issue(st, qb, rs, r0, lq, tid, sink);
-    dma.issue(st + C::QT, db, rs, r0, lq, tid, sink);
-    if constexpr (ACT == 0) rows_dma(st + 2 * C::QT + w * 256, row_h, r0, lq);
+    dma.issue(st, qb, rs, r0, lq, tid_b, sink);
+    dma.issue(st + C::QT, db, rs, r0, lq, tid_b, sink);
+    if constexpr (ACT == 0) {
+      rows_dma(st + 2 * C::QT + w * 256, delta_h, r0, lq);
+      rows_dma(st + 2 * C::QT + (w - C::NPAIRS) * 256, lse2_h, r0, lq);
+    }
   };
 
   // Prologue: stages 0 and 1, then this lane's key (A) or value (B) row as
   // B-operand fragments (d-slots 16*kk + 8*g + e); all of it lands before
   // the loop, and the rest of the ring is issued after the barrier.
-  for (int s = 0; s < min(2, nst); ++s) issue_stage(s);
+  if (!role_a)
+    for (int s = 0; s < min(2, nst); ++s) issue_stage(s);
   frag_t<T> xf[C::NK];
   {
     const int j = min(my_key, lk - 1);
@@ -206,8 +217,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   }
   dma_wait();
   __syncthreads();
-  for (int s = 2; s <= C::NS - 2; ++s)
-    if (s < nst) issue_stage(s);
+  if (!role_a)
+    for (int s = 2; s <= C::NS - 2; ++s)
+      if (s < nst) issue_stage(s);
 
   f32x16 acc[C::ND];   // dV^T (A) or dK^T (B): lane = key, registers = d
 #pragma unroll
@@ -278,26 +290,39 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     return (qa + 32 > lq) || (kw0 + 32 > lk) || (a.causal && kw0 + 31 > qa + off);
   };
 
+  // B, one sub-block behind: dK^T += Q^T dS(n) from the packed dS in sf and
+  // stage n's Q rows (k-step ss covers rows 16*ss .. +15 of the sub-block)
+  frag_t<T> sf[2];
+  auto b_dk = [&](int n) {
+    const char* qt = slot(n);
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int d2 = 0; d2 < C::ND; ++d2) mma(acc[d2], lds_col_frag<T, D, true>(qt, 16 * ss, 32 * d2), sf[ss]);
+  };
+
   f32x16 x;   // A: S(n), then P(n);  B: dP(n), then dS(n)
   if (role_a && nst > 0 && visible(0)) products(x, slot(0));
   for (int n = 0; n < nst; ++n) {
     const char* st = slot(n);
-    const char* qt = st;
     const char* dt = st + C::QT;
     const bool vis = visible(n);
-    if (vis) {
-      if (role_a) {
+    if (role_a) {
+      if (vis) {
         if (needs_mask(n)) a_weights(std::true_type{}, x, n, st);
         else a_weights(std::false_type{}, x, n, st);
-      } else {
-        products(x, dt);
       }
+    } else {
+      // stage n-1 is refilled only after this sub-block's barrier
+      if (n > 0 && visible(n - 1)) b_dk(n - 1);
+      if (vis) products(x, dt);
     }
-    // stage n+1 must have landed before the barrier; later ones may be in flight
-    if (n + 1 < nst) wait_stage<NPS>(min(C::NS - 3, nst - 2 - n));
+    // stage n+1 must have landed before the barrier (B issued it; A has no
+    // copies in flight); later ones may be in flight
+    if (!role_a && n + 1 < nst) wait_stage<NPS>(min(C::NS - 3, nst - 2 - n));
     __syncthreads();
     // every wave is done with stage n-1: refill its slot
-    if (n + C::NS - 1 < nst) issue_stage(n + C::NS - 1);
+    if (!role_a && n + C::NS - 1 < nst) issue_stage(n + C::NS - 1);
     if (role_a) {
       // dV^T += dO^T P(n); k-step ss covers rows 16*ss .. +15 of the sub-block
       if (vis) {
@@ -323,15 +348,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
           x[r] = ACT == 0 ? e8[e] * (x[r] - dl[r]) : x[r] * e8[e];   // dS
         }
       }
-      // dK^T += Q^T dS
 #pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        const frag_t<T> sf = pack_frag<T>(x, ss);
-#pragma unroll
-        for (int d2 = 0; d2 < C::ND; ++d2) mma(acc[d2], lds_col_frag<T, D, true>(qt, 16 * ss, 32 * d2), sf);
-      }
+      for (int ss = 0; ss < 2; ++ss) sf[ss] = pack_frag<T>(x, ss);
     }
   }
+  // the last sub-block's dK (its stage is never refilled)
+  if (!role_a && nst > 0 && visible(nst - 1)) b_dk(nst - 1);
 
   // the ring is free once every wave is past the loop: stage the rows there
   __syncthreads();
