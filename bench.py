@@ -5,8 +5,8 @@
 
 A step is one pass of the whole hot path over one batch: the forward call
 (work-list build + attention kernel) and the backward call (work-list
-builds, dQ kernel -- which also forms the softmax row statistics -- and
-dK/dV kernel).  Inputs are generated on
+builds, softmax row statistics, dK/dV kernel -- which also stores the dS
+blocks -- and dQ kernel).  Inputs are generated on
 the host, copied to HBM before timing, and stay resident.  Prints one JSON
 line: useful TFLOPS counted on the visible (query, key) pairs of the real,
 unpadded tokens -- 4*d FLOPs per pair forward, 10*d backward -- the split
@@ -99,31 +99,52 @@ def visible_pairs(q_lengths, kv_lengths, causal):
     return out
 
 
-def kernel_accounting(wl, T_q, T_k, pairs_total):
+def ds_blocks(q_lengths, kv_lengths, causal, blk=32):
+    """Number of 32 x 32 dS blocks that hold a visible pair (the blocks the
+    dK/dV pass stores and the dQ pass reads), over all sequences, per head."""
+    n = 0
+    for lq, lk in zip(np.asarray(q_lengths, np.int64), np.asarray(kv_lengths, np.int64)):
+        if lq <= 0 or lk <= 0:
+            continue
+        last = np.minimum(np.arange(blk, lq + blk, blk), lq) - 1   # last row of each query block
+        kv_end = np.minimum(lk, last + (lk - lq) + 1) if causal else np.full(len(last), lk)
+        n += int(np.sum(-(-np.maximum(kv_end, 0) // blk)))
+    return n
+
+
+def kernel_accounting(wl, T_q, T_k, pairs_total, n_ds_blocks, ds_path):
     """Algorithmic FLOPs (the products each kernel must execute per visible
     pair) and bytes (every tensor the kernel must touch, once) per launch."""
     H, d = wl.heads, wl.head_dim
     es = 2 if wl.dtype == "bf16" else 4
     q_bytes, k_bytes = T_q * H * d * es, T_k * H * d * es
     row_f32 = T_q * H * 4
+    ds_bytes = n_ds_blocks * H * 32 * 32 * es if ds_path else 0
     soft = wl.activation == "softmax"
     acc = {
         "fwd": dict(flops=4 * d * H * pairs_total,
                     bytes=q_bytes + 2 * k_bytes + q_bytes + (row_f32 if soft else 0)),
+        # reads Q, dO, K, V (and lse2, delta); writes dK, dV and the dS blocks
         "bwd_dkdv": dict(flops=8 * d * H * pairs_total,
-                         bytes=2 * q_bytes + 2 * k_bytes + (2 * row_f32 if soft else 0) + 2 * k_bytes),
-        # softmax: also reads O and lse and writes the (lse, delta) row pairs
-        "bwd_dq": dict(flops=6 * d * H * pairs_total + (2 * T_q * H * d if soft else 0),
-                       bytes=2 * q_bytes + 2 * k_bytes + q_bytes + ((q_bytes + 3 * row_f32) if soft else 0)),
+                         bytes=2 * q_bytes + 2 * k_bytes + (2 * row_f32 if soft else 0) + 2 * k_bytes + ds_bytes),
     }
+    if ds_path:   # dQ = scale * dS K: reads the dS blocks and K, writes dQ
+        acc["bwd_dq"] = dict(flops=2 * d * H * pairs_total, bytes=ds_bytes + k_bytes + q_bytes)
+    else:         # recomputes S, P, dP, dS: reads Q, dO, K, V, lse2, delta, writes dQ
+        acc["bwd_dq"] = dict(flops=6 * d * H * pairs_total,
+                             bytes=2 * q_bytes + 2 * k_bytes + q_bytes + (2 * row_f32 if soft else 0))
+    if soft:      # reads O, dO and lse, writes lse2 and delta
+        acc["bwd_stats"] = dict(flops=2 * d * H * T_q, bytes=2 * q_bytes + 3 * row_f32)
     return acc
 
 
-def stored_traffic(kernel, digest):
+def stored_traffic(kernel, digest, workload):
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
+        return None
+    if data.get("workload") != workload:
         return None
     rec = data.get(kernel)
     if not rec or rec.get("source_digest") != digest:
@@ -226,8 +247,12 @@ def main():
     lse = torch.empty((H, T_q), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     B = len(batch.q_lengths)
-    ws_f = jfa.workspace(B, H, D, T_q, T_k, False, dev)
-    ws_b = jfa.workspace(B, H, D, T_q, T_k, True, dev)
+    ws_f = jfa.workspace(B, H, D, T_q, T_k, mk, q.dtype, False, dev)
+    ws_b = jfa.workspace(B, H, D, T_q, T_k, mk, q.dtype, True, dev)
+    # the dK/dV pass stores dS and the dQ pass reads it, unless switched off
+    # or the store was left out of the workspace
+    ds_path = (os.environ.get("JFA_BWD_DS") != "0"
+               and ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, 0, q.dtype, True))
     L = jfa.lib()
     P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
     act = jfa.ACTIVATIONS[wl.activation]
@@ -264,7 +289,7 @@ def main():
 
     K = args.steps
     ef = [ev.create(3) for _ in range(K)]
-    eb = [ev.create(4) for _ in range(K)] if run_bwd else []
+    eb = [ev.create(5) for _ in range(K)] if run_bwd else []
     edge = ev.create(2)
     torch.cuda.synchronize()
     ev.lib.hipEventRecord(edge[0], stream)
@@ -283,8 +308,9 @@ def main():
     fwd_ms = avg(ef, 0, 2)
     bwd_ms = 0.0
     if run_bwd:
-        kern_ms.update({"bwd_sched": avg(eb, 0, 1), "bwd_dq": avg(eb, 1, 2), "bwd_dkdv": avg(eb, 2, 3)})
-        bwd_ms = avg(eb, 0, 3)
+        kern_ms.update({"bwd_sched": avg(eb, 0, 1), "bwd_stats": avg(eb, 1, 2), "bwd_dkdv": avg(eb, 2, 3),
+                        "bwd_dq": avg(eb, 3, 4)})
+        bwd_ms = avg(eb, 0, 4)
 
     pairs = int(visible_pairs(batch.q_lengths, batch.kv_lengths, wl.causal).sum())
     useful_fwd = 4.0 * D * H * pairs
@@ -294,7 +320,8 @@ def main():
     bwd_tf = useful_bwd / (bwd_ms * 1e-3) / 1e12 if run_bwd else None
 
     # roofline of the dominant kernel
-    acct = kernel_accounting(wl, T_q, T_k, pairs)
+    n_blk = ds_blocks(batch.q_lengths, batch.kv_lengths, wl.causal) if run_bwd else 0
+    acct = kernel_accounting(wl, T_q, T_k, pairs, n_blk, ds_path)
     name = max((n for n in acct if n in kern_ms), key=lambda n: kern_ms[n])
     t_s = kern_ms[name] * 1e-3
     ai = acct[name]["flops"] / acct[name]["bytes"]
@@ -305,7 +332,7 @@ def main():
         roof = {"bound": "mfma", "achieved": acct[name]["flops"] / t_s / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(name, digest)
+    roof["traffic"] = stored_traffic(name, digest, wl.name)
     roof.update({"kernel": name, "avg_launch_us": kern_ms[name] * 1e3,
                  "algorithmic_bytes": acct[name]["bytes"], "algorithmic_flops": acct[name]["flops"],
                  "arith_intensity": ai, "mfma_frac": acct[name]["flops"] / t_s / 1e12 / PEAK_BF16_TFLOPS})
@@ -317,6 +344,7 @@ def main():
         "config": {"workload": wl.description, "name": wl.name, "batch": B, "heads": H, "head_dim": D,
                    "causal": wl.causal, "activation": wl.activation, "seed": args.seed, "total_q_tokens": T_q,
                    "total_kv_tokens": T_k, "visible_pairs_per_head": pairs,
+                   "bwd_dq_from_stored_ds": bool(run_bwd and ds_path),
                    "useful_gflop_per_step": (useful_fwd + useful_bwd) / 1e9},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "fwd_tflops": fwd_tf, "fwd_pct_peak": 100.0 * fwd_tf / PEAK_BF16_TFLOPS,

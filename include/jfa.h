@@ -87,10 +87,15 @@ enum jfa_dtype { JFA_DTYPE_BF16 = 0, JFA_DTYPE_FP32 = 1 };
 enum jfa_pass { JFA_PASS_QUERY_TILES = 0, JFA_PASS_KEY_TILES = 1, JFA_PASS_DQ_TILES = 2 };
 
 /* Bytes of device workspace jfa_forward (for_backward = 0) or jfa_backward
- * (for_backward = 1) needs for these sizes.  Never fails; returns 0 for
- * arguments the calls would reject. */
+ * (for_backward = 1) needs for these sizes and element type (dtype is a
+ * jfa_dtype).  Never fails; returns 0 for arguments the calls would reject.
+ * The backward's workspace includes a store for the dS blocks (32 queries x
+ * 32 keys each, in the element type) of every query block:
+ * heads * (total_q / 32 + batch) * ceil(max_kv_len / 32) blocks.  When that
+ * store would exceed 16 GiB it is left out, and the backward then recomputes
+ * dS in its dQ pass (slower, same results up to rounding). */
 size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
-                          int32_t total_kv, int32_t for_backward);
+                          int32_t total_kv, int32_t max_kv_len, int32_t dtype, int32_t for_backward);
 
 /* Forward pass (Jagged Flash Attention item; GDPA item for JFA_ACT_SILU).
  * scale: score scale, typically 1/sqrt(head_dim).  lse may be NULL only for
@@ -107,8 +112,12 @@ int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_of
  * output row summed in registers and stored once).  out and lse are the
  * forward's outputs; both may be NULL only for JFA_ACT_SILU.  Results are
  * bitwise reproducible from run to run.  Enqueues: the work-list builder
- * (both lists), the dQ kernel (which also writes the per-row softmax
- * statistics into the workspace), then the dK/dV kernel. */
+ * (both lists), the row statistics kernel (softmax only: per row,
+ * sum(dout * out) and lse in log2 units, into the workspace), the dK/dV
+ * kernel (which also stores the dS blocks in the workspace), then the dQ
+ * kernel (dQ = scale * dS K over the stored blocks).  The environment
+ * variable JFA_BWD_DS=0, or a workspace sized without the dS store, makes
+ * the dQ kernel recompute dS from Q, K, V and dout instead. */
 int jfa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
                  int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
@@ -119,11 +128,11 @@ int jfa_backward(const void* q, const void* k, const void* v, const void* out, c
  * `stream` between their kernel launches, for per-kernel timing (every
  * kernel still runs; with events == NULL they are jfa_forward and
  * jfa_backward).  Forward: 3 events -- [0] before the work-list builder,
- * [1] before the attention kernel, [2] after it.  Backward: 4 events --
+ * [1] before the attention kernel, [2] after it.  Backward: 5 events --
  * [0] start, [1] after the work-list builder (both lists, one launch),
- * [2] after the dQ kernel (which also forms the per-row softmax
- * statistics), [3] after the dK/dV kernel.  Events are not recorded when the
- * call is a no-op or is rejected. */
+ * [2] after the row statistics kernel (right after [1] for SiLU),
+ * [3] after the dK/dV kernel, [4] after the dQ kernel.  Events are not
+ * recorded when the call is a no-op or is rejected. */
 int jfa_forward_profiled(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                          const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
                          int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation,

@@ -4,6 +4,7 @@
 #include "jfa.h"
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -24,14 +25,22 @@ int hip_fail(hipError_t e, const char* where) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Largest dS store the backward keeps in its workspace; beyond it the dQ
+// pass recomputes dS instead (see jfa.h).
+constexpr uint64_t kDsMaxBytes = uint64_t(16) << 30;
+
 struct WsLayout {
   jfa::WorklistLayout wq{}, wkv{};
-  size_t off_wq = 0, off_wkv = 0, off_stats = 0, bytes = 0;
+  size_t off_wq = 0, off_wkv = 0, off_stats = 0, off_ds = 0, bytes = 0;
+  int64_t ds_rows = 0, ds_kb = 0;
+  bool ds = false;   // the workspace holds the dS blocks
 };
 
 // Forward: the query-tile list.  Backward: the dQ-tile list (in the same
-// slot), the key-tile list and the per-row statistics.
-WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv, bool backward) {
+// slot), the key-tile list, the per-row statistics and, when they fit the
+// limit, the dS blocks.
+WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv, int32_t max_kv_len,
+                   int32_t dtype, bool backward) {
   WsLayout L;
   L.wq = jfa::worklist_layout(backward ? jfa::kPassDQ : jfa::kPassQ, batch, heads, total_q);
   L.off_wq = 0;
@@ -42,9 +51,25 @@ WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_
     off += L.wkv.bytes;
     L.off_stats = off;
     off += align256(static_cast<size_t>(heads) * static_cast<size_t>(total_q) * 2 * sizeof(float));
+    L.ds_rows = jfa::ds_block_rows(batch, total_q);
+    L.ds_kb = jfa::ds_key_blocks(max_kv_len);
+    const uint64_t block = uint64_t(jfa::kDsBlock) * jfa::kDsBlock * (dtype == JFA_DTYPE_FP32 ? 4 : 2);
+    const uint64_t ds_bytes = uint64_t(heads) * uint64_t(L.ds_rows) * uint64_t(L.ds_kb) * block;
+    if (ds_bytes <= kDsMaxBytes) {
+      L.ds = true;
+      L.off_ds = off;
+      off += align256(static_cast<size_t>(ds_bytes));
+    }
   }
   L.bytes = off;
   return L;
+}
+
+// JFA_BWD_DS=0 makes the backward recompute dS in the dQ pass even when the
+// workspace holds the dS blocks (for tests of that pass).
+bool ds_disabled() {
+  const char* e = std::getenv("JFA_BWD_DS");
+  return e && e[0] == '0' && e[1] == 0;
 }
 
 // Records events[i] on the stream when the caller asked for stage events.
@@ -116,9 +141,10 @@ const char* jfa_status_string(int status) {
 const char* jfa_last_error(void) { return g_last_error.c_str(); }
 
 size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
-                          int32_t for_backward) {
-  if (check_sizes(batch, heads, head_dim, total_q, total_kv, 0, 0) != JFA_OK) return 0;
-  return ws_layout(batch, heads, total_q, total_kv, for_backward != 0).bytes;
+                          int32_t max_kv_len, int32_t dtype, int32_t for_backward) {
+  if (check_sizes(batch, heads, head_dim, total_q, total_kv, 0, max_kv_len) != JFA_OK) return 0;
+  if (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_FP32) return 0;
+  return ws_layout(batch, heads, total_q, total_kv, max_kv_len, dtype, for_backward != 0).bytes;
 }
 
 bool valid_pass(int32_t pass) {
@@ -185,7 +211,7 @@ int jfa_forward_profiled(const void* q, const void* k, const void* v, const int3
   const int32_t nb = buckets_for(max_kv_len, jfa::kFwdBN);
   if (nb > jfa::kMaxBuckets) return fail(JFA_ERR_UNSUPPORTED, "max_kv_len exceeds the scheduler's range");
   if (batch == 0 || total_q == 0) return JFA_OK;   // nothing to write
-  const WsLayout L = ws_layout(batch, heads, total_q, total_kv, false);
+  const WsLayout L = ws_layout(batch, heads, total_q, total_kv, max_kv_len, dtype, false);
   if (!workspace || workspace_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
 
   char* ws = static_cast<char*>(workspace);
@@ -246,7 +272,7 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   if (nbq > jfa::kMaxBuckets || nbk > jfa::kMaxBuckets)
     return fail(JFA_ERR_UNSUPPORTED, "maximum length exceeds the scheduler's range");
   if (batch == 0 || (total_q == 0 && total_kv == 0)) return JFA_OK;   // nothing to write
-  const WsLayout L = ws_layout(batch, heads, total_q, total_kv, true);
+  const WsLayout L = ws_layout(batch, heads, total_q, total_kv, max_kv_len, dtype, true);
   if (!workspace || workspace_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
 
   char* ws = static_cast<char*>(workspace);
@@ -264,6 +290,11 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   a.meta_kv = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wkv + L.wkv.meta_off);
   a.lse2 = reinterpret_cast<float*>(ws + L.off_stats);
   a.delta = a.lse2 + static_cast<size_t>(heads) * static_cast<size_t>(total_q);
+  if (L.ds && !ds_disabled()) {
+    a.ds = ws + L.off_ds;
+    a.ds_head_blocks = L.ds_rows * L.ds_kb;
+    a.ds_kb = static_cast<int32_t>(L.ds_kb);
+  }
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -287,17 +318,23 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   }
   if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
   if ((e = record(events, 1, stream)) != hipSuccess) return hip_fail(e, "event record");
-  // dQ first: it also writes the per-row lse and delta the dK/dV pass reads
-  if (total_q > 0) {
-    e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, L.wq.capacity, stream);
-    if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
+  // per-row lse2 and delta, read by both gradient passes (softmax)
+  if (activation == JFA_ACT_SOFTMAX && total_q > 0) {
+    e = jfa::launch_bwd_stats(a, head_dim, dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "row statistics kernel launch");
   }
   if ((e = record(events, 2, stream)) != hipSuccess) return hip_fail(e, "event record");
+  // dK/dV first: it also stores the dS blocks the dQ pass reads
   if (total_kv > 0) {
     e = jfa::launch_bwd_dkdv(a, head_dim, dtype, activation, L.wkv.capacity, stream);
     if (e != hipSuccess) return hip_fail(e, "dK/dV kernel launch");
   }
   if ((e = record(events, 3, stream)) != hipSuccess) return hip_fail(e, "event record");
+  if (total_q > 0) {
+    e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, L.wq.capacity, stream);
+    if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
+  }
+  if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;
 }
 

@@ -5,21 +5,23 @@
 //
 // The gradient sums over queries (dK, dV) and over keys (dQ) are split into
 // two passes so that every output row is owned by exactly one workgroup and
-// stored once:
+// stored once.  Launch order:
+//   row statistics (softmax only) -- per (row, head): delta_i =
+//     sum_c dO_ic O_ic, the row sum of P o dP that the softmax Jacobian
+//     needs, and lse_i * log2(e);
 //   dK/dV pass -- one work item per (sequence, head, 64-key tile); each
 //     pair of waves owns 32 keys and walks the query rows that see them in
 //     32-row sub-blocks.  P and dS are recomputed from lse (softmax) or from
-//     the scores (SiLU).
-//   dQ pass -- one work item per (sequence, head, 128-query tile); each wave
-//     owns 32 queries and walks the keys they see in 32-key sub-blocks.
-// The dQ pass runs first: while loading its rows it also forms
-// delta_i = sum_c dO_ic O_ic (softmax only), the row sum of P o dP that the
-// softmax Jacobian needs, and stores it and lse_i * log2(e) for the dK/dV
-// pass.
+//     the scores (SiLU).  It also stores every dS block it forms (bf16 or
+//     fp32, 32 queries x 32 keys), so that
+//   dQ pass -- one work item per (sequence, head, 64-query tile) -- is the
+//     single product dQ = scale * dS K over the stored blocks.  When the dS
+//     blocks would not fit the workspace limit, the dQ pass instead
+//     recomputes S, P, dP and dS itself (three products instead of one).
 //
-// Both passes stream the operand they walk (Q and dO, or K and V) from HBM
-// straight into a ring of swizzled LDS stages, two or more stages ahead of
-// use (buffer loads that write LDS).
+// Every pass streams the operand it walks (Q and dO, K and V, or K and dS)
+// from HBM straight into a ring of swizzled LDS stages, two or more stages
+// ahead of use (buffer loads that write LDS).
 //
 // Per (query i, key j) pair, with x = scale * q_i.k_j:
 //   softmax: P = exp(x - lse_i);        dS = P (dP - delta_i)
@@ -38,24 +40,6 @@ namespace jfa {
 // lse in log2 units, with rows that see no key (lse = -inf) mapped to 0:
 // those rows are fully masked, and a finite value keeps every product finite.
 __device__ __forceinline__ float lse_log2(float lse) { return lse > -INFINITY ? lse * kLog2e : 0.f; }
-
-// Sum of the products of the 8 elements of two fragments.
-__device__ __forceinline__ float frag_dot(const bf16x8& x, const bf16x8& y) {
-  const u32x4 a = __builtin_bit_cast(u32x4, x), b = __builtin_bit_cast(u32x4, y);
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
-    acc = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), acc);
-  }
-  return acc;
-}
-__device__ __forceinline__ float frag_dot(const f32x8& x, const f32x8& y) {
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc = fmaf(x[e], y[e], acc);
-  return acc;
-}
 
 // The 8 values of a fragment as floats (element e of the fragment -> v[e]).
 __device__ __forceinline__ void frag_unpack(const bf16x8& f, float* v) {
@@ -117,6 +101,80 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   else dma_wait_all_but<0>();
 }
 
+// ---------------------------------------------------------------- row statistics
+
+// delta = sum_c dO_c O_c (fp32 sum of the stored values' products) and
+// lse * log2(e) for every (row, head).  Rows are read as a flat array of
+// total_q * heads vectors of D values; LPR lanes share one vector, 16 bytes
+// each, and reduce with cross-lane swaps.  Memory-bound: every O and dO byte
+// is read once.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void stats_kernel(BwdArgs a) {
+  constexpr int LPR = D * (int)sizeof(T) / 16;   // lanes per (row, head)
+  constexpr int PPB = 256 / LPR;                 // (row, head) vectors per pass of the block
+  constexpr int kIter = 4;                       // passes per block, loads first
+  constexpr int EPL = 16 / (int)sizeof(T);       // elements per lane
+  const int tid = threadIdx.x, sub = tid % LPR;
+  const int64_t nvec = (int64_t)a.total_q * a.heads;
+  const int64_t v0 = (int64_t)blockIdx.x * (PPB * kIter) + tid / LPR;
+  u32x4 o[kIter], d[kIter];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int64_t vi = v0 + (int64_t)i * PPB;
+    o[i] = u32x4{0u, 0u, 0u, 0u};
+    d[i] = o[i];
+    if (vi < nvec) {
+      const size_t e = (size_t)vi * D + (size_t)sub * EPL;
+      o[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.out) + e);
+      d[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + e);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    float part = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if constexpr (sizeof(T) == 2) {
+        part = fmaf(__uint_as_float(o[i][w] << 16), __uint_as_float(d[i][w] << 16), part);
+        part = fmaf(__uint_as_float(o[i][w] & 0xffff0000u), __uint_as_float(d[i][w] & 0xffff0000u), part);
+      } else {
+        part = fmaf(__uint_as_float(o[i][w]), __uint_as_float(d[i][w]), part);
+      }
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+    const int64_t vi = v0 + (int64_t)i * PPB;
+    if (sub == 0 && vi < nvec) {
+      const int64_t row = vi / a.heads, h = vi % a.heads;
+      const size_t si = (size_t)h * a.total_q + row;
+      a.delta[si] = part;
+      a.lse2[si] = lse_log2(a.lse[si]);
+    }
+  }
+}
+
+// One stored dS block: 32 x 32 values of a [key][query] tile in the LDS
+// layout of 32-element rows (Swz<T, 32>), so that the dQ pass copies it into
+// LDS unchanged and reads dS^T fragments with transposed LDS reads.
+template <typename T>
+struct DsTile {
+  using S = Swz<T, kDsBlock>;
+  static constexpr int BYTES = S::tile_bytes(kDsBlock);
+};
+
+// The 8 values of a fragment -- row r, columns c0 .. c0+7 (c0 a multiple
+// of 8) -- stored into a dS block image.
+template <typename T>
+__device__ __forceinline__ void ds_store(char* blk, int r, int c0, const frag_t<T>& f) {
+  using S = typename DsTile<T>::S;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<u32x4*>(blk + S::off(r, c0 >> 3)) = __builtin_bit_cast(u32x4, f);
+  } else {
+    *reinterpret_cast<f32x4*>(blk + S::off(r, c0 >> 2)) = f32x4{f[0], f[1], f[2], f[3]};
+    *reinterpret_cast<f32x4*>(blk + S::off(r, (c0 >> 2) + 1)) = f32x4{f[4], f[5], f[6], f[7]};
+  }
+}
+
 // ---------------------------------------------------------------- dK / dV
 
 // Four waves per 64-key item: two pairs, each pair owning 32 keys.  Wave A of
@@ -154,7 +212,7 @@ struct DkdvCfg {
   static constexpr int ND = D / 32, NK = D / 16;
 };
 
-template <typename T, int D, int ACT>
+template <typename T, int D, int ACT, bool DS>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<T, D>;
   static_assert(C::NT / kWave * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
@@ -171,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, l = lane_id(), w = tid >> 6, g = l >> 5, c32 = l & 31;
   const int pair = w % C::NPAIRS;
-  const bool role_a = w < C::NPAIRS;       // A: S, P, dV;  B: dP, dS, dK
+  const bool role_a = w < C::NPAIRS;       // A: S, P, dV;  B: dP, dS, dK (and the dS store)
   const int kw0 = t * C::BN + 32 * pair;   // first key of this pair
   const int my_key = kw0 + c32;            // the key this lane owns (its column of S)
   const bool wave_live = kw0 < lk;
@@ -179,6 +237,13 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   const int q_first = kv_tile_first_q_block(lq, lk, t, C::SR, C::BN, a.causal) * C::SR;
   const int rs = a.heads * D;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
+  // DS: this pair's dS block of sub-block 0; sub-block n is n block rows on
+  [[maybe_unused]] char* ds_blk = nullptr;
+  [[maybe_unused]] const int ds_row_bytes = a.ds_kb * DsTile<T>::BYTES;
+  if constexpr (DS)
+    ds_blk = static_cast<char*>(a.ds) +
+             ((int64_t)h * a.ds_head_blocks + (int64_t)(qs / kDsBlock + m.seq + q_first / kDsBlock) * a.ds_kb +
+              kw0 / kDsBlock) * DsTile<T>::BYTES;
 
   const T* qb = static_cast<const T*>(a.q) + (size_t)qs * rs + (size_t)h * D;
   const T* db = static_cast<const T*>(a.dout) + (size_t)qs * rs + (size_t)h * D;
@@ -350,6 +415,13 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) sf[ss] = pack_frag<T>(x, ss);
+      if constexpr (DS) {
+        // the dS the dK product uses, for the dQ pass: this lane's key row,
+        // queries 16*ss + 8*g .. +7 of the sub-block
+        char* blk = ds_blk + (int64_t)n * ds_row_bytes;
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) ds_store<T>(blk, c32, 16 * ss + 8 * g, sf[ss]);
+      }
     }
   }
   // the last sub-block's dK (its stage is never refilled)
@@ -372,7 +444,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
 // dP^T = V dO^T and the handed-over values, accumulates dQ^T += K^T dS^T,
 // then forms dP^T of sub-block n.  A's exponentials overlap B's products on
 // the same SIMD; one barrier per sub-block.  Every lane owns one query, so
-// lse and delta are per-lane scalars (written here for the dK/dV pass).
+// lse and delta (from the row statistics kernel) are per-lane scalars.
+// This is the dQ pass used when the dS blocks are not stored.
 template <typename T, int D>
 struct DqCfg {
   static constexpr int BM = kDqBM;
@@ -436,21 +509,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     const T* xp = static_cast<const T*>(role_a ? a.q : a.dout) + ro;
 #pragma unroll
     for (int kk = 0; kk < C::NK; ++kk) xf[kk] = global_frag<T>(xp + 16 * kk);
-    if (ACT == 0) {
-      const size_t si = (size_t)h * a.total_q + qs + r;
-      if (role_a) {
-        stat = lse_log2(a.lse[si]);
-      } else {
-        // delta of this lane's row: each lane group holds half the row's
-        // d-slots, summed across the two groups
-        const T* op = static_cast<const T*>(a.out) + ro;
-        float part = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < C::NK; ++kk) part += frag_dot(global_frag<T>(op + 16 * kk), xf[kk]);
-        stat = xor32_sum(part);
-      }
-      if (g == 0 && my_row < lq) (role_a ? a.lse2 : a.delta)[si] = stat;
-    }
+    if (ACT == 0) stat = (role_a ? a.lse2 : a.delta)[(size_t)h * a.total_q + qs + r];
 #pragma unroll
     for (int kk = 0; kk < C::NK; ++kk) settle(xf[kk]);
     settle(stat);
@@ -556,38 +615,190 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   store_rows_lds<T, D>(dqp, rs, min(32, lq - row0), dq, a.scale, smem + w * store_scratch_bytes<T, D>());
 }
 
+
+// dQ from the stored dS blocks: dQ^T = scale * K^T dS^T, one product per
+// (query, key) pair instead of three.  One workgroup per 64-query item; wave
+// w owns query block w & 1 (32 queries) and half of the d-blocks (w >> 1).
+// Each stage of the LDS ring holds 32 key rows and the item's two dS blocks
+// of those keys, copied unchanged from HBM; K^T and dS^T fragments both come
+// from transposed LDS reads (rows = keys).  A dS block is read only where the
+// dK/dV pass wrote it: query blocks that see some key of the key block.
+template <typename T, int D>
+struct DqDsCfg {
+  static constexpr int BM = kDqBM;                       // queries per item
+  static constexpr int NQB = BM / kDsBlock;              // dS blocks per stage
+  static constexpr int SR = kDsBlock;                    // key rows per stage
+  static constexpr int NT = 256;
+  static constexpr int KT = Swz<T, D>::tile_bytes(SR);   // K tile
+  static constexpr int DT = DsTile<T>::BYTES;            // one dS block
+  static constexpr int STAGE = KT + NQB * DT;
+  using Dma = TileDma<T, D, SR, false, NT>;              // key rows in order
+  static constexpr int NDS = NQB * DT / 16 / NT;         // dS copies per thread per stage
+  static_assert(NQB * DT % (16 * NT) == 0 && (DT / 16) % kWave == 0, "dS copies must split by whole waves");
+  static constexpr int SINK = Dma::N * NT > Dma::CHUNKS ? NT / kWave * 1024 : 0;
+  static constexpr int NS = 4;
+  static constexpr int LDS = NS * STAGE + SINK;
+  static constexpr int ND = D / 32;
+  static constexpr int NDW = ND >= 2 ? ND / 2 : 1;       // d-blocks per wave
+  static constexpr int WGS = LDS <= 52 * 1024 ? 3 : LDS <= 80 * 1024 ? 2 : 1;   // workgroups per CU
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, (DqDsCfg<T, D>::WGS)) void dq_ds_kernel(BwdArgs a) {
+  using C = DqDsCfg<T, D>;
+  static_assert(4 * store_scratch_bytes<T, C::NDW * 32>() <= C::LDS,
+                "output staging must fit the LDS");
+  using Dma = typename C::Dma;
+  constexpr int NPS = Dma::N + C::NDS;   // copies per thread per stage
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  char* const sink = smem + C::NS * C::STAGE;
+
+  const ItemMeta m = a.meta_q[blockIdx.x];   // one load: offsets, lengths, head, tile, sequence
+  if (m.lq < 0) return;                       // past the item count
+  const int qs = m.qs, lq = m.lq, ks = m.ks, lk = m.lk, h = m.head, t = m.tile;
+  const int off = lk - lq;
+
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int qw = w & 1, dh = w >> 1;            // query block, d-half
+  const bool has_d = dh * C::NDW < C::ND;       // D = 32: only waves 0 and 1 multiply
+  const int row0 = t * C::BM + kDsBlock * qw;   // first query of this wave
+  const bool wave_live = row0 < lq;
+  const int nst = q_tile_kv_blocks(lq, lk, t, C::BM, C::SR, a.causal);
+  const int rs = a.heads * D;
+
+  // query block qb of the item sees key block n (so its dS block exists)
+  auto sees = [&](int qb, int n) {
+    const int r0 = t * C::BM + kDsBlock * qb;
+    return r0 < lq && (!a.causal || kDsBlock * n <= r0 + kDsBlock - 1 + off);
+  };
+  const T* kb = static_cast<const T*>(a.k) + (size_t)ks * rs + (size_t)h * D;
+  // dS block row of the item's first query block; a block row is ds_kb blocks
+  const char* ds0 = static_cast<const char*>(a.ds) +
+                    ((int64_t)h * a.ds_head_blocks + (int64_t)(qs / kDsBlock + m.seq + t * C::NQB) * a.ds_kb) * C::DT;
+  Dma dma;
+  dma.init(rs, tid);
+  auto slot = [&](int s) { return smem + (s % C::NS) * C::STAGE; };
+  auto issue_stage = [&](int s) {
+    char* st = slot(s);
+    dma.issue(st, kb, rs, s * C::SR, lk, tid, sink);
+#pragma unroll
+    for (int i = 0; i < C::NDS; ++i) {
+      const int pw = i * C::NT + kWave * w;    // this wave's first chunk of the stage's dS blocks
+      const int qb = pw / (C::DT / 16), ch = pw % (C::DT / 16);
+      const char* blk = ds0 + ((int64_t)qb * a.ds_kb + s) * C::DT;
+      // blocks the dK/dV pass did not write are never read: zeros instead
+      buffer_load_lds16(uniform_rsrc(blk, sees(qb, s) ? C::DT : 0), (ch + lane_id()) * 16, st + C::KT + pw * 16);
+    }
+  };
+
+  for (int s = 0; s < min(2, nst); ++s) issue_stage(s);
+  dma_wait();
+  __syncthreads();
+  for (int s = 2; s <= C::NS - 2; ++s)
+    if (s < nst) issue_stage(s);
+
+  f32x16 acc[C::NDW];   // dQ^T (d x queries) for this wave's d-blocks, lane = query
+#pragma unroll
+  for (int i = 0; i < C::NDW; ++i) acc[i] = f32x16{};
+
+  for (int n = 0; n < nst; ++n) {
+    if (has_d && wave_live && sees(qw, n)) {
+      const char* kt = slot(n);
+      const char* dt = kt + C::KT + qw * C::DT;
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        const frag_t<T> sf = lds_col_frag<T, kDsBlock, false>(dt, 16 * ss, 0);
+#pragma unroll
+        for (int j = 0; j < C::NDW; ++j)
+          mma(acc[j], lds_col_frag<T, D, false>(kt, 16 * ss, 32 * (dh * C::NDW + j)), sf);
+      }
+    }
+    // stage n+1 must have landed before the barrier; later ones may be in flight
+    if (n + 1 < nst) wait_stage<NPS>(min(C::NS - 3, nst - 2 - n));
+    __syncthreads();
+    // every wave is done with stage n-1: refill its slot
+    if (n + C::NS - 1 < nst) issue_stage(n + C::NS - 1);
+  }
+
+  // the loop's last barrier follows every wave's last LDS read (and with no
+  // stage at all, the prologue's barrier): stage the rows there
+  if (!has_d || !wave_live) return;
+  T* dqp = static_cast<T*>(a.dq) + (size_t)(qs + row0) * rs + (size_t)h * D + dh * C::NDW * 32;
+  store_rows_lds<T, C::NDW * 32>(dqp, rs, min(32, lq - row0), acc, a.scale,
+                                 smem + w * store_scratch_bytes<T, C::NDW * 32>());
+}
+
 #define JFA_BWD_INST(T, D, ACT)                                      \
-  template __global__ void dkdv_kernel<T, D, ACT>(BwdArgs);          \
+  template __global__ void dkdv_kernel<T, D, ACT, false>(BwdArgs);   \
+  template __global__ void dkdv_kernel<T, D, ACT, true>(BwdArgs);    \
   template __global__ void dq_kernel<T, D, ACT>(BwdArgs);
 JFA_BWD_INST(__bf16, 32, 0) JFA_BWD_INST(__bf16, 64, 0) JFA_BWD_INST(__bf16, 128, 0)
 JFA_BWD_INST(__bf16, 32, 1) JFA_BWD_INST(__bf16, 64, 1) JFA_BWD_INST(__bf16, 128, 1)
 JFA_BWD_INST(float, 32, 0) JFA_BWD_INST(float, 64, 0) JFA_BWD_INST(float, 128, 0)
 JFA_BWD_INST(float, 32, 1) JFA_BWD_INST(float, 64, 1) JFA_BWD_INST(float, 128, 1)
 #undef JFA_BWD_INST
+#define JFA_BWD_INST2(T, D)                                          \
+  template __global__ void stats_kernel<T, D>(BwdArgs);              \
+  template __global__ void dq_ds_kernel<T, D>(BwdArgs);
+JFA_BWD_INST2(__bf16, 32) JFA_BWD_INST2(__bf16, 64) JFA_BWD_INST2(__bf16, 128)
+JFA_BWD_INST2(float, 32) JFA_BWD_INST2(float, 64) JFA_BWD_INST2(float, 128)
+#undef JFA_BWD_INST2
 
 // ---------------------------------------------------------------- launchers
 
-#define JFA_BWD_LAUNCHER(NAME, KERNEL, THREADS)                                                          \
-  template <typename T, int ACT>                                                                         \
-  static hipError_t NAME##_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {         \
-    switch (head_dim) {                                                                                  \
-      case 32: hipLaunchKernelGGL((KERNEL<T, 32, ACT>), dim3((unsigned)grid), dim3(THREADS), 0, stream, a); break;  \
-      case 64: hipLaunchKernelGGL((KERNEL<T, 64, ACT>), dim3((unsigned)grid), dim3(THREADS), 0, stream, a); break;  \
-      case 128: hipLaunchKernelGGL((KERNEL<T, 128, ACT>), dim3((unsigned)grid), dim3(THREADS), 0, stream, a); break; \
-      default: return hipErrorInvalidValue;                                                              \
-    }                                                                                                    \
-    return hipGetLastError();                                                                            \
-  }                                                                                                      \
-  hipError_t launch_bwd_##NAME(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid,         \
-                               hipStream_t stream) {                                                     \
-    if (grid <= 0) return hipSuccess;                                                                    \
-    if (dtype == 0) return act == 0 ? NAME##_d<__bf16, 0>(a, head_dim, grid, stream)                     \
-                                    : NAME##_d<__bf16, 1>(a, head_dim, grid, stream);                    \
-    return act == 0 ? NAME##_d<float, 0>(a, head_dim, grid, stream)                                      \
-                    : NAME##_d<float, 1>(a, head_dim, grid, stream);                                     \
-  }
+template <typename K>
+static hipError_t launch_k(K kernel, const BwdArgs& a, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
-JFA_BWD_LAUNCHER(dkdv, dkdv_kernel, 256)
-JFA_BWD_LAUNCHER(dq, dq_kernel, 256)
+// kernel variant for (dtype, head_dim): pick(dtype 0 = bf16 / 1 = fp32, D)
+#define JFA_PICK_D(EXPR_T_D)                                      \
+  switch (head_dim) {                                             \
+    case 32: { constexpr int D = 32; EXPR_T_D; }                  \
+    case 64: { constexpr int D = 64; EXPR_T_D; }                  \
+    case 128: { constexpr int D = 128; EXPR_T_D; }                \
+  }                                                               \
+  return hipErrorInvalidValue;
+
+template <typename T, int ACT>
+static hipError_t dkdv_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
+  const bool ds = a.ds != nullptr;
+  JFA_PICK_D(return launch_k(ds ? dkdv_kernel<T, D, ACT, true> : dkdv_kernel<T, D, ACT, false>, a, grid, stream))
+}
+template <typename T, int ACT>
+static hipError_t dq_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
+  if (a.ds != nullptr) {
+    JFA_PICK_D(return launch_k(dq_ds_kernel<T, D>, a, grid, stream))
+  }
+  JFA_PICK_D(return launch_k(dq_kernel<T, D, ACT>, a, grid, stream))
+}
+template <typename T>
+static hipError_t stats_d(const BwdArgs& a, int head_dim, hipStream_t stream) {
+  const int64_t nvec = (int64_t)a.total_q * a.heads;
+  JFA_PICK_D({
+    constexpr int per_block = 256 / (D * (int)sizeof(T) / 16) * 4;   // vectors per block (stats_kernel)
+    const int64_t grid = (nvec + per_block - 1) / per_block;
+    if (grid <= 0) return hipSuccess;
+    return launch_k(stats_kernel<T, D>, a, grid, stream);
+  })
+}
+#undef JFA_PICK_D
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (dtype == 0) return act == 0 ? dkdv_d<__bf16, 0>(a, head_dim, grid, stream) : dkdv_d<__bf16, 1>(a, head_dim, grid, stream);
+  return act == 0 ? dkdv_d<float, 0>(a, head_dim, grid, stream) : dkdv_d<float, 1>(a, head_dim, grid, stream);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (dtype == 0) return act == 0 ? dq_d<__bf16, 0>(a, head_dim, grid, stream) : dq_d<__bf16, 1>(a, head_dim, grid, stream);
+  return act == 0 ? dq_d<float, 0>(a, head_dim, grid, stream) : dq_d<float, 1>(a, head_dim, grid, stream);
+}
+
+hipError_t launch_bwd_stats(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream) {
+  return dtype == 0 ? stats_d<__bf16>(a, head_dim, stream) : stats_d<float>(a, head_dim, stream);
+}
 
 }  // namespace jfa

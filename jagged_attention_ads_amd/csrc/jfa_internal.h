@@ -21,11 +21,21 @@ constexpr int kMaxHeads = 256;      // head index is packed into 8 bits
 enum Pass { kPassQ = 0, kPassKV = 1, kPassDQ = 2 };
 
 // Per-item record the attention kernels read with one load: the sequence's
-// first query and key rows and lengths, and the item's head and tile.
-// Records past the item count have lq = -1.
+// first query and key rows and lengths, the item's head and tile, and the
+// sequence index.  Records past the item count have lq = -1.
 struct ItemMeta {
-  int32_t qs, lq, ks, lk, head, tile, unused0, unused1;
+  int32_t qs, lq, ks, lk, head, tile, seq, unused;
 };
+
+// dS blocks of the backward: 32 queries x 32 keys, stored as the byte image
+// of a [key][query] LDS tile.  Sequence b's query block i (rows 32i .. 32i+31
+// of the sequence) is block row q_offsets[b] / 32 + b + i, which keeps the
+// sequences' ranges disjoint without a prefix sum; a block row holds
+// ceil(max_kv_len / 32) key blocks, and a head holds total_q / 32 + batch
+// block rows.
+constexpr int kDsBlock = 32;
+inline int64_t ds_block_rows(int32_t batch, int32_t total_q) { return (int64_t)total_q / kDsBlock + batch; }
+inline int64_t ds_key_blocks(int32_t max_kv_len) { return ((int64_t)max_kv_len + kDsBlock - 1) / kDsBlock; }
 
 // Device layout of a work list (all offsets in bytes from its base):
 //   0                      int32   item count
@@ -76,8 +86,12 @@ struct BwdArgs {
   const ItemMeta* meta_q;   // dQ-tile records (dQ pass)
   const ItemMeta* meta_kv;  // key-tile records (dK/dV pass)
   float* lse2;             // [heads, total_q] workspace: lse * log2(e) per row, and
-  float* delta;            // [heads, total_q] delta per row; both written by the dQ pass
-                           // (softmax), read by the dK/dV pass
+  float* delta;            // [heads, total_q] delta per row; both written by the row
+                           // statistics kernel (softmax), read by both gradient passes
+  void* ds;                // dS blocks (see kDsBlock), written by the dK/dV pass and read by
+                           // the dQ pass; null when the dQ pass recomputes dS
+  int64_t ds_head_blocks;  // blocks per head: ds_block_rows * ds_kb
+  int32_t ds_kb;           // key blocks per block row
   void* dq;
   void* dk;
   void* dv;
@@ -89,7 +103,11 @@ struct BwdArgs {
   float scale_log2;
 };
 
+// Row statistics (softmax): lse2 and delta for every (row, head).
+hipError_t launch_bwd_stats(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
+// dK/dV pass; with a.ds set it also stores dS for the dQ pass.
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
+// dQ pass: from the stored dS when a.ds is set, else recomputing dS.
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
 
 }  // namespace jfa

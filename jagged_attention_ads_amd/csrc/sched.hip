@@ -298,7 +298,7 @@ __device__ void sched_body_lds(const int* __restrict__ qo, const int* __restrict
       const int u = (int)(w & 0xffff), hh = (int)(w >> 16);
       const int b = (int)(tile_info[u].x >> kTileInfoBits), t = u - ts[b];
       job.items[p] = make_int2(b, (t << 8) | hh);
-      m = ItemMeta{qof[b], qof[b + 1] - qof[b], kof[b], kof[b + 1] - kof[b], hh, t, 0, 0};
+      m = ItemMeta{qof[b], qof[b + 1] - qof[b], kof[b], kof[b + 1] - kof[b], hh, t, b, 0};
     }
     job.meta[p] = m;
   }
@@ -410,7 +410,7 @@ __device__ void sched_body_global(const int* __restrict__ qo, const int* __restr
       const int q0 = qo[b], q1 = qo[b + 1], k0 = ko[b], k1 = ko[b + 1];
       const int lq = i < n_in ? q1 - q0 : -1;
       const u32x4 lo = {(uint32_t)q0, (uint32_t)lq, (uint32_t)k0, (uint32_t)(k1 - k0)};
-      const u32x4 hi = {(uint32_t)(it[r].y & 255), (uint32_t)(it[r].y >> 8), 0u, 0u};
+      const u32x4 hi = {(uint32_t)(it[r].y & 255), (uint32_t)(it[r].y >> 8), (uint32_t)b, 0u};
       const int off = i * (int)sizeof(ItemMeta);
       __builtin_amdgcn_raw_buffer_store_b128(lo, mrs, off, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(hi, mrs, off + 16, 0, 0);

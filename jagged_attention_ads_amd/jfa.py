@@ -52,7 +52,7 @@ def lib():
                               % _LIB_PATH)
         L = ctypes.CDLL(_LIB_PATH)
         L.jfa_workspace_size.restype = _sz
-        L.jfa_workspace_size.argtypes = [_i32] * 6
+        L.jfa_workspace_size.argtypes = [_i32] * 8
         L.jfa_forward.restype = ctypes.c_int
         L.jfa_forward.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_i32] * 7 + [_f32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
         L.jfa_backward.restype = ctypes.c_int
@@ -110,8 +110,11 @@ def jfa_status_string(status):
     return lib().jfa_status_string(status).decode()
 
 
-def jfa_workspace_size(batch, heads, head_dim, total_q, total_kv, for_backward):
-    return lib().jfa_workspace_size(batch, heads, head_dim, total_q, total_kv, int(for_backward))
+def jfa_workspace_size(batch, heads, head_dim, total_q, total_kv, max_kv_len, dtype, for_backward):
+    """dtype: a torch dtype (bfloat16 / float32) or its jfa_dtype code."""
+    code = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return lib().jfa_workspace_size(batch, heads, head_dim, total_q, total_kv, int(max_kv_len), code,
+                                    int(for_backward))
 
 
 def jfa_worklist_bytes(pass_, batch, heads, total_q, total_kv):
@@ -166,8 +169,8 @@ def jfa_build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, m
 
 # ---------------------------------------------------------------- allocating wrappers
 
-def workspace(batch, heads, head_dim, total_q, total_kv, for_backward, device):
-    n = jfa_workspace_size(batch, heads, head_dim, total_q, total_kv, for_backward)
+def workspace(batch, heads, head_dim, total_q, total_kv, max_kv_len, dtype, for_backward, device):
+    n = jfa_workspace_size(batch, heads, head_dim, total_q, total_kv, max_kv_len, dtype, for_backward)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
@@ -180,7 +183,7 @@ def forward(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale=None, a
     out = torch.empty_like(q)
     lse = torch.empty((H, T_q), dtype=torch.float32, device=q.device) if activation == "softmax" else None
     if ws is None:
-        ws = workspace(q_offsets.numel() - 1, H, D, T_q, k.shape[0], False, q.device)
+        ws = workspace(q_offsets.numel() - 1, H, D, T_q, k.shape[0], max_kv_len, q.dtype, False, q.device)
     jfa_forward(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation, causal, out, lse, ws)
     return out, lse
 
@@ -193,7 +196,7 @@ def backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_l
         scale = 1.0 / math.sqrt(D)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if ws is None:
-        ws = workspace(q_offsets.numel() - 1, H, D, T_q, k.shape[0], True, q.device)
+        ws = workspace(q_offsets.numel() - 1, H, D, T_q, k.shape[0], max_kv_len, q.dtype, True, q.device)
     jfa_backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation,
                  causal, dq, dk, dv, ws)
     return dq, dk, dv
@@ -204,7 +207,7 @@ def build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, max_q
     """Runs the device work-list builder; returns (items int32 [n, 2], tile_start int32 [B+1]) on the host.
 
     with_records: also return the per-item records the attention kernels read,
-    int32 [capacity, 8] = (q start, q length, kv start, kv length, head, tile, 0, 0),
+    int32 [capacity, 8] = (q start, q length, kv start, kv length, head, tile, sequence, 0),
     q length -1 past the item count (an internal layout, for tests)."""
     B = q_offsets.numel() - 1
     nbytes = jfa_worklist_bytes(pass_, B, heads, total_q, total_kv)

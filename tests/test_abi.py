@@ -96,11 +96,23 @@ def test_backward_noop_and_silu_optional():
 
 
 def test_workspace_sizes():
-    fwd = jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 0)
-    bwd = jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 1)
+    fwd = jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 1024, 0, 0)
+    bwd = jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 1024, 0, 1)
     assert 0 < fwd < bwd
-    assert bwd - fwd >= 4 * 97000 * 8            # holds (lse, delta) pairs [heads, total_q] fp32
-    assert jfa.jfa_workspace_size(2, 2, 48, 10, 10, 0) == 0
+    # (lse, delta) pairs [heads, total_q] fp32, then the dS store: heads x
+    # (total_q // 32 + batch) block rows x ceil(max_kv_len / 32) blocks of 32 x 32 bf16
+    ds = 4 * (97000 // 32 + 256) * 32 * 32 * 32 * 2
+    assert bwd - fwd >= 4 * 97000 * 8 + ds
+    # fp32 blocks are twice the size
+    bwd32 = jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 1024, 1, 1)
+    assert bwd32 - bwd >= ds
+    # the forward does not depend on the key length or the element type
+    assert jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 5, 1, 0) == fwd
+    # a dS store beyond 16 GiB is left out (the dQ pass then recomputes dS)
+    big = jfa.jfa_workspace_size(64, 64, 128, 260000, 260000, 65000, 0, 1)
+    assert 0 < big < (16 << 30)
+    assert jfa.jfa_workspace_size(2, 2, 48, 10, 10, 10, 0, 0) == 0
+    assert jfa.jfa_workspace_size(2, 2, 32, 10, 10, 10, 5, 1) == 0   # bad dtype
 
 
 def test_tile_shapes_and_worklist_size():

@@ -72,12 +72,12 @@ def test_worklist_bit_exact(name, batch, causal, pass_, sched_stage):
     items, tile_start, records = jfa.build_worklist(pass_, qo_d, ko_d, H, int(qo[-1]), int(ko[-1]), int(lq.max()),
                                                     int(lk.max()), causal, with_records=True)
     assert np.array_equal(items.numpy(), ref_arr)
-    # the kernels' per-item records: offsets, lengths, head and tile of each
+    # the kernels' per-item records: offsets, lengths, head, tile and sequence of each
     # item in list order, then lq = -1 up to the capacity
     n = len(ref_arr)
     bb = ref_arr[:, 0].astype(np.int64)
     want = np.stack([qo[bb], lq[bb], ko[bb], lk[bb], ref_arr[:, 1] & 255, ref_arr[:, 1] >> 8,
-                     np.zeros(n, np.int64), np.zeros(n, np.int64)], axis=1).astype(np.int32)
+                     bb, np.zeros(n, np.int64)], axis=1).astype(np.int32)
     rec = records.numpy()
     assert np.array_equal(rec[:n], want)
     assert np.all(rec[n:, 1] == -1)
@@ -110,7 +110,7 @@ def test_every_slot_written_once_and_guards_intact(name):
     lse_b = torch.full((H * T_q + 7,), canary, dtype=torch.float32, device=dev())
     out, dq, dk, dv = out_b[:T_q], dq_b[:T_q], dk_b[:T_k], dv_b[:T_k]
     lse = lse_b[:H * T_q].view(H, T_q) if wl.activation == "softmax" else None
-    ws = jfa.workspace(len(b.q_lengths), H, D, T_q, T_k, True, dev())
+    ws = jfa.workspace(len(b.q_lengths), H, D, T_q, T_k, d.mk, d.q.dtype, True, dev())
     jfa.jfa_forward(d.q, d.k, d.v, d.qo, d.ko, d.mq, d.mk, d.scale, d.act, d.causal, out, lse, ws)
     jfa.jfa_backward(d.q, d.k, d.v, out, d.do, lse, d.qo, d.ko, d.mq, d.mk, d.scale, d.act, d.causal, dq, dk, dv, ws)
     torch.cuda.synchronize()

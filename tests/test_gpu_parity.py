@@ -71,8 +71,31 @@ def _edge_batch(name):
     return make_batch(wl, 100 + sorted(EDGE).index(name), q_lengths=lq, kv_lengths=lk, with_dout=True)
 
 
+@pytest.fixture(params=["stored_ds", "recompute"])
+def dq_path(request, monkeypatch):
+    """The backward's two dQ passes: from the dS blocks the dK/dV pass stores
+    (the default), or recomputing dS (JFA_BWD_DS=0; also what runs when the
+    dS store would not fit the workspace limit)."""
+    if request.param == "recompute":
+        monkeypatch.setenv("JFA_BWD_DS", "0")
+    else:
+        monkeypatch.delenv("JFA_BWD_DS", raising=False)
+    return request.param
+
+
+@pytest.mark.parametrize("name,batch", [x for x in REDUCED if WORKLOADS[x[0]].backward])
+def test_backward_reduced_recompute(name, batch, monkeypatch):
+    monkeypatch.setenv("JFA_BWD_DS", "0")
+    b = make_batch(name, _seed(name), batch=batch)
+    d = Dev(b)
+    out, lse = d.forward()
+    grads = d.backward(out, lse)
+    torch.cuda.synchronize()
+    check_backward(grads, oracle_bwd(b))
+
+
 @pytest.mark.parametrize("name", sorted(EDGE))
-def test_edge_cases(name):
+def test_edge_cases(name, dq_path):
     b = _edge_batch(name)
     d = Dev(b)
     out, lse = d.forward()
