@@ -3,6 +3,7 @@
 // contract.
 #include "jfa.h"
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -31,6 +32,7 @@ constexpr uint64_t kDsMaxBytes = uint64_t(16) << 30;
 
 struct WsLayout {
   jfa::WorklistLayout wq{}, wkv{};
+  jfa::WorklistLayout wq_fwd{};   // backward: the 128-row query tiles of the dQ pass over stored dS
   size_t off_wq = 0, off_wkv = 0, off_stats = 0, off_ds = 0, bytes = 0;
   int64_t ds_rows = 0, ds_kb = 0;
   bool ds = false;   // the workspace holds the dS blocks
@@ -45,6 +47,10 @@ WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_
   L.wq = jfa::worklist_layout(backward ? jfa::kPassDQ : jfa::kPassQ, batch, heads, total_q);
   L.off_wq = 0;
   size_t off = L.wq.bytes;
+  if (backward) {   // the slot holds either query-tile list
+    L.wq_fwd = jfa::worklist_layout(jfa::kPassQ, batch, heads, total_q);
+    off = std::max(off, L.wq_fwd.bytes);
+  }
   if (backward) {
     L.wkv = jfa::worklist_layout(jfa::kPassKV, batch, heads, total_kv);
     L.off_wkv = off;
@@ -269,6 +275,7 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   }
   const int32_t nbq = buckets_for(max_kv_len, jfa::kDqBN);
   const int32_t nbk = buckets_for(max_q_len, jfa::kBwdBM);
+  static_assert(jfa::kDqBN == jfa::kFwdBN, "both query-tile lists count 64-key blocks");
   if (nbq > jfa::kMaxBuckets || nbk > jfa::kMaxBuckets)
     return fail(JFA_ERR_UNSUPPORTED, "maximum length exceeds the scheduler's range");
   if (batch == 0 || (total_q == 0 && total_kv == 0)) return JFA_OK;   // nothing to write
@@ -286,11 +293,16 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   a.lse = lse;
   a.qo = q_offsets;
   a.ko = kv_offsets;
-  a.meta_q = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + L.wq.meta_off);
+  // the dQ pass over stored dS walks the forward's 128-row query tiles, the
+  // recomputing one 64-row tiles
+  const bool use_ds = L.ds && !ds_disabled();
+  const int qpass = use_ds ? jfa::kPassQ : jfa::kPassDQ;
+  const jfa::WorklistLayout& lay_q = use_ds ? L.wq_fwd : L.wq;
+  a.meta_q = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + lay_q.meta_off);
   a.meta_kv = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wkv + L.wkv.meta_off);
   a.lse2 = reinterpret_cast<float*>(ws + L.off_stats);
   a.delta = a.lse2 + static_cast<size_t>(heads) * static_cast<size_t>(total_q);
-  if (L.ds && !ds_disabled()) {
+  if (use_ds) {
     a.ds = ws + L.off_ds;
     a.ds_head_blocks = L.ds_rows * L.ds_kb;
     a.ds_kb = static_cast<int32_t>(L.ds_kb);
@@ -305,22 +317,26 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
 
+  // per-row lse2 and delta, read by both gradient passes (softmax): formed
+  // by the work-list launch's spare workgroups when it builds both lists,
+  // else by a kernel of their own
+  const bool stats = activation == JFA_ACT_SOFTMAX && total_q > 0;
+  const jfa::StatsArgs sa{out, dout, lse, a.lse2, a.delta, heads, total_q};
   if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
-  if (total_q > 0 && total_kv > 0) {
-    e = jfa::launch_sched_pair(q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq, nbk,
-                               ws + L.off_wkv, L.wkv, stream);
+  const bool pair = total_q > 0 && total_kv > 0;
+  if (pair) {
+    e = jfa::launch_sched_pair(qpass, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, lay_q, nbk,
+                               ws + L.off_wkv, L.wkv, stats ? &sa : nullptr, dtype, head_dim, stream);
   } else if (total_q > 0) {
-    e = jfa::launch_sched(jfa::kPassDQ, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq,
-                          stream);
+    e = jfa::launch_sched(qpass, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, lay_q, stream);
   } else {
     e = jfa::launch_sched(jfa::kPassKV, q_offsets, kv_offsets, batch, heads, causal, nbk, ws + L.off_wkv, L.wkv,
                           stream);
   }
   if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
   if ((e = record(events, 1, stream)) != hipSuccess) return hip_fail(e, "event record");
-  // per-row lse2 and delta, read by both gradient passes (softmax)
-  if (activation == JFA_ACT_SOFTMAX && total_q > 0) {
-    e = jfa::launch_bwd_stats(a, head_dim, dtype, stream);
+  if (stats && !pair) {
+    e = jfa::launch_bwd_stats(sa, head_dim, dtype, stream);
     if (e != hipSuccess) return hip_fail(e, "row statistics kernel launch");
   }
   if ((e = record(events, 2, stream)) != hipSuccess) return hip_fail(e, "event record");
@@ -331,7 +347,7 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   }
   if ((e = record(events, 3, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (total_q > 0) {
-    e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, L.wq.capacity, stream);
+    e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, lay_q.capacity, stream);
     if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
   }
   if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");

@@ -30,6 +30,7 @@
 //   dV_j += P dO_i,  dP = dO_i . V_j,  dK_j += scale dS q_i,  dQ_i += scale dS k_j
 #include <type_traits>
 
+#include "bwd_stats.hpp"
 #include "jfa_common.hpp"
 #include "jfa_internal.h"
 
@@ -37,9 +38,6 @@ namespace jfa {
 
 // ---------------------------------------------------------------- shared math
 
-// lse in log2 units, with rows that see no key (lse = -inf) mapped to 0:
-// those rows are fully masked, and a finite value keeps every product finite.
-__device__ __forceinline__ float lse_log2(float lse) { return lse > -INFINITY ? lse * kLog2e : 0.f; }
 
 // The 8 values of a fragment as floats (element e of the fragment -> v[e]).
 __device__ __forceinline__ void frag_unpack(const bf16x8& f, float* v) {
@@ -103,54 +101,12 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 
 // ---------------------------------------------------------------- row statistics
 
-// delta = sum_c dO_c O_c (fp32 sum of the stored values' products) and
-// lse * log2(e) for every (row, head).  Rows are read as a flat array of
-// total_q * heads vectors of D values; LPR lanes share one vector, 16 bytes
-// each, and reduce with cross-lane swaps.  Memory-bound: every O and dO byte
-// is read once.
+// Row statistics (softmax) as a kernel of its own: workgroup (x, y) covers
+// head y of the rows of chunk x (the backward's work-list launch forms them
+// in its spare workgroups instead whenever it builds both lists).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void stats_kernel(BwdArgs a) {
-  constexpr int LPR = D * (int)sizeof(T) / 16;   // lanes per (row, head)
-  constexpr int PPB = 256 / LPR;                 // (row, head) vectors per pass of the block
-  constexpr int kIter = 4;                       // passes per block, loads first
-  constexpr int EPL = 16 / (int)sizeof(T);       // elements per lane
-  const int tid = threadIdx.x, sub = tid % LPR;
-  const int64_t nvec = (int64_t)a.total_q * a.heads;
-  const int64_t v0 = (int64_t)blockIdx.x * (PPB * kIter) + tid / LPR;
-  u32x4 o[kIter], d[kIter];
-#pragma unroll
-  for (int i = 0; i < kIter; ++i) {
-    const int64_t vi = v0 + (int64_t)i * PPB;
-    o[i] = u32x4{0u, 0u, 0u, 0u};
-    d[i] = o[i];
-    if (vi < nvec) {
-      const size_t e = (size_t)vi * D + (size_t)sub * EPL;
-      o[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.out) + e);
-      d[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dout) + e);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kIter; ++i) {
-    float part = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if constexpr (sizeof(T) == 2) {
-        part = fmaf(__uint_as_float(o[i][w] << 16), __uint_as_float(d[i][w] << 16), part);
-        part = fmaf(__uint_as_float(o[i][w] & 0xffff0000u), __uint_as_float(d[i][w] & 0xffff0000u), part);
-      } else {
-        part = fmaf(__uint_as_float(o[i][w]), __uint_as_float(d[i][w]), part);
-      }
-    }
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m);
-    const int64_t vi = v0 + (int64_t)i * PPB;
-    if (sub == 0 && vi < nvec) {
-      const int64_t row = vi / a.heads, h = vi % a.heads;
-      const size_t si = (size_t)h * a.total_q + row;
-      a.delta[si] = part;
-      a.lse2[si] = lse_log2(a.lse[si]);
-    }
-  }
+__global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
+  stats_block<T, D, 256>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // One stored dS block: 32 x 32 values of a [key][query] tile in the LDS
@@ -163,15 +119,18 @@ struct DsTile {
 };
 
 // The 8 values of a fragment -- row r, columns c0 .. c0+7 (c0 a multiple
-// of 8) -- stored into a dS block image.
+// of 8) -- stored into a dS block image.  Non-temporal: each block is read
+// once, by the dQ pass, and should not displace the Q and dO rows that the
+// dK/dV pass re-reads through the cache.
 template <typename T>
 __device__ __forceinline__ void ds_store(char* blk, int r, int c0, const frag_t<T>& f) {
   using S = typename DsTile<T>::S;
   if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<u32x4*>(blk + S::off(r, c0 >> 3)) = __builtin_bit_cast(u32x4, f);
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, f), reinterpret_cast<u32x4*>(blk + S::off(r, c0 >> 3)));
   } else {
-    *reinterpret_cast<f32x4*>(blk + S::off(r, c0 >> 2)) = f32x4{f[0], f[1], f[2], f[3]};
-    *reinterpret_cast<f32x4*>(blk + S::off(r, (c0 >> 2) + 1)) = f32x4{f[4], f[5], f[6], f[7]};
+    __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<f32x4*>(blk + S::off(r, c0 >> 2)));
+    __builtin_nontemporal_store(f32x4{f[4], f[5], f[6], f[7]},
+                                reinterpret_cast<f32x4*>(blk + S::off(r, (c0 >> 2) + 1)));
   }
 }
 
@@ -617,18 +576,19 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 
 
 // dQ from the stored dS blocks: dQ^T = scale * K^T dS^T, one product per
-// (query, key) pair instead of three.  One workgroup per 64-query item; wave
-// w owns query block w & 1 (32 queries) and half of the d-blocks (w >> 1).
-// Each stage of the LDS ring holds 32 key rows and the item's two dS blocks
-// of those keys, copied unchanged from HBM; K^T and dS^T fragments both come
-// from transposed LDS reads (rows = keys).  A dS block is read only where the
-// dK/dV pass wrote it: query blocks that see some key of the key block.
+// (query, key) pair instead of three.  One workgroup per 128-query item (the
+// forward's tiles: each K row is fetched once per 128 queries); wave w owns
+// query block w (32 queries) and every d-block.  Each stage of the LDS ring
+// holds 32 key rows and the item's four dS blocks of those keys, copied
+// unchanged from HBM; K^T and dS^T fragments both come from transposed LDS
+// reads (rows = keys).  A dS block is read only where the dK/dV pass wrote
+// it: query blocks that see some key of the key block.
 template <typename T, int D>
 struct DqDsCfg {
-  static constexpr int BM = kDqBM;                       // queries per item
-  static constexpr int NQB = BM / kDsBlock;              // dS blocks per stage
+  static constexpr int BM = kFwdBM;                      // queries per item
+  static constexpr int NQB = BM / kDsBlock;              // dS blocks per stage = waves
   static constexpr int SR = kDsBlock;                    // key rows per stage
-  static constexpr int NT = 256;
+  static constexpr int NT = NQB * kWave;
   static constexpr int KT = Swz<T, D>::tile_bytes(SR);   // K tile
   static constexpr int DT = DsTile<T>::BYTES;            // one dS block
   static constexpr int STAGE = KT + NQB * DT;
@@ -636,18 +596,28 @@ struct DqDsCfg {
   static constexpr int NDS = NQB * DT / 16 / NT;         // dS copies per thread per stage
   static_assert(NQB * DT % (16 * NT) == 0 && (DT / 16) % kWave == 0, "dS copies must split by whole waves");
   static constexpr int SINK = Dma::N * NT > Dma::CHUNKS ? NT / kWave * 1024 : 0;
-  static constexpr int NS = 4;
+  static constexpr int NS = 4 * STAGE + SINK <= 80 * 1024 ? 4 : 3;   // two stages in flight where it fits
   static constexpr int LDS = NS * STAGE + SINK;
   static constexpr int ND = D / 32;
-  static constexpr int NDW = ND >= 2 ? ND / 2 : 1;       // d-blocks per wave
   static constexpr int WGS = LDS <= 52 * 1024 ? 3 : LDS <= 80 * 1024 ? 2 : 1;   // workgroups per CU
 };
 
+// Waits until stage s has landed in a ring of NS stages whose later stages
+// (up to NS - 2 of them, N copies each per thread) may still be in flight.
+template <int N, int NS>
+__device__ __forceinline__ void wait_ring(int ahead) {
+  if constexpr (NS >= 4) {
+    wait_stage<N>(ahead);
+  } else {
+    if (ahead >= 1) dma_wait_all_but<N>();
+    else dma_wait_all_but<0>();
+  }
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256, (DqDsCfg<T, D>::WGS)) void dq_ds_kernel(BwdArgs a) {
+__global__ __launch_bounds__((DqDsCfg<T, D>::NT), (DqDsCfg<T, D>::WGS)) void dq_ds_kernel(BwdArgs a) {
   using C = DqDsCfg<T, D>;
-  static_assert(4 * store_scratch_bytes<T, C::NDW * 32>() <= C::LDS,
-                "output staging must fit the LDS");
+  static_assert(C::NQB * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
   using Dma = typename C::Dma;
   constexpr int NPS = Dma::N + C::NDS;   // copies per thread per stage
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -659,9 +629,7 @@ __global__ __launch_bounds__(256, (DqDsCfg<T, D>::WGS)) void dq_ds_kernel(BwdArg
   const int off = lk - lq;
 
   const int tid = threadIdx.x, w = tid >> 6;
-  const int qw = w & 1, dh = w >> 1;            // query block, d-half
-  const bool has_d = dh * C::NDW < C::ND;       // D = 32: only waves 0 and 1 multiply
-  const int row0 = t * C::BM + kDsBlock * qw;   // first query of this wave
+  const int row0 = t * C::BM + kDsBlock * w;   // first query of this wave
   const bool wave_live = row0 < lq;
   const int nst = q_tile_kv_blocks(lq, lk, t, C::BM, C::SR, a.causal);
   const int rs = a.heads * D;
@@ -686,8 +654,9 @@ __global__ __launch_bounds__(256, (DqDsCfg<T, D>::WGS)) void dq_ds_kernel(BwdArg
       const int pw = i * C::NT + kWave * w;    // this wave's first chunk of the stage's dS blocks
       const int qb = pw / (C::DT / 16), ch = pw % (C::DT / 16);
       const char* blk = ds0 + ((int64_t)qb * a.ds_kb + s) * C::DT;
-      // blocks the dK/dV pass did not write are never read: zeros instead
-      buffer_load_lds16(uniform_rsrc(blk, sees(qb, s) ? C::DT : 0), (ch + lane_id()) * 16, st + C::KT + pw * 16);
+      // blocks the dK/dV pass did not write are never read: zeros instead.
+      // Non-temporal copies: every dS block is read exactly once
+      buffer_load_lds16<true>(uniform_rsrc(blk, sees(qb, s) ? C::DT : 0), (ch + lane_id()) * 16, st + C::KT + pw * 16);
     }
   };
 
@@ -697,24 +666,23 @@ __global__ __launch_bounds__(256, (DqDsCfg<T, D>::WGS)) void dq_ds_kernel(BwdArg
   for (int s = 2; s <= C::NS - 2; ++s)
     if (s < nst) issue_stage(s);
 
-  f32x16 acc[C::NDW];   // dQ^T (d x queries) for this wave's d-blocks, lane = query
+  f32x16 acc[C::ND];   // dQ^T (d x queries) of this wave's queries, lane = query
 #pragma unroll
-  for (int i = 0; i < C::NDW; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < C::ND; ++i) acc[i] = f32x16{};
 
   for (int n = 0; n < nst; ++n) {
-    if (has_d && wave_live && sees(qw, n)) {
+    if (sees(w, n)) {
       const char* kt = slot(n);
-      const char* dt = kt + C::KT + qw * C::DT;
+      const char* dt = kt + C::KT + w * C::DT;
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
         const frag_t<T> sf = lds_col_frag<T, kDsBlock, false>(dt, 16 * ss, 0);
 #pragma unroll
-        for (int j = 0; j < C::NDW; ++j)
-          mma(acc[j], lds_col_frag<T, D, false>(kt, 16 * ss, 32 * (dh * C::NDW + j)), sf);
+        for (int j = 0; j < C::ND; ++j) mma(acc[j], lds_col_frag<T, D, false>(kt, 16 * ss, 32 * j), sf);
       }
     }
     // stage n+1 must have landed before the barrier; later ones may be in flight
-    if (n + 1 < nst) wait_stage<NPS>(min(C::NS - 3, nst - 2 - n));
+    if (n + 1 < nst) wait_ring<NPS, C::NS>(min(C::NS - 3, nst - 2 - n));
     __syncthreads();
     // every wave is done with stage n-1: refill its slot
     if (n + C::NS - 1 < nst) issue_stage(n + C::NS - 1);
@@ -722,10 +690,9 @@ __global__ __launch_bounds__(256, (DqDsCfg<T, D>::WGS)) void dq_ds_kernel(BwdArg
 
   // the loop's last barrier follows every wave's last LDS read (and with no
   // stage at all, the prologue's barrier): stage the rows there
-  if (!has_d || !wave_live) return;
-  T* dqp = static_cast<T*>(a.dq) + (size_t)(qs + row0) * rs + (size_t)h * D + dh * C::NDW * 32;
-  store_rows_lds<T, C::NDW * 32>(dqp, rs, min(32, lq - row0), acc, a.scale,
-                                 smem + w * store_scratch_bytes<T, C::NDW * 32>());
+  if (!wave_live) return;
+  T* dqp = static_cast<T*>(a.dq) + (size_t)(qs + row0) * rs + (size_t)h * D;
+  store_rows_lds<T, D>(dqp, rs, min(32, lq - row0), acc, a.scale, smem + w * store_scratch_bytes<T, D>());
 }
 
 #define JFA_BWD_INST(T, D, ACT)                                      \
@@ -738,7 +705,7 @@ JFA_BWD_INST(float, 32, 0) JFA_BWD_INST(float, 64, 0) JFA_BWD_INST(float, 128, 0
 JFA_BWD_INST(float, 32, 1) JFA_BWD_INST(float, 64, 1) JFA_BWD_INST(float, 128, 1)
 #undef JFA_BWD_INST
 #define JFA_BWD_INST2(T, D)                                          \
-  template __global__ void stats_kernel<T, D>(BwdArgs);              \
+  template __global__ void stats_kernel<T, D>(StatsArgs);            \
   template __global__ void dq_ds_kernel<T, D>(BwdArgs);
 JFA_BWD_INST2(__bf16, 32) JFA_BWD_INST2(__bf16, 64) JFA_BWD_INST2(__bf16, 128)
 JFA_BWD_INST2(float, 32) JFA_BWD_INST2(float, 64) JFA_BWD_INST2(float, 128)
@@ -747,8 +714,8 @@ JFA_BWD_INST2(float, 32) JFA_BWD_INST2(float, 64) JFA_BWD_INST2(float, 128)
 // ---------------------------------------------------------------- launchers
 
 template <typename K>
-static hipError_t launch_k(K kernel, const BwdArgs& a, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+static hipError_t launch_k(K kernel, const BwdArgs& a, int64_t grid, hipStream_t stream, int threads = 256) {
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -769,18 +736,17 @@ static hipError_t dkdv_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream
 template <typename T, int ACT>
 static hipError_t dq_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
   if (a.ds != nullptr) {
-    JFA_PICK_D(return launch_k(dq_ds_kernel<T, D>, a, grid, stream))
+    JFA_PICK_D(return launch_k(dq_ds_kernel<T, D>, a, grid, stream, DqDsCfg<T, D>::NT))
   }
   JFA_PICK_D(return launch_k(dq_kernel<T, D, ACT>, a, grid, stream))
 }
 template <typename T>
-static hipError_t stats_d(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  const int64_t nvec = (int64_t)a.total_q * a.heads;
+static hipError_t stats_d(const StatsArgs& a, int head_dim, hipStream_t stream) {
   JFA_PICK_D({
-    constexpr int per_block = 256 / (D * (int)sizeof(T) / 16) * 4;   // vectors per block (stats_kernel)
-    const int64_t grid = (nvec + per_block - 1) / per_block;
-    if (grid <= 0) return hipSuccess;
-    return launch_k(stats_kernel<T, D>, a, grid, stream);
+    const int gx = (a.total_q + (StatsCfg<T, D, 256>::ROWS) - 1) / (StatsCfg<T, D, 256>::ROWS);
+    if (gx <= 0) return hipSuccess;
+    hipLaunchKernelGGL((stats_kernel<T, D>), dim3((unsigned)gx, (unsigned)a.heads), dim3(256), 0, stream, a);
+    return hipGetLastError();
   })
 }
 #undef JFA_PICK_D
@@ -797,7 +763,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, int act, int
   return act == 0 ? dq_d<float, 0>(a, head_dim, grid, stream) : dq_d<float, 1>(a, head_dim, grid, stream);
 }
 
-hipError_t launch_bwd_stats(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream) {
+hipError_t launch_bwd_stats(const StatsArgs& a, int head_dim, int dtype, hipStream_t stream) {
   return dtype == 0 ? stats_d<__bf16>(a, head_dim, stream) : stats_d<float>(a, head_dim, stream);
 }
 

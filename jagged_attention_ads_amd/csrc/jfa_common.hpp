@@ -384,9 +384,14 @@ struct TileStage {
 // sooner, and M0 may have just been written by a scalar instruction, which
 // an LDS copy must not follow in the next cycle.  The compiler inserts these
 // waits for its own instructions but cannot see into inline assembly.
+// NT: non-temporal (streaming) cache policy, for data read exactly once.
+template <bool NT = false>
 __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, int voff, const char* lds) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(JFA_LDS const char*)lds;   // the compiler moves it to M0
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+  if constexpr (NT)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+  else
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
 }
 
 // Raw buffer resource over `bytes` bytes at `base`, for values that are

@@ -51,10 +51,24 @@ WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t t
 hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                         int32_t causal, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
                         hipStream_t stream);
-// The backward's two lists in one launch (two workgroups): dQ tiles and key tiles.
-hipError_t launch_sched_pair(const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads, int32_t causal,
-                             int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv, void* wl_kv,
-                             const WorklistLayout& lay_kv, hipStream_t stream);
+// Inputs and outputs of the softmax backward's row statistics.
+struct StatsArgs {
+  const void* out;
+  const void* dout;
+  const float* lse;
+  float* lse2;    // [heads, total_q]
+  float* delta;   // [heads, total_q]
+  int32_t heads;
+  int32_t total_q;
+};
+
+// The backward's two lists in one launch (two workgroups): the dQ pass's
+// query tiles (qpass: kPassQ or kPassDQ) and the key tiles.  With `stats`,
+// the launch's further workgroups form the row statistics meanwhile.
+hipError_t launch_sched_pair(int qpass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
+                             int32_t causal, int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv,
+                             void* wl_kv, const WorklistLayout& lay_kv, const StatsArgs* stats, int dtype,
+                             int head_dim, hipStream_t stream);
 
 struct FwdArgs {
   const void* q;
@@ -83,7 +97,8 @@ struct BwdArgs {
   const float* lse;
   const int32_t* qo;
   const int32_t* ko;
-  const ItemMeta* meta_q;   // dQ-tile records (dQ pass)
+  const ItemMeta* meta_q;   // query-tile records of the dQ pass (128-row tiles when it reads
+                            // the stored dS, 64-row tiles when it recomputes dS)
   const ItemMeta* meta_kv;  // key-tile records (dK/dV pass)
   float* lse2;             // [heads, total_q] workspace: lse * log2(e) per row, and
   float* delta;            // [heads, total_q] delta per row; both written by the row
@@ -104,7 +119,7 @@ struct BwdArgs {
 };
 
 // Row statistics (softmax): lse2 and delta for every (row, head).
-hipError_t launch_bwd_stats(const BwdArgs& a, int head_dim, int dtype, hipStream_t stream);
+hipError_t launch_bwd_stats(const StatsArgs& a, int head_dim, int dtype, hipStream_t stream);
 // dK/dV pass; with a.ds set it also stores dS for the dQ pass.
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
 // dQ pass: from the stored dS when a.ds is set, else recomputing dS.

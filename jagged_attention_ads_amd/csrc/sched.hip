@@ -16,6 +16,7 @@
 #include <cstdint>
 #include <cstdlib>
 
+#include "bwd_stats.hpp"
 #include "jfa_common.hpp"
 #include "jfa_internal.h"
 
@@ -432,14 +433,27 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
   sched_body<PASS>(qo, ko, B, H, causal, job, smem);
 }
 
-// The backward's two lists in one launch: workgroup 0 builds the dQ-tile
-// list, workgroup 1 the key-tile list.
+// The backward's two lists in one launch: workgroup 0 builds the
+// query-tile list of the dQ pass (QPASS: the forward's 128-row tiles or the
+// 64-row dQ tiles), workgroup 1 the key-tile list.  Further workgroups, when
+// launched (softmax), form the row statistics of elements T and head
+// dimension D meanwhile: workgroup 2 + i covers row chunk i / heads of head
+// i % heads.  The two builders run alone on their compute units for most of
+// their time; the statistics fill the rest of the chip.
+template <int QPASS, typename T, int D>
 __global__ __launch_bounds__(kSchedThreads) void sched_pair_kernel(const int* __restrict__ qo,
                                                                    const int* __restrict__ ko, int B, int H,
-                                                                   int causal, SchedJob jdq, SchedJob jkv) {
+                                                                   int causal, SchedJob jdq, SchedJob jkv,
+                                                                   StatsArgs sa) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  if (blockIdx.x == 0) sched_body<kPassDQ>(qo, ko, B, H, causal, jdq, smem);
-  else sched_body<kPassKV>(qo, ko, B, H, causal, jkv, smem);
+  if (blockIdx.x == 0) {
+    sched_body<QPASS>(qo, ko, B, H, causal, jdq, smem);
+  } else if (blockIdx.x == 1) {
+    sched_body<kPassKV>(qo, ko, B, H, causal, jkv, smem);
+  } else {
+    const int i = (int)blockIdx.x - 2;
+    stats_block<T, D, kSchedThreads>(sa, i / sa.heads, i % sa.heads, (int)threadIdx.x);
+  }
 }
 
 WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t total_rows) {
@@ -512,15 +526,43 @@ hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t 
   return hipGetLastError();
 }
 
-hipError_t launch_sched_pair(const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads, int32_t causal,
-                             int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv, void* wl_kv,
-                             const WorklistLayout& lay_kv, hipStream_t stream) {
+template <int QPASS, typename T, int D>
+static hipError_t pair_launch(const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads, int32_t causal,
+                              const SchedJob& jq, const SchedJob& jkv, const StatsArgs* stats, size_t lds,
+                              hipStream_t stream) {
+  constexpr int rows = StatsCfg<T, D, kSchedThreads>::ROWS;
+  const int64_t extra = stats ? (int64_t)((stats->total_q + rows - 1) / rows) * heads : 0;
+  const StatsArgs sa = stats ? *stats : StatsArgs{};
+  hipLaunchKernelGGL((sched_pair_kernel<QPASS, T, D>), dim3((unsigned)(2 + extra)), dim3(kSchedThreads), lds, stream,
+                     qo, ko, batch, heads, causal, jq, jkv, sa);
+  return hipGetLastError();
+}
+
+template <int QPASS, typename T>
+static hipError_t pair_launch_d(int head_dim, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
+                                int32_t causal, const SchedJob& jq, const SchedJob& jkv, const StatsArgs* stats,
+                                size_t lds, hipStream_t stream) {
+  switch (head_dim) {
+    case 32: return pair_launch<QPASS, T, 32>(qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream);
+    case 64: return pair_launch<QPASS, T, 64>(qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream);
+    case 128: return pair_launch<QPASS, T, 128>(qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_sched_pair(int qpass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
+                             int32_t causal, int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv,
+                             void* wl_kv, const WorklistLayout& lay_kv, const StatsArgs* stats, int dtype,
+                             int head_dim, hipStream_t stream) {
   size_t lds_q, lds_kv;
   const SchedJob jq = make_job(batch, heads, nb_dq, wl_dq, lay_dq, lds_q);
   const SchedJob jkv = make_job(batch, heads, nb_kv, wl_kv, lay_kv, lds_kv);
-  hipLaunchKernelGGL(sched_pair_kernel, dim3(2), dim3(kSchedThreads), lds_q > lds_kv ? lds_q : lds_kv, stream, qo,
-                     ko, batch, heads, causal, jq, jkv);
-  return hipGetLastError();
+  const size_t lds = lds_q > lds_kv ? lds_q : lds_kv;
+  if (qpass == kPassQ)
+    return dtype == 0 ? pair_launch_d<kPassQ, __bf16>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream)
+                      : pair_launch_d<kPassQ, float>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream);
+  return dtype == 0 ? pair_launch_d<kPassDQ, __bf16>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream)
+                    : pair_launch_d<kPassDQ, float>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream);
 }
 
 }  // namespace jfa
