@@ -252,7 +252,7 @@ def main():
     # the dK/dV pass stores dS and the dQ pass reads it, unless switched off
     # or the store was left out of the workspace
     ds_path = (os.environ.get("JFA_BWD_DS") != "0"
-               and ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, 0, q.dtype, True))
+               and ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, mk, q.dtype, 2))
     L = jfa.lib()
     P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
     act = jfa.ACTIVATIONS[wl.activation]

@@ -93,7 +93,10 @@ enum jfa_pass { JFA_PASS_QUERY_TILES = 0, JFA_PASS_KEY_TILES = 1, JFA_PASS_DQ_TI
  * 32 keys each, in the element type) of every query block:
  * heads * (total_q / 32 + batch) * ceil(max_kv_len / 32) blocks.  When that
  * store would exceed 16 GiB it is left out, and the backward then recomputes
- * dS in its dQ pass (slower, same results up to rounding). */
+ * dS in its dQ pass (slower, same results up to rounding).
+ * for_backward = 2 gives the smallest workspace jfa_backward accepts: the
+ * same without the dS store.  jfa_backward given less than the full size but
+ * at least that recomputes dS in its dQ pass. */
 size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
                           int32_t total_kv, int32_t max_kv_len, int32_t dtype, int32_t for_backward);
 

@@ -42,7 +42,7 @@ struct WsLayout {
 // slot), the key-tile list, the per-row statistics and, when they fit the
 // limit, the dS blocks.
 WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv, int32_t max_kv_len,
-                   int32_t dtype, bool backward) {
+                   int32_t dtype, bool backward, bool with_ds = true) {
   WsLayout L;
   L.wq = jfa::worklist_layout(backward ? jfa::kPassDQ : jfa::kPassQ, batch, heads, total_q);
   L.off_wq = 0;
@@ -61,7 +61,7 @@ WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_
     L.ds_kb = jfa::ds_key_blocks(max_kv_len);
     const uint64_t block = uint64_t(jfa::kDsBlock) * jfa::kDsBlock * (dtype == JFA_DTYPE_FP32 ? 4 : 2);
     const uint64_t ds_bytes = uint64_t(heads) * uint64_t(L.ds_rows) * uint64_t(L.ds_kb) * block;
-    if (ds_bytes <= kDsMaxBytes) {
+    if (with_ds && ds_bytes <= kDsMaxBytes) {
       L.ds = true;
       L.off_ds = off;
       off += align256(static_cast<size_t>(ds_bytes));
@@ -150,7 +150,8 @@ size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_
                           int32_t max_kv_len, int32_t dtype, int32_t for_backward) {
   if (check_sizes(batch, heads, head_dim, total_q, total_kv, 0, max_kv_len) != JFA_OK) return 0;
   if (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_FP32) return 0;
-  return ws_layout(batch, heads, total_q, total_kv, max_kv_len, dtype, for_backward != 0).bytes;
+  if (for_backward < 0 || for_backward > 2) return 0;
+  return ws_layout(batch, heads, total_q, total_kv, max_kv_len, dtype, for_backward != 0, for_backward != 2).bytes;
 }
 
 bool valid_pass(int32_t pass) {
@@ -279,7 +280,10 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   if (nbq > jfa::kMaxBuckets || nbk > jfa::kMaxBuckets)
     return fail(JFA_ERR_UNSUPPORTED, "maximum length exceeds the scheduler's range");
   if (batch == 0 || (total_q == 0 && total_kv == 0)) return JFA_OK;   // nothing to write
-  const WsLayout L = ws_layout(batch, heads, total_q, total_kv, max_kv_len, dtype, true);
+  // a workspace without room for the dS store (the store is its last part)
+  // runs the dQ pass that recomputes dS
+  WsLayout L = ws_layout(batch, heads, total_q, total_kv, max_kv_len, dtype, true);
+  if (workspace && workspace_bytes < L.bytes) L = ws_layout(batch, heads, total_q, total_kv, max_kv_len, dtype, true, false);
   if (!workspace || workspace_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
 
   char* ws = static_cast<char*>(workspace);

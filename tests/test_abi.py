@@ -108,9 +108,13 @@ def test_workspace_sizes():
     assert bwd32 - bwd >= ds
     # the forward does not depend on the key length or the element type
     assert jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 5, 1, 0) == fwd
+    # for_backward = 2: the same without the dS store
+    assert jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 1024, 0, 2) == bwd - ds
+    assert jfa.jfa_workspace_size(256, 4, 128, 97000, 97000, 1024, 0, 3) == 0
     # a dS store beyond 16 GiB is left out (the dQ pass then recomputes dS)
     big = jfa.jfa_workspace_size(64, 64, 128, 260000, 260000, 65000, 0, 1)
     assert 0 < big < (16 << 30)
+    assert big == jfa.jfa_workspace_size(64, 64, 128, 260000, 260000, 65000, 0, 2)
     assert jfa.jfa_workspace_size(2, 2, 48, 10, 10, 10, 0, 0) == 0
     assert jfa.jfa_workspace_size(2, 2, 32, 10, 10, 10, 5, 1) == 0   # bad dtype
 

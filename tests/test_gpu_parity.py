@@ -94,6 +94,29 @@ def test_backward_reduced_recompute(name, batch, monkeypatch):
     check_backward(grads, oracle_bwd(b))
 
 
+def test_backward_small_workspace_recomputes():
+    """A workspace without the dS store (for_backward = 2) is accepted and
+    gives the recomputing dQ pass: results within the gates, and dK, dV
+    bitwise equal to the full workspace's (the dK/dV pass is the same)."""
+    from jagged_attention_ads_amd import jfa
+    b = make_batch("selfattn_causal", _seed("selfattn_causal"), batch=12)
+    d = Dev(b)
+    out, lse = d.forward()
+    T_q, H, D = d.q.shape
+    B = len(b.q_lengths)
+    full = jfa.workspace(B, H, D, T_q, d.k.shape[0], d.mk, d.q.dtype, 1, d.q.device)
+    small = jfa.workspace(B, H, D, T_q, d.k.shape[0], d.mk, d.q.dtype, 2, d.q.device)
+    assert small.numel() < full.numel()
+    g_full = jfa.backward(d.q, d.k, d.v, out, d.do, lse, d.qo, d.ko, d.mq, d.mk, d.scale, d.act, d.causal, ws=full)
+    g_small = jfa.backward(d.q, d.k, d.v, out, d.do, lse, d.qo, d.ko, d.mq, d.mk, d.scale, d.act, d.causal, ws=small)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(b)
+    check_backward(g_full, ref)
+    check_backward(g_small, ref)
+    for x, y in zip(g_full[1:], g_small[1:]):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 @pytest.mark.parametrize("name", sorted(EDGE))
 def test_edge_cases(name, dq_path):
     b = _edge_batch(name)
