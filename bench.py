@@ -38,10 +38,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_digest():
-    """Digest of the kernel sources, to tell whether stored counters still apply."""
+    """Digest of the device sources (kernels and the headers they include;
+    not the host-side C ABI layer), to tell whether stored counters still
+    apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "jagged_attention_ads_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".hpp", ".h")):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
