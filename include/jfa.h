@@ -59,8 +59,10 @@
  *   JFA_ERR_WORKSPACE_TOO_SMALL  workspace_bytes < jfa_workspace_size(...);
  *   JFA_ERR_HIP  a HIP launch failed; jfa_last_error() has HIP's message.
  * batch == 0 (or no rows at all) is a successful no-op.  The offsets live in
- * device memory and are NOT validated: offsets that break the rules above,
- * or lengths above max_q_len / max_kv_len, are undefined behaviour.
+ * device memory and are not validated by default: offsets that break the
+ * rules above, or lengths above max_q_len / max_kv_len, are undefined
+ * behaviour.  With the environment variable JFA_CHECK_OFFSETS=1 they are
+ * checked on the device instead (see jfa_check_device_error).
  */
 #ifndef JFA_H_
 #define JFA_H_
@@ -171,6 +173,19 @@ int jfa_tile_shape(int32_t pass, int32_t* tile_rows, int32_t* block_rows);
 int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
                        int32_t heads, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
                        int32_t causal, void* out, size_t out_bytes, hipStream_t stream);
+
+/* Device check of the offsets (debug; the jagged-input item's offsets
+ * contract).  With JFA_CHECK_OFFSETS=1 in the environment, the work-list
+ * builder of jfa_forward and jfa_backward first checks on the device that
+ * q_offsets[0] = kv_offsets[0] = 0, that neither array decreases, that
+ * q_offsets[batch] = total_q and kv_offsets[batch] = total_kv, and that no
+ * length exceeds max_q_len / max_kv_len.  If a rule fails, no attention
+ * kernel does any work and no output, lse or gradient is written.
+ * jfa_check_device_error synchronises `stream` and reports the check of the
+ * last call that built a work list in `workspace`: JFA_OK (also when the
+ * check was off), or JFA_ERR_INVALID_ARGUMENT with the failed rules in
+ * jfa_last_error(); JFA_ERR_HIP if the word cannot be read. */
+int jfa_check_device_error(const void* workspace, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* jfa_status_string(int status);

@@ -38,18 +38,20 @@ struct WsLayout {
   bool ds = false;   // the workspace holds the dS blocks
 };
 
-// Forward: the query-tile list.  Backward: the dQ-tile list (in the same
-// slot), the key-tile list, the per-row statistics and, when they fit the
-// limit, the dS blocks.
+// Both: the offsets-check word at byte 0 (256 bytes reserved).  Forward:
+// the query-tile list.  Backward: the dQ-tile list (in the same slot), the
+// key-tile list, the per-row statistics and, when they fit the limit, the
+// dS blocks.
+constexpr size_t kStatusBytes = 256;
 WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv, int32_t max_kv_len,
                    int32_t dtype, bool backward, bool with_ds = true) {
   WsLayout L;
   L.wq = jfa::worklist_layout(backward ? jfa::kPassDQ : jfa::kPassQ, batch, heads, total_q);
-  L.off_wq = 0;
-  size_t off = L.wq.bytes;
+  L.off_wq = kStatusBytes;
+  size_t off = L.off_wq + L.wq.bytes;
   if (backward) {   // the slot holds either query-tile list
     L.wq_fwd = jfa::worklist_layout(jfa::kPassQ, batch, heads, total_q);
-    off = std::max(off, L.wq_fwd.bytes);
+    off = std::max(off, L.off_wq + L.wq_fwd.bytes);
   }
   if (backward) {
     L.wkv = jfa::worklist_layout(jfa::kPassKV, batch, heads, total_kv);
@@ -69,6 +71,18 @@ WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_
   }
   L.bytes = off;
   return L;
+}
+
+// JFA_CHECK_OFFSETS=1: the work-list builder validates the offsets on the
+// device first (see jfa_check_device_error).
+bool check_offsets_enabled() {
+  const char* e = std::getenv("JFA_CHECK_OFFSETS");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+jfa::OffsetCheck offset_check(void* ws, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len) {
+  return jfa::OffsetCheck{static_cast<int*>(ws), check_offsets_enabled() ? 1 : 0, total_q, total_kv, max_q_len,
+                          max_kv_len};
 }
 
 // JFA_BWD_DS=0 makes the backward recompute dS in the dQ pass even when the
@@ -198,7 +212,8 @@ int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv
   if (batch == 0) return JFA_OK;
   if (!out) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL output pointer");
   if (out_bytes < lay.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "worklist buffer too small");
-  hipError_t e = jfa::launch_sched(pass, q_offsets, kv_offsets, batch, heads, causal, nb, out, lay, stream);
+  const jfa::OffsetCheck none{nullptr, 0, total_q, total_kv, max_q_len, max_kv_len};
+  hipError_t e = jfa::launch_sched(pass, q_offsets, kv_offsets, batch, heads, causal, nb, out, lay, none, stream);
   if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
   return JFA_OK;
 }
@@ -224,7 +239,8 @@ int jfa_forward_profiled(const void* q, const void* k, const void* v, const int3
   char* ws = static_cast<char*>(workspace);
   hipError_t e;
   if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
-  e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nb, ws + L.off_wq, L.wq, stream);
+  e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nb, ws + L.off_wq, L.wq,
+                        offset_check(ws, total_q, total_kv, max_q_len, max_kv_len), stream);
   if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
   if ((e = record(events, 1, stream)) != hipSuccess) return hip_fail(e, "event record");
   jfa::FwdArgs a{};
@@ -328,13 +344,14 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   const jfa::StatsArgs sa{out, dout, lse, a.lse2, a.delta, heads, total_q};
   if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
   const bool pair = total_q > 0 && total_kv > 0;
+  const jfa::OffsetCheck chk = offset_check(ws, total_q, total_kv, max_q_len, max_kv_len);
   if (pair) {
     e = jfa::launch_sched_pair(qpass, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, lay_q, nbk,
-                               ws + L.off_wkv, L.wkv, stats ? &sa : nullptr, dtype, head_dim, stream);
+                               ws + L.off_wkv, L.wkv, stats ? &sa : nullptr, dtype, head_dim, chk, stream);
   } else if (total_q > 0) {
-    e = jfa::launch_sched(qpass, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, lay_q, stream);
+    e = jfa::launch_sched(qpass, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, lay_q, chk, stream);
   } else {
-    e = jfa::launch_sched(jfa::kPassKV, q_offsets, kv_offsets, batch, heads, causal, nbk, ws + L.off_wkv, L.wkv,
+    e = jfa::launch_sched(jfa::kPassKV, q_offsets, kv_offsets, batch, heads, causal, nbk, ws + L.off_wkv, L.wkv, chk,
                           stream);
   }
   if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
@@ -356,6 +373,21 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   }
   if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;
+}
+
+int jfa_check_device_error(const void* workspace, hipStream_t stream) {
+  if (!workspace) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL workspace");
+  int word = 0;
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "reading the offsets-check word");
+  if (word == 0) return JFA_OK;
+  std::string msg = "offsets rejected on the device:";
+  if (word & jfa::kOffsetsBadFirst) msg += " first offset not 0;";
+  if (word & jfa::kOffsetsBadOrder) msg += " offsets decrease;";
+  if (word & jfa::kOffsetsBadTotal) msg += " last offset differs from the total;";
+  if (word & jfa::kOffsetsBadLength) msg += " a length exceeds the maximum;";
+  return fail(JFA_ERR_INVALID_ARGUMENT, msg);
 }
 
 int jfa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,

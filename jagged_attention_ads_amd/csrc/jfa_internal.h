@@ -48,9 +48,26 @@ struct WorklistLayout {
 };
 WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t total_rows);
 
+// Optional device check of the offsets before a list is built: with `check`
+// set, the builder validates them first; if a rule fails it writes the
+// failed rules (kOffsetsBad* bits) to *status and an empty list whose records
+// make every attention workgroup exit.  *status is always written when not
+// null (0: valid, or not checked).
+enum {
+  kOffsetsBadFirst = 1,    // q_offsets[0] or kv_offsets[0] is not 0
+  kOffsetsBadOrder = 2,    // an offset array decreases
+  kOffsetsBadTotal = 4,    // q_offsets[batch] != total_q or kv_offsets[batch] != total_kv
+  kOffsetsBadLength = 8,   // a length above max_q_len or max_kv_len
+};
+struct OffsetCheck {
+  int* status;
+  int32_t check;
+  int32_t total_q, total_kv, max_q_len, max_kv_len;
+};
+
 hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                         int32_t causal, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
-                        hipStream_t stream);
+                        const OffsetCheck& chk, hipStream_t stream);
 // Inputs and outputs of the softmax backward's row statistics.
 struct StatsArgs {
   const void* out;
@@ -68,7 +85,7 @@ struct StatsArgs {
 hipError_t launch_sched_pair(int qpass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                              int32_t causal, int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv,
                              void* wl_kv, const WorklistLayout& lay_kv, const StatsArgs* stats, int dtype,
-                             int head_dim, hipStream_t stream);
+                             int head_dim, const OffsetCheck& chk, hipStream_t stream);
 
 struct FwdArgs {
   const void* q;

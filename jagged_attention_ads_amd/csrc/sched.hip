@@ -122,6 +122,7 @@ struct SchedJob {
   int2* items;
   int* tile_start;
   ItemMeta* meta;
+  OffsetCheck chk;
 };
 
 // Cost-bucket arrays in LDS, shared by both bodies.
@@ -419,9 +420,40 @@ __device__ void sched_body_global(const int* __restrict__ qo, const int* __restr
   }
 }
 
+// The offsets' rules (kOffsetsBad* bits that fail), over the whole
+// workgroup.  Reads q_offsets[0 .. B] and kv_offsets[0 .. B] only.
+__device__ int offsets_violations(const int* __restrict__ qo, const int* __restrict__ ko, int B,
+                                  const OffsetCheck& c) {
+  int bits = 0;
+  for (int b = threadIdx.x; b <= B; b += kSchedThreads) {
+    const int q = qo[b], k = ko[b];
+    if (b == 0 && (q != 0 || k != 0)) bits |= kOffsetsBadFirst;
+    if (b == B && (q != c.total_q || k != c.total_kv)) bits |= kOffsetsBadTotal;
+    if (b < B) {
+      const int64_t lq = (int64_t)qo[b + 1] - q, lk = (int64_t)ko[b + 1] - k;
+      if (lq < 0 || lk < 0) bits |= kOffsetsBadOrder;
+      if (lq > c.max_q_len || lk > c.max_kv_len) bits |= kOffsetsBadLength;
+    }
+  }
+  int all = 0;
+  for (int bit = 1; bit <= kOffsetsBadLength; bit <<= 1)
+    if (__syncthreads_or(bits & bit)) all |= bit;
+  return all;
+}
+
 template <int PASS>
 __device__ void sched_body(const int* __restrict__ qo, const int* __restrict__ ko, int B, int H, int causal,
                            const SchedJob& job, char* smem) {
+  const int bad = job.chk.check ? offsets_violations(qo, ko, B, job.chk) : 0;
+  if (job.chk.status && threadIdx.x == 0) *job.chk.status = bad;
+  if (bad) {
+    // nothing is enumerated from such offsets: an empty list whose records
+    // send every attention workgroup home
+    if (threadIdx.x == 0) *job.count = 0;
+    for (int64_t p = threadIdx.x; p < job.capacity; p += kSchedThreads) job.meta[p] = ItemMeta{0, -1, 0, 0, 0, 0, 0, 0};
+    for (int b = threadIdx.x; b <= B; b += kSchedThreads) job.tile_start[b] = 0;
+    return;
+  }
   if (job.in_lds) sched_body_lds<PASS>(qo, ko, B, H, causal, job, smem);
   else sched_body_global<PASS>(qo, ko, B, H, causal, job, smem);
 }
@@ -490,9 +522,10 @@ static bool sched_lds_allowed() {
 
 // The job of one pass and the dynamic LDS it needs.
 static SchedJob make_job(int32_t batch, int32_t heads, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
-                         size_t& lds) {
+                         const OffsetCheck& chk, size_t& lds) {
   char* base = static_cast<char*>(wl_base);
   SchedJob j;
+  j.chk = chk;
   j.nbuckets = nbuckets;
   j.capacity = lay.capacity;
   // heads >= 1 items per tile: capacity / heads bounds the tile count
@@ -511,9 +544,9 @@ static SchedJob make_job(int32_t batch, int32_t heads, int32_t nbuckets, void* w
 
 hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                         int32_t causal, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
-                        hipStream_t stream) {
+                        const OffsetCheck& chk, hipStream_t stream) {
   size_t lds;
-  const SchedJob j = make_job(batch, heads, nbuckets, wl_base, lay, lds);
+  const SchedJob j = make_job(batch, heads, nbuckets, wl_base, lay, chk, lds);
   if (pass == kPassQ)
     hipLaunchKernelGGL(sched_kernel<kPassQ>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
                        causal, j);
@@ -553,10 +586,10 @@ static hipError_t pair_launch_d(int head_dim, const int32_t* qo, const int32_t* 
 hipError_t launch_sched_pair(int qpass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                              int32_t causal, int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv,
                              void* wl_kv, const WorklistLayout& lay_kv, const StatsArgs* stats, int dtype,
-                             int head_dim, hipStream_t stream) {
+                             int head_dim, const OffsetCheck& chk, hipStream_t stream) {
   size_t lds_q, lds_kv;
-  const SchedJob jq = make_job(batch, heads, nb_dq, wl_dq, lay_dq, lds_q);
-  const SchedJob jkv = make_job(batch, heads, nb_kv, wl_kv, lay_kv, lds_kv);
+  const SchedJob jq = make_job(batch, heads, nb_dq, wl_dq, lay_dq, chk, lds_q);
+  const SchedJob jkv = make_job(batch, heads, nb_kv, wl_kv, lay_kv, chk, lds_kv);
   const size_t lds = lds_q > lds_kv ? lds_q : lds_kv;
   if (qpass == kPassQ)
     return dtype == 0 ? pair_launch_d<kPassQ, __bf16>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream)

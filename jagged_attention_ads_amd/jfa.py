@@ -29,7 +29,8 @@ PASS_KEY_TILES = 1
 PASS_DQ_TILES = 2
 
 EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_profiled", "jfa_backward_profiled",
-            "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_status_string", "jfa_last_error")
+            "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_check_device_error",
+            "jfa_status_string", "jfa_last_error")
 
 
 class JfaError(RuntimeError):
@@ -67,6 +68,8 @@ def lib():
         L.jfa_tile_shape.argtypes = [_i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
         L.jfa_build_worklist.restype = ctypes.c_int
         L.jfa_build_worklist.argtypes = [_i32, _vp, _vp] + [_i32] * 7 + [_vp, _sz, _vp]
+        L.jfa_check_device_error.restype = ctypes.c_int
+        L.jfa_check_device_error.argtypes = [_vp, _vp]
         L.jfa_status_string.restype = ctypes.c_char_p
         L.jfa_status_string.argtypes = [ctypes.c_int]
         L.jfa_last_error.restype = ctypes.c_char_p
@@ -165,6 +168,14 @@ def jfa_build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, m
     _check(lib().jfa_build_worklist(pass_, _ptr(q_offsets), _ptr(kv_offsets), q_offsets.numel() - 1, heads,
                                     total_q, total_kv, int(max_q_len), int(max_kv_len), int(bool(causal)),
                                     _ptr(out), out.numel(), _stream()))
+
+
+def jfa_check_device_error(workspace):
+    """Synchronises the current stream; returns (status, message) of the
+    offsets check of the last call that built a work list in `workspace`
+    (JFA_CHECK_OFFSETS=1)."""
+    st = lib().jfa_check_device_error(_ptr(workspace), _stream())
+    return st, (lib().jfa_last_error().decode() if st != JFA_OK else "")
 
 
 # ---------------------------------------------------------------- allocating wrappers

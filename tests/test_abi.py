@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     L = jfa.lib()
     for n in names:
         assert hasattr(L, n), n

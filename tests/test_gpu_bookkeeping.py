@@ -219,3 +219,51 @@ def test_noop_and_zero_rows():
     dq, dk, dv = jfa.backward(q, k, k, q, q, torch.empty((H, 0), device=dev()), qo, ko, 0, 5)
     torch.cuda.synchronize()
     assert (dk == 0).all() and (dv == 0).all()
+
+
+# malformed offsets, each breaking one rule of the offsets contract, for
+# q lengths [5, 0, 4] (total 9, longest 5); the call is made with the valid
+# totals and maxima (the last case lowers max_q_len / max_kv_len instead)
+_BAD_OFFSETS = {
+    "first_not_zero": ([1, 5, 5, 9], 5, "first offset not 0"),
+    "decreasing": ([0, 5, 4, 9], 5, "offsets decrease"),
+    "last_not_total": ([0, 5, 5, 8], 5, "last offset differs from the total"),
+    "too_long": ([0, 5, 5, 9], 4, "a length exceeds the maximum"),
+}
+
+
+@pytest.mark.parametrize("case", ["valid"] + sorted(_BAD_OFFSETS))
+def test_device_offsets_check(case, monkeypatch):
+    """JFA_CHECK_OFFSETS=1: malformed offsets are rejected on the device, no
+    output is written and jfa_check_device_error names the rule; valid ones
+    run as usual and report JFA_OK."""
+    monkeypatch.setenv("JFA_CHECK_OFFSETS", "1")
+    H, D, T, B = 2, 64, 9, 3
+    qo_list, mx, words = ([0, 5, 5, 9], 5, None) if case == "valid" else _BAD_OFFSETS[case]
+    g = torch.Generator().manual_seed(7)
+    q, k, v, do = (torch.randn((T, H, D), generator=g).to(torch.bfloat16).to(dev()) for _ in range(4))
+    qo = torch.tensor(qo_list, dtype=torch.int32, device=dev())
+    nan = float("nan")
+    out = torch.full((T, H, D), nan, dtype=torch.bfloat16, device=dev())
+    lse = torch.full((H, T), nan, dtype=torch.float32, device=dev())
+    dq, dk, dv = (torch.full((T, H, D), nan, dtype=torch.bfloat16, device=dev()) for _ in range(3))
+    ws_f = jfa.workspace(B, H, D, T, T, mx, q.dtype, 0, dev())
+    ws_b = jfa.workspace(B, H, D, T, T, mx, q.dtype, 1, dev())
+    jfa.jfa_forward(q, k, v, qo, qo, mx, mx, 0.125, "softmax", True, out, lse, ws_f)
+    st_f, msg_f = jfa.jfa_check_device_error(ws_f)
+    if case == "valid":
+        jfa.jfa_backward(q, k, v, out, do, lse, qo, qo, mx, mx, 0.125, "softmax", True, dq, dk, dv, ws_b)
+        st_b, _ = jfa.jfa_check_device_error(ws_b)
+        assert st_f == 0 and st_b == 0
+        for t in (out, lse, dq, dk, dv):
+            assert torch.isfinite(t).all()
+        return
+    # the backward gets the forward's untouched outputs (NaN): nothing runs on them
+    jfa.jfa_backward(q, k, v, out, do, lse, qo, qo, mx, mx, 0.125, "softmax", True, dq, dk, dv, ws_b)
+    st_b, msg_b = jfa.jfa_check_device_error(ws_b)
+    assert st_f == 1 and st_b == 1   # JFA_ERR_INVALID_ARGUMENT
+    assert words in msg_f and words in msg_b
+    for t in (out, lse, dq, dk, dv):
+        assert torch.isnan(t).all(), "an output was written from rejected offsets"
+    # offsets untouched
+    assert qo.cpu().tolist() == qo_list
