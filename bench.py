@@ -143,14 +143,15 @@ def kernel_accounting(wl, T_q, T_k, pairs_total, n_ds_blocks, ds_path):
 
 
 def stored_traffic(kernel, digest, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the stored counter
+    runs (profiles/traffic.json), or None when none were taken with the
+    current device sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    if data.get("workload") != workload:
-        return None
-    rec = data.get(kernel)
+    rec = data.get("workloads", {}).get(workload, {}).get(kernel)
     if not rec or rec.get("source_digest") != digest:
         return None
     return rec.get("bytes_per_launch")
