@@ -267,3 +267,25 @@ def test_device_offsets_check(case, monkeypatch):
         assert torch.isnan(t).all(), "an output was written from rejected offsets"
     # offsets untouched
     assert qo.cpu().tolist() == qo_list
+
+
+@pytest.mark.parametrize("recompute", [False, True])
+def test_no_keys_at_all(recompute, monkeypatch):
+    """total_kv = 0 with queries present: only the query-tile list is built and
+    the row statistics run as a kernel of their own; out = 0, lse = -inf and
+    dq = 0 for every row (both dQ passes)."""
+    if recompute:
+        monkeypatch.setenv("JFA_BWD_DS", "0")
+    H, D = 2, 128
+    q = torch.randn((7, H, D), device=dev()).to(torch.bfloat16)
+    do = torch.randn((7, H, D), device=dev()).to(torch.bfloat16)
+    k = torch.zeros((0, H, D), dtype=torch.bfloat16, device=dev())
+    qo = torch.tensor([0, 3, 7], dtype=torch.int32, device=dev())
+    ko = torch.zeros(3, dtype=torch.int32, device=dev())
+    for causal in (False, True):
+        out, lse = jfa.forward(q, k, k, qo, ko, 4, 0, causal=causal)
+        dq, dk, dv = jfa.backward(q, k, k, out, do, lse, qo, ko, 4, 0, causal=causal)
+        torch.cuda.synchronize()
+        assert (out == 0).all() and (dq == 0).all()
+        assert torch.isneginf(lse).all()
+        assert dk.shape == (0, H, D) and dv.shape == (0, H, D)
