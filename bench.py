@@ -218,6 +218,9 @@ def main():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", action="store_true",
+                    help="before each step, overwrite a 512 MiB buffer (evicting the last-level cache and L2), "
+                         "and time each step by its own events, flush excluded")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain elementwise copy of known size (256 MiB read + 256 MiB written per "
                          "dispatch, 3 dispatches), to scale the HBM byte counters")
@@ -296,9 +299,12 @@ def main():
     ef = [ev.create(3) for _ in range(K)]
     eb = [ev.create(5) for _ in range(K)] if run_bwd else []
     edge = ev.create(2)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
     torch.cuda.synchronize()
     ev.lib.hipEventRecord(edge[0], stream)
     for i in range(K):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xff)
         fwd(ef[i])
         if run_bwd:
             bwd(eb[i])
@@ -306,6 +312,8 @@ def main():
     torch.cuda.synchronize()
     total_ms = ev.ms(edge[0], edge[1])
     ms_step = total_ms / K
+    if flush_buf is not None:   # each step from its first to its last event
+        ms_step = float(np.mean([ev.ms(ef[i][0], (eb[i][4] if run_bwd else ef[i][2])) for i in range(K)]))
 
     def avg(lst, a, b):
         return float(np.mean([ev.ms(e[a], e[b]) for e in lst])) if lst else 0.0
@@ -355,6 +363,7 @@ def main():
         "fwd_tflops": fwd_tf, "fwd_pct_peak": 100.0 * fwd_tf / PEAK_BF16_TFLOPS,
         "bwd_tflops": bwd_tf, "bwd_pct_peak": (100.0 * bwd_tf / PEAK_BF16_TFLOPS) if bwd_tf else None,
         "kernel_us": {k_: v_ * 1e3 for k_, v_ in kern_ms.items()},
+        "cache": "flushed before each step (512 MiB written)" if args.flush else "warm (steps back to back)",
         "kernel_source_digest": digest,
         "roofline": roof,
     }
