@@ -8,16 +8,18 @@
 // stored once.  Launch order:
 //   row statistics (softmax only) -- per (row, head): delta_i =
 //     sum_c dO_ic O_ic, the row sum of P o dP that the softmax Jacobian
-//     needs, and lse_i * log2(e);
+//     needs, and lse_i * log2(e) (bwd_stats.hpp; normally formed in the
+//     spare workgroups of the work-list launch);
 //   dK/dV pass -- one work item per (sequence, head, 64-key tile); each
 //     pair of waves owns 32 keys and walks the query rows that see them in
 //     32-row sub-blocks.  P and dS are recomputed from lse (softmax) or from
 //     the scores (SiLU).  It also stores every dS block it forms (bf16 or
 //     fp32, 32 queries x 32 keys), so that
-//   dQ pass -- one work item per (sequence, head, 64-query tile) -- is the
+//   dQ pass -- one work item per (sequence, head, 128-query tile) -- is the
 //     single product dQ = scale * dS K over the stored blocks.  When the dS
-//     blocks would not fit the workspace limit, the dQ pass instead
-//     recomputes S, P, dP and dS itself (three products instead of one).
+//     blocks are not in the workspace, the dQ pass instead walks 64-query
+//     tiles and recomputes S, P, dP and dS itself (three products instead
+//     of one).
 //
 // Every pass streams the operand it walks (Q and dO, K and V, or K and dS)
 // from HBM straight into a ring of swizzled LDS stages, two or more stages
