@@ -62,6 +62,10 @@ EDGE = {
     "d128_fp32_silu": ("tiny_fp32", [20, 66], [33, 66], dict(head_dim=128, activation="silu")),
     "d32_bf16_cross": ("cross_asym", [1, 64, 17], [4096, 5, 300], dict(head_dim=32, heads=3)),
     "many_heads": ("selfattn_causal", [50, 130], [50, 130], dict(heads=16, head_dim=64)),
+    # the largest key length the scheduler accepts (1023 cost classes of 64 keys)
+    "max_kv_len": ("cross_asym", [64, 3], [65472, 1000], dict(heads=2)),
+    # the largest head count (the head index is packed into 8 bits of an item)
+    "max_heads": ("selfattn_causal", [3, 40], [3, 40], dict(heads=256, head_dim=32)),
 }
 
 
