@@ -15,6 +15,11 @@ Readings of points the pages leave open (each is stated where it is used):
   * a softmax row with no visible key has out = 0 and lse = -inf.
   * the GDPA activation is silu(s * q.k) / Lk, Lk being the sequence's own key
     count (also under causal masking); invisible entries weigh 0.
+  * BlockAttention's fixed blocks ([GEM-MFU, Detailed notes: BlockAttention])
+    are read as: self attention in which every run of `block` consecutive
+    tokens of a sequence, counted from its first token, attends only within
+    itself -- each block is a sequence of its own (so the GDPA normaliser is
+    the block's key count, and causal masking applies inside the block).
 """
 
 import numpy as np
@@ -43,6 +48,25 @@ def _sigmoid(x):
     e = np.exp(x[~pos])
     out[~pos] = e / (1.0 + e)
     return out
+
+
+def _segments(qo, ko, block):
+    """(q start, q end, k start, k end) of every attention unit: the sequences,
+    or with block > 0 the consecutive `block`-token runs of each sequence
+    ([GEM-MFU, Detailed notes: BlockAttention]: fixed blocks of 64 tokens,
+    which turn the cost from quadratic to linear in the length)."""
+    segs = []
+    for b in range(len(qo) - 1):
+        qs, qe, ks, ke = qo[b], qo[b + 1], ko[b], ko[b + 1]
+        if block <= 0:
+            segs.append((qs, qe, ks, ke))
+            continue
+        if qe - qs != ke - ks:
+            raise ValueError("block attention is self attention: equal query and key lengths")
+        for c in range(0, qe - qs, block):
+            n = min(block, qe - qs - c)
+            segs.append((qs + c, qs + c + n, ks + c, ks + c + n))
+    return segs
 
 
 def _check(q, k, v, q_offsets, kv_offsets, activation):
@@ -83,13 +107,14 @@ def _probs(S, vis, activation, lk):
     return A, None
 
 
-def attention_fwd(q, k, v, q_offsets, kv_offsets, scale, activation="softmax", causal=False):
+def attention_fwd(q, k, v, q_offsets, kv_offsets, scale, activation="softmax", causal=False, block=0):
     """Jagged attention forward in fp64.
 
     Returns (out [T_q, H, d], lse [H, T_q] or None for silu).
     [GEM-MFU, Detailed notes: JFA] for softmax, [GEM-MFU, Detailed notes: GDPA]
     for silu; every sequence is independent of the others
-    ([GEM-MFU, Detailed notes: jagged input]).
+    ([GEM-MFU, Detailed notes: jagged input]).  block > 0: BlockAttention,
+    attention within each `block`-token run of a sequence (see _segments).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -98,8 +123,7 @@ def attention_fwd(q, k, v, q_offsets, kv_offsets, scale, activation="softmax", c
     T_q, H, d = q.shape
     out = np.zeros((T_q, H, v.shape[2]))
     lse = np.full((H, T_q), -np.inf) if activation == "softmax" else None
-    for b in range(len(qo) - 1):
-        qs, qe, ks, ke = qo[b], qo[b + 1], ko[b], ko[b + 1]
+    for qs, qe, ks, ke in _segments(qo, ko, block):
         lq, lk = qe - qs, ke - ks
         if lq == 0:
             continue
@@ -114,7 +138,7 @@ def attention_fwd(q, k, v, q_offsets, kv_offsets, scale, activation="softmax", c
     return out, lse
 
 
-def attention_bwd(q, k, v, dout, q_offsets, kv_offsets, scale, activation="softmax", causal=False):
+def attention_bwd(q, k, v, dout, q_offsets, kv_offsets, scale, activation="softmax", causal=False, block=0):
     """Gradients (dq, dk, dv) of sum(out * dout) for the forward above, fp64.
 
     The chain rule written out per (sequence, head) block:
@@ -123,7 +147,8 @@ def attention_bwd(q, k, v, dout, q_offsets, kv_offsets, scale, activation="softm
                entries, silu'(x) = sig(x) (1 + x (1 - sig(x))),
       both:    dQ = scale dS K, dK = scale dS^T Q.
     The backward's parallel split without atomics ([GEM-MFU, Detailed notes:
-    JFA]) changes only how these sums are formed, not their values.
+    JFA]) changes only how these sums are formed, not their values.  block:
+    as in attention_fwd.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -136,8 +161,7 @@ def attention_bwd(q, k, v, dout, q_offsets, kv_offsets, scale, activation="softm
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for b in range(len(qo) - 1):
-        qs, qe, ks, ke = qo[b], qo[b + 1], ko[b], ko[b + 1]
+    for qs, qe, ks, ke in _segments(qo, ko, block):
         lq, lk = qe - qs, ke - ks
         if lq == 0 or lk == 0:
             continue

@@ -299,3 +299,105 @@ def test_gradients_by_central_differences(activation, causal):
             num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
         err = np.linalg.norm(num - g) / max(np.linalg.norm(g), 1e-30)
         assert err <= 1e-6, (which, err)
+
+
+# ---------------------------------------------------------------- BlockAttention (fixed blocks)
+
+def brute_force_block_fwd(q, k, v, qo, scale, activation, causal, block):
+    """Independent scalar implementation of block-local self attention: query
+    i of a sequence sees key j iff both lie in the same run of `block` tokens
+    counted from the sequence's first token (and j <= i when causal); the
+    SiLU normaliser is the number of keys in that run."""
+    H, d = q.shape[1], q.shape[2]
+    out = np.zeros(q.shape)
+    lse = np.full((H, q.shape[0]), -math.inf)
+    for b in range(len(qo) - 1):
+        L = qo[b + 1] - qo[b]
+        for h in range(H):
+            for i in range(L):
+                run = i // block
+                n_run = min(block, L - run * block)
+                scores, idx = [], []
+                for j in range(L):
+                    if j // block != run or (causal and j > i):
+                        continue
+                    s = sum(q[qo[b] + i, h, c] * k[qo[b] + j, h, c] for c in range(d))
+                    scores.append(scale * s)
+                    idx.append(j)
+                if activation == "softmax":
+                    mx = max(scores)
+                    ex = [math.exp(x - mx) for x in scores]
+                    tot = sum(ex)
+                    w = [e / tot for e in ex]
+                    lse[h, qo[b] + i] = mx + math.log(tot)
+                else:
+                    w = [x / (1.0 + math.exp(-x)) / n_run for x in scores]
+                for wj, j in zip(w, idx):
+                    for c in range(d):
+                        out[qo[b] + i, h, c] += wj * v[qo[b] + j, h, c]
+    return out, lse
+
+
+@pytest.mark.parametrize("activation", ["softmax", "silu"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block", [1, 2, 3, 4])
+def test_block_attention_matches_brute_force(block, causal, activation):
+    lens = [5, 0, 8, 3, 1]
+    q, k, v, _, qo, _ = _draw(lens, lens, 2, 3, seed=21 + block)
+    s = 0.7
+    out, lse = oracle.attention_fwd(q, k, v, qo, qo, s, activation, causal, block=block)
+    ref_out, ref_lse = brute_force_block_fwd(q, k, v, qo, s, activation, causal, block)
+    assert np.abs(out - ref_out).max() <= 1e-12
+    if activation == "softmax":
+        assert np.array_equal(np.isfinite(lse), np.isfinite(ref_lse))
+        fin = np.isfinite(ref_lse)
+        assert np.abs(lse[fin] - ref_lse[fin]).max() <= 1e-12
+
+
+def test_block_of_one_token_gives_its_own_value():
+    """Softmax over a single visible key: out_i = v_i and lse_i = s q_i.k_i."""
+    lens = [4, 2]
+    q, k, v, _, qo, _ = _draw(lens, lens, 2, 3, seed=33)
+    s = 0.9
+    out, lse = oracle.attention_fwd(q, k, v, qo, qo, s, "softmax", False, block=1)
+    assert np.abs(out - v).max() <= 1e-12
+    assert np.abs(lse - s * np.einsum("thc,thc->ht", q, k)).max() <= 1e-12
+
+
+@pytest.mark.parametrize("activation", ["softmax", "silu"])
+def test_block_wider_than_sequences_is_plain_attention(activation):
+    lens = [5, 7]
+    q, k, v, do, qo, _ = _draw(lens, lens, 2, 3, seed=34)
+    for causal in (False, True):
+        a = oracle.attention_fwd(q, k, v, qo, qo, 0.5, activation, causal, block=7)
+        b = oracle.attention_fwd(q, k, v, qo, qo, 0.5, activation, causal)
+        assert np.array_equal(a[0], b[0])
+
+
+@pytest.mark.parametrize("activation", ["softmax", "silu"])
+def test_block_gradients_by_central_differences(activation):
+    lens = [5, 3]
+    q, k, v, do, qo, _ = _draw(lens, lens, 2, 3, seed=35)
+    s, block = 0.8, 2
+    loss = lambda qq, kk, vv: float((oracle.attention_fwd(qq, kk, vv, qo, qo, s, activation, True, block=block)[0] * do).sum())  # noqa: E731
+    grads = oracle.attention_bwd(q, k, v, do, qo, qo, s, activation, True, block=block)
+    h = 1e-6
+    for which, g in zip(range(3), grads):
+        base = [q, k, v]
+        num = np.zeros_like(g)
+        it = np.nditer(base[which], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        err = np.linalg.norm(num - g) / max(np.linalg.norm(g), 1e-30)
+        assert err <= 1e-6, (which, err)
+
+
+def test_block_attention_rejects_cross_pairs():
+    q, k, v, _, qo, ko = _draw([3], [4], 1, 2, seed=36)
+    with pytest.raises(ValueError):
+        oracle.attention_fwd(q, k, v, qo, ko, 1.0, "softmax", False, block=2)
