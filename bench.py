@@ -90,6 +90,15 @@ class HipEvents:
             self.lib.hipEventDestroy(h)
 
 
+def block_runs(lengths, block):
+    """Lengths of the `block`-token runs of every sequence, in order
+    (BlockAttention: each run attends within itself)."""
+    out = []
+    for n in np.asarray(lengths, dtype=np.int64):
+        out += [block] * int(n // block) + ([int(n % block)] if n % block else [])
+    return np.asarray(out, dtype=np.int64)
+
+
 def visible_pairs(q_lengths, kv_lengths, causal):
     """Per sequence, the number of (query, key) pairs that are visible."""
     lq = np.asarray(q_lengths, dtype=np.int64)
@@ -172,16 +181,22 @@ def cpu_baseline(batch, budget_s):
     q, k, v = batch.f64("q"), batch.f64("k"), batch.f64("v")
     do = batch.f64("dout") if batch.dout is not None else None
     qo, ko = batch.q_offsets, batch.kv_offsets
-    pairs = visible_pairs(batch.q_lengths, batch.kv_lengths, wl.causal)
+    blk = wl.block
+    if blk:
+        pairs = np.array([visible_pairs(block_runs([n], blk), block_runs([n], blk), wl.causal).sum()
+                          for n in batch.q_lengths])
+    else:
+        pairs = visible_pairs(batch.q_lengths, batch.kv_lengths, wl.causal)
     done, flops, t0 = 0, 0.0, time.perf_counter()
     while done < len(pairs) and time.perf_counter() - t0 < budget_s:
         b = done
         sl_q, sl_k = slice(qo[b], qo[b + 1]), slice(ko[b], ko[b + 1])
         one_q = np.array([0, qo[b + 1] - qo[b]])
         one_k = np.array([0, ko[b + 1] - ko[b]])
-        oracle.attention_fwd(q[sl_q], k[sl_k], v[sl_k], one_q, one_k, s, wl.activation, wl.causal)
+        oracle.attention_fwd(q[sl_q], k[sl_k], v[sl_k], one_q, one_k, s, wl.activation, wl.causal, block=blk)
         if wl.backward and do is not None:
-            oracle.attention_bwd(q[sl_q], k[sl_k], v[sl_k], do[sl_q], one_q, one_k, s, wl.activation, wl.causal)
+            oracle.attention_bwd(q[sl_q], k[sl_k], v[sl_k], do[sl_q], one_q, one_k, s, wl.activation, wl.causal,
+                                 block=blk)
         flops += (14 if wl.backward else 4) * wl.head_dim * wl.heads * pairs[b]
         done += 1
     el = time.perf_counter() - t0
@@ -255,19 +270,36 @@ def main():
     lse = torch.empty((H, T_q), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     B = len(batch.q_lengths)
+    L = jfa.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    derive = None
+    q_lens, kv_lens = batch.q_lengths, batch.kv_lengths
+    if wl.block:
+        # BlockAttention: the runs of wl.block tokens as sequences, derived on
+        # the device from the sequences' offsets in every step
+        seq_off, n_seq = qo, B
+        n_runs = L.jfa_block_offsets_count(n_seq, T_q, wl.block)
+        runs = torch.empty(n_runs, dtype=torch.int32, device=dev)
+
+        def derive():
+            st = L.jfa_block_offsets(P(seq_off), n_seq, T_q, wl.block, P(runs), n_runs, stream)
+            if st != 0:
+                raise jfa.JfaError(st, L.jfa_last_error().decode())
+        qo = ko = runs
+        B = n_runs - 1
+        mq = mk = min(wl.block, mq)
+        q_lens = kv_lens = block_runs(batch.q_lengths, wl.block)
     ws_f = jfa.workspace(B, H, D, T_q, T_k, mk, q.dtype, False, dev)
     ws_b = jfa.workspace(B, H, D, T_q, T_k, mk, q.dtype, True, dev)
     # the dK/dV pass stores dS and the dQ pass reads it, unless switched off
     # or the store was left out of the workspace
     ds_path = (os.environ.get("JFA_BWD_DS") != "0"
                and ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, mk, q.dtype, 2))
-    L = jfa.lib()
-    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
     act = jfa.ACTIVATIONS[wl.activation]
     dt = jfa.DTYPES[q.dtype]
     soft = wl.activation == "softmax"
     lse_arg = lse if soft else None
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def evp(events):
         return ctypes.cast(events, ctypes.c_void_p) if events is not None else None
@@ -290,6 +322,8 @@ def main():
     ev = HipEvents()
     run_bwd = wl.backward
     for _ in range(args.warmup):
+        if derive:
+            derive()
         fwd(None)
         if run_bwd:
             bwd(None)
@@ -305,6 +339,8 @@ def main():
     for i in range(K):
         if flush_buf is not None:
             flush_buf.fill_(i & 0xff)
+        if derive:
+            derive()
         fwd(ef[i])
         if run_bwd:
             bwd(eb[i])
@@ -325,7 +361,7 @@ def main():
                         "bwd_dq": avg(eb, 3, 4)})
         bwd_ms = avg(eb, 0, 4)
 
-    pairs = int(visible_pairs(batch.q_lengths, batch.kv_lengths, wl.causal).sum())
+    pairs = int(visible_pairs(q_lens, kv_lens, wl.causal).sum())
     useful_fwd = 4.0 * D * H * pairs
     useful_bwd = 10.0 * D * H * pairs if run_bwd else 0.0
     value = (useful_fwd + useful_bwd) / (ms_step * 1e-3) / 1e12
@@ -333,7 +369,7 @@ def main():
     bwd_tf = useful_bwd / (bwd_ms * 1e-3) / 1e12 if run_bwd else None
 
     # roofline of the dominant kernel
-    n_blk = ds_blocks(batch.q_lengths, batch.kv_lengths, wl.causal) if run_bwd else 0
+    n_blk = ds_blocks(q_lens, kv_lens, wl.causal) if run_bwd else 0
     acct = kernel_accounting(wl, T_q, T_k, pairs, n_blk, ds_path)
     name = max((n for n in acct if n in kern_ms), key=lambda n: kern_ms[n])
     t_s = kern_ms[name] * 1e-3
@@ -356,7 +392,7 @@ def main():
         "dtype": wl.dtype, "data": "synthetic (seeded; lengths and values drawn per the workload recipe)",
         "config": {"workload": wl.description, "name": wl.name, "batch": B, "heads": H, "head_dim": D,
                    "causal": wl.causal, "activation": wl.activation, "seed": args.seed, "total_q_tokens": T_q,
-                   "total_kv_tokens": T_k, "visible_pairs_per_head": pairs,
+                   "total_kv_tokens": T_k, "visible_pairs_per_head": pairs, "block": wl.block,
                    "bwd_dq_from_stored_ds": bool(run_bwd and ds_path),
                    "useful_gflop_per_step": (useful_fwd + useful_bwd) / 1e9},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,

@@ -174,6 +174,25 @@ int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv
                        int32_t heads, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
                        int32_t causal, void* out, size_t out_bytes, hipStream_t stream);
 
+/* BlockAttention with fixed blocks (same page and section, BlockAttention
+ * item: fixed blocks of 64 tokens make attention's cost linear in the
+ * length).  Self attention restricted to each run of `block` consecutive
+ * tokens of a sequence, counted from its first token, is jagged attention
+ * over those runs taken as sequences (the SiLU normaliser is then the run's
+ * key count).  jfa_block_offsets writes, into `out` (device int32, at least
+ * jfa_block_offsets_count(batch, total, block) = total / block + batch + 1
+ * entries), the offsets of those runs for the sequences of `offsets` (device
+ * int32 [batch + 1], rows 0 .. total-1), in order, followed by empty
+ * sequences up to that count.  Passing `out` as both q_offsets and
+ * kv_offsets to jfa_forward / jfa_backward, with batch' = count - 1 and
+ * max lengths min(block, longest sequence), computes block attention on the
+ * unchanged q, k, v tensors.  Asynchronous on `stream`; writes only
+ * out[0 .. count-1].  Errors: NULL pointers, batch or total < 0, block < 1,
+ * out_len below the count: JFA_ERR_INVALID_ARGUMENT. */
+int64_t jfa_block_offsets_count(int32_t batch, int32_t total, int32_t block);
+int jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t total, int32_t block, int32_t* out,
+                      int64_t out_len, hipStream_t stream);
+
 /* Device check of the offsets (debug; the jagged-input item's offsets
  * contract).  With JFA_CHECK_OFFSETS=1 in the environment, the work-list
  * builder of jfa_forward and jfa_backward first checks on the device that

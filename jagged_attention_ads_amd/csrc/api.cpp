@@ -375,6 +375,24 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   return JFA_OK;
 }
 
+int64_t jfa_block_offsets_count(int32_t batch, int32_t total, int32_t block) {
+  if (batch < 0 || total < 0 || block < 1) return 0;
+  return (int64_t)total / block + batch + 1;
+}
+
+int jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t total, int32_t block, int32_t* out,
+                      int64_t out_len, hipStream_t stream) {
+  if (!offsets || !out) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL offsets pointer");
+  if (batch < 0 || total < 0) return fail(JFA_ERR_INVALID_ARGUMENT, "negative batch or total");
+  if (block < 1) return fail(JFA_ERR_INVALID_ARGUMENT, "block < 1");
+  const int64_t need = jfa_block_offsets_count(batch, total, block);
+  if (out_len < need) return fail(JFA_ERR_INVALID_ARGUMENT, "out has fewer than total / block + batch + 1 entries");
+  if (need > INT32_MAX) return fail(JFA_ERR_UNSUPPORTED, "too many blocks");
+  hipError_t e = jfa::launch_block_offsets(offsets, batch, total, block, out, (int32_t)need, stream);
+  if (e != hipSuccess) return hip_fail(e, "block offsets kernel launch");
+  return JFA_OK;
+}
+
 int jfa_check_device_error(const void* workspace, hipStream_t stream) {
   if (!workspace) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL workspace");
   int word = 0;

@@ -105,6 +105,11 @@ struct FwdArgs {
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
 
+// BlockAttention: the runs of `block` tokens of every sequence as offsets
+// (see blocks.hip).
+hipError_t launch_block_offsets(const int32_t* off, int32_t batch, int32_t total, int32_t block, int32_t* out,
+                                int32_t out_len, hipStream_t stream);
+
 struct BwdArgs {
   const void* q;
   const void* k;

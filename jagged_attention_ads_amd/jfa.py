@@ -30,7 +30,7 @@ PASS_DQ_TILES = 2
 
 EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_profiled", "jfa_backward_profiled",
             "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_check_device_error",
-            "jfa_status_string", "jfa_last_error")
+            "jfa_block_offsets_count", "jfa_block_offsets", "jfa_status_string", "jfa_last_error")
 
 
 class JfaError(RuntimeError):
@@ -68,6 +68,10 @@ def lib():
         L.jfa_tile_shape.argtypes = [_i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]
         L.jfa_build_worklist.restype = ctypes.c_int
         L.jfa_build_worklist.argtypes = [_i32, _vp, _vp] + [_i32] * 7 + [_vp, _sz, _vp]
+        L.jfa_block_offsets_count.restype = ctypes.c_int64
+        L.jfa_block_offsets_count.argtypes = [_i32, _i32, _i32]
+        L.jfa_block_offsets.restype = ctypes.c_int
+        L.jfa_block_offsets.argtypes = [_vp, _i32, _i32, _i32, _vp, ctypes.c_int64, _vp]
         L.jfa_check_device_error.restype = ctypes.c_int
         L.jfa_check_device_error.argtypes = [_vp, _vp]
         L.jfa_status_string.restype = ctypes.c_char_p
@@ -168,6 +172,19 @@ def jfa_build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, m
     _check(lib().jfa_build_worklist(pass_, _ptr(q_offsets), _ptr(kv_offsets), q_offsets.numel() - 1, heads,
                                     total_q, total_kv, int(max_q_len), int(max_kv_len), int(bool(causal)),
                                     _ptr(out), out.numel(), _stream()))
+
+
+def jfa_block_offsets(offsets, total, block=64):
+    """Device int32 offsets of the `block`-token runs of every sequence,
+    padded with empty sequences to jfa_block_offsets_count entries (see
+    include/jfa.h).  Use them as both q and kv offsets, with batch
+    len(result) - 1, for block attention."""
+    _offsets("offsets", offsets)
+    batch = offsets.numel() - 1
+    n = lib().jfa_block_offsets_count(batch, int(total), int(block))
+    out = torch.empty(max(n, 1), dtype=torch.int32, device=offsets.device)
+    _check(lib().jfa_block_offsets(_ptr(offsets), batch, int(total), int(block), _ptr(out), out.numel(), _stream()))
+    return out
 
 
 def jfa_check_device_error(workspace):

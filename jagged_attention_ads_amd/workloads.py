@@ -42,6 +42,7 @@ class Workload:
     kv_law: tuple | None  # length law of the key side (None: same lengths as q)
     backward: bool        # whether the workload runs the backward pass
     description: str
+    block: int = 0        # > 0: BlockAttention, attention within runs of `block` tokens
 
 
 WORKLOADS = {
@@ -73,6 +74,15 @@ WORKLOADS = {
 }
 
 # Workload order as listed above; index 1 is the headline workload.
+# BlockAttention (piletech.kr/articles/112134, Detailed notes, BlockAttention
+# item: fixed 64-token blocks) on the lengths of the causal self-attention
+# workload; not one of the five configurations, measured beside them.
+WORKLOADS["block_attn"] = Workload(
+    "block_attn", 256, 4, 128, "bf16", 1.0, True, "softmax",
+    ("lognormal", 256, 1024), None, True,
+    "BlockAttention (causal within fixed 64-token blocks), batch 256, log-normal lengths "
+    "(median 256, max 1024), 4 heads, d 128, bf16", block=64)
+
 ORDER = ["tiny_fp32", "selfattn_causal", "cross_asym", "gdpa_silu", "pareto_train"]
 
 

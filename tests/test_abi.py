@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     L = jfa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -130,3 +130,13 @@ def test_tile_shapes_and_worklist_size():
     cap = ((300 + 3 * 127) // 128) * 2
     assert n >= 16 + 8 * cap + 4 * 4
     assert jfa.jfa_worklist_bytes(9, 3, 2, 300, 10) == 0
+
+
+def test_block_offsets_validation():
+    assert jfa.lib().jfa_block_offsets_count(3, 200, 64) == 200 // 64 + 3 + 1
+    assert jfa.lib().jfa_block_offsets_count(3, 200, 0) == 0
+    L = jfa.lib()
+    assert L.jfa_block_offsets(P, 3, 200, 0, P, 100, None) == INVALID      # block < 1
+    assert L.jfa_block_offsets(P, 3, 200, 64, P, 6, None) == INVALID       # out shorter than the count (7)
+    assert L.jfa_block_offsets(None, 3, 200, 64, P, 7, None) == INVALID
+    assert L.jfa_block_offsets(P, -1, 200, 64, P, 7, None) == INVALID
