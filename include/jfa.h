@@ -86,7 +86,12 @@ enum jfa_status {
 
 enum jfa_activation { JFA_ACT_SOFTMAX = 0, JFA_ACT_SILU = 1 };
 enum jfa_dtype { JFA_DTYPE_BF16 = 0, JFA_DTYPE_FP32 = 1 };
-enum jfa_pass { JFA_PASS_QUERY_TILES = 0, JFA_PASS_KEY_TILES = 1, JFA_PASS_DQ_TILES = 2 };
+enum jfa_pass {
+  JFA_PASS_QUERY_TILES = 0,
+  JFA_PASS_KEY_TILES = 1,
+  JFA_PASS_DQ_TILES = 2,
+  JFA_PASS_DQ_STORED_TILES = 3
+};
 
 /* Bytes of device workspace jfa_forward (for_backward = 0) or jfa_backward
  * (for_backward = 1) needs for these sizes and element type (dtype is a
@@ -166,8 +171,10 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
  * JFA_SCHED_STAGE=0 selects the global-memory body everywhere, for tests of
  * it.  Both give the same list.
  * JFA_PASS_QUERY_TILES is the list of the
- * forward kernel, JFA_PASS_DQ_TILES that of the dQ kernel (smaller query
- * tiles) and JFA_PASS_KEY_TILES that of the dK/dV kernel. */
+ * forward kernel, JFA_PASS_DQ_STORED_TILES that of the dQ kernel over the
+ * stored dS (larger query tiles), JFA_PASS_DQ_TILES that of the dQ kernel
+ * that recomputes dS (smaller query tiles) and JFA_PASS_KEY_TILES that of
+ * the dK/dV kernel. */
 size_t jfa_worklist_bytes(int32_t pass, int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv);
 int jfa_tile_shape(int32_t pass, int32_t* tile_rows, int32_t* block_rows);
 int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,

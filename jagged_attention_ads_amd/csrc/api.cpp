@@ -32,7 +32,7 @@ constexpr uint64_t kDsMaxBytes = uint64_t(16) << 30;
 
 struct WsLayout {
   jfa::WorklistLayout wq{}, wkv{};
-  jfa::WorklistLayout wq_fwd{};   // backward: the 128-row query tiles of the dQ pass over stored dS
+  jfa::WorklistLayout wq_fwd{}, wq_dqs{};   // backward: the 128- and 256-row query tiles of the dQ pass over stored dS
   size_t off_wq = 0, off_wkv = 0, off_stats = 0, off_ds = 0, bytes = 0;
   int64_t ds_rows = 0, ds_kb = 0;
   bool ds = false;   // the workspace holds the dS blocks
@@ -51,7 +51,8 @@ WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_
   size_t off = L.off_wq + L.wq.bytes;
   if (backward) {   // the slot holds either query-tile list
     L.wq_fwd = jfa::worklist_layout(jfa::kPassQ, batch, heads, total_q);
-    off = std::max(off, L.off_wq + L.wq_fwd.bytes);
+    L.wq_dqs = jfa::worklist_layout(jfa::kPassDQS, batch, heads, total_q);
+    off = std::max({off, L.off_wq + L.wq_fwd.bytes, L.off_wq + L.wq_dqs.bytes});
   }
   if (backward) {
     L.wkv = jfa::worklist_layout(jfa::kPassKV, batch, heads, total_kv);
@@ -169,7 +170,8 @@ size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_
 }
 
 bool valid_pass(int32_t pass) {
-  return pass == JFA_PASS_QUERY_TILES || pass == JFA_PASS_KEY_TILES || pass == JFA_PASS_DQ_TILES;
+  return pass == JFA_PASS_QUERY_TILES || pass == JFA_PASS_KEY_TILES || pass == JFA_PASS_DQ_TILES ||
+         pass == JFA_PASS_DQ_STORED_TILES;
 }
 
 size_t jfa_worklist_bytes(int32_t pass, int32_t batch, int32_t heads, int32_t total_q, int32_t total_kv) {
@@ -189,6 +191,9 @@ int jfa_tile_shape(int32_t pass, int32_t* tile_rows, int32_t* block_rows) {
   } else if (pass == JFA_PASS_DQ_TILES) {
     *tile_rows = jfa::kDqBM;
     *block_rows = jfa::kDqBN;
+  } else if (pass == JFA_PASS_DQ_STORED_TILES) {
+    *tile_rows = jfa::kDqDsBM;
+    *block_rows = jfa::kDqBN;
   } else {
     return fail(JFA_ERR_INVALID_ARGUMENT, "bad pass");
   }
@@ -204,8 +209,8 @@ int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv
   int st = check_sizes(batch, heads, 32, total_q, total_kv, max_q_len, max_kv_len);
   if (st != JFA_OK) return st;
   const int32_t nb = pass == JFA_PASS_QUERY_TILES ? buckets_for(max_kv_len, jfa::kFwdBN)
-                     : pass == JFA_PASS_DQ_TILES    ? buckets_for(max_kv_len, jfa::kDqBN)
-                                                    : buckets_for(max_q_len, jfa::kBwdBM);
+                     : pass == JFA_PASS_KEY_TILES   ? buckets_for(max_q_len, jfa::kBwdBM)
+                                                    : buckets_for(max_kv_len, jfa::kDqBN);
   if (nb > jfa::kMaxBuckets) return fail(JFA_ERR_UNSUPPORTED, "maximum length exceeds the scheduler's range");
   const jfa::WorklistLayout lay =
       jfa::worklist_layout(pass, batch, heads, pass == JFA_PASS_KEY_TILES ? total_kv : total_q);
@@ -292,7 +297,7 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   }
   const int32_t nbq = buckets_for(max_kv_len, jfa::kDqBN);
   const int32_t nbk = buckets_for(max_q_len, jfa::kBwdBM);
-  static_assert(jfa::kDqBN == jfa::kFwdBN, "both query-tile lists count 64-key blocks");
+  static_assert(jfa::kDqBN == jfa::kFwdBN, "every query-tile list counts 64-key blocks");
   if (nbq > jfa::kMaxBuckets || nbk > jfa::kMaxBuckets)
     return fail(JFA_ERR_UNSUPPORTED, "maximum length exceeds the scheduler's range");
   if (batch == 0 || (total_q == 0 && total_kv == 0)) return JFA_OK;   // nothing to write
@@ -316,8 +321,14 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   // the dQ pass over stored dS walks the forward's 128-row query tiles, the
   // recomputing one 64-row tiles
   const bool use_ds = L.ds && !ds_disabled();
-  const int qpass = use_ds ? jfa::kPassQ : jfa::kPassDQ;
-  const jfa::WorklistLayout& lay_q = use_ds ? L.wq_fwd : L.wq;
+  // 256-row items halve the K re-reads of the dQ pass over stored dS, but
+  // its longest item doubles: they are used only when no sequence is much
+  // longer than the average (max <= 4 x mean), where the longest items do
+  // not set the pass's duration.
+  const bool wide = max_q_len > 128 && (int64_t)max_q_len * batch <= 4 * ((int64_t)total_q + batch - 1);
+  const int qpass = use_ds ? (wide ? jfa::kPassDQS : jfa::kPassQ) : jfa::kPassDQ;
+  const jfa::WorklistLayout& lay_q = use_ds ? (wide ? L.wq_dqs : L.wq_fwd) : L.wq;
+  a.dq_rows = wide ? jfa::kDqDsBM : 128;
   a.meta_q = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + lay_q.meta_off);
   a.meta_kv = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wkv + L.wkv.meta_off);
   a.lse2 = reinterpret_cast<float*>(ws + L.off_stats);

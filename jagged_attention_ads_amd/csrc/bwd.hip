@@ -578,16 +578,17 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 
 
 // dQ from the stored dS blocks: dQ^T = scale * K^T dS^T, one product per
-// (query, key) pair instead of three.  One workgroup per 128-query item (the
-// forward's tiles: each K row is fetched once per 128 queries); wave w owns
-// query block w (32 queries) and every d-block.  Each stage of the LDS ring
-// holds 32 key rows and the item's four dS blocks of those keys, copied
-// unchanged from HBM; K^T and dS^T fragments both come from transposed LDS
-// reads (rows = keys).  A dS block is read only where the dK/dV pass wrote
-// it: query blocks that see some key of the key block.
-template <typename T, int D>
+// (query, key) pair instead of three.  One workgroup per BM-query item
+// (BM = 128: the forward's tiles; BM = 256 when no sequence is much longer
+// than the average, so that each K row is fetched once per 256 queries):
+// wave w owns query block w (32 queries) and every d-block.  Each stage of
+// the LDS ring holds 32 key rows and the item's BM / 32 dS blocks of those
+// keys, copied unchanged from HBM; K^T and dS^T fragments both come from
+// transposed LDS reads (rows = keys).  A dS block is read only where the
+// dK/dV pass wrote it: query blocks that see some key of the key block.
+template <typename T, int D, int BM_>
 struct DqDsCfg {
-  static constexpr int BM = kFwdBM;                      // queries per item
+  static constexpr int BM = BM_;                         // queries per item
   static constexpr int NQB = BM / kDsBlock;              // dS blocks per stage = waves
   static constexpr int SR = kDsBlock;                    // key rows per stage
   static constexpr int NT = NQB * kWave;
@@ -616,9 +617,9 @@ __device__ __forceinline__ void wait_ring(int ahead) {
   }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__((DqDsCfg<T, D>::NT), (DqDsCfg<T, D>::WGS)) void dq_ds_kernel(BwdArgs a) {
-  using C = DqDsCfg<T, D>;
+template <typename T, int D, int BM>
+__global__ __launch_bounds__((DqDsCfg<T, D, BM>::NT), (DqDsCfg<T, D, BM>::WGS)) void dq_ds_kernel(BwdArgs a) {
+  using C = DqDsCfg<T, D, BM>;
   static_assert(C::NQB * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
   using Dma = typename C::Dma;
   constexpr int NPS = Dma::N + C::NDS;   // copies per thread per stage
@@ -708,7 +709,8 @@ JFA_BWD_INST(float, 32, 1) JFA_BWD_INST(float, 64, 1) JFA_BWD_INST(float, 128, 1
 #undef JFA_BWD_INST
 #define JFA_BWD_INST2(T, D)                                          \
   template __global__ void stats_kernel<T, D>(StatsArgs);            \
-  template __global__ void dq_ds_kernel<T, D>(BwdArgs);
+  template __global__ void dq_ds_kernel<T, D, 128>(BwdArgs);         \
+  template __global__ void dq_ds_kernel<T, D, kDqDsBM>(BwdArgs);
 JFA_BWD_INST2(__bf16, 32) JFA_BWD_INST2(__bf16, 64) JFA_BWD_INST2(__bf16, 128)
 JFA_BWD_INST2(float, 32) JFA_BWD_INST2(float, 64) JFA_BWD_INST2(float, 128)
 #undef JFA_BWD_INST2
@@ -738,7 +740,10 @@ static hipError_t dkdv_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream
 template <typename T, int ACT>
 static hipError_t dq_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
   if (a.ds != nullptr) {
-    JFA_PICK_D(return launch_k(dq_ds_kernel<T, D>, a, grid, stream, DqDsCfg<T, D>::NT))
+    if (a.dq_rows == kDqDsBM) {
+      JFA_PICK_D(return launch_k(dq_ds_kernel<T, D, kDqDsBM>, a, grid, stream, DqDsCfg<T, D, kDqDsBM>::NT))
+    }
+    JFA_PICK_D(return launch_k(dq_ds_kernel<T, D, 128>, a, grid, stream, DqDsCfg<T, D, 128>::NT))
   }
   JFA_PICK_D(return launch_k(dq_kernel<T, D, ACT>, a, grid, stream))
 }

@@ -15,10 +15,11 @@ constexpr int kBwdBN = 64;      // key rows per dK/dV work item
 constexpr int kBwdBM = 64;      // query rows per dK/dV cost block
 constexpr int kDqBM = 64;       // query rows per dQ work item
 constexpr int kDqBN = 64;       // key rows per dQ cost block
+constexpr int kDqDsBM = 256;    // query rows per work item of the dQ pass over stored dS
 constexpr int kMaxBuckets = 1024;   // distinct tile costs the scheduler can sort
 constexpr int kMaxHeads = 256;      // head index is packed into 8 bits
 
-enum Pass { kPassQ = 0, kPassKV = 1, kPassDQ = 2 };
+enum Pass { kPassQ = 0, kPassKV = 1, kPassDQ = 2, kPassDQS = 3 };
 
 // Per-item record the attention kernels read with one load: the sequence's
 // first query and key rows and lengths, the item's head and tile, and the
@@ -80,7 +81,7 @@ struct StatsArgs {
 };
 
 // The backward's two lists in one launch (two workgroups): the dQ pass's
-// query tiles (qpass: kPassQ or kPassDQ) and the key tiles.  With `stats`,
+// query tiles (qpass: kPassQ or kPassDQS over stored dS, kPassDQ recomputing) and the key tiles.  With `stats`,
 // the launch's further workgroups form the row statistics meanwhile.
 hipError_t launch_sched_pair(int qpass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                              int32_t causal, int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv,
@@ -129,6 +130,7 @@ struct BwdArgs {
                            // the dQ pass; null when the dQ pass recomputes dS
   int64_t ds_head_blocks;  // blocks per head: ds_block_rows * ds_kb
   int32_t ds_kb;           // key blocks per block row
+  int32_t dq_rows;         // query rows per item of the dQ pass over stored dS (128 or kDqDsBM)
   void* dq;
   void* dk;
   void* dv;

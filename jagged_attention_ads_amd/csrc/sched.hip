@@ -76,14 +76,16 @@ constexpr size_t kSchedMinLds = 64 * 1024;   // budget when the device does not 
 
 template <int PASS>
 struct TileRule {
-  // Tiles split the query side (forward: kPassQ, dQ: kPassDQ) or the key
-  // side (dK/dV: kPassKV).
+  // Tiles split the query side (forward: kPassQ; dQ: kPassDQ recomputing dS,
+  // kPassDQS over the stored dS) or the key side (dK/dV: kPassKV).
   static constexpr bool kQuery = PASS != kPassKV;
-  static constexpr int kTile = PASS == kPassQ ? kFwdBM : PASS == kPassDQ ? kDqBM : kBwdBN;
+  static constexpr int kTile =
+      PASS == kPassQ ? kFwdBM : PASS == kPassDQ ? kDqBM : PASS == kPassDQS ? kDqDsBM : kBwdBN;
   __device__ static int rows(int lq, int lk) { return kQuery ? lq : lk; }
   __device__ static int cost(int lq, int lk, int t, int causal) {
     if (PASS == kPassQ) return q_tile_kv_blocks(lq, lk, t, kFwdBM, kFwdBN, causal);
     if (PASS == kPassDQ) return q_tile_kv_blocks(lq, lk, t, kDqBM, kDqBN, causal);
+    if (PASS == kPassDQS) return q_tile_kv_blocks(lq, lk, t, kDqDsBM, kDqBN, causal);
     return kv_tile_q_blocks(lq, lk, t, kBwdBM, kBwdBN, causal);
   }
   // Costs are monotone in t within a sequence: non-decreasing for query
@@ -466,8 +468,9 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
 }
 
 // The backward's two lists in one launch: workgroup 0 builds the
-// query-tile list of the dQ pass (QPASS: the forward's 128-row tiles or the
-// 64-row dQ tiles), workgroup 1 the key-tile list.  Further workgroups, when
+// query-tile list of the dQ pass (QPASS: 128- or 256-row tiles over the
+// stored dS, or the 64-row tiles of the recomputing pass), workgroup 1 the
+// key-tile list.  Further workgroups, when
 // launched (softmax), form the row statistics of elements T and head
 // dimension D meanwhile: workgroup 2 + i covers row chunk i / heads of head
 // i % heads.  The two builders run alone on their compute units for most of
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_pair_kernel(const int* __
 }
 
 WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t total_rows) {
-  const int64_t tile = pass == kPassQ ? kFwdBM : pass == kPassDQ ? kDqBM : kBwdBN;
+  const int64_t tile = pass == kPassQ ? kFwdBM : pass == kPassDQ ? kDqBM : pass == kPassDQS ? kDqDsBM : kBwdBN;
   // sum over sequences of ceil(L_b / tile) <= (total + batch * (tile - 1)) / tile
   const int64_t tiles = (static_cast<int64_t>(total_rows) + static_cast<int64_t>(batch) * (tile - 1)) / tile;
   WorklistLayout lay;
@@ -550,6 +553,9 @@ hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t 
   if (pass == kPassQ)
     hipLaunchKernelGGL(sched_kernel<kPassQ>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
                        causal, j);
+  else if (pass == kPassDQS)
+    hipLaunchKernelGGL(sched_kernel<kPassDQS>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
+                       causal, j);
   else if (pass == kPassDQ)
     hipLaunchKernelGGL(sched_kernel<kPassDQ>, dim3(1), dim3(kSchedThreads), lds, stream, qo, ko, batch, heads,
                        causal, j);
@@ -591,6 +597,9 @@ hipError_t launch_sched_pair(int qpass, const int32_t* qo, const int32_t* ko, in
   const SchedJob jq = make_job(batch, heads, nb_dq, wl_dq, lay_dq, chk, lds_q);
   const SchedJob jkv = make_job(batch, heads, nb_kv, wl_kv, lay_kv, chk, lds_kv);
   const size_t lds = lds_q > lds_kv ? lds_q : lds_kv;
+  if (qpass == kPassDQS)
+    return dtype == 0 ? pair_launch_d<kPassDQS, __bf16>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream)
+                      : pair_launch_d<kPassDQS, float>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream);
   if (qpass == kPassQ)
     return dtype == 0 ? pair_launch_d<kPassQ, __bf16>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream)
                       : pair_launch_d<kPassQ, float>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, lds, stream);

@@ -27,6 +27,7 @@ DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 PASS_QUERY_TILES = 0
 PASS_KEY_TILES = 1
 PASS_DQ_TILES = 2
+PASS_DQ_STORED_TILES = 3
 
 EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_profiled", "jfa_backward_profiled",
             "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_check_device_error",

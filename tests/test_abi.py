@@ -123,6 +123,7 @@ def test_tile_shapes_and_worklist_size():
     assert jfa.jfa_tile_shape(jfa.PASS_QUERY_TILES) == (128, 64)
     assert jfa.jfa_tile_shape(jfa.PASS_KEY_TILES) == (64, 64)
     assert jfa.jfa_tile_shape(jfa.PASS_DQ_TILES) == (64, 64)
+    assert jfa.jfa_tile_shape(jfa.PASS_DQ_STORED_TILES) == (256, 64)
     with pytest.raises(jfa.JfaError):
         jfa.jfa_tile_shape(7)
     # capacity bound: sum ceil(L/128) <= (T + B*127)/128 items per head

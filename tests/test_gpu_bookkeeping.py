@@ -61,7 +61,8 @@ def sched_stage(request, monkeypatch):
 
 
 @pytest.mark.parametrize("name,batch,causal", WL_CASES)
-@pytest.mark.parametrize("pass_", [jfa.PASS_QUERY_TILES, jfa.PASS_KEY_TILES, jfa.PASS_DQ_TILES])
+@pytest.mark.parametrize("pass_", [jfa.PASS_QUERY_TILES, jfa.PASS_KEY_TILES, jfa.PASS_DQ_TILES,
+                                   jfa.PASS_DQ_STORED_TILES])
 def test_worklist_bit_exact(name, batch, causal, pass_, sched_stage):
     qo, ko, H, causal = _worklist_case(name, batch, causal)
     tile = jfa.jfa_tile_shape(pass_)[0]

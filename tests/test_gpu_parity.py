@@ -62,6 +62,10 @@ EDGE = {
     "d128_fp32_silu": ("tiny_fp32", [20, 66], [33, 66], dict(head_dim=128, activation="silu")),
     "d32_bf16_cross": ("cross_asym", [1, 64, 17], [4096, 5, 300], dict(head_dim=32, heads=3)),
     "many_heads": ("selfattn_causal", [50, 130], [50, 130], dict(heads=16, head_dim=64)),
+    # the dQ pass over stored dS takes 256-row items when no sequence is much
+    # longer than the mean (max <= 4 x mean, max > 128), 128-row items otherwise
+    "dq_items_256": ("selfattn_causal", [300, 260, 290, 129], [300, 260, 290, 129], {}),
+    "dq_items_128": ("selfattn_causal", [900] + [5] * 20, [900] + [5] * 20, {}),
     # the largest key length the scheduler accepts (1023 cost classes of 64 keys)
     "max_kv_len": ("cross_asym", [64, 3], [65472, 1000], dict(heads=2)),
     # the largest head count (the head index is packed into 8 bits of an item)
