@@ -116,3 +116,33 @@ def test_lse_base_mistake_is_caught():
     _, lse = oracle.attention_fwd(q, k, v, [0, 1], [0, 2], 1.0, "softmax", False)
     assert abs(lse[0, 0] - math.log(4)) < 1e-14
     assert abs(lse[0, 0] / math.log(2) - math.log(4)) > 0.1
+
+
+def _segments_shifted(qo, ko, block):
+    """Blocks counted from the second token of each sequence instead of its first."""
+    segs = []
+    for b in range(len(qo) - 1):
+        qs, qe = qo[b], qo[b + 1]
+        cuts = [qs] + list(range(qs + 1, qe, block)) + [qe] if qe - qs > 1 else [qs, qe]
+        cuts = sorted(set(cuts))
+        segs += [(x, y, x - qs + ko[b], y - qs + ko[b]) for x, y in zip(cuts[:-1], cuts[1:])]
+    return segs
+
+
+def _segments_sequence_normaliser(qo, ko, block):
+    """Blocks right, but a mistake of the GDPA normaliser: its units are the
+    whole sequences (the blocks' masks are lost)."""
+    return [(qo[b], qo[b + 1], ko[b], ko[b + 1]) for b in range(len(qo) - 1)]
+
+
+@pytest.mark.parametrize("mutant", [_segments_shifted, _segments_sequence_normaliser])
+@pytest.mark.parametrize("activation", ["softmax", "silu"])
+def test_block_mistakes_are_caught(monkeypatch, mutant, activation):
+    from tests.test_oracle_pins import brute_force_block_fwd
+    lens = [7, 3, 9]
+    q, k, v, _, qo, _ = _draw(lens, lens, 2, 3, seed=44)
+    monkeypatch.setattr(A, "_segments", mutant)
+    out, _ = oracle.attention_fwd(q, k, v, qo, qo, 0.6, activation, True, block=3)
+    monkeypatch.undo()
+    ref, _ = brute_force_block_fwd(q, k, v, qo, 0.6, activation, True, 3)
+    assert np.abs(out - ref).max() > 1e-3
