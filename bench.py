@@ -6,7 +6,8 @@
 A step is one pass of the whole hot path over one batch: the forward call
 (work-list build + attention kernel) and the backward call (work-list
 builds, softmax row statistics, dK/dV kernel -- which also stores the dS
-blocks -- and dQ kernel).  Inputs are generated on
+blocks, and writes the dQ of sequences of at most 64 tokens -- and dQ
+kernel).  Inputs are generated on
 the host, copied to HBM before timing, and stay resident.  Prints one JSON
 line: useful TFLOPS counted on the visible (query, key) pairs of the real,
 unpadded tokens -- 4*d FLOPs per pair forward, 10*d backward -- the split
@@ -125,27 +126,45 @@ def ds_blocks(q_lengths, kv_lengths, causal, blk=32):
     return n
 
 
-def kernel_accounting(wl, T_q, T_k, pairs_total, n_ds_blocks, ds_path):
+def short_split(q_lengths, kv_lengths, causal):
+    """(query rows, key rows, visible pairs, dS blocks) of the short
+    sequences -- at most 64 queries and 1 .. 64 keys -- whose dQ the dK/dV
+    pass writes itself, so that the dQ pass skips them."""
+    lq = np.asarray(q_lengths, dtype=np.int64)
+    lk = np.asarray(kv_lengths, dtype=np.int64)
+    m = (lq <= 64) & (lk >= 1) & (lk <= 64)
+    return (int(lq[m].sum()), int(lk[m].sum()), int(visible_pairs(lq[m], lk[m], causal).sum()),
+            ds_blocks(lq[m], lk[m], causal))
+
+
+def kernel_accounting(wl, T_q, T_k, pairs_total, n_ds_blocks, ds_path, short=(0, 0, 0, 0)):
     """Algorithmic FLOPs (the products each kernel must execute per visible
-    pair) and bytes (every tensor the kernel must touch, once) per launch."""
+    pair) and bytes (every tensor the kernel must touch, once) per launch.
+    `short` is short_split of the sequences whose dQ the dK/dV pass forms
+    (all zeros when it forms none): their dS stays on chip, and the dQ pass
+    does not touch them."""
     H, d = wl.heads, wl.head_dim
     es = 2 if wl.dtype == "bf16" else 4
+    sq, sk, sp, sb = short
     q_bytes, k_bytes = T_q * H * d * es, T_k * H * d * es
+    lq_bytes, lk_bytes = (T_q - sq) * H * d * es, (T_k - sk) * H * d * es   # sequences the dQ pass takes
     row_f32 = T_q * H * 4
-    ds_bytes = n_ds_blocks * H * 32 * 32 * es if ds_path else 0
+    ds_bytes = (n_ds_blocks - sb) * H * 32 * 32 * es if ds_path else 0
     soft = wl.activation == "softmax"
     acc = {
         "fwd": dict(flops=4 * d * H * pairs_total,
                     bytes=q_bytes + 2 * k_bytes + q_bytes + (row_f32 if soft else 0)),
-        # reads Q, dO, K, V (and lse2, delta); writes dK, dV and the dS blocks
-        "bwd_dkdv": dict(flops=8 * d * H * pairs_total,
-                         bytes=2 * q_bytes + 2 * k_bytes + (2 * row_f32 if soft else 0) + 2 * k_bytes + ds_bytes),
+        # reads Q, dO, K, V (and lse2, delta); writes dK, dV, the dS blocks
+        # and the short sequences' dQ
+        "bwd_dkdv": dict(flops=8 * d * H * pairs_total + 2 * d * H * sp,
+                         bytes=2 * q_bytes + 2 * k_bytes + (2 * row_f32 if soft else 0) + 2 * k_bytes + ds_bytes
+                         + sq * H * d * es),
     }
     if ds_path:   # dQ = scale * dS K: reads the dS blocks and K, writes dQ
-        acc["bwd_dq"] = dict(flops=2 * d * H * pairs_total, bytes=ds_bytes + k_bytes + q_bytes)
+        acc["bwd_dq"] = dict(flops=2 * d * H * (pairs_total - sp), bytes=ds_bytes + lk_bytes + lq_bytes)
     else:         # recomputes S, P, dP, dS: reads Q, dO, K, V, lse2, delta, writes dQ
-        acc["bwd_dq"] = dict(flops=6 * d * H * pairs_total,
-                             bytes=2 * q_bytes + 2 * k_bytes + q_bytes + (2 * row_f32 if soft else 0))
+        acc["bwd_dq"] = dict(flops=6 * d * H * (pairs_total - sp),
+                             bytes=3 * lq_bytes + 2 * lk_bytes + (2 * (T_q - sq) * H * 4 if soft else 0))
     if soft:      # reads O, dO and lse, writes lse2 and delta
         acc["bwd_stats"] = dict(flops=2 * d * H * T_q, bytes=2 * q_bytes + 3 * row_f32)
     return acc
@@ -296,6 +315,12 @@ def main():
     # or the store was left out of the workspace
     ds_path = (os.environ.get("JFA_BWD_DS") != "0"
                and ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, mk, q.dtype, 2))
+    # the dK/dV pass writes the dQ of short sequences (bf16, d 64 or 128: where
+    # its LDS has room) when every sequence is short, or always with
+    # JFA_BWD_FUSE_SHORT=2; never with 0
+    fuse_mode = os.environ.get("JFA_BWD_FUSE_SHORT", "1")
+    fuse_short = (fuse_mode != "0" and wl.dtype == "bf16" and D in (64, 128)
+                  and (fuse_mode == "2" or max(mq, mk) <= 64))
     act = jfa.ACTIVATIONS[wl.activation]
     dt = jfa.DTYPES[q.dtype]
     soft = wl.activation == "softmax"
@@ -370,7 +395,8 @@ def main():
 
     # roofline of the dominant kernel
     n_blk = ds_blocks(q_lens, kv_lens, wl.causal) if run_bwd else 0
-    acct = kernel_accounting(wl, T_q, T_k, pairs, n_blk, ds_path)
+    short = short_split(q_lens, kv_lens, wl.causal) if run_bwd and fuse_short else (0, 0, 0, 0)
+    acct = kernel_accounting(wl, T_q, T_k, pairs, n_blk, ds_path, short)
     name = max((n for n in acct if n in kern_ms), key=lambda n: kern_ms[n])
     t_s = kern_ms[name] * 1e-3
     ai = acct[name]["flops"] / acct[name]["bytes"]
@@ -394,6 +420,7 @@ def main():
                    "causal": wl.causal, "activation": wl.activation, "seed": args.seed, "total_q_tokens": T_q,
                    "total_kv_tokens": T_k, "visible_pairs_per_head": pairs, "block": wl.block,
                    "bwd_dq_from_stored_ds": bool(run_bwd and ds_path),
+                   "bwd_short_seqs_dq_in_dkdv": bool(run_bwd and fuse_short),
                    "useful_gflop_per_step": (useful_fwd + useful_bwd) / 1e9},
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "fwd_tflops": fwd_tf, "fwd_pct_peak": 100.0 * fwd_tf / PEAK_BF16_TFLOPS,

@@ -127,7 +127,14 @@ int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_of
  * kernel (which also stores the dS blocks in the workspace), then the dQ
  * kernel (dQ = scale * dS K over the stored blocks).  The environment
  * variable JFA_BWD_DS=0, or a workspace sized without the dS store, makes
- * the dQ kernel recompute dS from Q, K, V and dout instead. */
+ * the dQ kernel recompute dS from Q, K, V and dout instead.  When every
+ * sequence is short (max_q_len <= 64 and max_kv_len <= 64, bf16 with
+ * head_dim 64 or 128), each (sequence, head) is one dK/dV work item that
+ * sees all of its keys and queries; that item then also forms and writes
+ * the sequence's dQ from dS kept on chip, and the dQ kernel only zeroes the
+ * rows of sequences without keys.  The results equal the two-pass ones bit
+ * for bit.  JFA_BWD_FUSE_SHORT=0 turns this off; =2 applies it to the short
+ * sequences of any batch (the dQ kernel then skips them). */
 int jfa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
                  int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,

@@ -93,6 +93,21 @@ bool ds_disabled() {
   return e && e[0] == '0' && e[1] == 0;
 }
 
+// Whether the dK/dV pass writes the dQ of short sequences (at most 64
+// queries and 1 .. 64 keys) itself.  By default only when every sequence is
+// short (the maximum lengths say so): then the dQ pass has nothing left but
+// the zero rows of sequences without keys.  In a batch that also holds long
+// sequences, the long ones set the dQ pass's duration and the short ones
+// fill its gaps at no cost, while fusing lengthens the dK/dV pass.
+// JFA_BWD_FUSE_SHORT=0: never; =2: whenever the kernel can (for tests and
+// timing).
+bool fuse_short_wanted(int32_t max_q_len, int32_t max_kv_len) {
+  const char* e = std::getenv("JFA_BWD_FUSE_SHORT");
+  if (e && e[0] == '0' && e[1] == 0) return false;
+  if (e && e[0] == '2' && e[1] == 0) return true;
+  return max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kBwdBN;
+}
+
 // Records events[i] on the stream when the caller asked for stage events.
 hipError_t record(hipEvent_t* events, int i, hipStream_t stream) {
   if (!events) return hipSuccess;
@@ -329,6 +344,7 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   const int qpass = use_ds ? (wide ? jfa::kPassDQS : jfa::kPassQ) : jfa::kPassDQ;
   const jfa::WorklistLayout& lay_q = use_ds ? (wide ? L.wq_dqs : L.wq_fwd) : L.wq;
   a.dq_rows = wide ? jfa::kDqDsBM : 128;
+  a.fuse_short = fuse_short_wanted(max_q_len, max_kv_len) && jfa::dkdv_fuses_short(dtype, head_dim) ? 1 : 0;
   a.meta_q = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + lay_q.meta_off);
   a.meta_kv = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wkv + L.wkv.meta_off);
   a.lse2 = reinterpret_cast<float*>(ws + L.off_stats);
@@ -379,7 +395,12 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   }
   if ((e = record(events, 3, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (total_q > 0) {
-    e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, lay_q.capacity, stream);
+    // every sequence short (or without keys): the dK/dV pass wrote all dQ
+    // rows that see a key, the rest are zeros
+    if (a.fuse_short && max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kBwdBN)
+      e = jfa::launch_bwd_dq_keyless(a, batch, head_dim, dtype, stream);
+    else
+      e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, lay_q.capacity, stream);
     if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
   }
   if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");

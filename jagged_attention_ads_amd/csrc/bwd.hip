@@ -121,18 +121,22 @@ struct DsTile {
 };
 
 // The 8 values of a fragment -- row r, columns c0 .. c0+7 (c0 a multiple
-// of 8) -- stored into a dS block image.  Non-temporal: each block is read
-// once, by the dQ pass, and should not displace the Q and dO rows that the
-// dK/dV pass re-reads through the cache.
-template <typename T>
+// of 8) -- stored into a dS block image, in HBM (GLOBAL) or in LDS.  The
+// HBM stores are non-temporal: each block is read once, by the dQ pass, and
+// should not displace the Q and dO rows that the dK/dV pass re-reads
+// through the cache.
+template <typename T, bool GLOBAL = true>
 __device__ __forceinline__ void ds_store(char* blk, int r, int c0, const frag_t<T>& f) {
   using S = typename DsTile<T>::S;
+  auto put = [](char* p, const u32x4& v) {
+    if constexpr (GLOBAL) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
+  };
   if constexpr (sizeof(T) == 2) {
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, f), reinterpret_cast<u32x4*>(blk + S::off(r, c0 >> 3)));
+    put(blk + S::off(r, c0 >> 3), __builtin_bit_cast(u32x4, f));
   } else {
-    __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<f32x4*>(blk + S::off(r, c0 >> 2)));
-    __builtin_nontemporal_store(f32x4{f[4], f[5], f[6], f[7]},
-                                reinterpret_cast<f32x4*>(blk + S::off(r, (c0 >> 2) + 1)));
+    put(blk + S::off(r, c0 >> 2), __builtin_bit_cast(u32x4, f32x4{f[0], f[1], f[2], f[3]}));
+    put(blk + S::off(r, (c0 >> 2) + 1), __builtin_bit_cast(u32x4, f32x4{f[4], f[5], f[6], f[7]}));
   }
 }
 
@@ -152,6 +156,15 @@ __device__ __forceinline__ void ds_store(char* blk, int r, int c0, const frag_t<
 // dK(n-1) and forms dP(n); after it, A accumulates dV(n) and already forms
 // S(n+1), and B forms dS(n).  B's dK runs one sub-block behind so that both
 // sides of the barrier carry MFMA work for both waves.
+//
+// A short sequence (short_sequence: at most 64 queries and 64 keys) is one
+// item that sees all of the sequence's keys and queries, so with fuse_short
+// set the item also forms dQ = scale dS K: wave B keeps its dS blocks in
+// LDS instead of HBM, wave A puts the K rows it loaded there too, and after
+// the loop the four waves take the (at most two) 32-query blocks of dQ, one
+// half of d each, while they stage dK and dV.  The ring's slots 2 and 3 hold
+// K and dS; a short sequence has at most two sub-blocks and never reaches
+// them.
 template <typename T, int D>
 struct DkdvCfg {
   static constexpr int BN = kBwdBN;
@@ -171,6 +184,10 @@ struct DkdvCfg {
   static constexpr int NS = (4 * STAGE + XCH + SINK <= 80 * 1024) ? 4 : 3;   // stages in the ring
   static constexpr int LDS = NS * STAGE + XCH + SINK;
   static constexpr int ND = D / 32, NK = D / 16;
+  static constexpr int DT = DsTile<T>::BYTES;            // one 32 x 32 dS block
+  // short sequences: K rows (two query-tile images) and [query block][pair]
+  // dS blocks in the slots past the first two
+  static constexpr bool FUSE = sizeof(T) == 2 && NS >= 4 && (NS - 2) * STAGE >= 2 * QT + 2 * NPAIRS * DT;
 };
 
 template <typename T, int D, int ACT, bool DS>
@@ -198,6 +215,10 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   const int q_first = kv_tile_first_q_block(lq, lk, t, C::SR, C::BN, a.causal) * C::SR;
   const int rs = a.heads * D;
   const float inv_lk = lk > 0 ? 1.0f / (float)lk : 0.f;
+  bool fuse = false;   // uniform: this item also forms the sequence's dQ
+  if constexpr (C::FUSE) fuse = a.fuse_short && short_sequence(lq, lk);
+  char* const kq = smem + 2 * C::STAGE;   // fused: K rows 0-31, then 32-63
+  char* const dsl = kq + 2 * C::QT;       // fused: dS blocks [query block][pair]
   // DS: this pair's dS block of sub-block 0; sub-block n is n block rows on
   [[maybe_unused]] char* ds_blk = nullptr;
   [[maybe_unused]] const int ds_row_bytes = a.ds_kb * DsTile<T>::BYTES;
@@ -240,6 +261,17 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     for (int kk = 0; kk < C::NK; ++kk) xf[kk] = global_frag<T>(xp + 16 * kk);
 #pragma unroll
     for (int kk = 0; kk < C::NK; ++kk) settle(xf[kk]);
+  }
+  if constexpr (C::FUSE) {
+    // fused dQ: wave A's key row into LDS, at row swap23(key) of its pair's
+    // 32-row image as the query-tile copies place rows (rows past lk repeat
+    // row lk - 1; their dS is zero)
+    if (fuse && role_a) {
+      char* kt = kq + pair * C::QT;
+#pragma unroll
+      for (int kk = 0; kk < C::NK; ++kk)
+        *reinterpret_cast<frag_t<T>*>(kt + Swz<T, D>::off(swap23(c32), 2 * kk + g)) = xf[kk];
+    }
   }
   dma_wait();
   __syncthreads();
@@ -306,11 +338,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // sub-blocks in which this pair's keys are seen by some row
-  auto visible = [&](int n) {
+  // sub-blocks in which the keys kw .. kw+31 are seen by some row
+  auto visible_of = [&](int n, int kw) {
     const int qa = q_first + 32 * n;
-    return wave_live && qa < lq && !(a.causal && qa + 31 + off < kw0);
+    return kw < lk && qa < lq && !(a.causal && qa + 31 + off < kw);
   };
+  auto visible = [&](int n) { return visible_of(n, kw0); };
   auto needs_mask = [&](int n) {
     const int qa = q_first + 32 * n;
     return (qa + 32 > lq) || (kw0 + 32 > lk) || (a.causal && kw0 + 31 > qa + off);
@@ -376,9 +409,14 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) sf[ss] = pack_frag<T>(x, ss);
-      if constexpr (DS) {
-        // the dS the dK product uses, for the dQ pass: this lane's key row,
-        // queries 16*ss + 8*g .. +7 of the sub-block
+      // the dS the dK product uses, for dQ: this lane's key row, queries
+      // 16*ss + 8*g .. +7 of the sub-block; in HBM for the dQ pass, or
+      // (short sequence) in LDS for this workgroup's own dQ
+      if (fuse) {
+        char* blk = dsl + ((q_first / 32 + n) * C::NPAIRS + pair) * C::DT;
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) ds_store<T, false>(blk, c32, 16 * ss + 8 * g, sf[ss]);
+      } else if constexpr (DS) {
         char* blk = ds_blk + (int64_t)n * ds_row_bytes;
 #pragma unroll
         for (int ss = 0; ss < 2; ++ss) ds_store<T>(blk, c32, 16 * ss + 8 * g, sf[ss]);
@@ -390,10 +428,52 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
 
   // the ring is free once every wave is past the loop: stage the rows there
   __syncthreads();
-  if (!wave_live) return;
-  T* op = static_cast<T*>(role_a ? a.dv : a.dk) + (size_t)(ks + kw0) * rs + (size_t)h * D;
-  store_rows_lds<T, D>(op, rs, min(32, lk - kw0), acc, role_a ? 1.0f : a.scale,
-                       smem + w * store_scratch_bytes<T, D>());
+  auto store_dkdv = [&]() {
+    T* op = static_cast<T*>(role_a ? a.dv : a.dk) + (size_t)(ks + kw0) * rs + (size_t)h * D;
+    store_rows_lds<T, D>(op, rs, min(32, lk - kw0), acc, role_a ? 1.0f : a.scale,
+                         smem + w * store_scratch_bytes<T, D>());
+  };
+  if constexpr (C::FUSE) {
+    if (fuse) {
+      // dQ^T = K^T dS^T, one wave per (query block qb, half of d); a short
+      // sequence has at most two query blocks.  The sum runs over the key
+      // blocks whose dS block wave B wrote (the pairs that saw sub-block
+      // qb - q_first/32); rows that see no key get zeros.
+      constexpr int NDH = C::ND / 2;
+      const int qb = w & 1, half = w >> 1, qa = 32 * qb, n = qb - q_first / 32;
+      const bool q_live = qa < lq;
+      f32x16 accq[NDH];
+#pragma unroll
+      for (int i = 0; i < NDH; ++i) accq[i] = f32x16{};
+      if (q_live && n >= 0) {
+#pragma unroll
+        for (int p = 0; p < C::NPAIRS; ++p) {
+          if (!visible_of(n, 32 * p)) continue;
+          const char* dt = dsl + (qb * C::NPAIRS + p) * C::DT;
+          const char* kt = kq + p * C::QT;
+#pragma unroll
+          for (int ss = 0; ss < 2; ++ss) {
+            const frag_t<T> sq = lds_col_frag<T, kDsBlock, false>(dt, 16 * ss, 0);
+#pragma unroll
+            for (int j = 0; j < NDH; ++j)
+              mma(accq[j], lds_col_frag<T, D, true>(kt, 16 * ss, 32 * (half * NDH + j)), sq);
+          }
+        }
+      }
+      // dK and dV are staged in slots 0 and 1 while other waves may still
+      // read slots 2 and 3
+      static_assert(C::NT / kWave * store_scratch_bytes<T, D>() <= 2 * C::STAGE, "dK/dV staging must fit slots 0-1");
+      static_assert(C::NT / kWave * store_scratch_bytes<T, D / 2>() <= (C::NS - 2) * C::STAGE,
+                    "dQ staging must fit the slots past the first two");
+      if (wave_live) store_dkdv();
+      __syncthreads();   // K rows and dS blocks read: their LDS stages dQ
+      if (q_live)
+        store_rows_lds<T, D / 2>(static_cast<T*>(a.dq) + (size_t)(qs + qa) * rs + (size_t)h * D + half * (D / 2), rs,
+                                 min(32, lq - qa), accq, a.scale, kq + w * store_scratch_bytes<T, D / 2>());
+      return;
+    }
+  }
+  if (wave_live) store_dkdv();
 }
 
 // ---------------------------------------------------------------- dQ
@@ -435,6 +515,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 
   const ItemMeta m = a.meta_q[blockIdx.x];   // one load: offsets, lengths, head, tile
   if (m.lq < 0) return;                       // past the item count
+  if (a.fuse_short && short_sequence(m.lq, m.lk)) return;   // dQ written by the dK/dV pass
   const int qs = m.qs, lq = m.lq, ks = m.ks, lk = m.lk, h = m.head, t = m.tile;
   const int off = lk - lq;
 
@@ -628,6 +709,7 @@ __global__ __launch_bounds__((DqDsCfg<T, D, BM>::NT), (DqDsCfg<T, D, BM>::WGS)) 
 
   const ItemMeta m = a.meta_q[blockIdx.x];   // one load: offsets, lengths, head, tile, sequence
   if (m.lq < 0) return;                       // past the item count
+  if (a.fuse_short && short_sequence(m.lq, m.lk)) return;   // dQ written by the dK/dV pass
   const int qs = m.qs, lq = m.lq, ks = m.ks, lk = m.lk, h = m.head, t = m.tile;
   const int off = lk - lq;
 
@@ -732,6 +814,19 @@ static hipError_t launch_k(K kernel, const BwdArgs& a, int64_t grid, hipStream_t
   }                                                               \
   return hipErrorInvalidValue;
 
+bool dkdv_fuses_short(int dtype, int head_dim) {
+  auto pick = [&](auto tag) -> bool {
+    using T = decltype(tag);
+    switch (head_dim) {
+      case 32: return DkdvCfg<T, 32>::FUSE;
+      case 64: return DkdvCfg<T, 64>::FUSE;
+      case 128: return DkdvCfg<T, 128>::FUSE;
+    }
+    return false;
+  };
+  return dtype == 0 ? pick(__bf16{}) : pick(float{});
+}
+
 template <typename T, int ACT>
 static hipError_t dkdv_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
   const bool ds = a.ds != nullptr;
@@ -768,6 +863,26 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, int act, int
   if (grid <= 0) return hipSuccess;
   if (dtype == 0) return act == 0 ? dq_d<__bf16, 0>(a, head_dim, grid, stream) : dq_d<__bf16, 1>(a, head_dim, grid, stream);
   return act == 0 ? dq_d<float, 0>(a, head_dim, grid, stream) : dq_d<float, 1>(a, head_dim, grid, stream);
+}
+
+// The dQ pass when every sequence is short or has no keys: the dK/dV pass
+// wrote the short sequences' dQ, and a sequence without keys gets zero rows.
+// One workgroup per sequence; offsets outside [0, total_q] write nothing.
+__global__ __launch_bounds__(256) void dq_keyless_kernel(BwdArgs a, int row_bytes) {
+  const int b = blockIdx.x;
+  if (a.ko[b + 1] != a.ko[b]) return;
+  const int q0 = a.qo[b], q1 = a.qo[b + 1];
+  if (q0 < 0 || q1 > a.total_q || q1 <= q0) return;
+  u32x4* p = reinterpret_cast<u32x4*>(static_cast<char*>(a.dq) + (size_t)q0 * row_bytes);
+  const int64_t n = (int64_t)(q1 - q0) * (row_bytes / 16);
+  for (int64_t i = threadIdx.x; i < n; i += 256) p[i] = u32x4{0, 0, 0, 0};
+}
+
+hipError_t launch_bwd_dq_keyless(const BwdArgs& a, int batch, int head_dim, int dtype, hipStream_t stream) {
+  const int row_bytes = a.heads * head_dim * (dtype == 0 ? 2 : 4);
+  if (batch <= 0 || row_bytes % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dq_keyless_kernel, dim3(batch), dim3(256), 0, stream, a, row_bytes);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_stats(const StatsArgs& a, int head_dim, int dtype, hipStream_t stream) {

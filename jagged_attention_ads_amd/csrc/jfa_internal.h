@@ -38,6 +38,12 @@ constexpr int kDsBlock = 32;
 inline int64_t ds_block_rows(int32_t batch, int32_t total_q) { return (int64_t)total_q / kDsBlock + batch; }
 inline int64_t ds_key_blocks(int32_t max_kv_len) { return ((int64_t)max_kv_len + kDsBlock - 1) / kDsBlock; }
 
+// Short sequences of the backward: at most kBwdBN queries and 1 .. kBwdBN
+// keys.  Such a sequence is a single dK/dV item whose workgroup sees every
+// key and every query, so (where the dK/dV kernel has the LDS for it) that
+// workgroup also writes the sequence's dQ rows, and the dQ pass skips it.
+constexpr bool short_sequence(int lq, int lk) { return lq <= kBwdBN && lk >= 1 && lk <= kBwdBN; }
+
 // Device layout of a work list (all offsets in bytes from its base):
 //   0                      int32   item count
 //   16                     int2    items[capacity]   (x = sequence, y = tile << 8 | head)
@@ -131,6 +137,7 @@ struct BwdArgs {
   int64_t ds_head_blocks;  // blocks per head: ds_block_rows * ds_kb
   int32_t ds_kb;           // key blocks per block row
   int32_t dq_rows;         // query rows per item of the dQ pass over stored dS (128 or kDqDsBM)
+  int32_t fuse_short;      // 1: the dK/dV pass writes dQ of short sequences (see short_sequence)
   void* dq;
   void* dk;
   void* dv;
@@ -144,8 +151,14 @@ struct BwdArgs {
 
 // Row statistics (softmax): lse2 and delta for every (row, head).
 hipError_t launch_bwd_stats(const StatsArgs& a, int head_dim, int dtype, hipStream_t stream);
+// Whether the dK/dV kernel for this dtype (0 bf16, 1 fp32) and head_dim
+// writes the dQ rows of short sequences when BwdArgs::fuse_short is set.
+bool dkdv_fuses_short(int dtype, int head_dim);
 // dK/dV pass; with a.ds set it also stores dS for the dQ pass.
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
+// dQ pass when every sequence is short or has no keys (a.fuse_short set):
+// zero rows for the sequences without keys.
+hipError_t launch_bwd_dq_keyless(const BwdArgs& a, int batch, int head_dim, int dtype, hipStream_t stream);
 // dQ pass: from the stored dS when a.ds is set, else recomputing dS.
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
 

@@ -51,3 +51,33 @@ def test_kernel_accounting_shapes():
     no_ds = bench.kernel_accounting(wl, 1000, 1000, 12345, 77, False)
     assert acct["bwd_dkdv"]["bytes"] - no_ds["bwd_dkdv"]["bytes"] == ds
     assert acct["bwd_dq"]["bytes"] >= ds
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_short_split(causal):
+    """The short sequences (<= 64 queries, 1 .. 64 keys) whose dQ the dK/dV
+    pass writes: their rows, pairs and dS blocks by brute force, and moving
+    them out of the dQ pass leaves the backward's FLOPs at 10 d per pair over
+    stored dS (the recomputing dQ pass adds S and dP again: 4 d per pair of
+    the sequences it takes)."""
+    from jagged_attention_ads_amd.workloads import WORKLOADS
+    wl = WORKLOADS["selfattn_causal"]
+    for lq, lk in _cases():
+        sq = sk = sp = sb = 0
+        for q, k in zip(lq, lk):
+            if q <= 64 and 1 <= k <= 64:
+                vis = oracle.visible_mask(q, k, causal)
+                sq, sk, sp = sq + q, sk + k, sp + int(vis.sum())
+                sb += sum(bool(vis[i0:i0 + 32, j0:j0 + 32].any()) for i0 in range(0, q, 32) for j0 in range(0, k, 32))
+        short = bench.short_split(lq, lk, causal)
+        assert short == (sq, sk, sp, sb)
+        pairs = int(bench.visible_pairs(lq, lk, causal).sum())
+        nb = bench.ds_blocks(lq, lk, causal)
+        T_q, T_k = int(np.sum(lq)), int(np.sum(lk))
+        for ds_path in (True, False):
+            a = bench.kernel_accounting(wl, T_q, T_k, pairs, nb, ds_path, short)
+            b = bench.kernel_accounting(wl, T_q, T_k, pairs, nb, ds_path)
+            dH = wl.head_dim * wl.heads
+            assert a["bwd_dkdv"]["flops"] + a["bwd_dq"]["flops"] == dH * (10 * pairs if ds_path else
+                                                                           14 * pairs - 4 * sp)
+            assert a["bwd_dq"]["bytes"] <= b["bwd_dq"]["bytes"]

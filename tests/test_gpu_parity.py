@@ -79,15 +79,20 @@ def _edge_batch(name):
     return make_batch(wl, 100 + sorted(EDGE).index(name), q_lengths=lq, kv_lengths=lk, with_dout=True)
 
 
-@pytest.fixture(params=["stored_ds", "recompute"])
+@pytest.fixture(params=["stored_ds", "recompute", "short_in_dkdv"])
 def dq_path(request, monkeypatch):
-    """The backward's two dQ passes: from the dS blocks the dK/dV pass stores
-    (the default), or recomputing dS (JFA_BWD_DS=0; also what runs when the
-    dS store would not fit the workspace limit)."""
+    """The backward's dQ paths: from the dS blocks the dK/dV pass stores (the
+    default), or recomputing dS (JFA_BWD_DS=0; also what runs when the dS
+    store would not fit the workspace limit).  short_in_dkdv
+    (JFA_BWD_FUSE_SHORT=2) has the dK/dV pass write the dQ of the short
+    sequences (<= 64 queries, 1 .. 64 keys) in any batch, not only in one
+    where every sequence is short, and the dQ pass skip them."""
+    monkeypatch.delenv("JFA_BWD_DS", raising=False)
+    monkeypatch.delenv("JFA_BWD_FUSE_SHORT", raising=False)
     if request.param == "recompute":
         monkeypatch.setenv("JFA_BWD_DS", "0")
-    else:
-        monkeypatch.delenv("JFA_BWD_DS", raising=False)
+    elif request.param == "short_in_dkdv":
+        monkeypatch.setenv("JFA_BWD_FUSE_SHORT", "2")
     return request.param
 
 
@@ -135,6 +140,52 @@ def test_edge_cases(name, dq_path):
     ref_out, ref_lse = oracle_fwd(b)
     check_forward(out, lse, ref_out, ref_lse, b.workload.activation)
     check_backward(grads, oracle_bwd(b))
+
+
+# ------------------------------------------------------------------ short sequences
+
+# Short sequences (at most 64 queries and 1 .. 64 keys) are one dK/dV item each;
+# that item can also write their dQ, and the dQ pass then skips them.  It does
+# by default when every sequence is short (or has no keys): the dQ pass only
+# zeroes the rows of sequences without keys.  In mixed batches it does with
+# JFA_BWD_FUSE_SHORT=2: short sequences next to ones the dQ pass takes, ones
+# with no keys or no queries, and causal cases where the first query block
+# sees no key (64 queries, 10 keys).
+SHORT_Q = [1, 31, 32, 33, 63, 64, 64, 40, 0, 7, 300, 64, 17]
+SHORT_K = [1, 31, 32, 33, 63, 64, 10, 20, 5, 0, 300, 65, 64]
+ALL_SHORT_Q = [1, 64, 40, 7, 0, 33, 64, 12]
+ALL_SHORT_K = [1, 10, 64, 0, 5, 33, 64, 0]
+SHORT = {
+    "softmax_causal": ("selfattn_causal", {}, SHORT_Q, SHORT_K),
+    "softmax_noncausal": ("selfattn_causal", dict(causal=False), SHORT_Q, SHORT_K),
+    "silu_causal_d64": ("gdpa_silu", dict(head_dim=64), SHORT_Q, SHORT_K),
+    "softmax_noncausal_d64": ("cross_asym", dict(heads=3), SHORT_Q, SHORT_K),
+    "all_short_causal": ("selfattn_causal", {}, ALL_SHORT_Q, ALL_SHORT_K),
+    "all_short_silu": ("gdpa_silu", dict(causal=False), ALL_SHORT_Q, ALL_SHORT_K),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHORT))
+def test_short_sequences_dq_in_dkdv(name, monkeypatch):
+    """Within the gates of the oracle, and bitwise equal to the results with
+    the short sequences left to the dQ pass over stored dS: both take the
+    same dS blocks and sum the same products in the same order."""
+    base, over, lq, lk = SHORT[name]
+    wl = dataclasses.replace(WORKLOADS[base], backward=True, **over)
+    b = make_batch(wl, 200 + sorted(SHORT).index(name), q_lengths=lq, kv_lengths=lk, with_dout=True)
+    d = Dev(b)
+    monkeypatch.delenv("JFA_BWD_DS", raising=False)
+    monkeypatch.delenv("JFA_BWD_FUSE_SHORT", raising=False)
+    if max(lq) > 64 or max(lk) > 64:
+        monkeypatch.setenv("JFA_BWD_FUSE_SHORT", "2")
+    out, lse = d.forward()
+    fused = d.backward(out, lse)
+    monkeypatch.setenv("JFA_BWD_FUSE_SHORT", "0")
+    apart = d.backward(out, lse)
+    torch.cuda.synchronize()
+    check_backward(fused, oracle_bwd(b))
+    for x, y in zip(fused, apart):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
 # ------------------------------------------------------------------ full sizes, sampled
