@@ -23,6 +23,7 @@
 namespace jfa {
 
 constexpr int kSchedThreads = 1024;
+constexpr int kStatsWorkgroups = 254;   // 256 CUs less the two list builders
 constexpr int kSchedWaves = kSchedThreads / kWave;
 
 // Exclusive block scan of one value per thread.  `tmp` holds kSchedWaves ints.
@@ -472,9 +473,11 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(const int* __restr
 // stored dS, or the 64-row tiles of the recomputing pass), workgroup 1 the
 // key-tile list.  Further workgroups, when
 // launched (softmax), form the row statistics of elements T and head
-// dimension D meanwhile: workgroup 2 + i covers row chunk i / heads of head
-// i % heads.  The two builders run alone on their compute units for most of
-// their time; the statistics fill the rest of the chip.
+// dimension D meanwhile: with G of them, workgroup 2 + i takes the units
+// i, i + G, i + 2G, ... (unit u: row chunk u / heads of head u % heads), and
+// has the next unit's reads in flight while it reduces the current one.
+// The two builders run alone on their compute units for most of their
+// time; the statistics fill the rest of the chip, one workgroup per CU.
 template <int QPASS, typename T, int D>
 __global__ __launch_bounds__(kSchedThreads) void sched_pair_kernel(const int* __restrict__ qo,
                                                                    const int* __restrict__ ko, int B, int H,
@@ -486,8 +489,19 @@ __global__ __launch_bounds__(kSchedThreads) void sched_pair_kernel(const int* __
   } else if (blockIdx.x == 1) {
     sched_body<kPassKV>(qo, ko, B, H, causal, jkv, smem);
   } else {
-    const int i = (int)blockIdx.x - 2;
-    stats_block<T, D, kSchedThreads>(sa, i / sa.heads, i % sa.heads, (int)threadIdx.x);
+    using R = StatsRows<T, D, kSchedThreads>;
+    const int64_t units = (int64_t)((sa.total_q + R::C::ROWS - 1) / R::C::ROWS) * sa.heads;
+    const int64_t g = (int64_t)gridDim.x - 2;
+    const int tid = (int)threadIdx.x;
+    int64_t u = (int64_t)blockIdx.x - 2;
+    R cur, nxt;
+    cur.load(sa, (int)(u / sa.heads), (int)(u % sa.heads), tid);
+    for (; u < units; u += g) {
+      const int64_t v = u + g;
+      if (v < units) nxt.load(sa, (int)(v / sa.heads), (int)(v % sa.heads), tid);
+      cur.finish(sa, (int)(u / sa.heads), (int)(u % sa.heads), tid);
+      cur = nxt;
+    }
   }
 }
 
@@ -570,7 +584,10 @@ static hipError_t pair_launch(const int32_t* qo, const int32_t* ko, int32_t batc
                               const SchedJob& jq, const SchedJob& jkv, const StatsArgs* stats, size_t lds,
                               hipStream_t stream) {
   constexpr int rows = StatsCfg<T, D, kSchedThreads>::ROWS;
-  const int64_t extra = stats ? (int64_t)((stats->total_q + rows - 1) / rows) * heads : 0;
+  // one statistics workgroup per remaining CU at most (the builders' LDS
+  // may leave room for only one 1024-thread workgroup per CU), each looping
+  const int64_t units = stats ? (int64_t)((stats->total_q + rows - 1) / rows) * heads : 0;
+  const int64_t extra = std::min<int64_t>(units, kStatsWorkgroups);
   const StatsArgs sa = stats ? *stats : StatsArgs{};
   hipLaunchKernelGGL((sched_pair_kernel<QPASS, T, D>), dim3((unsigned)(2 + extra)), dim3(kSchedThreads), lds, stream,
                      qo, ko, batch, heads, causal, jq, jkv, sa);
