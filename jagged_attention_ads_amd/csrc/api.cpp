@@ -398,7 +398,7 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
     // every sequence short (or without keys): the dK/dV pass wrote all dQ
     // rows that see a key, the rest are zeros
     if (a.fuse_short && max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kBwdBN)
-      e = jfa::launch_bwd_dq_keyless(a, batch, head_dim, dtype, stream);
+      e = jfa::launch_bwd_dq_keyless(a, chk.status, batch, head_dim, dtype, stream);
     else
       e = jfa::launch_bwd_dq(a, head_dim, dtype, activation, lay_q.capacity, stream);
     if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");

@@ -867,10 +867,12 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, int act, int
 
 // The dQ pass when every sequence is short or has no keys: the dK/dV pass
 // wrote the short sequences' dQ, and a sequence without keys gets zero rows.
-// One workgroup per sequence; offsets outside [0, total_q] write nothing.
-__global__ __launch_bounds__(256) void dq_keyless_kernel(BwdArgs a, int row_bytes) {
+// One workgroup per sequence.  Nothing is written when the list builder
+// rejected the offsets (status word not 0), and offsets outside
+// [0, total_q] write nothing either.
+__global__ __launch_bounds__(256) void dq_keyless_kernel(BwdArgs a, const int* status, int row_bytes) {
   const int b = blockIdx.x;
-  if (a.ko[b + 1] != a.ko[b]) return;
+  if (*status != 0 || a.ko[b + 1] != a.ko[b]) return;
   const int q0 = a.qo[b], q1 = a.qo[b + 1];
   if (q0 < 0 || q1 > a.total_q || q1 <= q0) return;
   u32x4* p = reinterpret_cast<u32x4*>(static_cast<char*>(a.dq) + (size_t)q0 * row_bytes);
@@ -878,10 +880,11 @@ __global__ __launch_bounds__(256) void dq_keyless_kernel(BwdArgs a, int row_byte
   for (int64_t i = threadIdx.x; i < n; i += 256) p[i] = u32x4{0, 0, 0, 0};
 }
 
-hipError_t launch_bwd_dq_keyless(const BwdArgs& a, int batch, int head_dim, int dtype, hipStream_t stream) {
+hipError_t launch_bwd_dq_keyless(const BwdArgs& a, const int* status, int batch, int head_dim, int dtype,
+                                 hipStream_t stream) {
   const int row_bytes = a.heads * head_dim * (dtype == 0 ? 2 : 4);
-  if (batch <= 0 || row_bytes % 16 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(dq_keyless_kernel, dim3(batch), dim3(256), 0, stream, a, row_bytes);
+  if (batch <= 0 || row_bytes % 16 != 0 || !status) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dq_keyless_kernel, dim3(batch), dim3(256), 0, stream, a, status, row_bytes);
   return hipGetLastError();
 }
 

@@ -157,8 +157,10 @@ bool dkdv_fuses_short(int dtype, int head_dim);
 // dK/dV pass; with a.ds set it also stores dS for the dQ pass.
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
 // dQ pass when every sequence is short or has no keys (a.fuse_short set):
-// zero rows for the sequences without keys.
-hipError_t launch_bwd_dq_keyless(const BwdArgs& a, int batch, int head_dim, int dtype, hipStream_t stream);
+// zero rows for the sequences without keys, unless the offsets check word
+// `status` (written by the list builder) reports rejected offsets.
+hipError_t launch_bwd_dq_keyless(const BwdArgs& a, const int* status, int batch, int head_dim, int dtype,
+                                 hipStream_t stream);
 // dQ pass: from the stored dS when a.ds is set, else recomputing dS.
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
 

@@ -270,6 +270,28 @@ def test_device_offsets_check(case, monkeypatch):
     assert qo.cpu().tolist() == qo_list
 
 
+def test_device_offsets_check_keyless(monkeypatch):
+    """Rejected offsets in a batch of short sequences, one of them without
+    keys: the dQ launch, which there only zeroes the rows of sequences
+    without keys, writes nothing either."""
+    monkeypatch.setenv("JFA_CHECK_OFFSETS", "1")
+    H, D, T, B = 2, 64, 9, 3
+    g = torch.Generator().manual_seed(8)
+    q, k, v, do = (torch.randn((T, H, D), generator=g).to(torch.bfloat16).to(dev()) for _ in range(4))
+    qo = torch.tensor([1, 5, 5, 9], dtype=torch.int32, device=dev())   # first offset not 0
+    ko = torch.tensor([0, 0, 4, 9], dtype=torch.int32, device=dev())   # sequence 0 has no keys
+    out = torch.zeros((T, H, D), dtype=torch.bfloat16, device=dev())
+    lse = torch.zeros((H, T), dtype=torch.float32, device=dev())
+    nan = float("nan")
+    dq, dk, dv = (torch.full((T, H, D), nan, dtype=torch.bfloat16, device=dev()) for _ in range(3))
+    ws_b = jfa.workspace(B, H, D, T, T, 5, q.dtype, 1, dev())
+    jfa.jfa_backward(q, k, v, out, do, lse, qo, ko, 5, 5, 0.125, "softmax", True, dq, dk, dv, ws_b)
+    st, msg = jfa.jfa_check_device_error(ws_b)
+    assert st == 1 and "first offset not 0" in msg
+    for t in (dq, dk, dv):
+        assert torch.isnan(t).all(), "an output was written from rejected offsets"
+
+
 @pytest.mark.parametrize("recompute", [False, True])
 def test_no_keys_at_all(recompute, monkeypatch):
     """total_kv = 0 with queries present: only the query-tile list is built and
