@@ -277,7 +277,12 @@ int jfa_forward_profiled(const void* q, const void* k, const void* v, const int3
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  e = jfa::launch_fwd(a, head_dim, dtype, activation, L.wq.capacity, stream);
+  // every sequence at most 64 queries and 64 keys: the two-wave variant
+  // (JFA_FWD_SHORT=0 keeps the four-wave kernel, for tests and timing)
+  const char* fs = std::getenv("JFA_FWD_SHORT");
+  const bool short_batch =
+      !(fs && fs[0] == '0' && fs[1] == 0) && max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kFwdBN;
+  e = jfa::launch_fwd(a, head_dim, dtype, activation, L.wq.capacity, short_batch, stream);
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
   if ((e = record(events, 2, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;

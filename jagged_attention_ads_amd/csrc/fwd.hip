@@ -24,22 +24,33 @@
 
 namespace jfa {
 
-template <typename T, int D>
+// SHORT: the variant for batches whose sequences all have at most 64
+// queries and 64 keys (BlockAttention's runs).  Such an item has one key
+// tile and fills only the first two waves' rows of its 128-row tile, so
+// the variant runs those two waves with one K and one V slot: half the LDS
+// and registers per item, twice the items in flight per CU, the same
+// arithmetic per row.
+template <typename T, int D, bool SHORT = false>
 struct FwdCfg {
-  static constexpr int BM = kFwdBM, BN = kFwdBN, NT = 256;
+  static constexpr int BM = kFwdBM, BN = kFwdBN;
+  static constexpr int NT = SHORT ? 128 : 256;
   static constexpr int KT = Swz<T, D>::tile_bytes(BN);   // one K or V tile
-  static constexpr int LDS = 4 * KT;                     // K slots 0, 1; V slots 0, 1
+  static constexpr int SLOTS = SHORT ? 1 : 2;            // K slots, and as many V slots
+  static constexpr int LDS = 2 * SLOTS * KT;
   static constexpr int ND = D / 32;                      // 32-wide d blocks of O^T
   static constexpr int NK = D / 16;                      // k-steps of S^T
+  // waves per SIMD to fit (the second launch bound): two, i.e. two
+  // workgroups per CU, or four of the two-wave SHORT variant
+  static constexpr int WPS = (D >= 128 && sizeof(T) == 4) ? 1 : 2;
 };
 
-template <typename T, int D, int ACT>
-__global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd_kernel(FwdArgs a) {
-  using C = FwdCfg<T, D>;
-  static_assert(4 * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
+template <typename T, int D, int ACT, bool SHORT>
+__global__ __launch_bounds__((FwdCfg<T, D, SHORT>::NT), (FwdCfg<T, D, SHORT>::WPS)) void fwd_kernel(FwdArgs a) {
+  using C = FwdCfg<T, D, SHORT>;
+  static_assert(C::NT / kWave * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   char* const kslot0 = smem;
-  char* const vslot0 = smem + 2 * C::KT;
+  char* const vslot0 = smem + C::SLOTS * C::KT;
 
   const ItemMeta m = a.meta[blockIdx.x];   // one load: offsets, lengths, head, tile
   if (m.lq < 0) return;                       // past the item count
@@ -52,13 +63,18 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
   const bool wave_live = row0 < lq;
   const int n_kv = q_tile_kv_blocks(lq, lk, t, C::BM, C::BN, a.causal);
   const int rs = a.heads * D;            // elements between consecutive tokens
+  // SHORT runs only where the host knows every length is at most 64; an
+  // item that breaks that (lengths beyond the stated maxima) is left alone
+  // rather than read past the one K and V slot
+  if constexpr (SHORT)
+    if (n_kv > 1 || lq > 2 * 32) return;
 
   const T* kb = static_cast<const T*>(a.k) + (size_t)ks * rs + (size_t)h * D;
   const T* vb = static_cast<const T*>(a.v) + (size_t)ks * rs + (size_t)h * D;
 
   // K rows are stored swap23-permuted, V rows in order (see the header note)
-  TileDma<T, D, C::BN, true> kdma;
-  TileDma<T, D, C::BN, false> vdma;
+  TileDma<T, D, C::BN, true, C::NT> kdma;
+  TileDma<T, D, C::BN, false, C::NT> vdma;
   kdma.init(rs, tid);
   vdma.init(rs, tid);
 
@@ -285,7 +301,9 @@ __global__ __launch_bounds__(256, (D >= 128 && sizeof(T) == 4) ? 1 : 2) void fwd
 
 // Explicit instantiation of every variant (the host pass otherwise left some
 // kernel stubs undefined).
-#define JFA_FWD_INST(T, D, ACT) template __global__ void fwd_kernel<T, D, ACT>(FwdArgs);
+#define JFA_FWD_INST(T, D, ACT)                                 \
+  template __global__ void fwd_kernel<T, D, ACT, false>(FwdArgs); \
+  template __global__ void fwd_kernel<T, D, ACT, true>(FwdArgs);
 JFA_FWD_INST(__bf16, 32, 0) JFA_FWD_INST(__bf16, 64, 0) JFA_FWD_INST(__bf16, 128, 0)
 JFA_FWD_INST(__bf16, 32, 1) JFA_FWD_INST(__bf16, 64, 1) JFA_FWD_INST(__bf16, 128, 1)
 JFA_FWD_INST(float, 32, 0) JFA_FWD_INST(float, 64, 0) JFA_FWD_INST(float, 128, 0)
@@ -293,26 +311,33 @@ JFA_FWD_INST(float, 32, 1) JFA_FWD_INST(float, 64, 1) JFA_FWD_INST(float, 128, 1
 #undef JFA_FWD_INST
 
 template <typename T, int D, int ACT>
-static hipError_t launch_one(const FwdArgs& a, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<T, D, ACT>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+static hipError_t launch_one(const FwdArgs& a, int64_t grid, bool short_batch, hipStream_t stream) {
+  if (short_batch)
+    hipLaunchKernelGGL((fwd_kernel<T, D, ACT, true>), dim3((unsigned)grid), dim3(FwdCfg<T, D, true>::NT), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, ACT, false>), dim3((unsigned)grid), dim3(FwdCfg<T, D, false>::NT), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int ACT>
-static hipError_t launch_d(const FwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
+static hipError_t launch_d(const FwdArgs& a, int head_dim, int64_t grid, bool short_batch, hipStream_t stream) {
   switch (head_dim) {
-    case 32: return launch_one<T, 32, ACT>(a, grid, stream);
-    case 64: return launch_one<T, 64, ACT>(a, grid, stream);
-    case 128: return launch_one<T, 128, ACT>(a, grid, stream);
+    case 32: return launch_one<T, 32, ACT>(a, grid, short_batch, stream);
+    case 64: return launch_one<T, 64, ACT>(a, grid, short_batch, stream);
+    case 128: return launch_one<T, 128, ACT>(a, grid, short_batch, stream);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_t grid, bool short_batch,
+                      hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  if (dtype == 0) return act == 0 ? launch_d<__bf16, 0>(a, head_dim, grid, stream)
-                                  : launch_d<__bf16, 1>(a, head_dim, grid, stream);
-  return act == 0 ? launch_d<float, 0>(a, head_dim, grid, stream) : launch_d<float, 1>(a, head_dim, grid, stream);
+  if (dtype == 0) return act == 0 ? launch_d<__bf16, 0>(a, head_dim, grid, short_batch, stream)
+                                  : launch_d<__bf16, 1>(a, head_dim, grid, short_batch, stream);
+  return act == 0 ? launch_d<float, 0>(a, head_dim, grid, short_batch, stream)
+                  : launch_d<float, 1>(a, head_dim, grid, short_batch, stream);
 }
 
 }  // namespace jfa

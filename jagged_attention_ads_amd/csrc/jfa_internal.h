@@ -110,7 +110,10 @@ struct FwdArgs {
   float scale_log2;   // scale * log2(e)
 };
 
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_t grid, hipStream_t stream);
+// short_batch: every sequence has at most 64 queries and 64 keys (the
+// two-wave variant of the kernel).
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_t grid, bool short_batch,
+                      hipStream_t stream);
 
 // BlockAttention: the runs of `block` tokens of every sequence as offsets
 // (see blocks.hip).

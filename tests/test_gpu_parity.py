@@ -188,6 +188,28 @@ def test_short_sequences_dq_in_dkdv(name, monkeypatch):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", [n for n in sorted(SHORT) if n.startswith("all_short")])
+def test_short_batch_forward_variant(name, monkeypatch):
+    """A batch whose sequences all have at most 64 queries and keys runs the
+    two-wave forward variant: within the gates of the oracle, and bitwise
+    equal to the four-wave kernel (JFA_FWD_SHORT=0), whose per-row
+    arithmetic it shares."""
+    base, over, lq, lk = SHORT[name]
+    wl = dataclasses.replace(WORKLOADS[base], **over)
+    b = make_batch(wl, 300 + sorted(SHORT).index(name), q_lengths=lq, kv_lengths=lk, with_dout=False)
+    d = Dev(b)
+    monkeypatch.delenv("JFA_FWD_SHORT", raising=False)
+    out, lse = d.forward()
+    monkeypatch.setenv("JFA_FWD_SHORT", "0")
+    out4, lse4 = d.forward()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_fwd(b)
+    check_forward(out, lse, ref_out, ref_lse, b.workload.activation)
+    assert torch.equal(out.view(torch.int16), out4.view(torch.int16))
+    if lse is not None:
+        assert torch.equal(lse.view(torch.int32), lse4.view(torch.int32))
+
+
 # ------------------------------------------------------------------ full sizes, sampled
 
 def _sample(b, rng, n=3):
