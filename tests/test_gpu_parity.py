@@ -162,6 +162,10 @@ SHORT = {
     "softmax_noncausal_d64": ("cross_asym", dict(heads=3), SHORT_Q, SHORT_K),
     "all_short_causal": ("selfattn_causal", {}, ALL_SHORT_Q, ALL_SHORT_K),
     "all_short_silu": ("gdpa_silu", dict(causal=False), ALL_SHORT_Q, ALL_SHORT_K),
+    # no room for the fused dQ in these dK/dV kernels: two passes, while the
+    # forward still takes its two-wave variant
+    "all_short_fp32_d128": ("tiny_fp32", dict(head_dim=128, causal=True), ALL_SHORT_Q, ALL_SHORT_K),
+    "all_short_bf16_d32": ("selfattn_causal", dict(head_dim=32, heads=3), ALL_SHORT_Q, ALL_SHORT_K),
 }
 
 
@@ -185,7 +189,7 @@ def test_short_sequences_dq_in_dkdv(name, monkeypatch):
     torch.cuda.synchronize()
     check_backward(fused, oracle_bwd(b))
     for x, y in zip(fused, apart):
-        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
 
 @pytest.mark.parametrize("name", [n for n in sorted(SHORT) if n.startswith("all_short")])
@@ -205,7 +209,7 @@ def test_short_batch_forward_variant(name, monkeypatch):
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle_fwd(b)
     check_forward(out, lse, ref_out, ref_lse, b.workload.activation)
-    assert torch.equal(out.view(torch.int16), out4.view(torch.int16))
+    assert torch.equal(out.view(torch.uint8), out4.view(torch.uint8))
     if lse is not None:
         assert torch.equal(lse.view(torch.int32), lse4.view(torch.int32))
 
