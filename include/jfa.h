@@ -114,7 +114,9 @@ size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_
  * sequence is short (max_q_len <= 64 and max_kv_len <= 64) the attention
  * kernel runs as a two-wave variant that fits twice the work items per
  * compute unit; its outputs equal the four-wave kernel's bit for bit, and
- * JFA_FWD_SHORT=0 in the environment keeps the four-wave kernel. */
+ * JFA_FWD_SHORT=0 in the environment keeps the four-wave kernel.  That
+ * variant takes one workgroup per (sequence, head) straight from the
+ * offsets, and no work list is built, unless JFA_CHECK_OFFSETS=1. */
 int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                 const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim,
                 int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale,

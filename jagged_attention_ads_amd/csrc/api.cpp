@@ -258,10 +258,20 @@ int jfa_forward_profiled(const void* q, const void* k, const void* v, const int3
 
   char* ws = static_cast<char*>(workspace);
   hipError_t e;
+  // every sequence at most 64 queries and 64 keys: the two-wave variant
+  // (JFA_FWD_SHORT=0 keeps the four-wave kernel, for tests and timing).
+  // Its items all cost at most one key block, so without the offsets check
+  // it takes one block per (sequence, head) and no work list is built.
+  const char* fs = std::getenv("JFA_FWD_SHORT");
+  const bool short_batch =
+      !(fs && fs[0] == '0' && fs[1] == 0) && max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kFwdBN;
+  const bool direct = short_batch && !check_offsets_enabled() && (int64_t)batch * heads <= INT32_MAX;
   if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
-  e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nb, ws + L.off_wq, L.wq,
-                        offset_check(ws, total_q, total_kv, max_q_len, max_kv_len), stream);
-  if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+  if (!direct) {
+    e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nb, ws + L.off_wq, L.wq,
+                          offset_check(ws, total_q, total_kv, max_q_len, max_kv_len), stream);
+    if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+  }
   if ((e = record(events, 1, stream)) != hipSuccess) return hip_fail(e, "event record");
   jfa::FwdArgs a{};
   a.q = q;
@@ -269,20 +279,17 @@ int jfa_forward_profiled(const void* q, const void* k, const void* v, const int3
   a.v = v;
   a.qo = q_offsets;
   a.ko = kv_offsets;
-  a.meta = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + L.wq.meta_off);
+  a.meta = direct ? nullptr : reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + L.wq.meta_off);
   a.out = out;
   a.lse = lse;
   a.heads = heads;
   a.total_q = total_q;
+  a.total_kv = total_kv;
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  // every sequence at most 64 queries and 64 keys: the two-wave variant
-  // (JFA_FWD_SHORT=0 keeps the four-wave kernel, for tests and timing)
-  const char* fs = std::getenv("JFA_FWD_SHORT");
-  const bool short_batch =
-      !(fs && fs[0] == '0' && fs[1] == 0) && max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kFwdBN;
-  e = jfa::launch_fwd(a, head_dim, dtype, activation, L.wq.capacity, short_batch, stream);
+  e = jfa::launch_fwd(a, head_dim, dtype, activation, direct ? (int64_t)batch * heads : L.wq.capacity, short_batch,
+                      stream);
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
   if ((e = record(events, 2, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;

@@ -52,8 +52,20 @@ __global__ __launch_bounds__((FwdCfg<T, D, SHORT>::NT), (FwdCfg<T, D, SHORT>::WP
   char* const kslot0 = smem;
   char* const vslot0 = smem + C::SLOTS * C::KT;
 
-  const ItemMeta m = a.meta[blockIdx.x];   // one load: offsets, lengths, head, tile
-  if (m.lq < 0) return;                       // past the item count
+  ItemMeta m;
+  if (SHORT && a.meta == nullptr) {
+    // no work list: every item costs at most one key block, so the order
+    // hardly matters; block b * heads + h takes sequence b, head h (offsets
+    // outside the tensors, possible only when the offsets break their
+    // contract, are left alone)
+    const int b = (int)blockIdx.x / a.heads, hh = (int)blockIdx.x % a.heads;
+    const int q0 = a.qo[b], q1 = a.qo[b + 1], k0 = a.ko[b], k1 = a.ko[b + 1];
+    if (q0 < 0 || q1 <= q0 || q1 > a.total_q || k0 < 0 || k1 < k0 || k1 > a.total_kv) return;
+    m = ItemMeta{q0, q1 - q0, k0, k1 - k0, hh, 0, b, 0};
+  } else {
+    m = a.meta[blockIdx.x];   // one load: offsets, lengths, head, tile
+    if (m.lq < 0) return;     // past the item count
+  }
   const int qs = m.qs, lq = m.lq, ks = m.ks, lk = m.lk, h = m.head, t = m.tile;
   const int off = lk - lq;   // causal: query i sees keys j <= i + off
 

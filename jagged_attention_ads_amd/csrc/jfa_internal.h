@@ -100,18 +100,22 @@ struct FwdArgs {
   const void* v;
   const int32_t* qo;
   const int32_t* ko;
-  const ItemMeta* meta;     // query-tile records
+  const ItemMeta* meta;     // query-tile records; null: one item per (sequence, head), block
+                            // b * heads + h (batches of short sequences only, see launch_fwd)
   void* out;
   float* lse;
   int32_t heads;
   int32_t total_q;
+  int32_t total_kv;
   int32_t causal;
   float scale;        // softmax / silu score scale
   float scale_log2;   // scale * log2(e)
 };
 
 // short_batch: every sequence has at most 64 queries and 64 keys (the
-// two-wave variant of the kernel).
+// two-wave variant of the kernel).  With a.meta null (short_batch only) the
+// grid is batch * heads, one block per (sequence, head), and no work list
+// is read.
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_t grid, bool short_batch,
                       hipStream_t stream);
 
