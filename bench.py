@@ -12,9 +12,11 @@ the host, copied to HBM before timing, and stay resident.  Prints one JSON
 line: useful TFLOPS counted on the visible (query, key) pairs of the real,
 unpadded tokens -- 4*d FLOPs per pair forward, 10*d backward -- the split
 into forward and backward, the share of the bf16 MFMA peak, per-kernel
-durations from HIP events recorded between the library's launches, the
-roofline position of the dominant kernel, and the CPU oracle timed on a
-bounded sample of the same batch.
+durations from HIP events recorded between the library's launches (in an
+untimed pass: each event adds a few microseconds between launches), the
+roofline position of the dominant kernel (timed by the only two events
+inside the timed steps), and the CPU oracle timed on a bounded sample of
+the same batch.
 """
 
 import argparse
@@ -355,26 +357,19 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # Per-kernel breakdown: an untimed pass of K steps with an event between
+    # every two launches.  Each recorded event adds a few microseconds
+    # between launches, so the timed pass below records only the two around
+    # the dominant kernel.
     ef = [ev.create(3) for _ in range(K)]
     eb = [ev.create(5) for _ in range(K)] if run_bwd else []
-    edge = ev.create(2)
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
-    torch.cuda.synchronize()
-    ev.lib.hipEventRecord(edge[0], stream)
     for i in range(K):
-        if flush_buf is not None:
-            flush_buf.fill_(i & 0xff)
         if derive:
             derive()
         fwd(ef[i])
         if run_bwd:
             bwd(eb[i])
-    ev.lib.hipEventRecord(edge[1], stream)
     torch.cuda.synchronize()
-    total_ms = ev.ms(edge[0], edge[1])
-    ms_step = total_ms / K
-    if flush_buf is not None:   # each step from its first to its last event
-        ms_step = float(np.mean([ev.ms(ef[i][0], (eb[i][4] if run_bwd else ef[i][2])) for i in range(K)]))
 
     def avg(lst, a, b):
         return float(np.mean([ev.ms(e[a], e[b]) for e in lst])) if lst else 0.0
@@ -387,18 +382,55 @@ def main():
         bwd_ms = avg(eb, 0, 4)
 
     pairs = int(visible_pairs(q_lens, kv_lens, wl.causal).sum())
+    n_blk = ds_blocks(q_lens, kv_lens, wl.causal) if run_bwd else 0
+    short = short_split(q_lens, kv_lens, wl.causal) if run_bwd and fuse_short else (0, 0, 0, 0)
+    acct = kernel_accounting(wl, T_q, T_k, pairs, n_blk, ds_path, short)
+    name = max((n for n in acct if n in kern_ms), key=lambda n: kern_ms[n])   # the dominant kernel
+    side, i0, i1 = {"sched_q": (0, 0, 1), "fwd": (0, 1, 2), "bwd_sched": (1, 0, 1), "bwd_stats": (1, 1, 2),
+                    "bwd_dkdv": (1, 2, 3), "bwd_dq": (1, 3, 4)}[name]
+
+    # Timed pass: exactly K steps between two events and synchronisations;
+    # inside them only the events around the dominant kernel (and with
+    # --flush, each step's start and end)
+    dom_a, dom_b = ev.create(K), ev.create(K)
+    tev = []
+    for i in range(K):
+        arr = (ctypes.c_void_p * (3 if side == 0 else 5))()
+        arr[i0], arr[i1] = dom_a[i], dom_b[i]
+        tev.append(arr)
+    st_a, st_b = (ev.create(K), ev.create(K)) if args.flush else (None, None)
+    edge = ev.create(2)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
+    torch.cuda.synchronize()
+    ev.lib.hipEventRecord(edge[0], stream)
+    for i in range(K):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xff)
+        if derive:
+            derive()
+        if st_a is not None:
+            ev.lib.hipEventRecord(st_a[i], stream)
+        fwd(tev[i] if side == 0 else None)
+        if run_bwd:
+            bwd(tev[i] if side == 1 else None)
+        if st_b is not None:
+            ev.lib.hipEventRecord(st_b[i], stream)
+    ev.lib.hipEventRecord(edge[1], stream)
+    torch.cuda.synchronize()
+    total_ms = ev.ms(edge[0], edge[1])
+    ms_step = total_ms / K
+    if st_a is not None:   # each step from its start to its end, without the flush
+        ms_step = float(np.mean([ev.ms(st_a[i], st_b[i]) for i in range(K)]))
+    dom_ms = float(np.mean([ev.ms(dom_a[i], dom_b[i]) for i in range(K)]))
+
     useful_fwd = 4.0 * D * H * pairs
     useful_bwd = 10.0 * D * H * pairs if run_bwd else 0.0
     value = (useful_fwd + useful_bwd) / (ms_step * 1e-3) / 1e12
     fwd_tf = useful_fwd / (fwd_ms * 1e-3) / 1e12
     bwd_tf = useful_bwd / (bwd_ms * 1e-3) / 1e12 if run_bwd else None
 
-    # roofline of the dominant kernel
-    n_blk = ds_blocks(q_lens, kv_lens, wl.causal) if run_bwd else 0
-    short = short_split(q_lens, kv_lens, wl.causal) if run_bwd and fuse_short else (0, 0, 0, 0)
-    acct = kernel_accounting(wl, T_q, T_k, pairs, n_blk, ds_path, short)
-    name = max((n for n in acct if n in kern_ms), key=lambda n: kern_ms[n])
-    t_s = kern_ms[name] * 1e-3
+    # roofline of the dominant kernel, timed inside the timed pass
+    t_s = dom_ms * 1e-3
     ai = acct[name]["flops"] / acct[name]["bytes"]
     digest = kernel_source_digest()
     if ai < RIDGE:
@@ -408,7 +440,7 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(name, digest, wl.name)
-    roof.update({"kernel": name, "avg_launch_us": kern_ms[name] * 1e3,
+    roof.update({"kernel": name, "avg_launch_us": dom_ms * 1e3,
                  "algorithmic_bytes": acct[name]["bytes"], "algorithmic_flops": acct[name]["flops"],
                  "arith_intensity": ai, "mfma_frac": acct[name]["flops"] / t_s / 1e12 / PEAK_BF16_TFLOPS})
 
@@ -426,11 +458,12 @@ def main():
         "fwd_tflops": fwd_tf, "fwd_pct_peak": 100.0 * fwd_tf / PEAK_BF16_TFLOPS,
         "bwd_tflops": bwd_tf, "bwd_pct_peak": (100.0 * bwd_tf / PEAK_BF16_TFLOPS) if bwd_tf else None,
         "kernel_us": {k_: v_ * 1e3 for k_, v_ in kern_ms.items()},
+        "kernel_us_from": "an untimed pass of the same steps with an event between every two launches",
         "cache": "flushed before each step (512 MiB written)" if args.flush else "warm (steps back to back)",
         "kernel_source_digest": digest,
         "roofline": roof,
     }
-    for lst in ef + eb + [edge]:
+    for lst in ef + eb + [edge, dom_a, dom_b] + ([st_a, st_b] if st_a is not None else []):
         ev.destroy(lst)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)

@@ -154,8 +154,10 @@ int jfa_backward(const void* q, const void* k, const void* v, const void* out, c
  * [1] before the attention kernel, [2] after it.  Backward: 5 events --
  * [0] start, [1] after the work-list builder (both lists, one launch),
  * [2] after the row statistics kernel (right after [1] for SiLU),
- * [3] after the dK/dV kernel, [4] after the dQ kernel.  Events are not
- * recorded when the call is a no-op or is rejected. */
+ * [3] after the dK/dV kernel, [4] after the dQ kernel.  A NULL entry of
+ * `events` skips that point (each recorded event can add a few microseconds
+ * between launches).  Events are not recorded when the call is a no-op or
+ * is rejected. */
 int jfa_forward_profiled(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                          const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
                          int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation,

@@ -108,9 +108,10 @@ bool fuse_short_wanted(int32_t max_q_len, int32_t max_kv_len) {
   return max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kBwdBN;
 }
 
-// Records events[i] on the stream when the caller asked for stage events.
+// Records events[i] on the stream when the caller asked for stage events
+// (a null entry skips that point).
 hipError_t record(hipEvent_t* events, int i, hipStream_t stream) {
-  if (!events) return hipSuccess;
+  if (!events || !events[i]) return hipSuccess;
   return hipEventRecord(events[i], stream);
 }
 
