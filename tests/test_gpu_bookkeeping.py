@@ -312,3 +312,50 @@ def test_no_keys_at_all(recompute, monkeypatch):
         assert (out == 0).all() and (dq == 0).all()
         assert torch.isneginf(lse).all()
         assert dk.shape == (0, H, D) and dv.shape == (0, H, D)
+
+
+def test_profiled_calls_with_partial_events():
+    """jfa_forward_profiled / jfa_backward_profiled record only the non-NULL
+    entries of their events array (the timed steps of the benchmark keep two
+    of them), and give the plain calls' results bit for bit."""
+    import ctypes
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "bench", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    b = make_batch("selfattn_causal", 5, batch=6)
+    d = Dev(b)
+    out, lse = d.forward()
+    grads = d.backward(out, lse)
+    T_q, H, D = d.q.shape
+    B = len(b.q_lengths)
+    L = jfa.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ev = bench.HipEvents()
+    pair = ev.create(2)
+    fe = (ctypes.c_void_p * 3)()
+    fe[1], fe[2] = pair[0], pair[1]
+    be = (ctypes.c_void_p * 5)()
+    be[2], be[3] = pair[0], pair[1]
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    dq2, dk2, dv2 = (torch.empty_like(g) for g in grads)
+    ws_f = jfa.workspace(B, H, D, T_q, d.k.shape[0], d.mk, d.q.dtype, 0, d.q.device)
+    ws_b = jfa.workspace(B, H, D, T_q, d.k.shape[0], d.mk, d.q.dtype, 1, d.q.device)
+    st = L.jfa_forward_profiled(P(d.q), P(d.k), P(d.v), P(d.qo), P(d.ko), B, H, D, T_q, d.k.shape[0], d.mq, d.mk,
+                                d.scale, 0, 1, 0, P(out2), P(lse2), P(ws_f), ws_f.numel(), stream,
+                                ctypes.cast(fe, ctypes.c_void_p))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert ev.ms(pair[0], pair[1]) > 0
+    st = L.jfa_backward_profiled(P(d.q), P(d.k), P(d.v), P(out2), P(d.do), P(lse2), P(d.qo), P(d.ko), B, H, D, T_q,
+                                 d.k.shape[0], d.mq, d.mk, d.scale, 0, 1, 0, P(dq2), P(dk2), P(dv2), P(ws_b),
+                                 ws_b.numel(), stream, ctypes.cast(be, ctypes.c_void_p))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert ev.ms(pair[0], pair[1]) > 0
+    ev.destroy(pair)
+    for x, y in zip((out, lse) + tuple(grads), (out2, lse2, dq2, dk2, dv2)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
