@@ -7,16 +7,23 @@ A step is one pass of the whole hot path over one batch: the forward call
 (work-list build + attention kernel) and the backward call (work-list
 builds, softmax row statistics, dK/dV kernel -- which also stores the dS
 blocks, and writes the dQ of sequences of at most 64 tokens -- and dQ
-kernel).  Inputs are generated on
-the host, copied to HBM before timing, and stay resident.  Prints one JSON
-line: useful TFLOPS counted on the visible (query, key) pairs of the real,
-unpadded tokens -- 4*d FLOPs per pair forward, 10*d backward -- the split
-into forward and backward, the share of the bf16 MFMA peak, per-kernel
-durations from HIP events recorded between the library's launches (in an
-untimed pass: each event adds a few microseconds between launches), the
-roofline position of the dominant kernel (timed by the only two events
-inside the timed steps), and the CPU oracle timed on a bounded sample of
-the same batch.
+kernel).  Inputs are generated on the host, copied to HBM before timing,
+and stay resident.
+
+Timing: W untimed warm-up steps, then K timed steps (default 10 and 50).
+Before each timed step a 512 MiB buffer is overwritten, which evicts L2 and
+the last-level cache; each step is timed by its own HIP events (the flush
+excluded) and the headline is the median step, with p10 and p90.  The same
+K steps back to back (warm caches) are reported beside it, labelled.
+
+Prints one JSON line: useful TFLOPS counted on the visible (query, key)
+pairs of the real, unpadded tokens -- 4*d FLOPs per pair forward, 10*d
+backward -- the forward and backward passes against their targets,
+per-kernel durations (from untimed steps with an event between every two
+launches), the roofline position of the dominant kernel (its algorithmic
+bytes: the method's own tensors, each once; timed by two events inside the
+timed steps), the mean over further seeds, and the CPU oracle timed on the
+host's cores.
 """
 
 import argparse
@@ -141,7 +148,11 @@ def short_split(q_lengths, kv_lengths, causal):
 
 def kernel_accounting(wl, T_q, T_k, pairs_total, n_ds_blocks, ds_path, short=(0, 0, 0, 0)):
     """Algorithmic FLOPs (the products each kernel must execute per visible
-    pair) and bytes (every tensor the kernel must touch, once) per launch.
+    pair) and algorithmic bytes per launch: the method's own tensors the
+    kernel's step touches, each once -- Q, K, V, O, dO, dQ, dK, dV, lse and
+    delta.  Re-reads and the library's own intermediates are not algorithmic:
+    the dS blocks that the dK/dV pass stores and the dQ pass reads back are
+    reported apart, as `ds_store_bytes` (workspace traffic, once each way).
     `short` is short_split of the sequences whose dQ the dK/dV pass forms
     (all zeros when it forms none): their dS stays on chip, and the dQ pass
     does not touch them."""
@@ -151,23 +162,26 @@ def kernel_accounting(wl, T_q, T_k, pairs_total, n_ds_blocks, ds_path, short=(0,
     q_bytes, k_bytes = T_q * H * d * es, T_k * H * d * es
     lq_bytes, lk_bytes = (T_q - sq) * H * d * es, (T_k - sk) * H * d * es   # sequences the dQ pass takes
     row_f32 = T_q * H * 4
-    ds_bytes = (n_ds_blocks - sb) * H * 32 * 32 * es if ds_path else 0
     soft = wl.activation == "softmax"
+    ds_bytes = (n_ds_blocks - sb) * H * 32 * 32 * es if ds_path else 0
     acc = {
+        # reads Q, K, V; writes O (and lse)
         "fwd": dict(flops=4 * d * H * pairs_total,
                     bytes=q_bytes + 2 * k_bytes + q_bytes + (row_f32 if soft else 0)),
-        # reads Q, dO, K, V (and lse2, delta); writes dK, dV, the dS blocks
-        # and the short sequences' dQ
+        # reads Q, dO, K, V (and lse, delta); writes dK, dV and the short
+        # sequences' dQ
         "bwd_dkdv": dict(flops=8 * d * H * pairs_total + 2 * d * H * sp,
-                         bytes=2 * q_bytes + 2 * k_bytes + (2 * row_f32 if soft else 0) + 2 * k_bytes + ds_bytes
-                         + sq * H * d * es),
+                         bytes=2 * q_bytes + 2 * k_bytes + (2 * row_f32 if soft else 0) + 2 * k_bytes
+                         + sq * H * d * es,
+                         ds_store_bytes=ds_bytes),
     }
-    if ds_path:   # dQ = scale * dS K: reads the dS blocks and K, writes dQ
-        acc["bwd_dq"] = dict(flops=2 * d * H * (pairs_total - sp), bytes=ds_bytes + lk_bytes + lq_bytes)
-    else:         # recomputes S, P, dP, dS: reads Q, dO, K, V, lse2, delta, writes dQ
+    if ds_path:   # dQ = scale * dS K: reads K, writes dQ (plus the dS blocks: workspace)
+        acc["bwd_dq"] = dict(flops=2 * d * H * (pairs_total - sp), bytes=lk_bytes + lq_bytes,
+                             ds_store_bytes=ds_bytes)
+    else:         # recomputes S, P, dP, dS: reads Q, dO, K, V, lse, delta, writes dQ
         acc["bwd_dq"] = dict(flops=6 * d * H * (pairs_total - sp),
                              bytes=3 * lq_bytes + 2 * lk_bytes + (2 * (T_q - sq) * H * 4 if soft else 0))
-    if soft:      # reads O, dO and lse, writes lse2 and delta
+    if soft:      # reads O, dO and lse, writes delta (and lse in log2 units)
         acc["bwd_stats"] = dict(flops=2 * d * H * T_q, bytes=2 * q_bytes + 3 * row_f32)
     return acc
 
@@ -187,44 +201,134 @@ def stored_traffic(kernel, digest, workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(batch, budget_s):
-    """The CPU oracle, as it is, on the first sequences of the same batch
-    until about `budget_s` seconds of work; useful TFLOPS under the same
-    accounting."""
-    import oracle
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers():
+    """Worker processes of the CPU baseline: every core this process may run
+    on, at most 16 (a GPU's share of the host on the boxes this runs on)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+# The batch the CPU-baseline workers read: set in the parent before the pool
+# forks, so that every worker sees it without a copy.
+_CPU_BATCH = {}
+
+
+def _cpu_worker_init():
+    # single-threaded BLAS in every worker: the pool provides the parallelism
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        threads = 1
+        pass
+
+
+def _cpu_unit(arg):
+    """One (sequence, head) unit of the oracle: forward, or forward and
+    backward; returns its useful FLOPs."""
+    import oracle
+    b, h, with_bwd = arg
+    c = _CPU_BATCH
+    qo, ko, blk = c["qo"], c["ko"], c["block"]
+    sq, sk = slice(qo[b], qo[b + 1]), slice(ko[b], ko[b + 1])
+    one_q, one_k = np.array([0, qo[b + 1] - qo[b]]), np.array([0, ko[b + 1] - ko[b]])
+    hs = slice(h, h + 1)
+    q, k, v = c["q"][sq, hs], c["k"][sk, hs], c["v"][sk, hs]
+    oracle.attention_fwd(q, k, v, one_q, one_k, c["scale"], c["act"], c["causal"], block=blk)
+    if with_bwd:
+        oracle.attention_bwd(q, k, v, c["do"][sq, hs], one_q, one_k, c["scale"], c["act"], c["causal"], block=blk)
+    return (14 if with_bwd else 4) * c["d"] * c["pairs"][b]
+
+
+def cpu_baseline(batch, budget_s):
+    """The CPU oracle, as it is, on the host: worker processes with
+    single-threaded BLAS over (sequence, head) units handed out longest
+    first, forward alone and forward + backward timed separately, plus the
+    same on one core.  The sample is every s-th sequence of the batch, s
+    chosen from a one-core calibration so that the pool runs about
+    `budget_s` seconds; useful TFLOPS under the GPU's accounting.  Runs
+    before anything touches the GPU (the pool forks this process)."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
     wl = batch.workload
-    s = 1.0 / math.sqrt(wl.head_dim)
-    q, k, v = batch.f64("q"), batch.f64("k"), batch.f64("v")
-    do = batch.f64("dout") if batch.dout is not None else None
-    qo, ko = batch.q_offsets, batch.kv_offsets
+    qo, ko = np.asarray(batch.q_offsets), np.asarray(batch.kv_offsets)
     blk = wl.block
     if blk:
         pairs = np.array([visible_pairs(block_runs([n], blk), block_runs([n], blk), wl.causal).sum()
                           for n in batch.q_lengths])
     else:
         pairs = visible_pairs(batch.q_lengths, batch.kv_lengths, wl.causal)
-    done, flops, t0 = 0, 0.0, time.perf_counter()
-    while done < len(pairs) and time.perf_counter() - t0 < budget_s:
-        b = done
-        sl_q, sl_k = slice(qo[b], qo[b + 1]), slice(ko[b], ko[b + 1])
-        one_q = np.array([0, qo[b + 1] - qo[b]])
-        one_k = np.array([0, ko[b + 1] - ko[b]])
-        oracle.attention_fwd(q[sl_q], k[sl_k], v[sl_k], one_q, one_k, s, wl.activation, wl.causal, block=blk)
-        if wl.backward and do is not None:
-            oracle.attention_bwd(q[sl_q], k[sl_k], v[sl_k], do[sl_q], one_q, one_k, s, wl.activation, wl.causal,
-                                 block=blk)
-        flops += (14 if wl.backward else 4) * wl.head_dim * wl.heads * pairs[b]
-        done += 1
-    el = time.perf_counter() - t0
+    _CPU_BATCH.update(q=batch.f64("q"), k=batch.f64("k"), v=batch.f64("v"),
+                      do=batch.f64("dout") if batch.dout is not None else None, qo=qo, ko=ko, block=blk,
+                      scale=1.0 / math.sqrt(wl.head_dim), act=wl.activation, causal=wl.causal, d=wl.head_dim,
+                      pairs=pairs)
+    B, H = len(pairs), wl.heads
+    with_bwd = bool(wl.backward and batch.dout is not None)
+    dense = (np.diff(qo) * np.diff(ko)).astype(np.float64)   # the oracle's work follows Lq * Lk
+    order = np.argsort(-dense, kind="stable")
+    workers = cpu_workers()
+
+    def one_core(seqs, bwd):
+        t0, f = time.perf_counter(), 0.0
+        with threadpool_limits(1):
+            for b in seqs:
+                for h in range(H):
+                    f += _cpu_unit((b, h, bwd))
+        return f, time.perf_counter() - t0
+
+    # one-core calibration on a spread of sequences (median-ish first)
+    calib = [int(b) for b in order[len(order) // 2::max(1, B // 8)]][:8]
+    _, t1 = one_core(calib, with_bwd)
+    rate = dense[calib].sum() * H / max(t1, 1e-9)   # dense pairs per second on one core
+    total_s = dense.sum() * H / rate / workers        # the whole batch on the pool
+    stride = max(1, int(math.ceil(total_s / (0.45 * budget_s))))
+    sample = [b for b in order if b % stride == 0]
+    ctx = mp.get_context("fork")
+    res = {}
+    for name, bwd in (("fwd", False), ("fwd_bwd", True)):
+        if bwd and not with_bwd:
+            continue
+        units = [(int(b), h, bwd) for b in sample for h in range(H)]   # longest first
+        with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+            t0 = time.perf_counter()
+            flops = float(sum(pool.imap_unordered(_cpu_unit, units, chunksize=1)))
+            el = time.perf_counter() - t0
+        res[name] = (flops, el)
+    # one core, on a sub-sample of the sample sized to about 0.15 * budget_s
+    # (fwd + bwd where it runs)
+    one_core_s = dense[sample].sum() * H / rate
+    sub = sample[::max(1, int(math.ceil(one_core_s / (0.15 * budget_s))))] or sample[:1]
+    fo, to = one_core(sub, with_bwd)
+    key = "fwd_bwd" if with_bwd else "fwd"
+    flops, el = res[key]
+    _CPU_BATCH.clear()
     return {
-        "value": flops / el / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
-        "sample": "fp64 NumPy oracle, %s on the first %d of %d sequences of the same batch (%.1f s, %.3g useful GFLOP)"
-                  % ("fwd+bwd" if wl.backward else "fwd", done, len(pairs), el, flops / 1e9),
+        "value": flops / el / 1e12, "unit": "TFLOPS", "cores": workers, "kind": "oracle",
+        "sample": "fp64 NumPy oracle, %s, every %d-th sequence of the same batch (%d of %d sequences x %d heads, "
+                  "%.3g useful GFLOP, %.1f s); %d worker processes with single-threaded BLAS, (sequence, head) "
+                  "units longest first" % ("fwd+bwd" if with_bwd else "fwd", stride, len(sample), B, H,
+                                           flops / 1e9, el, workers),
+        "cpu_model": cpu_model(),
+        "fwd_tflops": res["fwd"][0] / res["fwd"][1] / 1e12,
+        "fwd_bwd_tflops": (res["fwd_bwd"][0] / res["fwd_bwd"][1] / 1e12) if with_bwd else None,
+        "one_core_tflops": fo / to / 1e12,
+        "one_core_sample": "%s on %d sequences x %d heads (%.1f s)" % ("fwd+bwd" if with_bwd else "fwd", len(sub),
+                                                                       H, to),
     }
 
 
@@ -245,18 +349,198 @@ def calibrate_copy():
                       "dispatches": 3}))
 
 
+def pctl(xs, p):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), p))
+
+
+class Runner:
+    """One batch on the device with its outputs, workspaces and the two
+    library calls of a step (through the C ABI's profiled entry points, which
+    record caller events between launches)."""
+
+    def __init__(self, wl, batch, dev):
+        import torch
+        from jagged_attention_ads_amd import jfa
+        self.torch, self.jfa = torch, jfa
+        self.wl, self.batch = wl, batch
+        T_q, T_k, H, D = int(batch.q_offsets[-1]), int(batch.kv_offsets[-1]), wl.heads, wl.head_dim
+        self.T_q, self.T_k, self.H, self.D = T_q, T_k, H, D
+
+        def to_dev(a):
+            if wl.dtype == "bf16":
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+        self.q, self.k, self.v, self.do = (to_dev(x) for x in (batch.q, batch.k, batch.v, batch.dout))
+        qo = torch.from_numpy(batch.q_offsets.astype(np.int32)).to(dev)
+        ko = torch.from_numpy(batch.kv_offsets.astype(np.int32)).to(dev)
+        mq, mk = int(batch.q_lengths.max()), int(batch.kv_lengths.max())
+        self.scale = 1.0 / math.sqrt(D)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((H, T_q), dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        B = len(batch.q_lengths)
+        L = self.L = jfa.lib()
+        P = self.P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.derive = None
+        self.q_lens, self.kv_lens = batch.q_lengths, batch.kv_lengths
+        if wl.block:
+            # BlockAttention: the runs of wl.block tokens as sequences, derived
+            # on the device from the sequences' offsets in every step
+            seq_off, n_seq = qo, B
+            n_runs = L.jfa_block_offsets_count(n_seq, T_q, wl.block)
+            runs = torch.empty(n_runs, dtype=torch.int32, device=dev)
+
+            def derive():
+                st = L.jfa_block_offsets(P(seq_off), n_seq, T_q, wl.block, P(runs), n_runs, self.stream)
+                if st != 0:
+                    raise jfa.JfaError(st, L.jfa_last_error().decode())
+            self.derive = derive
+            qo = ko = runs
+            B = n_runs - 1
+            mq = mk = min(wl.block, mq)
+            self.q_lens = self.kv_lens = block_runs(batch.q_lengths, wl.block)
+        self.qo, self.ko, self.B, self.mq, self.mk = qo, ko, B, mq, mk
+        self.ws_f = jfa.workspace(B, H, D, T_q, T_k, mk, self.q.dtype, False, dev)
+        self.ws_b = jfa.workspace(B, H, D, T_q, T_k, mk, self.q.dtype, True, dev)
+        # the dK/dV pass stores dS and the dQ pass reads it, unless switched
+        # off or the store was left out of the workspace
+        self.ds_path = (os.environ.get("JFA_BWD_DS") != "0"
+                        and self.ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, mk, self.q.dtype, 2))
+        # the dK/dV pass writes the dQ of short sequences (bf16, d 64 or 128:
+        # where its LDS has room) when every sequence is short, or always with
+        # JFA_BWD_FUSE_SHORT=2; never with 0
+        fuse_mode = os.environ.get("JFA_BWD_FUSE_SHORT", "1")
+        self.fuse_short = (fuse_mode != "0" and wl.dtype == "bf16" and D in (64, 128)
+                           and (fuse_mode == "2" or max(mq, mk) <= 64))
+        self.act = jfa.ACTIVATIONS[wl.activation]
+        self.dt = jfa.DTYPES[self.q.dtype]
+        self.lse_arg = self.lse if wl.activation == "softmax" else None
+        self.run_bwd = wl.backward
+
+    def fwd(self, events):
+        st = self.L.jfa_forward_profiled(
+            self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.qo), self.P(self.ko), self.B, self.H,
+            self.D, self.T_q, self.T_k, self.mq, self.mk, self.scale, self.act, int(self.wl.causal), self.dt,
+            self.P(self.out), self.P(self.lse_arg), self.P(self.ws_f), self.ws_f.numel(), self.stream,
+            ctypes.cast(events, ctypes.c_void_p) if events is not None else None)
+        if st != 0:
+            raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+
+    def bwd(self, events):
+        st = self.L.jfa_backward_profiled(
+            self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.out), self.P(self.do),
+            self.P(self.lse_arg), self.P(self.qo), self.P(self.ko), self.B, self.H, self.D, self.T_q, self.T_k,
+            self.mq, self.mk, self.scale, self.act, int(self.wl.causal), self.dt, self.P(self.dq), self.P(self.dk),
+            self.P(self.dv), self.P(self.ws_b), self.ws_b.numel(), self.stream,
+            ctypes.cast(events, ctypes.c_void_p) if events is not None else None)
+        if st != 0:
+            raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+
+    def step(self, ef=None, eb=None):
+        if self.derive:
+            self.derive()
+        self.fwd(ef)
+        if self.run_bwd:
+            self.bwd(eb)
+
+    def pairs(self):
+        return int(visible_pairs(self.q_lens, self.kv_lens, self.wl.causal).sum())
+
+
+def timed_steps(r, ev, K, flush_buf, dom=None):
+    """K steps, each timed by its own events (with flush_buf, the buffer is
+    overwritten before each step, outside its events), bracketed by a
+    synchronisation on both sides.  Events per step: the forward's start,
+    the backward's start, the backward's end (the forward's end for a
+    forward-only workload); `dom` = (side, i0, i1) adds the two events around
+    that kernel (side 0: the forward's event slots, 1: the backward's).
+    Returns per-step lists of milliseconds: step, fwd, bwd, dominant kernel,
+    and the whole timed region."""
+    nf, nb = 3, 5
+    evs = []
+    for _ in range(K):
+        ef, eb = (ctypes.c_void_p * nf)(), (ctypes.c_void_p * nb)()
+        made = ev.create(5)
+        ef[0] = made[0]
+        if r.run_bwd:
+            eb[0], eb[4] = made[1], made[2]
+        else:
+            ef[2] = made[2]
+        if dom is not None:
+            arr = ef if dom[0] == 0 else eb
+            # the two slots may coincide with the step events (e.g. forward-only)
+            arr[dom[1]] = arr[dom[1]] or made[3]
+            arr[dom[2]] = arr[dom[2]] or made[4]
+        evs.append((ef, eb, made))
+    edge = ev.create(2)
+    r.torch.cuda.synchronize()
+    ev.lib.hipEventRecord(edge[0], r.stream)
+    for i in range(K):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xff)
+        ef, eb, _ = evs[i]
+        r.step(ef, eb if r.run_bwd else None)
+    ev.lib.hipEventRecord(edge[1], r.stream)
+    r.torch.cuda.synchronize()
+    out = {"step": [], "fwd": [], "bwd": [], "dom": [], "region": ev.ms(edge[0], edge[1])}
+    for ef, eb, made in evs:
+        end = eb[4] if r.run_bwd else ef[2]
+        out["step"].append(ev.ms(ef[0], end))
+        if r.run_bwd:
+            out["fwd"].append(ev.ms(ef[0], eb[0]))
+            out["bwd"].append(ev.ms(eb[0], eb[4]))
+        else:
+            out["fwd"].append(ev.ms(ef[0], ef[2]))
+        if dom is not None:
+            arr = ef if dom[0] == 0 else eb
+            out["dom"].append(ev.ms(arr[dom[1]], arr[dom[2]]))
+        ev.destroy(made)
+    ev.destroy(edge)
+    return out
+
+
+def kernel_breakdown(r, ev, K, flush_buf):
+    """Mean per-kernel milliseconds from K steps with an event between every
+    two launches (each event adds a few microseconds between launches, so
+    these steps are not the timed ones)."""
+    ef = [ev.create(3) for _ in range(K)]
+    eb = [ev.create(5) for _ in range(K)] if r.run_bwd else []
+    r.torch.cuda.synchronize()
+    for i in range(K):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xff)
+        r.step(ef[i], eb[i] if r.run_bwd else None)
+    r.torch.cuda.synchronize()
+
+    def avg(lst, a, b):
+        return float(np.mean([ev.ms(e[a], e[b]) for e in lst])) if lst else 0.0
+    kern = {"sched_q": avg(ef, 0, 1), "fwd": avg(ef, 1, 2)}
+    if r.run_bwd:
+        kern.update({"bwd_sched": avg(eb, 0, 1), "bwd_stats": avg(eb, 1, 2), "bwd_dkdv": avg(eb, 2, 3),
+                     "bwd_dq": avg(eb, 3, 4)})
+    for e in ef + eb:
+        ev.destroy(e)
+    return kern
+
+
+SLOTS = {"sched_q": (0, 0, 1), "fwd": (0, 1, 2), "bwd_sched": (1, 0, 1), "bwd_stats": (1, 1, 2),
+         "bwd_dkdv": (1, 2, 3), "bwd_dq": (1, 3, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="selfattn_causal")
     ap.add_argument("--seed", type=int, default=2)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--seed-mean", default="11-15",
+                    help="seeds a-b of the same workload whose flushed median steps are averaged ('' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--flush", action="store_true",
-                    help="before each step, overwrite a 512 MiB buffer (evicting the last-level cache and L2), "
-                         "and time each step by its own events, flush excluded")
+    ap.add_argument("--warm", action="store_true",
+                    help="headline from warm steps (no flush before each step); the default flushes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain elementwise copy of known size (256 MiB read + 256 MiB written per "
                          "dispatch, 3 dispatches), to scale the HBM byte counters")
@@ -269,204 +553,119 @@ def main():
               "(sequences are independent; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-    from jagged_attention_ads_amd import jfa
     from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch
-
     wl = WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
     batch = make_batch(wl, args.seed, with_dout=True)
-    T_q, T_k, H, D = int(batch.q_offsets[-1]), int(batch.kv_offsets[-1]), wl.heads, wl.head_dim
+    # the CPU oracle first: its worker pool forks this process, which must
+    # not have touched the GPU yet
+    cpu = None if args.no_cpu_baseline else cpu_baseline(batch, args.cpu_seconds)
 
-    def to_dev(a):
-        if wl.dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-    q, k, v, do = (to_dev(x) for x in (batch.q, batch.k, batch.v, batch.dout))
-    qo = torch.from_numpy(batch.q_offsets.astype(np.int32)).to(dev)
-    ko = torch.from_numpy(batch.kv_offsets.astype(np.int32)).to(dev)
-    mq, mk = int(batch.q_lengths.max()), int(batch.kv_lengths.max())
-    scale = 1.0 / math.sqrt(D)
-    out = torch.empty_like(q)
-    lse = torch.empty((H, T_q), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    B = len(batch.q_lengths)
-    L = jfa.lib()
-    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    derive = None
-    q_lens, kv_lens = batch.q_lengths, batch.kv_lengths
-    if wl.block:
-        # BlockAttention: the runs of wl.block tokens as sequences, derived on
-        # the device from the sequences' offsets in every step
-        seq_off, n_seq = qo, B
-        n_runs = L.jfa_block_offsets_count(n_seq, T_q, wl.block)
-        runs = torch.empty(n_runs, dtype=torch.int32, device=dev)
-
-        def derive():
-            st = L.jfa_block_offsets(P(seq_off), n_seq, T_q, wl.block, P(runs), n_runs, stream)
-            if st != 0:
-                raise jfa.JfaError(st, L.jfa_last_error().decode())
-        qo = ko = runs
-        B = n_runs - 1
-        mq = mk = min(wl.block, mq)
-        q_lens = kv_lens = block_runs(batch.q_lengths, wl.block)
-    ws_f = jfa.workspace(B, H, D, T_q, T_k, mk, q.dtype, False, dev)
-    ws_b = jfa.workspace(B, H, D, T_q, T_k, mk, q.dtype, True, dev)
-    # the dK/dV pass stores dS and the dQ pass reads it, unless switched off
-    # or the store was left out of the workspace
-    ds_path = (os.environ.get("JFA_BWD_DS") != "0"
-               and ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, mk, q.dtype, 2))
-    # the dK/dV pass writes the dQ of short sequences (bf16, d 64 or 128: where
-    # its LDS has room) when every sequence is short, or always with
-    # JFA_BWD_FUSE_SHORT=2; never with 0
-    fuse_mode = os.environ.get("JFA_BWD_FUSE_SHORT", "1")
-    fuse_short = (fuse_mode != "0" and wl.dtype == "bf16" and D in (64, 128)
-                  and (fuse_mode == "2" or max(mq, mk) <= 64))
-    act = jfa.ACTIVATIONS[wl.activation]
-    dt = jfa.DTYPES[q.dtype]
-    soft = wl.activation == "softmax"
-    lse_arg = lse if soft else None
-
-    def evp(events):
-        return ctypes.cast(events, ctypes.c_void_p) if events is not None else None
-
-    def fwd(events):
-        st = L.jfa_forward_profiled(P(q), P(k), P(v), P(qo), P(ko), B, H, D, T_q, T_k, mq, mk, scale, act,
-                                    int(wl.causal), dt, P(out), P(lse_arg), P(ws_f), ws_f.numel(), stream, evp(events))
-        if st != 0:
-            raise jfa.JfaError(st, L.jfa_last_error().decode())
-
-    def bwd(events):
-        st = L.jfa_backward_profiled(P(q), P(k), P(v), P(out), P(do), P(lse_arg), P(qo), P(ko), B, H, D, T_q, T_k,
-                                     mq, mk, scale, act, int(wl.causal), dt, P(dq), P(dk), P(dv), P(ws_b),
-                                     ws_b.numel(), stream, evp(events))
-        if st != 0:
-            raise jfa.JfaError(st, L.jfa_last_error().decode())
-
-
-    torch.cuda.synchronize()
+    import torch
+    dev = torch.device("cuda:0")
+    r = Runner(wl, batch, dev)
     ev = HipEvents()
-    run_bwd = wl.backward
+    flush_buf = None if args.warm else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    warm_buf = None
     for _ in range(args.warmup):
-        if derive:
-            derive()
-        fwd(None)
-        if run_bwd:
-            bwd(None)
+        r.step()
     torch.cuda.synchronize()
-
     K = args.steps
-    # Per-kernel breakdown: an untimed pass of K steps with an event between
-    # every two launches.  Each recorded event adds a few microseconds
-    # between launches, so the timed pass below records only the two around
-    # the dominant kernel.
-    ef = [ev.create(3) for _ in range(K)]
-    eb = [ev.create(5) for _ in range(K)] if run_bwd else []
-    for i in range(K):
-        if derive:
-            derive()
-        fwd(ef[i])
-        if run_bwd:
-            bwd(eb[i])
-    torch.cuda.synchronize()
 
-    def avg(lst, a, b):
-        return float(np.mean([ev.ms(e[a], e[b]) for e in lst])) if lst else 0.0
-    kern_ms = {"sched_q": avg(ef, 0, 1), "fwd": avg(ef, 1, 2)}
-    fwd_ms = avg(ef, 0, 2)
-    bwd_ms = 0.0
-    if run_bwd:
-        kern_ms.update({"bwd_sched": avg(eb, 0, 1), "bwd_stats": avg(eb, 1, 2), "bwd_dkdv": avg(eb, 2, 3),
-                        "bwd_dq": avg(eb, 3, 4)})
-        bwd_ms = avg(eb, 0, 4)
-
-    pairs = int(visible_pairs(q_lens, kv_lens, wl.causal).sum())
-    n_blk = ds_blocks(q_lens, kv_lens, wl.causal) if run_bwd else 0
-    short = short_split(q_lens, kv_lens, wl.causal) if run_bwd and fuse_short else (0, 0, 0, 0)
-    acct = kernel_accounting(wl, T_q, T_k, pairs, n_blk, ds_path, short)
+    # per-kernel breakdown (untimed steps, flushed like the headline)
+    kern_ms = kernel_breakdown(r, ev, K, flush_buf)
+    pairs = r.pairs()
+    n_blk = ds_blocks(r.q_lens, r.kv_lens, wl.causal) if r.run_bwd else 0
+    short = short_split(r.q_lens, r.kv_lens, wl.causal) if r.run_bwd and r.fuse_short else (0, 0, 0, 0)
+    acct = kernel_accounting(wl, r.T_q, r.T_k, pairs, n_blk, r.ds_path, short)
     name = max((n for n in acct if n in kern_ms), key=lambda n: kern_ms[n])   # the dominant kernel
-    side, i0, i1 = {"sched_q": (0, 0, 1), "fwd": (0, 1, 2), "bwd_sched": (1, 0, 1), "bwd_stats": (1, 1, 2),
-                    "bwd_dkdv": (1, 2, 3), "bwd_dq": (1, 3, 4)}[name]
 
-    # Timed pass: exactly K steps between two events and synchronisations;
-    # inside them only the events around the dominant kernel (and with
-    # --flush, each step's start and end)
-    dom_a, dom_b = ev.create(K), ev.create(K)
-    tev = []
-    for i in range(K):
-        arr = (ctypes.c_void_p * (3 if side == 0 else 5))()
-        arr[i0], arr[i1] = dom_a[i], dom_b[i]
-        tev.append(arr)
-    st_a, st_b = (ev.create(K), ev.create(K)) if args.flush else (None, None)
-    edge = ev.create(2)
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
-    torch.cuda.synchronize()
-    ev.lib.hipEventRecord(edge[0], stream)
-    for i in range(K):
-        if flush_buf is not None:
-            flush_buf.fill_(i & 0xff)
-        if derive:
-            derive()
-        if st_a is not None:
-            ev.lib.hipEventRecord(st_a[i], stream)
-        fwd(tev[i] if side == 0 else None)
-        if run_bwd:
-            bwd(tev[i] if side == 1 else None)
-        if st_b is not None:
-            ev.lib.hipEventRecord(st_b[i], stream)
-    ev.lib.hipEventRecord(edge[1], stream)
-    torch.cuda.synchronize()
-    total_ms = ev.ms(edge[0], edge[1])
-    ms_step = total_ms / K
-    if st_a is not None:   # each step from its start to its end, without the flush
-        ms_step = float(np.mean([ev.ms(st_a[i], st_b[i]) for i in range(K)]))
-    dom_ms = float(np.mean([ev.ms(dom_a[i], dom_b[i]) for i in range(K)]))
-
+    # the timed steps: headline (flushed unless --warm), then the same warm
+    t = timed_steps(r, ev, K, flush_buf, SLOTS[name])
+    t_warm = timed_steps(r, ev, K, warm_buf) if flush_buf is not None else None
+    ms_step = float(np.median(t["step"]))
+    D, H = r.D, r.H
     useful_fwd = 4.0 * D * H * pairs
-    useful_bwd = 10.0 * D * H * pairs if run_bwd else 0.0
-    value = (useful_fwd + useful_bwd) / (ms_step * 1e-3) / 1e12
-    fwd_tf = useful_fwd / (fwd_ms * 1e-3) / 1e12
-    bwd_tf = useful_bwd / (bwd_ms * 1e-3) / 1e12 if run_bwd else None
+    useful_bwd = 10.0 * D * H * pairs if r.run_bwd else 0.0
+    tf = lambda flops, ms: flops / (ms * 1e-3) / 1e12  # noqa: E731
+    value = tf(useful_fwd + useful_bwd, ms_step)
+    fwd_ms, bwd_ms = float(np.median(t["fwd"])), (float(np.median(t["bwd"])) if r.run_bwd else None)
+    dom_ms = float(np.mean(t["dom"]))
 
-    # roofline of the dominant kernel, timed inside the timed pass
+    # roofline of the dominant kernel, timed inside the timed steps
     t_s = dom_ms * 1e-3
-    ai = acct[name]["flops"] / acct[name]["bytes"]
+    a = acct[name]
+    ai = a["flops"] / a["bytes"]
     digest = kernel_source_digest()
     if ai < RIDGE:
-        roof = {"bound": "hbm", "achieved": acct[name]["bytes"] / t_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": a["bytes"] / t_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": acct[name]["flops"] / t_s / 1e12, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": a["flops"] / t_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(name, digest, wl.name)
-    roof.update({"kernel": name, "avg_launch_us": dom_ms * 1e3,
-                 "algorithmic_bytes": acct[name]["bytes"], "algorithmic_flops": acct[name]["flops"],
-                 "arith_intensity": ai, "mfma_frac": acct[name]["flops"] / t_s / 1e12 / PEAK_BF16_TFLOPS})
+    roof.update({
+        "traffic_from": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, copy-scaled, stored in "
+                         "profiles/traffic.json for these device sources (digest %s)" % digest)
+                        if roof["traffic"] is not None else "no counters for the current device sources",
+        "kernel": name, "avg_launch_us": dom_ms * 1e3,
+        "algorithmic_bytes": a["bytes"], "algorithmic_flops": a["flops"], "arith_intensity": ai,
+        "workspace_ds_bytes": a.get("ds_store_bytes", 0),
+        "mfma_frac": a["flops"] / t_s / 1e12 / PEAK_BF16_TFLOPS})
 
+    def pass_summary(useful, ms, target):
+        if ms is None:
+            return None
+        v = tf(useful, ms)
+        return {"tflops": v, "pct_of_peak": 100.0 * v / PEAK_BF16_TFLOPS, "target_pct": target,
+                "median_us": ms * 1e3}
     res = {
         "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic (seeded; lengths and values drawn per the workload recipe)",
-        "config": {"workload": wl.description, "name": wl.name, "batch": B, "heads": H, "head_dim": D,
-                   "causal": wl.causal, "activation": wl.activation, "seed": args.seed, "total_q_tokens": T_q,
-                   "total_kv_tokens": T_k, "visible_pairs_per_head": pairs, "block": wl.block,
-                   "bwd_dq_from_stored_ds": bool(run_bwd and ds_path),
-                   "bwd_short_seqs_dq_in_dkdv": bool(run_bwd and fuse_short),
+        "config": {"workload": wl.description, "name": wl.name, "batch": r.B, "heads": H, "head_dim": D,
+                   "causal": wl.causal, "activation": wl.activation, "seed": args.seed, "total_q_tokens": r.T_q,
+                   "total_kv_tokens": r.T_k, "visible_pairs_per_head": pairs, "block": wl.block,
+                   "bwd_dq_from_stored_ds": bool(r.run_bwd and r.ds_path),
+                   "bwd_short_seqs_dq_in_dkdv": bool(r.run_bwd and r.fuse_short),
                    "useful_gflop_per_step": (useful_fwd + useful_bwd) / 1e9},
+        "timing": ("median over %d steps, each flushed first (512 MiB written, evicting L2 and the last-level "
+                   "cache), timed by its own HIP events" % K) if flush_buf is not None else
+                  ("median over %d warm steps, each timed by its own HIP events" % K),
+        "ms_p10": pctl(t["step"], 10), "ms_p90": pctl(t["step"], 90), "timed_region_ms": t["region"],
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "fwd_tflops": fwd_tf, "fwd_pct_peak": 100.0 * fwd_tf / PEAK_BF16_TFLOPS,
-        "bwd_tflops": bwd_tf, "bwd_pct_peak": (100.0 * bwd_tf / PEAK_BF16_TFLOPS) if bwd_tf else None,
+        "fwd": pass_summary(useful_fwd, fwd_ms, 40.0),
+        "bwd": pass_summary(useful_bwd, bwd_ms, 30.0) if r.run_bwd else None,
         "kernel_us": {k_: v_ * 1e3 for k_, v_ in kern_ms.items()},
-        "kernel_us_from": "an untimed pass of the same steps with an event between every two launches",
-        "cache": "flushed before each step (512 MiB written)" if args.flush else "warm (steps back to back)",
+        "kernel_us_from": "mean of %d %s steps with an event between every two launches" % (
+            K, "flushed" if flush_buf is not None else "warm"),
         "kernel_source_digest": digest,
         "roofline": roof,
     }
-    for lst in ef + eb + [edge, dom_a, dom_b] + ([st_a, st_b] if st_a is not None else []):
-        ev.destroy(lst)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+    if t_warm is not None:
+        wms = float(np.median(t_warm["step"]))
+        res["warm"] = {"value": tf(useful_fwd + useful_bwd, wms), "ms_per_step": wms,
+                       "ms_p10": pctl(t_warm["step"], 10), "ms_p90": pctl(t_warm["step"], 90),
+                       "fwd_tflops": tf(useful_fwd, float(np.median(t_warm["fwd"]))),
+                       "bwd_tflops": tf(useful_bwd, float(np.median(t_warm["bwd"]))) if r.run_bwd else None,
+                       "timing": "median over %d warm steps (back to back, no flush)" % K}
+    # the same workload at other seeds: flushed median step of each
+    if args.seed_mean:
+        lo, hi = (int(x) for x in args.seed_mean.split("-"))
+        vals = []
+        del r
+        torch.cuda.empty_cache()
+        for sd in range(lo, hi + 1):
+            rs = Runner(wl, make_batch(wl, sd, with_dout=True), dev)
+            for _ in range(3):
+                rs.step()
+            ts = timed_steps(rs, ev, min(K, 20), flush_buf)
+            p = rs.pairs()
+            vals.append(tf((4.0 + (10.0 if rs.run_bwd else 0.0)) * D * H * p, float(np.median(ts["step"]))))
+            del rs
+            torch.cuda.empty_cache()
+        res["seed_mean"] = {"seeds": list(range(lo, hi + 1)), "values": vals, "mean": float(np.mean(vals)),
+                            "timing": "median of %d steps per seed, as the headline" % min(K, 20)}
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

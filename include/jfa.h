@@ -50,7 +50,9 @@
  * Errors.  Every function returns a jfa_status.  Arguments are validated on
  * the host before anything is enqueued:
  *   JFA_ERR_INVALID_ARGUMENT  a required pointer is NULL; batch < 0;
- *       heads < 1; a total or max length < 0; a non-finite scale; a bad
+ *       heads < 1; a total or max length < 0; a scale that is not finite
+ *       or is below 1e-20 (zero and negative scales included: masking
+ *       needs a positive scale); a bad
  *       activation, dtype or causal flag; a value pointer not 16-byte
  *       aligned; total_* * heads * head_dim >= 2^31 elements;
  *   JFA_ERR_UNSUPPORTED  head_dim not in {32, 64, 128}; heads > 256; a

@@ -123,6 +123,9 @@ bool finite_float(float x) {
   return (u & 0x7f800000u) != 0x7f800000u;
 }
 
+// Smallest accepted score scale (see check_common).
+constexpr float kMinScale = 1e-20f;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int32_t buckets_for(int32_t max_len, int32_t block) { return (max_len + block - 1) / block + 1; }
@@ -151,6 +154,11 @@ int check_common(const void* q, const void* k, const void* v, const int32_t* qo,
   if (!qo || !ko) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL offsets pointer");
   if ((total_q > 0 && !q) || (total_kv > 0 && (!k || !v))) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL input pointer");
   if (!finite_float(scale)) return fail(JFA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  // The softmax kernels mask a score by subtracting kMaskShift = 1e30 before
+  // scaling and take the row max of the raw scores: both need a positive
+  // scale large enough that a masked weight, exp2(-1e30 * scale * log2 e),
+  // is exactly 0 in fp32.  One rule for both activations.
+  if (!(scale >= kMinScale)) return fail(JFA_ERR_INVALID_ARGUMENT, "scale below 1e-20 (it must be positive)");
   if (activation != JFA_ACT_SOFTMAX && activation != JFA_ACT_SILU)
     return fail(JFA_ERR_INVALID_ARGUMENT, "bad activation");
   if (causal != 0 && causal != 1) return fail(JFA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");

@@ -64,7 +64,8 @@ def _bwd(**kw):
     (dict(q=None), INVALID), (dict(qo=None), INVALID), (dict(out=None), INVALID),
     (dict(lse=None), INVALID), (dict(batch=-1), INVALID), (dict(heads=0), INVALID),
     (dict(tq=-3), INVALID), (dict(mk=-1), INVALID), (dict(scale=math.nan), INVALID),
-    (dict(scale=math.inf), INVALID), (dict(act=2), INVALID), (dict(causal=2), INVALID), (dict(dtype=5), INVALID),
+    (dict(scale=math.inf), INVALID), (dict(scale=0.0), INVALID), (dict(scale=-0.125), INVALID),
+    (dict(scale=1e-30), INVALID), (dict(scale=-math.inf), INVALID), (dict(act=2), INVALID), (dict(causal=2), INVALID), (dict(dtype=5), INVALID),
     (dict(k=MIS), INVALID), (dict(out=MIS), INVALID), (dict(tq=1 << 24, heads=2, d=128), INVALID),
     (dict(d=48), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(heads=257), UNSUPPORTED),
     (dict(mk=64 * 1023 + 1), UNSUPPORTED), (dict(ws=None), WS_SMALL), (dict(wsb=16), WS_SMALL),

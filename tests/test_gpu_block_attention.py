@@ -58,7 +58,7 @@ def test_block_attention_parity(name, causal):
     ref_out, ref_lse = oracle.attention_fwd(*args, b.q_offsets, b.kv_offsets, s, wl.activation, causal, block=64)
     check_forward(out, lse, ref_out, ref_lse, wl.activation)
     ref_g = oracle.attention_bwd(*args, b.f64("dout"), b.q_offsets, b.kv_offsets, s, wl.activation, causal, block=64)
-    check_backward(grads, ref_g)
+    check_backward(grads, ref_g, q_off=b.q_offsets, k_off=b.kv_offsets)
 
 
 def test_block_attention_full_size_sampled():
@@ -83,4 +83,4 @@ def test_block_attention_full_size_sampled():
         ref_out, ref_lse = oracle.attention_fwd(*args, one, one, s, wl.activation, wl.causal, block=wl.block)
         check_forward(out[sl], lse[:, sl], ref_out, ref_lse, wl.activation)
         ref_g = oracle.attention_bwd(*args, b.f64("dout")[sl], one, one, s, wl.activation, wl.causal, block=wl.block)
-        check_backward(tuple(g[sl] for g in grads), ref_g)
+        check_backward(tuple(g[sl] for g in grads), ref_g, q_off=one, k_off=one)

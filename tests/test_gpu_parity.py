@@ -1,8 +1,10 @@
 """Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
 
-Gates: forward max abs error <= 1e-2 and lse abs error <= 1e-3 (lse = -inf
-exactly where the oracle has no visible key); per-tensor relative L2 error of
-dq, dk, dv <= 2e-2.
+Gates (bf16): forward abs error <= 1e-2 per element where |out| < 2, and
+1e-2 plus half a bf16 ulp of |out| above (the stored output's own rounding);
+lse abs error <= 1e-3 (lse = -inf exactly where the oracle has no visible
+key); relative L2 error of dq, dk, dv <= 2e-2, per tensor and per sequence.
+fp32 inputs: 1e-4 for the forward and for the gradients.
 """
 
 import dataclasses
@@ -12,7 +14,7 @@ import pytest
 import torch
 
 from jagged_attention_ads_amd.workloads import ORDER, WORKLOADS, make_batch
-from tests.gpu_util import (Dev, check_backward, check_forward, oracle_bwd, oracle_fwd, rows_of)
+from tests.gpu_util import (Dev, check_backward, check_forward, oracle_bwd, oracle_fwd, rows_of, seq_offsets)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +44,7 @@ def test_backward_reduced(name, batch):
     out, lse = d.forward()
     grads = d.backward(out, lse)
     torch.cuda.synchronize()
-    check_backward(grads, oracle_bwd(b))
+    check_backward(grads, oracle_bwd(b), q_off=b.q_offsets, k_off=b.kv_offsets)
 
 
 # ------------------------------------------------------------------ edge cases
@@ -104,7 +106,7 @@ def test_backward_reduced_recompute(name, batch, monkeypatch):
     out, lse = d.forward()
     grads = d.backward(out, lse)
     torch.cuda.synchronize()
-    check_backward(grads, oracle_bwd(b))
+    check_backward(grads, oracle_bwd(b), q_off=b.q_offsets, k_off=b.kv_offsets)
 
 
 def test_backward_small_workspace_recomputes():
@@ -124,8 +126,8 @@ def test_backward_small_workspace_recomputes():
     g_small = jfa.backward(d.q, d.k, d.v, out, d.do, lse, d.qo, d.ko, d.mq, d.mk, d.scale, d.act, d.causal, ws=small)
     torch.cuda.synchronize()
     ref = oracle_bwd(b)
-    check_backward(g_full, ref)
-    check_backward(g_small, ref)
+    check_backward(g_full, ref, q_off=b.q_offsets, k_off=b.kv_offsets)
+    check_backward(g_small, ref, q_off=b.q_offsets, k_off=b.kv_offsets)
     for x, y in zip(g_full[1:], g_small[1:]):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
@@ -139,7 +141,7 @@ def test_edge_cases(name, dq_path):
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle_fwd(b)
     check_forward(out, lse, ref_out, ref_lse, b.workload.activation)
-    check_backward(grads, oracle_bwd(b))
+    check_backward(grads, oracle_bwd(b), q_off=b.q_offsets, k_off=b.kv_offsets)
 
 
 # ------------------------------------------------------------------ short sequences
@@ -187,7 +189,7 @@ def test_short_sequences_dq_in_dkdv(name, monkeypatch):
     monkeypatch.setenv("JFA_BWD_FUSE_SHORT", "0")
     apart = d.backward(out, lse)
     torch.cuda.synchronize()
-    check_backward(fused, oracle_bwd(b))
+    check_backward(fused, oracle_bwd(b), q_off=b.q_offsets, k_off=b.kv_offsets)
     for x, y in zip(fused, apart):
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
@@ -238,7 +240,8 @@ def test_full_size_sampled(name):
     ref_out, ref_lse = oracle_fwd(b, seqs)
     check_forward(out, lse, ref_out, ref_lse, b.workload.activation, q_rows=qr)
     if grads is not None:
-        check_backward(grads, oracle_bwd(b, seqs), q_rows=qr, k_rows=kr)
+        qso, kso = seq_offsets(b, seqs)
+        check_backward(grads, oracle_bwd(b, seqs), q_rows=qr, k_rows=kr, q_off=qso, k_off=kso)
     # every row of the full outputs is finite (no row was skipped or left unwritten)
     assert torch.isfinite(out).all()
     if grads is not None:
