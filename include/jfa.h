@@ -125,6 +125,27 @@ int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_of
                 int32_t activation, int32_t causal, int32_t dtype, void* out, float* lse, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
+/* jfa_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The work list and the offsets-check
+ * word that jfa_forward keeps in the caller's workspace live in an array of
+ * the library's own device memory instead: 8 MiB on every GPU the library
+ * runs on, held until the process ends.  Arguments, layout, results (bit
+ * for bit) and errors are those of jfa_forward, plus JFA_ERR_UNSUPPORTED
+ * when jfa_workspace_size(..., for_backward = 0) exceeds 8 MiB (8388608
+ * bytes; e.g. batch 256, heads 4, total_q 97k needs about 140 KB) and
+ * JFA_ERR_HIP if the array's device address cannot be looked up.  It calls
+ * no allocating routine.  All calls on one GPU share its array: calls that
+ * overlap on one GPU (several streams or threads) race and must be ordered
+ * by the caller.  With JFA_CHECK_OFFSETS=1 the offsets are still checked
+ * (rejected offsets write nothing), but the check word is not readable
+ * through jfa_check_device_error. */
+int jfa_forward_noalloc(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                        const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim,
+                        int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale,
+                        int32_t activation, int32_t causal, int32_t dtype, void* out, float* lse,
+                        hipStream_t stream);
+
 /* Backward pass (Jagged Flash Attention item: no atomics -- dK/dV are
  * formed by key-tile-major work items and dQ by query-tile-major ones, each
  * output row summed in registers and stored once).  out and lse are the

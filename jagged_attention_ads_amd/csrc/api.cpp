@@ -170,6 +170,24 @@ int check_common(const void* q, const void* k, const void* v, const int32_t* qo,
 
 }  // namespace
 
+int jfa::report(int status, const std::string& msg) { return fail(status, msg); }
+
+int jfa::forward_args_status(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                             const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim,
+                             int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale,
+                             int32_t activation, int32_t causal, int32_t dtype, const void* out, const float* lse) {
+  int st = check_common(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
+                        max_kv_len, scale, activation, causal, dtype);
+  if (st != JFA_OK) return st;
+  if (total_q > 0 && !out) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL out");
+  if (!aligned16(out)) return fail(JFA_ERR_INVALID_ARGUMENT, "out not 16-byte aligned");
+  if (activation == JFA_ACT_SOFTMAX && total_q > 0 && !lse)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "NULL lse for softmax");
+  if (buckets_for(max_kv_len, jfa::kFwdBN) > jfa::kMaxBuckets)
+    return fail(JFA_ERR_UNSUPPORTED, "max_kv_len exceeds the scheduler's range");
+  return JFA_OK;
+}
+
 extern "C" {
 
 const char* jfa_status_string(int status) {
@@ -252,15 +270,10 @@ int jfa_forward_profiled(const void* q, const void* k, const void* v, const int3
                          int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation,
                          int32_t causal, int32_t dtype, void* out, float* lse, void* workspace,
                          size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
-  int st = check_common(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
-                        max_kv_len, scale, activation, causal, dtype);
+  int st = jfa::forward_args_status(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv,
+                                    max_q_len, max_kv_len, scale, activation, causal, dtype, out, lse);
   if (st != JFA_OK) return st;
-  if (total_q > 0 && !out) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL out");
-  if (!aligned16(out)) return fail(JFA_ERR_INVALID_ARGUMENT, "out not 16-byte aligned");
-  if (activation == JFA_ACT_SOFTMAX && total_q > 0 && !lse)
-    return fail(JFA_ERR_INVALID_ARGUMENT, "NULL lse for softmax");
   const int32_t nb = buckets_for(max_kv_len, jfa::kFwdBN);
-  if (nb > jfa::kMaxBuckets) return fail(JFA_ERR_UNSUPPORTED, "max_kv_len exceeds the scheduler's range");
   if (batch == 0 || total_q == 0) return JFA_OK;   // nothing to write
   const WsLayout L = ws_layout(batch, heads, total_q, total_kv, max_kv_len, dtype, false);
   if (!workspace || workspace_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");

@@ -6,7 +6,18 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace jfa {
+
+// Records `msg` as the calling thread's jfa_last_error() and returns status.
+int report(int status, const std::string& msg);
+// jfa_forward's argument checks (everything but the workspace): JFA_OK, or
+// the status it would return, with jfa_last_error() set.
+int forward_args_status(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                        const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                        int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation,
+                        int32_t causal, int32_t dtype, const void* out, const float* lse);
 
 // Tile geometry, shared by the launchers and the host-side sizing code.
 constexpr int kFwdBM = 128;     // query rows per forward / dQ work item

@@ -31,7 +31,8 @@ PASS_DQ_STORED_TILES = 3
 
 EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_profiled", "jfa_backward_profiled",
             "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_check_device_error",
-            "jfa_block_offsets_count", "jfa_block_offsets", "jfa_status_string", "jfa_last_error")
+            "jfa_block_offsets_count", "jfa_block_offsets", "jfa_status_string", "jfa_last_error",
+            "jfa_forward_noalloc")
 
 
 class JfaError(RuntimeError):
@@ -57,6 +58,9 @@ def lib():
         L.jfa_workspace_size.argtypes = [_i32] * 8
         L.jfa_forward.restype = ctypes.c_int
         L.jfa_forward.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_i32] * 7 + [_f32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+        L.jfa_forward_noalloc.restype = ctypes.c_int
+        L.jfa_forward_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_i32] * 7 + [_f32, _i32, _i32, _i32, _vp, _vp,
+                                                                            _vp]
         L.jfa_backward.restype = ctypes.c_int
         L.jfa_backward.argtypes = [_vp] * 8 + [_i32] * 7 + [_f32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
         L.jfa_forward_profiled.restype = ctypes.c_int
@@ -147,6 +151,21 @@ def jfa_forward(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, ac
                              H, D, T_q, k.shape[0], int(max_q_len), int(max_kv_len), float(scale),
                              ACTIVATIONS[activation], int(bool(causal)), dt, _ptr(out), _ptr(lse), _ptr(workspace),
                              workspace.numel() if workspace is not None else 0, _stream()))
+
+
+def jfa_forward_noalloc(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation, causal, out,
+                        lse):
+    """jfa_forward without a workspace: the library's own device scratch holds the work list."""
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _values(name, t, q.dtype)
+    _offsets("q_offsets", q_offsets)
+    _offsets("kv_offsets", kv_offsets)
+    T_q, H, D = q.shape
+    _check(lib().jfa_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets),
+                                     q_offsets.numel() - 1, H, D, T_q, k.shape[0], int(max_q_len), int(max_kv_len),
+                                     float(scale), ACTIVATIONS[activation], int(bool(causal)), dt, _ptr(out),
+                                     _ptr(lse), _stream()))
 
 
 def jfa_backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation, causal,

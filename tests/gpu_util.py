@@ -17,9 +17,11 @@ GRAD_RTOL = 2e-2     # relative L2 error of dq, dk, dv: per tensor and per seque
 GRAD_RTOL_FP32 = 1e-4  # the same for fp32 inputs
 # Per-sequence gate: a sequence's reference norm is floored at this fraction
 # of what an average sequence of its size has (its share of the tensor's
-# norm), so that sequences whose gradient nearly cancels (one key, ...) are
-# measured against the tensor's scale instead of their own tiny norm.
-SEQ_NORM_FLOOR = 1e-2
+# norm), so that sequences whose gradient cancels (one key gives dq = 0
+# exactly) are measured against the tensor's scale instead of their own
+# tiny norm.  At 1e-2 the fp32 path's rounding in such a sequence (about
+# 1e-6 of its share) read as 1.2e-4 against the 1e-4 gate.
+SEQ_NORM_FLOOR = 1e-1
 
 
 def dev():

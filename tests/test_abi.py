@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     L = jfa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -142,3 +142,16 @@ def test_block_offsets_validation():
     assert L.jfa_block_offsets(P, 3, 200, 64, P, 6, None) == INVALID       # out shorter than the count (7)
     assert L.jfa_block_offsets(None, 3, 200, 64, P, 7, None) == INVALID
     assert L.jfa_block_offsets(P, -1, 200, 64, P, 7, None) == INVALID
+
+
+def test_forward_noalloc_rejects_sizes_beyond_its_scratch():
+    """The allocation-free forward refuses, on the host and before any HIP
+    call, sizes whose work list would not fit its 8 MiB device array."""
+    L = jfa.lib()
+    assert jfa.jfa_workspace_size(100000, 8, 128, 1000000, 1000000, 64, 0, 0) > 8 << 20
+    st = L.jfa_forward_noalloc(P, P, P, P, P, 100000, 8, 128, 1000000, 1000000, 64, 64, 0.125, 0, 0, 0, P, P, None)
+    assert st == UNSUPPORTED
+    assert b"8 MiB" in L.jfa_last_error()
+    # invalid arguments are reported as jfa_forward reports them
+    st = L.jfa_forward_noalloc(P, P, P, P, P, 2, 2, 48, 10, 10, 5, 5, 0.125, 0, 0, 0, P, P, None)
+    assert st == UNSUPPORTED and b"head_dim" in L.jfa_last_error()
