@@ -247,3 +247,4 @@ def test_full_size_sampled(name):
     if grads is not None:
         for g in grads:
             assert torch.isfinite(g).all()
+
