@@ -528,6 +528,87 @@ SLOTS = {"sched_q": (0, 0, 1), "fwd": (0, 1, 2), "bwd_sched": (1, 0, 1), "bwd_st
          "bwd_dkdv": (1, 2, 3), "bwd_dq": (1, 3, 4)}
 
 
+def bbs_study(args):
+    """Base Batch Shuffling against plain consecutive batches, one GPU
+    standing in for R ranks.  The samples of each rank's pool are drawn from
+    the workload's length law; a rank's step takes two base batches of 128
+    samples: the next two in order (plain), or the rank's BBS merged batch
+    (jfa_bbs_plan over its own pool: no exchange between ranks).  Every
+    merged batch's forward + backward is timed on the GPU (median of its
+    flushed repetitions); a synchronous step lasts as long as its slowest
+    rank.  Prints one JSON line."""
+    import torch
+    from jagged_attention_ads_amd import jfa
+    from jagged_attention_ads_amd.workloads import WORKLOADS, draw_lengths
+    wl = WORKLOADS[args.workload]
+    R, S, base = args.ranks, args.bbs_steps, 128
+    rng = np.random.default_rng(args.seed)
+    pools = [draw_lengths(rng, wl.q_law, S * 2 * base).astype(np.int32) for _ in range(R)]
+    plans = {"plain": [], "bbs": []}
+    t0 = time.perf_counter()
+    for pool in pools:
+        perm, start = jfa.jfa_bbs_plan(pool, base, args.bbs_cost)
+        plans["bbs"].append([pool[perm[start[i]:start[i + 1]]] for i in range(len(start) - 1)])
+        plans["plain"].append([pool[2 * base * i:2 * base * (i + 1)] for i in range(S)])
+    plan_us = (time.perf_counter() - t0) / R * 1e6
+    dev = torch.device("cuda:0")
+    H, D = wl.heads, wl.head_dim
+    t_max = max(int(b.sum()) for p in plans.values() for rk in p for b in rk)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q, k, v, do = (torch.randn((t_max, H, D), device=dev).to(dt) * wl.std for _ in range(4))
+    ev = HipEvents()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    L = jfa.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+
+    def time_batch(lengths):
+        T = int(lengths.sum())
+        off = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).to(dev)
+        B, mq = len(lengths), int(lengths.max())
+        qs, ks, vs, dos = q[:T], k[:T], v[:T], do[:T]
+        out, dq, dk, dv = (torch.empty_like(qs) for _ in range(4))
+        lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+        wf = jfa.workspace(B, H, D, T, T, mq, dt, False, dev)
+        wb = jfa.workspace(B, H, D, T, T, mq, dt, True, dev)
+        act, sc = jfa.ACTIVATIONS[wl.activation], 1.0 / math.sqrt(D)
+        lse_arg = lse if wl.activation == "softmax" else None
+
+        def step():
+            st = L.jfa_forward(P(qs), P(ks), P(vs), P(off), P(off), B, H, D, T, T, mq, mq, sc, act, int(wl.causal),
+                               jfa.DTYPES[dt], P(out), P(lse_arg), P(wf), wf.numel(), stream)
+            st |= L.jfa_backward(P(qs), P(ks), P(vs), P(out), P(dos), P(lse_arg), P(off), P(off), B, H, D, T, T, mq,
+                                 mq, sc, act, int(wl.causal), jfa.DTYPES[dt], P(dq), P(dk), P(dv), P(wb),
+                                 wb.numel(), stream)
+            if st != 0:
+                raise jfa.JfaError(st, L.jfa_last_error().decode())
+        step()
+        e = ev.create(2 * args.bbs_reps)
+        for i in range(args.bbs_reps):
+            flush.fill_(i & 0xff)
+            ev.lib.hipEventRecord(e[2 * i], stream)
+            step()
+            ev.lib.hipEventRecord(e[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([ev.ms(e[2 * i], e[2 * i + 1]) for i in range(args.bbs_reps)]))
+        ev.destroy(e)
+        return ms
+
+    res = {"study": "base batch shuffling", "workload": wl.description, "ranks": R, "steps": S,
+           "base_batch": base, "cost": args.bbs_cost, "seed": args.seed, "plan_us_per_rank_pool": plan_us,
+           "timing": "per merged batch: forward + backward, median of %d flushed repetitions" % args.bbs_reps}
+    for name, plan in plans.items():
+        t = np.array([[time_batch(plan[r][s]) for s in range(S)] for r in range(R)])   # [rank, step]
+        work = np.array([[int((plan[r][s].astype(np.int64) ** 2).sum()) for s in range(S)] for r in range(R)])
+        step = t.max(axis=0)
+        res[name] = {"sync_step_ms_mean": float(step.mean()), "rank_ms_mean": float(t.mean()),
+                     "spread_across_ranks": float(np.mean((t.max(0) - t.min(0)) / t.mean(0))),
+                     "idle_frac": float(np.mean(1.0 - t.mean(0) / step)),
+                     "work_spread_across_ranks": float(np.mean((work.max(0) - work.min(0)) / work.mean(0)))}
+    res["sync_step_speedup"] = res["plain"]["sync_step_ms_mean"] / res["bbs"]["sync_step_ms_mean"]
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -544,9 +625,18 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain elementwise copy of known size (256 MiB read + 256 MiB written per "
                          "dispatch, 3 dispatches), to scale the HBM byte counters")
+    ap.add_argument("--study", choices=["bbs"], default=None,
+                    help="bbs: Base Batch Shuffling against plain batches (its own JSON line, not the headline)")
+    ap.add_argument("--ranks", type=int, default=8)
+    ap.add_argument("--bbs-steps", type=int, default=6)
+    ap.add_argument("--bbs-reps", type=int, default=5)
+    ap.add_argument("--bbs-cost", choices=["tokens", "pairs"], default="tokens")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.study == "bbs":
+        bbs_study(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

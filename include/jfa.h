@@ -238,6 +238,33 @@ int64_t jfa_block_offsets_count(int32_t batch, int32_t total, int32_t block);
 int jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t total, int32_t block, int32_t* out,
                       int64_t out_len, hipStream_t stream);
 
+/* Base Batch Shuffling (page piletech.kr/articles/112134, section 핵심
+ * 포인트 / Key points, BBS bullet, and section 상세 정리 / Detailed notes,
+ * Base Batch Shuffling item): the batch former ahead of this path.  The
+ * samples, in input order, form base batches of `base_batch` consecutive
+ * samples (the last may be shorter).  A base batch's load is the sum over
+ * its samples of their length (cost JFA_BBS_COST_TOKENS) or of its square
+ * (JFA_BBS_COST_PAIRS: the (query, key) pairs of self attention).  Base
+ * batches are sorted by load, heaviest first (ties: lower index first), and
+ * the k-th heaviest is merged with the k-th lightest into merged batch k
+ * (the heavier one's samples first, each in input order); with an odd number
+ * of base batches the median one is a merged batch of its own, last.  For
+ * pairs this minimises the largest merged load.
+ * Host arrays (the data loader knows the lengths before any copy):
+ *   lengths      int32 [n_samples], >= 0
+ *   perm         int64 [n_samples], out: input index of every output sample
+ *   batch_start  int64 [jfa_bbs_batch_count(...) + 1], out: merged batch i
+ *                is perm[batch_start[i] .. batch_start[i+1]-1]
+ * jfa_bbs_batch_count returns ceil(ceil(n_samples / base_batch) / 2), 0 for
+ * invalid arguments.  Errors (JFA_ERR_INVALID_ARGUMENT): n_samples < 0,
+ * base_batch < 1, a bad cost, a negative length, NULL arrays (lengths and
+ * perm may be NULL when n_samples is 0).  Synchronous, host only, no
+ * device access. */
+enum jfa_bbs_cost { JFA_BBS_COST_TOKENS = 0, JFA_BBS_COST_PAIRS = 1 };
+int64_t jfa_bbs_batch_count(int64_t n_samples, int32_t base_batch);
+int jfa_bbs_plan(const int32_t* lengths, int64_t n_samples, int32_t base_batch, int32_t cost, int64_t* perm,
+                 int64_t* batch_start);
+
 /* Device check of the offsets (debug; the jagged-input item's offsets
  * contract).  With JFA_CHECK_OFFSETS=1 in the environment, the work-list
  * builder of jfa_forward and jfa_backward first checks on the device that

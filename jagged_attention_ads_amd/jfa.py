@@ -32,7 +32,8 @@ PASS_DQ_STORED_TILES = 3
 EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_profiled", "jfa_backward_profiled",
             "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_check_device_error",
             "jfa_block_offsets_count", "jfa_block_offsets", "jfa_status_string", "jfa_last_error",
-            "jfa_forward_noalloc")
+            "jfa_forward_noalloc", "jfa_bbs_batch_count", "jfa_bbs_plan")
+BBS_COSTS = {"tokens": 0, "pairs": 1}
 
 
 class JfaError(RuntimeError):
@@ -81,6 +82,10 @@ def lib():
         L.jfa_check_device_error.argtypes = [_vp, _vp]
         L.jfa_status_string.restype = ctypes.c_char_p
         L.jfa_status_string.argtypes = [ctypes.c_int]
+        L.jfa_bbs_batch_count.restype = ctypes.c_int64
+        L.jfa_bbs_batch_count.argtypes = [ctypes.c_int64, _i32]
+        L.jfa_bbs_plan.restype = ctypes.c_int
+        L.jfa_bbs_plan.argtypes = [_vp, ctypes.c_int64, _i32, _i32, _vp, _vp]
         L.jfa_last_error.restype = ctypes.c_char_p
         L.jfa_last_error.argtypes = []
         _lib = L
@@ -213,6 +218,21 @@ def jfa_check_device_error(workspace):
     (JFA_CHECK_OFFSETS=1)."""
     st = lib().jfa_check_device_error(_ptr(workspace), _stream())
     return st, (lib().jfa_last_error().decode() if st != JFA_OK else "")
+
+
+def jfa_bbs_plan(lengths, base_batch=128, cost="tokens"):
+    """Base Batch Shuffling over host lengths (a sequence of ints or an int32
+    numpy array).  Returns (perm, batch_start) as int64 numpy arrays: merged
+    batch i is perm[batch_start[i]:batch_start[i+1]]."""
+    import numpy as np
+    lens = np.ascontiguousarray(lengths, dtype=np.int32)
+    n = int(lens.size)
+    nb = lib().jfa_bbs_batch_count(n, int(base_batch))
+    perm = np.empty(max(n, 1), dtype=np.int64)
+    start = np.empty(nb + 1, dtype=np.int64)
+    _check(lib().jfa_bbs_plan(lens.ctypes.data if n else None, n, int(base_batch), BBS_COSTS[cost],
+                              perm.ctypes.data if n else None, start.ctypes.data))
+    return perm[:n], start
 
 
 # ---------------------------------------------------------------- allocating wrappers

@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     L = jfa.lib()
     for n in names:
         assert hasattr(L, n), n
