@@ -28,6 +28,8 @@ HIP path computes, written from the pages that describe the method:
 Modules:
   attention -- jagged forward / backward, softmax and SiLU (GDPA)
   schedule  -- the integer work-list enumeration of the tile scheduler
+  rope      -- rotary position embedding of BlockAttention
+               ([GEM-MFU, Detailed notes: BlockAttention item])
   bbs       -- Base Batch Shuffling, the batch former ahead of the path
                ([GEM-MFU, Detailed notes: Base Batch Shuffling item])
 
@@ -38,6 +40,7 @@ and finite differences.
 
 from .attention import attention_fwd, attention_bwd, visible_mask  # noqa: F401
 from .bbs import bbs_plan, merged_loads  # noqa: F401
+from .rope import rope, sequence_positions  # noqa: F401
 from .schedule import (  # noqa: F401
     fwd_tile_costs,
     kv_tile_costs,

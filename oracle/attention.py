@@ -107,7 +107,15 @@ def _probs(S, vis, activation, lk):
     return A, None
 
 
-def attention_fwd(q, k, v, q_offsets, kv_offsets, scale, activation="softmax", causal=False, block=0):
+def _rope_inputs(q, k, qo, ko, rope_base):
+    """Q and K rotated at their positions within their sequences (see
+    oracle.rope; [GEM-MFU, Detailed notes: BlockAttention item])."""
+    from .rope import rope, sequence_positions
+    return rope(q, sequence_positions(qo), rope_base), rope(k, sequence_positions(ko), rope_base)
+
+
+def attention_fwd(q, k, v, q_offsets, kv_offsets, scale, activation="softmax", causal=False, block=0,
+                  rope_base=None):
     """Jagged attention forward in fp64.
 
     Returns (out [T_q, H, d], lse [H, T_q] or None for silu).
@@ -115,11 +123,15 @@ def attention_fwd(q, k, v, q_offsets, kv_offsets, scale, activation="softmax", c
     for silu; every sequence is independent of the others
     ([GEM-MFU, Detailed notes: jagged input]).  block > 0: BlockAttention,
     attention within each `block`-token run of a sequence (see _segments).
+    rope_base: Q and K first rotated by the rotary embedding of that base
+    at their positions within their sequences (oracle.rope).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     qo, ko = _check(q, k, v, q_offsets, kv_offsets, activation)
+    if rope_base is not None:
+        q, k = _rope_inputs(q, k, qo, ko, rope_base)
     T_q, H, d = q.shape
     out = np.zeros((T_q, H, v.shape[2]))
     lse = np.full((H, T_q), -np.inf) if activation == "softmax" else None
@@ -138,7 +150,8 @@ def attention_fwd(q, k, v, q_offsets, kv_offsets, scale, activation="softmax", c
     return out, lse
 
 
-def attention_bwd(q, k, v, dout, q_offsets, kv_offsets, scale, activation="softmax", causal=False, block=0):
+def attention_bwd(q, k, v, dout, q_offsets, kv_offsets, scale, activation="softmax", causal=False, block=0,
+                  rope_base=None):
     """Gradients (dq, dk, dv) of sum(out * dout) for the forward above, fp64.
 
     The chain rule written out per (sequence, head) block:
@@ -148,13 +161,20 @@ def attention_bwd(q, k, v, dout, q_offsets, kv_offsets, scale, activation="softm
       both:    dQ = scale dS K, dK = scale dS^T Q.
     The backward's parallel split without atomics ([GEM-MFU, Detailed notes:
     JFA]) changes only how these sums are formed, not their values.  block:
-    as in attention_fwd.
+    as in attention_fwd.  rope_base: the gradients are those of the rotated
+    Q and K turned back, dq = R(p)^T dq' (oracle.rope, inverse).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
     qo, ko = _check(q, k, v, q_offsets, kv_offsets, activation)
+    if rope_base is not None:
+        from .rope import rope, sequence_positions
+        qr, kr = _rope_inputs(q, k, qo, ko, rope_base)
+        dq, dk, dv = attention_bwd(qr, kr, v, dout, qo, ko, scale, activation, causal, block)
+        return (rope(dq, sequence_positions(qo), rope_base, inverse=True),
+                rope(dk, sequence_positions(ko), rope_base, inverse=True), dv)
     if dout.shape != q.shape[:2] + (v.shape[2],):
         raise ValueError("dout must have the shape of out")
     T_q, H, d = q.shape
