@@ -248,9 +248,10 @@ def _cpu_unit(arg):
     one_q, one_k = np.array([0, qo[b + 1] - qo[b]]), np.array([0, ko[b + 1] - ko[b]])
     hs = slice(h, h + 1)
     q, k, v = c["q"][sq, hs], c["k"][sk, hs], c["v"][sk, hs]
-    oracle.attention_fwd(q, k, v, one_q, one_k, c["scale"], c["act"], c["causal"], block=blk)
+    oracle.attention_fwd(q, k, v, one_q, one_k, c["scale"], c["act"], c["causal"], block=blk, rope_base=c["rope"])
     if with_bwd:
-        oracle.attention_bwd(q, k, v, c["do"][sq, hs], one_q, one_k, c["scale"], c["act"], c["causal"], block=blk)
+        oracle.attention_bwd(q, k, v, c["do"][sq, hs], one_q, one_k, c["scale"], c["act"], c["causal"], block=blk,
+                             rope_base=c["rope"])
     return (14 if with_bwd else 4) * c["d"] * c["pairs"][b]
 
 
@@ -276,7 +277,7 @@ def cpu_baseline(batch, budget_s):
     _CPU_BATCH.update(q=batch.f64("q"), k=batch.f64("k"), v=batch.f64("v"),
                       do=batch.f64("dout") if batch.dout is not None else None, qo=qo, ko=ko, block=blk,
                       scale=1.0 / math.sqrt(wl.head_dim), act=wl.activation, causal=wl.causal, d=wl.head_dim,
-                      pairs=pairs)
+                      pairs=pairs, rope=wl.rope_base or None)
     B, H = len(pairs), wl.heads
     with_bwd = bool(wl.backward and batch.dout is not None)
     dense = (np.diff(qo) * np.diff(ko)).astype(np.float64)   # the oracle's work follows Lq * Lk
@@ -384,7 +385,12 @@ class Runner:
         self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.derive = None
         self.q_lens, self.kv_lens = batch.q_lengths, batch.kv_lengths
-        if wl.block:
+        self.seq_off, self.n_seq = qo, B
+        if wl.block and wl.rope_base:
+            # BlockAttention with the fused rotary embedding: the block calls
+            # derive the runs' offsets themselves (between events 0 and 1)
+            self.q_lens = self.kv_lens = block_runs(batch.q_lengths, wl.block)
+        elif wl.block:
             # BlockAttention: the runs of wl.block tokens as sequences, derived
             # on the device from the sequences' offsets in every step
             seq_off, n_seq = qo, B
@@ -401,24 +407,42 @@ class Runner:
             mq = mk = min(wl.block, mq)
             self.q_lens = self.kv_lens = block_runs(batch.q_lengths, wl.block)
         self.qo, self.ko, self.B, self.mq, self.mk = qo, ko, B, mq, mk
-        self.ws_f = jfa.workspace(B, H, D, T_q, T_k, mk, self.q.dtype, False, dev)
-        self.ws_b = jfa.workspace(B, H, D, T_q, T_k, mk, self.q.dtype, True, dev)
+        if wl.block and wl.rope_base:
+            dtc = jfa.DTYPES[self.q.dtype]
+            self.ws_f = torch.empty(L.jfa_block_workspace_size(B, H, D, T_q, wl.block, dtc, 0), dtype=torch.uint8,
+                                    device=dev)
+            self.ws_b = torch.empty(L.jfa_block_workspace_size(B, H, D, T_q, wl.block, dtc, 1), dtype=torch.uint8,
+                                    device=dev)
+            self.B = int(L.jfa_block_offsets_count(B, T_q, wl.block)) - 1   # the runs, for reporting
+        else:
+            self.ws_f = jfa.workspace(B, H, D, T_q, T_k, mk, self.q.dtype, False, dev)
+            self.ws_b = jfa.workspace(B, H, D, T_q, T_k, mk, self.q.dtype, True, dev)
         # the dK/dV pass stores dS and the dQ pass reads it, unless switched
         # off or the store was left out of the workspace
-        self.ds_path = (os.environ.get("JFA_BWD_DS") != "0"
+        self.ds_path = (not wl.rope_base and os.environ.get("JFA_BWD_DS") != "0"
                         and self.ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, mk, self.q.dtype, 2))
         # the dK/dV pass writes the dQ of short sequences (bf16, d 64 or 128:
         # where its LDS has room) when every sequence is short, or always with
         # JFA_BWD_FUSE_SHORT=2; never with 0
         fuse_mode = os.environ.get("JFA_BWD_FUSE_SHORT", "1")
-        self.fuse_short = (fuse_mode != "0" and wl.dtype == "bf16" and D in (64, 128)
-                           and (fuse_mode == "2" or max(mq, mk) <= 64))
+        self.fuse_short = (wl.dtype == "bf16" and D in (64, 128)
+                           and (bool(wl.rope_base) or (fuse_mode != "0" and (fuse_mode == "2" or max(mq, mk) <= 64))))
         self.act = jfa.ACTIVATIONS[wl.activation]
         self.dt = jfa.DTYPES[self.q.dtype]
         self.lse_arg = self.lse if wl.activation == "softmax" else None
         self.run_bwd = wl.backward
 
     def fwd(self, events):
+        ev = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
+        if self.wl.rope_base:
+            st = self.L.jfa_block_forward(
+                self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.seq_off), self.n_seq, self.H, self.D,
+                self.T_q, int(self.batch.q_lengths.max()), self.wl.block, self.scale, self.act, int(self.wl.causal),
+                self.dt, self.wl.rope_base, self.P(self.out), self.P(self.lse_arg), self.P(self.ws_f),
+                self.ws_f.numel(), self.stream, ev)
+            if st != 0:
+                raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+            return
         st = self.L.jfa_forward_profiled(
             self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.qo), self.P(self.ko), self.B, self.H,
             self.D, self.T_q, self.T_k, self.mq, self.mk, self.scale, self.act, int(self.wl.causal), self.dt,
@@ -428,6 +452,17 @@ class Runner:
             raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
 
     def bwd(self, events):
+        ev = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
+        if self.wl.rope_base:
+            st = self.L.jfa_block_backward(
+                self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.out), self.P(self.do),
+                self.P(self.lse_arg), self.P(self.seq_off), self.n_seq, self.H, self.D, self.T_q,
+                int(self.batch.q_lengths.max()), self.wl.block, self.scale, self.act, int(self.wl.causal), self.dt,
+                self.wl.rope_base, self.P(self.dq), self.P(self.dk), self.P(self.dv), self.P(self.ws_b),
+                self.ws_b.numel(), self.stream, ev)
+            if st != 0:
+                raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+            return
         st = self.L.jfa_backward_profiled(
             self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.out), self.P(self.do),
             self.P(self.lse_arg), self.P(self.qo), self.P(self.ko), self.B, self.H, self.D, self.T_q, self.T_k,

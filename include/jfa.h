@@ -265,6 +265,43 @@ int64_t jfa_bbs_batch_count(int64_t n_samples, int32_t base_batch);
 int jfa_bbs_plan(const int32_t* lengths, int64_t n_samples, int32_t base_batch, int32_t cost, int64_t* perm,
                  int64_t* batch_start);
 
+/* BlockAttention with its fused rotary position embedding (page
+ * piletech.kr/articles/112134, section 상세 정리 / Detailed notes,
+ * BlockAttention item: fixed blocks of 64 tokens, combined with a fused
+ * rotary position embedding).  Self attention of every sequence of
+ * `offsets` (device int32 [batch + 1], rows 0 .. total-1 of q, k, v, out,
+ * dout, dq, dk, dv laid out as for jfa_forward) restricted to each run of
+ * `block` consecutive tokens counted from the sequence's first token
+ * (1 <= block <= 64).  rope_base = 0: no rotary embedding (the same as
+ * jfa_block_offsets + jfa_forward / jfa_backward, bit for bit).  rope_base >
+ * 1: Q and K are first turned by the rotary embedding of that base
+ * (rotate-half pairing: element i < head_dim/2 pairs with i + head_dim/2 and
+ * turns by angle p * base^(-2i/head_dim) at position p), and the gradients
+ * of q and k are those of the unturned inputs.  Positions are counted from
+ * each block's first token; attention within a block depends on positions
+ * only through their differences, so this equals counting from the
+ * sequence's first token.  The rotation is fused into the attention
+ * kernels (each Q and K row is turned once, on chip): it needs bf16 and
+ * head_dim 64 or 128 (JFA_ERR_UNSUPPORTED otherwise).  max_len: the longest
+ * sequence (>= 0).  The workspace (jfa_block_workspace_size, for_backward 0
+ * or 1) holds the blocks' offsets and the jagged calls' workspace.  events:
+ * NULL, or as for jfa_forward_profiled / jfa_backward_profiled (the block
+ * offsets kernel runs between events [0] and [1]).  Errors as for
+ * jfa_forward / jfa_backward, plus JFA_ERR_INVALID_ARGUMENT for block
+ * outside 1 .. 64, a rope_base that is neither 0 nor a finite value above
+ * 1, or max_len < 0. */
+size_t jfa_block_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total, int32_t block,
+                                int32_t dtype, int32_t for_backward);
+int jfa_block_forward(const void* q, const void* k, const void* v, const int32_t* offsets, int32_t batch,
+                      int32_t heads, int32_t head_dim, int32_t total, int32_t max_len, int32_t block, float scale,
+                      int32_t activation, int32_t causal, int32_t dtype, float rope_base, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+int jfa_block_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                       const float* lse, const int32_t* offsets, int32_t batch, int32_t heads, int32_t head_dim,
+                       int32_t total, int32_t max_len, int32_t block, float scale, int32_t activation, int32_t causal,
+                       int32_t dtype, float rope_base, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+
 /* Device check of the offsets (debug; the jagged-input item's offsets
  * contract).  With JFA_CHECK_OFFSETS=1 in the environment, the work-list
  * builder of jfa_forward and jfa_backward first checks on the device that

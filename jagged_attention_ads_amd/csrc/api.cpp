@@ -4,6 +4,7 @@
 #include "jfa.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -265,11 +266,13 @@ int jfa_build_worklist(int32_t pass, const int32_t* q_offsets, const int32_t* kv
   return JFA_OK;
 }
 
-int jfa_forward_profiled(const void* q, const void* k, const void* v, const int32_t* q_offsets,
-                         const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
-                         int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation,
-                         int32_t causal, int32_t dtype, void* out, float* lse, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+// jfa_forward_profiled with BlockAttention's fused rotary embedding when
+// rope.on (batches of short sequences, bf16, head_dim 64 or 128).
+static int forward_impl(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                        const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                        int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation,
+                        int32_t causal, int32_t dtype, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, hipEvent_t* events, const jfa::RopeArgs& rope) {
   int st = jfa::forward_args_status(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv,
                                     max_q_len, max_kv_len, scale, activation, causal, dtype, out, lse);
   if (st != JFA_OK) return st;
@@ -285,8 +288,11 @@ int jfa_forward_profiled(const void* q, const void* k, const void* v, const int3
   // Its items all cost at most one key block, so without the offsets check
   // it takes one block per (sequence, head) and no work list is built.
   const char* fs = std::getenv("JFA_FWD_SHORT");
-  const bool short_batch =
-      !(fs && fs[0] == '0' && fs[1] == 0) && max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kFwdBN;
+  const bool lengths_short = max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kFwdBN;
+  if (rope.on && (!lengths_short || dtype != JFA_DTYPE_BF16 || (head_dim != 64 && head_dim != 128)))
+    return fail(JFA_ERR_UNSUPPORTED, "the rotary embedding needs lengths <= 64, bf16 and head_dim 64 or 128");
+  // the rotary embedding lives in the two-wave variant only
+  const bool short_batch = lengths_short && (rope.on || !(fs && fs[0] == '0' && fs[1] == 0));
   const bool direct = short_batch && !check_offsets_enabled() && (int64_t)batch * heads <= INT32_MAX;
   if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (!direct) {
@@ -310,11 +316,22 @@ int jfa_forward_profiled(const void* q, const void* k, const void* v, const int3
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.rope = rope;
   e = jfa::launch_fwd(a, head_dim, dtype, activation, direct ? (int64_t)batch * heads : L.wq.capacity, short_batch,
                       stream);
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
   if ((e = record(events, 2, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;
+}
+
+int jfa_forward_profiled(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                         const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                         int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t activation,
+                         int32_t causal, int32_t dtype, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  return forward_impl(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
+                      max_kv_len, scale, activation, causal, dtype, out, lse, workspace, workspace_bytes, stream,
+                      events, jfa::RopeArgs{});
 }
 
 int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
@@ -327,12 +344,15 @@ int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_of
                               stream, nullptr);
 }
 
-int jfa_backward_profiled(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                          const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
-                          int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
-                          int32_t max_kv_len, float scale, int32_t activation, int32_t causal, int32_t dtype,
-                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream, hipEvent_t* events) {
+// jfa_backward_profiled with BlockAttention's fused rotary embedding when
+// rope.on (every sequence short, bf16, head_dim 64 or 128: the dK/dV pass
+// forms dQ itself).
+static int backward_impl(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                         const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
+                         int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
+                         int32_t max_kv_len, float scale, int32_t activation, int32_t causal, int32_t dtype, void* dq,
+                         void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         hipEvent_t* events, const jfa::RopeArgs& rope) {
   int st = check_common(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
                         max_kv_len, scale, activation, causal, dtype);
   if (st != JFA_OK) return st;
@@ -378,7 +398,12 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   const int qpass = use_ds ? (wide ? jfa::kPassDQS : jfa::kPassQ) : jfa::kPassDQ;
   const jfa::WorklistLayout& lay_q = use_ds ? (wide ? L.wq_dqs : L.wq_fwd) : L.wq;
   a.dq_rows = wide ? jfa::kDqDsBM : 128;
-  a.fuse_short = fuse_short_wanted(max_q_len, max_kv_len) && jfa::dkdv_fuses_short(dtype, head_dim) ? 1 : 0;
+  const bool lengths_short = max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kBwdBN;
+  if (rope.on && (!lengths_short || !jfa::dkdv_fuses_short(dtype, head_dim)))
+    return fail(JFA_ERR_UNSUPPORTED, "the rotary embedding needs lengths <= 64, bf16 and head_dim 64 or 128");
+  // the rotary embedding lives in the fused short-sequence path only
+  a.fuse_short =
+      (rope.on || fuse_short_wanted(max_q_len, max_kv_len)) && jfa::dkdv_fuses_short(dtype, head_dim) ? 1 : 0;
   a.meta_q = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + lay_q.meta_off);
   a.meta_kv = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wkv + L.wkv.meta_off);
   a.lse2 = reinterpret_cast<float*>(ws + L.off_stats);
@@ -397,6 +422,7 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.rope = rope;
 
   // per-row lse2 and delta, read by both gradient passes (softmax): formed
   // by the work-list launch's spare workgroups when it builds both lists,
@@ -441,6 +467,17 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
   return JFA_OK;
 }
 
+int jfa_backward_profiled(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                          const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
+                          int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
+                          int32_t max_kv_len, float scale, int32_t activation, int32_t causal, int32_t dtype,
+                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream, hipEvent_t* events) {
+  return backward_impl(q, k, v, out, dout, lse, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv,
+                       max_q_len, max_kv_len, scale, activation, causal, dtype, dq, dk, dv, workspace, workspace_bytes,
+                       stream, events, jfa::RopeArgs{});
+}
+
 int64_t jfa_block_offsets_count(int32_t batch, int32_t total, int32_t block) {
   if (batch < 0 || total < 0 || block < 1) return 0;
   return (int64_t)total / block + batch + 1;
@@ -457,6 +494,106 @@ int jfa_block_offsets(const int32_t* offsets, int32_t batch, int32_t total, int3
   hipError_t e = jfa::launch_block_offsets(offsets, batch, total, block, out, (int32_t)need, stream);
   if (e != hipSuccess) return hip_fail(e, "block offsets kernel launch");
   return JFA_OK;
+}
+
+// BlockAttention's calls: the run offsets go to the start of the workspace
+// (jfa_block_offsets), the jagged calls' workspace follows.
+static size_t block_runs_bytes(int32_t batch, int32_t total, int32_t block) {
+  return align256((size_t)jfa_block_offsets_count(batch, total, block) * sizeof(int32_t));
+}
+
+static int block_check(int32_t batch, int32_t total, int32_t max_len, int32_t block, float rope_base, int32_t dtype,
+                       int32_t head_dim, const int32_t* offsets) {
+  if (!offsets) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL offsets pointer");
+  if (batch < 0 || total < 0 || max_len < 0) return fail(JFA_ERR_INVALID_ARGUMENT, "negative batch, total or max_len");
+  if (block < 1 || block > jfa::kBwdBN) return fail(JFA_ERR_INVALID_ARGUMENT, "block must be 1 .. 64");
+  if (jfa_block_offsets_count(batch, total, block) > INT32_MAX) return fail(JFA_ERR_UNSUPPORTED, "too many blocks");
+  if (!finite_float(rope_base) || (rope_base != 0.f && !(rope_base > 1.f)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "rope_base must be 0 (none) or a finite base above 1");
+  if (rope_base != 0.f && (dtype != JFA_DTYPE_BF16 || (head_dim != 64 && head_dim != 128)))
+    return fail(JFA_ERR_UNSUPPORTED, "the rotary embedding needs bf16 and head_dim 64 or 128");
+  return JFA_OK;
+}
+
+static jfa::RopeArgs rope_args(float rope_base, int32_t head_dim) {
+  jfa::RopeArgs r{};
+  if (rope_base != 0.f) {
+    r.on = 1;
+    r.k2 = (float)(-2.0 * std::log2((double)rope_base) / (double)head_dim);
+  }
+  return r;
+}
+
+size_t jfa_block_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total, int32_t block,
+                                int32_t dtype, int32_t for_backward) {
+  if (batch < 0 || total < 0 || block < 1 || block > jfa::kBwdBN || for_backward < 0 || for_backward > 1) return 0;
+  const int64_t n = jfa_block_offsets_count(batch, total, block);
+  if (n > INT32_MAX) return 0;
+  // the backward over runs of at most 64 tokens forms dQ in its dK/dV pass
+  // where it can and needs no dS store; elsewhere it recomputes dS
+  const size_t inner = jfa_workspace_size((int32_t)(n - 1), heads, head_dim, total, total, block, dtype,
+                                          for_backward ? 2 : 0);
+  if (inner == 0) return 0;
+  return block_runs_bytes(batch, total, block) + inner;
+}
+
+int jfa_block_forward(const void* q, const void* k, const void* v, const int32_t* offsets, int32_t batch,
+                      int32_t heads, int32_t head_dim, int32_t total, int32_t max_len, int32_t block, float scale,
+                      int32_t activation, int32_t causal, int32_t dtype, float rope_base, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  int st = block_check(batch, total, max_len, block, rope_base, dtype, head_dim, offsets);
+  if (st != JFA_OK) return st;
+  const int32_t m = std::min(block, max_len);
+  const int64_t n = jfa_block_offsets_count(batch, total, block);
+  // every argument the forward takes, checked before anything is enqueued
+  st = jfa::forward_args_status(q, k, v, offsets, offsets, (int32_t)(n - 1), heads, head_dim, total, total, m, m,
+                                scale, activation, causal, dtype, out, lse);
+  if (st != JFA_OK) return st;
+  if (batch == 0 || total == 0) return JFA_OK;
+  const size_t need = jfa_block_workspace_size(batch, heads, head_dim, total, block, dtype, 0);
+  if (!workspace || workspace_bytes < need) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  int32_t* runs = static_cast<int32_t*>(workspace);
+  const size_t rb = block_runs_bytes(batch, total, block);
+  hipError_t e = record(events, 0, stream);
+  if (e != hipSuccess) return hip_fail(e, "event record");
+  e = jfa::launch_block_offsets(offsets, batch, total, block, runs, (int32_t)n, stream);
+  if (e != hipSuccess) return hip_fail(e, "block offsets kernel launch");
+  hipEvent_t later[3] = {nullptr, events ? events[1] : nullptr, events ? events[2] : nullptr};
+  return forward_impl(q, k, v, runs, runs, (int32_t)(n - 1), heads, head_dim, total, total, m, m, scale, activation,
+                      causal, dtype, out, lse, static_cast<char*>(workspace) + rb, workspace_bytes - rb, stream,
+                      later, rope_args(rope_base, head_dim));
+}
+
+int jfa_block_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                       const float* lse, const int32_t* offsets, int32_t batch, int32_t heads, int32_t head_dim,
+                       int32_t total, int32_t max_len, int32_t block, float scale, int32_t activation, int32_t causal,
+                       int32_t dtype, float rope_base, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  int st = block_check(batch, total, max_len, block, rope_base, dtype, head_dim, offsets);
+  if (st != JFA_OK) return st;
+  const int32_t m = std::min(block, max_len);
+  const int64_t n = jfa_block_offsets_count(batch, total, block);
+  st = check_common(q, k, v, offsets, offsets, (int32_t)(n - 1), heads, head_dim, total, total, m, m, scale,
+                    activation, causal, dtype);
+  if (st != JFA_OK) return st;
+  if (batch == 0 || total == 0) return JFA_OK;
+  const size_t need = jfa_block_workspace_size(batch, heads, head_dim, total, block, dtype, 1);
+  if (!workspace || workspace_bytes < need) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  // the remaining pointer checks are the backward's own; the run offsets
+  // are written only once it would proceed
+  if (!dout || !dq || !dk || !dv || (activation == JFA_ACT_SOFTMAX && (!out || !lse)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "NULL gradient, out or lse pointer");
+  int32_t* runs = static_cast<int32_t*>(workspace);
+  const size_t rb = block_runs_bytes(batch, total, block);
+  hipError_t e = record(events, 0, stream);
+  if (e != hipSuccess) return hip_fail(e, "event record");
+  e = jfa::launch_block_offsets(offsets, batch, total, block, runs, (int32_t)n, stream);
+  if (e != hipSuccess) return hip_fail(e, "block offsets kernel launch");
+  hipEvent_t later[5] = {nullptr};
+  for (int i = 1; i < 5 && events; ++i) later[i] = events[i];
+  return backward_impl(q, k, v, out, dout, lse, runs, runs, (int32_t)(n - 1), heads, head_dim, total, total, m, m,
+                       scale, activation, causal, dtype, dq, dk, dv, static_cast<char*>(workspace) + rb,
+                       workspace_bytes - rb, stream, later, rope_args(rope_base, head_dim));
 }
 
 int jfa_check_device_error(const void* workspace, hipStream_t stream) {

@@ -190,9 +190,16 @@ struct DkdvCfg {
   static constexpr bool FUSE = sizeof(T) == 2 && NS >= 4 && (NS - 2) * STAGE >= 2 * QT + 2 * NPAIRS * DT;
 };
 
-template <typename T, int D, int ACT, bool DS>
+// ROPE (short sequences, bf16, with the fused dQ): BlockAttention's fused
+// rotary embedding.  Wave A turns its key row in registers, the item's Q
+// stages (all of a short sequence's queries, landed in the prologue) are
+// turned in LDS, dK is turned back in registers before its store, and the
+// fused dQ is turned back through an fp32 exchange in LDS (the two halves
+// of d that a rotation pairs belong to different waves).
+template <typename T, int D, int ACT, bool DS, bool ROPE = false>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   using C = DkdvCfg<T, D>;
+  static_assert(!ROPE || C::FUSE, "the rotary embedding runs with the fused dQ of short sequences");
   static_assert(C::NT / kWave * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
   using Dma = typename C::Dma;
   constexpr int NPS = 2 * Dma::N + (ACT == 0 ? 2 : 0);   // copies per B thread per stage
@@ -261,6 +268,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     for (int kk = 0; kk < C::NK; ++kk) xf[kk] = global_frag<T>(xp + 16 * kk);
 #pragma unroll
     for (int kk = 0; kk < C::NK; ++kk) settle(xf[kk]);
+    if constexpr (ROPE)
+      if (role_a) rope_frags<C::NK>(xf, my_key, a.rope.k2);
   }
   if constexpr (C::FUSE) {
     // fused dQ: wave A's key row into LDS, at row swap23(key) of its pair's
@@ -275,6 +284,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   }
   dma_wait();
   __syncthreads();
+  if constexpr (ROPE) {
+    // a short sequence's query rows are all in stages 0 and 1 by now: turn
+    // them in place, stage s holding rows q_first + 32 s + swap23(r)
+    for (int s = 0; s < min(2, nst); ++s) rope_lds_tile<D, true>(slot(s), C::SR, q_first + s * C::SR, a.rope.k2, tid, C::NT);
+    __syncthreads();
+  }
   if (!role_a)
     for (int s = 2; s <= C::NS - 2; ++s)
       if (s < nst) issue_stage(s);
@@ -429,6 +444,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   // the ring is free once every wave is past the loop: stage the rows there
   __syncthreads();
   auto store_dkdv = [&]() {
+    if constexpr (ROPE)
+      if (!role_a) rope_acc_inverse<C::ND>(acc, my_key, a.rope.k2);   // dK of the turned keys, turned back
     T* op = static_cast<T*>(role_a ? a.dv : a.dk) + (size_t)(ks + kw0) * rs + (size_t)h * D;
     store_rows_lds<T, D>(op, rs, min(32, lk - kw0), acc, role_a ? 1.0f : a.scale,
                          smem + w * store_scratch_bytes<T, D>());
@@ -467,9 +484,42 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
                     "dQ staging must fit the slots past the first two");
       if (wave_live) store_dkdv();
       __syncthreads();   // K rows and dS blocks read: their LDS stages dQ
+      char* dq_scratch = kq + w * store_scratch_bytes<T, D / 2>();
+      if constexpr (ROPE) {
+        // dQ of the turned queries, turned back: each wave puts its half of d
+        // of its query block into an fp32 exchange over the K rows and dS
+        // blocks (read by now), then takes its partner's half.  The dK/dV
+        // staging in slots 0 and 1 is free after the barrier above, and
+        // stages dQ instead.
+        static_assert(2 * 32 * D * (int)sizeof(float) <= (C::NS - 2) * C::STAGE, "dQ exchange must fit");
+        static_assert(C::NT / kWave * store_scratch_bytes<T, D / 2>() <= 2 * C::STAGE, "dQ staging must fit");
+        float* x = reinterpret_cast<float*>(kq) + qb * 32 * D;
+        auto col = [&](int j, int r) { return 32 * (half * NDH + j) + 8 * (r / 4) + 4 * g + r % 4; };
+        if (q_live) {
+#pragma unroll
+          for (int j = 0; j < NDH; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[c32 * D + col(j, r)] = accq[j][r];
+        }
+        __syncthreads();
+        if (q_live) {
+#pragma unroll
+          for (int j = 0; j < NDH; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int d = col(j, r), i = d % (D / 2);
+              const float other = x[c32 * D + (half ? d - D / 2 : d + D / 2)];
+              float lo = half ? other : accq[j][r], hi = half ? accq[j][r] : other;
+              const float rev = __builtin_amdgcn_exp2f((float)i * a.rope.k2) * 0.15915494309189535f;
+              rope_rotate(lo, hi, (float)(qa + c32) * rev, true);
+              accq[j][r] = half ? hi : lo;
+            }
+        }
+        dq_scratch = smem + w * store_scratch_bytes<T, D / 2>();
+      }
       if (q_live)
         store_rows_lds<T, D / 2>(static_cast<T*>(a.dq) + (size_t)(qs + qa) * rs + (size_t)h * D + half * (D / 2), rs,
-                                 min(32, lq - qa), accq, a.scale, kq + w * store_scratch_bytes<T, D / 2>());
+                                 min(32, lq - qa), accq, a.scale, dq_scratch);
       return;
     }
   }
@@ -796,6 +846,9 @@ JFA_BWD_INST(float, 32, 1) JFA_BWD_INST(float, 64, 1) JFA_BWD_INST(float, 128, 1
 JFA_BWD_INST2(__bf16, 32) JFA_BWD_INST2(__bf16, 64) JFA_BWD_INST2(__bf16, 128)
 JFA_BWD_INST2(float, 32) JFA_BWD_INST2(float, 64) JFA_BWD_INST2(float, 128)
 #undef JFA_BWD_INST2
+#define JFA_BWD_ROPE_INST(D, ACT) template __global__ void dkdv_kernel<__bf16, D, ACT, false, true>(BwdArgs);
+JFA_BWD_ROPE_INST(64, 0) JFA_BWD_ROPE_INST(128, 0) JFA_BWD_ROPE_INST(64, 1) JFA_BWD_ROPE_INST(128, 1)
+#undef JFA_BWD_ROPE_INST
 
 // ---------------------------------------------------------------- launchers
 
@@ -829,6 +882,12 @@ bool dkdv_fuses_short(int dtype, int head_dim) {
 
 template <typename T, int ACT>
 static hipError_t dkdv_d(const BwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
+  if (a.rope.on) {   // short sequences with the fused dQ only (bf16, d 64 or 128)
+    if (!a.fuse_short || sizeof(T) != 2) return hipErrorInvalidValue;
+    if (head_dim == 64) return launch_k(dkdv_kernel<__bf16, 64, ACT, false, true>, a, grid, stream);
+    if (head_dim == 128) return launch_k(dkdv_kernel<__bf16, 128, ACT, false, true>, a, grid, stream);
+    return hipErrorInvalidValue;
+  }
   const bool ds = a.ds != nullptr;
   JFA_PICK_D(return launch_k(ds ? dkdv_kernel<T, D, ACT, true> : dkdv_kernel<T, D, ACT, false>, a, grid, stream))
 }

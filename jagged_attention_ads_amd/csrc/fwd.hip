@@ -44,8 +44,13 @@ struct FwdCfg {
   static constexpr int WPS = (D >= 128 && sizeof(T) == 4) ? 1 : 2;
 };
 
-template <typename T, int D, int ACT, bool SHORT>
+// ROPE (SHORT, bf16 only): BlockAttention's fused rotary embedding.  The
+// lane's Q row is turned in its registers after the load, and the item's one
+// K tile in LDS after it lands (one more barrier), positions counted from the
+// sequence's first row.
+template <typename T, int D, int ACT, bool SHORT, bool ROPE = false>
 __global__ __launch_bounds__((FwdCfg<T, D, SHORT>::NT), (FwdCfg<T, D, SHORT>::WPS)) void fwd_kernel(FwdArgs a) {
+  static_assert(!ROPE || (SHORT && sizeof(T) == 2), "the rotary embedding runs in the short-sequence bf16 variant");
   using C = FwdCfg<T, D, SHORT>;
   static_assert(C::NT / kWave * store_scratch_bytes<T, D>() <= C::LDS, "output staging must fit the LDS");
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -105,6 +110,7 @@ __global__ __launch_bounds__((FwdCfg<T, D, SHORT>::NT), (FwdCfg<T, D, SHORT>::WP
     for (int kk = 0; kk < C::NK; ++kk) qf[kk] = global_frag<T>(qp + 16 * kk);
 #pragma unroll
     for (int kk = 0; kk < C::NK; ++kk) settle(qf[kk]);
+    if constexpr (ROPE) rope_frags<C::NK>(qf, my_row, a.rope.k2);
   }
 
   f32x16 o[C::ND];
@@ -288,6 +294,12 @@ __global__ __launch_bounds__((FwdCfg<T, D, SHORT>::NT), (FwdCfg<T, D, SHORT>::WP
 
   dma_wait();
   __syncthreads();
+  if constexpr (ROPE) {
+    // the one K tile of a short item, turned in place (rows past the
+    // sequence read as zeros and stay zeros)
+    rope_lds_tile<D, true>(kslot0, C::BN, 0, a.rope.k2, tid, C::NT);
+    __syncthreads();
+  }
   f32x16 sa[2], sb[2];
   if (n_kv > 0 && wave_active(0)) scores(std::integral_constant<int, 0>{}, sa);
   // the first step copies K(2) over K(0): every wave must be done reading it
@@ -321,9 +333,21 @@ JFA_FWD_INST(__bf16, 32, 1) JFA_FWD_INST(__bf16, 64, 1) JFA_FWD_INST(__bf16, 128
 JFA_FWD_INST(float, 32, 0) JFA_FWD_INST(float, 64, 0) JFA_FWD_INST(float, 128, 0)
 JFA_FWD_INST(float, 32, 1) JFA_FWD_INST(float, 64, 1) JFA_FWD_INST(float, 128, 1)
 #undef JFA_FWD_INST
+#define JFA_FWD_ROPE_INST(D, ACT) template __global__ void fwd_kernel<__bf16, D, ACT, true, true>(FwdArgs);
+JFA_FWD_ROPE_INST(64, 0) JFA_FWD_ROPE_INST(128, 0) JFA_FWD_ROPE_INST(64, 1) JFA_FWD_ROPE_INST(128, 1)
+#undef JFA_FWD_ROPE_INST
 
 template <typename T, int D, int ACT>
 static hipError_t launch_one(const FwdArgs& a, int64_t grid, bool short_batch, hipStream_t stream) {
+  if (a.rope.on) {
+    if constexpr (sizeof(T) == 2 && D >= 64) {
+      if (!short_batch) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((fwd_kernel<T, D, ACT, true, true>), dim3((unsigned)grid), dim3(FwdCfg<T, D, true>::NT), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (short_batch)
     hipLaunchKernelGGL((fwd_kernel<T, D, ACT, true>), dim3((unsigned)grid), dim3(FwdCfg<T, D, true>::NT), 0, stream,
                        a);

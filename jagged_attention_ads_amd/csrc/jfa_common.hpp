@@ -595,6 +595,112 @@ __device__ __forceinline__ void store_rows_lds(T* base, int row_stride, int nval
   }
 }
 
+// ---------------------------------------------------------------- rotary embedding
+
+// BlockAttention's fused rotary embedding (rotate-half pairing): dimension
+// i < d/2 of a Q or K row pairs with i + d/2, and the pair turns by angle
+// p * theta_i at position p, theta_i = base^(-2i/d).  Angles are handled in
+// revolutions, which is what the hardware sine and cosine take (their range,
+// +-256 revolutions, covers positions within a block of 64 tokens with room
+// to spare).  inverse turns the other way (the transpose of the rotation,
+// for gradients).
+__device__ __forceinline__ void rope_rotate(float& a, float& b, float rev, bool inverse) {
+  const float c = __builtin_amdgcn_cosf(rev), s0 = __builtin_amdgcn_sinf(rev);
+  const float s = inverse ? -s0 : s0;
+  const float x = a * c - b * s, y = b * c + a * s;
+  a = x;
+  b = y;
+}
+
+// theta_i / (2 pi) for eight consecutive pairs i0 .. i0 + 7: one exp2, then
+// the constant ratio base^(-2/d) between neighbours.  k2 = -2 log2(base) / d.
+__device__ __forceinline__ void rope_revs8(int i0, float k2, float* rev) {
+  constexpr float kInv2Pi = 0.15915494309189535f;
+  const float step = __builtin_amdgcn_exp2f(k2);
+  float th = __builtin_amdgcn_exp2f((float)i0 * k2) * kInv2Pi;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    rev[e] = th;
+    th *= step;
+  }
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4& u, float* v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(u[e] << 16);
+    v[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+  }
+}
+
+// A row's fragments as the MFMA operands hold them (lane l: d-slots
+// 16*kk + 8*(l/32) + e of fragment kk, e = 0..7), turned in place for
+// position `pos`: pair (kk, e) with (kk + NK/2, e).  bf16 results are
+// rounded to nearest even.
+template <int NK>
+__device__ __forceinline__ void rope_frags(bf16x8* f, int pos, float k2) {
+  const int g = lane_id() >> 5;
+#pragma unroll
+  for (int kk = 0; kk < NK / 2; ++kk) {
+    float a[8], b[8], rev[8];
+    unpack_bf16x8(__builtin_bit_cast(u32x4, f[kk]), a);
+    unpack_bf16x8(__builtin_bit_cast(u32x4, f[kk + NK / 2]), b);
+    rope_revs8(16 * kk + 8 * g, k2, rev);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rope_rotate(a[e], b[e], (float)pos * rev[e], false);
+    f[kk] = to_frag_bf16(a);
+    f[kk + NK / 2] = to_frag_bf16(b);
+  }
+}
+
+// Every row of a swizzled LDS tile of `rows` rows (bf16, D columns; with
+// SWAPPED, LDS row r holds tile row swap23(r)) turned in place, tile row t
+// at position pos0 + t; the nt threads of the workgroup share the work.
+// The caller waits for the tile to land and barriers before and after.
+template <int D, bool SWAPPED>
+__device__ __forceinline__ void rope_lds_tile(char* tile, int rows, int pos0, float k2, int tid, int nt) {
+  using S = Swz<__bf16, D>;
+  constexpr int HC = S::CH / 2;   // 16-byte chunks in half a row
+  for (int u = tid; u < rows * HC; u += nt) {
+    const int r = u / HC, c = u % HC;
+    const int pos = pos0 + (SWAPPED ? swap23(r) : r);
+    u32x4* pa = reinterpret_cast<u32x4*>(tile + S::off(r, c));
+    u32x4* pb = reinterpret_cast<u32x4*>(tile + S::off(r, c + HC));
+    float a[8], b[8], rev[8];
+    unpack_bf16x8(*pa, a);
+    unpack_bf16x8(*pb, b);
+    rope_revs8(8 * c, k2, rev);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rope_rotate(a[e], b[e], (float)pos * rev[e], false);
+    *pa = __builtin_bit_cast(u32x4, to_frag_bf16(a));
+    *pb = __builtin_bit_cast(u32x4, to_frag_bf16(b));
+  }
+}
+
+// Accumulator blocks of one row per lane (lane l%32 = row, register r of
+// block dt = element 32*dt + 8*(r/4) + 4*(l/32) + r%4) turned back in place
+// (the transpose of the rotation) for the lane's position: pair (dt, r) with
+// (dt + ND/2, r).
+template <int ND>
+__device__ __forceinline__ void rope_acc_inverse(f32x16* acc, int pos, float k2) {
+  const int g = lane_id() >> 5;
+#pragma unroll
+  for (int dt = 0; dt < ND / 2; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float rev[8];
+      rope_revs8(32 * dt + 8 * q4 + 4 * g, k2, rev);   // elements i0 .. i0 + 3 used
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q4 + e;
+        float lo = acc[dt][r], hi = acc[dt + ND / 2][r];
+        rope_rotate(lo, hi, (float)pos * rev[e], true);
+        acc[dt][r] = lo;
+        acc[dt + ND / 2][r] = hi;
+      }
+    }
+}
+
 // ---------------------------------------------------------------- work items
 
 // Number of `bn`-key blocks a `bm`-query tile visits (forward and dQ).

@@ -105,6 +105,19 @@ hipError_t launch_sched_pair(int qpass, const int32_t* qo, const int32_t* ko, in
                              void* wl_kv, const WorklistLayout& lay_kv, const StatsArgs* stats, int dtype,
                              int head_dim, const OffsetCheck& chk, hipStream_t stream);
 
+// BlockAttention's fused rotary embedding (see rope_rotate): on = 1 turns Q
+// and K (and back the gradients of Q and K); k2 = -2 log2(base) / head_dim,
+// so that pair i turns by base^(-2i/d) = exp2(i * k2) per position.  Only for
+// batches of short sequences (every query and key length at most 64), bf16,
+// head_dim 64 or 128: the kernels that run them turn each row once, counting
+// positions from the start of the sequence (for BlockAttention's blocks, of
+// the block: attention then depends on positions only through their
+// differences).
+struct RopeArgs {
+  int32_t on;
+  float k2;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -121,6 +134,7 @@ struct FwdArgs {
   int32_t causal;
   float scale;        // softmax / silu score scale
   float scale_log2;   // scale * log2(e)
+  RopeArgs rope;
 };
 
 // short_batch: every sequence has at most 64 queries and 64 keys (the
@@ -165,6 +179,7 @@ struct BwdArgs {
   int32_t causal;
   float scale;
   float scale_log2;
+  RopeArgs rope;
 };
 
 // Row statistics (softmax): lse2 and delta for every (row, head).

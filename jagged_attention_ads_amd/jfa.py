@@ -32,7 +32,8 @@ PASS_DQ_STORED_TILES = 3
 EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_profiled", "jfa_backward_profiled",
             "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_check_device_error",
             "jfa_block_offsets_count", "jfa_block_offsets", "jfa_status_string", "jfa_last_error",
-            "jfa_forward_noalloc", "jfa_bbs_batch_count", "jfa_bbs_plan")
+            "jfa_forward_noalloc", "jfa_bbs_batch_count", "jfa_bbs_plan", "jfa_block_workspace_size",
+            "jfa_block_forward", "jfa_block_backward")
 BBS_COSTS = {"tokens": 0, "pairs": 1}
 
 
@@ -86,6 +87,14 @@ def lib():
         L.jfa_bbs_batch_count.argtypes = [ctypes.c_int64, _i32]
         L.jfa_bbs_plan.restype = ctypes.c_int
         L.jfa_bbs_plan.argtypes = [_vp, ctypes.c_int64, _i32, _i32, _vp, _vp]
+        L.jfa_block_workspace_size.restype = _sz
+        L.jfa_block_workspace_size.argtypes = [_i32] * 7
+        L.jfa_block_forward.restype = ctypes.c_int
+        L.jfa_block_forward.argtypes = [_vp] * 4 + [_i32] * 6 + [_f32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _sz,
+                                                                 _vp, _vp]
+        L.jfa_block_backward.restype = ctypes.c_int
+        L.jfa_block_backward.argtypes = [_vp] * 7 + [_i32] * 6 + [_f32, _i32, _i32, _i32, _f32] + [_vp] * 4 + [
+            _sz, _vp, _vp]
         L.jfa_last_error.restype = ctypes.c_char_p
         L.jfa_last_error.argtypes = []
         _lib = L
@@ -233,6 +242,47 @@ def jfa_bbs_plan(lengths, base_batch=128, cost="tokens"):
     _check(lib().jfa_bbs_plan(lens.ctypes.data if n else None, n, int(base_batch), BBS_COSTS[cost],
                               perm.ctypes.data if n else None, start.ctypes.data))
     return perm[:n], start
+
+
+def block_forward(q, k, v, offsets, max_len, block=64, scale=None, activation="softmax", causal=True,
+                  rope_base=0.0):
+    """BlockAttention (with the fused rotary embedding when rope_base > 0)
+    over the sequences of `offsets`; returns (out, lse)."""
+    _offsets("offsets", offsets)
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _values(name, t, q.dtype)
+    T, H, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    B = offsets.numel() - 1
+    out = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if activation == "softmax" else None
+    ws = torch.empty(max(lib().jfa_block_workspace_size(B, H, D, T, block, dt, 0), 1), dtype=torch.uint8,
+                     device=q.device)
+    _check(lib().jfa_block_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(offsets), B, H, D, T, int(max_len), int(block),
+                                   float(scale), ACTIVATIONS[activation], int(bool(causal)), dt, float(rope_base),
+                                   _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(), None))
+    return out, lse
+
+
+def block_backward(q, k, v, out, dout, lse, offsets, max_len, block=64, scale=None, activation="softmax",
+                   causal=True, rope_base=0.0):
+    """Gradients (dq, dk, dv) of block_forward."""
+    _offsets("offsets", offsets)
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _values(name, t, q.dtype)
+    T, H, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    B = offsets.numel() - 1
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(lib().jfa_block_workspace_size(B, H, D, T, block, dt, 1), 1), dtype=torch.uint8,
+                     device=q.device)
+    _check(lib().jfa_block_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(offsets), B,
+                                    H, D, T, int(max_len), int(block), float(scale), ACTIVATIONS[activation],
+                                    int(bool(causal)), dt, float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                    ws.numel(), _stream(), None))
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------- allocating wrappers

@@ -43,6 +43,7 @@ class Workload:
     backward: bool        # whether the workload runs the backward pass
     description: str
     block: int = 0        # > 0: BlockAttention, attention within runs of `block` tokens
+    rope_base: float = 0.0  # > 0: BlockAttention's fused rotary embedding of that base
 
 
 WORKLOADS = {
@@ -82,6 +83,14 @@ WORKLOADS["block_attn"] = Workload(
     ("lognormal", 256, 1024), None, True,
     "BlockAttention (causal within fixed 64-token blocks), batch 256, log-normal lengths "
     "(median 256, max 1024), 4 heads, d 128, bf16", block=64)
+
+# The same with the rotary embedding the BlockAttention item fuses in (base
+# 10000, rotate-half pairs; positions from each block's first token).
+WORKLOADS["block_rope"] = Workload(
+    "block_rope", 256, 4, 128, "bf16", 1.0, True, "softmax",
+    ("lognormal", 256, 1024), None, True,
+    "BlockAttention with fused rotary embedding (base 10000), causal within fixed 64-token blocks, batch 256, "
+    "log-normal lengths (median 256, max 1024), 4 heads, d 128, bf16", block=64, rope_base=10000.0)
 
 ORDER = ["tiny_fp32", "selfattn_causal", "cross_asym", "gdpa_silu", "pareto_train"]
 

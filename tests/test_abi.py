@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     L = jfa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -155,3 +155,33 @@ def test_forward_noalloc_rejects_sizes_beyond_its_scratch():
     # invalid arguments are reported as jfa_forward reports them
     st = L.jfa_forward_noalloc(P, P, P, P, P, 2, 2, 48, 10, 10, 5, 5, 0.125, 0, 0, 0, P, P, None)
     assert st == UNSUPPORTED and b"head_dim" in L.jfa_last_error()
+
+
+def _blk(**kw):
+    a = dict(q=P, k=P, v=P, off=P, batch=2, heads=2, d=64, total=10, max_len=5, block=64, scale=0.125, act=0,
+             causal=1, dtype=0, rope=10000.0, out=P, lse=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return jfa.lib().jfa_block_forward(a["q"], a["k"], a["v"], a["off"], a["batch"], a["heads"], a["d"], a["total"],
+                                       a["max_len"], a["block"], a["scale"], a["act"], a["causal"], a["dtype"],
+                                       a["rope"], a["out"], a["lse"], a["ws"], a["wsb"], None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=0), INVALID), (dict(block=65), INVALID), (dict(rope=0.5), INVALID), (dict(rope=-3.0), INVALID),
+    (dict(rope=math.inf), INVALID), (dict(rope=math.nan), INVALID), (dict(max_len=-1), INVALID),
+    (dict(off=None), INVALID), (dict(dtype=1), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(q=None), INVALID),
+    (dict(scale=0.0), INVALID), (dict(ws=None), WS_SMALL), (dict(wsb=64), WS_SMALL),
+])
+def test_block_forward_rejects(kw, status):
+    """Argument checks of BlockAttention with the rotary embedding, on the
+    host before anything is enqueued."""
+    assert _blk(**kw) == status
+
+
+def test_block_workspace_size():
+    L = jfa.lib()
+    assert L.jfa_block_workspace_size(4, 2, 64, 1000, 64, 0, 0) > 0
+    assert L.jfa_block_workspace_size(4, 2, 64, 1000, 64, 0, 1) > L.jfa_block_workspace_size(4, 2, 64, 1000, 64, 0, 0)
+    assert L.jfa_block_workspace_size(4, 2, 64, 1000, 65, 0, 0) == 0
+    assert L.jfa_block_workspace_size(4, 2, 64, 1000, 64, 0, 2) == 0
+    assert _blk(batch=0, ws=None, wsb=0) == OK

@@ -71,3 +71,26 @@ def test_forward_bound_flat_below_two():
     assert tol[5] == pytest.approx(1e-2 + 2.0 ** -6)
     assert tol[7] == pytest.approx(1e-2 + 2.0 ** -6)
     assert np.all(gpu_util.forward_tolerance(ref, torch.float32) == gpu_util.FWD_ATOL_FP32)
+
+
+def test_rope_lse_bound_covers_bf16_rounding_of_turned_inputs():
+    """The lse bound for the fused rotary embedding holds for an emulation of
+    exactly what it accounts for -- Q and K turned in fp64, rounded to bf16,
+    then exact attention -- and is not loose by more than a few times."""
+    import math
+    import oracle
+    rng = np.random.default_rng(8)
+    lengths = [64, 30, 64, 5]
+    off = offsets_from_lengths(lengths)
+    T, H, d = int(off[-1]), 2, 64
+    q, k, v = (rng.standard_normal((T, H, d)) for _ in range(3))
+    s = 1.0 / math.sqrt(d)
+    pos = oracle.sequence_positions(off) % 64
+    as_bf16 = lambda x: torch.from_numpy(x).to(torch.bfloat16).double().numpy()  # noqa: E731
+    qr, kr = as_bf16(oracle.rope(q, pos)), as_bf16(oracle.rope(k, pos))
+    _, lse_em = oracle.attention_fwd(qr, kr, v, off, off, s, "softmax", True, block=64)
+    _, lse_ref = oracle.attention_fwd(q, k, v, off, off, s, "softmax", True, block=64, rope_base=10000.0)
+    bound = gpu_util.rope_lse_bound(q, k, off, 64, True, s) - gpu_util.LSE_ATOL
+    err = np.abs(lse_em - lse_ref)
+    assert np.all(err <= bound)
+    assert err.max() > bound.max() / 50
