@@ -247,6 +247,12 @@ def _cpu_unit(arg):
     sq, sk = slice(qo[b], qo[b + 1]), slice(ko[b], ko[b + 1])
     one_q, one_k = np.array([0, qo[b + 1] - qo[b]]), np.array([0, ko[b + 1] - ko[b]])
     hs = slice(h, h + 1)
+    if c["pooled"]:   # the shared seeds against sequence b's keys
+        k, v = c["k"][sk, hs], c["v"][sk, hs]
+        oracle.pooled_fwd(c["q"][:, hs], k, v, one_k, c["scale"], c["act"])
+        if with_bwd:
+            oracle.pooled_bwd(c["q"][:, hs], k, v, c["do"][sq, hs], one_k, c["scale"], c["act"])
+        return (14 if with_bwd else 4) * c["d"] * c["pairs"][b]
     q, k, v = c["q"][sq, hs], c["k"][sk, hs], c["v"][sk, hs]
     oracle.attention_fwd(q, k, v, one_q, one_k, c["scale"], c["act"], c["causal"], block=blk, rope_base=c["rope"])
     if with_bwd:
@@ -277,7 +283,7 @@ def cpu_baseline(batch, budget_s):
     _CPU_BATCH.update(q=batch.f64("q"), k=batch.f64("k"), v=batch.f64("v"),
                       do=batch.f64("dout") if batch.dout is not None else None, qo=qo, ko=ko, block=blk,
                       scale=1.0 / math.sqrt(wl.head_dim), act=wl.activation, causal=wl.causal, d=wl.head_dim,
-                      pairs=pairs, rope=wl.rope_base or None)
+                      pairs=pairs, rope=wl.rope_base or None, pooled=bool(wl.n_seeds))
     B, H = len(pairs), wl.heads
     with_bwd = bool(wl.backward and batch.dout is not None)
     dense = (np.diff(qo) * np.diff(ko)).astype(np.float64)   # the oracle's work follows Lq * Lk
@@ -376,7 +382,9 @@ class Runner:
         ko = torch.from_numpy(batch.kv_offsets.astype(np.int32)).to(dev)
         mq, mk = int(batch.q_lengths.max()), int(batch.kv_lengths.max())
         self.scale = 1.0 / math.sqrt(D)
-        self.out = torch.empty_like(self.q)
+        # pooled attention: q holds the shared seeds; the output has a row
+        # per (sequence, seed)
+        self.out = torch.empty((T_q, H, D), dtype=self.q.dtype, device=dev)
         self.lse = torch.empty((H, T_q), dtype=torch.float32, device=dev)
         self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
         B = len(batch.q_lengths)
@@ -407,7 +415,13 @@ class Runner:
             mq = mk = min(wl.block, mq)
             self.q_lens = self.kv_lens = block_runs(batch.q_lengths, wl.block)
         self.qo, self.ko, self.B, self.mq, self.mk = qo, ko, B, mq, mk
-        if wl.block and wl.rope_base:
+        if wl.n_seeds:
+            dtc = jfa.DTYPES[self.q.dtype]
+            self.ws_f = torch.empty(L.jfa_pooled_workspace_size(B, wl.n_seeds, H, D, T_k, mk, dtc, 0),
+                                    dtype=torch.uint8, device=dev)
+            self.ws_b = torch.empty(L.jfa_pooled_workspace_size(B, wl.n_seeds, H, D, T_k, mk, dtc, 1),
+                                    dtype=torch.uint8, device=dev)
+        elif wl.block and wl.rope_base:
             dtc = jfa.DTYPES[self.q.dtype]
             self.ws_f = torch.empty(L.jfa_block_workspace_size(B, H, D, T_q, wl.block, dtc, 0), dtype=torch.uint8,
                                     device=dev)
@@ -419,7 +433,7 @@ class Runner:
             self.ws_b = jfa.workspace(B, H, D, T_q, T_k, mk, self.q.dtype, True, dev)
         # the dK/dV pass stores dS and the dQ pass reads it, unless switched
         # off or the store was left out of the workspace
-        self.ds_path = (not wl.rope_base and os.environ.get("JFA_BWD_DS") != "0"
+        self.ds_path = (not wl.rope_base and not wl.n_seeds and os.environ.get("JFA_BWD_DS") != "0"
                         and self.ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, mk, self.q.dtype, 2))
         # the dK/dV pass writes the dQ of short sequences (bf16, d 64 or 128:
         # where its LDS has room) when every sequence is short, or always with
@@ -434,6 +448,14 @@ class Runner:
 
     def fwd(self, events):
         ev = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
+        if self.wl.n_seeds:
+            st = self.L.jfa_pooled_forward(
+                self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.ko), self.B, self.wl.n_seeds, self.H,
+                self.D, self.T_k, self.mk, self.scale, self.act, self.dt, self.P(self.out), self.P(self.lse_arg),
+                self.P(self.ws_f), self.ws_f.numel(), self.stream, ev)
+            if st != 0:
+                raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+            return
         if self.wl.rope_base:
             st = self.L.jfa_block_forward(
                 self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.seq_off), self.n_seq, self.H, self.D,
@@ -453,6 +475,15 @@ class Runner:
 
     def bwd(self, events):
         ev = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
+        if self.wl.n_seeds:
+            st = self.L.jfa_pooled_backward(
+                self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.out), self.P(self.do),
+                self.P(self.lse_arg), self.P(self.ko), self.B, self.wl.n_seeds, self.H, self.D, self.T_k, self.mk,
+                self.scale, self.act, self.dt, self.P(self.dq), self.P(self.dk), self.P(self.dv), self.P(self.ws_b),
+                self.ws_b.numel(), self.stream, ev)
+            if st != 0:
+                raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+            return
         if self.wl.rope_base:
             st = self.L.jfa_block_backward(
                 self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.out), self.P(self.do),

@@ -302,6 +302,37 @@ int jfa_block_backward(const void* q, const void* k, const void* v, const void* 
                        int32_t dtype, float rope_base, void* dq, void* dk, void* dv, void* workspace,
                        size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
 
+/* Pooled multi-head attention (page piletech.kr/articles/112134, section
+ * 상세 정리 / Detailed notes, jagged-input item, which names it among the
+ * attention patterns with no definition; this library reads it as pooling by
+ * attention): n_seeds query vectors `seeds` [n_seeds, heads, head_dim],
+ * shared by every sequence, attend over each sequence's keys and values (no
+ * causal mask), pooling sequence b into rows b*n_seeds .. b*n_seeds +
+ * n_seeds - 1 of out [batch * n_seeds, heads, head_dim] (lse [heads, batch *
+ * n_seeds] for softmax).  The backward writes the gradients of k and v and
+ * dseeds [n_seeds, heads, head_dim], the sum over sequences of the seeds'
+ * per-sequence gradients (summed in fp32 in sequence order: reproducible bit
+ * for bit; all zeros for batch 0).  Other arguments, layouts and errors as
+ * for jfa_forward / jfa_backward with total_q = batch * n_seeds and the
+ * library writing the query offsets, plus JFA_ERR_INVALID_ARGUMENT for
+ * n_seeds outside 1 .. 256 or NULL / misaligned seeds or dseeds.  The
+ * workspace (jfa_pooled_workspace_size) holds the query offsets, the seeds
+ * repeated once per sequence (and the per-sequence seed gradients) and the
+ * jagged calls' workspace.  events: NULL, or as for jfa_forward_profiled /
+ * jfa_backward_profiled (the seeds' repetition runs between events [0] and
+ * [1], the seeds' gradient sum before event [4]). */
+size_t jfa_pooled_workspace_size(int32_t batch, int32_t n_seeds, int32_t heads, int32_t head_dim, int32_t total_kv,
+                                 int32_t max_kv_len, int32_t dtype, int32_t for_backward);
+int jfa_pooled_forward(const void* seeds, const void* k, const void* v, const int32_t* kv_offsets, int32_t batch,
+                       int32_t n_seeds, int32_t heads, int32_t head_dim, int32_t total_kv, int32_t max_kv_len,
+                       float scale, int32_t activation, int32_t dtype, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+int jfa_pooled_backward(const void* seeds, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, const int32_t* kv_offsets, int32_t batch, int32_t n_seeds, int32_t heads,
+                        int32_t head_dim, int32_t total_kv, int32_t max_kv_len, float scale, int32_t activation,
+                        int32_t dtype, void* dseeds, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, hipEvent_t* events);
+
 /* Device check of the offsets (debug; the jagged-input item's offsets
  * contract).  With JFA_CHECK_OFFSETS=1 in the environment, the work-list
  * builder of jfa_forward and jfa_backward first checks on the device that

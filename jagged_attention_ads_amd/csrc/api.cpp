@@ -596,6 +596,115 @@ int jfa_block_backward(const void* q, const void* k, const void* v, const void* 
                        workspace_bytes - rb, stream, later, rope_args(rope_base, head_dim));
 }
 
+// Pooled multi-head attention: the workspace holds the per-sequence query
+// offsets, the seeds repeated per sequence (and, backward, the per-sequence
+// query gradients), then the jagged calls' workspace.
+struct PooledLayout {
+  size_t off_q = 0, off_dq = 0, off_inner = 0, bytes = 0;
+};
+
+static PooledLayout pooled_layout(int32_t batch, int32_t n_seeds, int32_t heads, int32_t head_dim, int32_t dtype,
+                                  bool backward) {
+  PooledLayout L;
+  const size_t rows = (size_t)batch * n_seeds * heads * head_dim * (dtype == JFA_DTYPE_FP32 ? 4 : 2);
+  L.off_q = align256(((size_t)batch + 1) * sizeof(int32_t));
+  L.off_dq = L.off_q + align256(rows);
+  L.off_inner = L.off_dq + (backward ? align256(rows) : 0);
+  return L;
+}
+
+static int pooled_check(int32_t batch, int32_t n_seeds, int32_t heads, int32_t head_dim, const void* seeds,
+                        int32_t activation) {
+  if (n_seeds < 1 || n_seeds > 256) return fail(JFA_ERR_INVALID_ARGUMENT, "n_seeds must be 1 .. 256");
+  if (batch < 0 || heads < 1) return fail(JFA_ERR_INVALID_ARGUMENT, "batch < 0 or heads < 1");
+  if ((int64_t)batch * n_seeds > INT32_MAX || (int64_t)batch * n_seeds * heads * head_dim >= (int64_t(1) << 31))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "batch * n_seeds rows exceed the index range");
+  if (!seeds) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL seeds");
+  if (!aligned16(seeds)) return fail(JFA_ERR_INVALID_ARGUMENT, "seeds not 16-byte aligned");
+  (void)activation;
+  return JFA_OK;
+}
+
+size_t jfa_pooled_workspace_size(int32_t batch, int32_t n_seeds, int32_t heads, int32_t head_dim, int32_t total_kv,
+                                 int32_t max_kv_len, int32_t dtype, int32_t for_backward) {
+  if (batch < 0 || n_seeds < 1 || n_seeds > 256 || for_backward < 0 || for_backward > 1) return 0;
+  if ((int64_t)batch * n_seeds > INT32_MAX) return 0;
+  const size_t inner = jfa_workspace_size(batch, heads, head_dim, batch * n_seeds, total_kv, max_kv_len, dtype,
+                                          for_backward);
+  if (inner == 0) return 0;
+  return pooled_layout(batch, n_seeds, heads, head_dim, dtype, for_backward != 0).off_inner + inner;
+}
+
+int jfa_pooled_forward(const void* seeds, const void* k, const void* v, const int32_t* kv_offsets, int32_t batch,
+                       int32_t n_seeds, int32_t heads, int32_t head_dim, int32_t total_kv, int32_t max_kv_len,
+                       float scale, int32_t activation, int32_t dtype, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  int st = pooled_check(batch, n_seeds, heads, head_dim, seeds, activation);
+  if (st != JFA_OK) return st;
+  const int32_t total_q = batch * n_seeds;
+  // every other argument as the forward checks it (kv_offsets standing in
+  // for the query offsets, which the library writes)
+  st = jfa::forward_args_status(seeds, k, v, kv_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv,
+                                n_seeds, max_kv_len, scale, activation, 0, dtype, out, lse);
+  if (st != JFA_OK) return st;
+  if (batch == 0) return JFA_OK;
+  const size_t need = jfa_pooled_workspace_size(batch, n_seeds, heads, head_dim, total_kv, max_kv_len, dtype, 0);
+  if (!workspace || workspace_bytes < need) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  char* ws = static_cast<char*>(workspace);
+  const PooledLayout L = pooled_layout(batch, n_seeds, heads, head_dim, dtype, false);
+  const int64_t seed_bytes = (int64_t)n_seeds * heads * head_dim * (dtype == JFA_DTYPE_FP32 ? 4 : 2);
+  int32_t* qo = reinterpret_cast<int32_t*>(ws);
+  hipError_t e = record(events, 0, stream);
+  if (e != hipSuccess) return hip_fail(e, "event record");
+  e = jfa::launch_pooled_prep(seeds, seed_bytes, batch, n_seeds, ws + L.off_q, qo, stream);
+  if (e != hipSuccess) return hip_fail(e, "pooled prep kernel launch");
+  hipEvent_t later[3] = {nullptr, events ? events[1] : nullptr, events ? events[2] : nullptr};
+  return forward_impl(ws + L.off_q, k, v, qo, kv_offsets, batch, heads, head_dim, total_q, total_kv, n_seeds,
+                      max_kv_len, scale, activation, 0, dtype, out, lse, ws + L.off_inner,
+                      workspace_bytes - L.off_inner, stream, later, jfa::RopeArgs{});
+}
+
+int jfa_pooled_backward(const void* seeds, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, const int32_t* kv_offsets, int32_t batch, int32_t n_seeds, int32_t heads,
+                        int32_t head_dim, int32_t total_kv, int32_t max_kv_len, float scale, int32_t activation,
+                        int32_t dtype, void* dseeds, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, hipEvent_t* events) {
+  int st = pooled_check(batch, n_seeds, heads, head_dim, seeds, activation);
+  if (st != JFA_OK) return st;
+  const int32_t total_q = batch * n_seeds;
+  st = check_common(seeds, k, v, kv_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, n_seeds,
+                    max_kv_len, scale, activation, 0, dtype);
+  if (st != JFA_OK) return st;
+  if (!dseeds || !aligned16(dseeds)) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL or misaligned dseeds");
+  if (total_q > 0 && (!dout || (activation == JFA_ACT_SOFTMAX && (!out || !lse))))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "NULL dout, out or lse");
+  if (total_kv > 0 && (!dk || !dv)) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL dk or dv");
+  const size_t need = jfa_pooled_workspace_size(batch, n_seeds, heads, head_dim, total_kv, max_kv_len, dtype, 1);
+  if (batch > 0 && (!workspace || workspace_bytes < need)) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  char* ws = static_cast<char*>(workspace);
+  const PooledLayout L = pooled_layout(batch, n_seeds, heads, head_dim, dtype, true);
+  const int64_t seed_elems = (int64_t)n_seeds * heads * head_dim;
+  const int64_t seed_bytes = seed_elems * (dtype == JFA_DTYPE_FP32 ? 4 : 2);
+  hipError_t e = record(events, 0, stream);
+  if (e != hipSuccess) return hip_fail(e, "event record");
+  if (batch > 0) {
+    int32_t* qo = reinterpret_cast<int32_t*>(ws);
+    e = jfa::launch_pooled_prep(seeds, seed_bytes, batch, n_seeds, ws + L.off_q, qo, stream);
+    if (e != hipSuccess) return hip_fail(e, "pooled prep kernel launch");
+    hipEvent_t later[5] = {nullptr};
+    for (int i = 1; i < 4 && events; ++i) later[i] = events[i];
+    st = backward_impl(ws + L.off_q, k, v, out, dout, lse, qo, kv_offsets, batch, heads, head_dim, total_q, total_kv,
+                       n_seeds, max_kv_len, scale, activation, 0, dtype, ws + L.off_dq, dk, dv, ws + L.off_inner,
+                       workspace_bytes - L.off_inner, stream, later, jfa::RopeArgs{});
+    if (st != JFA_OK) return st;
+  }
+  // with no sequences the seeds' gradient is zero: the sum over none
+  e = jfa::launch_pooled_reduce(batch > 0 ? ws + L.off_dq : nullptr, seed_elems, batch, dtype, dseeds, stream);
+  if (e != hipSuccess) return hip_fail(e, "pooled reduce kernel launch");
+  if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");
+  return JFA_OK;
+}
+
 int jfa_check_device_error(const void* workspace, hipStream_t stream) {
   if (!workspace) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL workspace");
   int word = 0;

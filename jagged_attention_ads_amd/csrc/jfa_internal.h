@@ -144,6 +144,14 @@ struct FwdArgs {
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_t grid, bool short_batch,
                       hipStream_t stream);
 
+// Pooled multi-head attention (see pooled.hip): query offsets b * n_seeds
+// and the seeds repeated per sequence; the seeds' gradient as the sum over
+// sequences (fp32, sequence order).
+hipError_t launch_pooled_prep(const void* seeds, int64_t seed_bytes, int32_t batch, int32_t n_seeds, void* q,
+                              int32_t* q_offsets, hipStream_t stream);
+hipError_t launch_pooled_reduce(const void* dq, int64_t seed_elems, int32_t batch, int dtype, void* dseeds,
+                                hipStream_t stream);
+
 // BlockAttention: the runs of `block` tokens of every sequence as offsets
 // (see blocks.hip).
 hipError_t launch_block_offsets(const int32_t* off, int32_t batch, int32_t total, int32_t block, int32_t* out,

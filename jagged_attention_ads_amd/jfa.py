@@ -33,7 +33,8 @@ EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_pr
             "jfa_worklist_bytes", "jfa_tile_shape", "jfa_build_worklist", "jfa_check_device_error",
             "jfa_block_offsets_count", "jfa_block_offsets", "jfa_status_string", "jfa_last_error",
             "jfa_forward_noalloc", "jfa_bbs_batch_count", "jfa_bbs_plan", "jfa_block_workspace_size",
-            "jfa_block_forward", "jfa_block_backward")
+            "jfa_block_forward", "jfa_block_backward", "jfa_pooled_workspace_size", "jfa_pooled_forward",
+            "jfa_pooled_backward")
 BBS_COSTS = {"tokens": 0, "pairs": 1}
 
 
@@ -95,6 +96,12 @@ def lib():
         L.jfa_block_backward.restype = ctypes.c_int
         L.jfa_block_backward.argtypes = [_vp] * 7 + [_i32] * 6 + [_f32, _i32, _i32, _i32, _f32] + [_vp] * 4 + [
             _sz, _vp, _vp]
+        L.jfa_pooled_workspace_size.restype = _sz
+        L.jfa_pooled_workspace_size.argtypes = [_i32] * 8
+        L.jfa_pooled_forward.restype = ctypes.c_int
+        L.jfa_pooled_forward.argtypes = [_vp] * 4 + [_i32] * 6 + [_f32, _i32, _i32, _vp, _vp, _vp, _sz, _vp, _vp]
+        L.jfa_pooled_backward.restype = ctypes.c_int
+        L.jfa_pooled_backward.argtypes = [_vp] * 7 + [_i32] * 6 + [_f32, _i32, _i32] + [_vp] * 4 + [_sz, _vp, _vp]
         L.jfa_last_error.restype = ctypes.c_char_p
         L.jfa_last_error.argtypes = []
         _lib = L
@@ -283,6 +290,43 @@ def block_backward(q, k, v, out, dout, lse, offsets, max_len, block=64, scale=No
                                     int(bool(causal)), dt, float(rope_base), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                                     ws.numel(), _stream(), None))
     return dq, dk, dv
+
+
+def pooled_forward(seeds, k, v, kv_offsets, max_kv_len, scale=None, activation="softmax"):
+    """Pooled multi-head attention: seeds [n, H, d] shared by every sequence
+    of kv_offsets; returns (out [batch * n, H, d], lse or None)."""
+    _offsets("kv_offsets", kv_offsets)
+    dt = _dtype_code(seeds)
+    for name, t in (("seeds", seeds), ("k", k), ("v", v)):
+        _values(name, t, seeds.dtype)
+    n, H, D = seeds.shape
+    B = kv_offsets.numel() - 1
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    out = torch.empty((B * n, H, D), dtype=seeds.dtype, device=seeds.device)
+    lse = torch.empty((H, B * n), dtype=torch.float32, device=seeds.device) if activation == "softmax" else None
+    ws = torch.empty(max(lib().jfa_pooled_workspace_size(B, n, H, D, k.shape[0], int(max_kv_len), dt, 0), 1),
+                     dtype=torch.uint8, device=seeds.device)
+    _check(lib().jfa_pooled_forward(_ptr(seeds), _ptr(k), _ptr(v), _ptr(kv_offsets), B, n, H, D, k.shape[0],
+                                    int(max_kv_len), float(scale), ACTIVATIONS[activation], dt, _ptr(out), _ptr(lse),
+                                    _ptr(ws), ws.numel(), _stream(), None))
+    return out, lse
+
+
+def pooled_backward(seeds, k, v, out, dout, lse, kv_offsets, max_kv_len, scale=None, activation="softmax"):
+    """Gradients (dseeds, dk, dv) of pooled_forward."""
+    _offsets("kv_offsets", kv_offsets)
+    dt = _dtype_code(seeds)
+    n, H, D = seeds.shape
+    B = kv_offsets.numel() - 1
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dseeds, dk, dv = torch.empty_like(seeds), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(lib().jfa_pooled_workspace_size(B, n, H, D, k.shape[0], int(max_kv_len), dt, 1), 1),
+                     dtype=torch.uint8, device=seeds.device)
+    _check(lib().jfa_pooled_backward(_ptr(seeds), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                     _ptr(kv_offsets), B, n, H, D, k.shape[0], int(max_kv_len), float(scale),
+                                     ACTIVATIONS[activation], dt, _ptr(dseeds), _ptr(dk), _ptr(dv), _ptr(ws),
+                                     ws.numel(), _stream(), None))
+    return dseeds, dk, dv
 
 
 # ---------------------------------------------------------------- allocating wrappers

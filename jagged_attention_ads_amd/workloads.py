@@ -44,6 +44,7 @@ class Workload:
     description: str
     block: int = 0        # > 0: BlockAttention, attention within runs of `block` tokens
     rope_base: float = 0.0  # > 0: BlockAttention's fused rotary embedding of that base
+    n_seeds: int = 0      # > 0: pooled attention, n_seeds shared queries per sequence (q_law unused)
 
 
 WORKLOADS = {
@@ -92,6 +93,15 @@ WORKLOADS["block_rope"] = Workload(
     "BlockAttention with fused rotary embedding (base 10000), causal within fixed 64-token blocks, batch 256, "
     "log-normal lengths (median 256, max 1024), 4 heads, d 128, bf16", block=64, rope_base=10000.0)
 
+# Pooled multi-head attention (Detailed notes, jagged-input item): 4 seed
+# queries shared by every sequence pool the user histories of the
+# cross-attention workload; forward and backward.
+WORKLOADS["pooled_hist"] = Workload(
+    "pooled_hist", 512, 8, 64, "bf16", 1.0, False, "softmax",
+    ("fixed", 4), ("lognormal", 1024, 4096), True,
+    "pooled multi-head attention, 4 seed queries shared by 512 sequences, key lengths log-normal (median 1024, "
+    "max 4096), 8 heads, d 64, bf16", n_seeds=4)
+
 ORDER = ["tiny_fp32", "selfattn_causal", "cross_asym", "gdpa_silu", "pareto_train"]
 
 
@@ -104,6 +114,8 @@ def draw_lengths(rng, law, n):
         median, hi = law[1], law[2]
         x = np.exp(math.log(median) + LOGNORMAL_SIGMA * rng.standard_normal(n))
         return np.clip(np.rint(x), 1, hi).astype(np.int64)
+    if kind == "fixed":                         # every length equal
+        return np.full(n, law[1], dtype=np.int64)
     if kind == "pareto":                        # Pareto type I, x_m, max, alpha
         xm, hi, alpha = law[1], law[2], law[3]
         u = 1.0 - rng.random(n)                 # uniform on (0, 1]
@@ -186,7 +198,9 @@ def make_batch(workload, seed, batch=None, q_lengths=None, kv_lengths=None, with
         kv_lengths = np.asarray(kv_lengths, dtype=np.int64)
     qo, ko = offsets_from_lengths(q_lengths), offsets_from_lengths(kv_lengths)
     H, d, dt, std = workload.heads, workload.head_dim, workload.dtype, workload.std
-    q = _values(rng, int(qo[-1]), H, d, std, dt)
+    # pooled attention: q holds the n_seeds shared queries; the query offsets
+    # (b * n_seeds) describe the pooled output rows
+    q = _values(rng, workload.n_seeds if workload.n_seeds else int(qo[-1]), H, d, std, dt)
     k = _values(rng, int(ko[-1]), H, d, std, dt)
     v = _values(rng, int(ko[-1]), H, d, std, dt)
     if with_dout is None:

@@ -30,6 +30,8 @@ Modules:
   schedule  -- the integer work-list enumeration of the tile scheduler
   rope      -- rotary position embedding of BlockAttention
                ([GEM-MFU, Detailed notes: BlockAttention item])
+  pooled    -- pooled multi-head attention (shared seed queries per sequence)
+               ([GEM-MFU, Detailed notes: jagged input])
   bbs       -- Base Batch Shuffling, the batch former ahead of the path
                ([GEM-MFU, Detailed notes: Base Batch Shuffling item])
 
@@ -40,6 +42,7 @@ and finite differences.
 
 from .attention import attention_fwd, attention_bwd, visible_mask  # noqa: F401
 from .bbs import bbs_plan, merged_loads  # noqa: F401
+from .pooled import pooled_bwd, pooled_fwd  # noqa: F401
 from .rope import rope, sequence_positions  # noqa: F401
 from .schedule import (  # noqa: F401
     fwd_tile_costs,

@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 22, names
     L = jfa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -185,3 +185,30 @@ def test_block_workspace_size():
     assert L.jfa_block_workspace_size(4, 2, 64, 1000, 65, 0, 0) == 0
     assert L.jfa_block_workspace_size(4, 2, 64, 1000, 64, 0, 2) == 0
     assert _blk(batch=0, ws=None, wsb=0) == OK
+
+
+def _pooled(**kw):
+    a = dict(seeds=P, k=P, v=P, ko=P, batch=2, n=4, heads=2, d=64, tk=10, mk=5, scale=0.125, act=0, dtype=0, out=P,
+             lse=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return jfa.lib().jfa_pooled_forward(a["seeds"], a["k"], a["v"], a["ko"], a["batch"], a["n"], a["heads"], a["d"],
+                                        a["tk"], a["mk"], a["scale"], a["act"], a["dtype"], a["out"], a["lse"],
+                                        a["ws"], a["wsb"], None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), INVALID), (dict(n=257), INVALID), (dict(seeds=None), INVALID), (dict(seeds=MIS), INVALID),
+    (dict(ko=None), INVALID), (dict(scale=-1.0), INVALID), (dict(d=48), UNSUPPORTED), (dict(lse=None), INVALID),
+    (dict(ws=None), WS_SMALL), (dict(wsb=100), WS_SMALL), (dict(batch=1 << 24, n=200), INVALID),
+])
+def test_pooled_forward_rejects(kw, status):
+    """Pooled attention's argument checks, on the host before anything is
+    enqueued."""
+    assert _pooled(**kw) == status
+
+
+def test_pooled_noop_and_workspace():
+    assert _pooled(batch=0, ws=None, wsb=0) == OK
+    L = jfa.lib()
+    assert L.jfa_pooled_workspace_size(2, 4, 2, 64, 10, 5, 0, 1) > L.jfa_pooled_workspace_size(2, 4, 2, 64, 10, 5, 0, 0) > 0
+    assert L.jfa_pooled_workspace_size(2, 0, 2, 64, 10, 5, 0, 0) == 0

@@ -1,0 +1,105 @@
+"""Pooled multi-head attention on the GPU (through the C ABI) against the
+oracle: n_seeds queries shared by every sequence pool its keys and values
+(page piletech.kr/articles/112134, Detailed notes, jagged-input item; the
+reading is in oracle/pooled.py).  Gates as for the jagged calls; the seeds'
+gradient is gated as one tensor."""
+
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from jagged_attention_ads_amd import jfa
+from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch
+from tests.gpu_util import Dev, check_backward, check_forward
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (n_seeds, key lengths, activation, head_dim, dtype)
+    "one_seed": (1, [1, 300, 64, 2000, 5], "softmax", 64, "bf16"),
+    "four_seeds_empty_seq": (4, [0, 129, 700, 1, 4096, 33], "softmax", 64, "bf16"),
+    "sixteen_seeds_d128": (16, [64, 65, 1000, 7], "softmax", 128, "bf16"),
+    "silu": (4, [10, 500, 1300, 0, 3], "silu", 64, "bf16"),
+    "fp32": (3, [20, 130, 1, 77], "softmax", 32, "fp32"),
+}
+
+
+def _batch(name):
+    n, lk, act, d, dt = CASES[name]
+    wl = dataclasses.replace(WORKLOADS["pooled_hist"], n_seeds=n, activation=act, head_dim=d, dtype=dt, heads=3)
+    return make_batch(wl, 80 + sorted(CASES).index(name), q_lengths=[n] * len(lk), kv_lengths=lk, with_dout=True)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_pooled_parity(name):
+    b = _batch(name)
+    wl = b.workload
+    d = Dev(b)
+    print("pooled case: %s" % name, flush=True)
+    out, lse = jfa.pooled_forward(d.q, d.k, d.v, d.ko, d.mk, d.scale, wl.activation)
+    grads = jfa.pooled_backward(d.q, d.k, d.v, out, d.do, lse, d.ko, d.mk, d.scale, wl.activation)
+    torch.cuda.synchronize()
+    s = 1.0 / math.sqrt(wl.head_dim)
+    ref_out, ref_lse = oracle.pooled_fwd(b.f64("q"), b.f64("k"), b.f64("v"), b.kv_offsets, s, wl.activation)
+    check_forward(out, lse, ref_out, ref_lse, wl.activation)
+    ref = oracle.pooled_bwd(b.f64("q"), b.f64("k"), b.f64("v"), b.f64("dout"), b.kv_offsets, s, wl.activation)
+    check_backward(grads, ref, q_off=np.array([0, wl.n_seeds]), k_off=b.kv_offsets)
+
+
+@pytest.mark.parametrize("name", ["four_seeds_empty_seq", "silu"])
+def test_pooled_equals_cross_attention_on_repeated_seeds(name):
+    """The pooled calls are the jagged cross attention with the seeds
+    repeated per sequence, bit for bit (out, lse, dK, dV), and the seeds'
+    gradient is the fp32 sum, in sequence order, of that attention's
+    per-sequence query gradients, rounded once."""
+    b = _batch(name)
+    wl = b.workload
+    d = Dev(b)
+    B, n = len(b.kv_lengths), wl.n_seeds
+    out, lse = jfa.pooled_forward(d.q, d.k, d.v, d.ko, d.mk, d.scale, wl.activation)
+    ds, dk, dv = jfa.pooled_backward(d.q, d.k, d.v, out, d.do, lse, d.ko, d.mk, d.scale, wl.activation)
+    qrep = d.q.repeat(B, 1, 1).contiguous()
+    qo = torch.arange(B + 1, dtype=torch.int32, device=d.q.device) * n
+    out2, lse2 = jfa.forward(qrep, d.k, d.v, qo, d.ko, n, d.mk, d.scale, wl.activation, False)
+    dq2, dk2, dv2 = jfa.backward(qrep, d.k, d.v, out2, d.do, lse2, qo, d.ko, n, d.mk, d.scale, wl.activation, False)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
+    if lse is not None:
+        assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    assert torch.equal(dk.view(torch.uint8), dk2.view(torch.uint8))
+    assert torch.equal(dv.view(torch.uint8), dv2.view(torch.uint8))
+    parts = dq2.float().cpu().numpy().reshape(B, n, *d.q.shape[1:])
+    acc = np.zeros(parts.shape[1:], dtype=np.float32)
+    for i in range(B):
+        acc = acc + parts[i]
+    want = torch.from_numpy(acc).to(d.q.dtype)
+    assert torch.equal(ds.cpu().view(torch.uint8), want.view(torch.uint8))
+
+
+def test_pooled_full_size_sampled():
+    """The benchmark's pooled batch: every row finite, sampled sequences'
+    pooled rows and key gradients against the oracle (the seeds' gradient,
+    a sum over all sequences, is checked on the whole batch)."""
+    b = make_batch("pooled_hist", 2)
+    wl = b.workload
+    d = Dev(b)
+    out, lse = jfa.pooled_forward(d.q, d.k, d.v, d.ko, d.mk, d.scale)
+    ds, dk, dv = jfa.pooled_backward(d.q, d.k, d.v, out, d.do, lse, d.ko, d.mk, d.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and all(torch.isfinite(g).all() for g in (ds, dk, dv))
+    s = 1.0 / math.sqrt(wl.head_dim)
+    ref_ds = oracle.pooled_bwd(b.f64("q"), b.f64("k"), b.f64("v"), b.f64("dout"), b.kv_offsets, s)[0]
+    check_backward((ds, ds, ds), (ref_ds, ref_ds, ref_ds))
+    n = wl.n_seeds
+    for seq in (int(np.argmax(b.kv_lengths)), 3, 100):
+        k0, k1 = int(b.kv_offsets[seq]), int(b.kv_offsets[seq + 1])
+        one = np.array([0, k1 - k0])
+        ro, rl = oracle.pooled_fwd(b.f64("q"), b.f64("k")[k0:k1], b.f64("v")[k0:k1], one, s)
+        sl = slice(seq * n, seq * n + n)
+        check_forward(out[sl], lse[:, sl], ro, rl, "softmax")
+        _, rdk, rdv = oracle.pooled_bwd(b.f64("q"), b.f64("k")[k0:k1], b.f64("v")[k0:k1], b.f64("dout")[sl], one, s)
+        check_backward((ds, dk[k0:k1], dv[k0:k1]), (ref_ds, rdk, rdv), k_off=one)
