@@ -311,8 +311,9 @@ int jfa_block_backward(const void* q, const void* k, const void* v, const void* 
  * n_seeds - 1 of out [batch * n_seeds, heads, head_dim] (lse [heads, batch *
  * n_seeds] for softmax).  The backward writes the gradients of k and v and
  * dseeds [n_seeds, heads, head_dim], the sum over sequences of the seeds'
- * per-sequence gradients (summed in fp32 in sequence order: reproducible bit
- * for bit; all zeros for batch 0).  Other arguments, layouts and errors as
+ * per-sequence gradients (in fp32: each of min(batch, 16) chunks of
+ * consecutive sequences summed in order, then the chunks in order:
+ * reproducible bit for bit; all zeros for batch 0).  Other arguments, layouts and errors as
  * for jfa_forward / jfa_backward with total_q = batch * n_seeds and the
  * library writing the query offsets, plus JFA_ERR_INVALID_ARGUMENT for
  * n_seeds outside 1 .. 256 or NULL / misaligned seeds or dseeds.  The

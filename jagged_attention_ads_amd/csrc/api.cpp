@@ -600,7 +600,7 @@ int jfa_block_backward(const void* q, const void* k, const void* v, const void* 
 // offsets, the seeds repeated per sequence (and, backward, the per-sequence
 // query gradients), then the jagged calls' workspace.
 struct PooledLayout {
-  size_t off_q = 0, off_dq = 0, off_inner = 0, bytes = 0;
+  size_t off_q = 0, off_dq = 0, off_part = 0, off_inner = 0, bytes = 0;
 };
 
 static PooledLayout pooled_layout(int32_t batch, int32_t n_seeds, int32_t heads, int32_t head_dim, int32_t dtype,
@@ -609,7 +609,8 @@ static PooledLayout pooled_layout(int32_t batch, int32_t n_seeds, int32_t heads,
   const size_t rows = (size_t)batch * n_seeds * heads * head_dim * (dtype == JFA_DTYPE_FP32 ? 4 : 2);
   L.off_q = align256(((size_t)batch + 1) * sizeof(int32_t));
   L.off_dq = L.off_q + align256(rows);
-  L.off_inner = L.off_dq + (backward ? align256(rows) : 0);
+  L.off_part = L.off_dq + (backward ? align256(rows) : 0);
+  L.off_inner = L.off_part + (backward ? align256((size_t)jfa::kPooledChunks * n_seeds * heads * head_dim * 4) : 0);
   return L;
 }
 
@@ -699,7 +700,9 @@ int jfa_pooled_backward(const void* seeds, const void* k, const void* v, const v
     if (st != JFA_OK) return st;
   }
   // with no sequences the seeds' gradient is zero: the sum over none
-  e = jfa::launch_pooled_reduce(batch > 0 ? ws + L.off_dq : nullptr, seed_elems, batch, dtype, dseeds, stream);
+  // with no sequences the sum is over none: zeros (no workspace is read)
+  e = jfa::launch_pooled_reduce(batch > 0 ? ws + L.off_dq : nullptr, seed_elems, batch, dtype,
+                                batch > 0 ? reinterpret_cast<float*>(ws + L.off_part) : nullptr, dseeds, stream);
   if (e != hipSuccess) return hip_fail(e, "pooled reduce kernel launch");
   if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;

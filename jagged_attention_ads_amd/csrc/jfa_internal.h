@@ -146,11 +146,16 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, int act, int64_
 
 // Pooled multi-head attention (see pooled.hip): query offsets b * n_seeds
 // and the seeds repeated per sequence; the seeds' gradient as the sum over
-// sequences (fp32, sequence order).
+// sequences (fp32, fixed order).
 hipError_t launch_pooled_prep(const void* seeds, int64_t seed_bytes, int32_t batch, int32_t n_seeds, void* q,
                               int32_t* q_offsets, hipStream_t stream);
-hipError_t launch_pooled_reduce(const void* dq, int64_t seed_elems, int32_t batch, int dtype, void* dseeds,
-                                hipStream_t stream);
+// The sum runs over min(batch, kPooledChunks) chunks of consecutive
+// sequences, each summed in order into `partial` (fp32 [chunks, seed
+// elements], workspace), then the partials in chunk order.
+constexpr int32_t kPooledChunks = 16;
+int32_t pooled_chunks(int32_t batch);
+hipError_t launch_pooled_reduce(const void* dq, int64_t seed_elems, int32_t batch, int dtype, float* partial,
+                                void* dseeds, hipStream_t stream);
 
 // BlockAttention: the runs of `block` tokens of every sequence as offsets
 // (see blocks.hip).

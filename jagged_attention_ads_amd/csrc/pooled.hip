@@ -7,9 +7,10 @@
 //   pooled_prep_kernel:   the per-sequence query offsets b * n_seeds and the
 //                         seeds repeated once per sequence (the queries of
 //                         the cross attention);
-//   pooled_reduce_kernel: the seeds' gradient, the sum over sequences of
-//                         their per-sequence query gradients, in fp32 and in
-//                         sequence order (no atomics: bitwise reproducible).
+//   pooled_partial_kernel, pooled_final_kernel: the seeds' gradient, the sum
+//                         over sequences of their per-sequence query
+//                         gradients, in fp32 and in a fixed order (no
+//                         atomics: bitwise reproducible).
 #include <algorithm>
 
 #include "jfa_common.hpp"
@@ -27,14 +28,29 @@ __global__ __launch_bounds__(256) void pooled_prep_kernel(const u32x4* seeds, in
   for (int64_t i = i0; i < total; i += stride) q[i] = seeds[i % seed_chunks];
 }
 
-// One thread per element of the seeds' gradient: the sum over the batch of
-// the same element of every sequence's n_seeds gradient rows.
+// The seeds' gradient in two passes, each element summed in a fixed order:
+// pass 1 sums the sequences of chunk c (sequences c*per .. c*per+per-1, in
+// order) into an fp32 partial, one thread per (element, chunk); pass 2 sums
+// the partials in chunk order and rounds once.
 template <typename T>
-__global__ __launch_bounds__(256) void pooled_reduce_kernel(const T* dq, int64_t seed_elems, int32_t batch, T* dseeds) {
+__global__ __launch_bounds__(256) void pooled_partial_kernel(const T* dq, int64_t seed_elems, int32_t batch,
+                                                             int32_t per, float* partial) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int32_t c = blockIdx.y;
+  if (e >= seed_elems) return;
+  const int32_t b0 = c * per, b1 = min(batch, b0 + per);
+  float acc = 0.f;
+  for (int32_t b = b0; b < b1; ++b) acc += (float)dq[(int64_t)b * seed_elems + e];
+  partial[(int64_t)c * seed_elems + e] = acc;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void pooled_final_kernel(const float* partial, int64_t seed_elems, int32_t chunks,
+                                                           T* dseeds) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= seed_elems) return;
   float acc = 0.f;
-  for (int32_t b = 0; b < batch; ++b) acc += (float)dq[(int64_t)b * seed_elems + e];
+  for (int32_t c = 0; c < chunks; ++c) acc += partial[(int64_t)c * seed_elems + e];
   dseeds[e] = (T)acc;
 }
 
@@ -49,16 +65,28 @@ hipError_t launch_pooled_prep(const void* seeds, int64_t seed_bytes, int32_t bat
   return hipGetLastError();
 }
 
-hipError_t launch_pooled_reduce(const void* dq, int64_t seed_elems, int32_t batch, int dtype, void* dseeds,
-                                hipStream_t stream) {
-  const unsigned grid = (unsigned)((seed_elems + 255) / 256);
-  if (grid == 0) return hipSuccess;
-  if (dtype == 0)
-    hipLaunchKernelGGL(pooled_reduce_kernel<__bf16>, dim3(grid), dim3(256), 0, stream, static_cast<const __bf16*>(dq),
-                       seed_elems, batch, static_cast<__bf16*>(dseeds));
-  else
-    hipLaunchKernelGGL(pooled_reduce_kernel<float>, dim3(grid), dim3(256), 0, stream, static_cast<const float*>(dq),
-                       seed_elems, batch, static_cast<float*>(dseeds));
+int32_t pooled_chunks(int32_t batch) { return std::max(1, std::min<int32_t>(kPooledChunks, batch)); }
+
+hipError_t launch_pooled_reduce(const void* dq, int64_t seed_elems, int32_t batch, int dtype, float* partial,
+                                void* dseeds, hipStream_t stream) {
+  const unsigned gx = (unsigned)((seed_elems + 255) / 256);
+  if (gx == 0) return hipSuccess;
+  // no sequences: pass 2 alone, over no partials, writes zeros
+  const int32_t chunks = batch > 0 ? pooled_chunks(batch) : 0;
+  const int32_t per = chunks > 0 ? (batch + chunks - 1) / chunks : 0;
+  if (dtype == 0) {
+    if (chunks > 0)
+      hipLaunchKernelGGL(pooled_partial_kernel<__bf16>, dim3(gx, (unsigned)chunks), dim3(256), 0, stream,
+                         static_cast<const __bf16*>(dq), seed_elems, batch, per, partial);
+    hipLaunchKernelGGL(pooled_final_kernel<__bf16>, dim3(gx), dim3(256), 0, stream, partial, seed_elems, chunks,
+                       static_cast<__bf16*>(dseeds));
+  } else {
+    if (chunks > 0)
+      hipLaunchKernelGGL(pooled_partial_kernel<float>, dim3(gx, (unsigned)chunks), dim3(256), 0, stream,
+                         static_cast<const float*>(dq), seed_elems, batch, per, partial);
+    hipLaunchKernelGGL(pooled_final_kernel<float>, dim3(gx), dim3(256), 0, stream, partial, seed_elems, chunks,
+                       static_cast<float*>(dseeds));
+  }
   return hipGetLastError();
 }
 

@@ -54,8 +54,8 @@ def test_pooled_parity(name):
 def test_pooled_equals_cross_attention_on_repeated_seeds(name):
     """The pooled calls are the jagged cross attention with the seeds
     repeated per sequence, bit for bit (out, lse, dK, dV), and the seeds'
-    gradient is the fp32 sum, in sequence order, of that attention's
-    per-sequence query gradients, rounded once."""
+    gradient is the fp32 sum, in the library's fixed order, of that
+    attention's per-sequence query gradients, rounded once."""
     b = _batch(name)
     wl = b.workload
     d = Dev(b)
@@ -72,10 +72,17 @@ def test_pooled_equals_cross_attention_on_repeated_seeds(name):
         assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
     assert torch.equal(dk.view(torch.uint8), dk2.view(torch.uint8))
     assert torch.equal(dv.view(torch.uint8), dv2.view(torch.uint8))
+    # the library's order: fp32 sums over chunks of consecutive sequences
+    # (min(16, B) chunks of ceil(B / chunks)), then over the chunks
     parts = dq2.float().cpu().numpy().reshape(B, n, *d.q.shape[1:])
+    chunks = min(16, B)
+    per = -(-B // chunks)
     acc = np.zeros(parts.shape[1:], dtype=np.float32)
-    for i in range(B):
-        acc = acc + parts[i]
+    for c in range(chunks):
+        part = np.zeros(parts.shape[1:], dtype=np.float32)
+        for i in range(c * per, min(B, c * per + per)):
+            part = part + parts[i]
+        acc = acc + part
     want = torch.from_numpy(acc).to(d.q.dtype)
     assert torch.equal(ds.cpu().view(torch.uint8), want.view(torch.uint8))
 
@@ -103,3 +110,20 @@ def test_pooled_full_size_sampled():
         check_forward(out[sl], lse[:, sl], ro, rl, "softmax")
         _, rdk, rdv = oracle.pooled_bwd(b.f64("q"), b.f64("k")[k0:k1], b.f64("v")[k0:k1], b.f64("dout")[sl], one, s)
         check_backward((ds, dk[k0:k1], dv[k0:k1]), (ref_ds, rdk, rdv), k_off=one)
+
+
+def test_pooled_no_sequences_gives_zero_seed_gradient():
+    """batch 0: nothing to pool, and the seeds' gradient (the sum over no
+    sequences) is written as zeros over a NaN canary."""
+    dev = torch.device("cuda:0")
+    seeds = torch.randn((4, 2, 64), device=dev).to(torch.bfloat16)
+    k = torch.empty((0, 2, 64), device=dev, dtype=torch.bfloat16)
+    ko = torch.zeros(1, dtype=torch.int32, device=dev)
+    ds = torch.full_like(seeds, float("nan"))
+    L = jfa.lib()
+    P = lambda t: jfa._ptr(t)  # noqa: E731
+    st = L.jfa_pooled_backward(P(seeds), None, None, None, None, None, P(ko), 0, 4, 2, 64, 0, 0, 0.125, 0, 0, P(ds),
+                               None, None, None, 0, jfa._stream(), None)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(ds.float(), torch.zeros_like(ds.float()))
