@@ -34,6 +34,10 @@ Modules:
                ([GEM-MFU, Detailed notes: jagged input])
   bbs       -- Base Batch Shuffling, the batch former ahead of the path
                ([GEM-MFU, Detailed notes: Base Batch Shuffling item])
+  mx        -- MXFP8 attention forward: OCP Microscaling E4M3 operands and
+               the online quantisation of the softmax numerator
+               ([GEM-MFU, Key points: MXFP8], [GEM-MFU, Detailed notes:
+               MXFP8 item])
 
 Every function is pinned by tests marked "not gpu" against an independent
 brute-force implementation, library special cases, closed forms, invariants
@@ -42,6 +46,7 @@ and finite differences.
 
 from .attention import attention_fwd, attention_bwd, visible_mask  # noqa: F401
 from .bbs import bbs_plan, merged_loads  # noqa: F401
+from .mx import mx_attention_fwd, mx_quantize_keys, mx_quantize_rows  # noqa: F401
 from .pooled import pooled_bwd, pooled_fwd  # noqa: F401
 from .rope import rope, sequence_positions  # noqa: F401
 from .schedule import (  # noqa: F401

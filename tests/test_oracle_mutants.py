@@ -146,3 +146,60 @@ def test_block_mistakes_are_caught(monkeypatch, mutant, activation):
     monkeypatch.undo()
     ref, _ = brute_force_block_fwd(q, k, v, qo, 0.6, activation, True, 3)
     assert np.abs(out - ref).max() > 1e-3
+
+
+# ------------------------------------------------------------------ MXFP8
+
+
+def _mx_loop_mismatch(monkeypatch, causal=True):
+    from tests.test_oracle_mx import _loop_mx_attention
+    import oracle.mx as mx
+    rng = np.random.default_rng(31)
+    lq, lk = [3, 36], [40, 36]
+    qo = np.concatenate([[0], np.cumsum(lq)])
+    ko = np.concatenate([[0], np.cumsum(lk)])
+    q = rng.standard_normal((qo[-1], 1, 32)) * 2
+    k = rng.standard_normal((ko[-1], 1, 32))
+    v = rng.standard_normal((ko[-1], 1, 32)) * np.exp2(rng.integers(-5, 5, (ko[-1], 1, 32)))
+    out, _ = mx.mx_attention_fwd(q, k, v, qo, ko, 0.4, causal)
+    monkeypatch.undo()
+    ref, _ = _loop_mx_attention(q, k, v, qo, ko, 0.4, causal)
+    return np.abs(out - ref).max()
+
+
+def test_mx_global_block_alignment_is_caught(monkeypatch):
+    import oracle.mx as mx
+    orig = mx.mx_quantize_keys
+
+    def global_blocks(x, offsets):
+        return orig(x, [0, np.asarray(x).shape[0]])   # blocks counted from row 0 of the packed tensor
+    monkeypatch.setattr(mx, "mx_quantize_keys", global_blocks)
+    assert _mx_loop_mismatch(monkeypatch) > 1e-6
+
+
+def test_mx_p_scale_from_rounded_max_is_caught(monkeypatch):
+    import oracle.mx as mx
+    orig_floor = np.floor
+
+    def quantize_p_round(t, vis):
+        monkeypatch.setattr(mx.np, "floor", np.round)
+        try:
+            return mx_quantize_p(t, vis)
+        finally:
+            monkeypatch.setattr(mx.np, "floor", orig_floor)
+    mx_quantize_p = mx.quantize_p
+    monkeypatch.setattr(mx, "quantize_p", quantize_p_round)
+    assert _mx_loop_mismatch(monkeypatch) > 1e-6
+
+
+def test_mx_quantised_denominator_is_caught():
+    import json
+    import os
+    import oracle.mx as mx
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "mx_cases.json")))
+    e = cases["p_examples"][0]
+    t = np.array(e["t"])
+    codes, fb = mx.quantize_p(t[None, :], np.ones((1, len(t)), bool))
+    w = mx.e4m3_decode(codes[0]) * 2.0 ** (fb[0, 0] - 8)
+    wrong = w / w.sum()          # normalised by the quantised weights instead of the exact ones
+    assert np.abs(wrong - np.array(e["out"])).max() > 1e-3
