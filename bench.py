@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "useful TFLOPS (unpadded tokens) fwd/bwd + % of bf16 MFMA peak, 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS   # dense fp8 (and MX fp8) products: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -183,6 +184,13 @@ def kernel_accounting(wl, T_q, T_k, pairs_total, n_ds_blocks, ds_path, short=(0,
                              bytes=3 * lq_bytes + 2 * lk_bytes + (2 * (T_q - sq) * H * 4 if soft else 0))
     if soft:      # reads O, dO and lse, writes delta (and lse in log2 units)
         acc["bwd_stats"] = dict(flops=2 * d * H * T_q, bytes=2 * q_bytes + 3 * row_f32)
+    if wl.mx:
+        # MXFP8: the quantisation reads Q, K, V (bf16) and writes their images
+        # (a byte per element plus a scale byte per 32); the attention reads
+        # the images and writes O (bf16) and lse
+        img = lambda rows: rows * H * d * (1 + 1.0 / 32)   # noqa: E731
+        acc = {"mx_quant": dict(flops=0, bytes=(T_q + 2 * T_k) * H * d * 2 + img(T_q) + 2 * img(T_k)),
+               "fwd": dict(flops=4 * d * H * pairs_total, bytes=img(T_q) + 2 * img(T_k) + T_q * H * d * 2 + row_f32)}
     return acc
 
 
@@ -254,6 +262,9 @@ def _cpu_unit(arg):
             oracle.pooled_bwd(c["q"][:, hs], k, v, c["do"][sq, hs], one_k, c["scale"], c["act"])
         return (14 if with_bwd else 4) * c["d"] * c["pairs"][b]
     q, k, v = c["q"][sq, hs], c["k"][sk, hs], c["v"][sk, hs]
+    if c["mx"]:   # MXFP8 forward (its V blocks start at each sequence: one sequence alone is the same)
+        oracle.mx_attention_fwd(q, k, v, one_q, one_k, c["scale"], c["causal"])
+        return 4 * c["d"] * c["pairs"][b]
     oracle.attention_fwd(q, k, v, one_q, one_k, c["scale"], c["act"], c["causal"], block=blk, rope_base=c["rope"])
     if with_bwd:
         oracle.attention_bwd(q, k, v, c["do"][sq, hs], one_q, one_k, c["scale"], c["act"], c["causal"], block=blk,
@@ -283,7 +294,7 @@ def cpu_baseline(batch, budget_s):
     _CPU_BATCH.update(q=batch.f64("q"), k=batch.f64("k"), v=batch.f64("v"),
                       do=batch.f64("dout") if batch.dout is not None else None, qo=qo, ko=ko, block=blk,
                       scale=1.0 / math.sqrt(wl.head_dim), act=wl.activation, causal=wl.causal, d=wl.head_dim,
-                      pairs=pairs, rope=wl.rope_base or None, pooled=bool(wl.n_seeds))
+                      pairs=pairs, rope=wl.rope_base or None, pooled=bool(wl.n_seeds), mx=wl.mx)
     B, H = len(pairs), wl.heads
     with_bwd = bool(wl.backward and batch.dout is not None)
     dense = (np.diff(qo) * np.diff(ko)).astype(np.float64)   # the oracle's work follows Lq * Lk
@@ -326,9 +337,9 @@ def cpu_baseline(batch, budget_s):
     _CPU_BATCH.clear()
     return {
         "value": flops / el / 1e12, "unit": "TFLOPS", "cores": workers, "kind": "oracle",
-        "sample": "fp64 NumPy oracle, %s, every %d-th sequence of the same batch (%d of %d sequences x %d heads, "
+        "sample": "fp64 NumPy oracle%s, %s, every %d-th sequence of the same batch (%d of %d sequences x %d heads, "
                   "%.3g useful GFLOP, %.1f s); %d worker processes with single-threaded BLAS, (sequence, head) "
-                  "units longest first" % ("fwd+bwd" if with_bwd else "fwd", stride, len(sample), B, H,
+                  "units longest first" % (" (MXFP8)" if wl.mx else "", "fwd+bwd" if with_bwd else "fwd", stride, len(sample), B, H,
                                            flops / 1e9, el, workers),
         "cpu_model": cpu_model(),
         "fwd_tflops": res["fwd"][0] / res["fwd"][1] / 1e12,
@@ -365,7 +376,7 @@ class Runner:
     library calls of a step (through the C ABI's profiled entry points, which
     record caller events between launches)."""
 
-    def __init__(self, wl, batch, dev):
+    def __init__(self, wl, batch, dev, mx_mode="attend"):
         import torch
         from jagged_attention_ads_amd import jfa
         self.torch, self.jfa = torch, jfa
@@ -415,7 +426,27 @@ class Runner:
             mq = mk = min(wl.block, mq)
             self.q_lens = self.kv_lens = block_runs(batch.q_lengths, wl.block)
         self.qo, self.ko, self.B, self.mq, self.mk = qo, ko, B, mq, mk
-        if wl.n_seeds:
+        # the forward call's event slots: its kernels between consecutive
+        # slots, its end at the last
+        # MXFP8: "attend" takes the operands as MX images, resident like
+        # any input (the pages fuse the quantisation into the producing
+        # norm / projection kernels); "forward" takes bf16 and quantises
+        # them first (jfa_mx_forward)
+        self.mx_mode = mx_mode if wl.mx else None
+        self.fwd_slots = {"sched_q": (0, 1), "fwd": (1, 2)}
+        if self.mx_mode == "forward":
+            self.fwd_slots = {"mx_quant": (0, 1), "sched_q": (1, 2), "fwd": (2, 3)}
+        self.nf = max(b for _, b in self.fwd_slots.values()) + 1
+        self.fwd_end = self.nf - 1
+        if wl.mx:
+            self.ws_f = torch.empty(max(L.jfa_mx_workspace_size(B, H, D, T_q, T_k, int(mx_mode == "forward")), 1),
+                                    dtype=torch.uint8, device=dev)
+            self.ws_b = None
+            if mx_mode == "attend":
+                self.images = [jfa.mx_quantize(t, o, lay) for t, o, lay in
+                               ((self.q, qo, "rows"), (self.k, ko, "rows"), (self.v, ko, "keys"))]
+                torch.cuda.synchronize()
+        elif wl.n_seeds:
             dtc = jfa.DTYPES[self.q.dtype]
             self.ws_f = torch.empty(L.jfa_pooled_workspace_size(B, wl.n_seeds, H, D, T_k, mk, dtc, 0),
                                     dtype=torch.uint8, device=dev)
@@ -433,7 +464,7 @@ class Runner:
             self.ws_b = jfa.workspace(B, H, D, T_q, T_k, mk, self.q.dtype, True, dev)
         # the dK/dV pass stores dS and the dQ pass reads it, unless switched
         # off or the store was left out of the workspace
-        self.ds_path = (not wl.rope_base and not wl.n_seeds and os.environ.get("JFA_BWD_DS") != "0"
+        self.ds_path = (not wl.rope_base and not wl.n_seeds and not wl.mx and os.environ.get("JFA_BWD_DS") != "0"
                         and self.ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, mk, self.q.dtype, 2))
         # the dK/dV pass writes the dQ of short sequences (bf16, d 64 or 128:
         # where its LDS has room) when every sequence is short, or always with
@@ -446,8 +477,31 @@ class Runner:
         self.lse_arg = self.lse if wl.activation == "softmax" else None
         self.run_bwd = wl.backward
 
+    def slots(self, name):
+        """(side, first event, second event) around kernel `name`."""
+        if name in self.fwd_slots:
+            return (0,) + self.fwd_slots[name]
+        return SLOTS[name]
+
     def fwd(self, events):
         ev = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
+        if self.mx_mode == "attend":
+            qi, ki, vi = self.images
+            st = self.L.jfa_mx_attend(
+                self.P(qi), self.P(ki), self.P(vi), self.P(self.qo), self.P(self.ko), self.B, self.H,
+                self.D, self.T_q, self.T_k, self.mq, self.mk, self.scale, int(self.wl.causal), self.P(self.out),
+                self.P(self.lse), self.P(self.ws_f), self.ws_f.numel(), self.stream, ev)
+            if st != 0:
+                raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+            return
+        if self.mx_mode == "forward":
+            st = self.L.jfa_mx_forward(
+                self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.qo), self.P(self.ko), self.B, self.H,
+                self.D, self.T_q, self.T_k, self.mq, self.mk, self.scale, int(self.wl.causal), self.P(self.out),
+                self.P(self.lse), self.P(self.ws_f), self.ws_f.numel(), self.stream, ev)
+            if st != 0:
+                raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+            return
         if self.wl.n_seeds:
             st = self.L.jfa_pooled_forward(
                 self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.ko), self.B, self.wl.n_seeds, self.H,
@@ -523,7 +577,7 @@ def timed_steps(r, ev, K, flush_buf, dom=None):
     that kernel (side 0: the forward's event slots, 1: the backward's).
     Returns per-step lists of milliseconds: step, fwd, bwd, dominant kernel,
     and the whole timed region."""
-    nf, nb = 3, 5
+    nf, nb = r.nf, 5
     evs = []
     for _ in range(K):
         ef, eb = (ctypes.c_void_p * nf)(), (ctypes.c_void_p * nb)()
@@ -532,7 +586,7 @@ def timed_steps(r, ev, K, flush_buf, dom=None):
         if r.run_bwd:
             eb[0], eb[4] = made[1], made[2]
         else:
-            ef[2] = made[2]
+            ef[r.fwd_end] = made[2]
         if dom is not None:
             arr = ef if dom[0] == 0 else eb
             # the two slots may coincide with the step events (e.g. forward-only)
@@ -551,13 +605,13 @@ def timed_steps(r, ev, K, flush_buf, dom=None):
     r.torch.cuda.synchronize()
     out = {"step": [], "fwd": [], "bwd": [], "dom": [], "region": ev.ms(edge[0], edge[1])}
     for ef, eb, made in evs:
-        end = eb[4] if r.run_bwd else ef[2]
+        end = eb[4] if r.run_bwd else ef[r.fwd_end]
         out["step"].append(ev.ms(ef[0], end))
         if r.run_bwd:
             out["fwd"].append(ev.ms(ef[0], eb[0]))
             out["bwd"].append(ev.ms(eb[0], eb[4]))
         else:
-            out["fwd"].append(ev.ms(ef[0], ef[2]))
+            out["fwd"].append(ev.ms(ef[0], ef[r.fwd_end]))
         if dom is not None:
             arr = ef if dom[0] == 0 else eb
             out["dom"].append(ev.ms(arr[dom[1]], arr[dom[2]]))
@@ -570,7 +624,7 @@ def kernel_breakdown(r, ev, K, flush_buf):
     """Mean per-kernel milliseconds from K steps with an event between every
     two launches (each event adds a few microseconds between launches, so
     these steps are not the timed ones)."""
-    ef = [ev.create(3) for _ in range(K)]
+    ef = [ev.create(r.nf) for _ in range(K)]
     eb = [ev.create(5) for _ in range(K)] if r.run_bwd else []
     r.torch.cuda.synchronize()
     for i in range(K):
@@ -581,7 +635,7 @@ def kernel_breakdown(r, ev, K, flush_buf):
 
     def avg(lst, a, b):
         return float(np.mean([ev.ms(e[a], e[b]) for e in lst])) if lst else 0.0
-    kern = {"sched_q": avg(ef, 0, 1), "fwd": avg(ef, 1, 2)}
+    kern = {n: avg(ef, a, b) for n, (a, b) in r.fwd_slots.items()}
     if r.run_bwd:
         kern.update({"bwd_sched": avg(eb, 0, 1), "bwd_stats": avg(eb, 1, 2), "bwd_dkdv": avg(eb, 2, 3),
                      "bwd_dq": avg(eb, 3, 4)})
@@ -736,7 +790,7 @@ def main():
     name = max((n for n in acct if n in kern_ms), key=lambda n: kern_ms[n])   # the dominant kernel
 
     # the timed steps: headline (flushed unless --warm), then the same warm
-    t = timed_steps(r, ev, K, flush_buf, SLOTS[name])
+    t = timed_steps(r, ev, K, flush_buf, r.slots(name))
     t_warm = timed_steps(r, ev, K, warm_buf) if flush_buf is not None else None
     ms_step = float(np.median(t["step"]))
     D, H = r.D, r.H
@@ -752,10 +806,13 @@ def main():
     a = acct[name]
     ai = a["flops"] / a["bytes"]
     digest = kernel_source_digest()
-    if ai < RIDGE:
+    # the MXFP8 attention's products run at the fp8 rate
+    peak_mfma = PEAK_FP8_TFLOPS if wl.mx and name == "fwd" else PEAK_BF16_TFLOPS
+    if ai < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
         roof = {"bound": "hbm", "achieved": a["bytes"] / t_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": a["flops"] / t_s / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": a["flops"] / t_s / 1e12, "peak": peak_mfma, "unit": "TFLOP/s",
+                "peak_dtype": "fp8 (MX E4M3)" if peak_mfma == PEAK_FP8_TFLOPS else "bf16"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(name, digest, wl.name)
     roof.update({
@@ -765,7 +822,7 @@ def main():
         "kernel": name, "avg_launch_us": dom_ms * 1e3,
         "algorithmic_bytes": a["bytes"], "algorithmic_flops": a["flops"], "arith_intensity": ai,
         "workspace_ds_bytes": a.get("ds_store_bytes", 0),
-        "mfma_frac": a["flops"] / t_s / 1e12 / PEAK_BF16_TFLOPS})
+        "mfma_frac": a["flops"] / t_s / 1e12 / peak_mfma})
 
     def pass_summary(useful, ms, target):
         if ms is None:
@@ -776,7 +833,9 @@ def main():
     res = {
         "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wl.dtype, "data": "synthetic (seeded; lengths and values drawn per the workload recipe)",
+        "dtype": ("mxfp8 (E4M3 operands, E8M0 block scales, fp32 accumulation; bf16 in and out)" if wl.mx
+                  else wl.dtype),
+        "data": "synthetic (seeded; lengths and values drawn per the workload recipe)",
         "config": {"workload": wl.description, "name": wl.name, "batch": r.B, "heads": H, "head_dim": D,
                    "causal": wl.causal, "activation": wl.activation, "seed": args.seed, "total_q_tokens": r.T_q,
                    "total_kv_tokens": r.T_k, "visible_pairs_per_head": pairs, "block": wl.block,
@@ -796,6 +855,38 @@ def main():
         "kernel_source_digest": digest,
         "roofline": roof,
     }
+    if wl.mx:
+        # the bf16 forward on the same batch, and the MXFP8 path from bf16
+        # inputs (quantisation included), timed the same way: the pages quote
+        # MXFP8's forward gain over the 16-bit kernel
+        res["fwd"]["pct_of_fp8_peak"] = 100.0 * res["fwd"]["tflops"] / PEAK_FP8_TFLOPS
+        import dataclasses
+        rb = Runner(dataclasses.replace(wl, mx=False), batch, dev)
+        rb.run_bwd = False
+        for _ in range(3):
+            rb.step()
+        tb = timed_steps(rb, ev, K, flush_buf)
+        bms = float(np.median(tb["fwd"]))
+        kb = kernel_breakdown(rb, ev, K, flush_buf)
+        res["bf16_forward"] = {"median_us": bms * 1e3, "tflops": tf(useful_fwd, bms),
+                               "kernel_us": {k_: v_ * 1e3 for k_, v_ in kb.items()},
+                               "mx_speedup": bms / fwd_ms,
+                               "mx_kernel_speedup": kb["fwd"] / kern_ms["fwd"],
+                               "timing": "the same batch through jfa_forward (bf16), timed as the headline"}
+        del rb
+        rq = Runner(wl, batch, dev, mx_mode="forward")
+        for _ in range(3):
+            rq.step()
+        tq = timed_steps(rq, ev, K, flush_buf)
+        qms = float(np.median(tq["fwd"]))
+        kq = kernel_breakdown(rq, ev, K, flush_buf)
+        qa = acct["mx_quant"]
+        res["mx_from_bf16"] = {"median_us": qms * 1e3, "tflops": tf(useful_fwd, qms), "vs_bf16_forward": bms / qms,
+                               "kernel_us": {k_: v_ * 1e3 for k_, v_ in kq.items()},
+                               "mx_quant_hbm_frac": qa["bytes"] / (kq["mx_quant"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               "timing": "jfa_mx_forward (bf16 q, k, v quantised, then attended), timed as the "
+                                         "headline"}
+        del rq
     if t_warm is not None:
         wms = float(np.median(t_warm["step"]))
         res["warm"] = {"value": tf(useful_fwd + useful_bwd, wms), "ms_per_step": wms,

@@ -334,6 +334,75 @@ int jfa_pooled_backward(const void* seeds, const void* k, const void* v, const v
                         int32_t dtype, void* dseeds, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         hipStream_t stream, hipEvent_t* events);
 
+/* MXFP8 attention forward (page piletech.kr/articles/112134, section 핵심
+ * 포인트 / Key points, MXFP8 bullet, and section 상세 정리 / Detailed
+ * notes, MXFP8 item: training in a microscaled 8-bit format, with the
+ * softmax output quantised online).  Number format: OCP Microscaling
+ * Formats (MX) v1.0, MXFP8 E4M3: blocks of 32 elements share an E8M0 scale
+ * 2^(floor(log2 max|x|) - 8) (at least 2^-127); each element is x / scale
+ * rounded to the nearest E4M3 value, ties to even, magnitudes beyond 448
+ * clamped to 448.  jfa_mx_forward computes softmax attention (layouts,
+ * offsets, causal rule and outputs as for jfa_forward, bf16 only, head_dim
+ * 64 or 128) from the MXFP8 quantisations of q and k (blocks of 32
+ * head-dim elements) and of v (blocks of 32 consecutive keys of a
+ * sequence, counted from its first key, per column), with the weights
+ * quantised as well: a row's weights 2^(t_j - m) (t_j = scale log2(e)
+ * q.k_j, m the row max) in blocks of 32 consecutive keys counted from the
+ * sequence's first key, the block's scale taken from its largest visible
+ * weight; invisible keys weigh 0.  The normaliser and lse use the exact
+ * weights.  Arithmetic: the products of the 8-bit operands accumulate in
+ * fp32; out is rounded to bf16.  Workspace: jfa_mx_workspace_size with
+ * with_images = 1 (256-byte aligned; it holds the work list and the three
+ * MX images); events: NULL, or 4 events recorded before the quantisation,
+ * after it, after the work list and after the attention kernel.  Errors as
+ * for jfa_forward with activation softmax and dtype bf16, plus
+ * JFA_ERR_UNSUPPORTED for head_dim other than 64 and 128 and
+ * JFA_ERR_INVALID_ARGUMENT for a workspace not 256-byte aligned.
+ *
+ * jfa_mx_attend is the same attention from operands already in MXFP8: the
+ * images of q and k (JFA_MX_ROWS) and of v (JFA_MX_KEYS) that
+ * jfa_mx_quantize writes, or that a producer fusing the quantisation into
+ * its own epilogue writes in that layout (the pages fuse it into the norm
+ * and projection kernels).  jfa_mx_forward(q, k, v) equals jfa_mx_quantize
+ * of each followed by jfa_mx_attend, bit for bit.  Workspace:
+ * jfa_mx_workspace_size with with_images = 0 (the work list); events:
+ * NULL, or 3 events, as for jfa_forward_profiled.  Errors as for
+ * jfa_mx_forward, plus JFA_ERR_INVALID_ARGUMENT for an image not 256-byte
+ * aligned.
+ *
+ * jfa_mx_quantize writes the MX image of one bf16 tensor x [total, heads,
+ * head_dim] (offsets as for jfa_forward) into `image` (jfa_mx_image_bytes,
+ * 256-byte aligned): uint8 E4M3 codes at byte 0, uint8 E8M0 scale codes
+ * (value 2^(code - 127)) at byte align256(heads * 32 N * head_dim), with N =
+ * total / 32 + batch block rows; row i of sequence b is image row
+ * 32 (offsets[b] / 32 + b) + i (block row offsets[b] / 32 + b + i / 32).
+ *   JFA_MX_ROWS (q, k): codes [heads][32 N][head_dim], scales [heads][32 N]
+ *     [head_dim / 32], blocks of 32 consecutive elements of a row.
+ *   JFA_MX_KEYS (v): codes [heads][N][head_dim][32]: within a column, row
+ *     i of the block at byte 16 ((i / 4) % 2) + 4 (i / 8) + i % 4 (the order
+ *     the attention kernel's weights arrive in); scales [heads][N][32]
+ *     [head_dim / 32], column 32 c + r at [r][c]; blocks of 32 consecutive
+ *     rows of a sequence, per column.
+ * Image rows past the end of a sequence's last block hold zero codes; rows
+ * in no sequence's blocks are not written.  Errors: those of the sizes as
+ * for jfa_forward, JFA_ERR_UNSUPPORTED for head_dim other than 64 and 128,
+ * JFA_ERR_INVALID_ARGUMENT for a bad layout or NULL / misaligned pointers,
+ * JFA_ERR_WORKSPACE_TOO_SMALL for image_bytes below jfa_mx_image_bytes. */
+enum jfa_mx_layout { JFA_MX_ROWS = 0, JFA_MX_KEYS = 1 };
+size_t jfa_mx_image_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t total);
+int jfa_mx_quantize(const void* x, const int32_t* offsets, int32_t batch, int32_t heads, int32_t head_dim,
+                    int32_t total, int32_t layout, void* image, size_t image_bytes, hipStream_t stream);
+size_t jfa_mx_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
+                             int32_t with_images);
+int jfa_mx_forward(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
+                   int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
+                   int32_t max_q_len, int32_t max_kv_len, float scale, int32_t causal, void* out, float* lse,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+int jfa_mx_attend(const void* q_image, const void* k_image, const void* v_image, const int32_t* q_offsets,
+                  const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                  int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t causal, void* out,
+                  float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+
 /* Device check of the offsets (debug; the jagged-input item's offsets
  * contract).  With JFA_CHECK_OFFSETS=1 in the environment, the work-list
  * builder of jfa_forward and jfa_backward first checks on the device that

@@ -699,13 +699,212 @@ int jfa_pooled_backward(const void* seeds, const void* k, const void* v, const v
                        workspace_bytes - L.off_inner, stream, later, jfa::RopeArgs{});
     if (st != JFA_OK) return st;
   }
-  // with no sequences the seeds' gradient is zero: the sum over none
   // with no sequences the sum is over none: zeros (no workspace is read)
   e = jfa::launch_pooled_reduce(batch > 0 ? ws + L.off_dq : nullptr, seed_elems, batch, dtype,
                                 batch > 0 ? reinterpret_cast<float*>(ws + L.off_part) : nullptr, dseeds, stream);
   if (e != hipSuccess) return hip_fail(e, "pooled reduce kernel launch");
   if ((e = record(events, 4, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;
+}
+
+// ------------------------------------------------------------------ MXFP8
+
+}  // extern "C"
+
+namespace {
+
+// An MX image: codes, then the E8M0 scale codes, each 256-byte aligned.
+struct MxImageLayout {
+  int64_t nbr = 0;
+  size_t scales = 0, bytes = 0;
+};
+MxImageLayout mx_image_layout(int32_t batch, int32_t heads, int32_t head_dim, int32_t total) {
+  MxImageLayout L;
+  L.nbr = jfa::mx_block_rows(batch, total);
+  const size_t rows = static_cast<size_t>(heads) * static_cast<size_t>(L.nbr) * 32;
+  L.scales = align256(rows * static_cast<size_t>(head_dim));
+  L.bytes = L.scales + align256(rows * static_cast<size_t>(head_dim / 32));
+  return L;
+}
+
+int mx_check_sizes(int32_t batch, int32_t heads, int32_t head_dim, int32_t total) {
+  int st = check_sizes(batch, heads, 64, total, 0, 0, 0);
+  if (st != JFA_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return fail(JFA_ERR_UNSUPPORTED, "MXFP8 needs head_dim 64 or 128");
+  if (int64_t(total) * heads * head_dim >= (int64_t(1) << 31))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "tensor has 2^31 or more elements");
+  return JFA_OK;
+}
+
+struct MxWsLayout {
+  jfa::WorklistLayout wq{};
+  MxImageLayout iq{}, ik{};
+  size_t off_wq = 0, off_q = 0, off_k = 0, off_v = 0, bytes = 0;
+};
+// the offsets-check word, the query-tile list, then the images of Q, K, V
+MxWsLayout mx_ws_layout(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv) {
+  MxWsLayout L;
+  L.wq = jfa::worklist_layout(jfa::kPassQ, batch, heads, total_q);
+  L.off_wq = kStatusBytes;
+  L.iq = mx_image_layout(batch, heads, head_dim, total_q);
+  L.ik = mx_image_layout(batch, heads, head_dim, total_kv);
+  L.off_q = align256(L.off_wq + L.wq.bytes);
+  L.off_k = L.off_q + L.iq.bytes;
+  L.off_v = L.off_k + L.ik.bytes;
+  L.bytes = L.off_v + L.ik.bytes;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t jfa_mx_image_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t total) {
+  if (mx_check_sizes(batch, heads, head_dim, total) != JFA_OK) return 0;
+  return mx_image_layout(batch, heads, head_dim, total).bytes;
+}
+
+int jfa_mx_quantize(const void* x, const int32_t* offsets, int32_t batch, int32_t heads, int32_t head_dim,
+                    int32_t total, int32_t layout, void* image, size_t image_bytes, hipStream_t stream) {
+  int st = mx_check_sizes(batch, heads, head_dim, total);
+  if (st != JFA_OK) return st;
+  if (layout != JFA_MX_ROWS && layout != JFA_MX_KEYS) return fail(JFA_ERR_INVALID_ARGUMENT, "bad MX layout");
+  if (!offsets) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL offsets pointer");
+  if (total > 0 && !x) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL input pointer");
+  if (!aligned16(x)) return fail(JFA_ERR_INVALID_ARGUMENT, "input not 16-byte aligned");
+  const MxImageLayout L = mx_image_layout(batch, heads, head_dim, total);
+  if (!image || (reinterpret_cast<uintptr_t>(image) & 255u) != 0)
+    return fail(JFA_ERR_INVALID_ARGUMENT, "NULL or not 256-byte aligned image");
+  if (image_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "image buffer too small");
+  if (batch == 0 || total == 0) return JFA_OK;
+  jfa::MxQuantArgs a{};
+  a.x[0] = x;
+  a.off[0] = offsets;
+  a.total[0] = total;
+  a.nbr[0] = static_cast<int32_t>(L.nbr);
+  a.keys[0] = layout == JFA_MX_KEYS ? 1 : 0;
+  a.codes[0] = static_cast<uint8_t*>(image);
+  a.scales[0] = static_cast<uint8_t*>(image) + L.scales;
+  a.batch = batch;
+  a.heads = heads;
+  hipError_t e = jfa::launch_mx_quant(a, head_dim, 1, stream);
+  if (e != hipSuccess) return hip_fail(e, "MX quantisation kernel launch");
+  return JFA_OK;
+}
+
+size_t jfa_mx_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
+                             int32_t with_images) {
+  if (mx_check_sizes(batch, heads, head_dim, total_q) != JFA_OK) return 0;
+  if (mx_check_sizes(batch, heads, head_dim, total_kv) != JFA_OK) return 0;
+  if (with_images != 0 && with_images != 1) return 0;
+  const MxWsLayout L = mx_ws_layout(batch, heads, head_dim, total_q, total_kv);
+  return with_images ? L.bytes : L.off_q;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The attention from MX images: the work list (events [0] before, [1]
+// after) and the kernel ([2] after).  Arguments already checked.
+int mx_attend_impl(const uint8_t* qimg, const uint8_t* kimg, const uint8_t* vimg, const int32_t* q_offsets,
+                   const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                   int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t causal, void* out,
+                   float* lse, char* ws, hipStream_t stream, hipEvent_t e0, hipEvent_t e1, hipEvent_t e2) {
+  const MxWsLayout L = mx_ws_layout(batch, heads, head_dim, total_q, total_kv);
+  hipError_t e;
+  if (e0 && (e = hipEventRecord(e0, stream)) != hipSuccess) return hip_fail(e, "event record");
+  e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, buckets_for(max_kv_len, jfa::kFwdBN),
+                        ws + L.off_wq, L.wq, offset_check(ws, total_q, total_kv, max_q_len, max_kv_len), stream);
+  if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+  if (e1 && (e = hipEventRecord(e1, stream)) != hipSuccess) return hip_fail(e, "event record");
+  jfa::MxFwdArgs a{};
+  a.qx = qimg;
+  a.qs = qimg + L.iq.scales;
+  a.kx = kimg;
+  a.ks = kimg + L.ik.scales;
+  a.vx = vimg;
+  a.vs = vimg + L.ik.scales;
+  a.rq = 32 * L.iq.nbr;
+  a.rk = 32 * L.ik.nbr;
+  a.meta = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + L.wq.meta_off);
+  a.out = out;
+  a.lse = lse;
+  a.heads = heads;
+  a.total_q = total_q;
+  a.causal = causal;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  e = jfa::launch_mx_fwd(a, head_dim, L.wq.capacity, stream);
+  if (e != hipSuccess) return hip_fail(e, "MXFP8 forward kernel launch");
+  if (e2 && (e = hipEventRecord(e2, stream)) != hipSuccess) return hip_fail(e, "event record");
+  return JFA_OK;
+}
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int jfa_mx_forward(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
+                   int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv,
+                   int32_t max_q_len, int32_t max_kv_len, float scale, int32_t causal, void* out, float* lse,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  int st = jfa::forward_args_status(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv,
+                                    max_q_len, max_kv_len, scale, JFA_ACT_SOFTMAX, causal, JFA_DTYPE_BF16, out, lse);
+  if (st != JFA_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return fail(JFA_ERR_UNSUPPORTED, "MXFP8 needs head_dim 64 or 128");
+  if (batch == 0 || total_q == 0) return JFA_OK;   // nothing to write
+  const MxWsLayout L = mx_ws_layout(batch, heads, head_dim, total_q, total_kv);
+  if (!workspace || workspace_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  if (!aligned256(workspace)) return fail(JFA_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e;
+  if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
+  jfa::MxQuantArgs qa{};
+  const void* src[3] = {q, k, v};
+  const int32_t* offs[3] = {q_offsets, kv_offsets, kv_offsets};
+  const int32_t tot[3] = {total_q, total_kv, total_kv};
+  const size_t base[3] = {L.off_q, L.off_k, L.off_v};
+  const MxImageLayout* lay[3] = {&L.iq, &L.ik, &L.ik};
+  for (int z = 0; z < 3; ++z) {
+    qa.x[z] = src[z];
+    qa.off[z] = offs[z];
+    qa.total[z] = tot[z];
+    qa.nbr[z] = tot[z] > 0 ? static_cast<int32_t>(lay[z]->nbr) : 0;
+    qa.keys[z] = z == 2 ? 1 : 0;
+    qa.codes[z] = reinterpret_cast<uint8_t*>(ws + base[z]);
+    qa.scales[z] = reinterpret_cast<uint8_t*>(ws + base[z] + lay[z]->scales);
+  }
+  qa.batch = batch;
+  qa.heads = heads;
+  e = jfa::launch_mx_quant(qa, head_dim, 3, stream);
+  if (e != hipSuccess) return hip_fail(e, "MX quantisation kernel launch");
+  return mx_attend_impl(reinterpret_cast<const uint8_t*>(ws + L.off_q), reinterpret_cast<const uint8_t*>(ws + L.off_k),
+                        reinterpret_cast<const uint8_t*>(ws + L.off_v), q_offsets, kv_offsets, batch, heads, head_dim,
+                        total_q, total_kv, max_q_len, max_kv_len, scale, causal, out, lse, ws, stream,
+                        events ? events[1] : nullptr, events ? events[2] : nullptr, events ? events[3] : nullptr);
+}
+
+int jfa_mx_attend(const void* q_image, const void* k_image, const void* v_image, const int32_t* q_offsets,
+                  const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                  int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t causal, void* out,
+                  float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  // the images stand where the bf16 values would: same pointer and size rules
+  int st = jfa::forward_args_status(q_image, k_image, v_image, q_offsets, kv_offsets, batch, heads, head_dim, total_q,
+                                    total_kv, max_q_len, max_kv_len, scale, JFA_ACT_SOFTMAX, causal, JFA_DTYPE_BF16,
+                                    out, lse);
+  if (st != JFA_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return fail(JFA_ERR_UNSUPPORTED, "MXFP8 needs head_dim 64 or 128");
+  if (!aligned256(q_image) || !aligned256(k_image) || !aligned256(v_image))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "image not 256-byte aligned");
+  if (batch == 0 || total_q == 0) return JFA_OK;
+  const MxWsLayout L = mx_ws_layout(batch, heads, head_dim, total_q, total_kv);
+  if (!workspace || workspace_bytes < L.off_q) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  return mx_attend_impl(static_cast<const uint8_t*>(q_image), static_cast<const uint8_t*>(k_image),
+                        static_cast<const uint8_t*>(v_image), q_offsets, kv_offsets, batch, heads, head_dim, total_q,
+                        total_kv, max_q_len, max_kv_len, scale, causal, out, lse, static_cast<char*>(workspace), stream,
+                        events ? events[0] : nullptr, events ? events[1] : nullptr, events ? events[2] : nullptr);
 }
 
 int jfa_check_device_error(const void* workspace, hipStream_t stream) {

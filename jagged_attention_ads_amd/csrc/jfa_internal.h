@@ -157,6 +157,49 @@ int32_t pooled_chunks(int32_t batch);
 hipError_t launch_pooled_reduce(const void* dq, int64_t seed_elems, int32_t batch, int dtype, float* partial,
                                 void* dseeds, hipStream_t stream);
 
+// MXFP8 (see mx.hip).  Images index a sequence's rows from a 32-row
+// boundary: row i of sequence b at image row 32 (off[b]/32 + b) + i, in
+// mx_block_rows(batch, total) blocks of 32 rows.
+inline int64_t mx_block_rows(int32_t batch, int32_t total) { return (int64_t)total / 32 + batch; }
+
+// Up to three bf16 [total, heads, D] tensors into MX images in one launch.
+// Row image (keys = 0): codes [heads][32 nbr][D], E8M0 scale codes
+// [heads][32 nbr][D/32], blocks of 32 elements along a row.  Column image
+// (keys = 1): codes [heads][nbr][D][32] with key i of a block at byte
+// mx_key_pos(i) of its column, scales [heads][nbr][32][D/32] (column
+// 32 c + r at [r][c]), blocks of 32 rows of a sequence per column.
+struct MxQuantArgs {
+  const void* x[3];
+  const int32_t* off[3];
+  int32_t total[3];
+  int32_t nbr[3];
+  int32_t keys[3];
+  uint8_t* codes[3];
+  uint8_t* scales[3];
+  int32_t batch;
+  int32_t heads;
+};
+hipError_t launch_mx_quant(const MxQuantArgs& a, int head_dim, int count, hipStream_t stream);
+
+struct MxFwdArgs {
+  const uint8_t* qx;   // Q row image: codes, scales
+  const uint8_t* qs;
+  const uint8_t* kx;   // K row image
+  const uint8_t* ks;
+  const uint8_t* vx;   // V column image
+  const uint8_t* vs;
+  int64_t rq;          // image rows (32 block rows) of Q and of K / V
+  int64_t rk;
+  const ItemMeta* meta;   // query-tile records (kPassQ)
+  void* out;              // bf16 [total_q, heads, D]
+  float* lse;             // [heads, total_q]
+  int32_t heads;
+  int32_t total_q;
+  int32_t causal;
+  float scale_log2;
+};
+hipError_t launch_mx_fwd(const MxFwdArgs& a, int head_dim, int64_t grid, hipStream_t stream);
+
 // BlockAttention: the runs of `block` tokens of every sequence as offsets
 // (see blocks.hip).
 hipError_t launch_block_offsets(const int32_t* off, int32_t batch, int32_t total, int32_t block, int32_t* out,

@@ -34,7 +34,9 @@ EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_pr
             "jfa_block_offsets_count", "jfa_block_offsets", "jfa_status_string", "jfa_last_error",
             "jfa_forward_noalloc", "jfa_bbs_batch_count", "jfa_bbs_plan", "jfa_block_workspace_size",
             "jfa_block_forward", "jfa_block_backward", "jfa_pooled_workspace_size", "jfa_pooled_forward",
-            "jfa_pooled_backward")
+            "jfa_pooled_backward", "jfa_mx_image_bytes", "jfa_mx_quantize", "jfa_mx_workspace_size",
+            "jfa_mx_forward", "jfa_mx_attend")
+MX_LAYOUTS = {"rows": 0, "keys": 1}
 BBS_COSTS = {"tokens": 0, "pairs": 1}
 
 
@@ -102,6 +104,16 @@ def lib():
         L.jfa_pooled_forward.argtypes = [_vp] * 4 + [_i32] * 6 + [_f32, _i32, _i32, _vp, _vp, _vp, _sz, _vp, _vp]
         L.jfa_pooled_backward.restype = ctypes.c_int
         L.jfa_pooled_backward.argtypes = [_vp] * 7 + [_i32] * 6 + [_f32, _i32, _i32] + [_vp] * 4 + [_sz, _vp, _vp]
+        L.jfa_mx_image_bytes.restype = _sz
+        L.jfa_mx_image_bytes.argtypes = [_i32] * 4
+        L.jfa_mx_quantize.restype = ctypes.c_int
+        L.jfa_mx_quantize.argtypes = [_vp, _vp] + [_i32] * 5 + [_vp, _sz, _vp]
+        L.jfa_mx_workspace_size.restype = _sz
+        L.jfa_mx_workspace_size.argtypes = [_i32] * 6
+        L.jfa_mx_forward.restype = ctypes.c_int
+        L.jfa_mx_forward.argtypes = [_vp] * 5 + [_i32] * 7 + [_f32, _i32, _vp, _vp, _vp, _sz, _vp, _vp]
+        L.jfa_mx_attend.restype = ctypes.c_int
+        L.jfa_mx_attend.argtypes = L.jfa_mx_forward.argtypes
         L.jfa_last_error.restype = ctypes.c_char_p
         L.jfa_last_error.argtypes = []
         _lib = L
@@ -327,6 +339,60 @@ def pooled_backward(seeds, k, v, out, dout, lse, kv_offsets, max_kv_len, scale=N
                                      ACTIVATIONS[activation], dt, _ptr(dseeds), _ptr(dk), _ptr(dv), _ptr(ws),
                                      ws.numel(), _stream(), None))
     return dseeds, dk, dv
+
+
+def mx_quantize(x, offsets, layout):
+    """MX image of a bf16 tensor x [total, H, d] (layout "rows" for q and k,
+    "keys" for v) as a uint8 device tensor; see jfa.h for its layout."""
+    _offsets("offsets", offsets)
+    _values("x", x, torch.bfloat16)
+    T, H, D = x.shape
+    B = offsets.numel() - 1
+    n = lib().jfa_mx_image_bytes(B, H, D, T)
+    img = torch.zeros(max(n, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().jfa_mx_quantize(_ptr(x), _ptr(offsets), B, H, D, T, MX_LAYOUTS[layout], _ptr(img), img.numel(),
+                                 _stream()))
+    return img
+
+
+def mx_forward(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale=None, causal=False, ws=None,
+               events=None):
+    """MXFP8 softmax attention forward (bf16 in and out); returns (out, lse)."""
+    _offsets("q_offsets", q_offsets)
+    _offsets("kv_offsets", kv_offsets)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _values(name, t, torch.bfloat16)
+    T_q, H, D = q.shape
+    B = q_offsets.numel() - 1
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    out = torch.empty_like(q)
+    lse = torch.empty((H, T_q), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(lib().jfa_mx_workspace_size(B, H, D, T_q, k.shape[0], 1), 1), dtype=torch.uint8,
+                         device=q.device)
+    _check(lib().jfa_mx_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), B, H, D, T_q,
+                                k.shape[0], int(max_q_len), int(max_kv_len), float(scale), int(bool(causal)),
+                                _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(), events))
+    return out, lse
+
+
+def mx_attend(q_image, k_image, v_image, q_offsets, kv_offsets, heads, head_dim, total_q, total_kv, max_q_len,
+              max_kv_len, scale=None, causal=False, device=None, events=None):
+    """MXFP8 attention from MX images (mx_quantize's output: q and k "rows",
+    v "keys"); returns (out bf16 [total_q, heads, head_dim], lse)."""
+    _offsets("q_offsets", q_offsets)
+    _offsets("kv_offsets", kv_offsets)
+    B = q_offsets.numel() - 1
+    dev_ = q_image.device if device is None else device
+    scale = 1.0 / math.sqrt(head_dim) if scale is None else scale
+    out = torch.empty((total_q, heads, head_dim), dtype=torch.bfloat16, device=dev_)
+    lse = torch.empty((heads, total_q), dtype=torch.float32, device=dev_)
+    ws = torch.empty(max(lib().jfa_mx_workspace_size(B, heads, head_dim, total_q, total_kv, 0), 1),
+                     dtype=torch.uint8, device=dev_)
+    _check(lib().jfa_mx_attend(_ptr(q_image), _ptr(k_image), _ptr(v_image), _ptr(q_offsets), _ptr(kv_offsets), B,
+                               heads, head_dim, total_q, total_kv, int(max_q_len), int(max_kv_len), float(scale),
+                               int(bool(causal)), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(), events))
+    return out, lse
 
 
 # ---------------------------------------------------------------- allocating wrappers

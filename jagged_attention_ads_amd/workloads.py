@@ -45,6 +45,7 @@ class Workload:
     block: int = 0        # > 0: BlockAttention, attention within runs of `block` tokens
     rope_base: float = 0.0  # > 0: BlockAttention's fused rotary embedding of that base
     n_seeds: int = 0      # > 0: pooled attention, n_seeds shared queries per sequence (q_law unused)
+    mx: bool = False      # MXFP8 forward (E4M3 operands, E8M0 block scales; bf16 in and out)
 
 
 WORKLOADS = {
@@ -101,6 +102,20 @@ WORKLOADS["pooled_hist"] = Workload(
     ("fixed", 4), ("lognormal", 1024, 4096), True,
     "pooled multi-head attention, 4 seed queries shared by 512 sequences, key lengths log-normal (median 1024, "
     "max 4096), 8 heads, d 64, bf16", n_seeds=4)
+
+# MXFP8 forward (Key points, MXFP8 bullet; Detailed notes, MXFP8 item) on the
+# shapes of the causal self-attention and cross-attention workloads, beside
+# the bf16 forward on the same batch.
+WORKLOADS["mx_selfattn_causal"] = Workload(
+    "mx_selfattn_causal", 256, 4, 128, "bf16", 1.0, True, "softmax",
+    ("lognormal", 256, 1024), None, False,
+    "MXFP8 (E4M3, E8M0 block scales) jagged causal self-attention forward, batch 256, log-normal lengths "
+    "(median 256, max 1024), 4 heads, d 128, bf16 in and out", mx=True)
+WORKLOADS["mx_cross_asym"] = Workload(
+    "mx_cross_asym", 512, 8, 64, "bf16", 1.0, False, "softmax",
+    ("uniform", 1, 64), ("lognormal", 1024, 4096), False,
+    "MXFP8 (E4M3, E8M0 block scales) asymmetric jagged cross-attention forward, batch 512, query lengths "
+    "U{1..64}, key lengths log-normal (median 1024, max 4096), 8 heads, d 64, bf16 in and out", mx=True)
 
 ORDER = ["tiny_fp32", "selfattn_causal", "cross_asym", "gdpa_silu", "pareto_train"]
 

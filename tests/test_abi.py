@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 22, names
+    assert len(names) == 27, names
     L = jfa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -212,3 +212,61 @@ def test_pooled_noop_and_workspace():
     L = jfa.lib()
     assert L.jfa_pooled_workspace_size(2, 4, 2, 64, 10, 5, 0, 1) > L.jfa_pooled_workspace_size(2, 4, 2, 64, 10, 5, 0, 0) > 0
     assert L.jfa_pooled_workspace_size(2, 0, 2, 64, 10, 5, 0, 0) == 0
+
+
+def _mx(**kw):
+    a = dict(q=P, k=P, v=P, qo=P, ko=P, batch=2, heads=2, d=64, tq=10, tk=10, mq=5, mk=5, scale=0.125, causal=0,
+             out=P, lse=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return jfa.lib().jfa_mx_forward(a["q"], a["k"], a["v"], a["qo"], a["ko"], a["batch"], a["heads"], a["d"],
+                                    a["tq"], a["tk"], a["mq"], a["mk"], a["scale"], a["causal"], a["out"], a["lse"],
+                                    a["ws"], a["wsb"], None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(lse=None), INVALID), (dict(scale=0.0), INVALID), (dict(causal=3), INVALID),
+    (dict(v=MIS), INVALID), (dict(d=32), UNSUPPORTED), (dict(d=48), UNSUPPORTED), (dict(heads=257), UNSUPPORTED),
+    (dict(ws=None), WS_SMALL), (dict(wsb=100), WS_SMALL), (dict(ws=P + 16), INVALID),
+])
+def test_mx_forward_rejects(kw, status):
+    """MXFP8 forward's argument checks, on the host before anything is
+    enqueued (P is 256-byte aligned; P + 16 is not)."""
+    assert _mx(**kw) == status
+
+
+def test_mx_noop_and_sizes():
+    assert _mx(batch=0, ws=None, wsb=0) == OK
+    assert _mx(tq=0, q=None, out=None, lse=None, ws=None, wsb=0) == OK
+    L = jfa.lib()
+    # image: codes H * 32 (T/32 + B) * d, then the scales, each 256-aligned
+    n = 100 // 32 + 3
+    assert L.jfa_mx_image_bytes(3, 2, 64, 100) == 2 * 32 * n * 64 + (2 * 32 * n * 2 + 255) // 256 * 256
+    assert L.jfa_mx_image_bytes(3, 2, 32, 100) == 0
+    assert L.jfa_mx_workspace_size(3, 2, 64, 100, 200, 1) > L.jfa_mx_image_bytes(3, 2, 64, 100) + \
+        2 * L.jfa_mx_image_bytes(3, 2, 64, 200)
+    assert 0 < L.jfa_mx_workspace_size(3, 2, 64, 100, 200, 0) < L.jfa_mx_image_bytes(3, 2, 64, 100)
+    assert L.jfa_mx_workspace_size(3, 2, 64, 100, 200, 2) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(q=P + 16), INVALID), (dict(d=128, heads=300), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED), (dict(wsb=100), WS_SMALL), (dict(lse=None), INVALID),
+])
+def test_mx_attend_rejects(kw, status):
+    a = dict(q=P, k=P, v=P, qo=P, ko=P, batch=2, heads=2, d=64, tq=10, tk=10, mq=5, mk=5, scale=0.125, causal=0,
+             out=P, lse=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    assert jfa.lib().jfa_mx_attend(a["q"], a["k"], a["v"], a["qo"], a["ko"], a["batch"], a["heads"], a["d"], a["tq"],
+                                   a["tk"], a["mq"], a["mk"], a["scale"], a["causal"], a["out"], a["lse"], a["ws"],
+                                   a["wsb"], None, None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(off=None), INVALID), (dict(layout=2), INVALID), (dict(img=None), INVALID),
+    (dict(img=P + 16), INVALID), (dict(d=128, nb=100), WS_SMALL), (dict(d=32), UNSUPPORTED), (dict(heads=0), INVALID),
+])
+def test_mx_quantize_rejects(kw, status):
+    a = dict(x=P, off=P, batch=2, heads=2, d=64, total=10, layout=0, img=P, nb=1 << 20)
+    a.update(kw)
+    assert jfa.lib().jfa_mx_quantize(a["x"], a["off"], a["batch"], a["heads"], a["d"], a["total"], a["layout"],
+                                     a["img"], a["nb"], None) == status
