@@ -48,15 +48,25 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_digest():
-    """Digest of the device sources (kernels and the headers they include;
-    not the host-side C ABI layer), to tell whether stored counters still
-    apply."""
+# Device sources each kernel of a step is built from (beside the shared
+# headers): stored counters stay valid while these are unchanged.
+COMMON_SRC = ("jfa_common.hpp", "jfa_internal.h")
+KERNEL_SRC = {"sched_q": ("sched.hip", "blocks.hip", "pooled.hip"), "fwd": ("fwd.hip",),
+              "bwd_sched": ("sched.hip", "bwd_stats.hpp", "pooled.hip"), "bwd_stats": ("bwd.hip", "bwd_stats.hpp"),
+              "bwd_dkdv": ("bwd.hip",), "bwd_dq": ("bwd.hip", "pooled.hip"), "mx_quant": ("mx.hip",),
+              "mx_fwd": ("mx.hip",)}
+
+
+def kernel_source_digest(kernel=None):
+    """Digest of the device sources of `kernel` (a key of KERNEL_SRC) and
+    the shared headers, or of every device source (None): tells whether
+    stored counters still apply (the host-side C ABI layer is left out)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "jagged_attention_ads_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if not name.endswith((".hip", ".hpp", ".h")):
-            continue
+    names = sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp", ".h")))
+    if kernel is not None:
+        names = sorted(set(COMMON_SRC) | set(KERNEL_SRC[kernel]))
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -805,7 +815,8 @@ def main():
     t_s = dom_ms * 1e-3
     a = acct[name]
     ai = a["flops"] / a["bytes"]
-    digest = kernel_source_digest()
+    src_key = "mx_fwd" if wl.mx and name == "fwd" else name
+    digest = kernel_source_digest(src_key)
     # the MXFP8 attention's products run at the fp8 rate
     peak_mfma = PEAK_FP8_TFLOPS if wl.mx and name == "fwd" else PEAK_BF16_TFLOPS
     if ai < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
@@ -852,7 +863,7 @@ def main():
         "kernel_us": {k_: v_ * 1e3 for k_, v_ in kern_ms.items()},
         "kernel_us_from": "mean of %d %s steps with an event between every two launches" % (
             K, "flushed" if flush_buf is not None else "warm"),
-        "kernel_source_digest": digest,
+        "kernel_source_digest": digest, "kernel_sources": list(COMMON_SRC) + list(KERNEL_SRC[src_key]),
         "roofline": roof,
     }
     if wl.mx:
