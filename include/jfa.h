@@ -204,10 +204,9 @@ int jfa_backward_profiled(const void* q, const void* k, const void* v, const voi
  * item, ordered by cost descending then (sequence, head, tile) ascending,
  * then int32 tile_start[batch + 1], then (32-byte aligned) the per-item
  * records the attention kernels read, whose layout is internal.
- * The builder keeps its working set in LDS when it fits (a second, slower
- * body works from global memory otherwise); the environment variable
- * JFA_SCHED_STAGE=0 selects the global-memory body everywhere, for tests of
- * it.  Both give the same list.
+ * The builder runs one workgroup per cost class: each counts the items of
+ * higher cost (they come first) and places its own class's items, a run of
+ * tiles per sequence, by one prefix sum over the sequences.
  * JFA_PASS_QUERY_TILES is the list of the
  * forward kernel, JFA_PASS_DQ_STORED_TILES that of the dQ kernel over the
  * stored dS (larger query tiles), JFA_PASS_DQ_TILES that of the dQ kernel

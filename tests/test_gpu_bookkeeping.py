@@ -19,15 +19,20 @@ import torch
 
 import oracle
 from jagged_attention_ads_amd import jfa
-from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch, offsets_from_lengths
+from jagged_attention_ads_amd.workloads import WORKLOADS, draw_lengths, make_batch, offsets_from_lengths
 from tests.gpu_util import Dev, dev, values_to_device
 
 pytestmark = pytest.mark.gpu
 
 
 def _worklist_case(name, batch, causal):
-    b = make_batch(name, 7, batch=batch, with_dout=False)
-    return b.q_offsets, b.kv_offsets, b.workload.heads, causal
+    """Offsets drawn from the workload's length laws (no values: the lists
+    depend on the offsets alone)."""
+    wl = WORKLOADS[name]
+    rng = np.random.default_rng(7)
+    lq = draw_lengths(rng, wl.q_law, batch)
+    lk = lq.copy() if wl.kv_law is None else draw_lengths(rng, wl.kv_law, batch)
+    return offsets_from_lengths(lq), offsets_from_lengths(lk), wl.heads, causal
 
 
 WL_CASES = [
@@ -37,6 +42,9 @@ WL_CASES = [
     ("cross_asym", 300, True),
     ("pareto_train", 1024, True),
     ("gdpa_silu", 256, True),
+    # more sequences than a builder workgroup has threads (chunked scans)
+    ("cross_asym", 3000, False),
+    ("selfattn_causal", 2500, True),
 ]
 
 
@@ -53,17 +61,10 @@ def _worklist_ref(name, batch, causal, pass_):
     return np.array([[b, (t << 8) | h] for b, h, t, _ in ref], dtype=np.int32).reshape(-1, 2)
 
 
-@pytest.fixture(params=["1", "0"])
-def sched_stage(request, monkeypatch):
-    """Both bodies of the builder (1: all in LDS where it fits, 0: global memory)."""
-    monkeypatch.setenv("JFA_SCHED_STAGE", request.param)
-    return request.param
-
-
 @pytest.mark.parametrize("name,batch,causal", WL_CASES)
 @pytest.mark.parametrize("pass_", [jfa.PASS_QUERY_TILES, jfa.PASS_KEY_TILES, jfa.PASS_DQ_TILES,
                                    jfa.PASS_DQ_STORED_TILES])
-def test_worklist_bit_exact(name, batch, causal, pass_, sched_stage):
+def test_worklist_bit_exact(name, batch, causal, pass_):
     qo, ko, H, causal = _worklist_case(name, batch, causal)
     tile = jfa.jfa_tile_shape(pass_)[0]
     ref_arr = _worklist_ref(name, batch, causal, pass_)
