@@ -339,6 +339,14 @@ WorklistLayout worklist_layout(int pass, int32_t batch, int32_t heads, int32_t t
   return lay;
 }
 
+// Workgroups per cost class: enough that each writes at most about four
+// items per thread even if one class held every item of the list (with few
+// distinct costs one class can: pooled attention's key tiles all cost one).
+static int sched_slices(const WorklistLayout& lay, int threads) {
+  const int64_t per = 4 * (int64_t)threads;
+  return (int)std::min<int64_t>(64, std::max<int64_t>(1, (lay.capacity + per - 1) / per));
+}
+
 // The job of one pass; `slices` workgroups per cost class.
 static SchedJob make_job(int32_t nbuckets, int slices, void* wl_base, const WorklistLayout& lay,
                          const OffsetCheck& chk) {
@@ -358,9 +366,7 @@ static SchedJob make_job(int32_t nbuckets, int slices, void* wl_base, const Work
 hipError_t launch_sched(int pass, const int32_t* qo, const int32_t* ko, int32_t batch, int32_t heads,
                         int32_t causal, int32_t nbuckets, void* wl_base, const WorklistLayout& lay,
                         const OffsetCheck& chk, hipStream_t stream) {
-  // large batches: four workgroups per class (one class can hold most of
-  // the items, and a lone list is on the critical path)
-  const SchedJob j = make_job(nbuckets, batch >= 512 ? 4 : 1, wl_base, lay, chk);
+  const SchedJob j = make_job(nbuckets, sched_slices(lay, kListThreads), wl_base, lay, chk);
   const dim3 grid((unsigned)(nbuckets * j.slices)), block(kListThreads);
   if (pass == kPassQ)
     hipLaunchKernelGGL(sched_kernel<kPassQ>, grid, block, 0, stream, qo, ko, batch, heads, causal, j);
@@ -403,9 +409,8 @@ hipError_t launch_sched_pair(int qpass, const int32_t* qo, const int32_t* ko, in
                              int32_t causal, int32_t nb_dq, void* wl_dq, const WorklistLayout& lay_dq, int32_t nb_kv,
                              void* wl_kv, const WorklistLayout& lay_kv, const StatsArgs* stats, int dtype,
                              int head_dim, const OffsetCheck& chk, hipStream_t stream) {
-  // one workgroup per class: these lists run beside the statistics
-  const SchedJob jq = make_job(nb_dq, 1, wl_dq, lay_dq, chk);
-  const SchedJob jkv = make_job(nb_kv, 1, wl_kv, lay_kv, chk);
+  const SchedJob jq = make_job(nb_dq, sched_slices(lay_dq, kPairThreads), wl_dq, lay_dq, chk);
+  const SchedJob jkv = make_job(nb_kv, sched_slices(lay_kv, kPairThreads), wl_kv, lay_kv, chk);
   if (qpass == kPassDQS)
     return dtype == 0 ? pair_launch_d<kPassDQS, __bf16>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, stream)
                       : pair_launch_d<kPassDQS, float>(head_dim, qo, ko, batch, heads, causal, jq, jkv, stats, stream);
