@@ -46,7 +46,7 @@ and finite differences.
 
 from .attention import attention_fwd, attention_bwd, visible_mask  # noqa: F401
 from .bbs import bbs_plan, merged_loads  # noqa: F401
-from .mx import mx_attention_fwd, mx_quantize_keys, mx_quantize_rows  # noqa: F401
+from .mx import mx_attention_bwd, mx_attention_fwd, mx_quantize_keys, mx_quantize_rows  # noqa: F401
 from .pooled import pooled_bwd, pooled_fwd  # noqa: F401
 from .rope import rope, sequence_positions  # noqa: F401
 from .schedule import (  # noqa: F401

@@ -41,6 +41,17 @@ Readings of what the pages leave open (each repeated where it is used):
      elements.
   R5 out and lse as in attention.attention_fwd (rows without a visible key:
      out = 0, lse = -inf; causal cross attention bottom-right aligned).
+  R6 backward (mx_attention_bwd): each product's operands in MX blocks along
+     its contraction axis -- S = Q K^T and dP = dO V^T over the head
+     dimension (row images), dV = P^T dO and dK = dS^T Q over queries
+     (blocks of 32 queries counted from the sequence's first one: P and dS
+     per key column, dO and Q per column), dQ = dS K over keys (dS per query
+     row, K per column).
+  R7 P is recomputed from the forward's lse in full precision (as the
+     plain backward does), delta = rowsum(dO o O) from the given O and dO,
+     and dS = P o (dP - delta) is formed before either of its
+     quantisations; P and dS take plain MX blocks (scale from their block's
+     largest magnitude).
 """
 
 import math
@@ -242,3 +253,76 @@ def mx_attention_fwd(q, k, v, q_offsets, kv_offsets, scale, causal=False):
             with np.errstate(divide="ignore"):
                 lse[h, qs:qe] = np.where(live, (m + np.log2(np.where(live, den, 1.0))) * math.log(2.0), -np.inf)
     return out, lse
+
+
+# ------------------------------------------------------------------ backward
+
+def mx_quantize_matrix(x, axis):
+    """OCP MX blocks of 32 consecutive entries of a 2-D block along `axis`
+    (0: down each column, 1: along each row), counted from index 0; returns
+    the dequantised values (R30: the weights and dS of one (sequence, head)
+    along queries or along keys)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = x if axis == 0 else x.T
+    out = np.zeros_like(y)
+    for r0 in range(0, y.shape[0], BLOCK):
+        blk = y[r0:r0 + BLOCK]
+        ex = e8m0_exponent(np.max(np.abs(blk), axis=0))
+        sc = np.exp2(ex.astype(np.float64))[None]
+        out[r0:r0 + BLOCK] = e4m3_decode(e4m3_encode(blk / sc)) * sc
+    return out if axis == 0 else out.T
+
+
+def mx_attention_bwd(q, k, v, out, dout, lse, q_offsets, kv_offsets, scale, causal=False, quantize=True):
+    """MXFP8 jagged softmax attention backward (R30 - R33), fp64 arithmetic on
+    the quantised operands.
+
+    out, lse: the forward's outputs (as jfa_backward takes them).  Each
+    product's operands are quantised along its contraction axis:
+      dP = dO V^T, S = Q K^T   over the head dimension: row images;
+      dV = P^T dO, dK = dS^T Q over queries: P and dS per key column, dO and
+                               Q per column, blocks of 32 queries;
+      dQ = dS K                over keys: dS per query row, K per column,
+                               blocks of 32 keys.
+    P = exp(scale S - lse) from the quantised S, in full precision, and
+    dS = P o (dP - delta), delta = rowsum(dO o O), before their own
+    quantisation.  quantize=False replaces every quantisation by the
+    identity (the plain attention backward; a structural pin)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    qo = np.asarray(q_offsets, dtype=np.int64)
+    ko = np.asarray(kv_offsets, dtype=np.int64)
+    if quantize:
+        rows = lambda x: mx_dequantize_rows(*mx_quantize_rows(x))          # noqa: E731
+        seq = lambda x, o: mx_dequantize_keys(*mx_quantize_keys(x, o))     # noqa: E731
+        mat = mx_quantize_matrix
+    else:
+        rows = lambda x: x                                                  # noqa: E731
+        seq = lambda x, o: x                                                # noqa: E731
+        mat = lambda x, axis: x                                             # noqa: E731
+    q_r, k_r, v_r, do_r = rows(q), rows(k), rows(v), rows(dout)
+    q_c, do_c, k_c = seq(q, qo), seq(dout, qo), seq(k, ko)
+    delta = (dout * out).sum(axis=2)   # [T_q, H]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    H = q.shape[1]
+    for b in range(len(qo) - 1):
+        qs, qe, ks, ke = int(qo[b]), int(qo[b + 1]), int(ko[b]), int(ko[b + 1])
+        lq, lk = qe - qs, ke - ks
+        if lq == 0 or lk == 0:
+            continue
+        vis = visible_mask(lq, lk, causal)
+        for h in range(H):
+            s = scale * (q_r[qs:qe, h] @ k_r[ks:ke, h].T)
+            lrow = lse[h, qs:qe]
+            p = np.where(vis & np.isfinite(lrow)[:, None], np.exp(s - np.where(np.isfinite(lrow), lrow, 0.0)[:, None]),
+                         0.0)
+            dv[ks:ke, h] = mat(p, 0).T @ do_c[qs:qe, h]
+            dp = do_r[qs:qe, h] @ v_r[ks:ke, h].T
+            ds = p * (dp - delta[qs:qe, h][:, None])
+            dk[ks:ke, h] = scale * (mat(ds, 0).T @ q_c[qs:qe, h])
+            dq[qs:qe, h] = scale * (mat(ds, 1) @ k_c[ks:ke, h])
+    return dq, dk, dv

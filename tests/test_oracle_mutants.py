@@ -203,3 +203,17 @@ def test_mx_quantised_denominator_is_caught():
     w = mx.e4m3_decode(codes[0]) * 2.0 ** (fb[0, 0] - 8)
     wrong = w / w.sum()          # normalised by the quantised weights instead of the exact ones
     assert np.abs(wrong - np.array(e["out"])).max() > 1e-3
+
+
+def test_mx_backward_wrong_quantisation_axis_is_caught(monkeypatch):
+    """dS quantised along keys for every product (instead of along queries
+    for dK and dV's P): the loop implementation rejects it."""
+    from tests.test_oracle_mx import _draw_bwd, _loop_mx_bwd
+    import oracle.mx as mx
+    q, k, v, out, do, lse, qo, ko = _draw_bwd([2, 35], [36, 33], 1, 32, 5, False)
+    orig = mx.mx_quantize_matrix
+    monkeypatch.setattr(mx, "mx_quantize_matrix", lambda x, axis: orig(x, 1))
+    got = mx.mx_attention_bwd(q, k, v, out, do, lse, qo, ko, 0.3, False)
+    monkeypatch.undo()
+    ref = _loop_mx_bwd(q, k, v, out, do, lse, qo, ko, 0.3, False)
+    assert max(np.abs(g - r).max() for g, r in zip(got, ref)) > 1e-6

@@ -317,3 +317,122 @@ def test_attention_close_to_exact_attention():
     assert np.abs(out - ref).max() < 0.125 * np.abs(v).max()
     assert np.abs(lse - ref_lse).max() < 0.1
     assert np.abs(out - ref).mean() < 0.015
+
+
+# ------------------------------------------------------------------ backward
+
+
+def _draw_bwd(lq, lk, heads, d, seed, causal):
+    rng = np.random.default_rng(seed)
+    qo = np.concatenate([[0], np.cumsum(lq)])
+    ko = np.concatenate([[0], np.cumsum(lk)])
+    q = rng.standard_normal((qo[-1], heads, d))
+    k = rng.standard_normal((ko[-1], heads, d))
+    v = rng.standard_normal((ko[-1], heads, d))
+    do = rng.standard_normal((qo[-1], heads, d))
+    out, lse = mx.mx_attention_fwd(q, k, v, qo, ko, 0.3, causal)
+    return q, k, v, out, do, lse, qo, ko
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_without_quantisation_is_the_attention_backward(causal):
+    q, k, v, _, do, _, qo, ko = _draw_bwd([3, 40, 0, 70], [35, 40, 5, 70], 2, 64, 4, causal)
+    out, lse = oracle.attention_fwd(q, k, v, qo, ko, 0.3, "softmax", causal)
+    got = mx.mx_attention_bwd(q, k, v, out, do, lse, qo, ko, 0.3, causal, quantize=False)
+    ref = oracle.attention_bwd(q, k, v, do, qo, ko, 0.3, "softmax", causal)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12)
+
+
+def test_matrix_blocks_closed_form():
+    # a 40 x 2 block: rows 0..31 and 32..39 are separate blocks per column
+    x = np.ones((40, 2))
+    x[5, 0] = 100.0
+    y = mx.mx_quantize_matrix(x, 0)
+    assert y[5, 0] == 96.0           # 100 = 1.5625 * 64 -> scale 2^-2, 400 -> nearest 384
+    assert np.all(y[32:, 0] == 1.0) and np.all(y[:, 1] == 1.0)
+    # along rows: the same with the matrix transposed
+    np.testing.assert_array_equal(mx.mx_quantize_matrix(x.T, 1), y.T)
+
+
+def test_backward_lossless_values_and_uniform_weights():
+    """Q = 0 makes every weight 1/L (L = 32: exact in E4M3); with V and dO
+    exactly representable, dV is exact, and dK = dS^T Q = 0."""
+    rng = np.random.default_rng(8)
+    L, H, d = 32, 1, 32
+    qo = np.array([0, L])
+    q = np.zeros((L, H, d))
+    k = rng.standard_normal((L, H, d))
+    v = rng.integers(-14, 15, (L, H, d)) * 2.0 ** -3
+    do = rng.integers(-14, 15, (L, H, d)) * 2.0 ** -3
+    v[0] = do[0] = 1.75   # block max 1.75 per column: scale 2^-8, every element exact
+    out, lse = mx.mx_attention_fwd(q, k, v, qo, qo, 0.25, False)
+    dq, dk, dv = mx.mx_attention_bwd(q, k, v, out, do, lse, qo, qo, 0.25, False)
+    ref = oracle.attention_bwd(q, k, v, do, qo, qo, 0.25, "softmax", False)
+    np.testing.assert_allclose(dv, ref[2], rtol=1e-13, atol=1e-13)
+    assert np.all(dk == 0)
+
+
+def _loop_mx_bwd(q, k, v, out, do, lse, qo, ko, scale, causal):
+    """Independent per-element loop implementation for tiny inputs: scalar
+    block scales from the bit-level definition and brute-force rounding."""
+    def quant(vals):
+        amax = max(abs(x) for x in vals)
+        ex = -127 if amax == 0 else max(-127, min(127, math.frexp(amax)[1] - 1 - 8))
+        return [_table_value(_nearest_code(x / 2.0 ** ex)) * 2.0 ** ex for x in vals]
+    T, H, d = q.shape
+    Tk = k.shape[0]
+    qr, kr, vr, dor = (np.zeros_like(x) for x in (q, k, v, do))
+    for src, dst in ((q, qr), (k, kr), (v, vr), (do, dor)):
+        for r in range(src.shape[0]):
+            for h in range(H):
+                for c0 in range(0, d, 32):
+                    dst[r, h, c0:c0 + 32] = quant(list(src[r, h, c0:c0 + 32]))
+    qc, doc, kc = np.zeros_like(q), np.zeros_like(do), np.zeros_like(k)
+    for src, dst, off in ((q, qc, qo), (do, doc, qo), (k, kc, ko)):
+        for b in range(len(off) - 1):
+            for r0 in range(off[b], off[b + 1], 32):
+                r1 = min(r0 + 32, off[b + 1])
+                for h in range(H):
+                    for col in range(d):
+                        dst[r0:r1, h, col] = quant(list(src[r0:r1, h, col]))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(qo) - 1):
+        lq, lk = qo[b + 1] - qo[b], ko[b + 1] - ko[b]
+        for h in range(H):
+            P = np.zeros((lq, lk))
+            dS = np.zeros((lq, lk))
+            for i in range(lq):
+                dlt = sum(do[qo[b] + i, h, c] * out[qo[b] + i, h, c] for c in range(d))
+                for j in range(lk):
+                    if causal and j > i + lk - lq:
+                        continue
+                    s = scale * float(np.dot(qr[qo[b] + i, h], kr[ko[b] + j, h]))
+                    P[i, j] = math.exp(s - lse[h, qo[b] + i])
+                    dp = float(np.dot(dor[qo[b] + i, h], vr[ko[b] + j, h]))
+                    dS[i, j] = P[i, j] * (dp - dlt)
+            Pq, dSq, dSk = np.zeros_like(P), np.zeros_like(dS), np.zeros_like(dS)
+            for j in range(lk):
+                for r0 in range(0, lq, 32):
+                    Pq[r0:r0 + 32, j] = quant(list(P[r0:r0 + 32, j]))
+                    dSq[r0:r0 + 32, j] = quant(list(dS[r0:r0 + 32, j]))
+            for i in range(lq):
+                for c0 in range(0, lk, 32):
+                    dSk[i, c0:c0 + 32] = quant(list(dS[i, c0:c0 + 32]))
+            for j in range(lk):
+                for c in range(d):
+                    dv[ko[b] + j, h, c] = sum(Pq[i, j] * doc[qo[b] + i, h, c] for i in range(lq))
+                    dk[ko[b] + j, h, c] = scale * sum(dSq[i, j] * qc[qo[b] + i, h, c] for i in range(lq))
+            for i in range(lq):
+                for c in range(d):
+                    dq[qo[b] + i, h, c] = scale * sum(dSk[i, j] * kc[ko[b] + j, h, c] for j in range(lk))
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_loop_implementation(causal):
+    q, k, v, out, do, lse, qo, ko = _draw_bwd([2, 35], [36, 33], 1, 32, 21 + causal, causal)
+    got = mx.mx_attention_bwd(q, k, v, out, do, lse, qo, ko, 0.3, causal)
+    ref = _loop_mx_bwd(q, k, v, out, do, lse, qo, ko, 0.3, causal)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-9, atol=1e-11)
