@@ -50,8 +50,16 @@ Readings of what the pages leave open (each repeated where it is used):
   R7 P is recomputed from the forward's lse in full precision (as the
      plain backward does), delta = rowsum(dO o O) from the given O and dO,
      and dS = P o (dP - delta) is formed before either of its
-     quantisations; P and dS take plain MX blocks (scale from their block's
-     largest magnitude).
+     quantisations.
+  R8 P and dS take the smallest power-of-two scale that keeps their block
+     unsaturated: 2^k with k the least integer for which max|x| <= 448 2^k
+     (e8m0_exponent_fit), not the vector conversion's 2^(floor(log2 max) -
+     8).  The latter saturates block maxima in (1.75, 2) x 2^j, and its
+     threshold sits exactly at P = 1, the weight of every row with a single
+     visible key (the first query of causal self attention): the last bit
+     of P's evaluation would decide between 1 and 0.875.  The fitted scale's
+     threshold is max = 448 2^k (P = 0.875 2^j), where weights do not
+     gather, and nothing saturates.
 """
 
 import math
@@ -257,24 +265,34 @@ def mx_attention_fwd(q, k, v, q_offsets, kv_offsets, scale, causal=False):
 
 # ------------------------------------------------------------------ backward
 
+def e8m0_exponent_fit(amax):
+    """Block exponent of P and dS (R8): the least integer k with amax <= 448
+    2^k, clamped to the E8M0 range; an all-zero block takes the smallest
+    exponent.  The block's largest element then lies in [224, 448]."""
+    amax = np.asarray(amax, dtype=np.float64)
+    k = e8m0_exponent(amax)   # floor(log2 amax) - 8: amax in [256, 512) x 2^k
+    k = np.where((amax > 0) & (amax > E4M3_MAX * np.exp2(k.astype(np.float64))), k + 1, k)
+    return np.clip(k, E8M0_MIN_EXP, E8M0_MAX_EXP)
+
+
 def mx_quantize_matrix(x, axis):
-    """OCP MX blocks of 32 consecutive entries of a 2-D block along `axis`
-    (0: down each column, 1: along each row), counted from index 0; returns
-    the dequantised values (R30: the weights and dS of one (sequence, head)
-    along queries or along keys)."""
+    """MX blocks of 32 consecutive entries of a 2-D block along `axis` (0:
+    down each column, 1: along each row), counted from index 0, with the
+    fitted block exponent (R8); returns the dequantised values (the weights
+    and dS of one (sequence, head) along queries or along keys)."""
     x = np.asarray(x, dtype=np.float64)
     y = x if axis == 0 else x.T
     out = np.zeros_like(y)
     for r0 in range(0, y.shape[0], BLOCK):
         blk = y[r0:r0 + BLOCK]
-        ex = e8m0_exponent(np.max(np.abs(blk), axis=0))
+        ex = e8m0_exponent_fit(np.max(np.abs(blk), axis=0))
         sc = np.exp2(ex.astype(np.float64))[None]
         out[r0:r0 + BLOCK] = e4m3_decode(e4m3_encode(blk / sc)) * sc
     return out if axis == 0 else out.T
 
 
 def mx_attention_bwd(q, k, v, out, dout, lse, q_offsets, kv_offsets, scale, causal=False, quantize=True):
-    """MXFP8 jagged softmax attention backward (R30 - R33), fp64 arithmetic on
+    """MXFP8 jagged softmax attention backward (R6 - R8), fp64 arithmetic on
     the quantised operands.
 
     out, lse: the forward's outputs (as jfa_backward takes them).  Each

@@ -247,6 +247,11 @@ def _loop_mx_attention(q, k, v, qo, ko, scale, causal):
         ex = -127 if amax == 0 else max(-127, min(127, math.frexp(amax)[1] - 1 - 8))
         return [_table_value(_nearest_code(x / 2.0 ** ex)) * 2.0 ** ex for x in vals]
 
+    def quant_fit(vals):   # P and dS: the least exponent whose range holds the block (R8)
+        amax = max(abs(x) for x in vals)
+        ex = next(e for e in range(-127, 128) if amax <= 448.0 * 2.0 ** e)
+        return [_table_value(_nearest_code(x / 2.0 ** ex)) * 2.0 ** ex for x in vals]
+
     for r in range(T):
         for h in range(H):
             for c0 in range(0, d, 32):
@@ -353,6 +358,27 @@ def test_matrix_blocks_closed_form():
     assert np.all(y[32:, 0] == 1.0) and np.all(y[:, 1] == 1.0)
     # along rows: the same with the matrix transposed
     np.testing.assert_array_equal(mx.mx_quantize_matrix(x.T, 1), y.T)
+    # the fitted exponent (R8) where it differs from floor(log2 max) - 8: a
+    # block max just below 1 keeps the scale 2^-8 (element 256 - 2^-22,
+    # rounded to 256: the value 1), where the vector conversion would take
+    # 2^-9 and saturate it to 448 (0.875); 1.9 takes 2^-7 (243.2 -> 240:
+    # 1.875) instead of saturating to 1.75
+    z = np.full((32, 3), 0.25)
+    z[0] = [1.0 - 2.0 ** -30, 1.9, 1.75]
+    w = mx.mx_quantize_matrix(z, 0)
+    assert w[0, 0] == 1.0 and w[0, 1] == 1.875 and w[0, 2] == 1.75
+    assert np.all(w[1:] == 0.25)
+
+
+def test_fit_exponent_closed_forms():
+    """R8: the least k with max <= 448 2^k."""
+    f = mx.e8m0_exponent_fit
+    assert f(1.0) == -8 and f(1.0 - 2.0 ** -40) == -8 and f(1.0 + 2.0 ** -40) == -8
+    assert f(1.75) == -8 and f(1.75 * (1 + 2.0 ** -40)) == -7 and f(2.0) == -7
+    assert f(448.0) == 0 and f(448.5) == 1 and f(0.0) == -127 and f(2.0 ** -200) == -127
+    a = np.exp2(np.random.default_rng(2).uniform(-100, 100, 1000))
+    r = a / np.exp2(f(a).astype(np.float64))
+    assert np.all((r > 224.0) & (r <= 448.0))
 
 
 def test_backward_lossless_values_and_uniform_weights():
@@ -379,6 +405,11 @@ def _loop_mx_bwd(q, k, v, out, do, lse, qo, ko, scale, causal):
     def quant(vals):
         amax = max(abs(x) for x in vals)
         ex = -127 if amax == 0 else max(-127, min(127, math.frexp(amax)[1] - 1 - 8))
+        return [_table_value(_nearest_code(x / 2.0 ** ex)) * 2.0 ** ex for x in vals]
+
+    def quant_fit(vals):   # P and dS: the least exponent whose range holds the block (R8)
+        amax = max(abs(x) for x in vals)
+        ex = next(e for e in range(-127, 128) if amax <= 448.0 * 2.0 ** e)
         return [_table_value(_nearest_code(x / 2.0 ** ex)) * 2.0 ** ex for x in vals]
     T, H, d = q.shape
     Tk = k.shape[0]
@@ -414,11 +445,11 @@ def _loop_mx_bwd(q, k, v, out, do, lse, qo, ko, scale, causal):
             Pq, dSq, dSk = np.zeros_like(P), np.zeros_like(dS), np.zeros_like(dS)
             for j in range(lk):
                 for r0 in range(0, lq, 32):
-                    Pq[r0:r0 + 32, j] = quant(list(P[r0:r0 + 32, j]))
-                    dSq[r0:r0 + 32, j] = quant(list(dS[r0:r0 + 32, j]))
+                    Pq[r0:r0 + 32, j] = quant_fit(list(P[r0:r0 + 32, j]))
+                    dSq[r0:r0 + 32, j] = quant_fit(list(dS[r0:r0 + 32, j]))
             for i in range(lq):
                 for c0 in range(0, lk, 32):
-                    dSk[i, c0:c0 + 32] = quant(list(dS[i, c0:c0 + 32]))
+                    dSk[i, c0:c0 + 32] = quant_fit(list(dS[i, c0:c0 + 32]))
             for j in range(lk):
                 for c in range(d):
                     dv[ko[b] + j, h, c] = sum(Pq[i, j] * doc[qo[b] + i, h, c] for i in range(lq))
@@ -436,3 +467,52 @@ def test_backward_matches_loop_implementation(causal):
     ref = _loop_mx_bwd(q, k, v, out, do, lse, qo, ko, 0.3, causal)
     for g, r in zip(got, ref):
         np.testing.assert_allclose(g, r, rtol=1e-9, atol=1e-11)
+
+
+def test_mx_bwd_gates_separate_mistakes(monkeypatch):
+    """The MXFP8 backward's GPU gates (tests.mx_util) are tight enough to see
+    the plausible mistakes of a kernel: each, planted in the oracle, fails
+    them by a factor of 3 or more -- relative L2 against the correct oracle,
+    per tensor or per sequence, at least 3x the gate in some gradient.
+
+    Not among them: the axis or the block boundaries of P's and dS's own
+    quantisation.  With the fitted exponent (R8) nothing saturates, so the
+    partition only decides which elements below 2^-17 of a block's largest
+    fall under E4M3's range, and those move the gradients by less than
+    1e-5: the partition is not visible in the values (and does not matter
+    to them)."""
+    from tests.gpu_util import rel_l2, seq_rel_l2
+    from tests.mx_util import MX_GRAD_RTOL, MX_GRAD_SEQ_RTOL
+    lengths = [1, 31, 32, 33, 64, 65, 200, 130]
+    q, k, v, out, do, lse, qo, ko = _draw_bwd(lengths, lengths, 2, 128, 3, True)
+    ref = mx.mx_attention_bwd(q, k, v, out, do, lse, qo, ko, 0.3, True)
+    orig_keys, orig_mat = mx.mx_quantize_keys, mx.mx_quantize_matrix
+
+    def mutant(name):
+        calls = [0]
+
+        def skip(which):   # mx_attention_bwd quantises P, dS (dK), dS (dQ) in turn
+            def f(x, axis):
+                calls[0] += 1
+                return x if (calls[0] - 1) % 3 in which else orig_mat(x, axis)
+            return f
+        with monkeypatch.context() as m:
+            if name == "blocks counted from packed row 0":
+                m.setattr(mx, "mx_quantize_keys", lambda x, o: orig_keys(x, np.array([0, x.shape[0]])))
+            elif name == "row images for the column operands":
+                m.setattr(mx, "mx_quantize_keys", lambda x, o: mx.mx_quantize_rows(x))
+                m.setattr(mx, "mx_dequantize_keys", mx.mx_dequantize_rows)
+            elif name == "P not quantised":
+                m.setattr(mx, "mx_quantize_matrix", skip((0,)))
+            elif name == "dS not quantised for dK":
+                m.setattr(mx, "mx_quantize_matrix", skip((1,)))
+            elif name == "dS not quantised for dQ":
+                m.setattr(mx, "mx_quantize_matrix", skip((2,)))
+            return mx.mx_attention_bwd(q, k, v, out, do, lse, qo, ko, 0.3, True)
+
+    for name in ("blocks counted from packed row 0", "row images for the column operands", "P not quantised",
+                 "dS not quantised for dK", "dS not quantised for dQ"):
+        got = mutant(name)
+        worst = max(max(rel_l2(g, r) / MX_GRAD_RTOL, seq_rel_l2(g, r, o)[0] / MX_GRAD_SEQ_RTOL)
+                    for g, r, o in zip(got, ref, (qo, ko, ko)))
+        assert worst >= 3.0, (name, worst)
