@@ -12,13 +12,17 @@ import oracle.mx as mx
 # MXFP8 backward gates: relative L2 error of dq, dk, dv against the oracle's
 # gradients rounded to bf16, per tensor and per sequence.  Kernel and oracle
 # quantise the same values by the same rules; what is left is fp32 against
-# fp64 arithmetic: bf16 roundings that fall the other way (fp32 error about
-# 1e-6 against a bf16 step of 2^-8: a fraction of a percent of the elements,
-# one bf16 step each) and the rare E4M3 decision of P or dS on the other side
-# of a midpoint (one element of one row moved by one E4M3 step).  The
-# plausible mistakes of a kernel move the gradients by 0.6 % or more per
-# tensor (test_mx_bwd_gates_separate_mistakes).
-MX_GRAD_RTOL = 2e-3
+# fp64 arithmetic.  dP = dO.v accumulates d products in fp32 (absolute error
+# about d 2^-24 times the largest term), so dS = P (dP - delta) is off by
+# 1e-6 to 1e-5 of itself where dP - delta is small against dP; an E4M3
+# decision of dS (or of P) within that distance of a midpoint goes the other
+# way -- a few in 10^4 elements -- and moves its element by one E4M3 step
+# (up to 1/8 of it).  Over a gradient that is about 1e-3 relative L2
+# (measured: 3e-4 on 64-key sequences to 1.6e-3 on 1000-key ones), on top
+# of bf16 roundings that fall the other way.  The plausible mistakes of a
+# kernel move the gradients by 1 % or more per tensor
+# (test_mx_bwd_gates_separate_mistakes).
+MX_GRAD_RTOL = 5e-3
 MX_GRAD_SEQ_RTOL = 1e-2
 
 

@@ -472,8 +472,10 @@ def test_backward_matches_loop_implementation(causal):
 def test_mx_bwd_gates_separate_mistakes(monkeypatch):
     """The MXFP8 backward's GPU gates (tests.mx_util) are tight enough to see
     the plausible mistakes of a kernel: each, planted in the oracle, fails
-    them by a factor of 3 or more -- relative L2 against the correct oracle,
-    per tensor or per sequence, at least 3x the gate in some gradient.
+    them by a factor of 2 or more -- relative L2 against the correct oracle,
+    per tensor or per sequence, at least 2x the gate in some gradient.
+    Sequences start off the 32-row grid (where a block boundary counted from
+    the packed row 0 differs from one counted from the sequence's start).
 
     Not among them: the axis or the block boundaries of P's and dS's own
     quantisation.  With the fitted exponent (R8) nothing saturates, so the
@@ -483,7 +485,7 @@ def test_mx_bwd_gates_separate_mistakes(monkeypatch):
     to them)."""
     from tests.gpu_util import rel_l2, seq_rel_l2
     from tests.mx_util import MX_GRAD_RTOL, MX_GRAD_SEQ_RTOL
-    lengths = [1, 31, 32, 33, 64, 65, 200, 130]
+    lengths = [5, 37, 50, 71, 100, 130, 201]
     q, k, v, out, do, lse, qo, ko = _draw_bwd(lengths, lengths, 2, 128, 3, True)
     ref = mx.mx_attention_bwd(q, k, v, out, do, lse, qo, ko, 0.3, True)
     orig_keys, orig_mat = mx.mx_quantize_keys, mx.mx_quantize_matrix
@@ -515,4 +517,4 @@ def test_mx_bwd_gates_separate_mistakes(monkeypatch):
         got = mutant(name)
         worst = max(max(rel_l2(g, r) / MX_GRAD_RTOL, seq_rel_l2(g, r, o)[0] / MX_GRAD_SEQ_RTOL)
                     for g, r, o in zip(got, ref, (qo, ko, ko)))
-        assert worst >= 3.0, (name, worst)
+        assert worst >= 2.0, (name, worst)
