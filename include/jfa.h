@@ -377,7 +377,8 @@ int jfa_pooled_backward(const void* seeds, const void* k, const void* v, const v
  * 32 (offsets[b] / 32 + b) + i (block row offsets[b] / 32 + b + i / 32).
  *   JFA_MX_ROWS (q, k): codes [heads][32 N][head_dim], scales [heads][32 N]
  *     [head_dim / 32], blocks of 32 consecutive elements of a row.
- *   JFA_MX_KEYS (v): codes [heads][N][head_dim][32]: within a column, row
+ *   JFA_MX_KEYS = JFA_MX_COLUMNS (v; for the backward also q, k and
+ *     dout): codes [heads][N][head_dim][32]: within a column, row
  *     i of the block at byte 16 ((i / 4) % 2) + 4 (i / 8) + i % 4 (the order
  *     the attention kernel's weights arrive in); scales [heads][N][32]
  *     [head_dim / 32], column 32 c + r at [r][c]; blocks of 32 consecutive
@@ -387,7 +388,7 @@ int jfa_pooled_backward(const void* seeds, const void* k, const void* v, const v
  * for jfa_forward, JFA_ERR_UNSUPPORTED for head_dim other than 64 and 128,
  * JFA_ERR_INVALID_ARGUMENT for a bad layout or NULL / misaligned pointers,
  * JFA_ERR_WORKSPACE_TOO_SMALL for image_bytes below jfa_mx_image_bytes. */
-enum jfa_mx_layout { JFA_MX_ROWS = 0, JFA_MX_KEYS = 1 };
+enum jfa_mx_layout { JFA_MX_ROWS = 0, JFA_MX_KEYS = 1, JFA_MX_COLUMNS = 1 };
 size_t jfa_mx_image_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t total);
 int jfa_mx_quantize(const void* x, const int32_t* offsets, int32_t batch, int32_t heads, int32_t head_dim,
                     int32_t total, int32_t layout, void* image, size_t image_bytes, hipStream_t stream);
@@ -401,6 +402,62 @@ int jfa_mx_attend(const void* q_image, const void* k_image, const void* v_image,
                   const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
                   int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t causal, void* out,
                   float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+
+/* MXFP8 attention backward (same page and sections as the MXFP8 forward:
+ * training in MXFP8 covers the backward as well).  Every product takes its
+ * two operands in MXFP8 blocks of 32 along its own contraction axis:
+ *   S = q k^T and dP = dout v^T over the head dimension: q, k, v and dout
+ *     in JFA_MX_ROWS images;
+ *   dV = P^T dout and dK = scale dS^T q over queries: P and dS quantised in
+ *     the kernel in blocks of 32 consecutive queries of a key, counted from
+ *     the sequence's first query; dout and q in JFA_MX_COLUMNS images (q
+ *     offsets);
+ *   dQ = scale dS k over keys: dS in blocks of 32 consecutive keys of a
+ *     query, counted from the sequence's first key; k in a JFA_MX_COLUMNS
+ *     image (kv offsets).
+ * P = exp(scale q.k - lse) is recomputed in fp32 from the quantised scores
+ * and the forward's lse; delta = rowsum(dout o out) from the bf16 out and
+ * dout; dS = P o (dP - delta) is formed in fp32 before either of its
+ * quantisations.  Products accumulate in fp32; dq, dk and dv are written
+ * in bf16 [total, heads, head_dim], every row (zeros where no pair is
+ * visible).  Each output row is written by one workgroup: no atomics, the
+ * result is reproducible bit for bit.
+ *
+ * jfa_mx_backward takes bf16 q, k, v, out, dout and the forward's lse
+ * (arguments, layouts and causal rule as for jfa_backward with activation
+ * softmax and dtype bf16, head_dim 64 or 128) and quantises the seven
+ * images itself.  Workspace: jfa_mx_backward_workspace_size with
+ * with_images = 1 (256-byte aligned: work lists, row statistics and the
+ * seven images); events: NULL, or 5 events recorded before the
+ * quantisation, after it, after the work lists and row statistics, after
+ * the dK/dV kernel and after the dQ kernel.
+ *
+ * jfa_mx_backward_images takes the seven images instead of q, k, v (and
+ * dout for the products; dout and out still give delta): `images` is a
+ * host array of 7 device pointers, in this order: q (JFA_MX_ROWS), q
+ * (JFA_MX_COLUMNS), k (ROWS), k (COLUMNS), v (ROWS), dout (ROWS), dout
+ * (COLUMNS), each as jfa_mx_quantize writes it (256-byte aligned; NULL
+ * allowed only for a side whose total is 0).  jfa_mx_backward equals
+ * jfa_mx_quantize of each followed by jfa_mx_backward_images, bit for bit.
+ * Workspace: jfa_mx_backward_workspace_size with with_images = 0; events:
+ * NULL, or 4 events (before the work lists, after them, after dK/dV, after
+ * dQ).
+ *
+ * Errors: as for jfa_backward (softmax, bf16), plus JFA_ERR_UNSUPPORTED for
+ * head_dim other than 64 and 128 and JFA_ERR_INVALID_ARGUMENT for a
+ * workspace or image not 256-byte aligned or a NULL image array. */
+size_t jfa_mx_backward_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                                      int32_t total_kv, int32_t with_images);
+int jfa_mx_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                    const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch, int32_t heads,
+                    int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
+                    float scale, int32_t causal, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
+int jfa_mx_backward_images(const void* const* images, const void* out, const void* dout, const float* lse,
+                           const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch, int32_t heads,
+                           int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
+                           int32_t max_kv_len, float scale, int32_t causal, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
 
 /* Device check of the offsets (debug; the jagged-input item's offsets
  * contract).  With JFA_CHECK_OFFSETS=1 in the environment, the work-list

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjfa.so")
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "bwd.hip", "blocks.hip", "noalloc.hip", "bbs.cpp", "pooled.hip", "mx.hip"]
+SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "bwd.hip", "blocks.hip", "noalloc.hip", "bbs.cpp", "pooled.hip", "mx.hip", "mx_bwd.hip"]
 
 
 def hipcc():

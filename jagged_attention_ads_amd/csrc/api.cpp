@@ -907,6 +907,199 @@ int jfa_mx_attend(const void* q_image, const void* k_image, const void* v_image,
                         events ? events[0] : nullptr, events ? events[1] : nullptr, events ? events[2] : nullptr);
 }
 
+}  // extern "C"
+
+namespace {
+
+// MXFP8 backward workspace: the offsets-check word, the query-tile list
+// (dQ pass), the key-tile list (dK/dV pass), the row statistics, then (when
+// the library quantises) the seven images in the order of kMxBwdImages.
+constexpr int kMxBwdImages = 7;   // Q rows, Q columns, K rows, K columns, V rows, dO rows, dO columns
+struct MxBwdWsLayout {
+  jfa::WorklistLayout wq{}, wkv{};
+  MxImageLayout iq{}, ik{};
+  size_t off_wq = 0, off_wkv = 0, off_stats = 0, off_img[kMxBwdImages] = {}, lists = 0, bytes = 0;
+};
+MxBwdWsLayout mx_bwd_ws_layout(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv) {
+  MxBwdWsLayout L;
+  L.wq = jfa::worklist_layout(jfa::kPassQ, batch, heads, total_q);
+  L.wkv = jfa::worklist_layout(jfa::kPassKV, batch, heads, total_kv);
+  L.off_wq = kStatusBytes;
+  L.off_wkv = align256(L.off_wq + L.wq.bytes);
+  L.off_stats = align256(L.off_wkv + L.wkv.bytes);
+  L.lists = L.off_stats + align256(static_cast<size_t>(heads) * static_cast<size_t>(total_q) * 2 * sizeof(float));
+  L.iq = mx_image_layout(batch, heads, head_dim, total_q);
+  L.ik = mx_image_layout(batch, heads, head_dim, total_kv);
+  size_t off = L.lists;
+  for (int i = 0; i < kMxBwdImages; ++i) {
+    L.off_img[i] = off;
+    off += (i == 2 || i == 3 || i == 4) ? L.ik.bytes : L.iq.bytes;
+  }
+  L.bytes = off;
+  return L;
+}
+
+int mx_bwd_check(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim,
+                 int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale,
+                 int32_t causal, void* dq, void* dk, void* dv) {
+  int st = jfa::forward_args_status(q, k, v, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv,
+                                    max_q_len, max_kv_len, scale, JFA_ACT_SOFTMAX, causal, JFA_DTYPE_BF16, out, lse);
+  if (st != JFA_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return fail(JFA_ERR_UNSUPPORTED, "MXFP8 needs head_dim 64 or 128");
+  if ((total_q > 0 && (!dout || !dq)) || (total_kv > 0 && (!dk || !dv)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "NULL gradient pointer");
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "gradient pointer not 16-byte aligned");
+  if (buckets_for(max_q_len, jfa::kBwdBM) > jfa::kMaxBuckets)
+    return fail(JFA_ERR_UNSUPPORTED, "max_q_len exceeds the scheduler's range");
+  return JFA_OK;
+}
+
+// The backward from the seven images: work lists and row statistics
+// (events [0] before, [1] after), dK/dV ([2] after), dQ ([3] after).
+// Arguments already checked.
+int mx_bwd_impl(const uint8_t* const* img, const void* out, const void* dout, const float* lse,
+                const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim,
+                int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale, int32_t causal,
+                void* dq, void* dk, void* dv, char* ws, hipStream_t stream, hipEvent_t* ev) {
+  const MxBwdWsLayout L = mx_bwd_ws_layout(batch, heads, head_dim, total_q, total_kv);
+  auto rec = [&](int i) { return ev && ev[i] ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  hipError_t e;
+  jfa::MxBwdArgs a{};
+  auto image = [&](int i, const MxImageLayout& il) { return jfa::MxImage{img[i], img[i] + il.scales}; };
+  a.q = image(0, L.iq);
+  a.qc = image(1, L.iq);
+  a.k = image(2, L.ik);
+  a.kc = image(3, L.ik);
+  a.v = image(4, L.ik);
+  a.dout = image(5, L.iq);
+  a.doc = image(6, L.iq);
+  a.rq = 32 * L.iq.nbr;
+  a.rk = 32 * L.ik.nbr;
+  a.meta_q = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wq + L.wq.meta_off);
+  a.meta_kv = reinterpret_cast<const jfa::ItemMeta*>(ws + L.off_wkv + L.wkv.meta_off);
+  float* lse2 = reinterpret_cast<float*>(ws + L.off_stats);
+  float* delta = lse2 + static_cast<size_t>(heads) * static_cast<size_t>(total_q);
+  a.lse2 = lse2;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.heads = heads;
+  a.total_q = total_q;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const jfa::StatsArgs sa{out, dout, lse, lse2, delta, heads, total_q};
+  const jfa::OffsetCheck chk = offset_check(ws, total_q, total_kv, max_q_len, max_kv_len);
+  const int32_t nbq = buckets_for(max_kv_len, jfa::kFwdBN), nbk = buckets_for(max_q_len, jfa::kBwdBM);
+  if ((e = rec(0)) != hipSuccess) return hip_fail(e, "event record");
+  const bool pair = total_q > 0 && total_kv > 0;
+  if (pair)
+    e = jfa::launch_sched_pair(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq, nbk,
+                               ws + L.off_wkv, L.wkv, &sa, JFA_DTYPE_BF16, head_dim, chk, stream);
+  else if (total_q > 0)
+    e = jfa::launch_sched(jfa::kPassQ, q_offsets, kv_offsets, batch, heads, causal, nbq, ws + L.off_wq, L.wq, chk,
+                          stream);
+  else
+    e = jfa::launch_sched(jfa::kPassKV, q_offsets, kv_offsets, batch, heads, causal, nbk, ws + L.off_wkv, L.wkv, chk,
+                          stream);
+  if (e != hipSuccess) return hip_fail(e, "work-list builder launch");
+  if (!pair && total_q > 0 && (e = jfa::launch_bwd_stats(sa, head_dim, JFA_DTYPE_BF16, stream)) != hipSuccess)
+    return hip_fail(e, "row statistics kernel launch");
+  if ((e = rec(1)) != hipSuccess) return hip_fail(e, "event record");
+  if (total_kv > 0 && (e = jfa::launch_mx_bwd_dkdv(a, head_dim, L.wkv.capacity, stream)) != hipSuccess)
+    return hip_fail(e, "MXFP8 dK/dV kernel launch");
+  if ((e = rec(2)) != hipSuccess) return hip_fail(e, "event record");
+  if (total_q > 0 && (e = jfa::launch_mx_bwd_dq(a, head_dim, L.wq.capacity, stream)) != hipSuccess)
+    return hip_fail(e, "MXFP8 dQ kernel launch");
+  if ((e = rec(3)) != hipSuccess) return hip_fail(e, "event record");
+  return JFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t jfa_mx_backward_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_t total_q,
+                                      int32_t total_kv, int32_t with_images) {
+  if (mx_check_sizes(batch, heads, head_dim, total_q) != JFA_OK) return 0;
+  if (mx_check_sizes(batch, heads, head_dim, total_kv) != JFA_OK) return 0;
+  if (with_images != 0 && with_images != 1) return 0;
+  const MxBwdWsLayout L = mx_bwd_ws_layout(batch, heads, head_dim, total_q, total_kv);
+  return with_images ? L.bytes : L.lists;
+}
+
+int jfa_mx_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                    const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch, int32_t heads,
+                    int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len,
+                    float scale, int32_t causal, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  int st = mx_bwd_check(q, k, v, out, dout, lse, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv,
+                        max_q_len, max_kv_len, scale, causal, dq, dk, dv);
+  if (st != JFA_OK) return st;
+  if (batch == 0 || (total_q == 0 && total_kv == 0)) return JFA_OK;   // nothing to write
+  if ((st = mx_check_sizes(batch, heads, head_dim, total_q)) != JFA_OK) return st;
+  if ((st = mx_check_sizes(batch, heads, head_dim, total_kv)) != JFA_OK) return st;
+  const MxBwdWsLayout L = mx_bwd_ws_layout(batch, heads, head_dim, total_q, total_kv);
+  if (!workspace || workspace_bytes < L.bytes) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  if (!aligned256(workspace)) return fail(JFA_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e;
+  if (events && events[0] && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "event record");
+  // the seven images in one launch
+  jfa::MxQuantArgs qa{};
+  const void* src[kMxBwdImages] = {q, q, k, k, v, dout, dout};
+  const bool qside[kMxBwdImages] = {true, true, false, false, false, true, true};
+  const bool cols[kMxBwdImages] = {false, true, false, true, false, false, true};
+  const uint8_t* img[kMxBwdImages];
+  for (int z = 0; z < kMxBwdImages; ++z) {
+    const MxImageLayout& il = qside[z] ? L.iq : L.ik;
+    const int32_t tot = qside[z] ? total_q : total_kv;
+    qa.x[z] = src[z];
+    qa.off[z] = qside[z] ? q_offsets : kv_offsets;
+    qa.total[z] = tot;
+    qa.nbr[z] = tot > 0 ? static_cast<int32_t>(il.nbr) : 0;
+    qa.keys[z] = cols[z] ? 1 : 0;
+    qa.codes[z] = reinterpret_cast<uint8_t*>(ws + L.off_img[z]);
+    qa.scales[z] = reinterpret_cast<uint8_t*>(ws + L.off_img[z] + il.scales);
+    img[z] = qa.codes[z];
+  }
+  qa.batch = batch;
+  qa.heads = heads;
+  e = jfa::launch_mx_quant(qa, head_dim, kMxBwdImages, stream);
+  if (e != hipSuccess) return hip_fail(e, "MX quantisation kernel launch");
+  return mx_bwd_impl(img, out, dout, lse, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
+                     max_kv_len, scale, causal, dq, dk, dv, ws, stream, events ? events + 1 : nullptr);
+}
+
+int jfa_mx_backward_images(const void* const* images, const void* out, const void* dout, const float* lse,
+                           const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch, int32_t heads,
+                           int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
+                           int32_t max_kv_len, float scale, int32_t causal, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  if (!images) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL image array");
+  const uint8_t* img[kMxBwdImages];
+  for (int i = 0; i < kMxBwdImages; ++i) {
+    const int32_t tot = (i == 2 || i == 3 || i == 4) ? total_kv : total_q;
+    if (tot > 0 && !images[i]) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL image");
+    if (!aligned256(images[i])) return fail(JFA_ERR_INVALID_ARGUMENT, "image not 256-byte aligned");
+    img[i] = static_cast<const uint8_t*>(images[i]);
+  }
+  // the images stand where the bf16 values would: same pointer and size rules
+  int st = mx_bwd_check(images[0], images[2], images[4], out, dout, lse, q_offsets, kv_offsets, batch, heads,
+                        head_dim, total_q, total_kv, max_q_len, max_kv_len, scale, causal, dq, dk, dv);
+  if (st != JFA_OK) return st;
+  if (batch == 0 || (total_q == 0 && total_kv == 0)) return JFA_OK;
+  if ((st = mx_check_sizes(batch, heads, head_dim, total_q)) != JFA_OK) return st;
+  if ((st = mx_check_sizes(batch, heads, head_dim, total_kv)) != JFA_OK) return st;
+  const MxBwdWsLayout L = mx_bwd_ws_layout(batch, heads, head_dim, total_q, total_kv);
+  if (!workspace || workspace_bytes < L.lists) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  return mx_bwd_impl(img, out, dout, lse, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
+                     max_kv_len, scale, causal, dq, dk, dv, static_cast<char*>(workspace), stream, events);
+}
+
 int jfa_check_device_error(const void* workspace, hipStream_t stream) {
   if (!workspace) return fail(JFA_ERR_INVALID_ARGUMENT, "NULL workspace");
   int word = 0;

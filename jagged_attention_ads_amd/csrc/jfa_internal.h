@@ -162,20 +162,22 @@ hipError_t launch_pooled_reduce(const void* dq, int64_t seed_elems, int32_t batc
 // mx_block_rows(batch, total) blocks of 32 rows.
 inline int64_t mx_block_rows(int32_t batch, int32_t total) { return (int64_t)total / 32 + batch; }
 
-// Up to three bf16 [total, heads, D] tensors into MX images in one launch.
+// Up to kMxQuantMax bf16 [total, heads, D] tensors into MX images in one
+// launch.
 // Row image (keys = 0): codes [heads][32 nbr][D], E8M0 scale codes
 // [heads][32 nbr][D/32], blocks of 32 elements along a row.  Column image
 // (keys = 1): codes [heads][nbr][D][32] with key i of a block at byte
 // mx_key_pos(i) of its column, scales [heads][nbr][32][D/32] (column
 // 32 c + r at [r][c]), blocks of 32 rows of a sequence per column.
+constexpr int kMxQuantMax = 8;
 struct MxQuantArgs {
-  const void* x[3];
-  const int32_t* off[3];
-  int32_t total[3];
-  int32_t nbr[3];
-  int32_t keys[3];
-  uint8_t* codes[3];
-  uint8_t* scales[3];
+  const void* x[kMxQuantMax];
+  const int32_t* off[kMxQuantMax];
+  int32_t total[kMxQuantMax];
+  int32_t nbr[kMxQuantMax];
+  int32_t keys[kMxQuantMax];
+  uint8_t* codes[kMxQuantMax];
+  uint8_t* scales[kMxQuantMax];
   int32_t batch;
   int32_t heads;
 };
@@ -199,6 +201,35 @@ struct MxFwdArgs {
   float scale_log2;
 };
 hipError_t launch_mx_fwd(const MxFwdArgs& a, int head_dim, int64_t grid, hipStream_t stream);
+
+// MXFP8 backward (see mx_bwd.hip): every product takes its operands in MX
+// blocks along its own contraction axis.  Row images (blocks along the head
+// dimension) of Q, K, V and dO for S and dP; column images (blocks of 32
+// rows of a sequence) of dO and Q for dV and dK, and of K for dQ.
+struct MxImage {
+  const uint8_t* x;    // codes
+  const uint8_t* s;    // E8M0 scale codes
+};
+struct MxBwdArgs {
+  MxImage q, k, v, dout;      // row images
+  MxImage qc, kc, doc;        // column images
+  int64_t rq;                 // image rows (32 block rows) of the query-side and key-side images
+  int64_t rk;
+  const ItemMeta* meta_q;     // 128-query tiles (kPassQ): the dQ pass
+  const ItemMeta* meta_kv;    // 64-key tiles (kPassKV): the dK/dV pass
+  const float* lse2;          // [heads, total_q]: lse * log2(e) (0 for rows without keys)
+  const float* delta;         // [heads, total_q]: rowsum(dO o O)
+  void* dq;                   // bf16 [total, heads, D]
+  void* dk;
+  void* dv;
+  int32_t heads;
+  int32_t total_q;
+  int32_t causal;
+  float scale;
+  float scale_log2;
+};
+hipError_t launch_mx_bwd_dkdv(const MxBwdArgs& a, int head_dim, int64_t grid, hipStream_t stream);
+hipError_t launch_mx_bwd_dq(const MxBwdArgs& a, int head_dim, int64_t grid, hipStream_t stream);
 
 // BlockAttention: the runs of `block` tokens of every sequence as offsets
 // (see blocks.hip).

@@ -35,8 +35,9 @@ EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_pr
             "jfa_forward_noalloc", "jfa_bbs_batch_count", "jfa_bbs_plan", "jfa_block_workspace_size",
             "jfa_block_forward", "jfa_block_backward", "jfa_pooled_workspace_size", "jfa_pooled_forward",
             "jfa_pooled_backward", "jfa_mx_image_bytes", "jfa_mx_quantize", "jfa_mx_workspace_size",
-            "jfa_mx_forward", "jfa_mx_attend")
-MX_LAYOUTS = {"rows": 0, "keys": 1}
+            "jfa_mx_forward", "jfa_mx_attend", "jfa_mx_backward_workspace_size", "jfa_mx_backward",
+            "jfa_mx_backward_images")
+MX_LAYOUTS = {"rows": 0, "keys": 1, "columns": 1}
 BBS_COSTS = {"tokens": 0, "pairs": 1}
 
 
@@ -114,6 +115,12 @@ def lib():
         L.jfa_mx_forward.argtypes = [_vp] * 5 + [_i32] * 7 + [_f32, _i32, _vp, _vp, _vp, _sz, _vp, _vp]
         L.jfa_mx_attend.restype = ctypes.c_int
         L.jfa_mx_attend.argtypes = L.jfa_mx_forward.argtypes
+        L.jfa_mx_backward_workspace_size.restype = _sz
+        L.jfa_mx_backward_workspace_size.argtypes = [_i32] * 6
+        L.jfa_mx_backward.restype = ctypes.c_int
+        L.jfa_mx_backward.argtypes = [_vp] * 8 + [_i32] * 7 + [_f32, _i32] + [_vp] * 4 + [_sz, _vp, _vp]
+        L.jfa_mx_backward_images.restype = ctypes.c_int
+        L.jfa_mx_backward_images.argtypes = [_vp] * 6 + [_i32] * 7 + [_f32, _i32] + [_vp] * 4 + [_sz, _vp, _vp]
         L.jfa_last_error.restype = ctypes.c_char_p
         L.jfa_last_error.argtypes = []
         _lib = L
@@ -343,7 +350,8 @@ def pooled_backward(seeds, k, v, out, dout, lse, kv_offsets, max_kv_len, scale=N
 
 def mx_quantize(x, offsets, layout):
     """MX image of a bf16 tensor x [total, H, d] (layout "rows" for q and k,
-    "keys" for v) as a uint8 device tensor; see jfa.h for its layout."""
+    "keys" = "columns" for v; the backward also takes q, k and dout as
+    "columns") as a uint8 device tensor; see jfa.h for its layout."""
     _offsets("offsets", offsets)
     _values("x", x, torch.bfloat16)
     T, H, D = x.shape
@@ -393,6 +401,58 @@ def mx_attend(q_image, k_image, v_image, q_offsets, kv_offsets, heads, head_dim,
                                heads, head_dim, total_q, total_kv, int(max_q_len), int(max_kv_len), float(scale),
                                int(bool(causal)), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(), events))
     return out, lse
+
+
+MX_BACKWARD_IMAGES = (("q", "rows"), ("q", "columns"), ("k", "rows"), ("k", "columns"), ("v", "rows"),
+                      ("dout", "rows"), ("dout", "columns"))
+
+
+def mx_backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_len, scale=None, causal=False,
+                ws=None, events=None):
+    """MXFP8 softmax attention backward from bf16 tensors (the library
+    quantises the seven operand images); returns (dq, dk, dv) in bf16."""
+    _offsets("q_offsets", q_offsets)
+    _offsets("kv_offsets", kv_offsets)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _values(name, t, torch.bfloat16)
+    T_q, H, D = q.shape
+    B = q_offsets.numel() - 1
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if ws is None:
+        ws = torch.empty(max(lib().jfa_mx_backward_workspace_size(B, H, D, T_q, k.shape[0], 1), 1),
+                         dtype=torch.uint8, device=q.device)
+    _check(lib().jfa_mx_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(q_offsets),
+                                 _ptr(kv_offsets), B, H, D, T_q, k.shape[0], int(max_q_len), int(max_kv_len),
+                                 float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                 ws.numel(), _stream(), events))
+    return dq, dk, dv
+
+
+def mx_backward_images(images, out, dout, lse, q_offsets, kv_offsets, heads, head_dim, total_q, total_kv,
+                       max_q_len, max_kv_len, scale=None, causal=False, ws=None, events=None):
+    """MXFP8 backward from the seven MX images, in the order of
+    MX_BACKWARD_IMAGES (mx_quantize's output); out and dout (bf16) give
+    delta.  Returns (dq, dk, dv) in bf16."""
+    _offsets("q_offsets", q_offsets)
+    _offsets("kv_offsets", kv_offsets)
+    if len(images) != len(MX_BACKWARD_IMAGES):
+        raise ValueError("mx_backward_images takes %d images" % len(MX_BACKWARD_IMAGES))
+    B = q_offsets.numel() - 1
+    dev_ = out.device
+    scale = 1.0 / math.sqrt(head_dim) if scale is None else scale
+    dq = torch.empty((total_q, heads, head_dim), dtype=torch.bfloat16, device=dev_)
+    dk = torch.empty((total_kv, heads, head_dim), dtype=torch.bfloat16, device=dev_)
+    dv = torch.empty_like(dk)
+    if ws is None:
+        ws = torch.empty(max(lib().jfa_mx_backward_workspace_size(B, heads, head_dim, total_q, total_kv, 0), 1),
+                         dtype=torch.uint8, device=dev_)
+    ptrs = (ctypes.c_void_p * len(images))(*[_ptr(x) for x in images])
+    _check(lib().jfa_mx_backward_images(ptrs, _ptr(out), _ptr(dout), _ptr(lse), _ptr(q_offsets), _ptr(kv_offsets), B,
+                                        heads, head_dim, total_q, total_kv, int(max_q_len), int(max_kv_len),
+                                        float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                        ws.numel(), _stream(), events))
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------- allocating wrappers

@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 27, names
+    assert len(names) == 30, names
     L = jfa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -270,3 +270,50 @@ def test_mx_quantize_rejects(kw, status):
     a.update(kw)
     assert jfa.lib().jfa_mx_quantize(a["x"], a["off"], a["batch"], a["heads"], a["d"], a["total"], a["layout"],
                                      a["img"], a["nb"], None) == status
+
+
+def _mxb(images=False, **kw):
+    a = dict(q=P, k=P, v=P, out=P, do=P, lse=P, qo=P, ko=P, batch=2, heads=2, d=64, tq=10, tk=10, mq=5, mk=5,
+             scale=0.125, causal=0, dq=P, dk=P, dv=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    tail = (a["qo"], a["ko"], a["batch"], a["heads"], a["d"], a["tq"], a["tk"], a["mq"], a["mk"], a["scale"],
+            a["causal"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], None, None)
+    if images:
+        imgs = a.get("imgs", (ctypes.c_void_p * 7)(*([a["q"]] * 7)))
+        return jfa.lib().jfa_mx_backward_images(imgs, a["out"], a["do"], a["lse"], *tail)
+    return jfa.lib().jfa_mx_backward(a["q"], a["k"], a["v"], a["out"], a["do"], a["lse"], *tail)
+
+
+@pytest.mark.parametrize("images", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=None), INVALID), (dict(out=None), INVALID), (dict(do=None), INVALID), (dict(dq=None), INVALID),
+    (dict(dv=MIS), INVALID), (dict(scale=0.0), INVALID), (dict(causal=3), INVALID), (dict(d=32), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED), (dict(heads=257), UNSUPPORTED), (dict(ws=None), WS_SMALL), (dict(wsb=100), WS_SMALL),
+    (dict(mq=1 << 20), UNSUPPORTED),
+])
+def test_mx_backward_rejects(images, kw, status):
+    """MXFP8 backward's argument checks, on the host before anything is
+    enqueued, for both entry points."""
+    assert _mxb(images, **kw) == status
+
+
+def test_mx_backward_rejects_images_and_workspace():
+    assert _mxb(False, ws=P + 16) == INVALID
+    assert _mxb(True, imgs=None) == INVALID
+    assert _mxb(True, imgs=(ctypes.c_void_p * 7)(*([P] * 6 + [None]))) == INVALID
+    assert _mxb(True, imgs=(ctypes.c_void_p * 7)(*([P] * 6 + [P + 16]))) == INVALID
+    # a side with no rows may pass NULL images and gradients
+    assert _mxb(True, tk=0, dk=None, dv=None, ws=None, wsb=0, batch=0) == OK
+
+
+def test_mx_backward_noop_and_sizes():
+    assert _mxb(False, batch=0, ws=None, wsb=0) == OK
+    assert _mxb(True, batch=0, ws=None, wsb=0) == OK
+    L = jfa.lib()
+    full = L.jfa_mx_backward_workspace_size(3, 2, 64, 100, 200, 1)
+    lists = L.jfa_mx_backward_workspace_size(3, 2, 64, 100, 200, 0)
+    # the seven images follow the lists: q, q, k, k, v, dout, dout
+    assert full == lists + 4 * L.jfa_mx_image_bytes(3, 2, 64, 100) + 3 * L.jfa_mx_image_bytes(3, 2, 64, 200)
+    assert lists > 2 * 2 * 100 * 4   # holds the row statistics
+    assert L.jfa_mx_backward_workspace_size(3, 2, 64, 100, 200, 2) == 0
+    assert L.jfa_mx_backward_workspace_size(3, 2, 48, 100, 200, 1) == 0
