@@ -54,7 +54,8 @@ COMMON_SRC = ("jfa_common.hpp", "jfa_internal.h")
 KERNEL_SRC = {"sched_q": ("sched.hip", "blocks.hip", "pooled.hip"), "fwd": ("fwd.hip",),
               "bwd_sched": ("sched.hip", "bwd_stats.hpp", "pooled.hip"), "bwd_stats": ("bwd.hip", "bwd_stats.hpp"),
               "bwd_dkdv": ("bwd.hip",), "bwd_dq": ("bwd.hip", "pooled.hip"), "mx_quant": ("mx.hip",),
-              "mx_fwd": ("mx.hip",)}
+              "mx_fwd": ("mx.hip", "mx_common.hpp"), "mx_bwd_dkdv": ("mx_bwd.hip", "mx_common.hpp"),
+              "mx_bwd_dq": ("mx_bwd.hip", "mx_common.hpp")}
 
 
 def kernel_source_digest(kernel=None):
@@ -197,10 +198,21 @@ def kernel_accounting(wl, T_q, T_k, pairs_total, n_ds_blocks, ds_path, short=(0,
     if wl.mx:
         # MXFP8: the quantisation reads Q, K, V (bf16) and writes their images
         # (a byte per element plus a scale byte per 32); the attention reads
-        # the images and writes O (bf16) and lse
+        # the images and writes O (bf16) and lse.  The backward's images:
+        # Q, dO along the head dimension and along queries, K along the head
+        # dimension and along keys, V along the head dimension (its
+        # quantisation reads Q, K, V, dO in bf16 and writes the seven); the
+        # dK/dV pass reads the Q and dO images of both kinds, the K and V
+        # rows, lse and delta and writes dK, dV; the dQ pass reads the Q and
+        # dO rows, the three K and V images, lse and delta and writes dQ
         img = lambda rows: rows * H * d * (1 + 1.0 / 32)   # noqa: E731
         acc = {"mx_quant": dict(flops=0, bytes=(T_q + 2 * T_k) * H * d * 2 + img(T_q) + 2 * img(T_k)),
-               "fwd": dict(flops=4 * d * H * pairs_total, bytes=img(T_q) + 2 * img(T_k) + T_q * H * d * 2 + row_f32)}
+               "fwd": dict(flops=4 * d * H * pairs_total, bytes=img(T_q) + 2 * img(T_k) + T_q * H * d * 2 + row_f32),
+               "mx_quant_bwd": dict(flops=0, bytes=(2 * T_q + 2 * T_k) * H * d * 2 + 4 * img(T_q) + 3 * img(T_k)),
+               "bwd_sched": dict(flops=2 * d * H * T_q, bytes=2 * q_bytes + 3 * row_f32),
+               "bwd_dkdv": dict(flops=8 * d * H * pairs_total, bytes=4 * img(T_q) + 2 * img(T_k) + 2 * row_f32
+                                + 2 * k_bytes),
+               "bwd_dq": dict(flops=6 * d * H * pairs_total, bytes=2 * img(T_q) + 3 * img(T_k) + 2 * row_f32 + q_bytes)}
     return acc
 
 
@@ -272,9 +284,11 @@ def _cpu_unit(arg):
             oracle.pooled_bwd(c["q"][:, hs], k, v, c["do"][sq, hs], one_k, c["scale"], c["act"])
         return (14 if with_bwd else 4) * c["d"] * c["pairs"][b]
     q, k, v = c["q"][sq, hs], c["k"][sk, hs], c["v"][sk, hs]
-    if c["mx"]:   # MXFP8 forward (its V blocks start at each sequence: one sequence alone is the same)
-        oracle.mx_attention_fwd(q, k, v, one_q, one_k, c["scale"], c["causal"])
-        return 4 * c["d"] * c["pairs"][b]
+    if c["mx"]:   # MXFP8 (its column blocks start at each sequence: one sequence alone is the same)
+        out, lse = oracle.mx_attention_fwd(q, k, v, one_q, one_k, c["scale"], c["causal"])
+        if with_bwd:
+            oracle.mx_attention_bwd(q, k, v, out, c["do"][sq, hs], lse, one_q, one_k, c["scale"], c["causal"])
+        return (14 if with_bwd else 4) * c["d"] * c["pairs"][b]
     oracle.attention_fwd(q, k, v, one_q, one_k, c["scale"], c["act"], c["causal"], block=blk, rope_base=c["rope"])
     if with_bwd:
         oracle.attention_bwd(q, k, v, c["do"][sq, hs], one_q, one_k, c["scale"], c["act"], c["causal"], block=blk,
@@ -448,13 +462,32 @@ class Runner:
             self.fwd_slots = {"mx_quant": (0, 1), "sched_q": (1, 2), "fwd": (2, 3)}
         self.nf = max(b for _, b in self.fwd_slots.values()) + 1
         self.fwd_end = self.nf - 1
+        # the backward call's event slots likewise (the list launch forms the
+        # row statistics: "bwd_stats" is empty unless a kernel of its own runs)
+        self.bwd_slots = {"bwd_sched": (0, 1), "bwd_stats": (1, 2), "bwd_dkdv": (2, 3), "bwd_dq": (3, 4)}
+        if self.mx_mode == "attend":
+            self.bwd_slots = {"bwd_sched": (0, 1), "bwd_dkdv": (1, 2), "bwd_dq": (2, 3)}
+        elif self.mx_mode == "forward":
+            self.bwd_slots = {"mx_quant_bwd": (0, 1), "bwd_sched": (1, 2), "bwd_dkdv": (2, 3), "bwd_dq": (3, 4)}
+        self.nb = max(b for _, b in self.bwd_slots.values()) + 1
+        self.bwd_end = self.nb - 1
         if wl.mx:
             self.ws_f = torch.empty(max(L.jfa_mx_workspace_size(B, H, D, T_q, T_k, int(mx_mode == "forward")), 1),
                                     dtype=torch.uint8, device=dev)
-            self.ws_b = None
+            self.ws_b = torch.empty(max(L.jfa_mx_backward_workspace_size(B, H, D, T_q, T_k,
+                                                                         int(mx_mode == "forward")), 1),
+                                    dtype=torch.uint8, device=dev)
             if mx_mode == "attend":
+                # the operands as their producers would hand them over: the
+                # forward's Q, K rows and V columns; the backward's seven
                 self.images = [jfa.mx_quantize(t, o, lay) for t, o, lay in
                                ((self.q, qo, "rows"), (self.k, ko, "rows"), (self.v, ko, "keys"))]
+                src = {"q": (self.q, qo), "k": (self.k, ko), "v": (self.v, ko), "dout": (self.do, qo)}
+                self.bwd_images = [self.images[0] if (t, lay) == ("q", "rows") else
+                                   self.images[1] if (t, lay) == ("k", "rows") else
+                                   jfa.mx_quantize(src[t][0], src[t][1], lay) for t, lay in jfa.MX_BACKWARD_IMAGES]
+                self.bwd_image_ptrs = (ctypes.c_void_p * len(self.bwd_images))(
+                    *[x.data_ptr() for x in self.bwd_images])
                 torch.cuda.synchronize()
         elif wl.n_seeds:
             dtc = jfa.DTYPES[self.q.dtype]
@@ -491,7 +524,7 @@ class Runner:
         """(side, first event, second event) around kernel `name`."""
         if name in self.fwd_slots:
             return (0,) + self.fwd_slots[name]
-        return SLOTS[name]
+        return (1,) + self.bwd_slots[name]
 
     def fwd(self, events):
         ev = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
@@ -539,6 +572,24 @@ class Runner:
 
     def bwd(self, events):
         ev = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
+        if self.mx_mode == "attend":
+            st = self.L.jfa_mx_backward_images(
+                self.bwd_image_ptrs, self.P(self.out), self.P(self.do), self.P(self.lse), self.P(self.qo),
+                self.P(self.ko), self.B, self.H, self.D, self.T_q, self.T_k, self.mq, self.mk, self.scale,
+                int(self.wl.causal), self.P(self.dq), self.P(self.dk), self.P(self.dv), self.P(self.ws_b),
+                self.ws_b.numel(), self.stream, ev)
+            if st != 0:
+                raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+            return
+        if self.mx_mode == "forward":
+            st = self.L.jfa_mx_backward(
+                self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.out), self.P(self.do), self.P(self.lse),
+                self.P(self.qo), self.P(self.ko), self.B, self.H, self.D, self.T_q, self.T_k, self.mq, self.mk,
+                self.scale, int(self.wl.causal), self.P(self.dq), self.P(self.dk), self.P(self.dv), self.P(self.ws_b),
+                self.ws_b.numel(), self.stream, ev)
+            if st != 0:
+                raise self.jfa.JfaError(st, self.L.jfa_last_error().decode())
+            return
         if self.wl.n_seeds:
             st = self.L.jfa_pooled_backward(
                 self.P(self.q), self.P(self.k), self.P(self.v), self.P(self.out), self.P(self.do),
@@ -587,14 +638,14 @@ def timed_steps(r, ev, K, flush_buf, dom=None):
     that kernel (side 0: the forward's event slots, 1: the backward's).
     Returns per-step lists of milliseconds: step, fwd, bwd, dominant kernel,
     and the whole timed region."""
-    nf, nb = r.nf, 5
+    nf, nb = r.nf, r.nb
     evs = []
     for _ in range(K):
         ef, eb = (ctypes.c_void_p * nf)(), (ctypes.c_void_p * nb)()
         made = ev.create(5)
         ef[0] = made[0]
         if r.run_bwd:
-            eb[0], eb[4] = made[1], made[2]
+            eb[0], eb[r.bwd_end] = made[1], made[2]
         else:
             ef[r.fwd_end] = made[2]
         if dom is not None:
@@ -615,11 +666,11 @@ def timed_steps(r, ev, K, flush_buf, dom=None):
     r.torch.cuda.synchronize()
     out = {"step": [], "fwd": [], "bwd": [], "dom": [], "region": ev.ms(edge[0], edge[1])}
     for ef, eb, made in evs:
-        end = eb[4] if r.run_bwd else ef[r.fwd_end]
+        end = eb[r.bwd_end] if r.run_bwd else ef[r.fwd_end]
         out["step"].append(ev.ms(ef[0], end))
         if r.run_bwd:
             out["fwd"].append(ev.ms(ef[0], eb[0]))
-            out["bwd"].append(ev.ms(eb[0], eb[4]))
+            out["bwd"].append(ev.ms(eb[0], eb[r.bwd_end]))
         else:
             out["fwd"].append(ev.ms(ef[0], ef[r.fwd_end]))
         if dom is not None:
@@ -635,7 +686,7 @@ def kernel_breakdown(r, ev, K, flush_buf):
     two launches (each event adds a few microseconds between launches, so
     these steps are not the timed ones)."""
     ef = [ev.create(r.nf) for _ in range(K)]
-    eb = [ev.create(5) for _ in range(K)] if r.run_bwd else []
+    eb = [ev.create(r.nb) for _ in range(K)] if r.run_bwd else []
     r.torch.cuda.synchronize()
     for i in range(K):
         if flush_buf is not None:
@@ -647,15 +698,10 @@ def kernel_breakdown(r, ev, K, flush_buf):
         return float(np.mean([ev.ms(e[a], e[b]) for e in lst])) if lst else 0.0
     kern = {n: avg(ef, a, b) for n, (a, b) in r.fwd_slots.items()}
     if r.run_bwd:
-        kern.update({"bwd_sched": avg(eb, 0, 1), "bwd_stats": avg(eb, 1, 2), "bwd_dkdv": avg(eb, 2, 3),
-                     "bwd_dq": avg(eb, 3, 4)})
+        kern.update({n: avg(eb, a, b) for n, (a, b) in r.bwd_slots.items()})
     for e in ef + eb:
         ev.destroy(e)
     return kern
-
-
-SLOTS = {"sched_q": (0, 0, 1), "fwd": (0, 1, 2), "bwd_sched": (1, 0, 1), "bwd_stats": (1, 1, 2),
-         "bwd_dkdv": (1, 2, 3), "bwd_dq": (1, 3, 4)}
 
 
 def bbs_study(args):
@@ -815,10 +861,11 @@ def main():
     t_s = dom_ms * 1e-3
     a = acct[name]
     ai = a["flops"] / a["bytes"]
-    src_key = "mx_fwd" if wl.mx and name == "fwd" else name
+    mx_kernel = wl.mx and name in ("fwd", "bwd_dkdv", "bwd_dq")
+    src_key = "mx_" + name if mx_kernel else name
     digest = kernel_source_digest(src_key)
     # the MXFP8 attention's products run at the fp8 rate
-    peak_mfma = PEAK_FP8_TFLOPS if wl.mx and name == "fwd" else PEAK_BF16_TFLOPS
+    peak_mfma = PEAK_FP8_TFLOPS if mx_kernel else PEAK_BF16_TFLOPS
     if ai < peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
         roof = {"bound": "hbm", "achieved": a["bytes"] / t_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
@@ -867,36 +914,50 @@ def main():
         "roofline": roof,
     }
     if wl.mx:
-        # the bf16 forward on the same batch, and the MXFP8 path from bf16
+        # the bf16 path on the same batch, and the MXFP8 path from bf16
         # inputs (quantisation included), timed the same way: the pages quote
-        # MXFP8's forward gain over the 16-bit kernel
+        # MXFP8's forward and backward gains over the 16-bit kernels
         res["fwd"]["pct_of_fp8_peak"] = 100.0 * res["fwd"]["tflops"] / PEAK_FP8_TFLOPS
+        if r.run_bwd:
+            res["bwd"]["pct_of_fp8_peak"] = 100.0 * res["bwd"]["tflops"] / PEAK_FP8_TFLOPS
         import dataclasses
         rb = Runner(dataclasses.replace(wl, mx=False), batch, dev)
-        rb.run_bwd = False
         for _ in range(3):
             rb.step()
         tb = timed_steps(rb, ev, K, flush_buf)
-        bms = float(np.median(tb["fwd"]))
+        bf = float(np.median(tb["fwd"]))
         kb = kernel_breakdown(rb, ev, K, flush_buf)
-        res["bf16_forward"] = {"median_us": bms * 1e3, "tflops": tf(useful_fwd, bms),
-                               "kernel_us": {k_: v_ * 1e3 for k_, v_ in kb.items()},
-                               "mx_speedup": bms / fwd_ms,
-                               "mx_kernel_speedup": kb["fwd"] / kern_ms["fwd"],
-                               "timing": "the same batch through jfa_forward (bf16), timed as the headline"}
+        base = {"fwd_us": bf * 1e3, "fwd_tflops": tf(useful_fwd, bf), "mx_fwd_speedup": bf / fwd_ms,
+                "mx_fwd_kernel_speedup": kb["fwd"] / kern_ms["fwd"],
+                "kernel_us": {k_: v_ * 1e3 for k_, v_ in kb.items()}}
+        if r.run_bwd:
+            bb, bs = float(np.median(tb["bwd"])), float(np.median(tb["step"]))
+            base.update({"bwd_us": bb * 1e3, "bwd_tflops": tf(useful_bwd, bb), "step_us": bs * 1e3,
+                         "mx_bwd_speedup": bb / bwd_ms, "mx_step_speedup": bs / ms_step,
+                         "mx_bwd_kernels_speedup": (kb["bwd_dkdv"] + kb["bwd_dq"])
+                         / (kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"])})
+        base["timing"] = "the same batch through jfa_forward / jfa_backward (bf16), timed as the headline"
+        res["bf16_path"] = base
         del rb
         rq = Runner(wl, batch, dev, mx_mode="forward")
         for _ in range(3):
             rq.step()
         tq = timed_steps(rq, ev, K, flush_buf)
-        qms = float(np.median(tq["fwd"]))
+        qf = float(np.median(tq["fwd"]))
         kq = kernel_breakdown(rq, ev, K, flush_buf)
         qa = acct["mx_quant"]
-        res["mx_from_bf16"] = {"median_us": qms * 1e3, "tflops": tf(useful_fwd, qms), "vs_bf16_forward": bms / qms,
-                               "kernel_us": {k_: v_ * 1e3 for k_, v_ in kq.items()},
-                               "mx_quant_hbm_frac": qa["bytes"] / (kq["mx_quant"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                               "timing": "jfa_mx_forward (bf16 q, k, v quantised, then attended), timed as the "
-                                         "headline"}
+        fb = {"fwd_us": qf * 1e3, "fwd_tflops": tf(useful_fwd, qf), "fwd_vs_bf16": bf / qf,
+              "kernel_us": {k_: v_ * 1e3 for k_, v_ in kq.items()},
+              "mx_quant_hbm_frac": qa["bytes"] / (kq["mx_quant"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        if r.run_bwd:
+            qb, qs_ = float(np.median(tq["bwd"])), float(np.median(tq["step"]))
+            qq = acct["mx_quant_bwd"]
+            fb.update({"bwd_us": qb * 1e3, "bwd_tflops": tf(useful_bwd, qb), "bwd_vs_bf16": bb / qb,
+                       "step_us": qs_ * 1e3, "step_vs_bf16": bs / qs_,
+                       "mx_quant_bwd_hbm_frac": qq["bytes"] / (kq["mx_quant_bwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS})
+        fb["timing"] = ("jfa_mx_forward / jfa_mx_backward (bf16 q, k, v, dO quantised by the library, then the "
+                        "attention), timed as the headline")
+        res["mx_from_bf16"] = fb
         del rq
     if t_warm is not None:
         wms = float(np.median(t_warm["step"]))

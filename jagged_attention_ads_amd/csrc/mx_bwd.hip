@@ -169,20 +169,19 @@ __global__ __launch_bounds__(256, 2) void mx_dkdv_kernel(MxBwdArgs a) {
   const float* rstat = (role_a ? a.lse2 : a.delta) + (size_t)h * a.total_q + qs;
   u32x4 st_r[C::RN];
   uint32_t st_w = 0u;
+  // Rows past the sequence repeat its last row (finite values, and every
+  // weight of such a query is masked to 0): the loads are unconditional, so
+  // that nothing has to wait for them before the stage is stored.
   auto stage_load = [&](int s) {
-    const int q0 = q_first + 64 * s, nv = min(64, lq - q0);
+    const int q0 = q_first + 64 * s, last = lq - 1 - q0;
 #pragma unroll
     for (int i = 0; i < C::RN; ++i) {
-      const int p = i * 128 + tr, r = p / C::CPR, pc = p % C::CPR;
-      st_r[i] = r < nv ? gload16(rimg.x + (qrow + q0 + r) * D + pc * 16) : u32x4{0u, 0u, 0u, 0u};
+      const int p = i * 128 + tr, r = min(p / C::CPR, last), pc = p % C::CPR;
+      st_r[i] = gload16(rimg.x + (qrow + q0 + r) * D + pc * 16);
     }
-    const bool lv = l < nv;
-    if (pair == 0) {
-      if (lv) st_w = scale_word<D>(rimg.s + (qrow + q0 + l) * (D / 32));
-    } else {
-      if (lv) st_w = __float_as_uint(rstat[q0 + l]);
-    }
-    if (!lv) st_w = 0u;
+    const int r = min(l, last);
+    if (pair == 0) st_w = scale_word<D>(rimg.s + (qrow + q0 + r) * (D / 32));
+    else st_w = __float_as_uint(rstat[q0 + r]);
   };
   auto slot = [&](int s) { return smem + (s & 1) * C::STAGE; };
   auto stage_store = [&](int s) {
@@ -205,20 +204,22 @@ __global__ __launch_bounds__(256, 2) void mx_dkdv_kernel(MxBwdArgs a) {
   // A operand of this wave's gradient product for step s: the dO (A) or Q
   // (B) column image, blocks q_first/32 + 2s and + 1 (k blocks 0 and 1),
   // column 32 dt + c32, lane half g's 16 bytes; the scale word of block
-  // q_first/32 + 2s + g, row c32 (byte dt: column 32 dt + c32).  Blocks past
-  // the sequence read as zeros.
+  // q_first/32 + 2s + g, row c32 (byte dt: column 32 dt + c32).  A block
+  // past the sequence is read as its last block instead: the B operand's
+  // codes of those queries are 0 (their weights are masked), so the product
+  // takes nothing from it, and the loads need no condition.
   const MxImage cimg = role_a ? a.doc : a.qc;
   const uint8_t* cx = cimg.x + ((int64_t)h * nbq + qb0) * (D * 32);
   const uint8_t* cs = cimg.s + ((int64_t)h * nbq + qb0) * D;
   auto col_load = [&](ColFrags<C::ND>& cf, int s) {
-    const int blk = q_first / 32 + 2 * s;
-    const bool v1 = blk + 1 < qblocks;
+    const int blk = q_first / 32 + 2 * s, blk1 = min(blk + 1, qblocks - 1);
 #pragma unroll
     for (int dt = 0; dt < C::ND; ++dt) {
-      const uint8_t* p = cx + ((int64_t)blk * D + 32 * dt + c32) * 32 + 16 * g;
-      cf.f[dt] = cat8(gload16(p), v1 ? gload16(p + D * 32) : u32x4{0u, 0u, 0u, 0u});
+      const int col = 32 * dt + c32;
+      cf.f[dt] = cat8(gload16(cx + ((int64_t)blk * D + col) * 32 + 16 * g),
+                      gload16(cx + ((int64_t)blk1 * D + col) * 32 + 16 * g));
     }
-    cf.s = blk + g < qblocks ? scale_word<D>(cs + ((int64_t)(blk + g) * 32 + c32) * (D / 32)) : 0u;
+    cf.s = scale_word<D>(cs + ((int64_t)(g ? blk1 : blk) * 32 + c32) * (D / 32));
   };
 
   // B operand of S (A: the lane's key row) or dP (B: its value row): head
@@ -339,40 +340,44 @@ __global__ __launch_bounds__(256, 2) void mx_dkdv_kernel(MxBwdArgs a) {
     return quantise_pair<false>(dd, sc, g);
   };
 
-  // Step s: stage s+1 and this step's gradient operands are read into
-  // registers first; stage s+1 is written to LDS at the end (its slot held
-  // stage s-1, which every wave finished before the last barrier), and every
-  // load has landed before the barrier, so none is in flight across
-  // iterations.  A works on step s; B finishes step s-1 (dS, then its dK
-  // products after dP of step s) and forms dP(s).  The roles run loops of
-  // their own (each wave meets the same nst + 1 barriers), so that neither
-  // keeps the other's values live.
+  // Step s: stage s+1 is read into registers first and written to LDS at
+  // the end (its slot held stage s-1, which every wave finished before the
+  // last barrier).  A works on step s; B finishes step s-1 (dS, then its dK
+  // products after dP of step s) and forms dP(s).  Each wave loads the
+  // gradient operands of the step it finishes next right after its
+  // products have consumed the current ones.  Every load is issued without a branch (past the last step
+  // they repeat it), which keeps the compiler's waits for them exact.  The
+  // roles run loops of their own (each wave meets the same nst + 1
+  // barriers), so that neither keeps the other's values live.  The
+  // barriers order LDS only (lds_barrier), so that the operand loads stay in
+  // flight across them.
   ColFrags<C::ND> cf;
-  if (role_a) {
+  if (nst > 0 && role_a) {
+    col_load(cf, 0);
     for (int s = 0; s < nst; ++s) {
-      if (s + 1 < nst) stage_load(s + 1);
+      const int nx = min(s + 1, nst - 1);   // the last step reloads its own operands, unused
+      stage_load(nx);
       if (visible(s)) {
-        col_load(cf, s);
         if (needs_mask(s)) a_step(std::true_type{}, s, cf);
         else a_step(std::false_type{}, s, cf);
       }
+      col_load(cf, nx);
       if (s + 1 < nst) stage_store(s + 1);
-      __syncthreads();
+      lds_barrier();
     }
-  } else {
+  } else if (nst > 0) {
     for (int s = 0; s <= nst; ++s) {
-      if (s + 1 < nst) stage_load(s + 1);
+      stage_load(min(s + 1, nst - 1));
       const bool prev = s > 0 && visible(s - 1);
+      const bool vis = s < nst && visible(s);
       i32x8 sc;
       uint32_t ss = 0u;
-      if (prev) {
-        col_load(cf, s - 1);
-        ss = b_ds(s - 1, sc);
-      }
-      if (s < nst && visible(s)) b_dp(s);
+      if (prev) ss = b_ds(s - 1, sc);
+      if (vis) b_dp(s);
       if (prev) grad_products<C::ND>(acc, cf.f, sc, cf.s, ss);
+      col_load(cf, min(s, nst - 1));
       if (s + 1 < nst) stage_store(s + 1);
-      if (s < nst) __syncthreads();
+      if (s < nst) lds_barrier();
     }
   }
 

@@ -45,7 +45,7 @@ class Workload:
     block: int = 0        # > 0: BlockAttention, attention within runs of `block` tokens
     rope_base: float = 0.0  # > 0: BlockAttention's fused rotary embedding of that base
     n_seeds: int = 0      # > 0: pooled attention, n_seeds shared queries per sequence (q_law unused)
-    mx: bool = False      # MXFP8 forward (E4M3 operands, E8M0 block scales; bf16 in and out)
+    mx: bool = False      # MXFP8 (E4M3 operands, E8M0 block scales; bf16 in and out)
 
 
 WORKLOADS = {
@@ -108,9 +108,9 @@ WORKLOADS["pooled_hist"] = Workload(
 # the bf16 forward on the same batch.
 WORKLOADS["mx_selfattn_causal"] = Workload(
     "mx_selfattn_causal", 256, 4, 128, "bf16", 1.0, True, "softmax",
-    ("lognormal", 256, 1024), None, False,
-    "MXFP8 (E4M3, E8M0 block scales) jagged causal self-attention forward, batch 256, log-normal lengths "
-    "(median 256, max 1024), 4 heads, d 128, bf16 in and out", mx=True)
+    ("lognormal", 256, 1024), None, True,
+    "MXFP8 (E4M3, E8M0 block scales) jagged causal self-attention forward and backward, batch 256, log-normal "
+    "lengths (median 256, max 1024), 4 heads, d 128, bf16 in and out", mx=True)
 WORKLOADS["mx_cross_asym"] = Workload(
     "mx_cross_asym", 512, 8, 64, "bf16", 1.0, False, "softmax",
     ("uniform", 1, 64), ("lognormal", 1024, 4096), False,
