@@ -46,13 +46,13 @@ namespace {
 
 __device__ __forceinline__ u32x4 gload16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Four signed elements of a block into one word, times the block's inverse
-// scale (byte i = x_i).
+// Four elements of a block into one word, times the block's inverse fitted
+// scale (byte i = x_i).  With the fitted scale no product exceeds 448, so
+// the conversion needs no clamp.
 __device__ __forceinline__ uint32_t codes4(const f32x16& x, int q, float inv) {
-  return fp8x4(x[4 * q] * inv, x[4 * q + 1] * inv, x[4 * q + 2] * inv, x[4 * q + 3] * inv);
-}
-__device__ __forceinline__ uint32_t codes4_pos(const f32x16& x, int q, float inv) {
-  return fp8x4_pos(x[4 * q] * inv, x[4 * q + 1] * inv, x[4 * q + 2] * inv, x[4 * q + 3] * inv);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q] * inv, x[4 * q + 1] * inv, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2] * inv, x[4 * q + 3] * inv, w, true);
+  return (uint32_t)w;
 }
 
 // E8M0 code of the fitted block scale of P and dS: the least 2^k with amax
@@ -81,7 +81,7 @@ __device__ __forceinline__ uint32_t quantise_pair(const f32x16* x, i32x8& out, i
     code[c] = e8m0_code_fit(xor32_max(amax));
     const float inv = e8m0_inverse(code[c]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) out[4 * c + q] = (int)(POS ? codes4_pos(x[c], q, inv) : codes4(x[c], q, inv));
+    for (int q = 0; q < 4; ++q) out[4 * c + q] = (int)codes4(x[c], q, inv);
   }
   return g ? code[1] : code[0];
 }
