@@ -394,7 +394,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     // stage n+1 must have landed before the barrier (B issued it; A has no
     // copies in flight); later ones may be in flight
     if (!role_a && n + 1 < nst) wait_stage<NPS>(min(C::NS - 3, nst - 2 - n));
-    __syncthreads();
+    // LDS only: a full barrier would also wait for every copy still meant to
+    // be in flight and for B's dS stores (one counter covers them all)
+    lds_barrier();
     // every wave is done with stage n-1: refill its slot
     if (!role_a && n + C::NS - 1 < nst) issue_stage(n + C::NS - 1);
     if (role_a) {

@@ -461,6 +461,20 @@ struct TileDma {
   }
 };
 
+// Workgroup barrier ordering LDS only: this wave's LDS reads and writes
+// complete before it, and later LDS accesses stay after it.  Unlike
+// __syncthreads it does not wait for the wave's global loads and stores
+// (vector memory shares one counter with the LDS copies), so copies and
+// loads issued for a later step, and stores to global memory, stay in
+// flight across it.  For use where nothing in global memory passes between
+// the workgroup's waves; copies into LDS are waited for explicitly
+// (dma_wait*) before it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wait until this wave's outstanding global->LDS copies have landed.
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

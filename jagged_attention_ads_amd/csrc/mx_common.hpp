@@ -101,17 +101,6 @@ __device__ __forceinline__ int mx_v_off(int c, int d, int g) {
   return c * D * 32 + d * 32 + ((g ^ ((d >> 3) & 1)) * 16);
 }
 
-// Workgroup barrier ordering LDS only: this wave's LDS reads and writes
-// complete before it, and later LDS accesses stay after it.  Unlike
-// __syncthreads it does not wait for the wave's global loads, so loads
-// issued for a later step stay in flight across it (nothing in global
-// memory passes between the workgroup's waves).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 __device__ __forceinline__ i32x8 cat8(const u32x4& a, const u32x4& b) {
   return __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
