@@ -507,14 +507,14 @@ class Runner:
             self.ws_b = jfa.workspace(B, H, D, T_q, T_k, mk, self.q.dtype, True, dev)
         # the dK/dV pass stores dS and the dQ pass reads it, unless switched
         # off or the store was left out of the workspace
-        self.ds_path = (not wl.rope_base and not wl.n_seeds and not wl.mx and os.environ.get("JFA_BWD_DS") != "0"
+        self.ds_path = (not wl.rope_base and not wl.n_seeds and not wl.mx and L.jfa_get_option(1) != 0
                         and self.ws_b.numel() > jfa.jfa_workspace_size(B, H, D, T_q, T_k, mk, self.q.dtype, 2))
         # the dK/dV pass writes the dQ of short sequences (bf16, d 64 or 128:
         # where its LDS has room) when every sequence is short, or always with
-        # JFA_BWD_FUSE_SHORT=2; never with 0
-        fuse_mode = os.environ.get("JFA_BWD_FUSE_SHORT", "1")
+        # the option bwd_short_dq on; never with it off
+        fuse_opt = L.jfa_get_option(2)
         self.fuse_short = (wl.dtype == "bf16" and D in (64, 128)
-                           and (bool(wl.rope_base) or (fuse_mode != "0" and (fuse_mode == "2" or max(mq, mk) <= 64))))
+                           and (bool(wl.rope_base) or (fuse_opt != 0 and (fuse_opt == 1 or max(mq, mk) <= 64))))
         self.act = jfa.ACTIVATIONS[wl.activation]
         self.dt = jfa.DTYPES[self.q.dtype]
         self.lse_arg = self.lse if wl.activation == "softmax" else None

@@ -63,8 +63,9 @@
  * batch == 0 (or no rows at all) is a successful no-op.  The offsets live in
  * device memory and are not validated by default: offsets that break the
  * rules above, or lengths above max_q_len / max_kv_len, are undefined
- * behaviour.  With the environment variable JFA_CHECK_OFFSETS=1 they are
- * checked on the device instead (see jfa_check_device_error).
+ * behaviour.  With the offsets check on (JFA_OPT_CHECK_OFFSETS, or the
+ * environment variable JFA_CHECK_OFFSETS=1) they are checked on the device
+ * instead (see jfa_check_device_error).
  */
 #ifndef JFA_H_
 #define JFA_H_
@@ -116,9 +117,9 @@ size_t jfa_workspace_size(int32_t batch, int32_t heads, int32_t head_dim, int32_
  * sequence is short (max_q_len <= 64 and max_kv_len <= 64) the attention
  * kernel runs as a two-wave variant that fits twice the work items per
  * compute unit; its outputs equal the four-wave kernel's bit for bit, and
- * JFA_FWD_SHORT=0 in the environment keeps the four-wave kernel.  That
+ * the option JFA_OPT_FWD_SHORT = 0 keeps the four-wave kernel.  That
  * variant takes one workgroup per (sequence, head) straight from the
- * offsets, and no work list is built, unless JFA_CHECK_OFFSETS=1. */
+ * offsets, and no work list is built, unless the offsets check is on. */
 int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                 const int32_t* kv_offsets, int32_t batch, int32_t heads, int32_t head_dim,
                 int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len, float scale,
@@ -137,7 +138,7 @@ int jfa_forward(const void* q, const void* k, const void* v, const int32_t* q_of
  * JFA_ERR_HIP if the array's device address cannot be looked up.  It calls
  * no allocating routine.  All calls on one GPU share its array: calls that
  * overlap on one GPU (several streams or threads) race and must be ordered
- * by the caller.  With JFA_CHECK_OFFSETS=1 the offsets are still checked
+ * by the caller.  With the offsets check on the offsets are still checked
  * (rejected offsets write nothing), but the check word is not readable
  * through jfa_check_device_error. */
 int jfa_forward_noalloc(const void* q, const void* k, const void* v, const int32_t* q_offsets,
@@ -154,16 +155,16 @@ int jfa_forward_noalloc(const void* q, const void* k, const void* v, const int32
  * (both lists), the row statistics kernel (softmax only: per row,
  * sum(dout * out) and lse in log2 units, into the workspace), the dK/dV
  * kernel (which also stores the dS blocks in the workspace), then the dQ
- * kernel (dQ = scale * dS K over the stored blocks).  The environment
- * variable JFA_BWD_DS=0, or a workspace sized without the dS store, makes
- * the dQ kernel recompute dS from Q, K, V and dout instead.  When every
+ * kernel (dQ = scale * dS K over the stored blocks).  The option
+ * JFA_OPT_BWD_DS_STORE = 0, or a workspace sized without the dS store,
+ * makes the dQ kernel recompute dS from Q, K, V and dout instead.  When every
  * sequence is short (max_q_len <= 64 and max_kv_len <= 64, bf16 with
  * head_dim 64 or 128), each (sequence, head) is one dK/dV work item that
  * sees all of its keys and queries; that item then also forms and writes
  * the sequence's dQ from dS kept on chip, and the dQ kernel only zeroes the
  * rows of sequences without keys.  The results equal the two-pass ones bit
- * for bit.  JFA_BWD_FUSE_SHORT=0 turns this off; =2 applies it to the short
- * sequences of any batch (the dQ kernel then skips them). */
+ * for bit.  The option JFA_OPT_BWD_SHORT_DQ = 0 turns this off; = 1 applies
+ * it to the short sequences of any batch (the dQ kernel then skips them). */
 int jfa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, const int32_t* q_offsets, const int32_t* kv_offsets, int32_t batch,
                  int32_t heads, int32_t head_dim, int32_t total_q, int32_t total_kv, int32_t max_q_len,
@@ -460,7 +461,8 @@ int jfa_mx_backward_images(const void* const* images, const void* out, const voi
                            void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events);
 
 /* Device check of the offsets (debug; the jagged-input item's offsets
- * contract).  With JFA_CHECK_OFFSETS=1 in the environment, the work-list
+ * contract).  With the option JFA_OPT_CHECK_OFFSETS = 1 (by default: the
+ * environment variable JFA_CHECK_OFFSETS=1, read once), the work-list
  * builder of jfa_forward and jfa_backward first checks on the device that
  * q_offsets[0] = kv_offsets[0] = 0, that neither array decreases, that
  * q_offsets[batch] = total_q and kv_offsets[batch] = total_kv, and that no
@@ -471,6 +473,33 @@ int jfa_mx_backward_images(const void* const* images, const void* out, const voi
  * check was off), or JFA_ERR_INVALID_ARGUMENT with the failed rules in
  * jfa_last_error(); JFA_ERR_HIP if the word cannot be read. */
 int jfa_check_device_error(const void* workspace, hipStream_t stream);
+
+/* Process-wide path options, for tests, timing studies and debugging.  Each
+ * holds -1 (the library's choice, the default), 0 (off) or 1 (on); a call
+ * takes the values set when it is made.  They choose between paths whose
+ * results are equal bit for bit (or, for the offsets check, add a device
+ * check of the inputs).
+ *   JFA_OPT_CHECK_OFFSETS   device check of the offsets (above); default:
+ *                           on iff JFA_CHECK_OFFSETS=1 in the environment.
+ *   JFA_OPT_BWD_DS_STORE    0: the dQ kernel recomputes dS even when the
+ *                           workspace holds the dS blocks.
+ *   JFA_OPT_BWD_SHORT_DQ    the dK/dV kernel forms the dQ of short
+ *                           sequences: 0 never, 1 whenever it can; default
+ *                           when every sequence is short.
+ *   JFA_OPT_FWD_SHORT       0: the forward keeps the four-wave kernel for
+ *                           batches of short sequences.
+ * jfa_set_option returns JFA_ERR_INVALID_ARGUMENT for an unknown option or
+ * a value outside -1 .. 1; jfa_get_option returns the value, or -2 for an
+ * unknown option. */
+enum jfa_option {
+  JFA_OPT_CHECK_OFFSETS = 0,
+  JFA_OPT_BWD_DS_STORE = 1,
+  JFA_OPT_BWD_SHORT_DQ = 2,
+  JFA_OPT_FWD_SHORT = 3,
+  JFA_OPT_COUNT = 4
+};
+int jfa_set_option(int32_t option, int32_t value);
+int32_t jfa_get_option(int32_t option);
 
 /* Human-readable name of a status code (static storage). */
 const char* jfa_status_string(int status);

@@ -4,6 +4,7 @@
 #include "jfa.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -75,11 +76,21 @@ WsLayout ws_layout(int32_t batch, int32_t heads, int32_t total_q, int32_t total_
   return L;
 }
 
-// JFA_CHECK_OFFSETS=1: the work-list builder validates the offsets on the
-// device first (see jfa_check_device_error).
+// Process-wide path options (jfa_set_option); -1 = chosen by the library.
+std::atomic<int32_t> g_options[JFA_OPT_COUNT] = {{-1}, {-1}, {-1}, {-1}};
+
+int32_t option(int32_t which) { return g_options[which].load(std::memory_order_relaxed); }
+
+// The work-list builder validates the offsets on the device first (see
+// jfa_check_device_error): JFA_OPT_CHECK_OFFSETS = 1, or by default the
+// environment variable JFA_CHECK_OFFSETS=1, read once.
 bool check_offsets_enabled() {
-  const char* e = std::getenv("JFA_CHECK_OFFSETS");
-  return e && e[0] == '1' && e[1] == 0;
+  static const bool env = [] {
+    const char* e = std::getenv("JFA_CHECK_OFFSETS");
+    return e && e[0] == '1' && e[1] == 0;
+  }();
+  const int32_t o = option(JFA_OPT_CHECK_OFFSETS);
+  return o < 0 ? env : o == 1;
 }
 
 jfa::OffsetCheck offset_check(void* ws, int32_t total_q, int32_t total_kv, int32_t max_q_len, int32_t max_kv_len) {
@@ -87,12 +98,9 @@ jfa::OffsetCheck offset_check(void* ws, int32_t total_q, int32_t total_kv, int32
                           max_kv_len};
 }
 
-// JFA_BWD_DS=0 makes the backward recompute dS in the dQ pass even when the
-// workspace holds the dS blocks (for tests of that pass).
-bool ds_disabled() {
-  const char* e = std::getenv("JFA_BWD_DS");
-  return e && e[0] == '0' && e[1] == 0;
-}
+// JFA_OPT_BWD_DS_STORE = 0 makes the backward recompute dS in the dQ pass
+// even when the workspace holds the dS blocks.
+bool ds_disabled() { return option(JFA_OPT_BWD_DS_STORE) == 0; }
 
 // Whether the dK/dV pass writes the dQ of short sequences (at most 64
 // queries and 1 .. 64 keys) itself.  By default only when every sequence is
@@ -100,12 +108,10 @@ bool ds_disabled() {
 // the zero rows of sequences without keys.  In a batch that also holds long
 // sequences, the long ones set the dQ pass's duration and the short ones
 // fill its gaps at no cost, while fusing lengthens the dK/dV pass.
-// JFA_BWD_FUSE_SHORT=0: never; =2: whenever the kernel can (for tests and
-// timing).
+// JFA_OPT_BWD_SHORT_DQ = 0: never; 1: whenever the kernel can.
 bool fuse_short_wanted(int32_t max_q_len, int32_t max_kv_len) {
-  const char* e = std::getenv("JFA_BWD_FUSE_SHORT");
-  if (e && e[0] == '0' && e[1] == 0) return false;
-  if (e && e[0] == '2' && e[1] == 0) return true;
+  const int32_t o = option(JFA_OPT_BWD_SHORT_DQ);
+  if (o >= 0) return o == 1;
   return max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kBwdBN;
 }
 
@@ -284,15 +290,15 @@ static int forward_impl(const void* q, const void* k, const void* v, const int32
   char* ws = static_cast<char*>(workspace);
   hipError_t e;
   // every sequence at most 64 queries and 64 keys: the two-wave variant
-  // (JFA_FWD_SHORT=0 keeps the four-wave kernel, for tests and timing).
-  // Its items all cost at most one key block, so without the offsets check
-  // it takes one block per (sequence, head) and no work list is built.
-  const char* fs = std::getenv("JFA_FWD_SHORT");
+  // (JFA_OPT_FWD_SHORT = 0 keeps the four-wave kernel, for tests and
+  // timing).  Its items all cost at most one key block, so without the
+  // offsets check it takes one block per (sequence, head) and no work list
+  // is built.
   const bool lengths_short = max_q_len <= jfa::kBwdBN && max_kv_len <= jfa::kFwdBN;
   if (rope.on && (!lengths_short || dtype != JFA_DTYPE_BF16 || (head_dim != 64 && head_dim != 128)))
     return fail(JFA_ERR_UNSUPPORTED, "the rotary embedding needs lengths <= 64, bf16 and head_dim 64 or 128");
   // the rotary embedding lives in the two-wave variant only
-  const bool short_batch = lengths_short && (rope.on || !(fs && fs[0] == '0' && fs[1] == 0));
+  const bool short_batch = lengths_short && (rope.on || option(JFA_OPT_FWD_SHORT) != 0);
   const bool direct = short_batch && !check_offsets_enabled() && (int64_t)batch * heads <= INT32_MAX;
   if ((e = record(events, 0, stream)) != hipSuccess) return hip_fail(e, "event record");
   if (!direct) {
@@ -1098,6 +1104,18 @@ int jfa_mx_backward_images(const void* const* images, const void* out, const voi
   if (!workspace || workspace_bytes < L.lists) return fail(JFA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   return mx_bwd_impl(img, out, dout, lse, q_offsets, kv_offsets, batch, heads, head_dim, total_q, total_kv, max_q_len,
                      max_kv_len, scale, causal, dq, dk, dv, static_cast<char*>(workspace), stream, events);
+}
+
+int jfa_set_option(int32_t which, int32_t value) {
+  if (which < 0 || which >= JFA_OPT_COUNT) return fail(JFA_ERR_INVALID_ARGUMENT, "unknown option");
+  if (value < -1 || value > 1) return fail(JFA_ERR_INVALID_ARGUMENT, "option value must be -1, 0 or 1");
+  g_options[which].store(value, std::memory_order_relaxed);
+  return JFA_OK;
+}
+
+int32_t jfa_get_option(int32_t which) {
+  if (which < 0 || which >= JFA_OPT_COUNT) return -2;
+  return option(which);
 }
 
 int jfa_check_device_error(const void* workspace, hipStream_t stream) {

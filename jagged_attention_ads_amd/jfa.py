@@ -36,8 +36,9 @@ EXPORTED = ("jfa_workspace_size", "jfa_forward", "jfa_backward", "jfa_forward_pr
             "jfa_block_forward", "jfa_block_backward", "jfa_pooled_workspace_size", "jfa_pooled_forward",
             "jfa_pooled_backward", "jfa_mx_image_bytes", "jfa_mx_quantize", "jfa_mx_workspace_size",
             "jfa_mx_forward", "jfa_mx_attend", "jfa_mx_backward_workspace_size", "jfa_mx_backward",
-            "jfa_mx_backward_images")
+            "jfa_mx_backward_images", "jfa_set_option", "jfa_get_option")
 MX_LAYOUTS = {"rows": 0, "keys": 1, "columns": 1}
+OPTIONS = {"check_offsets": 0, "bwd_ds_store": 1, "bwd_short_dq": 2, "fwd_short": 3}
 BBS_COSTS = {"tokens": 0, "pairs": 1}
 
 
@@ -115,6 +116,10 @@ def lib():
         L.jfa_mx_forward.argtypes = [_vp] * 5 + [_i32] * 7 + [_f32, _i32, _vp, _vp, _vp, _sz, _vp, _vp]
         L.jfa_mx_attend.restype = ctypes.c_int
         L.jfa_mx_attend.argtypes = L.jfa_mx_forward.argtypes
+        L.jfa_set_option.restype = ctypes.c_int
+        L.jfa_set_option.argtypes = [_i32, _i32]
+        L.jfa_get_option.restype = ctypes.c_int32
+        L.jfa_get_option.argtypes = [_i32]
         L.jfa_mx_backward_workspace_size.restype = _sz
         L.jfa_mx_backward_workspace_size.argtypes = [_i32] * 6
         L.jfa_mx_backward.restype = ctypes.c_int
@@ -250,7 +255,7 @@ def jfa_block_offsets(offsets, total, block=64):
 def jfa_check_device_error(workspace):
     """Synchronises the current stream; returns (status, message) of the
     offsets check of the last call that built a work list in `workspace`
-    (JFA_CHECK_OFFSETS=1)."""
+    (with the offsets check on)."""
     st = lib().jfa_check_device_error(_ptr(workspace), _stream())
     return st, (lib().jfa_last_error().decode() if st != JFA_OK else "")
 
@@ -346,6 +351,31 @@ def pooled_backward(seeds, k, v, out, dout, lse, kv_offsets, max_kv_len, scale=N
                                      ACTIVATIONS[activation], dt, _ptr(dseeds), _ptr(dk), _ptr(dv), _ptr(ws),
                                      ws.numel(), _stream(), None))
     return dseeds, dk, dv
+
+
+def set_option(name, value):
+    """Sets a process-wide path option (see jfa.h): value None (the library's
+    choice), False / 0 or True / 1.  Returns the previous value (None, 0 or
+    1)."""
+    old = lib().jfa_get_option(OPTIONS[name])
+    v = -1 if value is None else int(bool(value))
+    _check(lib().jfa_set_option(OPTIONS[name], v))
+    return None if old < 0 else old
+
+
+class option:
+    """Context manager: a path option set for the duration of a block."""
+
+    def __init__(self, name, value):
+        self.name, self.value = name, value
+
+    def __enter__(self):
+        self.old = set_option(self.name, self.value)
+        return self
+
+    def __exit__(self, *exc):
+        set_option(self.name, self.old)
+        return False
 
 
 def mx_quantize(x, offsets, layout):

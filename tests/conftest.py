@@ -27,3 +27,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def options():
+    """Sets the library's process-wide path options (jfa_set_option) for one
+    test: options(name, value); every option returns to the library's
+    choice afterwards."""
+    from jagged_attention_ads_amd import jfa
+    yield jfa.set_option
+    for name in jfa.OPTIONS:
+        jfa.set_option(name, None)

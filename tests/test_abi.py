@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 30, names
+    assert len(names) == 32, names
     L = jfa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -317,3 +317,17 @@ def test_mx_backward_noop_and_sizes():
     assert lists > 2 * 2 * 100 * 4   # holds the row statistics
     assert L.jfa_mx_backward_workspace_size(3, 2, 64, 100, 200, 2) == 0
     assert L.jfa_mx_backward_workspace_size(3, 2, 48, 100, 200, 1) == 0
+
+
+def test_options():
+    """Path options: set, read back, reset; bad names and values rejected."""
+    L = jfa.lib()
+    assert [L.jfa_get_option(i) for i in range(4)] == [-1, -1, -1, -1]
+    assert L.jfa_set_option(1, 0) == OK and L.jfa_get_option(1) == 0
+    assert L.jfa_set_option(1, -1) == OK and L.jfa_get_option(1) == -1
+    assert L.jfa_set_option(4, 0) == INVALID and L.jfa_set_option(-1, 0) == INVALID
+    assert L.jfa_set_option(0, 2) == INVALID and L.jfa_set_option(0, -2) == INVALID
+    assert L.jfa_get_option(4) == -2
+    with jfa.option("fwd_short", False):
+        assert L.jfa_get_option(3) == 0
+    assert L.jfa_get_option(3) == -1

@@ -235,11 +235,11 @@ _BAD_OFFSETS = {
 
 
 @pytest.mark.parametrize("case", ["valid"] + sorted(_BAD_OFFSETS))
-def test_device_offsets_check(case, monkeypatch):
-    """JFA_CHECK_OFFSETS=1: malformed offsets are rejected on the device, no
+def test_device_offsets_check(case, options):
+    """The offsets check on: malformed offsets are rejected on the device, no
     output is written and jfa_check_device_error names the rule; valid ones
     run as usual and report JFA_OK."""
-    monkeypatch.setenv("JFA_CHECK_OFFSETS", "1")
+    options("check_offsets", 1)
     H, D, T, B = 2, 64, 9, 3
     qo_list, mx, words = ([0, 5, 5, 9], 5, None) if case == "valid" else _BAD_OFFSETS[case]
     g = torch.Generator().manual_seed(7)
@@ -271,11 +271,11 @@ def test_device_offsets_check(case, monkeypatch):
     assert qo.cpu().tolist() == qo_list
 
 
-def test_device_offsets_check_keyless(monkeypatch):
+def test_device_offsets_check_keyless(options):
     """Rejected offsets in a batch of short sequences, one of them without
     keys: the dQ launch, which there only zeroes the rows of sequences
     without keys, writes nothing either."""
-    monkeypatch.setenv("JFA_CHECK_OFFSETS", "1")
+    options("check_offsets", 1)
     H, D, T, B = 2, 64, 9, 3
     g = torch.Generator().manual_seed(8)
     q, k, v, do = (torch.randn((T, H, D), generator=g).to(torch.bfloat16).to(dev()) for _ in range(4))
@@ -294,12 +294,12 @@ def test_device_offsets_check_keyless(monkeypatch):
 
 
 @pytest.mark.parametrize("recompute", [False, True])
-def test_no_keys_at_all(recompute, monkeypatch):
+def test_no_keys_at_all(recompute, options):
     """total_kv = 0 with queries present: only the query-tile list is built and
     the row statistics run as a kernel of their own; out = 0, lse = -inf and
     dq = 0 for every row (both dQ passes)."""
     if recompute:
-        monkeypatch.setenv("JFA_BWD_DS", "0")
+        options("bwd_ds_store", 0)
     H, D = 2, 128
     q = torch.randn((7, H, D), device=dev()).to(torch.bfloat16)
     do = torch.randn((7, H, D), device=dev()).to(torch.bfloat16)

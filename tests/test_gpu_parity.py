@@ -82,25 +82,23 @@ def _edge_batch(name):
 
 
 @pytest.fixture(params=["stored_ds", "recompute", "short_in_dkdv"])
-def dq_path(request, monkeypatch):
+def dq_path(request, options):
     """The backward's dQ paths: from the dS blocks the dK/dV pass stores (the
-    default), or recomputing dS (JFA_BWD_DS=0; also what runs when the dS
-    store would not fit the workspace limit).  short_in_dkdv
-    (JFA_BWD_FUSE_SHORT=2) has the dK/dV pass write the dQ of the short
-    sequences (<= 64 queries, 1 .. 64 keys) in any batch, not only in one
-    where every sequence is short, and the dQ pass skip them."""
-    monkeypatch.delenv("JFA_BWD_DS", raising=False)
-    monkeypatch.delenv("JFA_BWD_FUSE_SHORT", raising=False)
+    default), or recomputing dS (option bwd_ds_store off; also what runs when
+    the dS store would not fit the workspace limit).  short_in_dkdv (option
+    bwd_short_dq on) has the dK/dV pass write the dQ of the short sequences
+    (<= 64 queries, 1 .. 64 keys) in any batch, not only in one where every
+    sequence is short, and the dQ pass skip them."""
     if request.param == "recompute":
-        monkeypatch.setenv("JFA_BWD_DS", "0")
+        options("bwd_ds_store", 0)
     elif request.param == "short_in_dkdv":
-        monkeypatch.setenv("JFA_BWD_FUSE_SHORT", "2")
+        options("bwd_short_dq", 1)
     return request.param
 
 
 @pytest.mark.parametrize("name,batch", [x for x in REDUCED if WORKLOADS[x[0]].backward])
-def test_backward_reduced_recompute(name, batch, monkeypatch):
-    monkeypatch.setenv("JFA_BWD_DS", "0")
+def test_backward_reduced_recompute(name, batch, options):
+    options("bwd_ds_store", 0)
     b = make_batch(name, _seed(name), batch=batch)
     d = Dev(b)
     out, lse = d.forward()
@@ -150,7 +148,7 @@ def test_edge_cases(name, dq_path):
 # that item can also write their dQ, and the dQ pass then skips them.  It does
 # by default when every sequence is short (or has no keys): the dQ pass only
 # zeroes the rows of sequences without keys.  In mixed batches it does with
-# JFA_BWD_FUSE_SHORT=2: short sequences next to ones the dQ pass takes, ones
+# option bwd_short_dq on: short sequences next to ones the dQ pass takes, ones
 # with no keys or no queries, and causal cases where the first query block
 # sees no key (64 queries, 10 keys).
 SHORT_Q = [1, 31, 32, 33, 63, 64, 64, 40, 0, 7, 300, 64, 17]
@@ -172,7 +170,7 @@ SHORT = {
 
 
 @pytest.mark.parametrize("name", sorted(SHORT))
-def test_short_sequences_dq_in_dkdv(name, monkeypatch):
+def test_short_sequences_dq_in_dkdv(name, options):
     """Within the gates of the oracle, and bitwise equal to the results with
     the short sequences left to the dQ pass over stored dS: both take the
     same dS blocks and sum the same products in the same order."""
@@ -180,13 +178,11 @@ def test_short_sequences_dq_in_dkdv(name, monkeypatch):
     wl = dataclasses.replace(WORKLOADS[base], backward=True, **over)
     b = make_batch(wl, 200 + sorted(SHORT).index(name), q_lengths=lq, kv_lengths=lk, with_dout=True)
     d = Dev(b)
-    monkeypatch.delenv("JFA_BWD_DS", raising=False)
-    monkeypatch.delenv("JFA_BWD_FUSE_SHORT", raising=False)
     if max(lq) > 64 or max(lk) > 64:
-        monkeypatch.setenv("JFA_BWD_FUSE_SHORT", "2")
+        options("bwd_short_dq", 1)
     out, lse = d.forward()
     fused = d.backward(out, lse)
-    monkeypatch.setenv("JFA_BWD_FUSE_SHORT", "0")
+    options("bwd_short_dq", 0)
     apart = d.backward(out, lse)
     torch.cuda.synchronize()
     check_backward(fused, oracle_bwd(b), q_off=b.q_offsets, k_off=b.kv_offsets)
@@ -195,18 +191,17 @@ def test_short_sequences_dq_in_dkdv(name, monkeypatch):
 
 
 @pytest.mark.parametrize("name", [n for n in sorted(SHORT) if n.startswith("all_short")])
-def test_short_batch_forward_variant(name, monkeypatch):
+def test_short_batch_forward_variant(name, options):
     """A batch whose sequences all have at most 64 queries and keys runs the
     two-wave forward variant: within the gates of the oracle, and bitwise
-    equal to the four-wave kernel (JFA_FWD_SHORT=0), whose per-row
+    equal to the four-wave kernel (option fwd_short off), whose per-row
     arithmetic it shares."""
     base, over, lq, lk = SHORT[name]
     wl = dataclasses.replace(WORKLOADS[base], **over)
     b = make_batch(wl, 300 + sorted(SHORT).index(name), q_lengths=lq, kv_lengths=lk, with_dout=False)
     d = Dev(b)
-    monkeypatch.delenv("JFA_FWD_SHORT", raising=False)
     out, lse = d.forward()
-    monkeypatch.setenv("JFA_FWD_SHORT", "0")
+    options("fwd_short", 0)
     out4, lse4 = d.forward()
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle_fwd(b)
