@@ -46,13 +46,22 @@ namespace {
 
 __device__ __forceinline__ u32x4 gload16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Four elements of a block into one word, times the block's inverse fitted
-// scale (byte i = x_i).  With the fitted scale no product exceeds 448, so
-// the conversion needs no clamp.
-__device__ __forceinline__ uint32_t codes4(const f32x16& x, int q, float inv) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q] * inv, x[4 * q + 1] * inv, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * q + 2] * inv, x[4 * q + 3] * inv, w, true);
-  return (uint32_t)w;
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Four elements of a block into one word (byte i = x_i), divided by the
+// block's fitted scale in the conversion itself: v_cvt_scalef32_pk_fp8_f32
+// divides by 2^(e - 127), e the exponent field of its scale operand (the
+// significand is ignored), so the E8M0 code shifted into that field is the
+// scale; measured on the hardware bit for bit equal to converting x 2^(127
+// - code) for every code 0 .. 253, zero and subnormal inputs included.
+// With the fitted scale no quotient exceeds 448, so the conversion needs no
+// clamp.
+__device__ __forceinline__ uint32_t codes4(const f32x16& x, int q, uint32_t code) {
+  const float sc = __uint_as_float(code << 23);
+  s16x2 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[4 * q], x[4 * q + 1], sc, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x[4 * q + 2], x[4 * q + 3], sc, true);
+  return __builtin_bit_cast(uint32_t, w);
 }
 
 // E8M0 code of the fitted block scale of P and dS: the least 2^k with amax
@@ -79,9 +88,8 @@ __device__ __forceinline__ uint32_t quantise_pair(const f32x16* x, i32x8& out, i
 #pragma unroll
     for (int r = 0; r < 16; ++r) amax = fmaxf(amax, POS ? x[c][r] : fabsf(x[c][r]));
     code[c] = e8m0_code_fit(xor32_max(amax));
-    const float inv = e8m0_inverse(code[c]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) out[4 * c + q] = (int)codes4(x[c], q, inv);
+    for (int q = 0; q < 4; ++q) out[4 * c + q] = (int)codes4(x[c], q, code[c]);
   }
   return g ? code[1] : code[0];
 }
@@ -254,6 +262,10 @@ __global__ __launch_bounds__(256, 2) void mx_dkdv_kernel(MxBwdArgs a) {
     const int q0 = q_first + 64 * s;
     return q0 + 64 > lq || kw0 + 32 > lk || (a.causal && kw0 + 31 > q0 + off);
   };
+  // the row statistic (lse2 or delta) of register r of block c, 4 at a time
+  auto stat4 = [&](const char* st, int o, int c, int a4) {
+    return *reinterpret_cast<const f32x4*>(st + o + 4 * (32 * c + 8 * a4 + 4 * g));
+  };
   // x[c] = (Q or dO rows of step s) x (this lane's K or V row): block c's
   // query 32c + 8(r/4) + 4g + r%4 of the step in register r
   auto products = [&](f32x16* x, const char* tile, const char* sc) {
@@ -269,14 +281,11 @@ __global__ __launch_bounds__(256, 2) void mx_dkdv_kernel(MxBwdArgs a) {
                      sr, xsc);
     }
   };
-  // the row statistic (lse2 or delta) of register r of block c, 4 at a time
-  auto stat4 = [&](const char* st, int o, int c, int a4) {
-    return *reinterpret_cast<const f32x4*>(st + o + 4 * (32 * c + 8 * a4 + 4 * g));
-  };
   auto xslot = [&](int s) { return smem + 2 * C::STAGE + ((s & 1) * 2 + pair) * C::XS + l * 16; };
 
-  // Wave A, step s: S, P (handed to B), dV^T += dO^T Q(P)
-  auto a_step = [&](auto MASK, int s, const ColFrags<C::ND>& cf) {
+  // Wave A, step s: S, then P (handed to B) quantised into pc (returns the
+  // scale byte of this lane half's block)
+  auto a_p = [&](auto MASK, int s, i32x8& pc) {
     const char* st = slot(s);
     const int q0 = q_first + 64 * s;
     f32x16 x[2];
@@ -305,9 +314,7 @@ __global__ __launch_bounds__(256, 2) void mx_dkdv_kernel(MxBwdArgs a) {
       const int c = k >> 2, q = k & 3;
       *reinterpret_cast<f32x4*>(xo + k * kWave * 16) = f32x4{x[c][4 * q], x[c][4 * q + 1], x[c][4 * q + 2], x[c][4 * q + 3]};
     }
-    i32x8 pc;
-    const uint32_t sp = quantise_pair<true>(x, pc, g);
-    grad_products<C::ND>(acc, cf.f, pc, cf.s, sp);
+    return quantise_pair<true>(x, pc, g);
   };
 
   // Wave B: dP - delta of step s (kept in registers until A's P arrives)
@@ -358,8 +365,12 @@ __global__ __launch_bounds__(256, 2) void mx_dkdv_kernel(MxBwdArgs a) {
       const int nx = min(s + 1, nst - 1);   // the last step reloads its own operands, unused
       stage_load(nx);
       if (visible(s)) {
-        if (needs_mask(s)) a_step(std::true_type{}, s, cf);
-        else a_step(std::false_type{}, s, cf);
+        // one product site, so that the accumulators are updated in place
+        i32x8 pc;
+        uint32_t sp;
+        if (needs_mask(s)) sp = a_p(std::true_type{}, s, pc);
+        else sp = a_p(std::false_type{}, s, pc);
+        grad_products<C::ND>(acc, cf.f, pc, cf.s, sp);
       }
       col_load(cf, nx);
       if (s + 1 < nst) stage_store(s + 1);
@@ -507,14 +518,14 @@ __global__ __launch_bounds__(256, 2) void mx_dq_kernel(MxBwdArgs a) {
     const int kv0 = j * C::BN;
     return (kv0 + C::BN > lk) || (a.causal && kv0 + C::BN - 1 > row0 + off);
   };
-  // x[c] = (K or V rows of the tile, block c) x (this lane's Q or dO row):
-  // key 32c + 8(r/4) + 4g + r%4 of the tile in register r
-  auto products = [&](f32x16* x, const char* tile, const i32x8* yf, uint32_t ysc) {
+  // x[c] = x0 + (K or V rows of the tile, block c) x (this lane's Q or dO
+  // row): key 32c + 8(r/4) + 4g + r%4 of the tile in register r
+  auto products = [&](f32x16* x, const char* tile, const i32x8* yf, uint32_t ysc, const f32x16& x0) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int row = 32 * c + c32;
       const uint32_t sr = scale_word<D>(reinterpret_cast<const uint8_t*>(tile + C::KT) + row * (D / 32)) >> (8 * g);
-      x[c] = f32x16{};
+      x[c] = x0;
       mma_mx<0, 0>(x[c], cat8(lds16(tile + mx_k_off<D>(row, g)), lds16(tile + mx_k_off<D>(row, 2 + g))), yf[0], sr,
                    ysc);
       if constexpr (C::NK > 1)
@@ -522,11 +533,18 @@ __global__ __launch_bounds__(256, 2) void mx_dq_kernel(MxBwdArgs a) {
                      sr, ysc);
     }
   };
-  auto step = [&](auto MASK, int j) {
+  // dP^T accumulates onto -delta (the lane's query), so that the products
+  // leave dP - delta
+  f32x16 ndelta;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndelta[r] = -delta;
+  // dS^T of key tile j quantised along keys into sc (returns the scale byte
+  // of this lane half's block)
+  auto ds_tile = [&](auto MASK, int j, i32x8& sc) {
     const char* st = slot(j);
     f32x16 s[2], ds[2];
-    products(s, st, qf, qsc);
-    products(ds, st + C::OFF_V, df, dsc);
+    products(s, st, qf, qsc, f32x16{});
+    products(ds, st + C::OFF_V, df, dsc, ndelta);
     const int lim = row_limit - j * C::BN - 4 * g;   // masked iff key offset >= lim
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -535,12 +553,14 @@ __global__ __launch_bounds__(256, 2) void mx_dq_kernel(MxBwdArgs a) {
         const float p = fast_exp2(fmaf(s[c][r], a.scale_log2, -lse2));
         bool masked = false;
         if constexpr (decltype(MASK)::value) masked = 32 * c + 8 * (r >> 2) + (r & 3) >= lim;
-        ds[c][r] = masked ? 0.f : p * (ds[c][r] - delta);
+        ds[c][r] = masked ? 0.f : p * ds[c][r];
       }
     }
-    i32x8 sc;
-    const uint32_t ss = quantise_pair<false>(ds, sc, g);
-    const char* ct = st + C::OFF_C;
+    return quantise_pair<false>(ds, sc, g);
+  };
+  // dQ^T += K^T Q(dS^T) over key tile j
+  auto dq_products = [&](int j, const i32x8& sc, uint32_t ss) {
+    const char* ct = slot(j) + C::OFF_C;
     const uint32_t skc = scale_word<D>(reinterpret_cast<const uint8_t*>(ct + C::CT) + g * D + c32 * (D / 32));
     auto dq = [&](auto DT) {
       constexpr int dt = decltype(DT)::value;
@@ -562,8 +582,12 @@ __global__ __launch_bounds__(256, 2) void mx_dq_kernel(MxBwdArgs a) {
     // before the last barrier
     if (j + 1 < n_kv) issue(slot(j + 1), j + 1);
     if (wave_active(j)) {
-      if (needs_mask(j)) step(std::true_type{}, j);
-      else step(std::false_type{}, j);
+      // one product site, so that the accumulators are updated in place
+      i32x8 sc;
+      uint32_t ss;
+      if (needs_mask(j)) ss = ds_tile(std::true_type{}, j, sc);
+      else ss = ds_tile(std::false_type{}, j, sc);
+      dq_products(j, sc, ss);
     }
     dma_wait();
     __syncthreads();
