@@ -312,12 +312,16 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxFwdArgs a) {
     return (kv0 + C::BN > lk) || (a.causal && kv0 + C::BN - 1 > row0 + off);
   };
 
-  // Weights of tile j (quantised into the P^T operand), the scores of tile
-  // j+1 interleaved (NEXT), then O^T += V^T P^T.
-  auto tile_step = [&](auto MASK, auto NEXT, auto PAR, f32x16* s, f32x16* s_nxt, int j) {
-    constexpr bool kMask = decltype(MASK)::value;
-    constexpr int kPar = decltype(PAR)::value;
-    if constexpr (kMask) {
+  // Tile j in two halves, the scores of tile j+1 issued between them: the
+  // masks, block maxima and lazy rescale (returns the two blocks' maxima in
+  // log2 units); then the weights quantised into the P^T operand and
+  // O^T += V^T P^T.  Each call site is single, so that the score and output
+  // accumulators are written in place.
+  struct BlockMax {
+    float b0, b1;
+  };
+  auto tile_max = [&](auto MASK, f32x16* s, int j) {
+    if constexpr (decltype(MASK)::value) {
       const int lim = row_limit - j * C::BN - 4 * g;   // masked iff key offset >= lim
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -333,9 +337,10 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxFwdArgs a) {
       b0 = fmaxf(b0, s[0][r]);
       b1 = fmaxf(b1, s[1][r]);
     }
-    b0 = xor32_max(b0) * a.scale_log2;
-    b1 = xor32_max(b1) * a.scale_log2;
-    const float mx = fmaxf(b0, b1);
+    return BlockMax{xor32_max(b0) * a.scale_log2, xor32_max(b1) * a.scale_log2};
+  };
+  auto rescale = [&](const BlockMax& bm) {
+    const float mx = fmaxf(bm.b0, bm.b1);
     // lazy rescale, the max rounded up to an integer
     const bool grow = mx > m_run + kLazyRescale;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -346,9 +351,11 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxFwdArgs a) {
 #pragma unroll
       for (int i = 0; i < C::ND; ++i) o[i] *= alpha;
     }
-    if constexpr (decltype(NEXT)::value) scores(std::integral_constant<int, 1 - kPar>{}, s_nxt);
-    const float f0 = fmaxf(floorf(b0), m_run - kMxFloorGap);
-    const float f1 = fmaxf(floorf(b1), m_run - kMxFloorGap);
+  };
+  auto tile_pv = [&](auto PAR, const f32x16* s, const BlockMax& bm) {
+    constexpr int kPar = decltype(PAR)::value;
+    const float f0 = fmaxf(floorf(bm.b0), m_run - kMxFloorGap);
+    const float f1 = fmaxf(floorf(bm.b1), m_run - kMxFloorGap);
     // elements 2^(t - floor + 8) of each block, their exact sums, the codes
     float sum0 = 0.f, sum1 = 0.f;
     i32x8 pc;
@@ -384,25 +391,21 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxFwdArgs a) {
   };
 
   // one pipelined step for key tile j (the bf16 forward's schedule): copy
-  // K(j+2) over K(j) and V(j+1) over V(j-1), scores of j+1 with the weights
-  // of j, P V of j, then wait and barrier
+  // K(j+2) over K(j) and V(j+1) over V(j-1), the maxima of j, the scores of
+  // j+1, the weights and P V of j, then wait and barrier
   auto step = [&](auto PAR, int j, f32x16* s_cur, f32x16* s_nxt) {
     constexpr int kPar = decltype(PAR)::value;
     if (j + 2 < n_kv) issue_k(kslot0 + kPar * C::KSLOT, j + 2);
     if (j + 1 < n_kv) issue_v(vslot0 + (1 - kPar) * C::VSLOT, j + 1);
     const bool nxt = j + 1 < n_kv && wave_active(j + 1);
-    if (wave_active(j)) {
-      const bool msk = needs_mask(j);
-      if (nxt) {
-        if (msk) tile_step(std::true_type{}, std::true_type{}, PAR, s_cur, s_nxt, j);
-        else tile_step(std::false_type{}, std::true_type{}, PAR, s_cur, s_nxt, j);
-      } else {
-        if (msk) tile_step(std::true_type{}, std::false_type{}, PAR, s_cur, s_nxt, j);
-        else tile_step(std::false_type{}, std::false_type{}, PAR, s_cur, s_nxt, j);
-      }
-    } else if (nxt) {
-      scores(std::integral_constant<int, 1 - kPar>{}, s_nxt);
+    const bool act = wave_active(j);
+    BlockMax bm{0.f, 0.f};
+    if (act) {
+      bm = needs_mask(j) ? tile_max(std::true_type{}, s_cur, j) : tile_max(std::false_type{}, s_cur, j);
+      rescale(bm);
     }
+    if (nxt) scores(std::integral_constant<int, 1 - kPar>{}, s_nxt);
+    if (act) tile_pv(PAR, s_cur, bm);
     dma_wait();
     __syncthreads();
   };
