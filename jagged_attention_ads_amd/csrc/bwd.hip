@@ -213,8 +213,18 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   const int off = lk - lq;
 
   const int tid = threadIdx.x, l = lane_id(), w = tid >> 6, g = l >> 5, c32 = l & 31;
-  const int pair = w % C::NPAIRS;
-  const bool role_a = w < C::NPAIRS;       // A: S, P, dV;  B: dP, dS, dK (and the dS store)
+  // SiLU: roles alternate with the wave index (A: even waves, B: odd
+  // ones).  The hardware places a workgroup's waves on the CU's four SIMDs
+  // in a fixed order that starts one SIMD further for each new workgroup
+  // on the CU (read from the wave's hardware id on gfx950), so the two
+  // resident workgroups then put an A and a B wave on each SIMD; with A =
+  // waves 0, 1 half the SIMDs hold two waves of one role.  SiLU's longer
+  // weights phase (A) gains from the mix (dK/dV 990 -> 955 us on the
+  // long-sequence batch); the softmax pass does not (equal or 1 % slower),
+  // and keeps the halves.
+  constexpr bool kAltRoles = ACT == 1;
+  const int pair = kAltRoles ? w >> 1 : w % C::NPAIRS;
+  const bool role_a = kAltRoles ? (w & 1) == 0 : w < C::NPAIRS;   // A: S, P, dV;  B: dP, dS, dK (and the dS store)
   const int kw0 = t * C::BN + 32 * pair;   // first key of this pair
   const int my_key = kw0 + c32;            // the key this lane owns (its column of S)
   const bool wave_live = kw0 < lk;
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   // wave's private area of the stage
   const float* lse2_h = ACT == 0 ? a.lse2 + (size_t)h * a.total_q + qs : nullptr;
   const float* delta_h = ACT == 0 ? a.delta + (size_t)h * a.total_q + qs : nullptr;
-  const int tid_b = tid - C::NT / 2;   // B waves: 0 .. NT/2-1
+  const int tid_b = kAltRoles ? pair * kWave + l : tid - C::NT / 2;   // B waves: 0 .. NT/2-1
   Dma dma;   // Q and dO tiles share the geometry, hence the offsets
   if (!role_a) dma.init(rs, tid_b);
   auto slot = [&](int s) { return smem + (s % C::NS) * C::STAGE; };
@@ -250,8 +260,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
     dma.issue(st, qb, rs, r0, lq, tid_b, sink);
     dma.issue(st + C::QT, db, rs, r0, lq, tid_b, sink);
     if constexpr (ACT == 0) {
-      rows_dma(st + 2 * C::QT + w * 256, delta_h, r0, lq);
-      rows_dma(st + 2 * C::QT + (w - C::NPAIRS) * 256, lse2_h, r0, lq);
+      rows_dma(st + 2 * C::QT + w * 256, delta_h, r0, lq);         // this B wave's area
+      rows_dma(st + 2 * C::QT + (kAltRoles ? w ^ 1 : w - C::NPAIRS) * 256, lse2_h, r0, lq);   // its pair's A wave's area
     }
   };
 
