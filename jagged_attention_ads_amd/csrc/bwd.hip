@@ -216,7 +216,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdArgs a) {
   // SiLU: roles alternate with the wave index (A: even waves, B: odd
   // ones).  The hardware places a workgroup's waves on the CU's four SIMDs
   // in a fixed order that starts one SIMD further for each new workgroup
-  // on the CU (read from the wave's hardware id on gfx950), so the two
+  // on the CU (read from the waves' hardware ids on gfx950: 88 % of the
+  // workgroup pairs resident together differ by one step), so the two
   // resident workgroups then put an A and a B wave on each SIMD; with A =
   // waves 0, 1 half the SIMDs hold two waves of one role.  SiLU's longer
   // weights phase (A) gains from the mix (dK/dV 990 -> 955 us on the
