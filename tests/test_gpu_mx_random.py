@@ -1,0 +1,67 @@
+"""Seeded random configurations of the MXFP8 path against the oracle
+(oracle.mx): forward within the bound of tests/test_gpu_mx.py, backward
+within the gates of tests/test_gpu_mx_bwd.py.
+
+Each case draws, from its own seed: head_dim (64 or 128), the head count,
+causal or not, self- or cross-attention, and 1 to 8 sequences whose lengths
+mix empty sequences, single tokens, lengths one off an MX block or tile
+boundary (31 .. 257) and uniform ones up to 300.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.mx as mx
+from jagged_attention_ads_amd import jfa
+from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch
+from tests.test_gpu_mx import _check as check_forward, _run as run_forward
+from tests.test_gpu_mx_bwd import _check as check_backward, _device_case, _oracle_inputs
+
+pytestmark = pytest.mark.gpu
+
+BOUNDARY = [31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+N_CASES = 12
+
+
+def _length(rng):
+    kind = rng.integers(0, 6)
+    if kind == 0:
+        return 0
+    if kind == 1:
+        return 1
+    if kind in (2, 3):
+        return int(rng.choice(BOUNDARY))
+    return int(rng.integers(2, 301))
+
+
+def _batch(case):
+    rng = np.random.default_rng(8000 + case)
+    d = int(rng.choice([64, 128]))
+    heads = int(rng.choice([1, 2, 3, 4, 8]))
+    causal = bool(rng.random() < 0.5)
+    cross = bool(rng.random() < 0.4)
+    n = int(rng.integers(1, 9))
+    lq = [_length(rng) for _ in range(n)]
+    lk = [_length(rng) for _ in range(n)] if cross else list(lq)
+    wl = dataclasses.replace(WORKLOADS["selfattn_causal"], head_dim=d, heads=heads, causal=causal)
+    return make_batch(wl, 8100 + case, q_lengths=lq, kv_lengths=lk, with_dout=True)
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_mx_random_configuration(case):
+    b = _batch(case)
+    wl = b.workload
+    print("case %d: d %d heads %d causal %s q %s kv %s" % (
+        case, wl.head_dim, wl.heads, wl.causal, b.q_lengths.tolist(), b.kv_lengths.tolist()), flush=True)
+    out, lse = run_forward(b)
+    check_forward(out, lse, b.f64("q"), b.f64("k"), b.f64("v"), b.q_offsets, b.kv_offsets, b.scale, wl.causal)
+    out64, lse64 = _oracle_inputs(b)
+    q, k, v, outd, do, lsed, qo, ko, mq, mk = _device_case(b, out64, lse64)
+    got = jfa.mx_backward(q, k, v, outd, do, lsed, qo, ko, mq, mk, b.scale, wl.causal)
+    torch.cuda.synchronize()
+    ref = mx.mx_attention_bwd(b.f64("q"), b.f64("k"), b.f64("v"), out64, b.f64("dout"), lse64, b.q_offsets,
+                              b.kv_offsets, b.scale, wl.causal)
+    check_backward(got, ref, b.q_offsets, b.kv_offsets, "case %d" % case)

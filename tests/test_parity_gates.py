@@ -61,6 +61,41 @@ def test_per_sequence_floor_for_cancelling_sequences():
     assert at == 1 and worst > gpu_util.GRAD_RTOL
 
 
+def test_per_sequence_gate_on_an_all_zero_gradient():
+    """When the whole reference gradient is zero (every visible query sees a
+    single key: dS = 0, so dq = dk = 0), there is no scale to be relative
+    to, and the per-sequence error is the absolute norm, as the per-tensor
+    one is: rounding-level values pass, real ones do not."""
+    rng = np.random.default_rng(7)
+    off = offsets_from_lengths([33, 60])
+    r = np.zeros((93, 5, 128))
+    a = 1e-7 * rng.standard_normal(r.shape)
+    worst, _ = gpu_util.seq_rel_l2(a, r, off)
+    assert worst == pytest.approx(max(np.linalg.norm(a[:33]), np.linalg.norm(a[33:])), rel=1e-12)
+    assert worst < gpu_util.GRAD_RTOL_FP32
+    assert gpu_util.rel_l2(a, r) == pytest.approx(np.linalg.norm(a))
+    a[40:42] += 0.1
+    worst, at = gpu_util.seq_rel_l2(a, r, off)
+    assert at == 1 and worst > gpu_util.GRAD_RTOL
+
+
+def test_silu_weight_rounding_bound():
+    """The SiLU weight-rounding term: one key per query makes out = w v, so
+    the bound is 2^-9 |w| |v| per element, exactly; masked (causal) and
+    keyless rows get 0."""
+    import dataclasses
+    from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch
+    wl = dataclasses.replace(WORKLOADS["gdpa_silu"], head_dim=32, heads=2, causal=True)
+    b = make_batch(wl, 3, q_lengths=[4, 2], kv_lengths=[1, 0], with_dout=False)
+    bound = gpu_util.silu_weight_rounding(b)
+    q, k, v = b.f64("q"), b.f64("k"), b.f64("v")
+    # sequence 0: 4 queries, one key; causal offset -3: only query 3 sees it
+    assert not bound[:3].any() and not bound[4:].any()
+    s = (q[3] * k[0]).sum(axis=-1) * b.scale               # [H]
+    w = np.abs(s / (1.0 + np.exp(-s)))                      # L_kv = 1
+    assert np.allclose(bound[3], 2.0 ** -9 * w[:, None] * np.abs(v[0]), rtol=1e-12, atol=0)
+
+
 def test_forward_bound_flat_below_two():
     ref = np.array([0.0, 0.5, 1.99, 2.0, 3.9, 4.0, 7.9, -5.0])
     tol = gpu_util.forward_tolerance(ref, torch.bfloat16)
