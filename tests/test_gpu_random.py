@@ -21,7 +21,7 @@ from tests.gpu_util import Dev, check_backward, check_forward, oracle_bwd, oracl
 pytestmark = pytest.mark.gpu
 
 BOUNDARY = [31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
-N_CASES = 24
+N_CASES = 64
 
 
 def _length(rng):
