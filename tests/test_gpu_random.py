@@ -16,7 +16,8 @@ import pytest
 import torch
 
 from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch
-from tests.gpu_util import Dev, check_backward, check_forward, oracle_bwd, oracle_fwd, silu_weight_rounding
+from tests.gpu_util import (Dev, check_backward, check_forward, oracle_bwd, oracle_fwd, silu_weight_rounding,
+                            silu_weight_rounding_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +70,7 @@ def test_random_configuration(case, options):
     ref_out, ref_lse = oracle_fwd(b)
     # SiLU's weights are not normalised: their bf16 rounding moves the output
     # by up to 2^-9 of sum |w| |v| (tests.gpu_util.silu_weight_rounding)
-    extra = silu_weight_rounding(b) if wl.activation == "silu" and wl.dtype == "bf16" else None
+    extra = silu_weight_rounding_of(b) if wl.activation == "silu" and wl.dtype == "bf16" else None
     check_forward(out, lse, ref_out, ref_lse, wl.activation, extra_tol=extra)
     check_backward(grads, oracle_bwd(b), q_off=b.q_offsets, k_off=b.kv_offsets)
     # rows of sequences that see no key get zero dq; keys no query sees get
@@ -79,3 +80,101 @@ def test_random_configuration(case, options):
     for s in np.nonzero(b.q_lengths == 0)[0]:
         for g in grads[1:]:
             assert not (g[int(b.kv_offsets[s]):int(b.kv_offsets[s + 1])] != 0).any()
+
+
+# ------------------------------------------------------------------ BlockAttention and pooled
+
+def _block_config(case):
+    rng = np.random.default_rng(7500 + case)
+    rope = bool(rng.random() < 0.5)
+    d = int(rng.choice([64, 128])) if rope else int(rng.choice([32, 64, 128]))
+    fp32 = (not rope) and rng.random() < 0.2
+    block = 64 if rng.random() < 0.5 else int(rng.integers(1, 65))
+    heads = int(rng.choice([1, 2, 3, 4]))
+    act = "silu" if rng.random() < 0.35 else "softmax"
+    causal = bool(rng.random() < 0.5)
+    lengths = [_length(rng) for _ in range(int(rng.integers(1, 10)))]
+    base = "tiny_fp32" if fp32 else "selfattn_causal"
+    wl = dataclasses.replace(WORKLOADS[base], head_dim=d, heads=heads, activation=act, causal=causal, backward=True)
+    return wl, lengths, block, (10000.0 if rope else 0.0)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_block_configuration(case):
+    """BlockAttention through jfa_block_forward / jfa_block_backward: block
+    sizes 1 .. 64, with and without the fused rotary embedding (base 10000),
+    against the oracle's block mode."""
+    import math
+    import oracle
+    from jagged_attention_ads_amd import jfa
+    from tests.gpu_util import rope_lse_bound
+    wl, lengths, block, rope = _block_config(case)
+    print("case %d: %s d %d heads %d %s causal %s block %d rope %g lengths %s" % (
+        case, wl.dtype, wl.head_dim, wl.heads, wl.activation, wl.causal, block, rope, lengths), flush=True)
+    b = make_batch(wl, 7600 + case, q_lengths=lengths, kv_lengths=lengths, with_dout=True)
+    d = Dev(b)
+    ml = max(lengths)
+    out, lse = jfa.block_forward(d.q, d.k, d.v, d.qo, ml, block, d.scale, d.act, wl.causal, rope)
+    grads = jfa.block_backward(d.q, d.k, d.v, out, d.do, lse, d.qo, ml, block, d.scale, d.act, wl.causal, rope)
+    torch.cuda.synchronize()
+    s = 1.0 / math.sqrt(wl.head_dim)
+    args = (b.f64("q"), b.f64("k"), b.f64("v"))
+    rb = rope if rope > 0 else None   # the oracle's "no rotary embedding" is None, the ABI's is 0
+    ref_out, ref_lse = oracle.attention_fwd(*args, b.q_offsets, b.kv_offsets, s, wl.activation, wl.causal,
+                                            block=block, rope_base=rb)
+    lse_atol = rope_lse_bound(args[0], args[1], b.q_offsets, block, wl.causal, s) if rope else None
+    # SiLU: the weights of the block-token runs, over the rows the kernel
+    # multiplies (turned by the rotary embedding when there is one)
+    extra = None
+    if wl.activation == "silu" and wl.dtype == "bf16":
+        runs = _runs(b.q_offsets, block)
+        qk = args[:2]
+        if rope:
+            from oracle.rope import rope as turn, sequence_positions
+            qk = tuple(turn(x, sequence_positions(b.q_offsets), rope) for x in qk)
+        extra = silu_weight_rounding(qk[0], qk[1], args[2], runs, runs, s, wl.causal)
+    check_forward(out, lse, ref_out, ref_lse, wl.activation, lse_atol=lse_atol, extra_tol=extra)
+    ref_g = oracle.attention_bwd(*args, b.f64("dout"), b.q_offsets, b.kv_offsets, s, wl.activation, wl.causal,
+                                 block=block, rope_base=rb)
+    check_backward(grads, ref_g, q_off=b.q_offsets, k_off=b.kv_offsets)
+
+
+def _runs(offsets, block):
+    """Offsets of the block-token runs of every sequence, in order."""
+    starts = [int(offsets[i]) + c for i in range(len(offsets) - 1)
+              for c in range(0, int(offsets[i + 1] - offsets[i]), block)]
+    return np.array(starts + [int(offsets[-1])], dtype=np.int64)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_pooled_configuration(case):
+    """Pooled multi-head attention: 1 .. 16 seeds shared by every sequence."""
+    import math
+    import oracle
+    from jagged_attention_ads_amd import jfa
+    rng = np.random.default_rng(7800 + case)
+    n_seeds = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    d = int(rng.choice([32, 64, 128]))
+    fp32 = rng.random() < 0.2
+    act = "silu" if rng.random() < 0.35 else "softmax"
+    lk = [_length(rng) if rng.random() < 0.7 else int(rng.integers(300, 1500)) for _ in range(int(rng.integers(1, 9)))]
+    wl = dataclasses.replace(WORKLOADS["pooled_hist"], n_seeds=n_seeds, activation=act, head_dim=d,
+                             dtype="fp32" if fp32 else "bf16", heads=int(rng.choice([1, 2, 3, 8])))
+    print("case %d: %s d %d heads %d %s seeds %d key lengths %s" % (
+        case, wl.dtype, d, wl.heads, act, n_seeds, lk), flush=True)
+    b = make_batch(wl, 7900 + case, q_lengths=[n_seeds] * len(lk), kv_lengths=lk, with_dout=True)
+    dd = Dev(b)
+    out, lse = jfa.pooled_forward(dd.q, dd.k, dd.v, dd.ko, dd.mk, dd.scale, act)
+    grads = jfa.pooled_backward(dd.q, dd.k, dd.v, out, dd.do, lse, dd.ko, dd.mk, dd.scale, act)
+    torch.cuda.synchronize()
+    s = 1.0 / math.sqrt(d)
+    ref_out, ref_lse = oracle.pooled_fwd(b.f64("q"), b.f64("k"), b.f64("v"), b.kv_offsets, s, act)
+    extra = None
+    if act == "silu" and not fp32:
+        # the pooled rows: the seeds against each sequence's keys
+        q_rep = np.concatenate([b.f64("q")] * len(lk), axis=0)
+        extra = silu_weight_rounding(q_rep, b.f64("k"), b.f64("v"), np.arange(len(lk) + 1) * n_seeds, b.kv_offsets,
+                                     s, False)
+    check_forward(out, lse, ref_out, ref_lse, act, extra_tol=extra)
+    ref = oracle.pooled_bwd(b.f64("q"), b.f64("k"), b.f64("v"), b.f64("dout"), b.kv_offsets, s, act)
+    check_backward(grads, ref, q_off=np.array([0, n_seeds]), k_off=b.kv_offsets)

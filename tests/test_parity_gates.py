@@ -87,7 +87,7 @@ def test_silu_weight_rounding_bound():
     from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch
     wl = dataclasses.replace(WORKLOADS["gdpa_silu"], head_dim=32, heads=2, causal=True)
     b = make_batch(wl, 3, q_lengths=[4, 2], kv_lengths=[1, 0], with_dout=False)
-    bound = gpu_util.silu_weight_rounding(b)
+    bound = gpu_util.silu_weight_rounding_of(b)
     q, k, v = b.f64("q"), b.f64("k"), b.f64("v")
     # sequence 0: 4 queries, one key; causal offset -3: only query 3 sees it
     assert not bound[:3].any() and not bound[4:].any()
