@@ -544,3 +544,52 @@ def build_worklist(pass_, q_offsets, kv_offsets, heads, total_q, total_kv, max_q
     meta_off = (16 + 8 * cap + 4 * (B + 1) + 31) // 32 * 32
     records = words[meta_off // 4:meta_off // 4 + 8 * cap].view(cap, 8).clone()
     return items, tile_start, records
+
+
+# ---------------------------------------------------------------- autograd
+
+class _JaggedAttention(torch.autograd.Function):
+    """forward: jfa_forward (or the MXFP8 path); backward: jfa_backward with
+    the saved out and lse.  Only marshalling: both passes run in the
+    library's kernels."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation, causal, mx):
+        if mx:
+            out, lse = mx_forward(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, causal)
+        else:
+            out, lse = forward(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale, activation, causal)
+        ctx.save_for_backward(q, k, v, out, q_offsets, kv_offsets, *(() if lse is None else (lse,)))
+        ctx.args = (max_q_len, max_kv_len, scale, activation, causal, mx)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, q_offsets, kv_offsets, *rest = ctx.saved_tensors
+        lse = rest[0] if rest else None
+        max_q_len, max_kv_len, scale, activation, causal, mx = ctx.args
+        dout = dout.contiguous()
+        if mx:
+            dq, dk, dv = mx_backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_len, scale,
+                                     causal)
+        else:
+            dq, dk, dv = backward(q, k, v, out, dout, lse, q_offsets, kv_offsets, max_q_len, max_kv_len, scale,
+                                  activation, causal)
+        need = ctx.needs_input_grad
+        return (dq if need[0] else None, dk if need[1] else None, dv if need[2] else None,
+                None, None, None, None, None, None, None, None)
+
+
+def jagged_attention(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scale=None, activation="softmax",
+                     causal=False, mx=False):
+    """Jagged attention as a differentiable PyTorch op: out [T_q, H, d] from
+    q [T_q, H, d], k and v [T_kv, H, d] and int32 offsets [B + 1] (device
+    tensors, contiguous; bf16 or fp32, MXFP8 from bf16 with mx=True, softmax
+    only).  The backward runs jfa_backward (or jfa_mx_backward) with the
+    saved output and lse."""
+    D = q.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if mx and activation != "softmax":
+        raise ValueError("the MXFP8 path is softmax attention")
+    return _JaggedAttention.apply(q, k, v, q_offsets, kv_offsets, int(max_q_len), int(max_kv_len), scale,
+                                  activation, bool(causal), bool(mx))
