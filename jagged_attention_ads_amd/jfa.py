@@ -593,3 +593,56 @@ def jagged_attention(q, k, v, q_offsets, kv_offsets, max_q_len, max_kv_len, scal
         raise ValueError("the MXFP8 path is softmax attention")
     return _JaggedAttention.apply(q, k, v, q_offsets, kv_offsets, int(max_q_len), int(max_kv_len), scale,
                                   activation, bool(causal), bool(mx))
+
+
+class _BlockAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, offsets, max_len, block, scale, activation, causal, rope_base):
+        out, lse = block_forward(q, k, v, offsets, max_len, block, scale, activation, causal, rope_base)
+        ctx.save_for_backward(q, k, v, out, offsets, *(() if lse is None else (lse,)))
+        ctx.args = (max_len, block, scale, activation, causal, rope_base)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, offsets, *rest = ctx.saved_tensors
+        max_len, block, scale, activation, causal, rope_base = ctx.args
+        dq, dk, dv = block_backward(q, k, v, out, dout.contiguous(), rest[0] if rest else None, offsets, max_len,
+                                    block, scale, activation, causal, rope_base)
+        need = ctx.needs_input_grad
+        return (dq if need[0] else None, dk if need[1] else None, dv if need[2] else None,
+                None, None, None, None, None, None, None)
+
+
+def block_attention(q, k, v, offsets, max_len, block=64, scale=None, activation="softmax", causal=True,
+                    rope_base=0.0):
+    """BlockAttention (jfa_block_forward / jfa_block_backward) as a
+    differentiable PyTorch op; rope_base > 0 fuses the rotary embedding."""
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
+    return _BlockAttention.apply(q, k, v, offsets, int(max_len), int(block), scale, activation, bool(causal),
+                                 float(rope_base))
+
+
+class _PooledAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, seeds, k, v, kv_offsets, max_kv_len, scale, activation):
+        out, lse = pooled_forward(seeds, k, v, kv_offsets, max_kv_len, scale, activation)
+        ctx.save_for_backward(seeds, k, v, out, kv_offsets, *(() if lse is None else (lse,)))
+        ctx.args = (max_kv_len, scale, activation)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        seeds, k, v, out, kv_offsets, *rest = ctx.saved_tensors
+        max_kv_len, scale, activation = ctx.args
+        ds, dk, dv = pooled_backward(seeds, k, v, out, dout.contiguous(), rest[0] if rest else None, kv_offsets,
+                                     max_kv_len, scale, activation)
+        need = ctx.needs_input_grad
+        return (ds if need[0] else None, dk if need[1] else None, dv if need[2] else None, None, None, None, None)
+
+
+def pooled_attention(seeds, k, v, kv_offsets, max_kv_len, scale=None, activation="softmax"):
+    """Pooled multi-head attention (jfa_pooled_forward / jfa_pooled_backward)
+    as a differentiable PyTorch op: out [batch * n_seeds, H, d]."""
+    scale = 1.0 / math.sqrt(seeds.shape[-1]) if scale is None else float(scale)
+    return _PooledAttention.apply(seeds, k, v, kv_offsets, int(max_kv_len), scale, activation)

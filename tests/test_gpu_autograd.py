@@ -67,3 +67,40 @@ def test_autograd_only_requested_gradients():
     assert d.k.grad is None and d.v.grad is None
     with pytest.raises(ValueError):
         jfa.jagged_attention(q, d.k, d.v, d.qo, d.ko, d.mq, d.mk, activation="silu", mx=True)
+
+
+@pytest.mark.parametrize("rope", [0.0, 10000.0])
+def test_autograd_block_equals_direct_calls(rope):
+    wl = dataclasses.replace(WORKLOADS["selfattn_causal"], backward=True)
+    lengths = [0, 1, 63, 64, 65, 130, 257]
+    b = make_batch(wl, 97, q_lengths=lengths, kv_lengths=lengths, with_dout=True)
+    d = Dev(b)
+    q, k, v = (x.clone().requires_grad_(True) for x in (d.q, d.k, d.v))
+    out = jfa.block_attention(q, k, v, d.qo, max(lengths), 64, d.scale, "softmax", True, rope)
+    (out.float() * d.do.float()).sum().backward()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = jfa.block_forward(d.q, d.k, d.v, d.qo, max(lengths), 64, d.scale, "softmax", True, rope)
+    ref_g = jfa.block_backward(d.q, d.k, d.v, ref_out, d.do, ref_lse, d.qo, max(lengths), 64, d.scale, "softmax",
+                               True, rope)
+    torch.cuda.synchronize()
+    assert _same(out.detach(), ref_out)
+    for g, r in zip((q.grad, k.grad, v.grad), ref_g):
+        assert _same(g, r)
+
+
+@pytest.mark.parametrize("act", ["softmax", "silu"])
+def test_autograd_pooled_equals_direct_calls(act):
+    wl = dataclasses.replace(WORKLOADS["pooled_hist"], n_seeds=4, activation=act, heads=2)
+    lk = [0, 129, 700, 1, 33]
+    b = make_batch(wl, 98, q_lengths=[4] * len(lk), kv_lengths=lk, with_dout=True)
+    d = Dev(b)
+    s, k, v = (x.clone().requires_grad_(True) for x in (d.q, d.k, d.v))
+    out = jfa.pooled_attention(s, k, v, d.ko, d.mk, d.scale, act)
+    (out.float() * d.do.float()).sum().backward()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = jfa.pooled_forward(d.q, d.k, d.v, d.ko, d.mk, d.scale, act)
+    ref_g = jfa.pooled_backward(d.q, d.k, d.v, ref_out, d.do, ref_lse, d.ko, d.mk, d.scale, act)
+    torch.cuda.synchronize()
+    assert _same(out.detach(), ref_out)
+    for g, r in zip((s.grad, k.grad, v.grad), ref_g):
+        assert _same(g, r)
