@@ -45,6 +45,10 @@ WL_CASES = [
     # more sequences than a builder workgroup has threads (chunked scans)
     ("cross_asym", 3000, False),
     ("selfattn_causal", 2500, True),
+    # more sequences than the builder stages in LDS (8191): offsets read from
+    # global memory
+    ("selfattn_causal", 9000, True),
+    ("pareto_train", 12000, False),
 ]
 
 
