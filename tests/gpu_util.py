@@ -26,6 +26,18 @@ GRAD_RTOL_FP32 = 1e-4  # the same for fp32 inputs
 # 1.06e-4: the residue scales with the cancelling terms, which can be ten
 # times an average row's gradient.
 SEQ_NORM_FLOOR = 3e-1
+# ... and at this fraction of the norm of its own term magnitudes (sums of
+# |terms| of each gradient element, grad_term_magnitudes).  A gradient of n
+# terms of random sign has about 1/sqrt(n) of their magnitude (0.34 at 260
+# terms, 0.056 at 2000, measured), so below some 10^4 terms the floor is
+# under the sequence's own norm and changes nothing.  Where the terms
+# cancel -- dK and dQ with one key, where the fp32 path's residue read as
+# 7e-4 against the share floor (one key, 31 queries) -- the residue is
+# 3e-9 to 7e-7 of the
+# magnitudes (a plain float32 backward), so at most 7e-5 against this
+# floor, while an error that breaks the cancellation reads as its
+# fraction of the magnitudes times 100.
+MAG_FLOOR = 1e-2
 
 
 def dev():
@@ -116,17 +128,20 @@ def half_ulp_bf16(x):
     return np.exp2(np.floor(np.log2(ax)) - 8.0)
 
 
-def forward_tolerance(ref_out, dtype):
+def forward_tolerance(ref_out, dtype, extra=None):
     """Per-element bound on |out - ref|.  fp32: 1e-4 flat.  bf16: 1e-2 flat
     for |ref| < 2; above that the stored bf16 output alone is off by up to
     half a bf16 ulp of the value (0.0078 at 2, 0.0156 at 4: more than a flat
     1e-2 leaves for the arithmetic), so there the bound is 1e-2 plus half an
-    ulp, taken at |ref| + 1e-2 in case the rounding crosses into the next
-    binade."""
+    ulp.  extra: a per-element arithmetic bound added to the flat one
+    (which then holds below |ref| + extra = 2).  The ulp is taken where the
+    unrounded kernel value can reach, |ref| + 1e-2 + extra, in case the
+    rounding crosses into the next binade."""
+    e = 0.0 if extra is None else extra
     if dtype == torch.bfloat16:
         a = np.abs(ref_out)
-        return np.where(a < 2.0, FWD_ATOL, FWD_ATOL + half_ulp_bf16(a + FWD_ATOL))
-    return FWD_ATOL_FP32
+        return FWD_ATOL + e + np.where(a + e < 2.0, 0.0, half_ulp_bf16(a + FWD_ATOL + e))
+    return FWD_ATOL_FP32 + e
 
 
 def silu_weight_rounding(q, k, v, q_offsets, kv_offsets, scale, causal):
@@ -134,11 +149,12 @@ def silu_weight_rounding(q, k, v, q_offsets, kv_offsets, scale, causal):
     bf16 for the P V product moves the output by (q, k, v float64 [T, H, d],
     the rows the kernel multiplies; sequence b owns rows q_offsets[b] ..
     and kv_offsets[b] ..): each weight w_ij = silu(scale q_i.k_j) / L_kv is
-    rounded to 8 significant bits (relative error at most 2^-9), so out_ic
-    moves by at most 2^-9 sum_j |w_ij| |v_jc|.  The softmax weights are
-    normalised (a convex combination of V rows, the flat 1e-2 covers them);
-    SiLU's are not, and with few keys |out| reaches several units, where
-    2^-9 of it exceeds the flat 1e-2."""
+    rounded to 8 significant bits, which moves it by up to half a unit in
+    its last place: 2^-8 of it just above a power of two (4.0767 -> 4.0625),
+    so out_ic moves by at most 2^-8 sum_j |w_ij| |v_jc|.  The softmax
+    weights are normalised (a convex combination of V rows, the flat 1e-2
+    covers them); SiLU's are not, and with few keys |out| reaches several
+    units, where 2^-8 of it exceeds the flat 1e-2."""
     out = np.zeros(q.shape)
     for b in range(len(q_offsets) - 1):
         q0, q1, k0, k1 = int(q_offsets[b]), int(q_offsets[b + 1]), int(kv_offsets[b]), int(kv_offsets[b + 1])
@@ -151,7 +167,7 @@ def silu_weight_rounding(q, k, v, q_offsets, kv_offsets, scale, causal):
             j = np.arange(k1 - k0)[None, :]
             w = np.where((j <= i + (k1 - k0) - (q1 - q0))[None], w, 0.0)
         out[q0:q1] = np.einsum("hij,jhc->ihc", w, np.abs(v[k0:k1]))
-    return 2.0 ** -9 * out
+    return 2.0 ** -8 * out
 
 
 def silu_weight_rounding_of(batch):
@@ -163,8 +179,9 @@ def silu_weight_rounding_of(batch):
 def rope_lse_bound(q, k, offsets, block, causal, scale):
     """Per (head, row) bound on |lse_gpu - lse_ref| when Q and K are turned by
     the rotary embedding and the turned values rounded to bf16 before the
-    products: each rounding moves a value by at most 2^-9 of itself, so a
-    score moves by at most scale * 2^-8 * sum_c |q'_c| |k'_c|, and a turned
+    products: each rounding moves a value by at most 2^-8 of itself (half a
+    unit in the last of 8 significant bits, just above a power of two), so a
+    score moves by at most scale * 2^-7 * sum_c |q'_c| |k'_c|, and a turned
     pair (c, c + d/2) keeps its length, which bounds that sum by the pair
     lengths of the unturned rows (Cauchy-Schwarz).  lse is a smooth maximum
     of the row's scores: its error is at most the largest score error.
@@ -182,7 +199,7 @@ def rope_lse_bound(q, k, offsets, block, causal, scale):
             m = np.einsum("ihc,jhc->hij", qn[c0:c1], kn[c0:c1])   # [H, rows, keys]
             if causal:
                 m = np.where(np.tril(np.ones((c1 - c0, c1 - c0), dtype=bool))[None], m, 0.0)
-            out[:, c0:c1] += scale * 2.0 ** -8 * m.max(axis=2)
+            out[:, c0:c1] += scale * 2.0 ** -7 * m.max(axis=2)
     return out
 
 
@@ -196,9 +213,7 @@ def check_forward(out, lse, ref_out, ref_lse, activation, q_rows=None, lse_atol=
         o = o[q_rows]
     diff = np.abs(o - ref_out)
     err = float(diff.max()) if o.size else 0.0
-    tol = forward_tolerance(ref_out, out.dtype)
-    if extra_tol is not None:
-        tol = tol + extra_tol
+    tol = forward_tolerance(ref_out, out.dtype, extra_tol)
     excess = diff - tol
     worst = float(excess.max()) if o.size else -1.0
     print("forward: flat max abs error %.4g" % err)
@@ -226,14 +241,19 @@ def rel_l2(a, r):
     return na / nr
 
 
-def seq_rel_l2(a, r, offsets):
+def seq_rel_l2(a, r, offsets, mag=None):
     """Worst per-sequence relative L2 error of a jagged gradient [rows, H, d]
     whose sequence b owns rows offsets[b] .. offsets[b+1]-1, each sequence's
     reference norm floored at SEQ_NORM_FLOOR of its size's share of the
-    whole tensor's norm; and the sequence it occurs in.  A gradient that is
-    zero in exact arithmetic (e.g. dq and dk when every visible query sees a
-    single key: dP = delta, so dS = 0) has no scale to be relative to: as
-    rel_l2 does for a zero tensor, the error is then the absolute norm."""
+    whole tensor's norm, and (mag given: the gradient's term magnitudes,
+    grad_term_magnitudes) at MAG_FLOOR of the norm of its own term
+    magnitudes; and the sequence it occurs in.  A tensor that is zero in
+    exact arithmetic everywhere (e.g. dq and dk when every visible query
+    sees a single key: dP = delta, so dS = 0) has no scale to be relative
+    to: as rel_l2 does for a zero tensor, the error is then the absolute
+    norm (the magnitudes of its few terms -- one query against one key --
+    can be small against what fp32 leaves of them, which is itself small in
+    absolute terms)."""
     n = a.shape[0]
     tot = np.linalg.norm(r)
     worst, at = 0.0, -1
@@ -243,6 +263,8 @@ def seq_rel_l2(a, r, offsets):
             continue
         rb = r[s0:s1]
         den = max(np.linalg.norm(rb), SEQ_NORM_FLOOR * tot * math.sqrt((s1 - s0) / n))
+        if mag is not None and tot > 0:
+            den = max(den, MAG_FLOOR * np.linalg.norm(mag[s0:s1]))
         err = np.linalg.norm(a[s0:s1] - rb)
         e = float(err / den) if den > 0 else float(err)
         if e > worst:
@@ -250,12 +272,21 @@ def seq_rel_l2(a, r, offsets):
     return worst, at
 
 
-def check_backward(grads, refs, q_rows=None, k_rows=None, q_off=None, k_off=None):
+def beyond_slack(got, ref, allowance):
+    """got with each element's difference from ref reduced by its allowance
+    (to zero where the difference is within it)."""
+    d = got - ref
+    return ref + np.sign(d) * np.maximum(np.abs(d) - allowance, 0.0)
+
+
+def check_backward(grads, refs, q_rows=None, k_rows=None, q_off=None, k_off=None, mags=None):
     """Gates dq, dk, dv: relative L2 error per tensor, and per sequence when
     the offsets of the compared rows are given (q_off for dq, k_off for dk and
-    dv: the offsets of the rows as selected by q_rows / k_rows)."""
+    dv: the offsets of the rows as selected by q_rows / k_rows).  mags: the
+    gradients' term magnitudes (grad_term_magnitudes) like refs, for the
+    per-sequence floor MAG_FLOOR."""
     errs = []
-    for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+    for i, (name, g, r) in enumerate(zip(("dq", "dk", "dv"), grads, refs)):
         a = to_f64(g)
         rows = q_rows if name == "dq" else k_rows
         if rows is not None:
@@ -265,11 +296,61 @@ def check_backward(grads, refs, q_rows=None, k_rows=None, q_off=None, k_off=None
         assert e <= tol, "%s relative L2 error %.4g > %g" % (name, e, tol)
         off = q_off if name == "dq" else k_off
         if off is not None:
-            ws, at = seq_rel_l2(a, r, off)
+            ws, at = seq_rel_l2(a, r, off, None if mags is None else mags[i])
             print("%s: relative L2 %.4g, worst sequence %.4g (sequence %d)" % (name, e, ws, at))
             assert ws <= tol, "%s relative L2 error %.4g in sequence %d > %g" % (name, ws, at, tol)
         errs.append(e)
     return errs
+
+
+def grad_term_magnitudes(q, k, v, dout, q_offsets, kv_offsets, scale, activation, causal):
+    """Per-element sums of the magnitudes of the terms each gradient element
+    is made of (dq, dk, dv like q, k, v; float64 [T, H, d]; sequence b owns
+    rows q_offsets[b] .. and kv_offsets[b] ..), with softmax's
+    dS = P dP - P delta taken as its two parts:
+      softmax  dV_j: sum_i P_ij |dO_i|;
+               dK_j: scale sum_i P_ij (|dP_ij| + |delta_i|) |q_i|,
+               dQ_i: scale sum_j P_ij (|dP_ij| + |delta_i|) |k_j|;
+      SiLU     dV_j: sum_i |w_ij| |dO_i|, w = silu(scale q.k) / L_kv;
+               dK_j, dQ_i: scale sum |silu'(scale q.k)| |dP| / L_kv |q_i| (|k_j|).
+    fp32 arithmetic leaves a residue of a small multiple of u = 2^-24 times
+    these, whatever the exact value: where the terms cancel (one key: dP =
+    delta, so dS = 0 and dK = dQ = 0) the residue is all the fp32 result is,
+    and it has no scale of its own to be relative to."""
+    from oracle.attention import visible_mask
+    mq, mk, mv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(len(q_offsets) - 1):
+        q0, q1, k0, k1 = int(q_offsets[b]), int(q_offsets[b + 1]), int(kv_offsets[b]), int(kv_offsets[b + 1])
+        lq, lk = q1 - q0, k1 - k0
+        if lq == 0 or lk == 0:
+            continue
+        vis = visible_mask(lq, lk, causal)
+        for h in range(q.shape[1]):
+            qs, ks, vs, dos = q[q0:q1, h], k[k0:k1, h], v[k0:k1, h], dout[q0:q1, h]
+            x = scale * (qs @ ks.T)
+            dp = np.abs(dos @ vs.T)
+            if activation == "softmax":
+                xm = np.where(vis, x, -np.inf)
+                m = np.max(xm, axis=1, keepdims=True)
+                e = np.where(vis, np.exp(xm - np.where(np.isfinite(m), m, 0.0)), 0.0)
+                den = e.sum(axis=1, keepdims=True)
+                w = e / np.where(den > 0, den, 1.0)
+                delta = np.abs(((w @ vs) * dos).sum(axis=1, keepdims=True))
+                t = w * (dp + delta)
+            else:
+                sg = 1.0 / (1.0 + np.exp(-x))
+                w = np.where(vis, np.abs(x * sg) / lk, 0.0)
+                t = np.where(vis, np.abs(sg * (1.0 + x * (1.0 - sg))) / lk, 0.0) * dp
+            mv[k0:k1, h] = w.T @ np.abs(dos)
+            mk[k0:k1, h] = scale * (t.T @ np.abs(qs))
+            mq[q0:q1, h] = scale * (t @ np.abs(ks))
+    return mq, mk, mv
+
+
+def grad_term_magnitudes_of(batch):
+    """grad_term_magnitudes for a jagged batch as the jagged calls take it."""
+    return grad_term_magnitudes(batch.f64("q"), batch.f64("k"), batch.f64("v"), batch.f64("dout"), batch.q_offsets,
+                                batch.kv_offsets, batch.scale, batch.workload.activation, batch.workload.causal)
 
 
 def seq_offsets(batch, seqs=None):

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch
-from tests.gpu_util import (Dev, check_backward, check_forward, oracle_bwd, oracle_fwd, silu_weight_rounding,
-                            silu_weight_rounding_of)
+from tests.gpu_util import (Dev, check_backward, check_forward, grad_term_magnitudes, grad_term_magnitudes_of,
+                            oracle_bwd, oracle_fwd, silu_weight_rounding, silu_weight_rounding_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,10 +69,10 @@ def test_random_configuration(case, options):
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle_fwd(b)
     # SiLU's weights are not normalised: their bf16 rounding moves the output
-    # by up to 2^-9 of sum |w| |v| (tests.gpu_util.silu_weight_rounding)
+    # by up to 2^-8 of sum |w| |v| (tests.gpu_util.silu_weight_rounding)
     extra = silu_weight_rounding_of(b) if wl.activation == "silu" and wl.dtype == "bf16" else None
     check_forward(out, lse, ref_out, ref_lse, wl.activation, extra_tol=extra)
-    check_backward(grads, oracle_bwd(b), q_off=b.q_offsets, k_off=b.kv_offsets)
+    check_backward(grads, oracle_bwd(b), q_off=b.q_offsets, k_off=b.kv_offsets, mags=grad_term_magnitudes_of(b))
     # rows of sequences that see no key get zero dq; keys no query sees get
     # zero dk and dv
     for s in np.nonzero(b.kv_lengths == 0)[0]:
@@ -136,7 +136,12 @@ def test_random_block_configuration(case):
     check_forward(out, lse, ref_out, ref_lse, wl.activation, lse_atol=lse_atol, extra_tol=extra)
     ref_g = oracle.attention_bwd(*args, b.f64("dout"), b.q_offsets, b.kv_offsets, s, wl.activation, wl.causal,
                                  block=block, rope_base=rb)
-    check_backward(grads, ref_g, q_off=b.q_offsets, k_off=b.kv_offsets)
+    # term magnitudes of the block-token runs (the turned rows where there is
+    # a rotary embedding: the turn keeps pair lengths, not |q_c|, so those
+    # cases keep the share floor alone)
+    mags = None if rope else grad_term_magnitudes(*args, b.f64("dout"), _runs(b.q_offsets, block),
+                                                  _runs(b.q_offsets, block), s, wl.activation, wl.causal)
+    check_backward(grads, ref_g, q_off=b.q_offsets, k_off=b.kv_offsets, mags=mags)
 
 
 def _runs(offsets, block):
@@ -177,4 +182,10 @@ def test_random_pooled_configuration(case):
                                      s, False)
     check_forward(out, lse, ref_out, ref_lse, act, extra_tol=extra)
     ref = oracle.pooled_bwd(b.f64("q"), b.f64("k"), b.f64("v"), b.f64("dout"), b.kv_offsets, s, act)
-    check_backward(grads, ref, q_off=np.array([0, n_seeds]), k_off=b.kv_offsets)
+    # term magnitudes: every sequence's seed rows, the seeds' gradient summed
+    # over the sequences
+    q_rep = np.concatenate([b.f64("q")] * len(lk), axis=0)
+    mq, mk, mv = grad_term_magnitudes(q_rep, b.f64("k"), b.f64("v"), b.f64("dout"), np.arange(len(lk) + 1) * n_seeds,
+                                      b.kv_offsets, s, act, False)
+    mags = (mq.reshape(len(lk), n_seeds, *mq.shape[1:]).sum(axis=0), mk, mv)
+    check_backward(grads, ref, q_off=np.array([0, n_seeds]), k_off=b.kv_offsets, mags=mags)

@@ -81,7 +81,7 @@ def test_per_sequence_gate_on_an_all_zero_gradient():
 
 def test_silu_weight_rounding_bound():
     """The SiLU weight-rounding term: one key per query makes out = w v, so
-    the bound is 2^-9 |w| |v| per element, exactly; masked (causal) and
+    the bound is 2^-8 |w| |v| per element, exactly; masked (causal) and
     keyless rows get 0."""
     import dataclasses
     from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch
@@ -93,7 +93,20 @@ def test_silu_weight_rounding_bound():
     assert not bound[:3].any() and not bound[4:].any()
     s = (q[3] * k[0]).sum(axis=-1) * b.scale               # [H]
     w = np.abs(s / (1.0 + np.exp(-s)))                      # L_kv = 1
-    assert np.allclose(bound[3], 2.0 ** -9 * w[:, None] * np.abs(v[0]), rtol=1e-12, atol=0)
+    assert np.allclose(bound[3], 2.0 ** -8 * w[:, None] * np.abs(v[0]), rtol=1e-12, atol=0)
+
+
+def test_bf16_rounding_reaches_two_to_the_minus_8():
+    """The relative bound both rounding terms above use: bf16 keeps 8
+    significant bits, so rounding to nearest moves a value by at most 2^-8
+    of itself, and by more than 2^-9 just above a power of two (the weight
+    4.0767 of a one-key SiLU row rounds to 4.0625)."""
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.uniform(1.0, 2.0, 200000) * 2.0 ** rng.integers(-20, 20, 200000), [4.0767]])
+    r = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    rel = np.abs(r - x.astype(np.float32)) / np.abs(x.astype(np.float32))
+    assert rel.max() <= 2.0 ** -8
+    assert rel.max() > 0.99 * 2.0 ** -8 and rel[-1] > 2.0 ** -9
 
 
 def test_forward_bound_flat_below_two():
@@ -129,3 +142,96 @@ def test_rope_lse_bound_covers_bf16_rounding_of_turned_inputs():
     err = np.abs(lse_em - lse_ref)
     assert np.all(err <= bound)
     assert err.max() > bound.max() / 50
+
+
+def test_forward_bound_takes_the_ulp_where_the_value_can_reach():
+    """With a per-element bound added (SiLU's weights), the unrounded value
+    can cross into the next binade: the half-ulp is that binade's."""
+    ref = np.array([1.995, 3.97, 1.5, 1.97])
+    extra = np.array([0.02, 0.03, 0.0, 0.02])
+    tol = gpu_util.forward_tolerance(ref, torch.bfloat16, extra)
+    np.testing.assert_allclose(tol, [0.01 + 0.02 + 2.0 ** -7, 0.01 + 0.03 + 2.0 ** -6, 0.01, 0.01 + 0.02])
+
+
+def _fp32_backward(q, k, v, do, qo, ko, scale, act, causal, p_to_bf16=False):
+    """A plain float32 attention backward (the forward's O and lse too, in
+    float32), to measure what ordinary fp32 rounding does against the fp64
+    oracle.  p_to_bf16: round the weights to bf16 before the products (a
+    mistake an fp32 path could make)."""
+    from oracle.attention import visible_mask
+    f = np.float32
+    q, k, v, do = (x.astype(f) for x in (q, k, v, do))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    sc = f(scale)
+    for b in range(len(qo) - 1):
+        q0, q1, k0, k1 = int(qo[b]), int(qo[b + 1]), int(ko[b]), int(ko[b + 1])
+        lq, lk = q1 - q0, k1 - k0
+        if lq == 0 or lk == 0:
+            continue
+        vis = visible_mask(lq, lk, causal)
+        for h in range(q.shape[1]):
+            qs, ks, vs, ds = q[q0:q1, h], k[k0:k1, h], v[k0:k1, h], do[q0:q1, h]
+            x = (qs @ ks.T) * sc
+            dp = ds @ vs.T
+            if act == "softmax":
+                xm = np.where(vis, x, f(-np.inf))
+                m = np.max(xm, axis=1, keepdims=True)
+                with np.errstate(invalid="ignore"):   # rows that see no key: w = 0 below
+                    lse = m + np.log(np.exp(xm - m).sum(axis=1, keepdims=True))
+                w = np.where(vis, np.exp(xm - lse), f(0))
+                o = w @ vs
+                dsm = w * (dp - (ds * o).sum(axis=1, keepdims=True))
+            else:
+                sg = f(1) / (f(1) + np.exp(-x))
+                w = np.where(vis, x * sg / f(lk), f(0))
+                dsm = np.where(vis, sg * (f(1) + x * (f(1) - sg)) * dp / f(lk), f(0))
+            if p_to_bf16:
+                w = torch.from_numpy(np.ascontiguousarray(w)).to(torch.bfloat16).float().numpy()
+            dv[k0:k1, h] = w.T @ ds
+            dk[k0:k1, h] = (dsm.T @ qs) * sc
+            dq[q0:q1, h] = (dsm @ ks) * sc
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("act,causal", [("softmax", False), ("softmax", True), ("silu", False), ("silu", True)])
+def test_magnitude_floor(act, causal):
+    """The per-sequence floor on the gradients' term magnitudes: a plain
+    float32 backward passes the fp32 gate against the fp64 oracle in every
+    sequence -- long ones, one key against many queries (softmax: dK = dQ =
+    0 exactly, the float32 result is rounding residue) and cross lengths --
+    and the floor is below the norm of every sequence whose gradient does
+    not cancel, so it changes nothing there.  Mistakes an fp32 path could
+    make still fail: the weights rounded to bf16, or the one-key sequence's
+    cancellation broken (delta from a stale output)."""
+    import oracle
+    rng = np.random.default_rng(21)
+    lq, lk = [300, 700, 1, 40, 513, 31], [300, 1, 1, 260, 513, 1]
+    qo, ko = offsets_from_lengths(lq), offsets_from_lengths(lk)
+    H, d = 2, 128
+    q, do = (rng.standard_normal((int(qo[-1]), H, d)).astype(np.float32).astype(np.float64) for _ in range(2))
+    k, v = (rng.standard_normal((int(ko[-1]), H, d)).astype(np.float32).astype(np.float64) for _ in range(2))
+    scale = 1.0 / np.sqrt(d)
+    ref = oracle.attention_bwd(q, k, v, do, qo, ko, scale, act, causal)
+    mags = gpu_util.grad_term_magnitudes(q, k, v, do, qo, ko, scale, act, causal)
+    got = _fp32_backward(q, k, v, do, qo, ko, scale, act, causal)
+    worst = 0.0
+    for g, r, m, off in zip(got, ref, mags, (qo, ko, ko)):
+        w, _ = gpu_util.seq_rel_l2(g.astype(np.float64), r, off, m)
+        worst = max(worst, w)
+        for b in range(len(off) - 1):
+            s0, s1 = int(off[b]), int(off[b + 1])
+            rn = np.linalg.norm(r[s0:s1])
+            if rn > 1e-8 * np.linalg.norm(m[s0:s1]):   # not cancelling
+                assert gpu_util.MAG_FLOOR * np.linalg.norm(m[s0:s1]) < rn
+    assert worst < 0.1 * gpu_util.GRAD_RTOL_FP32
+    bad = _fp32_backward(q, k, v, do, qo, ko, scale, act, causal, p_to_bf16=True)
+    assert max(gpu_util.seq_rel_l2(g.astype(np.float64), r, off, m)[0]
+               for g, r, m, off in zip(bad, ref, mags, (qo, ko, ko))) > 2 * gpu_util.GRAD_RTOL_FP32
+    if act == "softmax" and not causal:
+        # sequence 1: 700 queries, one key; delta taken from out 1e-3 off
+        bad = [x.copy() for x in got]
+        s0, s1 = int(qo[1]), int(qo[2])
+        delta_err = 1e-3 * (do[s0:s1] * v[int(ko[1])]).sum(axis=-1)          # [700, H]
+        bad[1][int(ko[1])] -= scale * (delta_err[..., None] * q[s0:s1]).sum(axis=0)
+        w, at = gpu_util.seq_rel_l2(bad[1].astype(np.float64), ref[1], ko, mags[1])
+        assert at == 1 and w > 2 * gpu_util.GRAD_RTOL_FP32
