@@ -22,7 +22,7 @@ from tests.test_gpu_mx_bwd import _check as check_backward, _device_case, _oracl
 pytestmark = pytest.mark.gpu
 
 BOUNDARY = [31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
-N_CASES = 32
+N_CASES = 48
 
 
 def _length(rng):

@@ -22,7 +22,7 @@ from tests.gpu_util import (Dev, check_backward, check_forward, grad_term_magnit
 pytestmark = pytest.mark.gpu
 
 BOUNDARY = [31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
-N_CASES = 64
+N_CASES = 96
 
 
 def _length(rng):
