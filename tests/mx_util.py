@@ -90,12 +90,6 @@ def decode_keys_image(img, offsets, heads, d):
     return c, s, (np.concatenate([t.ravel() for t in tail]) if tail else np.zeros(0, np.uint8))
 
 
-# E4M3 midpoints between consecutive non-negative finite values and the step there
-_POS = np.sort(mx.e4m3_decode(np.arange(0x7F)))
-_MID = (_POS[:-1] + _POS[1:]) / 2
-_STEP = _POS[1:] - _POS[:-1]
-
-
 def score_error(qh, kh, t, c, eps_t=1e-5, eps_sum=3e-5):
     """Bound on the kernel's error in the scores t = c q.k (log2 units) of
     one (sequence, head) block, qh [lq, d] and kh [lk, d] the dequantised
