@@ -4,6 +4,8 @@ must reject.  A 20 % error confined to one 32-row tile of one sequence of a
 the per-sequence gate; the bf16 forward bound is a flat 1e-2 below |out| = 2
 and grows only by the output's own rounding above."""
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -235,3 +237,45 @@ def test_magnitude_floor(act, causal):
         bad[1][int(ko[1])] -= scale * (delta_err[..., None] * q[s0:s1]).sum(axis=0)
         w, at = gpu_util.seq_rel_l2(bad[1].astype(np.float64), ref[1], ko, mags[1])
         assert at == 1 and w > 2 * gpu_util.GRAD_RTOL_FP32
+
+
+@pytest.mark.parametrize("act,causal", [("softmax", False), ("softmax", True), ("silu", True)])
+def test_grad_term_magnitudes_brute_force(act, causal):
+    """grad_term_magnitudes against scalar loops over every term, written
+    from the gradients' definitions (softmax: dS = P dP - P delta, its two
+    parts apart; SiLU: dS = silu'(x) dP / L_kv), on tiny cross-length
+    sequences (causal: key j visible to query i when j <= i + L_kv - L_q)."""
+    rng = np.random.default_rng(31)
+    lq, lk = [3, 1, 4], [5, 2, 4]
+    qo, ko = offsets_from_lengths(lq), offsets_from_lengths(lk)
+    H, d, scale = 2, 4, 0.7
+    q, do = (rng.standard_normal((int(qo[-1]), H, d)) for _ in range(2))
+    k, v = (rng.standard_normal((int(ko[-1]), H, d)) for _ in range(2))
+    mq, mk, mv = gpu_util.grad_term_magnitudes(q, k, v, do, qo, ko, scale, act, causal)
+    eq, ek, ev = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(lq)):
+        for h in range(H):
+            for i in range(lq[b]):
+                qi = int(qo[b]) + i
+                keys = [j for j in range(lk[b]) if not causal or j <= i + lk[b] - lq[b]]
+                x = {j: scale * sum(q[qi, h, c] * k[int(ko[b]) + j, h, c] for c in range(d)) for j in keys}
+                dp = {j: sum(do[qi, h, c] * v[int(ko[b]) + j, h, c] for c in range(d)) for j in keys}
+                if act == "softmax":
+                    z = sum(math.exp(x[j]) for j in keys)
+                    p = {j: math.exp(x[j]) / z for j in keys}
+                    o = [sum(p[j] * v[int(ko[b]) + j, h, c] for j in keys) for c in range(d)]
+                    delta = sum(do[qi, h, c] * o[c] for c in range(d))
+                    w = p
+                    t = {j: p[j] * abs(dp[j]) + p[j] * abs(delta) for j in keys}
+                else:
+                    sg = {j: 1.0 / (1.0 + math.exp(-x[j])) for j in keys}
+                    w = {j: abs(x[j] * sg[j]) / lk[b] for j in keys}
+                    t = {j: abs(sg[j] * (1 + x[j] * (1 - sg[j])) * dp[j]) / lk[b] for j in keys}
+                for j in keys:
+                    kj = int(ko[b]) + j
+                    for c in range(d):
+                        ev[kj, h, c] += abs(w[j]) * abs(do[qi, h, c])
+                        ek[kj, h, c] += scale * t[j] * abs(q[qi, h, c])
+                        eq[qi, h, c] += scale * t[j] * abs(k[kj, h, c])
+    for got, exp in ((mq, eq), (mk, ek), (mv, ev)):
+        np.testing.assert_allclose(got, exp, rtol=1e-12, atol=1e-15)
