@@ -2,7 +2,11 @@
 must reject.  A 20 % error confined to one 32-row tile of one sequence of a
 12-sequence batch passes a whole-tensor relative L2 gate of 2e-2 but fails
 the per-sequence gate; the bf16 forward bound is a flat 1e-2 below |out| = 2
-and grows only by the output's own rounding above."""
+and grows only by the output's own rounding above.  The bounds and floors
+the gates add are checked here too: bf16 rounding reaches 2^-8 (the SiLU
+weight and RoPE terms), the term-magnitude floor leaves a plain float32
+backward passing and planted fp32 mistakes failing, and the term
+magnitudes themselves equal scalar loops over every term."""
 
 import math
 
