@@ -203,6 +203,27 @@ def rope_lse_bound(q, k, offsets, block, causal, scale):
     return out
 
 
+def rope_rounding_effect(q, k, v, offsets, block, scale, activation, causal, base):
+    """Per-element [T, H, d] effect on the output of the BlockAttention
+    kernels' rounding of the turned Q and K to bf16 before the products:
+    |attention(bf16(q'), bf16(k'), v) - attention(q', k', v)|, both by the
+    oracle's block attention in fp64, with q' and k' turned at their
+    positions within their `block`-token runs as the kernels turn them (any
+    origin gives the same attention in exact arithmetic, not the same
+    roundings).  q, k, v float64 [T, H, d]; self attention, sequence b owns
+    rows offsets[b] .."""
+    import oracle
+    from oracle.rope import rope as turn
+    off = np.asarray(offsets, dtype=np.int64)
+    pos = np.concatenate([np.arange(int(off[i + 1] - off[i])) % block for i in range(len(off) - 1)] +
+                         [np.zeros(0, np.int64)])
+    as_bf16 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()  # noqa: E731
+    qr, kr = as_bf16(turn(q, pos, base)), as_bf16(turn(k, pos, base))
+    emu, _ = oracle.attention_fwd(qr, kr, v, off, off, scale, activation, causal, block=block)
+    exact, _ = oracle.attention_fwd(q, k, v, off, off, scale, activation, causal, block=block, rope_base=base)
+    return np.abs(emu - exact)
+
+
 def check_forward(out, lse, ref_out, ref_lse, activation, q_rows=None, lse_atol=None, extra_tol=None):
     """Gates the forward; returns the flat max abs error over all elements
     (printed: the per-magnitude bound above is what is gated).  lse_atol:

@@ -13,7 +13,7 @@ import torch
 import oracle
 from jagged_attention_ads_amd import jfa
 from jagged_attention_ads_amd.workloads import WORKLOADS, make_batch, offsets_from_lengths
-from tests.gpu_util import Dev, check_backward, check_forward, dev, rope_lse_bound
+from tests.gpu_util import Dev, check_backward, check_forward, dev, rope_lse_bound, rope_rounding_effect
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +96,9 @@ ROPE_CASES = [("selfattn_causal", True, 128), ("selfattn_causal", False, 128), (
 def test_block_rope_parity(name, causal, d):
     """BlockAttention with the fused rotary embedding (base 10000) against the
     oracle (rotation of Q and K at their sequence positions, then attention
-    within 64-token blocks; gradients turned back), forward and backward."""
+    within 64-token blocks; gradients turned back), forward and backward.
+    The forward bound adds what rounding the turned Q and K to bf16 does to
+    the output (tests.gpu_util.rope_rounding_effect)."""
     wl = dataclasses.replace(WORKLOADS[name], causal=causal, head_dim=d, backward=True)
     lengths = [0, 1, 63, 64, 65, 130, 257, 40, 128, 700]
     b = make_batch(wl, 61 + d, q_lengths=lengths, kv_lengths=lengths, with_dout=True)
@@ -111,7 +113,8 @@ def test_block_rope_parity(name, causal, d):
     ref_out, ref_lse = oracle.attention_fwd(*args, b.q_offsets, b.kv_offsets, s, wl.activation, causal, block=64,
                                             rope_base=10000.0)
     check_forward(out, lse, ref_out, ref_lse, wl.activation,
-                  lse_atol=rope_lse_bound(args[0], args[1], b.q_offsets, 64, causal, s))
+                  lse_atol=rope_lse_bound(args[0], args[1], b.q_offsets, 64, causal, s),
+                  extra_tol=rope_rounding_effect(*args, b.q_offsets, 64, s, wl.activation, causal, 10000.0))
     ref_g = oracle.attention_bwd(*args, b.f64("dout"), b.q_offsets, b.kv_offsets, s, wl.activation, causal, block=64,
                                  rope_base=10000.0)
     check_backward(grads, ref_g, q_off=b.q_offsets, k_off=b.kv_offsets)
@@ -158,7 +161,8 @@ def test_block_rope_full_size_sampled():
         ref_out, ref_lse = oracle.attention_fwd(*args, one, one, s, wl.activation, wl.causal, block=wl.block,
                                                 rope_base=10000.0)
         check_forward(out[sl], lse[:, sl], ref_out, ref_lse, wl.activation,
-                      lse_atol=rope_lse_bound(args[0], args[1], one, wl.block, wl.causal, s))
+                      lse_atol=rope_lse_bound(args[0], args[1], one, wl.block, wl.causal, s),
+                      extra_tol=rope_rounding_effect(*args, one, wl.block, s, wl.activation, wl.causal, 10000.0))
         ref_g = oracle.attention_bwd(*args, b.f64("dout")[sl], one, one, s, wl.activation, wl.causal,
                                      block=wl.block, rope_base=10000.0)
         check_backward(tuple(g[sl] for g in grads), ref_g, q_off=one, k_off=one)

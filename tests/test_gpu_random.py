@@ -107,7 +107,7 @@ def test_random_block_configuration(case):
     import math
     import oracle
     from jagged_attention_ads_amd import jfa
-    from tests.gpu_util import rope_lse_bound
+    from tests.gpu_util import rope_lse_bound, rope_rounding_effect
     wl, lengths, block, rope = _block_config(case)
     print("case %d: %s d %d heads %d %s causal %s block %d rope %g lengths %s" % (
         case, wl.dtype, wl.head_dim, wl.heads, wl.activation, wl.causal, block, rope, lengths), flush=True)
@@ -123,16 +123,19 @@ def test_random_block_configuration(case):
     ref_out, ref_lse = oracle.attention_fwd(*args, b.q_offsets, b.kv_offsets, s, wl.activation, wl.causal,
                                             block=block, rope_base=rb)
     lse_atol = rope_lse_bound(args[0], args[1], b.q_offsets, block, wl.causal, s) if rope else None
+    # the rotary embedding: the turned Q and K are rounded to bf16 before the
+    # products (tests.gpu_util.rope_rounding_effect)
+    extra = rope_rounding_effect(*args, b.q_offsets, block, s, wl.activation, wl.causal, rope) if rope else None
     # SiLU: the weights of the block-token runs, over the rows the kernel
     # multiplies (turned by the rotary embedding when there is one)
-    extra = None
     if wl.activation == "silu" and wl.dtype == "bf16":
         runs = _runs(b.q_offsets, block)
         qk = args[:2]
         if rope:
             from oracle.rope import rope as turn, sequence_positions
             qk = tuple(turn(x, sequence_positions(b.q_offsets), rope) for x in qk)
-        extra = silu_weight_rounding(qk[0], qk[1], args[2], runs, runs, s, wl.causal)
+        sw = silu_weight_rounding(qk[0], qk[1], args[2], runs, runs, s, wl.causal)
+        extra = sw if extra is None else extra + sw
     check_forward(out, lse, ref_out, ref_lse, wl.activation, lse_atol=lse_atol, extra_tol=extra)
     ref_g = oracle.attention_bwd(*args, b.f64("dout"), b.q_offsets, b.kv_offsets, s, wl.activation, wl.causal,
                                  block=block, rope_base=rb)

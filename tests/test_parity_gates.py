@@ -283,3 +283,48 @@ def test_grad_term_magnitudes_brute_force(act, causal):
                         eq[qi, h, c] += scale * t[j] * abs(k[kj, h, c])
     for got, exp in ((mq, eq), (mk, ek), (mv, ev)):
         np.testing.assert_allclose(got, exp, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal,block", [(True, 64), (False, 35)])
+def test_rope_rounding_effect_within_its_first_order_bound(causal, block):
+    """rope_rounding_effect (the output change from rounding the turned Q
+    and K to bf16) against the bound that score errors |ds_ij| <= e_ij
+    imply for a softmax output to first order,
+      |d out_ic| <= sum_j p_ij (e_ij + sum_k p_ik e_ik) |v_jc - out_ic|,
+    with e_ij = scale 2^-7 sum over rotation pairs of the pair lengths of q_i
+    and k_j (each rounding moves a turned value by at most 2^-8 of itself;
+    a turn keeps pair lengths).  The effect is nonzero and within the bound,
+    and the bound is not loose by orders of magnitude."""
+    import oracle
+    from oracle.attention import visible_mask
+    rng = np.random.default_rng(41)
+    lengths = [64, 30, 100, 5]
+    off = offsets_from_lengths(lengths)
+    T, H, d = int(off[-1]), 2, 64
+    q, k, v = (rng.standard_normal((T, H, d)) for _ in range(3))
+    s = 1.0 / np.sqrt(d)
+    eff = gpu_util.rope_rounding_effect(q, k, v, off, block, s, "softmax", causal, 10000.0)
+    out, _ = oracle.attention_fwd(q, k, v, off, off, s, "softmax", causal, block=block, rope_base=10000.0)
+    h2 = d // 2
+    qn = np.sqrt(q[..., :h2] ** 2 + q[..., h2:] ** 2)
+    kn = np.sqrt(k[..., :h2] ** 2 + k[..., h2:] ** 2)
+    bound = np.zeros_like(eff)
+    for b in range(len(lengths)):
+        for c0 in range(int(off[b]), int(off[b + 1]), block):
+            c1 = min(c0 + block, int(off[b + 1]))
+            vis = visible_mask(c1 - c0, c1 - c0, causal)
+            for h in range(H):
+                from oracle.rope import rope as turn
+                pos = np.arange(c1 - c0)
+                qt, kt = turn(q[c0:c1, h:h + 1], pos)[:, 0], turn(k[c0:c1, h:h + 1], pos)[:, 0]
+                x = np.where(vis, s * (qt @ kt.T), -np.inf)
+                p = np.exp(x - x.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                e = s * 2.0 ** -7 * (qn[c0:c1, h] @ kn[c0:c1, h].T)
+                w = p * (e + (p * e).sum(axis=1, keepdims=True))
+                vv = v[c0:c1, h]
+                o = out[c0:c1, h]
+                bound[c0:c1, h] = np.einsum("ij,ijc->ic", w, np.abs(vv[None, :, :] - o[:, None, :]))
+    assert eff.max() > 0
+    assert np.all(eff <= bound * (1 + 1e-3) + 1e-12)
+    assert eff.max() > bound.max() / 100
