@@ -6,7 +6,8 @@ Each case draws, from its own seed: the element type, head_dim (32, 64,
 cross-attention, 1 to 9 sequences whose lengths mix empty sequences, single
 tokens, lengths one off a tile boundary (31 .. 257) and uniform ones up to
 300, and one of the backward's three dQ paths.  The edge-case tests pin the
-boundaries one at a time; these cases combine them.
+boundaries one at a time; these cases combine them.  Twelve more take 1 to 3
+sequences of up to 3000 tokens.
 """
 
 import dataclasses
@@ -80,6 +81,55 @@ def test_random_configuration(case, options):
     for s in np.nonzero(b.q_lengths == 0)[0]:
         for g in grads[1:]:
             assert not (g[int(b.kv_offsets[s]):int(b.kv_offsets[s + 1])] != 0).any()
+
+
+LONG = [1023, 1024, 1025, 2047, 2048, 2049]
+
+
+def _long_length(rng):
+    kind = rng.integers(0, 7)
+    if kind == 0:
+        return 1
+    if kind in (1, 2):
+        return int(rng.choice(LONG))
+    if kind == 3:
+        return int(rng.integers(2, 200))
+    return int(rng.integers(700, 3001))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_long_configuration(case, options):
+    """Long sequences: 1 to 3 of them, up to 3000 tokens (one off 1024 and
+    2048 among them), with short and single-token ones, through every
+    element type, activation, mask and dQ path, against the oracle."""
+    rng = np.random.default_rng(7200 + case)
+    fp32 = rng.random() < 0.25
+    d = int(rng.choice([32, 64, 128]))
+    heads = int(rng.choice([1, 2, 4]))
+    act = "silu" if rng.random() < 0.35 else "softmax"
+    causal = bool(rng.random() < 0.5)
+    cross = bool(rng.random() < 0.4)
+    n = int(rng.integers(1, 4))
+    lq = [_long_length(rng) for _ in range(n)]
+    lk = [_long_length(rng) for _ in range(n)] if cross else list(lq)
+    path = ["stored_ds", "recompute", "short_in_dkdv"][int(rng.integers(0, 3))]
+    wl = dataclasses.replace(WORKLOADS["tiny_fp32" if fp32 else "selfattn_causal"], head_dim=d, heads=heads,
+                             activation=act, causal=causal, backward=True)
+    print("case %d: %s d %d heads %d %s causal %s q %s kv %s dq path %s" % (
+        case, wl.dtype, d, heads, act, causal, lq, lk, path), flush=True)
+    if path == "recompute":
+        options("bwd_ds_store", 0)
+    elif path == "short_in_dkdv":
+        options("bwd_short_dq", 1)
+    b = make_batch(wl, 7300 + case, q_lengths=lq, kv_lengths=lk, with_dout=True)
+    dd = Dev(b)
+    out, lse = dd.forward()
+    grads = dd.backward(out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_fwd(b)
+    extra = silu_weight_rounding_of(b) if act == "silu" and not fp32 else None
+    check_forward(out, lse, ref_out, ref_lse, act, extra_tol=extra)
+    check_backward(grads, oracle_bwd(b), q_off=b.q_offsets, k_off=b.kv_offsets, mags=grad_term_magnitudes_of(b))
 
 
 # ------------------------------------------------------------------ BlockAttention and pooled
