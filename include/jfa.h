@@ -351,7 +351,10 @@ int jfa_pooled_backward(const void* seeds, const void* k, const void* v, const v
  * sequence's first key, the block's scale taken from its largest visible
  * weight; invisible keys weigh 0.  The normaliser and lse use the exact
  * weights.  Arithmetic: the products of the 8-bit operands accumulate in
- * fp32; out is rounded to bf16.  Workspace: jfa_mx_workspace_size with
+ * fp32; out is rounded to bf16.  When max_q_len <= 64 the attention kernel
+ * runs two waves per work item (twice the items per compute unit); its
+ * outputs equal the four-wave kernel's bit for bit, and the option
+ * JFA_OPT_FWD_SHORT = 0 keeps the four-wave kernel.  Workspace: jfa_mx_workspace_size with
  * with_images = 1 (256-byte aligned; it holds the work list and the three
  * MX images); events: NULL, or 4 events recorded before the quantisation,
  * after it, after the work list and after the attention kernel.  Errors as
@@ -487,7 +490,8 @@ int jfa_check_device_error(const void* workspace, hipStream_t stream);
  *                           sequences: 0 never, 1 whenever it can; default
  *                           when every sequence is short.
  *   JFA_OPT_FWD_SHORT       0: the forward keeps the four-wave kernel for
- *                           batches of short sequences.
+ *                           batches of short sequences, and the MXFP8
+ *                           forward for batches of short query sequences.
  * jfa_set_option returns JFA_ERR_INVALID_ARGUMENT for an unknown option or
  * a value outside -1 .. 1; jfa_get_option returns the value, or -2 for an
  * unknown option. */

@@ -840,7 +840,10 @@ int mx_attend_impl(const uint8_t* qimg, const uint8_t* kimg, const uint8_t* vimg
   a.total_q = total_q;
   a.causal = causal;
   a.scale_log2 = scale * 1.4426950408889634f;
-  e = jfa::launch_mx_fwd(a, head_dim, L.wq.capacity, stream);
+  // at most 64 queries per sequence: the two-wave kernel (JFA_OPT_FWD_SHORT =
+  // 0 keeps the four-wave one; the outputs are equal bit for bit)
+  const bool narrow = max_q_len <= 64 && option(JFA_OPT_FWD_SHORT) != 0;
+  e = jfa::launch_mx_fwd(a, head_dim, narrow, L.wq.capacity, stream);
   if (e != hipSuccess) return hip_fail(e, "MXFP8 forward kernel launch");
   if (e2 && (e = hipEventRecord(e2, stream)) != hipSuccess) return hip_fail(e, "event record");
   return JFA_OK;

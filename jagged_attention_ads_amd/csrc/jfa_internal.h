@@ -200,7 +200,7 @@ struct MxFwdArgs {
   int32_t causal;
   float scale_log2;
 };
-hipError_t launch_mx_fwd(const MxFwdArgs& a, int head_dim, int64_t grid, hipStream_t stream);
+hipError_t launch_mx_fwd(const MxFwdArgs& a, int head_dim, bool narrow, int64_t grid, hipStream_t stream);
 
 // MXFP8 backward (see mx_bwd.hip): every product takes its operands in MX
 // blocks along its own contraction axis.  Row images (blocks along the head

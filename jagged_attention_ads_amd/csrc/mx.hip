@@ -19,7 +19,9 @@
 //    that the sequences' blocks never share a block row and no prefix sum
 //    is needed.
 //  * mx_fwd_kernel: one workgroup (4 waves x 32 queries) per 128-query
-//    work item, K and V tiles of 64 keys copied into LDS by buffer loads
+//    work item -- 2 waves when no sequence has more than 64 queries, so
+//    that no wave of an item idles and twice the items fit a compute
+//    unit --, K and V tiles of 64 keys copied into LDS by buffer loads
 //    that write LDS.  S^T = K Q^T on the block-scaled matrix cores leaves
 //    every lane one query and 16 keys of each 32-key block; those 32 keys
 //    are exactly one MX block of P, so P's block max is a lane-local max and
@@ -195,9 +197,9 @@ hipError_t launch_mx_quant(const MxQuantArgs& a, int head_dim, int count, hipStr
 
 // ------------------------------------------------------------------ attention
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxFwdArgs a) {
-  using C = MxCfg<D>;
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void mx_fwd_kernel(MxFwdArgs a) {
+  using C = MxCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   char* const kslot0 = smem;                     // [K tile | K scales] x 2
   char* const vslot0 = smem + 2 * C::KSLOT;      // [V^T tile | V scales] x 2
@@ -432,13 +434,20 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxFwdArgs a) {
     a.lse[(size_t)h * a.total_q + qs + my_row] = row_live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-template __global__ void mx_fwd_kernel<64>(MxFwdArgs);
-template __global__ void mx_fwd_kernel<128>(MxFwdArgs);
+template __global__ void mx_fwd_kernel<64, 4>(MxFwdArgs);
+template __global__ void mx_fwd_kernel<128, 4>(MxFwdArgs);
+template __global__ void mx_fwd_kernel<64, 2>(MxFwdArgs);
+template __global__ void mx_fwd_kernel<128, 2>(MxFwdArgs);
 
-hipError_t launch_mx_fwd(const MxFwdArgs& a, int head_dim, int64_t grid, hipStream_t stream) {
+// narrow: every sequence has at most 64 queries, so every item of the
+// forward list is tile 0 and two waves cover its rows.
+hipError_t launch_mx_fwd(const MxFwdArgs& a, int head_dim, bool narrow, int64_t grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 64) hipLaunchKernelGGL(mx_fwd_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, a);
-  else if (head_dim == 128) hipLaunchKernelGGL(mx_fwd_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  const dim3 g((unsigned)grid);
+  if (head_dim == 64 && narrow) hipLaunchKernelGGL((mx_fwd_kernel<64, 2>), g, dim3(128), 0, stream, a);
+  else if (head_dim == 128 && narrow) hipLaunchKernelGGL((mx_fwd_kernel<128, 2>), g, dim3(128), 0, stream, a);
+  else if (head_dim == 64) hipLaunchKernelGGL((mx_fwd_kernel<64, 4>), g, dim3(256), 0, stream, a);
+  else if (head_dim == 128) hipLaunchKernelGGL((mx_fwd_kernel<128, 4>), g, dim3(256), 0, stream, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -66,9 +66,13 @@ __device__ __forceinline__ void bf16x2_to_float(uint32_t u, float& lo, float& hi
 // 0..3), the accumulator rows its scores arrive in, as 16 consecutive bytes.
 __host__ __device__ constexpr int mx_key_pos(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
-template <int D>
+// NW waves of 32 queries per work item: 4 (the forward list's 128-row
+// items), or 2 when no sequence has more than 64 queries (every item is then
+// tile 0, rows 0 .. 63, and twice the items fit a compute unit).
+template <int D, int NW = 4>
 struct MxCfg {
-  static constexpr int BM = kFwdBM, BN = kFwdBN, NT = 256;
+  static constexpr int BM = 32 * NW, BN = kFwdBN, NT = 64 * NW;
+  static_assert(NW == 2 || (NW == 4 && BM == kFwdBM), "two or four waves; four cover a forward tile");
   static constexpr int CPR = D / 16;          // 16-byte chunks per K row
   static constexpr int RPL = 256 / D;         // K rows per 256-byte LDS line
   static constexpr int KT = BN * D;           // K tile bytes

@@ -179,6 +179,30 @@ def test_mx_full_size_sampled(name):
            q_rows=qr)
 
 
+SHORT_Q = {
+    # name: (head_dim, heads, q lengths (each at most 64), kv lengths, causal)
+    "short_q_d64": (64, 8, [1, 17, 64, 0, 33, 5], [300, 5, 1000, 40, 0, 129], False),
+    "short_q_causal_d128": (128, 2, [64, 1, 40, 63], [64, 700, 33, 2], True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHORT_Q))
+def test_mx_two_wave_forward(name, options):
+    """No sequence longer than 64 queries: the forward runs two waves per
+    item.  Its outputs equal the four-wave kernel's (JFA_OPT_FWD_SHORT = 0)
+    bit for bit, and the oracle's within the bound."""
+    d, H, lq, lk, causal = SHORT_Q[name]
+    wl = dataclasses.replace(WORKLOADS["selfattn_causal"], head_dim=d, heads=H, causal=causal)
+    b = make_batch(wl, 1300 + sorted(SHORT_Q).index(name), q_lengths=lq, kv_lengths=lk, with_dout=False)
+    print("case", name, flush=True)
+    out, lse = _run(b)
+    options("fwd_short", 0)
+    out4, lse4 = _run(b)
+    assert torch.equal(out.view(torch.int16), out4.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse4.view(torch.int32))
+    _check(out, lse, b.f64("q"), b.f64("k"), b.f64("v"), b.q_offsets, b.kv_offsets, b.scale, causal)
+
+
 def test_mx_attend_from_images_equals_forward():
     """jfa_mx_forward is jfa_mx_quantize of q, k, v then jfa_mx_attend, bit
     for bit."""
